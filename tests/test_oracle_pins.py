@@ -1,0 +1,363 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test fixes the oracle to something independent of its own code: a
+hand-worked example, closed forms of the gated delta rule (Gated DeltaNet,
+ICLR 2025, Sec. 3), an exact-rational evaluation of the product form, an
+autograd derivation of the delta rule as one online-regression step, and
+structural invariants (prefix causality, chaining, linearity,
+non-expansiveness, key-head sharing).  A dropped term, a wrong sign, a wrong
+index or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(seed, NL=1, N=1, T=5, Hv=2, Hk=2, dk=6, dv=5):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((NL, N, T, Hk, dk))
+    k = r.standard_normal((NL, N, T, Hk, dk))
+    v = r.standard_normal((NL, N, T, Hv, dv))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((NL, N, T, Hv))))
+    g = -np.logaddexp(0.0, r.standard_normal((NL, N, T, Hv)))
+    S0 = 0.3 * r.standard_normal((NL, N, Hv, dk, dv))
+    return q, k, v, beta, g, S0
+
+
+def _unit(x):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + oracle.EPS)
+
+
+# ------------------------------------------------------------ hand example
+def test_hand_worked_two_steps():
+    case = json.load(open(os.path.join(GOLDEN, "hand_two_steps.json")))
+    S0m = np.array(case["S0"])          # dv x dk
+    steps = case["steps"]
+    T = len(steps)
+    q = np.array([s["q"] for s in steps]).reshape(1, 1, T, 1, 2)
+    k = np.array([s["k"] for s in steps]).reshape(1, 1, T, 1, 2)
+    v = np.array([s["v"] for s in steps]).reshape(1, 1, T, 1, 2)
+    beta = np.array([s["beta"] for s in steps]).reshape(1, 1, T, 1)
+    g = np.log(np.array([s["alpha"] for s in steps])).reshape(1, 1, T, 1)
+    S0 = S0m.T.reshape(1, 1, 1, 2, 2)   # stored key-major
+    o, st = oracle.verify(q, k, v, beta, g, S0, [T], l2norm=False,
+                          want_states=True)
+    for t, s in enumerate(steps):
+        np.testing.assert_allclose(st[0, 0, t, 0].T, np.array(s["S_after"]),
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_allclose(o[0, 0, t, 0], np.array(s["o"]),
+                                   rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------ closed forms
+def test_single_step_closed_form():
+    """T = 1: S_1 = S_0 alpha (I - beta khat khat^T) + beta v khat^T,
+    o = S_1 qhat, with L2 normalisation on."""
+    q, k, v, beta, g, S0 = _rand_case(1, T=1, Hv=3, Hk=3, dk=7, dv=4)
+    o, st = oracle.verify(q, k, v, beta, g, S0, [1], l2norm=True,
+                          want_states=True)
+    for h in range(3):
+        kh = _unit(k[0, 0, 0, h])
+        qh = _unit(q[0, 0, 0, h])
+        a, b = math.exp(g[0, 0, 0, h]), beta[0, 0, 0, h]
+        Sm = S0[0, 0, h].T
+        S1 = Sm @ (a * (np.eye(7) - b * np.outer(kh, kh))) + b * np.outer(
+            v[0, 0, 0, h], kh)
+        np.testing.assert_allclose(st[0, 0, 0, h].T, S1, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(o[0, 0, 0, h], S1 @ qh, rtol=0, atol=1e-13)
+
+
+def test_zero_gates_leave_state_unchanged():
+    """beta = 0 and g = 0 (alpha = 1): S_t = S_0 exactly, o_t = S_0 qhat_t."""
+    q, k, v, beta, g, S0 = _rand_case(2, T=6, Hv=4, Hk=2, dk=8, dv=8)
+    beta[:] = 0.0
+    g[:] = 0.0
+    o, st = oracle.verify(q, k, v, beta, g, S0, [6], l2norm=True,
+                          want_states=True)
+    for t in range(6):
+        for h in range(4):
+            assert np.array_equal(st[0, 0, t, h], S0[0, 0, h])
+            qh = _unit(q[0, 0, t, h // 2])
+            np.testing.assert_allclose(o[0, 0, t, h], S0[0, 0, h].T @ qh,
+                                       rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("basis", ["qr", "permuted_standard"])
+def test_delta_rule_writes_value_at_key(basis):
+    """alpha = 1, beta = 1, orthonormal k_1..k_T: S_T k_i = v_i for all i."""
+    dk, dv, T = 8, 5, 6
+    r = np.random.default_rng(3)
+    if basis == "qr":
+        Qm, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+        ks = Qm[:, :T].T
+    else:
+        perm = r.permutation(dk)[:T]
+        ks = np.eye(dk)[perm]
+    q = r.standard_normal((1, 1, T, 1, dk))
+    k = ks.reshape(1, 1, T, 1, dk)
+    v = r.standard_normal((1, 1, T, 1, dv))
+    beta = np.ones((1, 1, T, 1))
+    g = np.zeros((1, 1, T, 1))
+    S0 = r.standard_normal((1, 1, 1, dk, dv))
+    _, st = oracle.verify(q, k, v, beta, g, S0, [T], l2norm=False,
+                          want_states=True)
+    ST = st[0, 0, T - 1, 0].T
+    for i in range(T):
+        np.testing.assert_allclose(ST @ ks[i], v[0, 0, i, 0], rtol=0,
+                                   atol=1e-12)
+    # directions orthogonal to every key keep S_0's action
+    if basis == "permuted_standard":
+        for j in set(range(dk)) - set(perm.tolist()):
+            np.testing.assert_allclose(ST[:, j], S0[0, 0, 0].T[:, j], atol=1e-14)
+
+
+def test_full_forgetting():
+    """alpha = 0 (g = -inf): S_t = beta_t v_t khat_t^T, o_t = beta_t
+    (khat_t . qhat_t) v_t."""
+    q, k, v, beta, g, S0 = _rand_case(4, T=4, Hv=2, Hk=1, dk=6, dv=3)
+    g[:] = -np.inf
+    o, st = oracle.verify(q, k, v, beta, g, S0, [4], l2norm=True,
+                          want_states=True)
+    for t in range(4):
+        for h in range(2):
+            kh, qh = _unit(k[0, 0, t, 0]), _unit(q[0, 0, t, 0])
+            b = beta[0, 0, t, h]
+            np.testing.assert_allclose(st[0, 0, t, h].T,
+                                       b * np.outer(v[0, 0, t, h], kh),
+                                       rtol=0, atol=1e-15)
+            np.testing.assert_allclose(o[0, 0, t, h],
+                                       b * (kh @ qh) * v[0, 0, t, h],
+                                       rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------ independent derivations
+def test_delta_rule_is_online_regression_step():
+    """Each step equals one gradient step of size beta on the regression loss
+    0.5 * ||S' khat - v||^2 taken from the decayed state S' = alpha S_{t-1}
+    (the delta / Widrow-Hoff rule).  The gradient comes from torch autograd
+    in fp64, not from the oracle's formula."""
+    torch = pytest.importorskip("torch")
+    q, k, v, beta, g, S0 = _rand_case(5, T=7, Hv=2, Hk=1, dk=6, dv=4)
+    o, st = oracle.verify(q, k, v, beta, g, S0, [7], l2norm=True,
+                          want_states=True)
+    for h in range(2):
+        S = torch.tensor(S0[0, 0, h].T, dtype=torch.float64)
+        for t in range(7):
+            kh = torch.tensor(_unit(k[0, 0, t, 0]))
+            qh = torch.tensor(_unit(q[0, 0, t, 0]))
+            Sd = (math.exp(g[0, 0, t, h]) * S).detach().requires_grad_(True)
+            loss = 0.5 * torch.sum((Sd @ kh - torch.tensor(v[0, 0, t, h])) ** 2)
+            (grad,) = torch.autograd.grad(loss, Sd)
+            S = (Sd - beta[0, 0, t, h] * grad).detach()
+            np.testing.assert_allclose(st[0, 0, t, h].T, S.numpy(), rtol=0,
+                                       atol=1e-13)
+            np.testing.assert_allclose(o[0, 0, t, h], (S @ qh).numpy(),
+                                       rtol=0, atol=1e-13)
+
+
+def _frac_mat(rows):
+    return [[Fraction(x) for x in row] for row in rows]
+
+
+def _mm(A, B):
+    return [[sum(A[i][l] * B[l][j] for l in range(len(B)))
+             for j in range(len(B[0]))] for i in range(len(A))]
+
+
+def test_exact_rational_product_form():
+    """Brute force in exact rationals: S_t = S_0 A_1..A_t + sum_s beta_s v_s
+    k_s^T A_{s+1}..A_t with A_s = alpha_s (I - beta_s k_s k_s^T), no
+    normalisation.  The oracle must agree to fp64 rounding."""
+    dk, dv, T = 4, 3, 4
+    r = np.random.default_rng(6)
+    ri = lambda *s: r.integers(-4, 5, size=s)
+    k = [[Fraction(int(x), 4) for x in ri(dk)] for _ in range(T)]
+    qv = [[Fraction(int(x), 4) for x in ri(dk)] for _ in range(T)]
+    v = [[Fraction(int(x), 2) for x in ri(dv)] for _ in range(T)]
+    alpha = [Fraction(1, 2), Fraction(3, 4), Fraction(1, 1), Fraction(5, 8)]
+    beta = [Fraction(1, 4), Fraction(1, 2), Fraction(3, 8), Fraction(1, 8)]
+    S0 = [[Fraction(int(x), 8) for x in ri(dk)] for _ in range(dv)]  # dv x dk
+
+    def A(s):
+        return [[alpha[s] * ((1 if i == j else 0) - beta[s] * k[s][i] * k[s][j])
+                 for j in range(dk)] for i in range(dk)]
+
+    exp_S, exp_o = [], []
+    for t in range(T):
+        # S_0 A_0 .. A_t
+        acc = S0
+        for s in range(t + 1):
+            acc = _mm(acc, A(s))
+        for s in range(t + 1):
+            term = [[beta[s] * v[s][i] * k[s][j] for j in range(dk)]
+                    for i in range(dv)]
+            for s2 in range(s + 1, t + 1):
+                term = _mm(term, A(s2))
+            acc = [[acc[i][j] + term[i][j] for j in range(dk)] for i in range(dv)]
+        exp_S.append(acc)
+        exp_o.append([sum(acc[i][j] * qv[t][j] for j in range(dk))
+                      for i in range(dv)])
+
+    f = lambda x: np.array(x, dtype=np.float64)
+    q = f(qv).reshape(1, 1, T, 1, dk)
+    kk = f(k).reshape(1, 1, T, 1, dk)
+    vv = f(v).reshape(1, 1, T, 1, dv)
+    bb = f(beta).reshape(1, 1, T, 1)
+    gg = np.log(f(alpha)).reshape(1, 1, T, 1)
+    S0s = f(S0).T.reshape(1, 1, 1, dk, dv)
+    o, st = oracle.verify(q, kk, vv, bb, gg, S0s, [T], l2norm=False,
+                          want_states=True)
+    for t in range(T):
+        np.testing.assert_allclose(st[0, 0, t, 0].T, f(exp_S[t]), rtol=0,
+                                   atol=1e-13)
+        np.testing.assert_allclose(o[0, 0, t, 0], f(exp_o[t]), rtol=0,
+                                   atol=1e-13)
+
+
+# ------------------------------------------------------------- invariants
+def test_l2norm_flag_matches_prenormalised_inputs():
+    q, k, v, beta, g, S0 = _rand_case(7, T=5, Hv=2, Hk=2, dk=6, dv=4)
+    o1, s1 = oracle.verify(q, k, v, beta, g, S0, [5], l2norm=True,
+                           want_states=True)
+    o2, s2 = oracle.verify(_unit(q), _unit(k), v, beta, g, S0, [5],
+                           l2norm=False, want_states=True)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-14)
+
+
+def test_scale_multiplies_output_only():
+    q, k, v, beta, g, S0 = _rand_case(8, T=4)
+    o1, s1 = oracle.verify(q, k, v, beta, g, S0, [4], scale=1.0,
+                           want_states=True)
+    o2, s2 = oracle.verify(q, k, v, beta, g, S0, [4], scale=0.375,
+                           want_states=True)
+    assert np.array_equal(s1, s2)
+    np.testing.assert_allclose(o2, 0.375 * o1, rtol=1e-15, atol=0)
+
+
+def test_prefix_causality_and_commit():
+    """Column m of a T-window equals an m-window; commit(m) returns it; a
+    lane's rows past its own T_lane are untouched and lanes do not mix."""
+    q, k, v, beta, g, S0 = _rand_case(9, NL=2, N=3, T=6, Hv=4, Hk=2, dk=5,
+                                      dv=6)
+    t_full = np.array([6, 6, 6])
+    o, st = oracle.verify(q, k, v, beta, g, S0, t_full, want_states=True)
+    for m in range(0, 7):
+        t_short = np.array([m, 6, max(m, 1)])
+        o2, st2 = oracle.verify(q, k, v, beta, g, S0, t_short,
+                                want_states=True)
+        np.testing.assert_array_equal(o2[:, 0, :m], o[:, 0, :m])
+        assert not np.any(o2[:, 0, m:])
+        np.testing.assert_array_equal(o2[:, 1], o[:, 1])
+        Sc = oracle.commit(q, k, v, beta, g, S0, [m, 0, 6])
+        if m == 0:
+            np.testing.assert_array_equal(Sc[:, 0], S0[:, 0])
+        else:
+            np.testing.assert_array_equal(Sc[:, 0], st[:, 0, m - 1])
+        np.testing.assert_array_equal(Sc[:, 1], S0[:, 1])
+        np.testing.assert_array_equal(Sc[:, 2], st[:, 2, 5])
+
+
+def test_chained_rounds_equal_one_long_window():
+    """verify+commit(T1) then verify on the next window == one window of
+    T1 + T2 tokens."""
+    T1, T2 = 3, 4
+    q, k, v, beta, g, S0 = _rand_case(10, T=T1 + T2, Hv=2, Hk=1)
+    o, st = oracle.verify(q, k, v, beta, g, S0, [T1 + T2], want_states=True)
+    a = slice(0, T1)
+    b = slice(T1, T1 + T2)
+    S1 = oracle.commit(q[:, :, a], k[:, :, a], v[:, :, a], beta[:, :, a],
+                       g[:, :, a], S0, [T1])
+    o2, st2 = oracle.verify(q[:, :, b], k[:, :, b], v[:, :, b], beta[:, :, b],
+                            g[:, :, b], S1, [T2], want_states=True)
+    np.testing.assert_allclose(o2, o[:, :, b], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st2, st[:, :, b], rtol=0, atol=1e-13)
+
+
+def test_linear_in_state_and_values_jointly():
+    q, k, v, beta, g, S0 = _rand_case(11, T=5, Hv=2, Hk=2)
+    _, _, v2, _, _, S02 = _rand_case(12, T=5, Hv=2, Hk=2)
+    c = -1.75
+    oa, sa = oracle.verify(q, k, v, beta, g, S0, [5], want_states=True)
+    ob, sb = oracle.verify(q, k, v2, beta, g, S02, [5], want_states=True)
+    oc, sc = oracle.verify(q, k, v + c * v2, beta, g, S0 + c * S02, [5],
+                           want_states=True)
+    np.testing.assert_allclose(oc, oa + c * ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sc, sa + c * sb, rtol=0, atol=1e-12)
+
+
+def test_homogeneous_part_is_non_expansive():
+    """v = 0, beta in [0, 2], alpha <= 1: ||S_t||_2 never grows (and it
+    shrinks strictly along khat when 0 < beta < 2)."""
+    q, k, v, beta, g, S0 = _rand_case(13, T=12, Hv=3, Hk=3, dk=6, dv=6)
+    v[:] = 0.0
+    r = np.random.default_rng(13)
+    beta[:] = r.uniform(0.0, 2.0, size=beta.shape)
+    _, st = oracle.verify(q, k, v, beta, g, S0, [12], want_states=True)
+    for h in range(3):
+        prev = np.linalg.norm(S0[0, 0, h], 2)
+        for t in range(12):
+            cur = np.linalg.norm(st[0, 0, t, h], 2)
+            assert cur <= prev * (1 + 1e-12)
+            prev = cur
+    # a sign error (beta -> -beta) would make it expand: check that the
+    # invariant has teeth on the same data
+    _, st_neg = oracle.verify(q, k, v, -beta, np.zeros_like(g), S0, [12],
+                              want_states=True)
+    assert np.linalg.norm(st_neg[0, 0, 11, 0], 2) > np.linalg.norm(S0[0, 0, 0], 2)
+
+
+def test_key_head_sharing_matches_duplicated_keys():
+    """Value head h reads key head h // (Hv/Hk)."""
+    q, k, v, beta, g, S0 = _rand_case(14, T=4, Hv=6, Hk=2, dk=5, dv=3)
+    o, st = oracle.verify(q, k, v, beta, g, S0, [4], want_states=True)
+    idx = np.arange(6) // 3
+    o2, st2 = oracle.verify(q[:, :, :, idx], k[:, :, :, idx], v, beta, g, S0,
+                            [4], want_states=True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(st, st2)
+
+
+def test_prefill_matches_window_and_checkpoints():
+    """Prefill of L tokens: o and the states at multiples of the checkpoint
+    interval equal the step-by-step window run; S_final = S_L."""
+    L, Hv, Hk, dk, dv, ci = 23, 2, 1, 5, 4, 8
+    r = np.random.default_rng(15)
+    q = r.standard_normal((L, Hk, dk))
+    k = r.standard_normal((L, Hk, dk))
+    v = r.standard_normal((L, Hv, dv))
+    beta = r.uniform(0, 1, (L, Hv))
+    g = -r.uniform(0, 1, (L, Hv))
+    S_init = 0.1 * r.standard_normal((Hv, dk, dv))
+    o, ck, Sf = oracle.prefill(q, k, v, beta, g, S_init, ckpt_interval=ci)
+    ow, st = oracle.verify(q[None, None], k[None, None], v[None, None],
+                           beta[None, None], g[None, None], S_init[None, None],
+                           [L], want_states=True)
+    np.testing.assert_array_equal(o, ow[0, 0])
+    assert ck.shape == (L // ci, Hv, dk, dv)
+    for c in range(L // ci):
+        np.testing.assert_array_equal(ck[c], st[0, 0, ci * (c + 1) - 1])
+    np.testing.assert_array_equal(Sf, st[0, 0, L - 1])
+    # zero initial state when none is given
+    o0, _, Sf0 = oracle.prefill(q, k, v, beta, g, None, ckpt_interval=ci)
+    ow0, st0 = oracle.verify(q[None, None], k[None, None], v[None, None],
+                             beta[None, None], g[None, None],
+                             np.zeros((1, 1, Hv, dk, dv)), [L], want_states=True)
+    np.testing.assert_array_equal(o0, ow0[0, 0])
+    np.testing.assert_array_equal(Sf0, st0[0, 0, L - 1])
+
+
+def test_rejects_bad_arguments():
+    q, k, v, beta, g, S0 = _rand_case(16, T=3)
+    with pytest.raises(ValueError):
+        oracle.verify(q, k, v, beta, g, S0, [4])
+    with pytest.raises(ValueError):
+        oracle.commit(q, k, v, beta, g, S0, [-1])
