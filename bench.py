@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta speculative-decoding hot path on one MI355X.
+
+One step = one speculative round over the whole batch:
+    gdn_verify  (8 lanes x 48 layers x 32 value heads / 16 key heads,
+                 d_k = d_v = 128, T = 16 window tokens per lane)
+    gdn_commit  (m_lane ~ Uniform{0..16}, seeded, drawn up front)
+with the recurrent state carried from one step to the next.  Inputs are
+seeded synthetic tensors (gdn_synth), resident in HBM before the timed
+region; four input sets rotate so that the 256 MB Infinity Cache cannot
+hold a step's inputs from the previous use.
+
+Printed: one JSON line (metric, value = head-token updates/s, roofline of
+the dominant kernel, cpu_baseline = the fp64 oracle on a bounded sample).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "GDN verify+commit head-token updates/s & % HBM roofline (8 lanes, T=16)"
+
+NL, N, HV, HK, DK, DV, T = 48, 8, 32, 16, 128, 128, 16
+
+
+def alg_bytes_verify(t_lane):
+    """Algorithmic bytes of one verify call: per (layer, lane) the S0 read
+    (h_v*d_k*d_v*4) plus, per window token, q and k rows (bf16), v (bf16),
+    beta and g (f32), o (f32) and the records (khat f32 [h_k][d_k], u f32
+    [h_v][d_v], alpha f32 [h_v])."""
+    s0 = HV * DK * DV * 4
+    per_tok = (2 * HK * DK * 2 + HV * DV * 2 + 2 * HV * 4 + HV * DV * 4 +
+               HK * DK * 4 + HV * DV * 4 + HV * 4)
+    return NL * sum(s0 + per_tok * int(t) for t in t_lane)
+
+
+def alg_bytes_commit(m_lane):
+    """S0 read + S_m write for lanes with m > 0, plus m records each."""
+    s = HV * DK * DV * 4
+    rec = HK * DK * 4 + HV * DV * 4 + HV * 4
+    return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
+
+
+def cpu_baseline(rounds=3):
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload: `rounds` chained rounds (verify + commit) of the full
+    48-layer x 8-lane batch at T = 16; scaled to head-token updates/s."""
+    import gdn_synth as gs
+    import oracle
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
+    S = gs.initial_state(shape, (9, 0)).astype(np.float64)
+    dt = 0.0
+    for r in range(rounds):
+        w = gs.window_inputs(shape, (9, r))
+        m = gs.accepted_uniform(w.t_lane, (9, r))
+        q, k, v, b, g = w.as_f64()
+        t0 = time.perf_counter()
+        oracle.verify(q, k, v, b, g, S, w.t_lane)
+        S = oracle.commit(q, k, v, b, g, S, m)
+        dt += time.perf_counter() - t0
+    upd = rounds * NL * N * T * HV
+    return {"value": upd / dt, "unit": "head-token updates/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d chained rounds (verify + commit) of the full "
+                      "48-layer x 8-lane batch, T=16, fp64 C oracle with "
+                      "OpenMP over chains; %.1f s of oracle time" % (rounds, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pool", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; --gpus %d is not supported.  The "
+              "verify/commit path needs no exchange between GPUs: each GPU "
+              "runs its own share of the lanes (or of the value-head pairs) "
+              "independently." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
+    t_lane = np.full(N, T, dtype=np.int32)
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    pool = []
+    for p in range(args.pool):
+        w = gs.window_inputs(shape, (7, p))
+        pool.append((dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                     torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(w.g).to(dev)))
+    S = torch.from_numpy(gs.initial_state(shape, (7, 0))).to(dev)
+    o = torch.empty((NL, N, T, HV, DV), device=dev)
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    total = args.warmup + args.steps
+    m_all = [gs.accepted_uniform(t_lane, (7, 100 + s)) for s in range(total)]
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        q, k, v, beta, g = pool[s % len(pool)]
+        if ev is not None:
+            ev[0].record(stream)
+        gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_v = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_c = [e[1].elapsed_time(e[2]) for e in evs]
+
+    upd_per_step = int(t_lane.sum()) * NL * HV
+    ms_per_step = total_ms / args.steps
+    value = upd_per_step / (ms_per_step * 1e-3)
+    bv = alg_bytes_verify(t_lane)
+    bc = [alg_bytes_commit(m_all[args.warmup + s]) for s in range(args.steps)]
+    gbs_v = bv / (np.mean(ms_v) * 1e-3) / 1e9
+    gbs_c = np.mean(bc) / (np.mean(ms_c) * 1e-3) / 1e9
+    gbs_path = (bv + np.mean(bc)) / (ms_per_step * 1e-3) / 1e9
+    dominant = "verify" if np.mean(ms_v) >= np.mean(ms_c) else "commit"
+    if dominant == "verify":
+        ach, per_launch, kms = gbs_v, bv, float(np.mean(ms_v))
+    else:
+        ach, per_launch, kms = gbs_c, float(np.mean(bc)), float(np.mean(ms_c))
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-token updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state / bf16 q,k,v",
+        "data": "synthetic (seeded gdn_synth inputs; S0 ~ N(0, 0.01))",
+        "config": {"workload": "verify+commit round: 8 lanes x 48 layers x "
+                               "32 value / 16 key heads, d_k=d_v=128, T=16, "
+                               "m ~ U{0..16}, state carried across steps",
+                   "n_lanes": N, "n_layers": NL, "h_v": HV, "h_k": HK,
+                   "d_k": DK, "d_v": DV, "t": T},
+        "hbm_roofline_frac_path": gbs_path / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "gdn_verify" if dominant ==
+                     "verify" else "gdn_commit",
+                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": per_launch,
+                     "avg_launch_ms": kms},
+        "verify_ms": float(np.mean(ms_v)),
+        "commit_ms": float(np.mean(ms_c)),
+        "verify_alg_GBps": gbs_v,
+        "commit_alg_GBps": gbs_c,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

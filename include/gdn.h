@@ -1,0 +1,196 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated-delta speculative-decoding path.
+ *
+ * Three operations, all asynchronous on the caller's HIP stream:
+ *
+ *   gdn_verify           advance every (layer, lane, value head) recurrent
+ *                        state S0 over a draft window of T <= t_max tokens by
+ *                        the gated delta rule, write the outputs o_t = S_t q_t
+ *                        and compact per-step transition records.  S0 itself
+ *                        is never written.
+ *   gdn_commit           ReplaySSM commit: replay the first m records of each
+ *                        lane from the untouched S0 and store S_m in place.
+ *   gdn_prefill_chunked  run the same recurrence over a long sequence in
+ *                        chunks and emit fp32 state checkpoints at every
+ *                        multiple of the checkpoint interval.
+ *
+ * The rule (Yang, Kautz & Hatamizadeh, "Gated Delta Networks: Improving
+ * Mamba2 with Delta Rule", ICLR 2025, Sec. 3), per value head with state S
+ * (a d_v x d_k matrix mapping keys to values):
+ *
+ *   khat = k / sqrt(|k|^2 + 1e-6), qhat likewise  (when GDN_FLAG_L2NORM_QK)
+ *   alpha_t = exp(g_t)
+ *   u_t = beta_t * (v_t - alpha_t * S_{t-1} khat_t)
+ *   S_t = alpha_t * S_{t-1} + u_t khat_t^T
+ *   o_t = scale * S_t qhat_t
+ *
+ * Value head h reads key head h / (h_v / h_k).
+ *
+ * The window protocol follows the NInfer technical review (blog.123qwe.co.kr
+ * post 4624): section "Architecture 3: speculative decoding and ReplaySSM"
+ * (one checkpoint plus compact records, replay of the accepted prefix from the
+ * same S0, equality of the transitions in finite precision rather than over
+ * the reals; 1..5 or 1..15 drafts plus the anchor token) and section
+ * "Architecture 1: engine split by ownership" (results are provisional until
+ * the real prefix is fixed; only then is the model state committed, so a
+ * round that is cancelled simply never calls commit).  At most 8 active
+ * requests per engine (the review's "key facts" table) -- the library takes
+ * up to GDN_MAX_LANES.
+ *
+ * Storage layouts (row-major, outermost first; "bf16|f32" = in_dtype):
+ *   q, k    [n_layers][n_lanes][t_max][h_k][d_k]       bf16|f32
+ *   v       [n_layers][n_lanes][t_max][h_v][d_v]       bf16|f32
+ *   beta, g [n_layers][n_lanes][t_max][h_v]            f32
+ *   S       [n_layers][n_lanes][h_v][d_k][d_v]         f32 (S[.][j][i] = S_ij)
+ *   o       [n_layers][n_lanes][t_max][h_v][d_v]       f32
+ * Token rows t >= T_lane[lane] of q, k, v, beta, g are not read and the
+ * matching rows of o are not written.
+ *
+ * Ownership: the caller allocates every buffer (device memory unless stated
+ * "host"); the library allocates, frees and synchronises nothing and keeps no
+ * state between calls.  All pointers to device memory must be 4-byte aligned
+ * (16-byte aligned for best speed).
+ *
+ * Errors: every argument error is found on the host, before any HIP call, and
+ * returned as a negative gdn_status; nothing is launched then.  A launch
+ * failure returns GDN_EHIP.  No C++ exception crosses this interface.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_MAX_LANES 256 /* lanes per call */
+#define GDN_MAX_T 64      /* window tokens per lane (the pages use <= 16) */
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,       /* bad argument (null pointer, range, shape) */
+  GDN_EUNSUPPORTED = -2, /* valid but not built (e.g. d_k not in {16,32,64,128}) */
+  GDN_EWORKSPACE = -3,   /* workspace too small */
+  GDN_EHIP = -4          /* a HIP launch or runtime call failed */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+enum { GDN_FLAG_L2NORM_QK = 1 }; /* normalise q and k inside the kernels */
+
+typedef struct {
+  int32_t n_layers; /* >= 1: independent layers batched in one call       */
+  int32_t n_lanes;  /* 1..GDN_MAX_LANES: requests (execution lanes)        */
+  int32_t h_v;      /* >= 1 value heads                                    */
+  int32_t h_k;      /* >= 1 key heads, h_v % h_k == 0                      */
+  int32_t d_k;      /* key head dim: 16, 32, 64 or 128                     */
+  int32_t d_v;      /* value head dim: 1..1024                             */
+  int32_t t_max;    /* 1..GDN_MAX_T: window stride (anchor + drafts)       */
+} gdn_dims;
+
+/*
+ * Bytes of the opaque record buffer that gdn_verify fills and gdn_commit
+ * reads for these dims.  Returns 0 for invalid dims.  The records of one
+ * verify stay valid until the next gdn_verify into the same buffer; S must
+ * not be modified between a verify and its commit.
+ *
+ * Record contents (the "compact records that caused the transitions" of the
+ * ReplaySSM section): per (layer, lane, token) the raw key rows widened to
+ * f32 (f32 [h_k][d_k]), the decays alpha_t = exp(g_t) (f32 [h_v]) and the
+ * delta vectors with the key norm folded in, u_t / sqrt(|k_t|^2 + 1e-6)
+ * (f32 [h_v][d_v]).  About 24.7 KB per token per lane-layer at 32/16 heads
+ * of dim 128, against 2 MiB for a full per-token state snapshot.
+ */
+size_t gdn_records_bytes(const gdn_dims* dims);
+
+/*
+ * Speculative-window verify (ReplaySSM section of the review).
+ *   t_lane      host int32[n_lanes], 0..t_max: window length of each lane
+ *               (0 = idle lane, nothing read or written for it).
+ *   q, k, v     device, in_dtype; beta, g device f32 (layouts above).
+ *   S           device f32, the window checkpoint S0; read only.
+ *   o           device f32 outputs o_t = scale * S_t qhat_t.
+ *   records     device, gdn_records_bytes(dims) bytes, written.
+ *   dbg_states  device f32 [n_layers][n_lanes][t_max][h_v][d_k][d_v] or
+ *               NULL: when given, every intermediate state S_1..S_T, as the
+ *               kernel holds it (for tests; costs 64 KiB per head per token).
+ *   scale       multiplies o only (1.0f for o_t = S_t q_t).
+ *   flags       GDN_FLAG_L2NORM_QK or 0.
+ *   stream      hipStream_t (NULL = the null stream).
+ */
+int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
+               const void* k, const void* v, int in_dtype, const float* beta,
+               const float* g, const float* S, float* o, void* records,
+               float* dbg_states, float scale, int flags, void* stream);
+
+/*
+ * ReplaySSM commit (ReplaySSM section of the review): for every lane with
+ * m_lane[lane] > 0, replay records[0:m] from S (which must still hold the S0
+ * that the matching gdn_verify read) and store S_m into S in place.  Lanes
+ * with m = 0 are neither read nor written.  S_m is bit-for-bit the state that
+ * gdn_verify held after its m-th token (and wrote to dbg_states), because
+ * both run the same per-step instruction sequence; no steps are folded.
+ *   m_lane   host int32[n_lanes], 0..t_lane[lane]
+ *   t_lane   host int32[n_lanes], as passed to the matching gdn_verify
+ *   records  device, as filled by that gdn_verify
+ *   S        device f32, in: S0, out: S_m
+ */
+int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
+               const int32_t* t_lane, const void* records, float* S,
+               void* stream);
+
+/*
+ * Workspace bytes that gdn_prefill_chunked needs for these sizes (0 for
+ * invalid sizes).
+ */
+size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
+                                   int32_t h_v, int32_t h_k, int32_t d_k,
+                                   int32_t d_v);
+
+/*
+ * Chunked prefill of the gated delta rule with periodic state checkpoints
+ * (interval default 8192 tokens: context_cache.checkpoint_interval in the
+ * review's section "Architecture 2: context byte pool and prefix reuse").
+ * Chunks of 64 tokens use the WY/UT block form of Yang et al., "Parallelizing
+ * Linear Transformers with the Delta Rule over Sequence Length" (NeurIPS
+ * 2024), extended with the per-token decay of Gated DeltaNet.
+ *   n_seqs       >= 1 independent sequences of equal length seq_len >= 1
+ *   q, k         device [n_seqs][seq_len][h_k][d_k] in_dtype
+ *   v            device [n_seqs][seq_len][h_v][d_v] in_dtype
+ *   beta, g      device f32 [n_seqs][seq_len][h_v]
+ *   S_init       device f32 [n_seqs][h_v][d_k][d_v] or NULL (zero state)
+ *   S_final      device f32 [n_seqs][h_v][d_k][d_v], the state after the
+ *                last token (may alias S_init)
+ *   o            device f32 [n_seqs][seq_len][h_v][d_v]
+ *   checkpoints  device f32 [n_seqs][seq_len / ckpt_interval][h_v][d_k][d_v]
+ *                or NULL: the state after every token count that is a
+ *                positive multiple of ckpt_interval
+ *   ckpt_interval  positive multiple of 64
+ *   workspace    device, ws_bytes >= gdn_prefill_workspace_bytes(...)
+ * Supported: d_k == d_v == 128.
+ */
+int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
+                        int32_t h_k, int32_t d_k, int32_t d_v,
+                        int32_t ckpt_interval, const void* q, const void* k,
+                        const void* v, int in_dtype, const float* beta,
+                        const float* g, const float* S_init, float* S_final,
+                        float* o, float* checkpoints, void* workspace,
+                        size_t ws_bytes, float scale, int flags, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* gdn_strerror(int status);
+
+/*
+ * Detail of the most recent failing call on the calling thread (which
+ * argument was rejected, or the HIP error string of a failed launch).  The
+ * string is owned by the library and stays valid until the next failing call
+ * on the same thread; never NULL.
+ */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H_ */

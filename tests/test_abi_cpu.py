@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/gdn.h declares, and rejects bad arguments on the host with a status
+code before any HIP call (so these calls are safe on a machine with no GPU).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import commit_gated_delta_amd as gdn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "gdn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_exported_set():
+    assert _declared() == sorted(gdn.EXPORTED)
+
+
+@pytest.mark.parametrize("sym", sorted(gdn.EXPORTED))
+def test_symbol_exported(sym):
+    assert hasattr(gdn.lib, sym)
+    assert ctypes.cast(getattr(gdn.lib, sym), ctypes.c_void_p).value
+
+
+def test_strerror():
+    for st in (0, -1, -2, -3, -4, 17):
+        assert isinstance(gdn.lib.gdn_strerror(st), bytes)
+
+
+def _dims(**kw):
+    base = dict(n_layers=1, n_lanes=2, h_v=4, h_k=2, d_k=128, d_v=128, t_max=8)
+    base.update(kw)
+    return gdn.Dims.of(**base)
+
+
+def test_records_bytes():
+    d = _dims()
+    n = gdn.records_bytes(d)
+    ntok = 1 * 2 * 8
+    # raw key rows (f32 [h_k][d_k]) + ut (f32 [h_v][d_v]) + alpha (f32 [h_v])
+    assert n >= ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 4)
+    assert n < ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 4) + 3 * 256
+    assert n % 256 == 0
+    assert gdn.records_bytes(_dims(d_k=24)) == 0
+    assert gdn.records_bytes(_dims(h_v=3)) == 0
+    assert gdn.records_bytes(_dims(t_max=65)) == 0
+    assert gdn.records_bytes(_dims(n_lanes=257)) == 0
+
+
+class _Fake:
+    """Stands in for a tensor: a 256-aligned host address, never touched
+    because every call below is rejected before any memory access."""
+
+    def __init__(self, dtype_code=gdn.GDN_BF16, addr=1 << 20):
+        self.addr = addr
+        import torch
+        self.dtype = torch.bfloat16 if dtype_code == gdn.GDN_BF16 else torch.float32
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _verify(d, t_lane, **over):
+    a = dict(q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),
+             g=_Fake(gdn.GDN_F32), S=_Fake(gdn.GDN_F32), o=_Fake(gdn.GDN_F32),
+             rec=_Fake(gdn.GDN_F32))
+    a.update(over)
+    return gdn.verify(d, t_lane, a["q"], a["k"], a["v"], a["beta"], a["g"],
+                      a["S"], a["o"], a["rec"], stream=0, raw_status=True)
+
+
+def test_verify_rejects_bad_arguments_on_host():
+    d = _dims()
+    assert _verify(_dims(d_k=24), [1, 1]) == gdn.GDN_EUNSUPPORTED
+    assert _verify(_dims(h_v=3), [1, 1]) == gdn.GDN_EINVAL
+    assert _verify(_dims(t_max=0), [1, 1]) == gdn.GDN_EINVAL
+    assert _verify(_dims(t_max=65), [1, 1]) == gdn.GDN_EINVAL
+    assert _verify(_dims(d_v=0), [1, 1]) == gdn.GDN_EINVAL
+    assert _verify(_dims(d_v=1025), [1, 1]) == gdn.GDN_EINVAL
+    assert _verify(d, [9, 1]) == gdn.GDN_EINVAL          # T > t_max
+    assert _verify(d, [-1, 1]) == gdn.GDN_EINVAL
+    assert _verify(d, [1, 1], q=None) == gdn.GDN_EINVAL
+    assert _verify(d, [1, 1], rec=None) == gdn.GDN_EINVAL
+    assert _verify(d, [1, 1], S=_Fake(gdn.GDN_F32, addr=(1 << 20) + 2)) == gdn.GDN_EINVAL
+    assert _verify(d, [1, 1], rec=_Fake(gdn.GDN_F32, addr=(1 << 20) + 16)) == gdn.GDN_EINVAL
+    # unknown flag bits
+    st = gdn.lib.gdn_verify(ctypes.byref(d), (ctypes.c_int32 * 2)(1, 1),
+                            *[ctypes.c_void_p(1 << 20)] * 3, gdn.GDN_BF16,
+                            *[ctypes.c_void_p(1 << 20)] * 5, None,
+                            ctypes.c_float(1.0), 6, None)
+    assert st == gdn.GDN_EINVAL
+    # unknown dtype
+    st = gdn.lib.gdn_verify(ctypes.byref(d), (ctypes.c_int32 * 2)(1, 1),
+                            *[ctypes.c_void_p(1 << 20)] * 3, 7,
+                            *[ctypes.c_void_p(1 << 20)] * 5, None,
+                            ctypes.c_float(1.0), 1, None)
+    assert st == gdn.GDN_EINVAL
+
+
+def test_verify_with_only_idle_lanes_does_nothing():
+    # t_lane all zero: valid, nothing to launch, returns OK without HIP
+    assert _verify(_dims(), [0, 0]) == gdn.GDN_OK
+
+
+def test_commit_rejects_bad_arguments_on_host():
+    d = _dims()
+    rec, S = _Fake(gdn.GDN_F32), _Fake(gdn.GDN_F32)
+    c = lambda m, t, **kw: gdn.commit(kw.get("d", d), m, t, kw.get("rec", rec),
+                                      kw.get("S", S), stream=0,
+                                      raw_status=True)
+    assert c([3, 1], [2, 1]) == gdn.GDN_EINVAL     # m > T
+    assert c([-1, 0], [2, 1]) == gdn.GDN_EINVAL
+    assert c([0, 0], [9, 1]) == gdn.GDN_EINVAL     # T > t_max
+    assert c([0, 0], [2, 1], d=_dims(d_k=8)) == gdn.GDN_EUNSUPPORTED
+    assert c([1, 0], [2, 1], rec=None) == gdn.GDN_EINVAL
+    assert c([1, 0], [2, 1], S=_Fake(gdn.GDN_F32, addr=(1 << 20) + 1)) == gdn.GDN_EINVAL
+    # every m = 0: a cancelled round, nothing is launched
+    assert c([0, 0], [2, 1]) == gdn.GDN_OK
+
+
+def test_binding_checks_lane_count():
+    with pytest.raises(ValueError):
+        _verify(_dims(), [1, 1, 1])

@@ -1,0 +1,317 @@
+"""GPU parity of gdn_verify / gdn_commit against the fp64 oracle, and the
+bit-exact replay invariant (commit(m) == verify's own state after token m).
+
+Every call goes through the C ABI (libgdn.so via the ctypes binding).
+Tolerance: 2e-4 block-relative error on o and S (tests/gpu_util.py).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+import oracle
+from tests.gpu_util import (TOL, o_rel_err, s_rel_err, to_dev,
+                            window_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import commit_gated_delta_amd as gdn  # noqa: E402  (fails loudly if not built)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run_verify(dims, w, S_dev, dbg=False, scale=1.0, l2norm=True):
+    q, k, v, beta, g = window_to_dev(w, torch)
+    o = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
+                    dims.d_v), float("nan"), device="cuda")
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device="cuda")
+    dbg_t = None
+    if dbg:
+        dbg_t = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
+                            dims.d_k, dims.d_v), float("nan"), device="cuda")
+    gdn.verify(dims, w.t_lane, q, k, v, beta, g, S_dev, o, rec, dbg_t,
+               scale=scale, l2norm=l2norm)
+    return o, rec, dbg_t
+
+
+def _check_untouched_rows(o_np, t_lane):
+    T = o_np.shape[2]
+    for n, t in enumerate(t_lane):
+        assert np.all(np.isfinite(o_np[:, n, :t])), "missing output rows"
+        assert np.all(np.isnan(o_np[:, n, t:])), "rows past T_lane written"
+
+
+SMALL = [
+    # (name, NL, N, Hv, Hk, dk, dv, T, bf16, ragged, l2norm, scale)
+    ("cfg0_like", 1, 1, 2, 2, 16, 16, 4, False, False, True, 1.0),
+    ("d128_two_col_blocks", 2, 3, 4, 2, 128, 128, 16, True, True, True, 1.0),
+    ("d64_col_tail", 1, 2, 2, 1, 64, 96, 5, True, True, True, 1.0),
+    ("d32_dv200_f32", 1, 1, 3, 3, 32, 200, 7, False, False, True, 1.0),
+    ("d16_noscale_nonorm", 2, 2, 2, 2, 16, 16, 4, False, False, False, 0.5),
+    ("d128_group4", 1, 2, 8, 2, 128, 64, 3, True, False, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_window_parity_and_bitexact_replay(case):
+    name, NL, N, Hv, Hk, dk, dv, T, bf16, ragged, l2norm, scale = case
+    say("case", name)
+    shape = gs.WindowShape(NL, N, Hv, Hk, dk, dv, T)
+    key = (100, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=ragged)
+    if not l2norm:   # unnormalised keys must keep the rule stable
+        w.k = (w.k.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
+        w.q = (w.q.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(NL, N, Hv, Hk, dk, dv, T)
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True, scale=scale,
+                              l2norm=l2norm)
+    torch.cuda.synchronize()
+    o_np = o.cpu().numpy()
+    dbg_np = dbg.cpu().numpy()
+    assert np.array_equal(S_dev.cpu().numpy(), S0), "verify wrote S0"
+    _check_untouched_rows(o_np, w.t_lane)
+
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, st_ref = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane,
+                                  scale=scale, l2norm=l2norm, want_states=True)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    say("  o err %.3e" % e_o)
+    assert e_o <= TOL
+    for t in range(T):
+        lanes = [n for n in range(N) if w.t_lane[n] > t]
+        if lanes:
+            e_s = s_rel_err(dbg_np[:, lanes, t], st_ref[:, lanes, t])
+            assert e_s <= TOL, (t, e_s)
+
+    # commit(m) for every m of every lane, bitwise against verify's column m
+    for m in range(0, T + 1):
+        m_lane = np.minimum(m, w.t_lane)
+        S_c = to_dev(S0, torch)
+        gdn.commit(dims, m_lane, w.t_lane, rec, S_c)
+        S_c = S_c.cpu().numpy()
+        for n in range(N):
+            mm = int(m_lane[n])
+            want = S0[:, n] if mm == 0 else dbg_np[:, n, mm - 1]
+            assert np.array_equal(S_c[:, n], want), (m, n)
+        S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m_lane,
+                              l2norm=l2norm)
+        assert s_rel_err(S_c, S_ref) <= TOL
+
+
+def test_verify_is_deterministic_and_leaves_state():
+    shape = gs.WindowShape(2, 4, 4, 2, 128, 128, 16)
+    w = gs.window_inputs(shape, (101,), ragged=True)
+    S0 = gs.initial_state(shape, (101,))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o1, r1, _ = _run_verify(dims, w, S_dev)
+    o2, r2, _ = _run_verify(dims, w, S_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(o1, 7.0), torch.nan_to_num(o2, 7.0))
+    # records: every byte that verify writes is identical (unwritten padding
+    # rows of ragged lanes are compared through commit instead)
+    m = w.t_lane.copy()
+    Sa, Sb = to_dev(S0, torch), to_dev(S0, torch)
+    gdn.commit(dims, m, w.t_lane, r1, Sa)
+    gdn.commit(dims, m, w.t_lane, r2, Sb)
+    assert torch.equal(Sa, Sb)
+    assert np.array_equal(S_dev.cpu().numpy(), S0)
+
+
+def test_zero_gates_are_bitwise_identity():
+    """beta = 0, g = 0: u = 0 and alpha = 1, so every step is
+    fma(0, k, 1*S) = S exactly; commit(T) returns S0 bit for bit."""
+    shape = gs.WindowShape(1, 2, 4, 2, 128, 128, 8)
+    w = gs.window_inputs(shape, (102,))
+    w.beta[:] = 0.0
+    w.g[:] = 0.0
+    S0 = gs.initial_state(shape, (102,))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, _ = _run_verify(dims, w, S_dev)
+    gdn.commit(dims, w.t_lane, w.t_lane, rec, S_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(S_dev.cpu().numpy(), S0)
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
+    assert o_rel_err(o.cpu().numpy(), o_ref, w.t_lane) <= TOL
+
+
+def test_idle_lane_and_zero_accept():
+    """t_lane = 0 lanes are neither read nor written; m = 0 lanes keep S."""
+    shape = gs.WindowShape(1, 3, 2, 1, 64, 64, 4)
+    w = gs.window_inputs(shape, (103,), t_lane=[4, 0, 2])
+    S0 = gs.initial_state(shape, (103,))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    o_np = o.cpu().numpy()
+    assert np.all(np.isnan(o_np[:, 1]))
+    assert np.all(np.isnan(dbg.cpu().numpy()[:, 1]))
+    gdn.commit(dims, [0, 0, 2], w.t_lane, rec, S_dev)
+    S1 = S_dev.cpu().numpy()
+    assert np.array_equal(S1[:, 0], S0[:, 0])
+    assert np.array_equal(S1[:, 1], S0[:, 1])
+    assert np.array_equal(S1[:, 2], dbg.cpu().numpy()[:, 2, 1])
+
+
+def test_config0_tiny_case():
+    """1 lane, 1 layer, 2 heads, d = 16, T = 4, f32 inputs; m ~ U{0..4}."""
+    shape = gs.config_shape(0)
+    w = gs.window_inputs(shape, (0, 0), bf16=False)
+    S0 = gs.initial_state(shape, (0, 0))
+    m = gs.accepted_uniform(w.t_lane, (0, 0))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    gdn.commit(dims, m, w.t_lane, rec, S_dev)
+    torch.cuda.synchronize()
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
+    S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m)
+    S_gpu = S_dev.cpu().numpy()
+    say("config 0: m =", m, "o err %.2e S err %.2e" % (
+        o_rel_err(o.cpu().numpy(), o_ref, w.t_lane), s_rel_err(S_gpu, S_ref)))
+    assert o_rel_err(o.cpu().numpy(), o_ref, w.t_lane) <= TOL
+    assert s_rel_err(S_gpu, S_ref) <= TOL
+    want = S0 if m[0] == 0 else dbg.cpu().numpy()[:, :, m[0] - 1]
+    assert np.array_equal(S_gpu, want)
+
+
+def test_config2_full_size_ragged():
+    """8 lanes x 48 layers x 32/16 heads, d = 128, T_l ~ U{1..16},
+    m_l ~ U{0..T_l}: full o and S parity against the oracle, and bit-exact
+    replay on layer 0 (debug states)."""
+    shape = gs.config_shape(2)
+    say("config 2: generating inputs")
+    w = gs.window_inputs(shape, (2, 0), ragged=True)
+    S0 = gs.initial_state(shape, (2, 0))
+    m = gs.accepted_uniform(w.t_lane, (2, 0))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    say("config 2: verify, T =", w.t_lane, "m =", m)
+    o, rec, _ = _run_verify(dims, w, S_dev)
+    o_np = o.cpu().numpy()
+    _check_untouched_rows(o_np, w.t_lane)
+    gdn.commit(dims, m, w.t_lane, rec, S_dev)
+    S_gpu = S_dev.cpu().numpy()
+    say("config 2: oracle")
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    del o_ref
+    S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m)
+    e_s = s_rel_err(S_gpu, S_ref)
+    say("config 2: o err %.3e  S err %.3e" % (e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL
+
+    # bit-exact replay on layer 0 through a one-layer call with debug states
+    d1 = gdn.Dims.of(1, shape.n_lanes, shape.h_v, shape.h_k, 128, 128,
+                     shape.t_max)
+    w1 = gs.WindowInputs(d1, True, w.q[:1], w.k[:1], w.v[:1], w.beta[:1],
+                         w.g[:1], w.t_lane)
+    S1 = to_dev(S0[:1], torch)
+    _, rec1, dbg1 = _run_verify(d1, w1, S1, dbg=True)
+    gdn.commit(d1, m, w.t_lane, rec1, S1)
+    dbg1 = dbg1.cpu().numpy()
+    S1 = S1.cpu().numpy()
+    for n in range(shape.n_lanes):
+        want = S0[:1, n] if m[n] == 0 else dbg1[:, n, m[n] - 1]
+        assert np.array_equal(S1[:, n], want), n
+    # the one-layer call and the 48-layer call agree bit for bit
+    assert np.array_equal(S1, S_gpu[:1])
+
+
+def _chained(cfg, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
+    """Chained verify -> commit(m) rounds; the oracle follows the sampled
+    layers through every round.  Window inputs cycle through a pool of
+    seeded sets, gates are redrawn every round.  Returns per-round errors."""
+    shape = gs.config_shape(cfg)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S0 = gs.initial_state(shape, (cfg, 0))
+    S_dev = to_dev(S0, torch)
+    S_or = S0[sample_layers].astype(np.float64)
+    pool_w = [gs.window_inputs(shape, (cfg, 1000 + p)) for p in range(pool)]
+    o_buf = torch.empty((shape.n_layers, shape.n_lanes, shape.t_max, shape.h_v,
+                         shape.d_v), device="cuda")
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device="cuda")
+    sl = list(sample_layers)
+    errs = []
+    t_lane = np.full(shape.n_lanes, t_fixed, dtype=np.int32)
+    dev_pool = [window_to_dev(pw, torch)[:3] for pw in pool_w]
+    for r in range(rounds):
+        base = pool_w[r % pool]
+        gw = gs.window_inputs(gs.WindowShape(shape.n_layers, shape.n_lanes,
+                                             shape.h_v, 1, 1, 1, shape.t_max),
+                              (cfg, 5000 + r))
+        beta, g = gw.beta, gw.g
+        m = acc(t_lane, (cfg, r))
+        q, k, v = dev_pool[r % pool]
+        beta_d, g_d = to_dev(beta, torch), to_dev(g, torch)
+        # bit-exact replay, every round, on one sampled layer: a one-layer
+        # verify with debug states on the same pre-commit state
+        L = sl[r % len(sl)]
+        d1 = gdn.Dims.of(1, shape.n_lanes, shape.h_v, shape.h_k, shape.d_k,
+                         shape.d_v, shape.t_max)
+        S_L = S_dev[L:L + 1].clone()
+        o1 = torch.empty((1, shape.n_lanes, shape.t_max, shape.h_v,
+                          shape.d_v), device="cuda")
+        rec1 = torch.empty(gdn.records_bytes(d1), dtype=torch.uint8,
+                           device="cuda")
+        dbg1 = torch.empty((1, shape.n_lanes, shape.t_max, shape.h_v,
+                            shape.d_k, shape.d_v), device="cuda")
+        gdn.verify(d1, t_lane, q[L:L + 1], k[L:L + 1], v[L:L + 1],
+                   beta_d[L:L + 1], g_d[L:L + 1], S_L, o1, rec1, dbg1)
+        gdn.verify(dims, t_lane, q, k, v, beta_d, g_d, S_dev, o_buf, rec)
+        gdn.commit(dims, m, t_lane, rec, S_dev)
+        after = S_dev[L].cpu().numpy()
+        before = S_L[0].cpu().numpy()
+        snaps = dbg1[0].cpu().numpy()
+        for n in range(shape.n_lanes):
+            want = before[n] if m[n] == 0 else snaps[n, m[n] - 1]
+            assert np.array_equal(after[n], want), ("replay not bit-exact",
+                                                     r, L, n)
+        o_np = o_buf[sl].cpu().numpy()
+        q64, k64, v64 = (gs.bf16_bits_to_f64(a[sl]) for a in
+                         (base.q, base.k, base.v))
+        b64, g64 = beta[sl].astype(np.float64), g[sl].astype(np.float64)
+        o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S_or, t_lane)
+        S_or = oracle.commit(q64, k64, v64, b64, g64, S_or, m)
+        e_o = o_rel_err(o_np, o_ref, t_lane)
+        e_s = s_rel_err(S_dev[sl].cpu().numpy(), S_or)
+        errs.append((e_o, e_s))
+        if r % say_every == 0 or r == rounds - 1:
+            say("  round %d: m=%s o err %.2e S err %.2e" % (r, m[:4], e_o, e_s))
+    return errs
+
+
+def test_config1_chained_100_rounds():
+    """1 lane x 48 layers, T = 16, m ~ U{0..16}, 100 rounds carrying S."""
+    say("config 1")
+    errs = _chained(1, 100, gs.accepted_uniform, [0, 23, 47], 16)
+    assert max(max(e) for e in errs) <= TOL
+
+
+def test_config3_chained_256_rounds():
+    """12 lanes x 48 layers, T = 6, m ~ Binomial(6, 0.7), 256 rounds."""
+    say("config 3")
+    errs = _chained(3, 256, lambda t, key: gs.accepted_binomial(t, 0.7, key),
+                    [5], 6, say_every=32)
+    worst = max(max(e) for e in errs)
+    assert worst <= TOL
+    # the error does not drift upward over the chain (non-expansive rule)
+    first = max(max(e) for e in errs[:64])
+    last = max(max(e) for e in errs[-64:])
+    say("  first-64 worst %.2e  last-64 worst %.2e" % (first, last))
+    assert last <= 4 * first + 1e-6
