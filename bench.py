@@ -29,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+F32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published f32 vector peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 METRIC = "GDN verify+commit head-token updates/s & % HBM roofline (8 lanes, T=16)"
 
 NL, N, HV, HK, DK, DV, T = 48, 8, 32, 16, 128, 128, 16
@@ -50,6 +52,36 @@ def alg_bytes_commit(m_lane):
     s = HV * DK * DV * 4
     rec = HK * DK * 4 + HV * DV * 4 + HV * 4
     return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
+
+
+def alg_flops_verify(t_lane):
+    """Algorithmic flops of one verify call: per state element and token the
+    prediction (1 FMA = 2), the decayed rank-1 write (1 mul + 1 FMA = 3) and
+    the output (1 FMA = 2): 7 flops x d_k x d_v x h_v x T per lane-layer."""
+    return NL * sum(7 * DK * DV * HV * int(t) for t in t_lane)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gdn_window.hip", "gdn_step.h"):
+        with open(os.path.join(ROOT, "commit_gated_delta_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per launch from the committed counter record, or
+    None when the record is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    k = rec.get(kernel)
+    if not k or k.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(k["bytes_per_launch"])
 
 
 def cpu_baseline(rounds=3):
@@ -84,6 +116,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pool", type=int, default=4)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 256 MiB f32 copy kernel (y = x * 1) "
+                         "before the timed region, as the reference point "
+                         "for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU; --gpus %d is not supported.  The "
@@ -129,6 +165,13 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    if args.calibrate_copy:
+        cx = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        torch.mul(cx, 1.0, out=cy)
+        torch.cuda.synchronize()
+        del cx, cy
+
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -155,11 +198,11 @@ def main():
     gbs_v = bv / (np.mean(ms_v) * 1e-3) / 1e9
     gbs_c = np.mean(bc) / (np.mean(ms_c) * 1e-3) / 1e9
     gbs_path = (bv + np.mean(bc)) / (ms_per_step * 1e-3) / 1e9
-    dominant = "verify" if np.mean(ms_v) >= np.mean(ms_c) else "commit"
-    if dominant == "verify":
-        ach, per_launch, kms = gbs_v, bv, float(np.mean(ms_v))
-    else:
-        ach, per_launch, kms = gbs_c, float(np.mean(bc)), float(np.mean(ms_c))
+    fv = alg_flops_verify(t_lane)
+    ms_v_mean, ms_c_mean = float(np.mean(ms_v)), float(np.mean(ms_c))
+    # verify dominates the step; at T = 16 it is bound by f32 VALU issue
+    # (three FMAs per state element per token), not by HBM
+    tflops_v = fv / (ms_v_mean * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": value,
@@ -179,16 +222,19 @@ def main():
                    "n_lanes": N, "n_layers": NL, "h_v": HV, "h_k": HK,
                    "d_k": DK, "d_v": DV, "t": T},
         "hbm_roofline_frac_path": gbs_path / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "gdn_verify" if dominant ==
-                     "verify" else "gdn_commit",
-                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": per_launch,
-                     "avg_launch_ms": kms},
-        "verify_ms": float(np.mean(ms_v)),
-        "commit_ms": float(np.mean(ms_c)),
+        "roofline": {"bound": "alu", "kernel": "gdn_verify (verify_kernel)",
+                     "achieved": tflops_v, "peak": F32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops_v / F32_VECTOR_PEAK_TFLOPS,
+                     "traffic": measured_traffic("verify_kernel"),
+                     "alg_flops_per_launch": fv,
+                     "alg_bytes_per_launch": bv,
+                     "avg_launch_ms": ms_v_mean},
+        "verify_ms": ms_v_mean,
+        "commit_ms": ms_c_mean,
         "verify_alg_GBps": gbs_v,
         "commit_alg_GBps": gbs_c,
+        "commit_hbm_frac": gbs_c / HBM_PEAK_GBS,
+        "commit_traffic": measured_traffic("commit_kernel"),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
