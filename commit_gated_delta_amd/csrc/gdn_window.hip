@@ -56,6 +56,7 @@
 #include <utility>
 
 #include "gdn.h"
+#include "gdn_internal.h"
 #include "gdn_step.h"
 
 namespace gdn {
@@ -379,8 +380,12 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
 // ------------------------------------------------------------- host side
 static thread_local char g_last_error[256] = "";
 
+void set_error(const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+}
+
 static int fail(int status, const char* what) {
-  snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  set_error(what);
   return status;
 }
 

@@ -129,3 +129,52 @@ def test_commit_rejects_bad_arguments_on_host():
 def test_binding_checks_lane_count():
     with pytest.raises(ValueError):
         _verify(_dims(), [1, 1, 1])
+
+
+def test_prefill_workspace_bytes():
+    n = gdn.prefill_workspace_bytes(1, 32768, 32, 32, 128, 128)
+    # per (chunk, head): T and P as split bf16 (4 x 8 KiB) + row vectors
+    assert n >= 512 * 32 * (4 * 8192 + 64 * 16)
+    assert gdn.prefill_workspace_bytes(1, 100, 4, 3, 128, 128) == 0   # h_v % h_k
+    assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 64, 64) == 0     # d != 128
+    assert gdn.prefill_workspace_bytes(0, 100, 4, 4, 128, 128) == 0
+
+
+def _prefill(**over):
+    a = dict(n_seqs=1, L=256, hv=2, hk=1, dk=128, dv=128, interval=128,
+             q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),
+             g=_Fake(gdn.GDN_F32), Si=None, Sf=_Fake(gdn.GDN_F32),
+             o=_Fake(gdn.GDN_F32), ck=_Fake(gdn.GDN_F32), ws_bytes=1 << 30)
+
+    class _WS(_Fake):
+        def __init__(self, nbytes):
+            super().__init__(gdn.GDN_F32)
+            self.nb = nbytes
+
+        def numel(self):
+            return self.nb
+
+        def element_size(self):
+            return 1
+
+    a.update(over)
+    return gdn.prefill_chunked(a["n_seqs"], a["L"], a["hv"], a["hk"], a["dk"],
+                               a["dv"], a["q"], a["k"], a["v"], a["beta"],
+                               a["g"], a["Si"], a["Sf"], a["o"], a["ck"],
+                               _WS(a["ws_bytes"]),
+                               ckpt_interval=a["interval"], stream=0,
+                               raw_status=True)
+
+
+def test_prefill_rejects_bad_arguments_on_host():
+    assert _prefill(dk=64, dv=64) == gdn.GDN_EUNSUPPORTED
+    assert _prefill(hv=3, hk=2) == gdn.GDN_EINVAL
+    assert _prefill(L=0) == gdn.GDN_EINVAL
+    assert _prefill(interval=100) == gdn.GDN_EINVAL      # not a multiple of 64
+    assert _prefill(interval=0) == gdn.GDN_EINVAL
+    assert _prefill(q=_Fake(gdn.GDN_F32), k=_Fake(gdn.GDN_F32),
+                    v=_Fake(gdn.GDN_F32)) == gdn.GDN_EUNSUPPORTED
+    assert _prefill(o=None) == gdn.GDN_EINVAL
+    assert _prefill(ws_bytes=1024) == gdn.GDN_EWORKSPACE
+    assert _prefill(q=_Fake(addr=(1 << 20) + 8)) == gdn.GDN_EINVAL
+    assert b"prefill" in gdn.lib.gdn_last_error()

@@ -1,0 +1,176 @@
+"""GPU parity of gdn_prefill_chunked against the fp64 oracle; checkpoint
+resume is bitwise; short prefills agree with verify.
+
+Every call goes through the C ABI.  Tolerance: 2e-4 block-relative (per
+head: max |x - ref| / max |ref| over the head's tokens and columns, or over
+its state entries).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+import oracle
+from tests.gpu_util import TOL, block_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import commit_gated_delta_amd as gdn  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_prefill(p, n_seqs_inputs, S_init=None, ckpt_interval=8192, scale=1.0,
+                l2norm=True):
+    """p: list of PrefillInputs (one per sequence, equal shapes)."""
+    n_seqs = len(n_seqs_inputs)
+    L, Hv, Hk = p.seq_len, p.h_v, p.h_k
+    stack = lambda name: np.stack([getattr(x, name) for x in n_seqs_inputs])
+    q, k, v = (to_dev(stack(nm), torch) for nm in ("q", "k", "v"))
+    beta, g = to_dev(stack("beta"), torch), to_dev(stack("g"), torch)
+    Si = None if S_init is None else to_dev(np.ascontiguousarray(S_init), torch)
+    Sf = torch.empty((n_seqs, Hv, 128, 128), device="cuda")
+    o = torch.full((n_seqs, L, Hv, 128), float("nan"), device="cuda")
+    n_ck = L // ckpt_interval
+    ck = torch.full((n_seqs, max(n_ck, 1), Hv, 128, 128), float("nan"),
+                    device="cuda") if n_ck > 0 else None
+    ws = torch.empty(gdn.prefill_workspace_bytes(n_seqs, L, Hv, Hk, 128, 128),
+                     dtype=torch.uint8, device="cuda")
+    gdn.prefill_chunked(n_seqs, L, Hv, Hk, 128, 128, q, k, v, beta, g, Si, Sf,
+                        o, ck, ws, ckpt_interval=ckpt_interval, scale=scale,
+                        l2norm=l2norm)
+    torch.cuda.synchronize()
+    return (o.cpu().numpy(), None if ck is None else ck.cpu().numpy(),
+            Sf.cpu().numpy())
+
+
+def oracle_prefill(p, S_init, ckpt_interval, scale=1.0, l2norm=True,
+                   heads=None):
+    q, k, v, b, g = p.as_f64()
+    if heads is not None:   # heads are independent: run only some of them
+        grp = p.h_v // p.h_k
+        kidx = [h // grp for h in heads]
+        q, k = q[:, kidx], k[:, kidx]
+        v, b, g = v[:, heads], b[:, heads], g[:, heads]
+        S_init = None if S_init is None else S_init[heads]
+    return oracle.prefill(q, k, v, b, g, S_init, ckpt_interval=ckpt_interval,
+                          scale=scale, l2norm=l2norm)
+
+
+def o_err(o, ref):   # o: [L, H, dv] -> per head
+    return block_rel_err(o, ref, 1, move=(1, 0, 2))
+
+
+def s_err(S, ref):   # S: [..., H, dk, dv] -> per head
+    S = np.asarray(S).reshape(-1, 128, 128)
+    ref = np.asarray(ref).reshape(-1, 128, 128)
+    return block_rel_err(S, ref, 1)
+
+
+CASES = [
+    # (name, L, Hv, Hk, n_seqs, init, interval, scale, l2norm)
+    ("one_chunk", 64, 2, 1, 1, False, 64, 1.0, True),
+    ("tail_and_init", 200, 2, 1, 1, True, 64, 1.0, True),
+    ("two_seqs_group2", 333, 4, 2, 2, True, 128, 0.5, True),
+    ("eq_heads_no_init", 512, 4, 4, 1, False, 128, 1.0, True),
+    ("short_tail", 70, 2, 2, 1, True, 64, 1.0, True),
+    ("tiny", 5, 2, 1, 1, True, 64, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_parity(case):
+    name, L, Hv, Hk, n_seqs, init, interval, scale, l2norm = case
+    say("case", name)
+    ins = [gs.prefill_inputs(L, Hv, Hk, 128, 128, (40, hash_case(name), s))
+           for s in range(n_seqs)]
+    S_init = None
+    if init:
+        S_init = np.stack([gs.prefill_state(Hv, 128, 128, (40, s))
+                           for s in range(n_seqs)])
+    o, ck, Sf = run_prefill(ins[0], ins, S_init, interval, scale, l2norm)
+    for s in range(n_seqs):
+        assert np.all(np.isfinite(o[s])), "unwritten output rows"
+        o_ref, ck_ref, Sf_ref = oracle_prefill(
+            ins[s], None if S_init is None else S_init[s].astype(np.float64),
+            interval, scale, l2norm)
+        e_o, e_s = o_err(o[s], o_ref), s_err(Sf[s], Sf_ref)
+        say("  seq %d: o err %.2e  S err %.2e" % (s, e_o, e_s))
+        assert e_o <= TOL and e_s <= TOL
+        n_ck = L // interval
+        for j in range(n_ck):
+            assert s_err(ck[s, j], ck_ref[j]) <= TOL
+        if n_ck and L % interval == 0:
+            assert np.array_equal(ck[s, n_ck - 1], Sf[s])
+
+
+def hash_case(name):
+    import zlib
+    return zlib.crc32(name.encode()) % 10000
+
+
+def test_resume_from_checkpoint_is_bitwise():
+    L, Hv, Hk, interval = 640, 4, 2, 128
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (41,))
+    S0 = gs.prefill_state(Hv, 128, 128, (41,))[None]
+    o, ck, Sf = run_prefill(p, [p], S0, interval)
+    for j in (0, 2):
+        t = interval * (j + 1)
+        tail = gs.PrefillInputs(L - t, Hv, Hk, 128, 128, True, p.q[t:], p.k[t:],
+                                p.v[t:], p.beta[t:], p.g[t:])
+        o2, _, Sf2 = run_prefill(tail, [tail], ck[:, j], interval)
+        assert np.array_equal(Sf2, Sf), j
+        assert np.array_equal(o2[0], o[0, t:]), j
+
+
+def test_short_prefill_agrees_with_verify():
+    """A prefill of T <= 16 tokens and a verify window over the same tokens
+    run different kernels; both match the oracle, and each other."""
+    T, Hv, Hk = 13, 4, 2
+    p = gs.prefill_inputs(T, Hv, Hk, 128, 128, (42,), g_mean=0.0)
+    S0 = gs.prefill_state(Hv, 128, 128, (42,))
+    o_p, _, Sf_p = run_prefill(p, [p], S0[None], 64)
+    dims = gdn.Dims.of(1, 1, Hv, Hk, 128, 128, T)
+    q = to_dev(p.q[None, None], torch)
+    k = to_dev(p.k[None, None], torch)
+    v = to_dev(p.v[None, None], torch)
+    b = to_dev(p.beta[None, None], torch)
+    g = to_dev(p.g[None, None], torch)
+    S = to_dev(S0[None, None], torch)
+    o = torch.empty((1, 1, T, Hv, 128), device="cuda")
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device="cuda")
+    gdn.verify(dims, [T], q, k, v, b, g, S, o, rec)
+    gdn.commit(dims, [T], [T], rec, S)
+    o_v, S_v = o.cpu().numpy()[0, 0], S.cpu().numpy()[0, 0]
+    assert o_err(o_p[0], o_v) <= TOL
+    assert s_err(Sf_p[0], S_v) <= TOL
+
+
+@pytest.mark.parametrize("hk", [32, 16])
+def test_prefill_32k_tokens_32_heads(hk):
+    """L = 32,768, 32 value heads, d = 128, g = -softplus(N(-2, 1)), zero
+    initial state, checkpoints every 8,192 tokens.  The oracle runs a sample
+    of heads (heads are independent); every checkpoint of those heads and
+    S_final are compared, and the output of all their tokens."""
+    L, Hv = 32768, 32
+    say("prefill 32k, h_k =", hk, ": generating")
+    p = gs.prefill_inputs(L, Hv, hk, 128, 128, (4, hk))
+    o, ck, Sf = run_prefill(p, [p], None, 8192)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    assert np.array_equal(ck[0, 3], Sf[0])
+    heads = [0, 13, 31]
+    say("  oracle on heads", heads)
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, None, 8192, heads=heads)
+    e_o = o_err(o[0][:, heads], o_ref)
+    e_s = s_err(Sf[0][heads], Sf_ref)
+    e_c = max(s_err(ck[0, j][heads], ck_ref[j]) for j in range(4))
+    say("  o err %.2e  S err %.2e  ckpt err %.2e" % (e_o, e_s, e_c))
+    assert e_o <= TOL and e_s <= TOL and e_c <= TOL
