@@ -84,6 +84,76 @@ def measured_traffic(kernel):
     return float(k["bytes_per_launch"])
 
 
+PF_L, PF_H, PF_C = 32768, 32, 64
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def prefill_flops(L=PF_L, H=PF_H, C=PF_C, D=128):
+    """(useful, issued) MFMA flops of one chunked prefill.  Useful: the dense
+    contractions of the chunk form per (chunk, head) -- K K^T, Q K^T, T X,
+    P V_new (2 C^2 D each) and K H, Q H, K^T V' (2 C D^2 each).  Issued adds
+    the split-bf16 passes: 2 for K H, Q H, K^T V', 3 for T X and P V_new of
+    which a quarter is skipped by triangularity."""
+    n = ((L + C - 1) // C) * H
+    a, b = 2 * C * C * D, 2 * C * D * D
+    useful = n * (4 * a + 3 * b)
+    issued = n * (2 * a + 2 * 2 * b + 2 * 3 * 0.75 * a + 2 * b)
+    return useful, issued
+
+
+def bench_prefill(reps=10, warmup=2, h_k=PF_H):
+    """Chunked prefill of one 32,768-token sequence, 32 value heads (h_k key
+    heads), d = 128, bf16 q/k/v, zero initial state, checkpoints every
+    8,192 tokens.  Event-timed on the stream the kernels run on."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    p = gs.prefill_inputs(PF_L, PF_H, h_k, 128, 128, (4, h_k))
+
+    def d16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = d16(p.q[None]), d16(p.k[None]), d16(p.v[None])
+    beta = torch.from_numpy(p.beta[None]).to(dev)
+    g = torch.from_numpy(p.g[None]).to(dev)
+    Sf = torch.empty((1, PF_H, 128, 128), device=dev)
+    o = torch.empty((1, PF_L, PF_H, 128), device=dev)
+    ck = torch.empty((1, PF_L // 8192, PF_H, 128, 128), device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(1, PF_L, PF_H, h_k, 128, 128),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        gdn.prefill_chunked(1, PF_L, PF_H, h_k, 128, 128, q, k, v, beta, g,
+                            None, Sf, o, ck, ws, stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    useful, issued = prefill_flops()
+    io_bytes = (PF_L * h_k * 128 * 2 * 2 + PF_L * PF_H * 128 * 2 +
+                PF_L * PF_H * 4 * 2 + PF_L * PF_H * 128 * 4 +
+                (PF_L // 8192 + 1) * PF_H * 128 * 128 * 4)
+    return {"workload": "1 sequence x 32768 tokens, 32 value / %d key heads, "
+                        "d=128, chunk 64, checkpoints every 8192" % h_k,
+            "ms": ms, "head_tokens_per_s": PF_L * PF_H / (ms * 1e-3),
+            "useful_tflops": useful / (ms * 1e-3) / 1e12,
+            "issued_mfma_tflops": issued / (ms * 1e-3) / 1e12,
+            "mfma_frac_issued": issued / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "mfma_frac_useful": useful / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "io_GBps": io_bytes / (ms * 1e-3) / 1e9,
+            "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
+
+
 def cpu_baseline(rounds=3):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: `rounds` chained rounds (verify + commit) of the full
@@ -116,6 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pool", type=int, default=4)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB f32 copy kernel (y = x * 1) "
                          "before the timed region, as the reference point "
@@ -134,6 +207,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        cx = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        torch.mul(cx, 1.0, out=cy)
+        torch.cuda.synchronize()
+        del cx, cy
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(reps=args.steps,
+                                                   warmup=args.warmup)}),
+              flush=True)
+        return
     shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
     dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
     t_lane = np.full(N, T, dtype=np.int32)
@@ -164,13 +248,6 @@ def main():
         gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-
-    if args.calibrate_copy:
-        cx = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        cy = torch.empty_like(cx)
-        torch.mul(cx, 1.0, out=cy)
-        torch.cuda.synchronize()
-        del cx, cy
 
     for s in range(args.warmup):
         step(s)
@@ -236,6 +313,8 @@ def main():
         "commit_hbm_frac": gbs_c / HBM_PEAK_GBS,
         "commit_traffic": measured_traffic("commit_kernel"),
     }
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

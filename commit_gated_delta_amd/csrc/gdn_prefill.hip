@@ -69,28 +69,36 @@ struct PDims {
   int l2norm;
 };
 
-// Workspace per (sequence, chunk, value head).
+// Workspace per (sequence, chunk, value head).  T and P are stored as MFMA
+// A-operand fragments in the order p2 reads them: for wave w, piece x (T hi,
+// T lo for k-step 0, the same for k-step 1, then P likewise) and lane l, 16
+// bytes holding row 16w + l%16, columns 32*ks + 8*(l/16) + 0..7, at
+// ((w*8 + x)*64 + l)*16 -- one load instruction of a wave reads 1 KiB of
+// consecutive bytes.
 struct WsLayout {
-  static constexpr size_t kMat = kC * kC * sizeof(u16);  // one bf16 64x64
-  static constexpr size_t kThi = 0, kTlo = kMat, kPhi = 2 * kMat,
-                          kPlo = 3 * kMat;
-  static constexpr size_t kVec = 4 * kMat;  // float [64][4]: sb sk so sd
-  static constexpr size_t kGc = kVec + kC * 4 * sizeof(float);  // float
+  static constexpr size_t kFrag = 4 * 64 * 8 * 16;               // 32 KiB
+  static constexpr size_t kVec = kFrag;      // float [64][4]: sb sk so sd
+  static constexpr size_t kGc = kVec + kC * 4 * sizeof(float);   // float
   static constexpr size_t kBytes = (kGc + sizeof(float) + 255) & ~size_t(255);
 };
 
-__device__ __forceinline__ u16 bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two f32 values as packed bf16 pairs: hi = bf16(x) and lo = bf16(x - hi)
+// (round to nearest even, v_cvt_pk_bf16_f32); x = hi + lo + ~2^-17 |x|.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi,
+                                       uint32_t& lo) {
+  const f32x2 x = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const f32x2 xh = {__uint_as_float(hi << 16),
+                    __uint_as_float(hi & 0xffff0000u)};
+  const f32x2 r = {x[0] - xh[0], x[1] - xh[1]};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
+
 __device__ __forceinline__ float bf16_f(u16 b) {
   return __uint_as_float((uint32_t)b << 16);
-}
-// x = hi + lo (+ ~2^-17 |x|)
-__device__ __forceinline__ void split(float x, u16& hi, u16& lo) {
-  hi = bf16_rne(x);
-  lo = bf16_rne(x - bf16_f(hi));
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b,
@@ -134,26 +142,24 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int l = tid % 64;
 
-  // ---- load K, Q rows (bf16) to LDS; invalid tail rows are zero
+  // ---- load K, Q rows (bf16) to LDS.  Rows past the end of the sequence
+  // are read from the last valid row (no branch around the loads): they only
+  // meet beta = 0, or feed output rows that are not stored.
+  const int last = nv - 1;
   for (int it = 0; it < 4; ++it) {
     const int idx = it * kThreads + tid;  // 1024 pieces of 8 bf16
     const int row = idx / 16, col = (idx % 16) * 8;
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-    if (row < nv) {
-      const size_t off = (((size_t)s * d.L + t0 + row) * d.Hk + kh) * kD + col;
-      kv = *reinterpret_cast<const uint4*>(k + off);
-      qv = *reinterpret_cast<const uint4*>(q + off);
-    }
-    *reinterpret_cast<uint4*>(&Ks[row * KS + col]) = kv;
-    *reinterpret_cast<uint4*>(&Qs[row * KS + col]) = qv;
+    const size_t off =
+        (((size_t)s * d.L + t0 + min(row, last)) * d.Hk + kh) * kD + col;
+    *reinterpret_cast<uint4*>(&Ks[row * KS + col]) =
+        *reinterpret_cast<const uint4*>(k + off);
+    *reinterpret_cast<uint4*>(&Qs[row * KS + col]) =
+        *reinterpret_cast<const uint4*>(q + off);
   }
   if (tid < kC) {
-    float bb = 0.f, gg = 0.f;
-    if (tid < nv) {
-      const size_t gi = ((size_t)s * d.L + t0 + tid) * d.Hv + h;
-      bb = beta[gi];
-      gg = g[gi];
-    }
+    const size_t gi = ((size_t)s * d.L + t0 + min(tid, last)) * d.Hv + h;
+    const float bb = (tid < nv) ? beta[gi] : 0.f;
+    const float gg = (tid < nv) ? g[gi] : 0.f;
     b_s[tid] = bb;
     // inclusive prefix sum of g over the chunk (wave 0), fixed order
     float x = gg;
@@ -288,23 +294,25 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     __syncthreads();
   }
 
-  // ---- write T, P (split bf16) and the row vectors
+  // ---- write T, P (split bf16, fragment order) and the row vectors
   uint8_t* wsb = ws + ((size_t)bid) * WsLayout::kBytes;
-  u16* Thi = reinterpret_cast<u16*>(wsb + WsLayout::kThi);
-  u16* Tlo = reinterpret_cast<u16*>(wsb + WsLayout::kTlo);
-  u16* Phi = reinterpret_cast<u16*>(wsb + WsLayout::kPhi);
-  u16* Plo = reinterpret_cast<u16*>(wsb + WsLayout::kPlo);
-  for (int idx = tid; idx < kC * kC / 2; idx += kThreads) {
-    const int i = (2 * idx) / kC, j = (2 * idx) % kC;
-    u16 h0, l0, h1, l1;
-    split(Ts[i * FS + j], h0, l0);
-    split(Ts[i * FS + j + 1], h1, l1);
-    reinterpret_cast<uint32_t*>(Thi)[idx] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    reinterpret_cast<uint32_t*>(Tlo)[idx] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    split(Ps[i * FS + j], h0, l0);
-    split(Ps[i * FS + j + 1], h1, l1);
-    reinterpret_cast<uint32_t*>(Phi)[idx] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    reinterpret_cast<uint32_t*>(Plo)[idx] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  {
+    const int i = 16 * w + l % 16;
+    uint4* dst = reinterpret_cast<uint4*>(wsb) + (size_t)w * 8 * 64 + l;
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      const float* M = mat ? Ps : Ts;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int j0 = 32 * ks + 8 * (l / 16);
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          split2(M[i * FS + j0 + 2 * e], M[i * FS + j0 + 2 * e + 1], hi[e], lo[e]);
+        dst[(mat * 4 + ks * 2 + 0) * 64] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        dst[(mat * 4 + ks * 2 + 1) * 64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+    }
   }
   if (tid < kC) {
     const int i = tid;
@@ -323,13 +331,16 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
 // ------------------------------------------------------------------ p2
 // Per-chunk operands that a lane prefetches one chunk ahead.
 struct Pre {
-  uint4 q[4];        // A fragments of Q rows (4 k-steps)
-  uint4 thi[2], tlo[2], phi[2], plo[2];  // A fragments of T and P (2 k-steps)
-  u16 v[4];          // V[row 4*(l/16)+e of the wave's block][tile col]
-  float4 vec[4];     // sb sk so sd of those rows
+  uint4 q[4];     // A fragments of the lane's Q row (4 k-steps)
+  uint4 tp[8];    // A fragments of T and P (WsLayout order)
+  uint32_t v[4];  // bf16 V[row 16w + 4*(l/16) + e][column], in the low half
+  float4 vec[4];  // sb sk so sd of those rows
   float gc;
-  uint4 kr[4];       // raw K pieces for the LDS copy (row-major + transposed)
 };
+
+__device__ __forceinline__ uint2 pack4(const uint32_t (&x)[4], int e0) {
+  return make_uint2(x[e0], x[e0 + 1]);
+}
 
 __global__ __launch_bounds__(kThreads) void p2_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k,
@@ -339,12 +350,19 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
   constexpr int KS = kD + 8;   // Kr row stride (bf16)
   constexpr int TS = kC + 8;   // Kt / column-major tile row stride (bf16)
   constexpr int HS = kD + 8;   // Hb row stride (bf16)
-  __shared__ __attribute__((aligned(16))) u16 Kr[kC * KS];       // K rows
-  __shared__ __attribute__((aligned(16))) u16 Kt[kD * TS];       // K^T
-  __shared__ __attribute__((aligned(16))) u16 Hb[2][kTile * HS]; // H hi/lo [n][dk]
-  __shared__ __attribute__((aligned(16))) u16 Xb[2][kTile * TS]; // X hi/lo [n][j]
-  __shared__ __attribute__((aligned(16))) u16 Vb[2][kTile * TS]; // V_new hi/lo
-  __shared__ __attribute__((aligned(16))) u16 Db[2][kTile * TS]; // sd*V_new hi/lo
+  // double buffers (chunk parity) for the K copies and the state operand
+  __shared__ __attribute__((aligned(16))) u16 Kr[2][kC * KS];      // K rows
+  __shared__ __attribute__((aligned(16))) u16 Kt[2][kD * TS];      // K^T
+  __shared__ __attribute__((aligned(16))) u16 Hb[2][2][kTile * HS];// H hi/lo [n][dk]
+  __shared__ __attribute__((aligned(16))) u16 Xb[2][kTile * TS];   // X hi/lo [n][j]
+  __shared__ __attribute__((aligned(16))) u16 Vb[2][kTile * TS];   // V_new hi/lo
+  __shared__ __attribute__((aligned(16))) u16 Db[2][kTile * TS];   // sd V_new hi/lo
+  // Kt holds K^T with the 8-entry groups of each row XOR-swizzled by
+  // (dk / 8) % 8, so that the transposing stores of one wave spread over the
+  // LDS banks while every 8-entry group stays 16-byte aligned for the reads.
+  auto kt_at = [&](int dk, int j) {
+    return dk * TS + 8 * ((j >> 3) ^ ((dk >> 3) & 7)) + (j & 7);
+  };
 
   // block -> (sequence, head, tile); the tiles of a head share one XCD
   const int nb = gridDim.x;
@@ -360,6 +378,16 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
   const int n = l % 16;       // column inside the tile (C/D/B layouts)
   const int q4 = l / 16;      // 0..3
   const int col = kTile * tile + n;
+  const int nch = d.n_chunks;
+
+  // per-sequence bases; element offsets below fit in 32 bits (host check)
+  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
+  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const uint8_t* __restrict__ wss =
+      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+  const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
 
   // state fragments: wave w holds dk rows 32w + 16*mt + 4*q4 + e, column n
   f32x4 H[2];
@@ -371,110 +399,121 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
       H[mt][e] = S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
     }
 
-  auto write_H = [&]() {
+  auto write_H = [&](int buf) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      u16 hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split(H[mt][e], hi[e], lo[e]);
+      uint32_t hi[2], lo[2];
+      split2(H[mt][0], H[mt][1], hi[0], lo[0]);
+      split2(H[mt][2], H[mt][3], hi[1], lo[1]);
       const int r = 32 * w + 16 * mt + 4 * q4;
-      *reinterpret_cast<uint2*>(&Hb[0][n * HS + r]) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2*>(&Hb[1][n * HS + r]) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      *reinterpret_cast<uint2*>(&Hb[buf][0][n * HS + r]) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(&Hb[buf][1][n * HS + r]) = make_uint2(lo[0], lo[1]);
     }
   };
 
+  // Loads are unconditional: rows past the end of the sequence are read from
+  // the last valid row instead.  Their values never reach a result: P1 gives
+  // such rows beta = 0, so X, V_new and their state contributions are 0, and
+  // their output rows are not stored.  (A load under a branch would make the
+  // compiler wait for it at the end of the branch, which defeats the
+  // one-chunk-ahead prefetch.)
   auto prefetch = [&](int c, Pre& p) {
     const int t0 = c * kC;
-    const int nv = min(kC, d.L - t0);
-    const size_t wsi = (((size_t)s * d.n_chunks + c) * d.Hv + h) * WsLayout::kBytes;
-    const uint8_t* wb = ws + wsi;
-    const int arow = 16 * w + n;  // A-fragment row of this lane
+    const int last = min(kC, d.L - t0) - 1;
+    const uint4* wf = reinterpret_cast<const uint4*>(wss + (size_t)c * ws_chunk) +
+                      w * 8 * 64 + l;
+    const uint32_t qoff =
+        ((uint32_t)(t0 + min(16 * w + n, last)) * d.Hk + kh) * kD + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      p.q[ks] = make_uint4(0, 0, 0, 0);
-      if (arow < nv)
-        p.q[ks] = *reinterpret_cast<const uint4*>(
-            q + (((size_t)s * d.L + t0 + arow) * d.Hk + kh) * kD + 32 * ks + 8 * q4);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      p.q[ks] = *reinterpret_cast<const uint4*>(qs + qoff + 32 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const size_t off = (size_t)arow * kC + 32 * ks + 8 * q4;
-      p.thi[ks] = *reinterpret_cast<const uint4*>(wb + WsLayout::kThi + 2 * off);
-      p.tlo[ks] = *reinterpret_cast<const uint4*>(wb + WsLayout::kTlo + 2 * off);
-      p.phi[ks] = *reinterpret_cast<const uint4*>(wb + WsLayout::kPhi + 2 * off);
-      p.plo[ks] = *reinterpret_cast<const uint4*>(wb + WsLayout::kPlo + 2 * off);
-    }
+    for (int x = 0; x < 8; ++x) p.tp[x] = wf[x * 64];
+    const float4* vec = reinterpret_cast<const float4*>(
+        wss + (size_t)c * ws_chunk + WsLayout::kVec);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + 4 * q4 + e;
-      p.v[e] = (r < nv) ? v[(((size_t)s * d.L + t0 + r) * d.Hv + h) * kD + col] : (u16)0;
-      p.vec[e] = reinterpret_cast<const float4*>(wb + WsLayout::kVec)[r];
+      p.v[e] = vs[((uint32_t)(t0 + min(r, last)) * d.Hv + h) * kD + col];
+      p.vec[e] = vec[r];
     }
-    p.gc = *reinterpret_cast<const float*>(wb + WsLayout::kGc);
+    p.gc = *reinterpret_cast<const float*>(wss + (size_t)c * ws_chunk + WsLayout::kGc);
+  };
+
+  // raw K pieces of one chunk, for the row-major and transposed LDS copies
+  uint4 kr[4];
+  auto load_K = [&](int c) {
+    const int t0 = c * kC;
+    const int last = min(kC, d.L - t0) - 1;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = it * kThreads + tid;
       const int row = idx / 16, cc = (idx % 16) * 8;
-      p.kr[it] = make_uint4(0, 0, 0, 0);
-      if (row < nv)
-        p.kr[it] = *reinterpret_cast<const uint4*>(
-            k + (((size_t)s * d.L + t0 + row) * d.Hk + kh) * kD + cc);
+      kr[it] = *reinterpret_cast<const uint4*>(
+          kseq + ((uint32_t)(t0 + min(row, last)) * d.Hk + kh) * kD + cc);
     }
   };
 
-  auto store_K = [&](const Pre& p) {
+  auto stage_K = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = it * kThreads + tid;
       const int row = idx / 16, cc = (idx % 16) * 8;
-      *reinterpret_cast<uint4*>(&Kr[row * KS + cc]) = p.kr[it];
-      const u16* e8 = reinterpret_cast<const u16*>(&p.kr[it]);
+      *reinterpret_cast<uint4*>(&Kr[buf][row * KS + cc]) = kr[it];
+      const u16* e8 = reinterpret_cast<const u16*>(&kr[it]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Kt[(cc + e) * TS + row] = e8[e];
+      for (int e = 0; e < 8; ++e) Kt[buf][kt_at(cc + e, row)] = e8[e];
     }
   };
 
-  Pre cur, nxt;
-  prefetch(0, cur);
-  store_K(cur);
-  write_H();
-  __syncthreads();
+  // Every global load is issued about one chunk before its data is used: at
+  // the top of chunk c one explicit wait covers the operands of chunk c
+  // (issued during chunk c-1) and the K rows of chunk c+1 (issued at the top
+  // of chunk c-1); nothing later in the chunk reads a register that is still
+  // being loaded.
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
-  for (int c = 0; c < d.n_chunks; ++c) {
+  // one chunk: uses `cur`, prefetches chunk c+1 into `nxt`
+  auto chunk = [&](int c, const Pre& cur, Pre& nxt) {
+    const int buf = c & 1;
     const int t0 = c * kC;
     const int nv = min(kC, d.L - t0);
-    if (c + 1 < d.n_chunks) prefetch(c + 1, nxt);
+    wait_loads();
+    // K of chunk c+1 into the other buffers (last read in chunk c-1, before
+    // the barrier that ended it); visible to chunk c+1 after this chunk's
+    // barriers
+    if (c + 1 < nch) stage_K(buf ^ 1);
+    if (c + 2 < nch) load_K(c + 2);
 
     // ---- K H and Q H for rows 16w..16w+15 (2 passes: H hi, H lo)
     f32x4 KH = {0.f, 0.f, 0.f, 0.f}, QH = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kk = 32 * ks + 8 * q4;
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Kr[(16 * w + n) * KS + kk]));
+      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Kr[buf][(16 * w + n) * KS + kk]));
       const bf16x8 aq = as_bf16x8(cur.q[ks]);
-      const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[0][n * HS + kk]));
-      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[1][n * HS + kk]));
+      const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[buf][0][n * HS + kk]));
+      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[buf][1][n * HS + kk]));
       KH = mfma(ak, bh, KH);
-      KH = mfma(ak, bl, KH);
       QH = mfma(aq, bh, QH);
+      KH = mfma(ak, bl, KH);
       QH = mfma(aq, bl, QH);
     }
+    // operands of chunk c+1 (issued while the MFMAs above run)
+    if (c + 1 < nch) prefetch(c + 1, nxt);
 
     // ---- X = sb V - sk (K H), to LDS as split bf16 (column-major)
     {
-      u16 hi[4], lo[4];
+      float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = cur.vec[e].x * bf16_f(cur.v[e]) - cur.vec[e].y * KH[e];
-        split(x, hi[e], lo[e]);
-      }
+      for (int e = 0; e < 4; ++e)
+        x[e] = cur.vec[e].x * __uint_as_float(cur.v[e] << 16) - cur.vec[e].y * KH[e];
+      uint32_t hi[2], lo[2];
+      split2(x[0], x[1], hi[0], lo[0]);
+      split2(x[2], x[3], hi[1], lo[1]);
       const int r = 16 * w + 4 * q4;
-      *reinterpret_cast<uint2*>(&Xb[0][n * TS + r]) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2*>(&Xb[1][n * TS + r]) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      *reinterpret_cast<uint2*>(&Xb[0][n * TS + r]) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(&Xb[1][n * TS + r]) = make_uint2(lo[0], lo[1]);
     }
     __syncthreads();
 
@@ -487,27 +526,22 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
       const int kk = 32 * ks + 8 * q4;
       const bf16x8 xh = as_bf16x8(*reinterpret_cast<const uint4*>(&Xb[0][n * TS + kk]));
       const bf16x8 xl = as_bf16x8(*reinterpret_cast<const uint4*>(&Xb[1][n * TS + kk]));
-      const bf16x8 th = as_bf16x8(cur.thi[ks]), tl = as_bf16x8(cur.tlo[ks]);
+      const bf16x8 th = as_bf16x8(cur.tp[2 * ks]), tl = as_bf16x8(cur.tp[2 * ks + 1]);
       VN = mfma(th, xh, VN);
       VN = mfma(th, xl, VN);
       VN = mfma(tl, xh, VN);
     }
     {
-      u16 hi[4], lo[4], dh[4], dl[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        split(VN[e], hi[e], lo[e]);
-        split(cur.vec[e].w * VN[e], dh[e], dl[e]);
-      }
+      uint32_t hi[2], lo[2], dh[2], dl[2];
+      split2(VN[0], VN[1], hi[0], lo[0]);
+      split2(VN[2], VN[3], hi[1], lo[1]);
+      split2(cur.vec[0].w * VN[0], cur.vec[1].w * VN[1], dh[0], dl[0]);
+      split2(cur.vec[2].w * VN[2], cur.vec[3].w * VN[3], dh[1], dl[1]);
       const int r = 16 * w + 4 * q4;
-      *reinterpret_cast<uint2*>(&Vb[0][n * TS + r]) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2*>(&Vb[1][n * TS + r]) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-      *reinterpret_cast<uint2*>(&Db[0][n * TS + r]) =
-          make_uint2(dh[0] | ((uint32_t)dh[1] << 16), dh[2] | ((uint32_t)dh[3] << 16));
-      *reinterpret_cast<uint2*>(&Db[1][n * TS + r]) =
-          make_uint2(dl[0] | ((uint32_t)dl[1] << 16), dl[2] | ((uint32_t)dl[3] << 16));
+      *reinterpret_cast<uint2*>(&Vb[0][n * TS + r]) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(&Vb[1][n * TS + r]) = make_uint2(lo[0], lo[1]);
+      *reinterpret_cast<uint2*>(&Db[0][n * TS + r]) = make_uint2(dh[0], dh[1]);
+      *reinterpret_cast<uint2*>(&Db[1][n * TS + r]) = make_uint2(dl[0], dl[1]);
     }
     __syncthreads();
 
@@ -522,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
         const int kk = 32 * ks + 8 * q4;
         const bf16x8 vh = as_bf16x8(*reinterpret_cast<const uint4*>(&Vb[0][n * TS + kk]));
         const bf16x8 vl = as_bf16x8(*reinterpret_cast<const uint4*>(&Vb[1][n * TS + kk]));
-        const bf16x8 ph = as_bf16x8(cur.phi[ks]), pl = as_bf16x8(cur.plo[ks]);
+        const bf16x8 ph = as_bf16x8(cur.tp[4 + 2 * ks]), pl = as_bf16x8(cur.tp[5 + 2 * ks]);
         O = mfma(ph, vh, O);
         O = mfma(ph, vl, O);
         O = mfma(pl, vh, O);
@@ -530,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + 4 * q4 + e;
-        if (r < nv) o[(((size_t)s * d.L + t0 + r) * d.Hv + h) * kD + col] = O[e];
+        if (r < nv) os[((uint32_t)(t0 + r) * d.Hv + h) * kD + col] = O[e];
       }
     }
 
@@ -544,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int kk = 32 * ks + 8 * q4;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[arow * TS + kk]));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[buf][kt_at(arow, kk)]));
         const bf16x8 dh = as_bf16x8(*reinterpret_cast<const uint4*>(&Db[0][n * TS + kk]));
         const bf16x8 dl = as_bf16x8(*reinterpret_cast<const uint4*>(&Db[1][n * TS + kk]));
         acc = mfma(a, dh, acc);
@@ -566,13 +600,23 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
         }
     }
 
-    __syncthreads();  // every wave is done with Kr, Kt, Hb, Vb, Db of chunk c
-    if (c + 1 < d.n_chunks) {
-      write_H();
-      store_K(nxt);
-      cur = nxt;
-    }
+    // the state operand of chunk c+1 goes to the other buffer (last read in
+    // chunk c-1)
+    if (c + 1 < nch) write_H(buf ^ 1);
     __syncthreads();
+  };
+
+  Pre A, B;
+  load_K(0);
+  wait_loads();
+  stage_K(0);
+  prefetch(0, A);
+  if (nch > 1) load_K(1);
+  write_H(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, A, B);
+    if (c + 1 < nch) chunk(c + 1, B, A);
   }
 
 #pragma unroll
@@ -614,6 +658,8 @@ static int check_sizes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t Hk,
   if (dk != kD || dv != kD) {
     return fail(GDN_EUNSUPPORTED, "prefill: d_k = d_v = 128 only");
   }
+  if ((double)L * Hv * kD >= 2147483648.0 || (double)L * Hk * kD >= 2147483648.0)
+    return fail(GDN_EUNSUPPORTED, "prefill: seq_len x heads x 128 must stay below 2^31");
   const double blocks = (double)n_seqs * ((L + kC - 1) / kC) * Hv;
   const double elems = (double)n_seqs * L * Hv * kD;
   if (blocks > (double)INT_MAX || elems > 4.0e15) {
