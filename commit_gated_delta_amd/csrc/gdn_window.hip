@@ -83,7 +83,7 @@ struct CommitTable {
 
 // ------------------------------------------------------------- records
 struct RecLayout {
-  size_t k, u, alpha, total;
+  size_t k, u, scale, total;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -93,8 +93,8 @@ static RecLayout rec_layout(const gdn_dims& d) {
   const size_t ntok = (size_t)d.n_layers * d.n_lanes * d.t_max;
   r.k = 0;
   r.u = align256(ntok * d.h_k * d.d_k * sizeof(float));
-  r.alpha = r.u + align256(ntok * d.h_v * d.d_v * sizeof(float));
-  r.total = r.alpha + align256(ntok * d.h_v * sizeof(float));
+  r.scale = r.u + align256(ntok * d.h_v * d.d_v * sizeof(float));
+  r.total = r.scale + align256(ntok * d.h_v * sizeof(float2));
   return r;
 }
 
@@ -160,29 +160,24 @@ struct RowWords {
   }
 };
 
-// |row|^2 over the whole row (n <= 128 entries; lane x holds entries 2x and
-// 2x+1, returned through lo/hi so that the caller can copy the row out).
-__device__ __forceinline__ float row_sumsq(const uint16_t* __restrict__ row,
-                                           int n, int x, float& lo,
-                                           float& hi) {
+// Entries 2x and 2x+1 of a row of n <= 128 entries as f32 (0 past the end).
+__device__ __forceinline__ void row_pair(const uint16_t* __restrict__ row,
+                                         int n, int x, float& lo, float& hi) {
   lo = hi = 0.f;
   if (2 * x < n) {
     const uint32_t w = reinterpret_cast<const uint32_t*>(row)[x];
     lo = __uint_as_float(w << 16);
     hi = __uint_as_float(w & 0xffff0000u);
   }
-  return wave_sum(__builtin_fmaf(hi, hi, lo * lo));
 }
-__device__ __forceinline__ float row_sumsq(const float* __restrict__ row,
-                                           int n, int x, float& lo,
-                                           float& hi) {
+__device__ __forceinline__ void row_pair(const float* __restrict__ row, int n,
+                                         int x, float& lo, float& hi) {
   lo = hi = 0.f;
   if (2 * x < n) {
     const float2 p = reinterpret_cast<const float2*>(row)[x];
     lo = p.x;
     hi = p.y;
   }
-  return wave_sum(__builtin_fmaf(hi, hi, lo * lo));
 }
 
 __device__ __forceinline__ float inv_norm(float ss) {
@@ -190,19 +185,85 @@ __device__ __forceinline__ float inv_norm(float ss) {
 }
 
 // ------------------------------------------------------------- verify
+// Per-token scalars of one window, computed once in the prologue and shared
+// through LDS:
+//   f1 = c_t * rk_t           (prediction:  p = f1 * P)
+//   f2 = rk_t / c_t           (record:      ut = beta (v - p) * f2)
+//   f3 = scale * rq_t * c_t   (output:      o = f3 * (sum_j St_ij q_j
+//                                                     + ut * (k_t . q_t)),
+//                              St before the write: S_t q = c_t (St + ut k^T) q)
+//   fold = c_{t-1} * alpha_t when the scale is folded into St at token t
+//          (then c_t = 1), else 0
+// c_t (the scale after token t) and fold are recorded for commit, which
+// replays them instead of recomputing the scale sequence.
+struct StepScalars {
+  float f1, f2, f3, fold;
+  float beta, c, kq, pad;  // kq = k_t . q_t (raw rows)
+};
+
+// |k|^2, |q|^2 and k.q of one row, 16 lanes per row: lane `sub` holds the
+// entries 8*sub .. 8*sub+7 (zeros past the end) and the sums are reduced
+// over the 16-lane DPP row, so every lane of the row returns them.
+template <typename TIn>
+__device__ __forceinline__ void row_moments(const TIn* __restrict__ krow,
+                                            const TIn* __restrict__ qrow,
+                                            int n, int sub, float (&kk)[8],
+                                            float& skk, float& sqq,
+                                            float& skq) {
+  float qq[8];
+  if (8 * sub < n) {
+    if constexpr (sizeof(TIn) == 2) {
+      const uint4 kr = *reinterpret_cast<const uint4*>(krow + 8 * sub);
+      const uint4 qr = *reinterpret_cast<const uint4*>(qrow + 8 * sub);
+      const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+      const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk[2 * e] = __uint_as_float(kw[e] << 16);
+        kk[2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
+        qq[2 * e] = __uint_as_float(qw[e] << 16);
+        qq[2 * e + 1] = __uint_as_float(qw[e] & 0xffff0000u);
+      }
+    } else {
+      const float4 k0 = *reinterpret_cast<const float4*>(krow + 8 * sub);
+      const float4 k1 = *reinterpret_cast<const float4*>(krow + 8 * sub + 4);
+      const float4 q0 = *reinterpret_cast<const float4*>(qrow + 8 * sub);
+      const float4 q1 = *reinterpret_cast<const float4*>(qrow + 8 * sub + 4);
+      kk[0] = k0.x; kk[1] = k0.y; kk[2] = k0.z; kk[3] = k0.w;
+      kk[4] = k1.x; kk[5] = k1.y; kk[6] = k1.z; kk[7] = k1.w;
+      qq[0] = q0.x; qq[1] = q0.y; qq[2] = q0.z; qq[3] = q0.w;
+      qq[4] = q1.x; qq[5] = q1.y; qq[6] = q1.z; qq[7] = q1.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kk[e] = qq[e] = 0.f;
+  }
+  skk = sqq = skq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    skk = __builtin_fmaf(kk[e], kk[e], skk);
+    sqq = __builtin_fmaf(qq[e], qq[e], sqq);
+    skq = __builtin_fmaf(kk[e], qq[e], skq);
+  }
+  skk += dpp<0xB1>(skk); sqq += dpp<0xB1>(sqq); skq += dpp<0xB1>(skq);
+  skk += dpp<0x4E>(skk); sqq += dpp<0x4E>(sqq); skq += dpp<0x4E>(skq);
+  skk += dpp<0x141>(skk); sqq += dpp<0x141>(sqq); skq += dpp<0x141>(skq);
+  skk += dpp<0x140>(skk); sqq += dpp<0x140>(sqq); skq += dpp<0x140>(skq);
+}
+
 template <int DK, bool DBG, typename TIn>
-__global__ __launch_bounds__(kBlock) void verify_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6)))
+void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ g, const float* __restrict__ S,
     float* __restrict__ o, float* __restrict__ rec_k,
-    float* __restrict__ rec_u, float* __restrict__ rec_alpha,
+    float* __restrict__ rec_u, float2* __restrict__ rec_scale,
     float* __restrict__ dbg, WinDims d, LaneTable tl, float scale,
     int l2norm) {
   constexpr int R = DK / kWaves;  // key rows per wave
-  __shared__ float red_p[kWaves][kWave];
-  __shared__ float red_o[kWaves][kWave];
-  __shared__ float norm_s[2];
+  __shared__ float nrm[3][GDN_MAX_T];  // rk_t, rq_t, k_t . q_t (raw)
+  __shared__ StepScalars sc[GDN_MAX_T];
 
   int item = xcd_item(blockIdx.x, gridDim.x);
   const int cb = item % d.ncb;
@@ -221,94 +282,161 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(
   const bool act = i < d.dv;
   const int ic = act ? i : d.dv - 1;
   const int kh = h / d.group;
-  const bool key_writer = (h % d.group == 0) && cb == 0 && w == 0;
+  const bool key_writer = (h % d.group == 0) && cb == 0;
   const size_t ll = (size_t)layer * d.N + lane;
   const size_t dv = (size_t)d.dv;
+  // uniform row bases (token 0 of this lane-layer); per-lane offsets are
+  // 32-bit column indices, so addresses are scalar base + lane offset
+  const size_t kq_step = (size_t)d.Hk * DK;            // per token, q/k
+  const size_t vo_step = (size_t)d.Hv * dv;            // per token, v/o/u
+  const TIn* __restrict__ k0 = k + ((ll * d.T) * d.Hk + kh) * (size_t)DK;
+  const TIn* __restrict__ q0 = q + ((ll * d.T) * d.Hk + kh) * (size_t)DK;
+  const TIn* __restrict__ v0 = v + ((ll * d.T) * d.Hv + h) * dv;
+  float* __restrict__ o0 = o + ((ll * d.T) * d.Hv + h) * dv;
+  float* __restrict__ u0 = rec_u + ((ll * d.T) * d.Hv + h) * dv;
 
   float s[R];  // scaled state St (rows j0..j0+R-1, column i); S = c * St
   {
-    const float* Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv + ic;
+    const float* __restrict__ Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = __builtin_nontemporal_load(Sh + r * dv);
+    for (int r = 0; r < R; ++r)
+      s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
   }
-  float c = 1.0f;
 
+  // ---- prologue 1: per token (16 lanes each, 4 tokens per wave pass):
+  // |k_t|^2, |q_t|^2 and k_t.q_t over the whole row; the key record rows
+  for (int base = 4 * w; base < T; base += 16) {  // base is wave-uniform
+    const int t = base + x / 16;
+    const int tt = t < T ? t : T - 1;
+    const int sub = x % 16;
+    float kk[8], skk, sqq, skq;
+    row_moments<TIn>(k0 + tt * kq_step, q0 + tt * kq_step, DK, sub, kk, skk,
+                     sqq, skq);
+    if (t < T) {
+      if (sub == 0) {
+        nrm[0][t] = l2norm ? inv_norm(skk) : 1.0f;
+        nrm[1][t] = l2norm ? inv_norm(sqq) : 1.0f;
+        nrm[2][t] = skq;
+      }
+      if (key_writer && 8 * sub < DK) {
+        float4* dst = reinterpret_cast<float4*>(
+            rec_k + ((ll * d.T + t) * d.Hk + kh) * (size_t)DK + 8 * sub);
+        dst[0] = make_float4(kk[0], kk[1], kk[2], kk[3]);
+        dst[1] = make_float4(kk[4], kk[5], kk[6], kk[7]);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- prologue 2 (one wave, chosen per workgroup to spread the work over
+  // the SIMDs): lane t holds token t's gates; the scales c_t are an
+  // inclusive prefix product of alpha over the lanes.  If a prefix leaves
+  // [2^-32, 2^32] the scale is folded; that rare case walks the tokens in
+  // order in one lane instead.
+  if (w == (int)(blockIdx.x & 3)) {
+    const int tt = x < T ? x : T - 1;
+    const size_t gi = (ll * d.T + tt) * d.Hv + h;
+    const float a_t = x < T ? __expf(g[gi]) : 1.0f;
+    const float b_t = beta[gi];
+    float c = a_t;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(c, off, kWave);
+      if (x >= off) c *= y;
+    }
+    const bool out = !(c >= kScaleLo && c <= kScaleHi);
+    float fold = 0.f;
+    if (__builtin_amdgcn_ballot_w64(out && x < T) != 0) {
+      // sequential walk with folds (lane 0), results spread back by lane
+      __shared__ float seq_c[GDN_MAX_T], seq_f[GDN_MAX_T], seq_a[GDN_MAX_T];
+      if (x < T) seq_a[x] = a_t;
+      __builtin_amdgcn_wave_barrier();
+      if (x == 0) {
+        float cc = 1.0f;
+        for (int t = 0; t < T; ++t) {
+          float cn, fo = 0.f;
+          if (scale_step(cc, seq_a[t], cn)) {
+            fo = cn;
+            cn = 1.0f;
+          }
+          seq_c[t] = cn;
+          seq_f[t] = fo;
+          cc = cn;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (x < T) {
+        c = seq_c[x];
+        fold = seq_f[x];
+      }
+    }
+    if (x < T) {
+      const float rk = nrm[0][x], rq = nrm[1][x];
+      StepScalars z;
+      z.f1 = c * rk;
+      z.f2 = rk * __builtin_amdgcn_rcpf(c);
+      z.f3 = scale * rq * c;
+      z.fold = fold;
+      z.beta = b_t;
+      z.c = c;
+      z.kq = nrm[2][x];
+      z.pad = 0.f;
+      sc[x] = z;
+      if (cb == 0) rec_scale[gi] = make_float2(fold, c);
+    }
+  }
+  __syncthreads();
+
+  // ---- the window: one LDS exchange per token.  One pass over the state
+  // forms the partials of St k (prediction) and St q (output, from the state
+  // before the write); after the exchange a second pass applies the write.
+  __shared__ float2 red[2][kWaves][kWave];
+  RowWords<TIn, R> kw, qw;
+  kw.load(k0, j0);
+  qw.load(q0, j0);
   for (int t = 0; t < T; ++t) {
-    const size_t tok = ll * d.T + t;
-    const size_t krow = (tok * d.Hk + kh) * (size_t)DK;
-    const size_t gi = tok * d.Hv + h;
-    RowWords<TIn, R> kw, qw;
-    kw.load(k + krow, j0);
-    qw.load(q + krow, j0);
-    const float vi = load_in(v, gi * dv + ic);
+    const int buf = t & 1;
+    const float vi = load_in(v0 + t * vo_step, (uint32_t)ic);
+    const StepScalars z = sc[t];
+    if (z.fold != 0.f) fold_scale<R>(s, z.fold);
 
-    // norms (wave 0: key, wave 1: query) and the key record row
-    if (w == 0 && (l2norm || key_writer)) {
-      float lo, hi;
-      const float ss = row_sumsq(k + krow, DK, x, lo, hi);
-      if (x == 0) norm_s[0] = l2norm ? inv_norm(ss) : 1.0f;
-      if (key_writer && 2 * x < DK)
-        reinterpret_cast<float2*>(rec_k + krow)[x] = make_float2(lo, hi);
-    } else if (w == 1 && l2norm) {
-      float lo, hi;
-      const float ss = row_sumsq(q + krow, DK, x, lo, hi);
-      if (x == 0) norm_s[1] = inv_norm(ss);
-    }
-
-    const float alpha = __expf(g[gi]);
-    float cn;
-    if (scale_step(c, alpha, cn)) {
-      fold_scale<R>(s, cn);
-      cn = 1.0f;
-    }
-
-    // partial of P_i = sum_j St_ij k_j over this wave's rows (4 chains)
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float kv[R];
+    float a0 = 0.f, b0 = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; r += 4) {
-      a0 = __builtin_fmaf(s[r + 0], kw.at(r + 0), a0);
-      a1 = __builtin_fmaf(s[r + 1], kw.at(r + 1), a1);
-      a2 = __builtin_fmaf(s[r + 2], kw.at(r + 2), a2);
-      a3 = __builtin_fmaf(s[r + 3], kw.at(r + 3), a3);
+    for (int r = 0; r < R; ++r) {
+      kv[r] = kw.at(r);
+      a0 = __builtin_fmaf(s[r], kv[r], a0);
+      b0 = __builtin_fmaf(s[r], qw.at(r), b0);
     }
-    red_p[w][x] = (a0 + a1) + (a2 + a3);
+    red[buf][w][x] = make_float2(a0, b0);
     __syncthreads();
-    const float P = (red_p[0][x] + red_p[1][x]) + (red_p[2][x] + red_p[3][x]);
-    const float rk = l2norm ? norm_s[0] : 1.0f;
-    const float rq = l2norm ? norm_s[1] : 1.0f;
-    // p = alpha * (S_{t-1} khat) = (c_t * rk) * P;  ut = u * rk / c_t
-    const float p = (cn * rk) * P;
-    const float ut = (beta[gi] * (vi - p)) * (rk * __builtin_amdgcn_rcpf(cn));
-    if (w == 0) {
-      if (act) rec_u[gi * dv + i] = ut;
-      if (cb == 0 && x == 0) rec_alpha[gi] = alpha;
+    const float2 r0 = red[buf][0][x], r1 = red[buf][1][x];
+    const float2 r2 = red[buf][2][x], r3 = red[buf][3][x];
+    // key and query rows of the next token: requested after the partials
+    // are read (scalar and LDS loads share one wait counter), in flight
+    // during the write pass
+    if (t + 1 < T) {
+      kw.load(k0 + (t + 1) * kq_step, j0);
+      qw.load(q0 + (t + 1) * kq_step, j0);
+    }
+    const float P = (r0.x + r1.x) + (r2.x + r3.x);
+    const float PQ = (r0.y + r1.y) + (r2.y + r3.y);
+    const float p = z.f1 * P;
+    const float ut = (z.beta * (vi - p)) * z.f2;
+    const int owner = t % kWaves;  // wave that writes this token's outputs
+    if (w == owner && act) {
+      u0[t * vo_step + (uint32_t)i] = ut;
+      o0[t * vo_step + (uint32_t)i] = z.f3 * __builtin_fmaf(ut, z.kq, PQ);
     }
 
-    // rank-1 write, then the output partial on the new state
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    // rank-1 write
 #pragma unroll
-    for (int r = 0; r < R; r += 4) {
-      s[r + 0] = state_update(s[r + 0], ut, kw.at(r + 0));
-      s[r + 1] = state_update(s[r + 1], ut, kw.at(r + 1));
-      s[r + 2] = state_update(s[r + 2], ut, kw.at(r + 2));
-      s[r + 3] = state_update(s[r + 3], ut, kw.at(r + 3));
-      o0 = __builtin_fmaf(s[r + 0], qw.at(r + 0), o0);
-      o1 = __builtin_fmaf(s[r + 1], qw.at(r + 1), o1);
-      o2 = __builtin_fmaf(s[r + 2], qw.at(r + 2), o2);
-      o3 = __builtin_fmaf(s[r + 3], qw.at(r + 3), o3);
-    }
-    red_o[w][x] = (o0 + o1) + (o2 + o3);
-    c = cn;
+    for (int r = 0; r < R; ++r) s[r] = state_update(s[r], ut, kv[r]);
     if (DBG && act) {
-      float* dp = dbg + (gi * (size_t)DK + j0) * dv + i;
+      float* __restrict__ dp =
+          dbg + (((ll * d.T + t) * d.Hv + h) * (size_t)DK + j0) * dv;
 #pragma unroll
-      for (int r = 0; r < R; ++r) dp[r * dv] = materialise(c, s[r]);
-    }
-    __syncthreads();
-    if (w == 0 && act) {
-      const float osum =
-          (red_o[0][x] + red_o[1][x]) + (red_o[2][x] + red_o[3][x]);
-      o[gi * dv + i] = (scale * rq * c) * osum;
+      for (int r = 0; r < R; ++r)
+        dp[(uint32_t)(r * d.dv + i)] = materialise(z.c, s[r]);
     }
   }
 }
@@ -317,7 +445,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(
 template <int DK>
 __global__ __launch_bounds__(kBlock) void commit_kernel(
     const float* __restrict__ rec_k, const float* __restrict__ rec_u,
-    const float* __restrict__ rec_alpha, float* __restrict__ S, WinDims d,
+    const float2* __restrict__ rec_scale, float* __restrict__ S, WinDims d,
     CommitTable ct) {
   constexpr int R = DK / kWaves;
   int item = xcd_item(blockIdx.x, gridDim.x);
@@ -339,41 +467,42 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
   const int kh = h / d.group;
   const size_t ll = (size_t)layer * d.N + lane;
   const size_t dv = (size_t)d.dv;
-  float* Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv + ic;
+  float* __restrict__ Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
+  const float* __restrict__ k0 = rec_k + ((ll * d.T) * d.Hk + kh) * (size_t)DK;
+  const float* __restrict__ u0 = rec_u + ((ll * d.T) * d.Hv + h) * dv;
+  const float2* __restrict__ c0 = rec_scale + (ll * d.T) * d.Hv + h;
+  const size_t kq_step = (size_t)d.Hk * DK, vo_step = (size_t)d.Hv * dv;
 
   float s[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) s[r] = __builtin_nontemporal_load(Sh + r * dv);
-  float c = 1.0f;
+  for (int r = 0; r < R; ++r)
+    s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
 
   // the records of token t+1 are requested before token t is applied
-  size_t tok = ll * d.T;
-  float alpha = rec_alpha[tok * d.Hv + h];
-  float ut = rec_u[(tok * d.Hv + h) * dv + ic];
+  float2 fc = c0[0];
+  float ut = u0[(uint32_t)ic];
   RowWords<float, R> kw;
-  kw.load(rec_k + (tok * d.Hk + kh) * (size_t)DK, j0);
+  kw.load(k0, j0);
+  float c = 1.0f;
   for (int t = 0; t < m; ++t) {
-    const size_t nt = ll * d.T + (t + 1 < m ? t + 1 : t);
-    const float alpha_n = rec_alpha[nt * d.Hv + h];
-    const float ut_n = rec_u[(nt * d.Hv + h) * dv + ic];
+    const int nt = t + 1 < m ? t + 1 : t;
+    const float2 fc_n = c0[nt * d.Hv];
+    const float ut_n = u0[nt * vo_step + (uint32_t)ic];
     RowWords<float, R> kw_n;
-    kw_n.load(rec_k + (nt * d.Hk + kh) * (size_t)DK, j0);
-    float cn;
-    if (scale_step(c, alpha, cn)) {
-      fold_scale<R>(s, cn);
-      cn = 1.0f;
-    }
+    kw_n.load(k0 + nt * kq_step, j0);
+    if (fc.x != 0.f) fold_scale<R>(s, fc.x);
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = state_update(s[r], ut, kw.at(r));
-    c = cn;
-    alpha = alpha_n;
+    c = fc.y;
+    fc = fc_n;
     ut = ut_n;
     kw = kw_n;
   }
   if (act) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      __builtin_nontemporal_store(materialise(c, s[r]), Sh + r * dv);
+      __builtin_nontemporal_store(materialise(c, s[r]),
+                                  Sh + (uint32_t)(r * d.dv + i));
   }
 }
 
@@ -451,7 +580,7 @@ static hipError_t launch_verify_t(const WinDims& w, const LaneTable& tl,
                                   const void* q, const void* k, const void* v,
                                   const float* beta, const float* g,
                                   const float* S, float* o, float* rk,
-                                  float* ru, float* ra, float* dbg,
+                                  float* ru, float2* ra, float* dbg,
                                   float scale, int l2, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv * w.ncb;
   return launch(verify_kernel<DK, DBG, TIn>, dim3(blocks), dim3(kBlock), st,
@@ -464,7 +593,7 @@ static hipError_t launch_verify_d(const WinDims& w, const LaneTable& tl,
                                   const void* q, const void* k, const void* v,
                                   const float* beta, const float* g,
                                   const float* S, float* o, float* rk,
-                                  float* ru, float* ra, float* dbg,
+                                  float* ru, float2* ra, float* dbg,
                                   float scale, int l2, hipStream_t st) {
   switch (w.dk) {
     case 16: return launch_verify_t<16, DBG, TIn>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg, scale, l2, st);
@@ -520,7 +649,7 @@ extern "C" int gdn_verify(const gdn_dims* dims, const int32_t* t_lane,
   char* rb = (char*)records;
   float* rk = (float*)(rb + L.k);
   float* ru = (float*)(rb + L.u);
-  float* ra = (float*)(rb + L.alpha);
+  float2* ra = (float2*)(rb + L.scale);
   hipStream_t st = (hipStream_t)stream;
   const int l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
   hipError_t e;
@@ -567,7 +696,7 @@ extern "C" int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
   const char* rb = (const char*)records;
   const float* rk = (const float*)(rb + L.k);
   const float* ru = (const float*)(rb + L.u);
-  const float* ra = (const float*)(rb + L.alpha);
+  const float2* ra = (const float2*)(rb + L.scale);
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(d.n_layers * n_act * d.h_v * w.ncb);
   hipError_t e;
