@@ -39,18 +39,18 @@ NL, N, HV, HK, DK, DV, T = 48, 8, 32, 16, 128, 128, 16
 def alg_bytes_verify(t_lane):
     """Algorithmic bytes of one verify call: per (layer, lane) the S0 read
     (h_v*d_k*d_v*4) plus, per window token, q and k rows (bf16), v (bf16),
-    beta and g (f32), o (f32) and the records (khat f32 [h_k][d_k], u f32
-    [h_v][d_v], alpha f32 [h_v])."""
+    beta and g (f32), o (f32) and the records (raw k f32 [h_k][d_k], u f32
+    [h_v][d_v], a (fold, scale) f32 pair per value head)."""
     s0 = HV * DK * DV * 4
     per_tok = (2 * HK * DK * 2 + HV * DV * 2 + 2 * HV * 4 + HV * DV * 4 +
-               HK * DK * 4 + HV * DV * 4 + HV * 4)
+               HK * DK * 4 + HV * DV * 4 + HV * 8)
     return NL * sum(s0 + per_tok * int(t) for t in t_lane)
 
 
 def alg_bytes_commit(m_lane):
     """S0 read + S_m write for lanes with m > 0, plus m records each."""
     s = HV * DK * DV * 4
-    rec = HK * DK * 4 + HV * DV * 4 + HV * 4
+    rec = HK * DK * 4 + HV * DV * 4 + HV * 8
     return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
 
 
@@ -61,10 +61,10 @@ def alg_flops_verify(t_lane):
     return NL * sum(7 * DK * DV * HV * int(t) for t in t_lane)
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=("gdn_window.hip", "gdn_step.h")):
     import hashlib
     h = hashlib.sha256()
-    for f in ("gdn_window.hip", "gdn_step.h"):
+    for f in files:
         with open(os.path.join(ROOT, "commit_gated_delta_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -79,7 +79,9 @@ def measured_traffic(kernel):
     except (OSError, ValueError):
         return None
     k = rec.get(kernel)
-    if not k or k.get("source_sha256") != kernel_source_hash():
+    files = (("gdn_prefill.hip",) if kernel.startswith("prefill")
+             else ("gdn_window.hip", "gdn_step.h"))
+    if not k or k.get("source_sha256") != kernel_source_hash(files):
         return None
     return float(k["bytes_per_launch"])
 
@@ -151,10 +153,12 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
             "mfma_frac_issued": issued / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "mfma_frac_useful": useful / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "io_GBps": io_bytes / (ms * 1e-3) / 1e9,
+            "traffic_p1": measured_traffic("prefill_p1"),
+            "traffic_p2": measured_traffic("prefill_p2"),
             "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
 
 
-def cpu_baseline(rounds=3):
+def cpu_baseline(rounds=16):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: `rounds` chained rounds (verify + commit) of the full
     48-layer x 8-lane batch at T = 16; scaled to head-token updates/s."""

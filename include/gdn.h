@@ -98,10 +98,13 @@ typedef struct {
  *
  * Record contents (the "compact records that caused the transitions" of the
  * ReplaySSM section): per (layer, lane, token) the raw key rows widened to
- * f32 (f32 [h_k][d_k]), the decays alpha_t = exp(g_t) (f32 [h_v]) and the
- * delta vectors with the key norm folded in, u_t / sqrt(|k_t|^2 + 1e-6)
- * (f32 [h_v][d_v]).  About 24.7 KB per token per lane-layer at 32/16 heads
- * of dim 128, against 2 MiB for a full per-token state snapshot.
+ * f32 (f32 [h_k][d_k]); per value head the decay in scaled form, a float2
+ * (fold, c) where c is the running state scale after this token and fold
+ * the factor applied to the stored state before it (1 when none); and the
+ * delta vectors with key norm and scale folded in,
+ * u_t / (sqrt(|k_t|^2 + 1e-6) * c) (f32 [h_v][d_v]).  About 24.8 KB per
+ * token per lane-layer at 32/16 heads of dim 128, against 2 MiB for a full
+ * per-token state snapshot.
  */
 size_t gdn_records_bytes(const gdn_dims* dims);
 
@@ -168,8 +171,16 @@ size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
  *                or NULL: the state after every token count that is a
  *                positive multiple of ckpt_interval
  *   ckpt_interval  positive multiple of 64
- *   workspace    device, ws_bytes >= gdn_prefill_workspace_bytes(...)
- * Supported: d_k == d_v == 128.
+ *   workspace    device, ws_bytes >= gdn_prefill_workspace_bytes(...);
+ *                scratch owned by the caller, contents undefined on return
+ *   scale, flags as for gdn_verify
+ * Supported: d_k == d_v == 128, in_dtype == GDN_BF16 (q, k, v enter the
+ * matrix cores as bf16; GDN_F32 returns GDN_EUNSUPPORTED).  The state,
+ * decays and every accumulation are f32.  S_final and every checkpoint are
+ * exactly the state the same call would pass on from that token, so a
+ * prefill resumed from a checkpoint reproduces the rest bit for bit.
+ * Errors: GDN_EINVAL for bad sizes or NULL required pointers,
+ * GDN_EWORKSPACE when ws_bytes is too small, GDN_EHIP when a launch fails.
  */
 int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
                         int32_t h_k, int32_t d_k, int32_t d_v,
