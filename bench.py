@@ -62,11 +62,17 @@ def alg_flops_verify(t_lane):
 
 
 def kernel_source_hash(files=("gdn_window.hip", "gdn_step.h")):
+    """sha256 of the kernel sources with // comments and blank lines removed
+    (a comment edit leaves the recorded counters valid)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "commit_gated_delta_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "commit_gated_delta_amd", "csrc", f)) as fh:
+            for line in fh:
+                line = re.sub(r"//.*", "", line).rstrip()
+                if line:
+                    h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -20,11 +20,11 @@
 //   ut_i  = (beta * (v_i - p_i)) * (rk / c)     (= u_i * rk / c)
 //   St_ij <- fma(ut_i, k_j, St_ij)              (S = alpha S + u khat^T)
 //   o_i   = (scale * rq * c) * sum_j St_ij q_j
-// Records per token: alpha (f32 per value head), ut (f32 per value head and
-// column) and the raw key row widened to f32 (per key head).  Commit replays
-// the same scale steps and St_ij <- fma(ut_i, k_j, St_ij) from exactly these
-// values and stores S_m = c * St, so its result is bitwise the state verify
-// held after the same token.
+// Records per token: per value head the scale step (fold, c) as a float2,
+// ut (f32 per value head and column) and the raw key row widened to f32 (per
+// key head).  Commit replays the same folds and St_ij <- fma(ut_i, k_j,
+// St_ij) from exactly these values and stores S_m = c * St, so its result is
+// bitwise the state verify held after the same token.
 //
 // Work decomposition (CDNA4, wave64):
 //   One 256-thread workgroup per (layer, lane, value head, block of 64 value
@@ -32,15 +32,16 @@
 //   key rows j in [w*dk/4, (w+1)*dk/4).  A lane keeps its dk/4 state entries
 //   in VGPRs for the whole window (32 at dk = 128), which leaves room for
 //   eight waves per SIMD to hide memory latency.
-//   Both reductions over j are a register chain inside the lane plus a sum
-//   of four wave partials through LDS (two barriers per token).  The key and
-//   query values of a wave's rows are the same for all its lanes: they come
-//   in through scalar loads (SGPRs), bf16 pairs unpacked with two scalar ALU
-//   ops, and every multiply-add takes them as its SGPR operand -- no LDS
-//   broadcast traffic on the hot loop.
-//   The norms: wave 0 reduces |k|^2 and wave 1 reduces |q|^2 over the whole
-//   row (one dword per lane and a wave reduction) while the others work;
-//   the results travel with the first LDS exchange.
+//   Per token, one pass over the held entries forms the partial sums of
+//   St k (prediction) and St q (output) from the state before the token's
+//   write; the four wave partials meet in LDS behind one barrier; the
+//   output uses S_t q = c_t (St_{t-1} q + ut (k . q)); a second pass applies
+//   the write.  The key and query values of a wave's rows are the same for
+//   all its lanes: they come in through scalar loads (SGPRs), bf16 pairs
+//   unpacked with two scalar ALU ops, and every multiply-add takes them as
+//   its SGPR operand -- no LDS broadcast traffic on the hot loop.
+//   A prologue computes the norms, k . q and the whole scale sequence of
+//   the window once and leaves the per-token scalars in LDS.
 //   State loads/stores: for a fixed row j the 64 lanes of a wave touch 64
 //   consecutive f32 -- one 256-byte transaction per instruction.
 //   Blocks are dealt to the 8 XCDs round-robin; the block -> item map gives
