@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the gated-delta speculative-decoding hot path on one MI355X.
 
-One step = one speculative round over the whole batch:
-    gdn_verify  (8 lanes x 48 layers x 32 value heads / 16 key heads,
-                 d_k = d_v = 128, T = 16 window tokens per lane)
-    gdn_commit  (m_lane ~ Uniform{0..16}, seeded, drawn up front)
-with the recurrent state carried from one step to the next.  Inputs are
-seeded synthetic tensors (gdn_synth), resident in HBM before the timed
-region; four input sets rotate so that the 256 MB Infinity Cache cannot
-hold a step's inputs from the previous use.
+One step = one speculative round over the whole batch: the verify of a
+window (8 lanes x 48 layers x 32 value heads / 16 key heads, d_k = d_v =
+128, T = 16 window tokens per lane) and the commit of an accepted prefix
+(m_lane ~ Uniform{0..16}, seeded, drawn up front), with the recurrent state
+carried from one step to the next.  Two ways of running it are timed:
+    fused     gdn_commit_verify: the commit of the previous round's prefix
+              and the verify of this round in one launch (the headline)
+    two-call  gdn_verify, then gdn_commit
+Both do the same work per step in steady state.  Inputs are seeded
+synthetic tensors (gdn_synth), resident in HBM before the timed region; four
+input sets rotate so that the 256 MB Infinity Cache cannot hold a step's
+inputs from the previous use.
 
 Printed: one JSON line (metric, value = head-token updates/s, roofline of
 the dominant kernel, cpu_baseline = the fp64 oracle on a bounded sample).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--path fused|two-call|both]
 """
 from __future__ import annotations
 
@@ -59,6 +64,23 @@ def alg_flops_verify(t_lane):
     prediction (1 FMA = 2), the decayed rank-1 write (1 mul + 1 FMA = 3) and
     the output (1 FMA = 2): 7 flops x d_k x d_v x h_v x T per lane-layer."""
     return NL * sum(7 * DK * DV * HV * int(t) for t in t_lane)
+
+
+def alg_bytes_fused(t_lane, m_prev):
+    """Algorithmic bytes of one gdn_commit_verify: per lane-layer the state
+    read, the committed state write when m_prev > 0, m_prev records read,
+    and the verify traffic of the window without its own state read."""
+    s = HV * DK * DV * 4
+    rec = HK * DK * 4 + HV * DV * 4 + HV * 8
+    win = alg_bytes_verify(t_lane) - NL * len(t_lane) * s
+    return win + NL * sum(s + ((s + rec * int(m)) if m > 0 else 0)
+                          for m in m_prev)
+
+
+def alg_flops_fused(t_lane, m_prev):
+    """Verify flops plus the replay: one FMA (2 flops) per state element per
+    accepted token."""
+    return alg_flops_verify(t_lane) + NL * HV * DK * DV * 2 * int(np.sum(m_prev))
 
 
 def kernel_source_hash(files=("gdn_window.hip", "gdn_step.h")):
@@ -197,6 +219,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pool", type=int, default=4)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--path", choices=("fused", "two-call", "both"),
+                    default="both",
+                    help="which way of running a round to time (the fused "
+                         "one is the headline when timed)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -241,58 +267,122 @@ def main():
         pool.append((dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
                      torch.from_numpy(w.beta).to(dev),
                      torch.from_numpy(w.g).to(dev)))
-    S = torch.from_numpy(gs.initial_state(shape, (7, 0))).to(dev)
+    S0 = gs.initial_state(shape, (7, 0))
     o = torch.empty((NL, N, T, HV, DV), device=dev)
-    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    nrec = gdn.records_bytes(dims)
     total = args.warmup + args.steps
     m_all = [gs.accepted_uniform(t_lane, (7, 100 + s)) for s in range(total)]
     stream = torch.cuda.current_stream()
 
-    def step(s, ev=None):
-        q, k, v, beta, g = pool[s % len(pool)]
-        if ev is not None:
-            ev[0].record(stream)
-        gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        step(args.warmup + s, evs[s])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_v = [e[0].elapsed_time(e[1]) for e in evs]
-    ms_c = [e[1].elapsed_time(e[2]) for e in evs]
+    def timed(step, n_ev):
+        for s in range(args.warmup):
+            step(s)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+               for _ in range(args.steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(args.steps):
+            step(args.warmup + s, evs[s])
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, evs
 
     upd_per_step = int(t_lane.sum()) * NL * HV
-    ms_per_step = total_ms / args.steps
-    value = upd_per_step / (ms_per_step * 1e-3)
-    bv = alg_bytes_verify(t_lane)
-    bc = [alg_bytes_commit(m_all[args.warmup + s]) for s in range(args.steps)]
-    gbs_v = bv / (np.mean(ms_v) * 1e-3) / 1e9
-    gbs_c = np.mean(bc) / (np.mean(ms_c) * 1e-3) / 1e9
-    gbs_path = (bv + np.mean(bc)) / (ms_per_step * 1e-3) / 1e9
-    fv = alg_flops_verify(t_lane)
-    ms_v_mean, ms_c_mean = float(np.mean(ms_v)), float(np.mean(ms_c))
-    # verify dominates the step; at T = 16 it is bound by f32 VALU issue
-    # (three FMAs per state element per token), not by HBM
-    tflops_v = fv / (ms_v_mean * 1e-3) / 1e12
+    res = {}
+    if args.path in ("two-call", "both"):
+        S = torch.from_numpy(S0).to(dev)
+        rec = torch.empty(nrec, dtype=torch.uint8, device=dev)
+
+        def step2(s, ev=None):
+            q, k, v, beta, g = pool[s % len(pool)]
+            if ev is not None:
+                ev[0].record(stream)
+            gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+        ms, evs = timed(step2, 3)
+        ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        bv = alg_bytes_verify(t_lane)
+        bc = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
+                            for s in range(args.steps)]))
+        fv = alg_flops_verify(t_lane)
+        res["two-call"] = {
+            "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
+            "hbm_roofline_frac_path": (bv + bc) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "verify_ms": ms_v, "commit_ms": ms_c,
+            "verify_tflops": fv / (ms_v * 1e-3) / 1e12,
+            "verify_alg_GBps": bv / (ms_v * 1e-3) / 1e9,
+            "commit_alg_GBps": bc / (ms_c * 1e-3) / 1e9,
+            "commit_hbm_frac": bc / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "verify_traffic": measured_traffic("verify_kernel"),
+            "commit_traffic": measured_traffic("commit_kernel"),
+            "alg_bytes_per_step": bv + bc, "alg_flops_verify": fv}
+        del S, rec
+    if args.path in ("fused", "both"):
+        S = torch.from_numpy(S0).to(dev)
+        recs = [torch.empty(nrec, dtype=torch.uint8, device=dev)
+                for _ in range(2)]
+        zero = np.zeros(N, dtype=np.int32)
+
+        def m_prev_of(s):
+            return zero if s == 0 else m_all[s - 1]
+
+        def stepf(s, ev=None):
+            q, k, v, beta, g = pool[s % len(pool)]
+            if ev is not None:
+                ev[0].record(stream)
+            gdn.commit_verify(dims, m_prev_of(s), t_lane, recs[(s + 1) % 2],
+                              t_lane, q, k, v, beta, g, S, o, recs[s % 2],
+                              stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+
+        ms, evs = timed(stepf, 2)
+        ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        mp = [m_prev_of(args.warmup + s) for s in range(args.steps)]
+        bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in mp]))
+        ff = float(np.mean([alg_flops_fused(t_lane, m) for m in mp]))
+        res["fused"] = {
+            "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
+            "hbm_roofline_frac_path": bf / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": ms_f, "tflops": ff / (ms_f * 1e-3) / 1e12,
+            "alg_GBps": bf / (ms_f * 1e-3) / 1e9,
+            "traffic": measured_traffic("fused_kernel"),
+            "alg_bytes_per_step": bf, "alg_flops_per_launch": ff}
+        del S, recs
+
+    head = "fused" if "fused" in res else "two-call"
+    h = res[head]
+    ms_per_step = h["ms_per_step"]
+    if head == "fused":
+        roof = {"bound": "alu",
+                "kernel": "gdn_commit_verify (verify_kernel, replay on)",
+                "achieved": h["tflops"], "peak": F32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": h["tflops"] / F32_VECTOR_PEAK_TFLOPS,
+                "traffic": h["traffic"],
+                "alg_flops_per_launch": h["alg_flops_per_launch"],
+                "alg_bytes_per_launch": h["alg_bytes_per_step"],
+                "avg_launch_ms": h["kernel_ms"]}
+    else:
+        roof = {"bound": "alu", "kernel": "gdn_verify (verify_kernel)",
+                "achieved": h["verify_tflops"], "peak": F32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": h["verify_tflops"] / F32_VECTOR_PEAK_TFLOPS,
+                "traffic": h["verify_traffic"],
+                "alg_flops_per_launch": h["alg_flops_verify"],
+                "alg_bytes_per_launch": alg_bytes_verify(t_lane),
+                "avg_launch_ms": h["verify_ms"]}
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": h["updates_per_s"],
         "unit": "head-token updates/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -307,21 +397,10 @@ def main():
                                "32 value / 16 key heads, d_k=d_v=128, T=16, "
                                "m ~ U{0..16}, state carried across steps",
                    "n_lanes": N, "n_layers": NL, "h_v": HV, "h_k": HK,
-                   "d_k": DK, "d_v": DV, "t": T},
-        "hbm_roofline_frac_path": gbs_path / HBM_PEAK_GBS,
-        "roofline": {"bound": "alu", "kernel": "gdn_verify (verify_kernel)",
-                     "achieved": tflops_v, "peak": F32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops_v / F32_VECTOR_PEAK_TFLOPS,
-                     "traffic": measured_traffic("verify_kernel"),
-                     "alg_flops_per_launch": fv,
-                     "alg_bytes_per_launch": bv,
-                     "avg_launch_ms": ms_v_mean},
-        "verify_ms": ms_v_mean,
-        "commit_ms": ms_c_mean,
-        "verify_alg_GBps": gbs_v,
-        "commit_alg_GBps": gbs_c,
-        "commit_hbm_frac": gbs_c / HBM_PEAK_GBS,
-        "commit_traffic": measured_traffic("commit_kernel"),
+                   "d_k": DK, "d_v": DV, "t": T, "path": head},
+        "hbm_roofline_frac_path": h["hbm_roofline_frac_path"],
+        "roofline": roof,
+        "paths": res,
     }
     if not args.no_prefill:
         out["prefill"] = bench_prefill()

@@ -24,7 +24,7 @@ GDN_MAX_LANES = 256
 GDN_MAX_T = 64
 
 EXPORTED = ("gdn_records_bytes", "gdn_verify", "gdn_commit",
-            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+            "gdn_commit_verify", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_strerror", "gdn_last_error")
 
 
@@ -68,6 +68,10 @@ def _load_library():
     lib.gdn_verify.restype = ctypes.c_int
     lib.gdn_commit.argtypes = [dp, ip, ip, vp, vp, vp]
     lib.gdn_commit.restype = ctypes.c_int
+    lib.gdn_commit_verify.argtypes = [dp, ip, ip, vp, ip, vp, vp, vp,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, f,
+                                      ctypes.c_int, vp]
+    lib.gdn_commit_verify.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [i32] * 6
     lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_prefill_chunked.argtypes = [i32] * 7 + [vp] * 3 + [ctypes.c_int] + [
@@ -152,6 +156,23 @@ def commit(dims: Dims, m_lane, t_lane, records, S, stream=None,
     if raw_status:
         return st
     _check(st, "gdn_commit")
+
+
+def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
+                  beta, g, S, o, records, dbg_states=None, scale=1.0,
+                  l2norm=True, stream=None, raw_status=False):
+    """gdn_commit_verify on torch tensors: commit(m_prev) of the previous
+    window's records, then verify of the new window, in one launch."""
+    st = lib.gdn_commit_verify(
+        ctypes.byref(dims), _int_array(m_prev, dims.n_lanes),
+        _int_array(t_prev, dims.n_lanes), _ptr(records_prev),
+        _int_array(t_lane, dims.n_lanes), _ptr(q), _ptr(k), _ptr(v),
+        _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S), _ptr(o), _ptr(records),
+        _ptr(dbg_states), float(scale), GDN_FLAG_L2NORM_QK if l2norm else 0,
+        _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_commit_verify")
 
 
 def prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k, d_v) -> int:

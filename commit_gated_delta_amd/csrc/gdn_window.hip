@@ -252,16 +252,140 @@ __device__ __forceinline__ void row_moments(const TIn* __restrict__ krow,
   skk += dpp<0x140>(skk); sqq += dpp<0x140>(sqq); skq += dpp<0x140>(skq);
 }
 
-template <int DK, bool DBG, typename TIn>
+// Records of the previous window, replayed by the fused commit + verify
+// before the new window starts (unused by a plain verify).
+struct PrevRecords {
+  const float* k;
+  const float* u;
+  const float2* scale;
+  LaneTable m;  // accepted prefix per lane
+};
+
+// Replay of m recorded tokens on the held state (the commit of the
+// ReplaySSM section): the same fold, write and materialisation as
+// commit_kernel, in the same order, on the same values.  Returns the scale
+// of the state after the last replayed token.
+template <int R>
+__device__ __forceinline__ float replay(float (&s)[R], const float* __restrict__ k0,
+                                        const float* __restrict__ u0,
+                                        const float2* __restrict__ c0, int m,
+                                        int j0, int ic, size_t kq_step,
+                                        size_t vo_step, int Hv) {
+  // the records of token t+1 are requested before token t is applied
+  float2 fc = c0[0];
+  float ut = u0[(uint32_t)ic];
+  RowWords<float, R> kw;
+  kw.load(k0, j0);
+  float c = 1.0f;
+  for (int t = 0; t < m; ++t) {
+    const int nt = t + 1 < m ? t + 1 : t;
+    const float2 fc_n = c0[nt * Hv];
+    const float ut_n = u0[nt * vo_step + (uint32_t)ic];
+    RowWords<float, R> kw_n;
+    kw_n.load(k0 + nt * kq_step, j0);
+    if (fc.x != 0.f) fold_scale<R>(s, fc.x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = state_update(s[r], ut, kw.at(r));
+    c = fc.y;
+    fc = fc_n;
+    ut = ut_n;
+    kw = kw_n;
+  }
+  return c;
+}
+
+// Records of up to kTok tokens staged in LDS for the fused replay.
+template <int DK>
+struct ReplayStage {
+  static constexpr int kTok = 16;
+  float k[kTok][DK];     // raw key rows (this workgroup's key head)
+  float u[kTok][kWave];  // ut of this workgroup's 64 columns
+  float2 sc[kTok];       // (fold, c)
+};
+
+// The replay of the fused commit + verify.  The whole workgroup first loads
+// the records of up to kTok tokens into LDS (one wait for all of them), then
+// every wave applies them to its rows with the same operations, in the same
+// order and on the same values as replay(), so the result is bitwise the
+// same as gdn_commit's.  pk, pu, pc point at token 0 of this lane-layer
+// (key head, value head); all loads are clamped to valid tokens and columns.
+template <int DK, int R>
+__device__ __forceinline__ float replay_staged(
+    float (&s)[R], ReplayStage<DK>& st, const float* __restrict__ pk,
+    const float* __restrict__ pu, const float2* __restrict__ pc, int m,
+    int j0, int x, int cb, int dv, size_t kq_step, size_t vo_step, int Hv) {
+  constexpr int kTok = ReplayStage<DK>::kTok;
+  constexpr int kK4 = kTok * DK / 4;  // float4 slots of the key rows
+  const int tid = (int)threadIdx.x;
+  float c = 1.0f;
+  for (int t0 = 0; t0 < m; t0 += kTok) {
+    const int nb = m - t0 < kTok ? m - t0 : kTok;
+    float4 kreg[(kK4 + kBlock - 1) / kBlock];
+    float ureg[kTok * kWave / kBlock];
+#pragma unroll
+    for (int rep = 0; rep < (kK4 + kBlock - 1) / kBlock; ++rep) {
+      const int e = tid + rep * kBlock;
+      int tok = e / (DK / 4);
+      tok = tok < nb ? tok : nb - 1;
+      kreg[rep] = reinterpret_cast<const float4*>(
+          pk + (t0 + tok) * kq_step)[e % (DK / 4)];
+    }
+#pragma unroll
+    for (int rep = 0; rep < kTok * kWave / kBlock; ++rep) {
+      const int e = tid + rep * kBlock;
+      int tok = e / kWave;
+      tok = tok < nb ? tok : nb - 1;
+      int col = cb * kWave + e % kWave;
+      col = col < dv ? col : dv - 1;
+      ureg[rep] = pu[(t0 + tok) * vo_step + (uint32_t)col];
+    }
+    const float2 sreg = pc[(size_t)(t0 + (tid < nb ? tid : nb - 1)) * Hv];
+#pragma unroll
+    for (int rep = 0; rep < (kK4 + kBlock - 1) / kBlock; ++rep) {
+      const int e = tid + rep * kBlock;
+      if (e < kK4) reinterpret_cast<float4*>(&st.k[0][0])[e] = kreg[rep];
+    }
+#pragma unroll
+    for (int rep = 0; rep < kTok * kWave / kBlock; ++rep)
+      (&st.u[0][0])[tid + rep * kBlock] = ureg[rep];
+    if (tid < kTok) st.sc[tid] = sreg;
+    __syncthreads();
+    for (int t = 0; t < nb; ++t) {
+      const float2 fc = st.sc[t];
+      const float fold = __int_as_float(
+          __builtin_amdgcn_readfirstlane(__float_as_int(fc.x)));
+      if (fold != 0.f) fold_scale<R>(s, fold);
+      const float ut = st.u[t][x];
+      const float4* kr = reinterpret_cast<const float4*>(&st.k[t][j0]);
+#pragma unroll
+      for (int r4 = 0; r4 < R / 4; ++r4) {
+        const float4 kk = kr[r4];
+        s[4 * r4 + 0] = state_update(s[4 * r4 + 0], ut, kk.x);
+        s[4 * r4 + 1] = state_update(s[4 * r4 + 1], ut, kk.y);
+        s[4 * r4 + 2] = state_update(s[4 * r4 + 2], ut, kk.z);
+        s[4 * r4 + 3] = state_update(s[4 * r4 + 3], ut, kk.w);
+      }
+      c = fc.y;
+    }
+    __syncthreads();  // the next batch overwrites the stage
+  }
+  return c;
+}
+
+// REPLAY = false: gdn_verify (S is only read).  REPLAY = true: the fused
+// gdn_commit_verify -- replay the previous window's accepted prefix from S,
+// store the committed state S_m in place, then verify the new window from
+// the state still held in registers (the committed values, bit for bit).
+template <int DK, bool DBG, typename TIn, bool REPLAY>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6)))
 void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ beta,
-    const float* __restrict__ g, const float* __restrict__ S,
+    const float* __restrict__ g, float* S,
     float* __restrict__ o, float* __restrict__ rec_k,
     float* __restrict__ rec_u, float2* __restrict__ rec_scale,
     float* __restrict__ dbg, WinDims d, LaneTable tl, float scale,
-    int l2norm) {
+    int l2norm, PrevRecords prev) {
   constexpr int R = DK / kWaves;  // key rows per wave
   __shared__ float nrm[3][GDN_MAX_T];  // rk_t, rq_t, k_t . q_t (raw)
   __shared__ StepScalars sc[GDN_MAX_T];
@@ -274,7 +398,8 @@ void verify_kernel(
   const int lane = item % d.N;
   const int layer = item / d.N;
   const int T = tl.v[lane];
-  if (T == 0) return;
+  const int m_prev = REPLAY ? prev.m.v[lane] : 0;
+  if (T == 0 && m_prev == 0) return;
 
   const int w = uniform((int)threadIdx.x / kWave);
   const int x = (int)threadIdx.x % kWave;
@@ -298,11 +423,29 @@ void verify_kernel(
 
   float s[R];  // scaled state St (rows j0..j0+R-1, column i); S = c * St
   {
-    const float* __restrict__ Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
+    float* Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
+    if constexpr (REPLAY) {
+      if (m_prev > 0) {
+        __shared__ ReplayStage<DK> stage;
+        const float c = replay_staged<DK, R>(
+            s, stage, prev.k + ((ll * d.T) * d.Hk + kh) * (size_t)DK,
+            prev.u + ((ll * d.T) * d.Hv + h) * dv,
+            prev.scale + (ll * d.T) * d.Hv + h, m_prev, j0, x, cb, d.dv,
+            kq_step, vo_step, d.Hv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r] = materialise(c, s[r]);
+        if (act) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            __builtin_nontemporal_store(s[r], Sh + (uint32_t)(r * d.dv + i));
+        }
+      }
+    }
   }
+  if (REPLAY && T == 0) return;
 
   // ---- prologue 1: per token (16 lanes each, 4 tokens per wave pass):
   // |k_t|^2, |q_t|^2 and k_t.q_t over the whole row; the key record rows
@@ -478,27 +621,7 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r)
     s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
-
-  // the records of token t+1 are requested before token t is applied
-  float2 fc = c0[0];
-  float ut = u0[(uint32_t)ic];
-  RowWords<float, R> kw;
-  kw.load(k0, j0);
-  float c = 1.0f;
-  for (int t = 0; t < m; ++t) {
-    const int nt = t + 1 < m ? t + 1 : t;
-    const float2 fc_n = c0[nt * d.Hv];
-    const float ut_n = u0[nt * vo_step + (uint32_t)ic];
-    RowWords<float, R> kw_n;
-    kw_n.load(k0 + nt * kq_step, j0);
-    if (fc.x != 0.f) fold_scale<R>(s, fc.x);
-#pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = state_update(s[r], ut, kw.at(r));
-    c = fc.y;
-    fc = fc_n;
-    ut = ut_n;
-    kw = kw_n;
-  }
+  const float c = replay<R>(s, k0, u0, c0, m, j0, ic, kq_step, vo_step, d.Hv);
   if (act) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -576,32 +699,136 @@ static WinDims win_dims(const gdn_dims& d) {
   return w;
 }
 
-template <int DK, bool DBG, typename TIn>
+struct VerifyArgs {
+  const void *q, *k, *v;
+  const float *beta, *g;
+  float* S;
+  float* o;
+  float *rk, *ru;
+  float2* ra;
+  float* dbg;
+  float scale;
+  int l2;
+};
+
+template <int DK, bool DBG, typename TIn, bool REPLAY>
 static hipError_t launch_verify_t(const WinDims& w, const LaneTable& tl,
-                                  const void* q, const void* k, const void* v,
-                                  const float* beta, const float* g,
-                                  const float* S, float* o, float* rk,
-                                  float* ru, float2* ra, float* dbg,
-                                  float scale, int l2, hipStream_t st) {
+                                  const VerifyArgs& a, const PrevRecords& pr,
+                                  hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv * w.ncb;
-  return launch(verify_kernel<DK, DBG, TIn>, dim3(blocks), dim3(kBlock), st,
-                (const TIn*)q, (const TIn*)k, (const TIn*)v, beta, g, S, o, rk,
-                ru, ra, dbg, w, tl, scale, l2);
+  return launch(verify_kernel<DK, DBG, TIn, REPLAY>, dim3(blocks), dim3(kBlock),
+                st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.beta,
+                a.g, a.S, a.o, a.rk, a.ru, a.ra, a.dbg, w, tl, a.scale, a.l2,
+                pr);
 }
 
-template <bool DBG, typename TIn>
+template <bool DBG, typename TIn, bool REPLAY>
 static hipError_t launch_verify_d(const WinDims& w, const LaneTable& tl,
-                                  const void* q, const void* k, const void* v,
-                                  const float* beta, const float* g,
-                                  const float* S, float* o, float* rk,
-                                  float* ru, float2* ra, float* dbg,
-                                  float scale, int l2, hipStream_t st) {
+                                  const VerifyArgs& a, const PrevRecords& pr,
+                                  hipStream_t st) {
   switch (w.dk) {
-    case 16: return launch_verify_t<16, DBG, TIn>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg, scale, l2, st);
-    case 32: return launch_verify_t<32, DBG, TIn>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg, scale, l2, st);
-    case 64: return launch_verify_t<64, DBG, TIn>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg, scale, l2, st);
-    default: return launch_verify_t<128, DBG, TIn>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg, scale, l2, st);
+    case 16: return launch_verify_t<16, DBG, TIn, REPLAY>(w, tl, a, pr, st);
+    case 32: return launch_verify_t<32, DBG, TIn, REPLAY>(w, tl, a, pr, st);
+    case 64: return launch_verify_t<64, DBG, TIn, REPLAY>(w, tl, a, pr, st);
+    default: return launch_verify_t<128, DBG, TIn, REPLAY>(w, tl, a, pr, st);
   }
+}
+
+template <bool REPLAY>
+static hipError_t launch_verify(const WinDims& w, const LaneTable& tl,
+                                int in_dtype, const VerifyArgs& a,
+                                const PrevRecords& pr, hipStream_t st) {
+  if (in_dtype == GDN_BF16)
+    return a.dbg ? launch_verify_d<true, uint16_t, REPLAY>(w, tl, a, pr, st)
+                 : launch_verify_d<false, uint16_t, REPLAY>(w, tl, a, pr, st);
+  return a.dbg ? launch_verify_d<true, float, REPLAY>(w, tl, a, pr, st)
+               : launch_verify_d<false, float, REPLAY>(w, tl, a, pr, st);
+}
+
+// Checks shared by gdn_verify and gdn_commit_verify; fills the lane table
+// and the kernel arguments.  *any = 0 when every t_lane is 0.
+static int verify_setup(const char* fn, const gdn_dims* dims,
+                        const int32_t* t_lane, const void* q, const void* k,
+                        const void* v, int in_dtype, const float* beta,
+                        const float* g, const float* S, float* o,
+                        void* records, float* dbg_states, float scale,
+                        int flags, LaneTable& tl, VerifyArgs& a, int* any) {
+  char msg[128];
+  int rc = check_dims(dims);
+  if (rc != GDN_OK) return rc;
+  if (!t_lane || !q || !k || !v || !beta || !g || !S || !o || !records) {
+    snprintf(msg, sizeof(msg), "%s: required pointer is NULL", fn);
+    return fail(GDN_EINVAL, msg);
+  }
+  if (in_dtype != GDN_BF16 && in_dtype != GDN_F32) {
+    snprintf(msg, sizeof(msg), "%s: unknown in_dtype", fn);
+    return fail(GDN_EINVAL, msg);
+  }
+  if (flags & ~GDN_FLAG_L2NORM_QK) {
+    snprintf(msg, sizeof(msg), "%s: unknown flag bits", fn);
+    return fail(GDN_EINVAL, msg);
+  }
+  // q/k rows are read as dwords (bf16 pairs) or f32
+  if (misaligned(q, 4) || misaligned(k, 4) ||
+      misaligned(v, in_dtype == GDN_BF16 ? 2 : 4) || misaligned(beta, 4) ||
+      misaligned(g, 4) || misaligned(S, 4) || misaligned(o, 4) ||
+      misaligned(records, 256) || (dbg_states && misaligned(dbg_states, 4))) {
+    snprintf(msg, sizeof(msg), "%s: misaligned pointer", fn);
+    return fail(GDN_EINVAL, msg);
+  }
+  const gdn_dims& d = *dims;
+  memset(&tl, 0, sizeof(tl));
+  *any = 0;
+  for (int n = 0; n < d.n_lanes; ++n) {
+    if (t_lane[n] < 0 || t_lane[n] > d.t_max) {
+      snprintf(msg, sizeof(msg), "%s: t_lane out of 0..t_max", fn);
+      return fail(GDN_EINVAL, msg);
+    }
+    tl.v[n] = (uint8_t)t_lane[n];
+    *any |= t_lane[n];
+  }
+  const RecLayout L = rec_layout(d);
+  char* rb = (char*)records;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.S = const_cast<float*>(S);
+  a.o = o;
+  a.rk = (float*)(rb + L.k);
+  a.ru = (float*)(rb + L.u);
+  a.ra = (float2*)(rb + L.scale);
+  a.dbg = dbg_states;
+  a.scale = scale;
+  a.l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+  return GDN_OK;
+}
+
+// Lane table of a commit: m_lane[n] in 0..t_lane[n] <= t_max.
+static int commit_lanes(const char* fn, const gdn_dims& d,
+                        const int32_t* m_lane, const int32_t* t_lane,
+                        CommitTable& ct) {
+  char msg[128];
+  memset(&ct, 0, sizeof(ct));
+  int n_act = 0;
+  for (int n = 0; n < d.n_lanes; ++n) {
+    if (t_lane[n] < 0 || t_lane[n] > d.t_max) {
+      snprintf(msg, sizeof(msg), "%s: t_lane out of 0..t_max", fn);
+      return fail(GDN_EINVAL, msg);
+    }
+    if (m_lane[n] < 0 || m_lane[n] > t_lane[n]) {
+      snprintf(msg, sizeof(msg), "%s: m_lane out of 0..t_lane", fn);
+      return fail(GDN_EINVAL, msg);
+    }
+    if (m_lane[n] > 0) {
+      ct.lane[n_act] = (uint8_t)n;
+      ct.m[n_act] = (uint8_t)m_lane[n];
+      ++n_act;
+    }
+  }
+  ct.n_act = n_act;
+  return GDN_OK;
 }
 
 }  // namespace gdn
@@ -619,50 +846,17 @@ extern "C" int gdn_verify(const gdn_dims* dims, const int32_t* t_lane,
                           const float* S, float* o, void* records,
                           float* dbg_states, float scale, int flags,
                           void* stream) {
-  int rc = check_dims(dims);
-  if (rc != GDN_OK) return rc;
-  if (!t_lane || !q || !k || !v || !beta || !g || !S || !o || !records)
-    return fail(GDN_EINVAL, "gdn_verify: required pointer is NULL");
-  if (in_dtype != GDN_BF16 && in_dtype != GDN_F32)
-    return fail(GDN_EINVAL, "gdn_verify: unknown in_dtype");
-  if (flags & ~GDN_FLAG_L2NORM_QK)
-    return fail(GDN_EINVAL, "gdn_verify: unknown flag bits");
-  // q/k rows are read as dwords (bf16 pairs) or f32
-  if (misaligned(q, 4) || misaligned(k, 4) ||
-      misaligned(v, in_dtype == GDN_BF16 ? 2 : 4) || misaligned(beta, 4) ||
-      misaligned(g, 4) || misaligned(S, 4) || misaligned(o, 4) ||
-      misaligned(records, 256) || (dbg_states && misaligned(dbg_states, 4)))
-    return fail(GDN_EINVAL, "gdn_verify: misaligned pointer");
-  const gdn_dims& d = *dims;
   LaneTable tl;
-  memset(&tl, 0, sizeof(tl));
+  VerifyArgs a;
   int any = 0;
-  for (int n = 0; n < d.n_lanes; ++n) {
-    if (t_lane[n] < 0 || t_lane[n] > d.t_max)
-      return fail(GDN_EINVAL, "gdn_verify: t_lane out of 0..t_max");
-    tl.v[n] = (uint8_t)t_lane[n];
-    any |= t_lane[n];
-  }
+  int rc = verify_setup("gdn_verify", dims, t_lane, q, k, v, in_dtype, beta, g,
+                        S, o, records, dbg_states, scale, flags, tl, a, &any);
+  if (rc != GDN_OK) return rc;
   if (!any) return GDN_OK;
-
-  const WinDims w = win_dims(d);
-  const RecLayout L = rec_layout(d);
-  char* rb = (char*)records;
-  float* rk = (float*)(rb + L.k);
-  float* ru = (float*)(rb + L.u);
-  float2* ra = (float2*)(rb + L.scale);
-  hipStream_t st = (hipStream_t)stream;
-  const int l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
-  hipError_t e;
-  if (in_dtype == GDN_BF16) {
-    e = dbg_states
-            ? launch_verify_d<true, uint16_t>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states, scale, l2, st)
-            : launch_verify_d<false, uint16_t>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, nullptr, scale, l2, st);
-  } else {
-    e = dbg_states
-            ? launch_verify_d<true, float>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states, scale, l2, st)
-            : launch_verify_d<false, float>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, nullptr, scale, l2, st);
-  }
+  PrevRecords none;
+  memset(&none, 0, sizeof(none));
+  hipError_t e = launch_verify<false>(win_dims(*dims), tl, in_dtype, a, none,
+                                      (hipStream_t)stream);
   return hip_status(e, "gdn_verify launch");
 }
 
@@ -677,21 +871,9 @@ extern "C" int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
     return fail(GDN_EINVAL, "gdn_commit: misaligned pointer");
   const gdn_dims& d = *dims;
   CommitTable ct;
-  memset(&ct, 0, sizeof(ct));
-  int n_act = 0;
-  for (int n = 0; n < d.n_lanes; ++n) {
-    if (t_lane[n] < 0 || t_lane[n] > d.t_max)
-      return fail(GDN_EINVAL, "gdn_commit: t_lane out of 0..t_max");
-    if (m_lane[n] < 0 || m_lane[n] > t_lane[n])
-      return fail(GDN_EINVAL, "gdn_commit: m_lane out of 0..t_lane");
-    if (m_lane[n] > 0) {
-      ct.lane[n_act] = (uint8_t)n;
-      ct.m[n_act] = (uint8_t)m_lane[n];
-      ++n_act;
-    }
-  }
-  if (n_act == 0) return GDN_OK;
-  ct.n_act = n_act;
+  rc = commit_lanes("gdn_commit", d, m_lane, t_lane, ct);
+  if (rc != GDN_OK) return rc;
+  if (ct.n_act == 0) return GDN_OK;
   const WinDims w = win_dims(d);
   const RecLayout L = rec_layout(d);
   const char* rb = (const char*)records;
@@ -699,7 +881,7 @@ extern "C" int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
   const float* ru = (const float*)(rb + L.u);
   const float2* ra = (const float2*)(rb + L.scale);
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(d.n_layers * n_act * d.h_v * w.ncb);
+  const dim3 grid(d.n_layers * ct.n_act * d.h_v * w.ncb);
   hipError_t e;
   switch (d.d_k) {
     case 16: e = launch(commit_kernel<16>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
@@ -708,6 +890,51 @@ extern "C" int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
     default: e = launch(commit_kernel<128>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
   }
   return hip_status(e, "gdn_commit launch");
+}
+
+extern "C" int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
+                                 const int32_t* t_prev,
+                                 const void* records_prev,
+                                 const int32_t* t_lane, const void* q,
+                                 const void* k, const void* v, int in_dtype,
+                                 const float* beta, const float* g, float* S,
+                                 float* o, void* records, float* dbg_states,
+                                 float scale, int flags, void* stream) {
+  LaneTable tl;
+  VerifyArgs a;
+  int any = 0;
+  int rc = verify_setup("gdn_commit_verify", dims, t_lane, q, k, v, in_dtype,
+                        beta, g, S, o, records, dbg_states, scale, flags, tl,
+                        a, &any);
+  if (rc != GDN_OK) return rc;
+  if (!m_prev || !t_prev)
+    return fail(GDN_EINVAL, "gdn_commit_verify: required pointer is NULL");
+  const gdn_dims& d = *dims;
+  CommitTable ct;
+  rc = commit_lanes("gdn_commit_verify", d, m_prev, t_prev, ct);
+  if (rc != GDN_OK) return rc;
+  PrevRecords pr;
+  memset(&pr, 0, sizeof(pr));
+  if (ct.n_act > 0) {
+    if (!records_prev)
+      return fail(GDN_EINVAL, "gdn_commit_verify: records_prev is NULL");
+    if (misaligned(records_prev, 256))
+      return fail(GDN_EINVAL, "gdn_commit_verify: misaligned pointer");
+    const RecLayout L = rec_layout(d);
+    const char* p0 = (const char*)records_prev;
+    const char* p1 = (const char*)records;
+    if (p0 < p1 + L.total && p1 < p0 + L.total)
+      return fail(GDN_EINVAL,
+                  "gdn_commit_verify: records and records_prev overlap");
+    pr.k = (const float*)(p0 + L.k);
+    pr.u = (const float*)(p0 + L.u);
+    pr.scale = (const float2*)(p0 + L.scale);
+    for (int n = 0; n < d.n_lanes; ++n) pr.m.v[n] = (uint8_t)m_prev[n];
+  }
+  if (!any && ct.n_act == 0) return GDN_OK;
+  hipError_t e = launch_verify<true>(win_dims(d), tl, in_dtype, a, pr,
+                                     (hipStream_t)stream);
+  return hip_status(e, "gdn_commit_verify launch");
 }
 
 extern "C" const char* gdn_strerror(int status) {

@@ -1,7 +1,7 @@
 /*
  * gdn.h -- C ABI of the MI355X (gfx950) gated-delta speculative-decoding path.
  *
- * Three operations, all asynchronous on the caller's HIP stream:
+ * Four operations, all asynchronous on the caller's HIP stream:
  *
  *   gdn_verify           advance every (layer, lane, value head) recurrent
  *                        state S0 over a draft window of T <= t_max tokens by
@@ -10,6 +10,9 @@
  *                        is never written.
  *   gdn_commit           ReplaySSM commit: replay the first m records of each
  *                        lane from the untouched S0 and store S_m in place.
+ *   gdn_commit_verify    both in one launch: commit the previous window's
+ *                        accepted prefix, then verify the next window from
+ *                        the committed state without reading it again.
  *   gdn_prefill_chunked  run the same recurrence over a long sequence in
  *                        chunks and emit fp32 state checkpoints at every
  *                        multiple of the checkpoint interval.
@@ -143,6 +146,37 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
 int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
                const int32_t* t_lane, const void* records, float* S,
                void* stream);
+
+/*
+ * Fused commit + verify: the ReplaySSM commit of the previous window
+ * followed by the verify of the next one, in one launch.  Equivalent, bit
+ * for bit in S, o and records, to
+ *   gdn_commit(dims, m_prev, t_prev, records_prev, S, stream);
+ *   gdn_verify(dims, t_lane, q, k, v, in_dtype, beta, g, S, o, records,
+ *              dbg_states, scale, flags, stream);
+ * but the committed state S_m is passed from the replay to the new window in
+ * registers, so the state is read once and written once per round instead of
+ * read twice and written once (the commit mechanism of the ReplaySSM section,
+ * with verify's separate read of S0 removed).
+ *   m_prev, t_prev  host int32[n_lanes]: the previous window's accepted
+ *                   prefix (0..t_prev) and length; m_prev = 0 leaves the
+ *                   lane's S as it is
+ *   records_prev    device, the previous gdn_verify / gdn_commit_verify
+ *                   records (may be NULL when every m_prev is 0); must not
+ *                   overlap records
+ *   S               device f32, in: the previous window's S0, out: S_m
+ *                   (the new window's S0, never advanced by the new window)
+ *   other arguments as for gdn_verify.  A lane with t_lane = 0 and
+ *   m_prev > 0 is committed only.
+ * Errors: those of gdn_commit and gdn_verify, and GDN_EINVAL when the two
+ * record buffers overlap.
+ */
+int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
+                      const int32_t* t_prev, const void* records_prev,
+                      const int32_t* t_lane, const void* q, const void* k,
+                      const void* v, int in_dtype, const float* beta,
+                      const float* g, float* S, float* o, void* records,
+                      float* dbg_states, float scale, int flags, void* stream);
 
 /*
  * Workspace bytes that gdn_prefill_chunked needs for these sizes (0 for

@@ -45,9 +45,10 @@ def test_records_bytes():
     d = _dims()
     n = gdn.records_bytes(d)
     ntok = 1 * 2 * 8
-    # raw key rows (f32 [h_k][d_k]) + ut (f32 [h_v][d_v]) + alpha (f32 [h_v])
-    assert n >= ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 4)
-    assert n < ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 4) + 3 * 256
+    # raw key rows (f32 [h_k][d_k]) + ut (f32 [h_v][d_v]) + (fold, c)
+    # (float2 [h_v])
+    assert n >= ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 8)
+    assert n < ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 8) + 3 * 256
     assert n % 256 == 0
     assert gdn.records_bytes(_dims(d_k=24)) == 0
     assert gdn.records_bytes(_dims(h_v=3)) == 0
@@ -124,6 +125,38 @@ def test_commit_rejects_bad_arguments_on_host():
     assert c([1, 0], [2, 1], S=_Fake(gdn.GDN_F32, addr=(1 << 20) + 1)) == gdn.GDN_EINVAL
     # every m = 0: a cancelled round, nothing is launched
     assert c([0, 0], [2, 1]) == gdn.GDN_OK
+
+
+def _commit_verify(d, m_prev, t_prev, t_lane, **over):
+    a = dict(rec_prev=_Fake(gdn.GDN_F32, addr=1 << 30), q=_Fake(), k=_Fake(),
+             v=_Fake(), beta=_Fake(gdn.GDN_F32), g=_Fake(gdn.GDN_F32),
+             S=_Fake(gdn.GDN_F32), o=_Fake(gdn.GDN_F32),
+             rec=_Fake(gdn.GDN_F32))
+    a.update(over)
+    return gdn.commit_verify(d, m_prev, t_prev, a["rec_prev"], t_lane, a["q"],
+                             a["k"], a["v"], a["beta"], a["g"], a["S"],
+                             a["o"], a["rec"], stream=0, raw_status=True)
+
+
+def test_commit_verify_rejects_bad_arguments_on_host():
+    d = _dims()
+    cv = _commit_verify
+    assert cv(d, [3, 1], [2, 1], [1, 1]) == gdn.GDN_EINVAL    # m > t_prev
+    assert cv(d, [0, 0], [9, 1], [1, 1]) == gdn.GDN_EINVAL    # t_prev > t_max
+    assert cv(d, [0, 0], [2, 1], [9, 1]) == gdn.GDN_EINVAL    # T > t_max
+    assert cv(_dims(d_k=24), [0, 0], [2, 1], [1, 1]) == gdn.GDN_EUNSUPPORTED
+    assert cv(d, [1, 0], [2, 1], [1, 1], rec_prev=None) == gdn.GDN_EINVAL
+    assert cv(d, [1, 0], [2, 1], [1, 1], q=None) == gdn.GDN_EINVAL
+    assert cv(d, [1, 0], [2, 1], [1, 1],
+              rec_prev=_Fake(gdn.GDN_F32, addr=(1 << 30) + 8)) == gdn.GDN_EINVAL
+    # the two record buffers overlap
+    n = gdn.records_bytes(d)
+    assert cv(d, [1, 0], [2, 1], [1, 1],
+              rec_prev=_Fake(gdn.GDN_F32, addr=(1 << 20) + 256 * (n // 512))
+              ) == gdn.GDN_EINVAL
+    assert "overlap" in gdn.lib.gdn_last_error().decode()
+    # nothing to commit or verify: no launch
+    assert cv(d, [0, 0], [2, 1], [0, 0], rec_prev=None) == gdn.GDN_OK
 
 
 def test_binding_checks_lane_count():
