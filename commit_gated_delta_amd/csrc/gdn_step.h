@@ -11,13 +11,14 @@
 // output) instead of four.  When c leaves [2^-32, 2^32] -- after many small
 // decays, or alpha = 0 exactly -- it is folded into St (St <- c * St, c <- 1)
 // before the token is applied.  Verify takes these decisions and records,
-// per token, the fold factor (0 when none) and the scale after the token;
+// per token, the fold factor (1 when none; a real fold factor is never 1,
+// and alpha = 0 folds by 0) and the scale after the token;
 // commit replays the recorded values instead of recomputing them.  The
 // explicit state is materialised as S = c * St (one rounded product per
 // element).
 //
 // Verify and commit both run exactly these functions, in the same token
-// order, on the same recorded (fold, c, ut, k) values, so the state that
+// order, on the same recorded (phi, c, ut, k) values, so the state that
 // commit(m) stores is bit-for-bit the state verify held after token m: the
 // "transitions equal in finite precision" requirement of the ReplaySSM
 // section of the NInfer technical review (blog.123qwe.co.kr post 4624).

@@ -20,11 +20,12 @@
 //   ut_i  = (beta * (v_i - p_i)) * (rk / c)     (= u_i * rk / c)
 //   St_ij <- fma(ut_i, k_j, St_ij)              (S = alpha S + u khat^T)
 //   o_i   = (scale * rq * c) * sum_j St_ij q_j
-// Records per token: per value head the scale step (fold, c) as a float2,
-// ut (f32 per value head and column) and the raw key row widened to f32 (per
-// key head).  Commit replays the same folds and St_ij <- fma(ut_i, k_j,
-// St_ij) from exactly these values and stores S_m = c * St, so its result is
-// bitwise the state verify held after the same token.
+// Records per token: per value head the scale step (phi, c) as a float2 --
+// phi the factor folded into St before the token (1 when none), c the scale
+// after it -- ut (f32 per value head and column) and the raw key row widened
+// to f32 (per key head).  Commit replays the same folds and St_ij <-
+// fma(ut_i, k_j, St_ij) from exactly these values and stores S_m = c * St, so
+// its result is bitwise the state verify held after the same token.
 //
 // Work decomposition (CDNA4, wave64):
 //   One 256-thread workgroup per (layer, lane, value head, block of 64 value
@@ -193,12 +194,13 @@ __device__ __forceinline__ float inv_norm(float ss) {
 //   f3 = scale * rq_t * c_t   (output:      o = f3 * (sum_j St_ij q_j
 //                                                     + ut * (k_t . q_t)),
 //                              St before the write: S_t q = c_t (St + ut k^T) q)
-//   fold = c_{t-1} * alpha_t when the scale is folded into St at token t
-//          (then c_t = 1), else 0
-// c_t (the scale after token t) and fold are recorded for commit, which
+//   phi = c_{t-1} * alpha_t when the scale is folded into St at token t
+//         (then c_t = 1), else 1 (a fold factor is never 1: a fold happens
+//         only when the product leaves [2^-32, 2^32]; alpha = 0 folds by 0)
+// c_t (the scale after token t) and phi are recorded for commit, which
 // replays them instead of recomputing the scale sequence.
 struct StepScalars {
-  float f1, f2, f3, fold;
+  float f1, f2, f3, phi;
   float beta, c, kq, pad;  // kq = k_t . q_t (raw rows)
 };
 
@@ -283,7 +285,7 @@ __device__ __forceinline__ float replay(float (&s)[R], const float* __restrict__
     const float ut_n = u0[nt * vo_step + (uint32_t)ic];
     RowWords<float, R> kw_n;
     kw_n.load(k0 + nt * kq_step, j0);
-    if (fc.x != 0.f) fold_scale<R>(s, fc.x);
+    if (fc.x != 1.f) fold_scale<R>(s, fc.x);
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = state_update(s[r], ut, kw.at(r));
     c = fc.y;
@@ -300,7 +302,7 @@ struct ReplayStage {
   static constexpr int kTok = 16;
   float k[kTok][DK];     // raw key rows (this workgroup's key head)
   float u[kTok][kWave];  // ut of this workgroup's 64 columns
-  float2 sc[kTok];       // (fold, c)
+  float2 sc[kTok];       // (phi, c)
 };
 
 // The replay of the fused commit + verify.  The whole workgroup first loads
@@ -352,9 +354,9 @@ __device__ __forceinline__ float replay_staged(
     __syncthreads();
     for (int t = 0; t < nb; ++t) {
       const float2 fc = st.sc[t];
-      const float fold = __int_as_float(
+      const float phi = __int_as_float(
           __builtin_amdgcn_readfirstlane(__float_as_int(fc.x)));
-      if (fold != 0.f) fold_scale<R>(s, fold);
+      if (phi != 1.f) fold_scale<R>(s, phi);
       const float ut = st.u[t][x];
       const float4* kr = reinterpret_cast<const float4*>(&st.k[t][j0]);
 #pragma unroll
@@ -488,7 +490,7 @@ void verify_kernel(
       if (x >= off) c *= y;
     }
     const bool out = !(c >= kScaleLo && c <= kScaleHi);
-    float fold = 0.f;
+    float phi = 1.f;
     if (__builtin_amdgcn_ballot_w64(out && x < T) != 0) {
       // sequential walk with folds (lane 0), results spread back by lane
       __shared__ float seq_c[GDN_MAX_T], seq_f[GDN_MAX_T], seq_a[GDN_MAX_T];
@@ -497,7 +499,7 @@ void verify_kernel(
       if (x == 0) {
         float cc = 1.0f;
         for (int t = 0; t < T; ++t) {
-          float cn, fo = 0.f;
+          float cn, fo = 1.f;
           if (scale_step(cc, seq_a[t], cn)) {
             fo = cn;
             cn = 1.0f;
@@ -510,7 +512,7 @@ void verify_kernel(
       __builtin_amdgcn_wave_barrier();
       if (x < T) {
         c = seq_c[x];
-        fold = seq_f[x];
+        phi = seq_f[x];
       }
     }
     if (x < T) {
@@ -519,13 +521,13 @@ void verify_kernel(
       z.f1 = c * rk;
       z.f2 = rk * __builtin_amdgcn_rcpf(c);
       z.f3 = scale * rq * c;
-      z.fold = fold;
+      z.phi = phi;
       z.beta = b_t;
       z.c = c;
       z.kq = nrm[2][x];
       z.pad = 0.f;
       sc[x] = z;
-      if (cb == 0) rec_scale[gi] = make_float2(fold, c);
+      if (cb == 0) rec_scale[gi] = make_float2(phi, c);
     }
   }
   __syncthreads();
@@ -541,7 +543,7 @@ void verify_kernel(
     const int buf = t & 1;
     const float vi = load_in(v0 + t * vo_step, (uint32_t)ic);
     const StepScalars z = sc[t];
-    if (z.fold != 0.f) fold_scale<R>(s, z.fold);
+    if (z.phi != 1.f) fold_scale<R>(s, z.phi);
 
     float kv[R];
     float a0 = 0.f, b0 = 0.f;

@@ -102,8 +102,9 @@ typedef struct {
  * Record contents (the "compact records that caused the transitions" of the
  * ReplaySSM section): per (layer, lane, token) the raw key rows widened to
  * f32 (f32 [h_k][d_k]); per value head the decay in scaled form, a float2
- * (fold, c) where c is the running state scale after this token and fold
- * the factor applied to the stored state before it (1 when none); and the
+ * (phi, c) where c is the running state scale after this token and phi
+ * the factor folded into the stored state before it (1 when none, 0 when
+ * alpha_t = 0); and the
  * delta vectors with key norm and scale folded in,
  * u_t / (sqrt(|k_t|^2 + 1e-6) * c) (f32 [h_v][d_v]).  About 24.8 KB per
  * token per lane-layer at 32/16 heads of dim 128, against 2 MiB for a full

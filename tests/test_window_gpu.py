@@ -166,6 +166,70 @@ def test_idle_lane_and_zero_accept():
     assert np.array_equal(S1[:, 2], dbg.cpu().numpy()[:, 2, 1])
 
 
+FOLD_CASES = [
+    # (name, dk, dv, bf16): the matrix-core readout (bf16, d_k >= 32) and
+    # the general loop (f32 inputs, d_k = 16)
+    ("bf16_d128", 128, 128, True),
+    ("bf16_d64", 64, 96, True),
+    ("f32_d32", 32, 64, False),
+    ("f32_d16", 16, 16, False),
+]
+
+
+def _fold_check(name, dk, dv, bf16, g_fill):
+    shape = gs.WindowShape(1, 3, 4, 2, dk, dv, 16)
+    key = (104, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, t_lane=[16, 13, 7])
+    g_fill(w.g)
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    o_np, dbg_np = o.cpu().numpy(), dbg.cpu().numpy()
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, st_ref = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane,
+                                  want_states=True)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    say("  %s: o err %.2e" % (name, e_o))
+    assert e_o <= TOL
+    for t in range(16):
+        lanes = [n for n in range(3) if w.t_lane[n] > t]
+        assert s_rel_err(dbg_np[:, lanes, t], st_ref[:, lanes, t]) <= TOL, t
+    for m in (1, 4, 5, 12, 16):
+        m_lane = np.minimum(m, w.t_lane)
+        S_c = to_dev(S0, torch)
+        gdn.commit(dims, m_lane, w.t_lane, rec, S_c)
+        S_c = S_c.cpu().numpy()
+        for n in range(3):
+            assert np.array_equal(S_c[:, n], dbg_np[:, n, m_lane[n] - 1]), (m, n)
+
+
+@pytest.mark.parametrize("case", FOLD_CASES, ids=[c[0] for c in FOLD_CASES])
+def test_zero_decay_tokens(case):
+    """alpha = 0 exactly (g = -inf, and g = -200, which underflows in f32):
+    the state is forgotten at that token (a fold by factor 0)."""
+    name, dk, dv, bf16 = case
+
+    def fill(g):
+        g[:, :, 3] = -np.inf
+        g[:, :, 9, ::2] = -200.0
+        g[:, 1, 12] = -np.inf
+
+    _fold_check("zero_" + name, dk, dv, bf16, fill)
+
+
+@pytest.mark.parametrize("case", FOLD_CASES, ids=[c[0] for c in FOLD_CASES])
+def test_strong_decay_folds(case):
+    """g = -3 at every token: the scale leaves [2^-32, 2^32] every ~11
+    tokens, so windows fold once or twice at head-dependent tokens."""
+    name, dk, dv, bf16 = case
+
+    def fill(g):
+        g[:] = -3.0 - 0.5 * np.arange(g.shape[-1])[None, None, None, :]
+
+    _fold_check("decay_" + name, dk, dv, bf16, fill)
+
+
 def test_config0_tiny_case():
     """1 lane, 1 layer, 2 heads, d = 16, T = 4, f32 inputs; m ~ U{0..4}."""
     shape = gs.config_shape(0)
