@@ -186,6 +186,46 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
             "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
 
 
+def bench_snapshot(reps=5):
+    """Snapshot of the whole 8-lane, 48-layer state (768 MiB) to a device
+    buffer and to pinned host memory, and the restore from pinned memory:
+    gdn_state_snapshot / gdn_state_restore, event-timed."""
+    import torch
+    import commit_gated_delta_amd as gdn
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
+    lanes = list(range(N))
+    S = torch.randn((NL, N, HV, DK, DV), device="cuda")
+    dev_snap = torch.empty((N, NL, HV, DK, DV), device="cuda")
+    host_snap = torch.empty((N, NL, HV, DK, DV), pin_memory=True)
+    stream = torch.cuda.current_stream()
+    nbytes = S.numel() * 4
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    d2d = timed(lambda: gdn.state_snapshot(dims, lanes, S, dev_snap, stream=stream))
+    d2h = timed(lambda: gdn.state_snapshot(dims, lanes, S, host_snap, stream=stream))
+    h2d = timed(lambda: gdn.state_restore(dims, lanes, host_snap, S, stream=stream))
+    return {"workload": "state of 8 lanes x 48 layers x 32 heads x 128 x 128 "
+                        "f32 (768 MiB)",
+            "bytes": nbytes,
+            "device_ms": d2d, "device_GBps": 2 * nbytes / (d2d * 1e-3) / 1e9,
+            "device_hbm_frac": 2 * nbytes / (d2d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "to_pinned_host_ms": d2h,
+            "to_pinned_host_GBps": nbytes / (d2h * 1e-3) / 1e9,
+            "from_pinned_host_ms": h2d,
+            "from_pinned_host_GBps": nbytes / (h2d * 1e-3) / 1e9}
+
+
 def cpu_baseline(rounds=16):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: `rounds` chained rounds (verify + commit) of the full
@@ -223,6 +263,7 @@ def main():
                     default="both",
                     help="which way of running a round to time (the fused "
                          "one is the headline when timed)")
+    ap.add_argument("--no-snapshot", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -404,6 +445,8 @@ def main():
     }
     if not args.no_prefill:
         out["prefill"] = bench_prefill()
+    if not args.no_snapshot:
+        out["state_snapshot"] = bench_snapshot()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

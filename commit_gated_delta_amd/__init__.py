@@ -24,7 +24,8 @@ GDN_MAX_LANES = 256
 GDN_MAX_T = 64
 
 EXPORTED = ("gdn_records_bytes", "gdn_verify", "gdn_commit",
-            "gdn_commit_verify", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+            "gdn_commit_verify", "gdn_state_snapshot", "gdn_state_restore",
+            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_strerror", "gdn_last_error")
 
 
@@ -72,6 +73,9 @@ def _load_library():
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, f,
                                       ctypes.c_int, vp]
     lib.gdn_commit_verify.restype = ctypes.c_int
+    for fn in (lib.gdn_state_snapshot, lib.gdn_state_restore):
+        fn.argtypes = [dp, i32, ip, vp, vp, vp]
+        fn.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [i32] * 6
     lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_prefill_chunked.argtypes = [i32] * 7 + [vp] * 3 + [ctypes.c_int] + [
@@ -173,6 +177,34 @@ def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
     if raw_status:
         return st
     _check(st, "gdn_commit_verify")
+
+
+def _lane_list(lanes):
+    vals = [int(x) for x in lanes]
+    return len(vals), (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+def state_snapshot(dims: Dims, lanes, S, snapshot, stream=None,
+                   raw_status=False):
+    """gdn_state_snapshot: snapshot[j] = S[:, lanes[j]] (device or pinned
+    host tensor)."""
+    n, arr = _lane_list(lanes)
+    st = lib.gdn_state_snapshot(ctypes.byref(dims), n, arr, _ptr(S),
+                                _ptr(snapshot), _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_state_snapshot")
+
+
+def state_restore(dims: Dims, lanes, snapshot, S, stream=None,
+                  raw_status=False):
+    """gdn_state_restore: S[:, lanes[j]] = snapshot[j]."""
+    n, arr = _lane_list(lanes)
+    st = lib.gdn_state_restore(ctypes.byref(dims), n, arr, _ptr(snapshot),
+                               _ptr(S), _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_state_restore")
 
 
 def prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k, d_v) -> int:

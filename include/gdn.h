@@ -1,7 +1,7 @@
 /*
  * gdn.h -- C ABI of the MI355X (gfx950) gated-delta speculative-decoding path.
  *
- * Four operations, all asynchronous on the caller's HIP stream:
+ * The operations, all asynchronous on the caller's HIP stream:
  *
  *   gdn_verify           advance every (layer, lane, value head) recurrent
  *                        state S0 over a draft window of T <= t_max tokens by
@@ -13,6 +13,9 @@
  *   gdn_commit_verify    both in one launch: commit the previous window's
  *                        accepted prefix, then verify the next window from
  *                        the committed state without reading it again.
+ *   gdn_state_snapshot,  copy the recurrent state of chosen lanes out to a
+ *   gdn_state_restore    compact snapshot (device or pinned host memory) and
+ *                        back, for requests that are paused and resumed.
  *   gdn_prefill_chunked  run the same recurrence over a long sequence in
  *                        chunks and emit fp32 state checkpoints at every
  *                        multiple of the checkpoint interval.
@@ -224,6 +227,32 @@ int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
                         const float* g, const float* S_init, float* S_final,
                         float* o, float* checkpoints, void* workspace,
                         size_t ws_bytes, float scale, int flags, void* stream);
+
+/*
+ * Recurrent-state snapshot and restore.  Under memory pressure the review's
+ * engine pauses active requests and brings them back by replay or from a
+ * snapshot, with a pinned host budget for such context (NInfer technical
+ * review, section "Architecture 2: context byte pool and prefix reuse").
+ * gdn_state_snapshot gathers the f32 state of n_sel lanes into a compact
+ * lane-major snapshot; gdn_state_restore scatters a snapshot into lanes
+ * (any lanes: a paused request may resume in another lane).  Exact copies.
+ *   dims      as for gdn_verify (t_max and h_k are not used)
+ *   n_sel     0..n_lanes lanes to copy (0: nothing is launched)
+ *   lanes     host int32[n_sel], each in 0..n_lanes-1; restore rejects a
+ *             lane listed twice
+ *   S         device f32 [n_layers][n_lanes][h_v][d_k][d_v] (16-byte aligned)
+ *   snapshot  f32 [n_sel][n_layers][h_v][d_k][d_v], device memory or pinned
+ *             host memory (hipHostMalloc), 16-byte aligned; entry j holds
+ *             lane lanes[j]
+ * Errors: GDN_EINVAL for bad sizes, indices or pointers, GDN_EUNSUPPORTED
+ * when h_v*d_k*d_v is not a multiple of 4, GDN_EHIP when the launch fails.
+ */
+int gdn_state_snapshot(const gdn_dims* dims, int32_t n_sel,
+                       const int32_t* lanes, const float* S, float* snapshot,
+                       void* stream);
+int gdn_state_restore(const gdn_dims* dims, int32_t n_sel,
+                      const int32_t* lanes, const float* snapshot, float* S,
+                      void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* gdn_strerror(int status);

@@ -17,7 +17,10 @@ What is computed (see the C file for the passage-by-passage account):
     after the first m window steps from the untouched S_0;
   * prefill over a whole sequence with a state copy at every multiple of the
     checkpoint interval (same review, section "Architecture 2", the
-    context_cache.checkpoint_interval setting).
+    context_cache.checkpoint_interval setting);
+  * snapshot / restore of the recurrent state of chosen lanes (same section:
+    paused requests come back by replay or from a snapshot) -- exact copies,
+    written here as numpy indexing.
 
 Pins: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, exact-rational brute force,
@@ -183,3 +186,25 @@ def prefill(q, k, v, beta, g, S_init=None, ckpt_interval=8192, scale=1.0,
     if rc != 0:
         raise ValueError("oracle_prefill failed: %d" % rc)
     return o, ck, Sf
+
+
+def snapshot(S, lanes):
+    """Snapshot of the recurrent state of the chosen lanes (NInfer technical
+    review, "Architecture 2": paused requests resume from a snapshot).
+    S [NL, N, Hv, dk, dv]; returns [len(lanes), NL, Hv, dk, dv] with entry j
+    the state of lane lanes[j] in every layer -- an exact copy."""
+    S = np.asarray(S)
+    return np.stack([S[:, int(n)] for n in lanes]) if len(lanes) else \
+        np.zeros((0,) + S.shape[:1] + S.shape[2:], S.dtype)
+
+
+def restore(S, lanes, snap):
+    """Inverse of snapshot: a copy of S with lane lanes[j] replaced by
+    snap[j] in every layer.  A lane may not be listed twice."""
+    lanes = [int(n) for n in lanes]
+    if len(set(lanes)) != len(lanes):
+        raise ValueError("a lane is restored twice")
+    out = np.array(S, copy=True)
+    for j, n in enumerate(lanes):
+        out[:, n] = snap[j]
+    return out

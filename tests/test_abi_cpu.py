@@ -159,6 +159,24 @@ def test_commit_verify_rejects_bad_arguments_on_host():
     assert cv(d, [0, 0], [2, 1], [0, 0], rec_prev=None) == gdn.GDN_OK
 
 
+def test_state_copy_rejects_bad_arguments_on_host():
+    d = _dims(n_lanes=4)
+    S, snap = _Fake(gdn.GDN_F32), _Fake(gdn.GDN_F32, addr=1 << 30)
+    for fn in (gdn.state_snapshot, gdn.state_restore):
+        assert fn(d, [0, 4], S, snap, stream=0, raw_status=True) == gdn.GDN_EINVAL
+        assert fn(d, [-1], S, snap, stream=0, raw_status=True) == gdn.GDN_EINVAL
+        assert fn(d, [0, 1, 2, 3, 0], S, snap, stream=0,
+                  raw_status=True) == gdn.GDN_EINVAL            # n_sel > n_lanes
+        assert fn(d, [1], None, snap, stream=0, raw_status=True) == gdn.GDN_EINVAL
+        assert fn(d, [1], S, _Fake(gdn.GDN_F32, addr=(1 << 30) + 8), stream=0,
+                  raw_status=True) == gdn.GDN_EINVAL            # alignment
+        assert fn(d, [], S, snap, stream=0, raw_status=True) == gdn.GDN_OK
+    # restoring one lane twice would race
+    assert gdn.state_restore(d, [2, 2], snap, S, stream=0,
+                             raw_status=True) == gdn.GDN_EINVAL
+    assert "twice" in gdn.lib.gdn_last_error().decode()
+
+
 def test_binding_checks_lane_count():
     with pytest.raises(ValueError):
         _verify(_dims(), [1, 1, 1])

@@ -16,6 +16,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+import gdn_synth as gs
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -361,3 +362,54 @@ def test_rejects_bad_arguments():
         oracle.verify(q, k, v, beta, g, S0, [4])
     with pytest.raises(ValueError):
         oracle.commit(q, k, v, beta, g, S0, [-1])
+
+
+# --------------------------------------------------------------- snapshot
+def test_snapshot_restore_definition_by_loops():
+    """snapshot / restore against element-by-element loops on a tiny state,
+    and the round trip: restoring a snapshot into other lanes moves those
+    requests; restoring into the same lanes is the identity."""
+    rng = np.random.default_rng(5)
+    NL, N, Hv, dk, dv = 2, 4, 3, 2, 3
+    S = rng.standard_normal((NL, N, Hv, dk, dv))
+    lanes = [2, 0, 2]
+    snap = oracle.snapshot(S, lanes)
+    assert snap.shape == (3, NL, Hv, dk, dv)
+    for j, n in enumerate(lanes):
+        for l in range(NL):
+            for h in range(Hv):
+                for a in range(dk):
+                    for b in range(dv):
+                        assert snap[j, l, h, a, b] == S[l, n, h, a, b]
+    # identity round trip
+    assert np.array_equal(oracle.restore(S, [1, 3], oracle.snapshot(S, [1, 3])), S)
+    # move lane 1 into lane 3 and lane 3 into lane 1
+    swapped = oracle.restore(S, [3, 1], oracle.snapshot(S, [1, 3]))
+    for l in range(NL):
+        assert np.array_equal(swapped[l, 3], S[l, 1])
+        assert np.array_equal(swapped[l, 1], S[l, 3])
+        assert np.array_equal(swapped[l, 0], S[l, 0])
+    with pytest.raises(ValueError):
+        oracle.restore(S, [1, 1], oracle.snapshot(S, [1, 2]))
+
+
+def test_resume_from_snapshot_continues_the_chain():
+    """A request paused after a round and resumed in another lane from its
+    snapshot continues exactly as if it had not moved (the rule reads only
+    the lane's own state)."""
+    NL, N, Hv, Hk, dk, dv, T = 1, 3, 2, 1, 4, 3, 3
+    shape = gs.WindowShape(NL, N, Hv, Hk, dk, dv, T)
+    w = gs.window_inputs(shape, (77,), bf16=False)
+    S0 = gs.initial_state(shape, (77,)).astype(np.float64)
+    q, k, v, b, g = w.as_f64()
+    S1 = oracle.commit(q, k, v, b, g, S0, [3, 2, 1])
+    snap = oracle.snapshot(S1, [0])
+    moved = oracle.restore(S1, [2], snap)
+    w2 = gs.window_inputs(shape, (78,), bf16=False)
+    q2, k2, v2, b2, g2 = w2.as_f64()
+    # lane 0's next window, given to lane 2 after the move
+    for arr in (q2, k2, v2, b2, g2):
+        arr[:, 2] = arr[:, 0]
+    o_a, _ = oracle.verify(q2, k2, v2, b2, g2, S1, [3, 3, 3])
+    o_b, _ = oracle.verify(q2, k2, v2, b2, g2, moved, [3, 3, 3])
+    assert np.array_equal(o_a[:, 0], o_b[:, 2])
