@@ -198,3 +198,52 @@ def config_shape(cfg: int) -> WindowShape:
     if cfg == 3:
         return WindowShape(48, 12, 32, 16, 128, 128, 6)
     raise ValueError(cfg)
+
+
+# ------------------------------------------------------------- draft trees
+_STREAM_TREE = 9
+
+
+def tree_parents(t_lane, t_max: int, key: tuple, p_deeper: float = 0.6):
+    """Random draft trees, one per lane, in depth-first preorder: node 0 is
+    the root (parent -1); every later node's parent is the previous node
+    (probability p_deeper) or an ancestor of it on the current path.
+    Returns int32 [n_lanes, t_max]; entries past t_lane are -1."""
+    r = rng(_STREAM_TREE, *key)
+    out = np.full((len(t_lane), t_max), -1, dtype=np.int32)
+    for n, T in enumerate(t_lane):
+        stack = []  # path from the root to the previous node
+        for t in range(int(T)):
+            if t == 0:
+                out[n, t] = -1
+                stack = [0]
+                continue
+            if r.random() < p_deeper:
+                par = stack[-1]
+            else:
+                par = stack[int(r.integers(0, len(stack)))]
+            while stack[-1] != par:
+                stack.pop()
+            out[n, t] = par
+            stack.append(t)
+    return out
+
+
+def tree_path(parent_row, node: int):
+    """Nodes from the root to ``node`` (inclusive), root first."""
+    path = []
+    while node >= 0:
+        path.append(int(node))
+        node = int(parent_row[node])
+    return path[::-1]
+
+
+def accepted_tree_paths(parent, t_lane, key: tuple):
+    """For each lane an accepted path: the root-to-node path of a uniformly
+    drawn node, or [] (nothing accepted) with probability 1/(T+1)."""
+    r = rng(_STREAM_TREE + 1, *key)
+    paths = []
+    for n, T in enumerate(t_lane):
+        node = int(r.integers(-1, int(T)))
+        paths.append([] if node < 0 else tree_path(parent[n], node))
+    return paths

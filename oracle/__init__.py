@@ -18,6 +18,9 @@ What is computed (see the C file for the passage-by-passage account):
   * prefill over a whole sequence with a state copy at every multiple of the
     checkpoint interval (same review, section "Architecture 2", the
     context_cache.checkpoint_interval setting);
+  * draft-tree windows (the first page: draft trees with DFlash2): node t
+    steps from its parent's state, and a commit replays an accepted
+    root-to-node path from S_0;
   * snapshot / restore of the recurrent state of chosen lanes (same section:
     paused requests come back by replay or from a snapshot) -- exact copies,
     written here as numpy indexing.
@@ -72,6 +75,11 @@ def _load():
         lib.oracle_verify.restype = i
         lib.oracle_commit.argtypes = [i] * 7 + [ip] + [dp] * 6 + [i]
         lib.oracle_commit.restype = i
+        lib.oracle_verify_tree.argtypes = [i] * 7 + [ip, ip] + [dp] * 6 + [
+            ctypes.c_double, i, dp, dp]
+        lib.oracle_verify_tree.restype = i
+        lib.oracle_commit_path.argtypes = [i] * 7 + [ip, ip] + [dp] * 6 + [i]
+        lib.oracle_commit_path.restype = i
         lib.oracle_prefill.argtypes = [i] * 6 + [dp] * 6 + [
             ctypes.c_double, i, dp, dp, dp]
         lib.oracle_prefill.restype = i
@@ -157,6 +165,55 @@ def commit(q, k, v, beta, g, S, m_lane, l2norm=True):
         int(bool(l2norm)))
     if rc != 0:
         raise ValueError("oracle_commit failed: %d" % rc)
+    return out
+
+
+def verify_tree(q, k, v, beta, g, S0, t_lane, parent, scale=1.0,
+                l2norm=True, want_states=False):
+    """Draft-tree verify.  Shapes as verify(); parent int [N, T] with
+    parent[n][t] in -1..t-1 (-1: the node steps from S0).  Returns
+    (o, states or None): node t's output and state after its own step."""
+    lib = _load()
+    NL, N, T, Hk, dk = q.shape
+    Hv, dv = v.shape[3], v.shape[4]
+    q, qp = _d(q); k, kp = _d(k); v, vp = _d(v)
+    beta, bp = _d(beta); g, gp = _d(g); S0, sp = _d(S0)
+    tl = np.ascontiguousarray(t_lane, dtype=np.int32)
+    pa = np.ascontiguousarray(parent, dtype=np.int32)
+    assert pa.shape == (N, T)
+    o = np.zeros((NL, N, T, Hv, dv))
+    states = np.zeros((NL, N, T, Hv, dk, dv)) if want_states else None
+    ip = ctypes.POINTER(ctypes.c_int32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_verify_tree(
+        NL, N, Hv, Hk, dk, dv, T, tl.ctypes.data_as(ip), pa.ctypes.data_as(ip),
+        qp, kp, vp, bp, gp, sp, float(scale), int(bool(l2norm)),
+        o.ctypes.data_as(dp), states.ctypes.data_as(dp) if want_states else None)
+    if rc != 0:
+        raise ValueError("oracle_verify_tree failed: %d" % rc)
+    return o, states
+
+
+def commit_path(q, k, v, beta, g, S, m_lane, path, l2norm=True):
+    """Commit of accepted paths: a new array, S advanced by the steps of
+    nodes path[n][0..m_lane[n]-1] of each lane's window, in that order."""
+    lib = _load()
+    NL, N, T, Hk, dk = q.shape
+    Hv, dv = v.shape[3], v.shape[4]
+    q, qp = _d(q); k, kp = _d(k); v, vp = _d(v)
+    beta, bp = _d(beta); g, gp = _d(g)
+    out = np.array(S, dtype=np.float64, copy=True, order="C")
+    ml = np.ascontiguousarray(m_lane, dtype=np.int32)
+    pa = np.zeros((N, T), dtype=np.int32)
+    for n in range(N):
+        pa[n, :int(ml[n])] = np.asarray(path[n][:int(ml[n])], dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    rc = lib.oracle_commit_path(
+        NL, N, Hv, Hk, dk, dv, T, ml.ctypes.data_as(ip), pa.ctypes.data_as(ip),
+        qp, kp, vp, bp, gp, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        int(bool(l2norm)))
+    if rc != 0:
+        raise ValueError("oracle_commit_path failed: %d" % rc)
     return out
 
 

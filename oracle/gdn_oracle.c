@@ -29,6 +29,13 @@
  *   leaves S_0 as it is.  The oracle reaches S_m by running the rule for m
  *   steps -- records are an implementation device and do not appear here.
  *
+ *   Draft trees (the first page, the description of the MC engine: draft
+ *   trees used together with DFlash2): the window is a tree of T nodes in
+ *   an order where every node comes after its parent; node t's state is one
+ *   step of the rule from its parent's state (from S_0 for the root), and a
+ *   commit of an accepted root-to-node path is the state after the steps of
+ *   the path's nodes, in order, from S_0.
+ *
  *   Chunked prefill (same review, section "Architecture 2: context byte pool
  *   and prefix reuse", the context_cache.checkpoint_interval setting): the
  *   oracle runs the same rule token by token over the whole sequence and
@@ -191,6 +198,118 @@ int oracle_commit(int n_layers, int n_lanes, int h_v, int h_k, int d_k,
       double* Sh = S + ((size_t)ll * h_v + h) * hs;
       for (int t = 0; t < m_lane[lane]; ++t) {
         const size_t tok = (size_t)ll * t_max + t;
+        l2_normalise(k + (tok * h_k + kh_idx) * d_k, d_k, l2norm, kh);
+        l2_normalise(q + (tok * h_k + kh_idx) * d_k, d_k, l2norm, qh);
+        gdr_step(d_k, d_v, Sh, kh, qh, v + (tok * h_v + h) * d_v,
+                 beta[tok * h_v + h], g[tok * h_v + h], 1.0, NULL, work);
+      }
+    }
+    free(kh); free(qh); free(work);
+  }
+  return bad ? -2 : 0;
+}
+
+/*
+ * Draft-tree verify, oracle form.  Layouts as oracle_verify; parent is
+ * int32 [n_lanes][t_max]: parent[t] in -1..t-1 (-1: the node hangs off S_0).
+ * Node t's state is one step of the rule applied to its parent's state;
+ * states (nullable) receives every node's state.
+ */
+int oracle_verify_tree(int n_layers, int n_lanes, int h_v, int h_k, int d_k,
+                       int d_v, int t_max, const int32_t* t_lane,
+                       const int32_t* parent, const double* q,
+                       const double* k, const double* v, const double* beta,
+                       const double* g, const double* S0, double scale,
+                       int l2norm, double* o, double* states) {
+  if (n_layers < 1 || n_lanes < 1 || h_v < 1 || h_k < 1 || d_k < 1 ||
+      d_v < 1 || t_max < 1 || h_v % h_k != 0)
+    return -1;
+  for (int n = 0; n < n_lanes; ++n) {
+    if (t_lane[n] < 0 || t_lane[n] > t_max) return -1;
+    for (int t = 0; t < t_lane[n]; ++t) {
+      const int p = parent[(size_t)n * t_max + t];
+      if (p < -1 || p >= t) return -1;
+    }
+  }
+  const int group = h_v / h_k;
+  const long n_chains = (long)n_layers * n_lanes * h_v;
+  const size_t hs = (size_t)d_k * d_v;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long c = 0; c < n_chains; ++c) {
+    const int h = (int)(c % h_v);
+    const int lane = (int)((c / h_v) % n_lanes);
+    const int layer = (int)(c / ((long)h_v * n_lanes));
+    const int kh_idx = h / group;
+    const long ll = (long)layer * n_lanes + lane;
+    double* node = (double*)malloc((size_t)t_max * hs * sizeof(double));
+    double* kh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* qh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* work = (double*)malloc((size_t)d_v * sizeof(double));
+    if (!node || !kh || !qh || !work) {
+      bad = 1;
+    } else {
+      for (int t = 0; t < t_lane[lane]; ++t) {
+        const int p = parent[(size_t)lane * t_max + t];
+        double* S = node + (size_t)t * hs;
+        memcpy(S, p < 0 ? S0 + ((size_t)ll * h_v + h) * hs
+                        : node + (size_t)p * hs, hs * sizeof(double));
+        const size_t tok = (size_t)ll * t_max + t;
+        l2_normalise(k + (tok * h_k + kh_idx) * d_k, d_k, l2norm, kh);
+        l2_normalise(q + (tok * h_k + kh_idx) * d_k, d_k, l2norm, qh);
+        gdr_step(d_k, d_v, S, kh, qh, v + (tok * h_v + h) * d_v,
+                 beta[tok * h_v + h], g[tok * h_v + h], scale,
+                 o + (tok * h_v + h) * d_v, work);
+        if (states)
+          memcpy(states + (tok * h_v + h) * hs, S, hs * sizeof(double));
+      }
+    }
+    free(node); free(kh); free(qh); free(work);
+  }
+  return bad ? -2 : 0;
+}
+
+/*
+ * Commit of an accepted path, oracle form: for every lane with
+ * m_lane[lane] > 0, S is advanced by the steps of nodes path[lane][0..m-1]
+ * in that order (path int32 [n_lanes][t_max], node indices).
+ */
+int oracle_commit_path(int n_layers, int n_lanes, int h_v, int h_k, int d_k,
+                       int d_v, int t_max, const int32_t* m_lane,
+                       const int32_t* path, const double* q, const double* k,
+                       const double* v, const double* beta, const double* g,
+                       double* S, int l2norm) {
+  if (n_layers < 1 || n_lanes < 1 || h_v < 1 || h_k < 1 || d_k < 1 ||
+      d_v < 1 || t_max < 1 || h_v % h_k != 0)
+    return -1;
+  for (int n = 0; n < n_lanes; ++n) {
+    if (m_lane[n] < 0 || m_lane[n] > t_max) return -1;
+    for (int j = 0; j < m_lane[n]; ++j) {
+      const int node = path[(size_t)n * t_max + j];
+      if (node < 0 || node >= t_max) return -1;
+    }
+  }
+  const int group = h_v / h_k;
+  const long n_chains = (long)n_layers * n_lanes * h_v;
+  const size_t hs = (size_t)d_k * d_v;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long c = 0; c < n_chains; ++c) {
+    const int h = (int)(c % h_v);
+    const int lane = (int)((c / h_v) % n_lanes);
+    const int layer = (int)(c / ((long)h_v * n_lanes));
+    const int kh_idx = h / group;
+    const long ll = (long)layer * n_lanes + lane;
+    if (m_lane[lane] == 0) continue;
+    double* kh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* qh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* work = (double*)malloc((size_t)d_v * sizeof(double));
+    if (!kh || !qh || !work) {
+      bad = 1;
+    } else {
+      double* Sh = S + ((size_t)ll * h_v + h) * hs;
+      for (int j = 0; j < m_lane[lane]; ++j) {
+        const size_t tok = (size_t)ll * t_max + path[(size_t)lane * t_max + j];
         l2_normalise(k + (tok * h_k + kh_idx) * d_k, d_k, l2norm, kh);
         l2_normalise(q + (tok * h_k + kh_idx) * d_k, d_k, l2norm, qh);
         gdr_step(d_k, d_v, Sh, kh, qh, v + (tok * h_v + h) * d_v,

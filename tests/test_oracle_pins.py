@@ -413,3 +413,63 @@ def test_resume_from_snapshot_continues_the_chain():
     o_a, _ = oracle.verify(q2, k2, v2, b2, g2, S1, [3, 3, 3])
     o_b, _ = oracle.verify(q2, k2, v2, b2, g2, moved, [3, 3, 3])
     assert np.array_equal(o_a[:, 0], o_b[:, 2])
+
+
+# --------------------------------------------------------------- draft trees
+def _tree_case(key, NL=1, N=3, Hv=2, Hk=1, dk=8, dv=5, T=9):
+    shape = gs.WindowShape(NL, N, Hv, Hk, dk, dv, T)
+    w = gs.window_inputs(shape, key, bf16=False, t_lane=[T, T - 2, 4])
+    S0 = gs.initial_state(shape, key).astype(np.float64)
+    parent = gs.tree_parents(w.t_lane, T, key)
+    return w, S0, parent
+
+
+def test_tree_chain_is_the_linear_window():
+    """A chain (parent[t] = t - 1) is an ordinary window: same outputs and
+    states, and committing the first m nodes is the linear commit."""
+    w, S0, _ = _tree_case((80,))
+    chain = np.tile(np.arange(-1, 8, dtype=np.int32), (3, 1))
+    q, k, v, b, g = w.as_f64()
+    o_t, st_t = oracle.verify_tree(q, k, v, b, g, S0, w.t_lane, chain,
+                                   want_states=True)
+    o_l, st_l = oracle.verify(q, k, v, b, g, S0, w.t_lane, want_states=True)
+    assert np.array_equal(o_t, o_l) and np.array_equal(st_t, st_l)
+    m = [5, 0, 4]
+    S_p = oracle.commit_path(q, k, v, b, g, S0, m,
+                             [list(range(mm)) for mm in m])
+    assert np.array_equal(S_p, oracle.commit(q, k, v, b, g, S0, m))
+
+
+def test_tree_node_is_its_path_as_a_window():
+    """Every node's output and state equal those of the last token of a
+    linear window made of the node's root-to-node path (brute force over
+    all nodes), and committing that path yields that state."""
+    w, S0, parent = _tree_case((81,))
+    q, k, v, b, g = w.as_f64()
+    o_t, st_t = oracle.verify_tree(q, k, v, b, g, S0, w.t_lane, parent,
+                                   want_states=True)
+    assert (parent[:, 1:] != np.arange(0, 8)[None, :]).any(), "not a tree"
+    for n in range(3):
+        for node in range(int(w.t_lane[n])):
+            path = gs.tree_path(parent[n], node)
+            L = len(path)
+            sub = [a[:, n:n + 1, path] for a in (q, k, v, b, g)]
+            o_l, st_l = oracle.verify(*sub, S0[:, n:n + 1], [L],
+                                      want_states=True)
+            assert np.array_equal(o_t[:, n, node], o_l[:, 0, L - 1])
+            assert np.array_equal(st_t[:, n, node], st_l[:, 0, L - 1])
+            m = [0, 0, 0]
+            m[n] = L
+            paths = [[], [], []]
+            paths[n] = path
+            S_c = oracle.commit_path(q, k, v, b, g, S0, m, paths)
+            assert np.array_equal(S_c[:, n], st_t[:, n, node])
+
+
+def test_tree_rejects_a_parent_after_its_child():
+    w, S0, parent = _tree_case((82,))
+    q, k, v, b, g = w.as_f64()
+    bad = parent.copy()
+    bad[0, 3] = 5
+    with pytest.raises(ValueError):
+        oracle.verify_tree(q, k, v, b, g, S0, w.t_lane, bad)
