@@ -186,6 +186,61 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
             "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
 
 
+def bench_tree(reps=20, warmup=3):
+    """Draft-tree verify of the same batch (8 lanes x 48 layers x 32 value /
+    16 key heads, d = 128), 16-node trees per lane in depth-first order
+    (each node extends the previous one with probability 0.6), plus the
+    commit of a drawn accepted path; event-timed."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
+    t_lane = np.full(N, T, dtype=np.int32)
+    w = gs.window_inputs(shape, (8, 0))
+
+    def d16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = d16(w.q), d16(w.k), d16(w.v)
+    beta, g = torch.from_numpy(w.beta).to(dev), torch.from_numpy(w.g).to(dev)
+    parent = gs.tree_parents(t_lane, T, (8, 0))
+    paths = gs.accepted_tree_paths(parent, t_lane, (8, 0))
+    rebuilds = int(sum((parent[n, t] != t - 1) for n in range(N)
+                       for t in range(1, T)))
+    S = torch.from_numpy(gs.initial_state(shape, (8, 0))).to(dev)
+    o = torch.empty((NL, N, T, HV, DV), device=dev)
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    plist = [list(r) for r in parent]
+
+    def run_verify():
+        gdn.verify_tree(dims, t_lane, plist, q, k, v, beta, g, S, o, rec,
+                        stream=stream)
+
+    for _ in range(warmup):
+        run_verify()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(reps)]
+    S_c = S.clone()
+    for e in evs:
+        e[0].record(stream)
+        run_verify()
+        e[1].record(stream)
+        gdn.commit_path(dims, paths, t_lane, plist, rec, S_c, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    upd = N * T * NL * HV
+    return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, 16-node "
+                        "depth-first draft trees, accepted-path commit",
+            "rebuilds": rebuilds, "verify_ms": ms_v, "commit_ms": ms_c,
+            "node_updates_per_s": upd / ((ms_v + ms_c) * 1e-3)}
+
+
 def bench_snapshot(reps=5):
     """Snapshot of the whole 8-lane, 48-layer state (768 MiB) to a device
     buffer and to pinned host memory, and the restore from pinned memory:
@@ -264,6 +319,7 @@ def main():
                     help="which way of running a round to time (the fused "
                          "one is the headline when timed)")
     ap.add_argument("--no-snapshot", action="store_true")
+    ap.add_argument("--no-tree", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -447,6 +503,8 @@ def main():
         out["prefill"] = bench_prefill()
     if not args.no_snapshot:
         out["state_snapshot"] = bench_snapshot()
+    if not args.no_tree:
+        out["draft_tree"] = bench_tree()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -24,7 +24,8 @@ GDN_MAX_LANES = 256
 GDN_MAX_T = 64
 
 EXPORTED = ("gdn_records_bytes", "gdn_verify", "gdn_commit",
-            "gdn_commit_verify", "gdn_state_snapshot", "gdn_state_restore",
+            "gdn_commit_verify", "gdn_verify_tree", "gdn_commit_path",
+            "gdn_state_snapshot", "gdn_state_restore",
             "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_strerror", "gdn_last_error")
 
@@ -73,6 +74,11 @@ def _load_library():
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, f,
                                       ctypes.c_int, vp]
     lib.gdn_commit_verify.restype = ctypes.c_int
+    lib.gdn_verify_tree.argtypes = [dp, ip, ip, vp, vp, vp, ctypes.c_int, vp,
+                                    vp, vp, vp, vp, vp, f, ctypes.c_int, vp]
+    lib.gdn_verify_tree.restype = ctypes.c_int
+    lib.gdn_commit_path.argtypes = [dp, ip, ip, ip, ip, vp, vp, vp]
+    lib.gdn_commit_path.restype = ctypes.c_int
     for fn in (lib.gdn_state_snapshot, lib.gdn_state_restore):
         fn.argtypes = [dp, i32, ip, vp, vp, vp]
         fn.restype = ctypes.c_int
@@ -177,6 +183,50 @@ def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
     if raw_status:
         return st
     _check(st, "gdn_commit_verify")
+
+
+def _table(rows, n, t_max, fill):
+    """int32 [n][t_max] from per-lane sequences (padded with ``fill``)."""
+    import numpy as np
+    a = np.full((n, t_max), fill, dtype=np.int32)
+    if len(rows) != n:
+        raise ValueError("expected %d per-lane rows, got %d" % (n, len(rows)))
+    for i, r in enumerate(rows):
+        r = [int(x) for x in r]
+        a[i, :len(r)] = r
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def verify_tree(dims: Dims, t_lane, parent, q, k, v, beta, g, S, o, records,
+                dbg_states=None, scale=1.0, l2norm=True, stream=None,
+                raw_status=False):
+    """gdn_verify_tree; parent is [n_lanes][<= t_max] (-1: from S0)."""
+    keep, pp = _table(parent, dims.n_lanes, dims.t_max, -1)
+    st = lib.gdn_verify_tree(
+        ctypes.byref(dims), _int_array(t_lane, dims.n_lanes), pp, _ptr(q),
+        _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S),
+        _ptr(o), _ptr(records), _ptr(dbg_states), float(scale),
+        GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+    del keep
+    if raw_status:
+        return st
+    _check(st, "gdn_verify_tree")
+
+
+def commit_path(dims: Dims, paths, t_lane, parent, records, S, stream=None,
+                raw_status=False):
+    """gdn_commit_path; paths[n] lists the accepted nodes of lane n, root
+    first (empty: nothing accepted)."""
+    keep_p, pp = _table(paths, dims.n_lanes, dims.t_max, 0)
+    keep_t, tp = _table(parent, dims.n_lanes, dims.t_max, -1)
+    m = [len(p) for p in paths]
+    st = lib.gdn_commit_path(ctypes.byref(dims), _int_array(m, dims.n_lanes),
+                             pp, _int_array(t_lane, dims.n_lanes), tp,
+                             _ptr(records), _ptr(S), _stream(stream))
+    del keep_p, keep_t
+    if raw_status:
+        return st
+    _check(st, "gdn_commit_path")
 
 
 def _lane_list(lanes):

@@ -57,6 +57,8 @@
 #include <tuple>
 #include <utility>
 
+#include <type_traits>
+
 #include "gdn.h"
 #include "gdn_internal.h"
 #include "gdn_step.h"
@@ -82,6 +84,17 @@ struct CommitTable {
   uint8_t lane[GDN_MAX_LANES];
   uint8_t m[GDN_MAX_LANES];
 };
+
+// Draft trees (windows where a node steps from its parent's state): the
+// parents of every lane's nodes, or for a commit the accepted nodes of every
+// active lane, as bytes in the kernel arguments.
+constexpr int kTreeMaxT = 32;     // nodes per tree window
+constexpr int kTreeCells = 2048;  // n_lanes * t_max
+constexpr uint8_t kNoParent = 255;
+struct TreeTable {
+  uint8_t v[kTreeCells];  // [lane * t_max + t]: parent, or kNoParent
+};
+struct NoTable {};
 
 // ------------------------------------------------------------- records
 struct RecLayout {
@@ -267,20 +280,23 @@ struct PrevRecords {
 // ReplaySSM section): the same fold, write and materialisation as
 // commit_kernel, in the same order, on the same values.  Returns the scale
 // of the state after the last replayed token.
-template <int R>
+// node_of(t) is the record index of the t-th replayed step (t itself for a
+// window, the t-th node of the accepted path for a draft tree).
+template <int R, typename NodeOf>
 __device__ __forceinline__ float replay(float (&s)[R], const float* __restrict__ k0,
                                         const float* __restrict__ u0,
                                         const float2* __restrict__ c0, int m,
                                         int j0, int ic, size_t kq_step,
-                                        size_t vo_step, int Hv) {
-  // the records of token t+1 are requested before token t is applied
-  float2 fc = c0[0];
-  float ut = u0[(uint32_t)ic];
+                                        size_t vo_step, int Hv, NodeOf node_of) {
+  // the records of step t+1 are requested before step t is applied
+  const int n0 = node_of(0);
+  float2 fc = c0[n0 * Hv];
+  float ut = u0[n0 * vo_step + (uint32_t)ic];
   RowWords<float, R> kw;
-  kw.load(k0, j0);
+  kw.load(k0 + n0 * kq_step, j0);
   float c = 1.0f;
   for (int t = 0; t < m; ++t) {
-    const int nt = t + 1 < m ? t + 1 : t;
+    const int nt = node_of(t + 1 < m ? t + 1 : t);
     const float2 fc_n = c0[nt * Hv];
     const float ut_n = u0[nt * vo_step + (uint32_t)ic];
     RowWords<float, R> kw_n;
@@ -378,7 +394,14 @@ __device__ __forceinline__ float replay_staged(
 // gdn_commit_verify -- replay the previous window's accepted prefix from S,
 // store the committed state S_m in place, then verify the new window from
 // the state still held in registers (the committed values, bit for bit).
-template <int DK, bool DBG, typename TIn, bool REPLAY>
+// TREE: a draft-tree window.  Node t steps from the state of its parent
+// tree.v[lane * T + t] (S0 for kNoParent).  Nodes come in an order where a
+// parent precedes its children; when node t's parent is not node t-1, every
+// wave rebuilds the parent's state: S0 again, then the recorded steps of the
+// root-to-parent path (fold, ut from LDS, the raw key row) -- exactly the
+// operations a commit of that path performs, so the state at every node is
+// bitwise what gdn_commit_path reproduces.
+template <int DK, bool DBG, typename TIn, bool REPLAY, bool TREE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6)))
 void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -387,10 +410,16 @@ void verify_kernel(
     float* __restrict__ o, float* __restrict__ rec_k,
     float* __restrict__ rec_u, float2* __restrict__ rec_scale,
     float* __restrict__ dbg, WinDims d, LaneTable tl, float scale,
-    int l2norm, PrevRecords prev) {
+    int l2norm, PrevRecords prev,
+    std::conditional_t<TREE, TreeTable, NoTable> tree) {
   constexpr int R = DK / kWaves;  // key rows per wave
   __shared__ float nrm[3][GDN_MAX_T];  // rk_t, rq_t, k_t . q_t (raw)
   __shared__ StepScalars sc[GDN_MAX_T];
+  // draft trees: ut of every node (this workgroup's columns) and the
+  // root-to-node path of every node
+  __shared__ float uth[TREE ? kTreeMaxT : 1][kWave];
+  __shared__ uint8_t plist[TREE ? kTreeMaxT * (kTreeMaxT + 1) / 2 : 1];
+  __shared__ uint16_t pstart[TREE ? kTreeMaxT : 1];
 
   int item = xcd_item(blockIdx.x, gridDim.x);
   const int cb = item % d.ncb;
@@ -402,6 +431,15 @@ void verify_kernel(
   const int T = tl.v[lane];
   const int m_prev = REPLAY ? prev.m.v[lane] : 0;
   if (T == 0 && m_prev == 0) return;
+  // parent of node t (t - 1 in a plain window; -1: steps from S0)
+  auto parent_of = [&](int t) -> int {
+    if constexpr (TREE) {
+      const int p = tree.v[lane * d.T + t];
+      return p == kNoParent ? -1 : p;
+    } else {
+      return t - 1;
+    }
+  };
 
   const int w = uniform((int)threadIdx.x / kWave);
   const int x = (int)threadIdx.x % kWave;
@@ -424,8 +462,8 @@ void verify_kernel(
   float* __restrict__ u0 = rec_u + ((ll * d.T) * d.Hv + h) * dv;
 
   float s[R];  // scaled state St (rows j0..j0+R-1, column i); S = c * St
+  float* const Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
   {
-    float* Sh = S + ((ll * d.Hv + h) * (size_t)DK + j0) * dv;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
@@ -491,14 +529,17 @@ void verify_kernel(
     }
     const bool out = !(c >= kScaleLo && c <= kScaleHi);
     float phi = 1.f;
-    if (__builtin_amdgcn_ballot_w64(out && x < T) != 0) {
-      // sequential walk with folds (lane 0), results spread back by lane
+    if (TREE || __builtin_amdgcn_ballot_w64(out && x < T) != 0) {
+      // sequential walk with folds (lane 0), results spread back by lane;
+      // in a tree each node continues its parent's scale
       __shared__ float seq_c[GDN_MAX_T], seq_f[GDN_MAX_T], seq_a[GDN_MAX_T];
       if (x < T) seq_a[x] = a_t;
       __builtin_amdgcn_wave_barrier();
       if (x == 0) {
-        float cc = 1.0f;
+        [[maybe_unused]] int used = 0;
         for (int t = 0; t < T; ++t) {
+          const int par = parent_of(t);
+          const float cc = par < 0 ? 1.0f : seq_c[par];
           float cn, fo = 1.f;
           if (scale_step(cc, seq_a[t], cn)) {
             fo = cn;
@@ -506,7 +547,19 @@ void verify_kernel(
           }
           seq_c[t] = cn;
           seq_f[t] = fo;
-          cc = cn;
+          if constexpr (TREE) {  // root-to-node path of node t
+            pstart[t] = (uint16_t)used;
+            if (par >= 0) {
+              // copy the parent's path (it ends with par), then append t
+              int j = pstart[par];
+              while (true) {
+                const int u = plist[j++];
+                plist[used++] = (uint8_t)u;
+                if (u == par) break;
+              }
+            }
+            plist[used++] = (uint8_t)t;
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -541,6 +594,27 @@ void verify_kernel(
   qw.load(q0, j0);
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
+    if constexpr (TREE) {
+      const int par = parent_of(t);
+      if (t > 0 && par != t - 1) {
+        // rebuild the parent's state from S0 and its recorded path
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r] = Sh[(uint32_t)(r * d.dv + ic)];
+        if (par >= 0) {
+          for (int j = pstart[par];; ++j) {
+            const int u = uniform(plist[j]);
+            const float phu = sc[u].phi;
+            if (phu != 1.f) fold_scale<R>(s, phu);
+            const float utu = uth[u][x];
+            RowWords<TIn, R> ku;
+            ku.load(k0 + u * kq_step, j0);
+#pragma unroll
+            for (int r = 0; r < R; ++r) s[r] = state_update(s[r], utu, ku.at(r));
+            if (u == par) break;
+          }
+        }
+      }
+    }
     const float vi = load_in(v0 + t * vo_step, (uint32_t)ic);
     const StepScalars z = sc[t];
     if (z.phi != 1.f) fold_scale<R>(s, z.phi);
@@ -573,6 +647,9 @@ void verify_kernel(
       u0[t * vo_step + (uint32_t)i] = ut;
       o0[t * vo_step + (uint32_t)i] = z.f3 * __builtin_fmaf(ut, z.kq, PQ);
     }
+    if constexpr (TREE) {
+      if (w == owner) uth[t][x] = ut;  // read back after a later barrier
+    }
 
     // rank-1 write
 #pragma unroll
@@ -588,11 +665,13 @@ void verify_kernel(
 }
 
 // ------------------------------------------------------------- commit
-template <int DK>
+// PATH: the replayed steps are the accepted nodes path.v[a * T + t] of a
+// draft tree (a: the lane's index among the active lanes), not 0..m-1.
+template <int DK, bool PATH>
 __global__ __launch_bounds__(kBlock) void commit_kernel(
     const float* __restrict__ rec_k, const float* __restrict__ rec_u,
     const float2* __restrict__ rec_scale, float* __restrict__ S, WinDims d,
-    CommitTable ct) {
+    CommitTable ct, std::conditional_t<PATH, TreeTable, NoTable> path) {
   constexpr int R = DK / kWaves;
   int item = xcd_item(blockIdx.x, gridDim.x);
   const int cb = item % d.ncb;
@@ -623,7 +702,11 @@ __global__ __launch_bounds__(kBlock) void commit_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r)
     s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
-  const float c = replay<R>(s, k0, u0, c0, m, j0, ic, kq_step, vo_step, d.Hv);
+  const float c = replay<R>(s, k0, u0, c0, m, j0, ic, kq_step, vo_step, d.Hv,
+                            [&](int t) -> int {
+                              if constexpr (PATH) return path.v[a * d.T + t];
+                              else return t;
+                            });
   if (act) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -713,38 +796,39 @@ struct VerifyArgs {
   int l2;
 };
 
-template <int DK, bool DBG, typename TIn, bool REPLAY>
+template <int DK, bool DBG, typename TIn, bool REPLAY, bool TREE, typename Tab>
 static hipError_t launch_verify_t(const WinDims& w, const LaneTable& tl,
                                   const VerifyArgs& a, const PrevRecords& pr,
-                                  hipStream_t st) {
+                                  const Tab& tree, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv * w.ncb;
-  return launch(verify_kernel<DK, DBG, TIn, REPLAY>, dim3(blocks), dim3(kBlock),
-                st, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.beta,
-                a.g, a.S, a.o, a.rk, a.ru, a.ra, a.dbg, w, tl, a.scale, a.l2,
-                pr);
+  return launch(verify_kernel<DK, DBG, TIn, REPLAY, TREE>, dim3(blocks),
+                dim3(kBlock), st, (const TIn*)a.q, (const TIn*)a.k,
+                (const TIn*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
+                a.dbg, w, tl, a.scale, a.l2, pr, tree);
 }
 
-template <bool DBG, typename TIn, bool REPLAY>
+template <bool DBG, typename TIn, bool REPLAY, bool TREE, typename Tab>
 static hipError_t launch_verify_d(const WinDims& w, const LaneTable& tl,
                                   const VerifyArgs& a, const PrevRecords& pr,
-                                  hipStream_t st) {
+                                  const Tab& tree, hipStream_t st) {
   switch (w.dk) {
-    case 16: return launch_verify_t<16, DBG, TIn, REPLAY>(w, tl, a, pr, st);
-    case 32: return launch_verify_t<32, DBG, TIn, REPLAY>(w, tl, a, pr, st);
-    case 64: return launch_verify_t<64, DBG, TIn, REPLAY>(w, tl, a, pr, st);
-    default: return launch_verify_t<128, DBG, TIn, REPLAY>(w, tl, a, pr, st);
+    case 16: return launch_verify_t<16, DBG, TIn, REPLAY, TREE>(w, tl, a, pr, tree, st);
+    case 32: return launch_verify_t<32, DBG, TIn, REPLAY, TREE>(w, tl, a, pr, tree, st);
+    case 64: return launch_verify_t<64, DBG, TIn, REPLAY, TREE>(w, tl, a, pr, tree, st);
+    default: return launch_verify_t<128, DBG, TIn, REPLAY, TREE>(w, tl, a, pr, tree, st);
   }
 }
 
-template <bool REPLAY>
+template <bool REPLAY, bool TREE = false, typename Tab = NoTable>
 static hipError_t launch_verify(const WinDims& w, const LaneTable& tl,
                                 int in_dtype, const VerifyArgs& a,
-                                const PrevRecords& pr, hipStream_t st) {
+                                const PrevRecords& pr, hipStream_t st,
+                                const Tab& tree = Tab()) {
   if (in_dtype == GDN_BF16)
-    return a.dbg ? launch_verify_d<true, uint16_t, REPLAY>(w, tl, a, pr, st)
-                 : launch_verify_d<false, uint16_t, REPLAY>(w, tl, a, pr, st);
-  return a.dbg ? launch_verify_d<true, float, REPLAY>(w, tl, a, pr, st)
-               : launch_verify_d<false, float, REPLAY>(w, tl, a, pr, st);
+    return a.dbg ? launch_verify_d<true, uint16_t, REPLAY, TREE>(w, tl, a, pr, tree, st)
+                 : launch_verify_d<false, uint16_t, REPLAY, TREE>(w, tl, a, pr, tree, st);
+  return a.dbg ? launch_verify_d<true, float, REPLAY, TREE>(w, tl, a, pr, tree, st)
+               : launch_verify_d<false, float, REPLAY, TREE>(w, tl, a, pr, tree, st);
 }
 
 // Checks shared by gdn_verify and gdn_commit_verify; fills the lane table
@@ -885,13 +969,125 @@ extern "C" int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(d.n_layers * ct.n_act * d.h_v * w.ncb);
   hipError_t e;
+  const NoTable none{};
   switch (d.d_k) {
-    case 16: e = launch(commit_kernel<16>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
-    case 32: e = launch(commit_kernel<32>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
-    case 64: e = launch(commit_kernel<64>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
-    default: e = launch(commit_kernel<128>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct); break;
+    case 16: e = launch(commit_kernel<16, false>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, none); break;
+    case 32: e = launch(commit_kernel<32, false>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, none); break;
+    case 64: e = launch(commit_kernel<64, false>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, none); break;
+    default: e = launch(commit_kernel<128, false>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, none); break;
   }
   return hip_status(e, "gdn_commit launch");
+}
+
+// Host checks of a draft-tree window: sizes that fit the kernel-argument
+// table, and parent[t] in -1..t-1 for every node of every lane.
+static int tree_table(const char* fn, const gdn_dims& d, const int32_t* t_lane,
+                      const int32_t* parent, TreeTable& tab) {
+  char msg[128];
+  if (d.t_max > kTreeMaxT || d.n_lanes * d.t_max > kTreeCells) {
+    snprintf(msg, sizeof(msg), "%s: tree windows need t_max <= %d and "
+             "n_lanes * t_max <= %d", fn, kTreeMaxT, kTreeCells);
+    return fail(GDN_EUNSUPPORTED, msg);
+  }
+  if (!parent) {
+    snprintf(msg, sizeof(msg), "%s: parent is NULL", fn);
+    return fail(GDN_EINVAL, msg);
+  }
+  memset(&tab, kNoParent, sizeof(tab));
+  for (int n = 0; n < d.n_lanes; ++n) {
+    const int T = t_lane[n] < 0 ? 0 : t_lane[n];
+    for (int t = 0; t < T && t < d.t_max; ++t) {
+      const int p = parent[n * d.t_max + t];
+      if (p < -1 || p >= t) {
+        snprintf(msg, sizeof(msg), "%s: parent[%d][%d] = %d is not in -1..%d",
+                 fn, n, t, p, t - 1);
+        return fail(GDN_EINVAL, msg);
+      }
+      tab.v[n * d.t_max + t] = p < 0 ? kNoParent : (uint8_t)p;
+    }
+  }
+  return GDN_OK;
+}
+
+extern "C" int gdn_verify_tree(const gdn_dims* dims, const int32_t* t_lane,
+                               const int32_t* parent, const void* q,
+                               const void* k, const void* v, int in_dtype,
+                               const float* beta, const float* g,
+                               const float* S, float* o, void* records,
+                               float* dbg_states, float scale, int flags,
+                               void* stream) {
+  LaneTable tl;
+  VerifyArgs a;
+  int any = 0;
+  int rc = verify_setup("gdn_verify_tree", dims, t_lane, q, k, v, in_dtype,
+                        beta, g, S, o, records, dbg_states, scale, flags, tl,
+                        a, &any);
+  if (rc != GDN_OK) return rc;
+  TreeTable tab;
+  rc = tree_table("gdn_verify_tree", *dims, t_lane, parent, tab);
+  if (rc != GDN_OK) return rc;
+  if (!any) return GDN_OK;
+  PrevRecords none;
+  memset(&none, 0, sizeof(none));
+  hipError_t e = launch_verify<false, true>(win_dims(*dims), tl, in_dtype, a,
+                                            none, (hipStream_t)stream, tab);
+  return hip_status(e, "gdn_verify_tree launch");
+}
+
+extern "C" int gdn_commit_path(const gdn_dims* dims, const int32_t* m_lane,
+                               const int32_t* path, const int32_t* t_lane,
+                               const int32_t* parent, const void* records,
+                               float* S, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != GDN_OK) return rc;
+  if (!m_lane || !path || !t_lane || !records || !S)
+    return fail(GDN_EINVAL, "gdn_commit_path: required pointer is NULL");
+  if (misaligned(records, 256) || misaligned(S, 4))
+    return fail(GDN_EINVAL, "gdn_commit_path: misaligned pointer");
+  const gdn_dims& d = *dims;
+  TreeTable parents;
+  rc = tree_table("gdn_commit_path", d, t_lane, parent, parents);
+  if (rc != GDN_OK) return rc;
+  CommitTable ct;
+  rc = commit_lanes("gdn_commit_path", d, m_lane, t_lane, ct);
+  if (rc != GDN_OK) return rc;
+  // the accepted nodes of each active lane must be a root-to-node path
+  TreeTable nodes;
+  memset(&nodes, 0, sizeof(nodes));
+  for (int a_i = 0; a_i < ct.n_act; ++a_i) {
+    const int n = ct.lane[a_i], m = ct.m[a_i];
+    int prev = -1;
+    for (int j = 0; j < m; ++j) {
+      const int node = path[n * d.t_max + j];
+      const int par = (node >= 0 && node < t_lane[n])
+                          ? (parents.v[n * d.t_max + node] == kNoParent
+                                 ? -1
+                                 : parents.v[n * d.t_max + node])
+                          : -2;
+      if (par == -2 || par != prev)
+        return fail(GDN_EINVAL,
+                    "gdn_commit_path: path is not a root-to-node path of the tree");
+      nodes.v[a_i * d.t_max + j] = (uint8_t)node;
+      prev = node;
+    }
+  }
+  if (ct.n_act == 0) return GDN_OK;
+  const WinDims w = win_dims(d);
+  const RecLayout L = rec_layout(d);
+  const char* rb = (const char*)records;
+  const float* rk = (const float*)(rb + L.k);
+  const float* ru = (const float*)(rb + L.u);
+  const float2* ra = (const float2*)(rb + L.scale);
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid(d.n_layers * ct.n_act * d.h_v * w.ncb);
+  hipError_t e;
+  switch (d.d_k) {
+    case 16: e = launch(commit_kernel<16, true>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, nodes); break;
+    case 32: e = launch(commit_kernel<32, true>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, nodes); break;
+    case 64: e = launch(commit_kernel<64, true>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, nodes); break;
+    default: e = launch(commit_kernel<128, true>, grid, dim3(kBlock), st, rk, ru, ra, S, w, ct, nodes); break;
+  }
+  return hip_status(e, "gdn_commit_path launch");
 }
 
 extern "C" int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,

@@ -10,6 +10,8 @@
  *                        is never written.
  *   gdn_commit           ReplaySSM commit: replay the first m records of each
  *                        lane from the untouched S0 and store S_m in place.
+ *   gdn_verify_tree,     the same for a draft tree (node t steps from its
+ *   gdn_commit_path      parent) and the commit of an accepted path.
  *   gdn_commit_verify    both in one launch: commit the previous window's
  *                        accepted prefix, then verify the next window from
  *                        the committed state without reading it again.
@@ -150,6 +152,36 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
 int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
                const int32_t* t_lane, const void* records, float* S,
                void* stream);
+
+/*
+ * Draft-tree verify and accepted-path commit.  The speculative window of a
+ * lane is a tree of draft tokens (draft trees are used together with DFlash2
+ * by the engine the first page describes): node t steps from the state of
+ * its parent, not from node t-1.  Records are per node, in the layout of
+ * gdn_verify; commit replays the accepted root-to-node path from S0, and its
+ * result is bit for bit the state verify held at the path's last node (the
+ * ReplaySSM requirement, per node).
+ *   parent   host int32 [n_lanes][t_max]: parent[n][t] in -1..t-1 for
+ *            t < t_lane[n] (-1: the node steps from S0); nodes are ordered so
+ *            that a parent precedes its children.  Depth-first order is
+ *            cheapest: verify rebuilds the parent's state (S0 plus the
+ *            path's recorded steps) whenever parent[t] != t - 1.
+ *   path     host int32 [n_lanes][t_max]: the first m_lane[n] entries are the
+ *            accepted nodes, root first, each the parent of the next.
+ *   other arguments as for gdn_verify / gdn_commit.
+ * Supported: t_max <= 32 and n_lanes * t_max <= 2048 (GDN_EUNSUPPORTED
+ * otherwise); a bad parent or a path that is not a root-to-node chain is
+ * GDN_EINVAL.
+ */
+int gdn_verify_tree(const gdn_dims* dims, const int32_t* t_lane,
+                    const int32_t* parent, const void* q, const void* k,
+                    const void* v, int in_dtype, const float* beta,
+                    const float* g, const float* S, float* o, void* records,
+                    float* dbg_states, float scale, int flags, void* stream);
+int gdn_commit_path(const gdn_dims* dims, const int32_t* m_lane,
+                    const int32_t* path, const int32_t* t_lane,
+                    const int32_t* parent, const void* records, float* S,
+                    void* stream);
 
 /*
  * Fused commit + verify: the ReplaySSM commit of the previous window

@@ -159,6 +159,33 @@ def test_commit_verify_rejects_bad_arguments_on_host():
     assert cv(d, [0, 0], [2, 1], [0, 0], rec_prev=None) == gdn.GDN_OK
 
 
+def test_tree_calls_reject_bad_arguments_on_host():
+    d = _dims(n_lanes=2, t_max=4)
+    a = dict(q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),
+             g=_Fake(gdn.GDN_F32), S=_Fake(gdn.GDN_F32), o=_Fake(gdn.GDN_F32),
+             rec=_Fake(gdn.GDN_F32))
+
+    def vt(parent, t=(4, 3), dims=d):
+        return gdn.verify_tree(dims, t, parent, a["q"], a["k"], a["v"],
+                               a["beta"], a["g"], a["S"], a["o"], a["rec"],
+                               stream=0, raw_status=True)
+
+    good = [[-1, 0, 0, 2], [-1, 0, 1]]
+    assert vt([[-1, 0, 3, 2], [-1, 0, 1]]) == gdn.GDN_EINVAL   # parent after child
+    assert vt([[-1, 0, 0, 2], [-1, -2, 1]]) == gdn.GDN_EINVAL  # below -1
+    assert vt(good, dims=_dims(n_lanes=2, t_max=33)) == gdn.GDN_EUNSUPPORTED
+    assert vt(good, t=(0, 0)) == gdn.GDN_OK                    # nothing to run
+
+    def cp(paths, t=(4, 3), parent=good):
+        return gdn.commit_path(d, paths, t, parent, a["rec"], a["S"], stream=0,
+                               raw_status=True)
+
+    assert cp([[1, 2], []]) == gdn.GDN_EINVAL       # does not start at a root
+    assert cp([[0, 1, 3], []]) == gdn.GDN_EINVAL    # 3's parent is 2, not 1
+    assert cp([[], [0, 1, 2, 0]]) == gdn.GDN_EINVAL  # m > t_lane
+    assert cp([[], []]) == gdn.GDN_OK
+
+
 def test_state_copy_rejects_bad_arguments_on_host():
     d = _dims(n_lanes=4)
     S, snap = _Fake(gdn.GDN_F32), _Fake(gdn.GDN_F32, addr=1 << 30)
