@@ -21,6 +21,8 @@ What is computed (see the C file for the passage-by-passage account):
   * draft-tree windows (the first page: draft trees with DFlash2): node t
     steps from its parent's state, and a commit replays an accepted
     root-to-node path from S_0;
+  * KDA, the sibling rule with a per-key-channel decay (Kimi Delta
+    Attention; the review names its state and a kda_replay contract);
   * snapshot / restore of the recurrent state of chosen lanes (same section:
     paused requests come back by replay or from a snapshot) -- exact copies,
     written here as numpy indexing.
@@ -80,6 +82,9 @@ def _load():
         lib.oracle_verify_tree.restype = i
         lib.oracle_commit_path.argtypes = [i] * 7 + [ip, ip] + [dp] * 6 + [i]
         lib.oracle_commit_path.restype = i
+        lib.oracle_kda.argtypes = [i] * 7 + [ip, ip] + [dp] * 6 + [
+            ctypes.c_double, i, dp, dp]
+        lib.oracle_kda.restype = i
         lib.oracle_prefill.argtypes = [i] * 6 + [dp] * 6 + [
             ctypes.c_double, i, dp, dp, dp]
         lib.oracle_prefill.restype = i
@@ -214,6 +219,51 @@ def commit_path(q, k, v, beta, g, S, m_lane, path, l2norm=True):
         int(bool(l2norm)))
     if rc != 0:
         raise ValueError("oracle_commit_path failed: %d" % rc)
+    return out
+
+
+def kda_verify(q, k, v, beta, g, S0, t_lane, scale=1.0, l2norm=True,
+               want_states=False):
+    """KDA window verify.  Shapes as verify() except g [NL, N, T, Hv, dk]
+    (log-decay per key channel).  Returns (o, states or None)."""
+    lib = _load()
+    NL, N, T, Hk, dk = q.shape
+    Hv, dv = v.shape[3], v.shape[4]
+    assert g.shape == (NL, N, T, Hv, dk)
+    q, qp = _d(q); k, kp = _d(k); v, vp = _d(v)
+    beta, bp = _d(beta); g, gp = _d(g)
+    Sw = np.array(S0, dtype=np.float64, copy=True, order="C")
+    tl = np.ascontiguousarray(t_lane, dtype=np.int32)
+    o = np.zeros((NL, N, T, Hv, dv))
+    states = np.zeros((NL, N, T, Hv, dk, dv)) if want_states else None
+    ip = ctypes.POINTER(ctypes.c_int32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_kda(NL, N, Hv, Hk, dk, dv, T, tl.ctypes.data_as(ip), None,
+                        qp, kp, vp, bp, gp, Sw.ctypes.data_as(dp), float(scale),
+                        int(bool(l2norm)), o.ctypes.data_as(dp),
+                        states.ctypes.data_as(dp) if want_states else None)
+    if rc != 0:
+        raise ValueError("oracle_kda failed: %d" % rc)
+    return o, states
+
+
+def kda_commit(q, k, v, beta, g, S, m_lane, l2norm=True):
+    """KDA commit: a new array, S advanced by the first m_lane[n] steps."""
+    lib = _load()
+    NL, N, T, Hk, dk = q.shape
+    Hv, dv = v.shape[3], v.shape[4]
+    q, qp = _d(q); k, kp = _d(k); v, vp = _d(v)
+    beta, bp = _d(beta); g, gp = _d(g)
+    out = np.array(S, dtype=np.float64, copy=True, order="C")
+    ml = np.ascontiguousarray(m_lane, dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_kda(NL, N, Hv, Hk, dk, dv, T, ml.ctypes.data_as(ip),
+                        ml.ctypes.data_as(ip), qp, kp, vp, bp, gp,
+                        out.ctypes.data_as(dp), 1.0, int(bool(l2norm)), None,
+                        None)
+    if rc != 0:
+        raise ValueError("oracle_kda failed: %d" % rc)
     return out
 
 

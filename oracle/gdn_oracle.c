@@ -322,6 +322,99 @@ int oracle_commit_path(int n_layers, int n_lanes, int h_v, int h_k, int d_k,
 }
 
 /*
+ * KDA, the sibling rule with a decay per key channel (Kimi Delta Attention,
+ * Kimi Linear, 2025; the review names its recurrent state and a kda_replay
+ * op contract beside gdn_replay).  With alpha_t a d_k vector,
+ *     S'_t = S_{t-1} diag(alpha_t)          (column j scaled by alpha_tj)
+ *     p_t  = S'_t khat_t
+ *     u_t  = beta_t (v_t - p_t)
+ *     S_t  = S'_t + u_t khat_t^T
+ *     o_t  = scale * S_t qhat_t
+ * alpha_tj = exp(g_tj).  g is [..][h_v][d_k] (per value head and channel).
+ */
+static void kda_step(int dk, int dv, double* S, const double* kh,
+                     const double* qh, const double* v, double beta,
+                     const double* g, double scale, double* o, double* work) {
+  double* u = work;
+  /* S' = S diag(alpha) */
+  for (int j = 0; j < dk; ++j) {
+    const double a = exp(g[j]);
+    for (int i = 0; i < dv; ++i) S[(size_t)j * dv + i] *= a;
+  }
+  /* p = S' khat; u = beta (v - p) */
+  for (int i = 0; i < dv; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < dk; ++j) acc += S[(size_t)j * dv + i] * kh[j];
+    u[i] = beta * (v[i] - acc);
+  }
+  /* S = S' + u khat^T */
+  for (int j = 0; j < dk; ++j)
+    for (int i = 0; i < dv; ++i) S[(size_t)j * dv + i] += u[i] * kh[j];
+  if (o) {
+    for (int i = 0; i < dv; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < dk; ++j) acc += S[(size_t)j * dv + i] * qh[j];
+      o[i] = scale * acc;
+    }
+  }
+}
+
+/*
+ * KDA window verify (states nullable) and, with o == NULL and m_lane != NULL,
+ * commit: S advanced by the first m_lane[lane] steps.  Layouts as
+ * oracle_verify except g: [n_layers][n_lanes][t_max][h_v][d_k].
+ */
+int oracle_kda(int n_layers, int n_lanes, int h_v, int h_k, int d_k, int d_v,
+               int t_max, const int32_t* t_lane, const int32_t* m_lane,
+               const double* q, const double* k, const double* v,
+               const double* beta, const double* g, double* S, double scale,
+               int l2norm, double* o, double* states) {
+  if (n_layers < 1 || n_lanes < 1 || h_v < 1 || h_k < 1 || d_k < 1 ||
+      d_v < 1 || t_max < 1 || h_v % h_k != 0)
+    return -1;
+  for (int n = 0; n < n_lanes; ++n) {
+    const int steps = m_lane ? m_lane[n] : t_lane[n];
+    if (steps < 0 || steps > t_max) return -1;
+  }
+  const int group = h_v / h_k;
+  const long n_chains = (long)n_layers * n_lanes * h_v;
+  const size_t hs = (size_t)d_k * d_v;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long c = 0; c < n_chains; ++c) {
+    const int h = (int)(c % h_v);
+    const int lane = (int)((c / h_v) % n_lanes);
+    const int layer = (int)(c / ((long)h_v * n_lanes));
+    const int kh_idx = h / group;
+    const long ll = (long)layer * n_lanes + lane;
+    const int steps = m_lane ? m_lane[lane] : t_lane[lane];
+    double* Sw = (double*)malloc(hs * sizeof(double));
+    double* kh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* qh = (double*)malloc((size_t)d_k * sizeof(double));
+    double* work = (double*)malloc((size_t)d_v * sizeof(double));
+    if (!Sw || !kh || !qh || !work) {
+      bad = 1;
+    } else {
+      double* Sh = S + ((size_t)ll * h_v + h) * hs;
+      memcpy(Sw, Sh, hs * sizeof(double));
+      for (int t = 0; t < steps; ++t) {
+        const size_t tok = (size_t)ll * t_max + t;
+        l2_normalise(k + (tok * h_k + kh_idx) * d_k, d_k, l2norm, kh);
+        l2_normalise(q + (tok * h_k + kh_idx) * d_k, d_k, l2norm, qh);
+        kda_step(d_k, d_v, Sw, kh, qh, v + (tok * h_v + h) * d_v,
+                 beta[tok * h_v + h], g + (tok * h_v + h) * d_k, scale,
+                 m_lane ? NULL : o + (tok * h_v + h) * d_v, work);
+        if (states && !m_lane)
+          memcpy(states + (tok * h_v + h) * hs, Sw, hs * sizeof(double));
+      }
+      if (m_lane) memcpy(Sh, Sw, hs * sizeof(double));
+    }
+    free(Sw); free(kh); free(qh); free(work);
+  }
+  return bad ? -2 : 0;
+}
+
+/*
  * Prefill, oracle form: one sequence of seq_len tokens, token by token.
  *   q, k   [seq_len][h_k][d_k]
  *   v      [seq_len][h_v][d_v]

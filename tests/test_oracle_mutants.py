@@ -38,6 +38,18 @@ MUTANTS = [
      "const int kh_idx = h % h_k;"),
     ("checkpoint_off_by_one", "if (ckpt && (t + 1) % ckpt_interval == 0) {",
      "if (ckpt && t % ckpt_interval == 0 && t > 0) {"),
+    ("tree_steps_from_previous_node",
+     "const int p = parent[(size_t)lane * t_max + t];",
+     "const int p = t - 1;"),
+    ("path_commit_replays_first_nodes",
+     "const size_t tok = (size_t)ll * t_max + path[(size_t)lane * t_max + j];",
+     "const size_t tok = (size_t)ll * t_max + j;"),
+    ("kda_gate_not_exponentiated", "const double a = exp(g[j]);",
+     "const double a = 1.0 + g[j];"),
+    ("kda_channels_reversed", "const double a = exp(g[j]);",
+     "const double a = exp(g[dk - 1 - j]);"),
+    ("kda_delta_sign", "u[i] = beta * (v[i] - acc);",
+     "u[i] = beta * (v[i] + acc);"),
 ]
 
 PIN_TESTS = [
@@ -57,6 +69,12 @@ PIN_TESTS = [
     lambda: pins.test_homogeneous_part_is_non_expansive(),
     lambda: pins.test_key_head_sharing_matches_duplicated_keys(),
     lambda: pins.test_prefill_matches_window_and_checkpoints(),
+    lambda: pins.test_tree_chain_is_the_linear_window(),
+    lambda: pins.test_tree_node_is_its_path_as_a_window(),
+    lambda: pins.test_kda_with_equal_channels_is_the_gated_delta_rule(),
+    lambda: pins.test_kda_is_online_regression_step_from_the_channel_decayed_state(),
+    lambda: pins.test_kda_exact_rational_product_form(),
+    lambda: pins.test_kda_channel_forgetting(),
 ]
 
 

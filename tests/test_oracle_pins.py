@@ -473,3 +473,108 @@ def test_tree_rejects_a_parent_after_its_child():
     bad[0, 3] = 5
     with pytest.raises(ValueError):
         oracle.verify_tree(q, k, v, b, g, S0, w.t_lane, bad)
+
+
+# --------------------------------------------------------------------- KDA
+def _kda_case(seed, T=6, Hv=2, Hk=1, dk=6, dv=4):
+    q, k, v, beta, g, S0 = _rand_case(seed, T=T, Hv=Hv, Hk=Hk, dk=dk, dv=dv)
+    r = np.random.default_rng(seed + 100)
+    gk = -np.logaddexp(0.0, r.standard_normal((1, 1, T, Hv, dk)))
+    return q, k, v, beta, gk, S0
+
+
+def test_kda_with_equal_channels_is_the_gated_delta_rule():
+    """A KDA decay that is the same on every channel is the scalar gate of
+    the gated delta rule."""
+    q, k, v, beta, g, S0 = _rand_case(21, T=6, Hv=2, Hk=1, dk=6, dv=4)
+    gk = np.repeat(g[..., None], 6, axis=-1)
+    o_g, st_g = oracle.verify(q, k, v, beta, g, S0, [6], want_states=True)
+    o_k, st_k = oracle.kda_verify(q, k, v, beta, gk, S0, [6], want_states=True)
+    np.testing.assert_allclose(o_k, o_g, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st_k, st_g, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.kda_commit(q, k, v, beta, gk, S0, [4]),
+                               oracle.commit(q, k, v, beta, g, S0, [4]),
+                               rtol=0, atol=1e-13)
+
+
+def test_kda_is_online_regression_step_from_the_channel_decayed_state():
+    """Each KDA step is one gradient step of size beta on 0.5 ||S' khat -
+    v||^2 at S' = S diag(alpha) (torch autograd, fp64)."""
+    torch = pytest.importorskip("torch")
+    q, k, v, beta, gk, S0 = _kda_case(22, T=6)
+    o, st = oracle.kda_verify(q, k, v, beta, gk, S0, [6], want_states=True)
+    for h in range(2):
+        S = torch.tensor(S0[0, 0, h].T, dtype=torch.float64)
+        for t in range(6):
+            kh = torch.tensor(_unit(k[0, 0, t, 0]))
+            qh = torch.tensor(_unit(q[0, 0, t, 0]))
+            a = torch.exp(torch.tensor(gk[0, 0, t, h]))
+            Sd = (S * a[None, :]).detach().requires_grad_(True)
+            loss = 0.5 * torch.sum((Sd @ kh - torch.tensor(v[0, 0, t, h])) ** 2)
+            (grad,) = torch.autograd.grad(loss, Sd)
+            S = (Sd - beta[0, 0, t, h] * grad).detach()
+            np.testing.assert_allclose(st[0, 0, t, h].T, S.numpy(), rtol=0,
+                                       atol=1e-13)
+            np.testing.assert_allclose(o[0, 0, t, h], (S @ qh).numpy(),
+                                       rtol=0, atol=1e-13)
+
+
+def test_kda_exact_rational_product_form():
+    """Exact rationals: S_t = S_0 A_1..A_t + sum_s beta_s v_s k_s^T
+    A_{s+1}..A_t with A_s = diag(alpha_s) (I - beta_s k_s k_s^T)."""
+    dk, dv, T = 3, 2, 4
+    r = np.random.default_rng(23)
+    ri = lambda *s: r.integers(-4, 5, size=s)
+    k = [[Fraction(int(x), 4) for x in ri(dk)] for _ in range(T)]
+    qv = [[Fraction(int(x), 4) for x in ri(dk)] for _ in range(T)]
+    v = [[Fraction(int(x), 2) for x in ri(dv)] for _ in range(T)]
+    alpha = [[Fraction(int(a), 8) for a in r.integers(1, 9, size=dk)]
+             for _ in range(T)]
+    beta = [Fraction(1, 4), Fraction(1, 2), Fraction(3, 8), Fraction(1, 8)]
+    S0 = [[Fraction(int(x), 8) for x in ri(dk)] for _ in range(dv)]  # dv x dk
+
+    def A(s):
+        return [[alpha[s][i] * ((1 if i == j else 0) - beta[s] * k[s][i] * k[s][j])
+                 for j in range(dk)] for i in range(dk)]
+
+    exp_S = []
+    for t in range(T):
+        acc = S0
+        for s in range(t + 1):
+            acc = _mm(acc, A(s))
+        for s in range(t + 1):
+            term = [[beta[s] * v[s][i] * k[s][j] for j in range(dk)]
+                    for i in range(dv)]
+            for s2 in range(s + 1, t + 1):
+                term = _mm(term, A(s2))
+            acc = [[acc[i][j] + term[i][j] for j in range(dk)] for i in range(dv)]
+        exp_S.append(acc)
+    f = lambda x: np.array(x, dtype=np.float64)
+    q = f(qv).reshape(1, 1, T, 1, dk)
+    kk = f(k).reshape(1, 1, T, 1, dk)
+    vv = f(v).reshape(1, 1, T, 1, dv)
+    bb = f(beta).reshape(1, 1, T, 1)
+    gg = np.log(f(alpha)).reshape(1, 1, T, 1, dk)
+    S0s = f(S0).T.reshape(1, 1, 1, dk, dv)
+    o, st = oracle.kda_verify(q, kk, vv, bb, gg, S0s, [T], l2norm=False,
+                              want_states=True)
+    for t in range(T):
+        np.testing.assert_allclose(st[0, 0, t, 0].T, f(exp_S[t]), rtol=0,
+                                   atol=1e-13)
+        np.testing.assert_allclose(
+            o[0, 0, t, 0], f(exp_S[t]) @ f(qv[t]), rtol=0, atol=1e-13)
+
+
+def test_kda_channel_forgetting():
+    """alpha = 0 on one channel clears that column before the write: the new
+    column is u_t khat_tj with u_t computed from the cleared state."""
+    q, k, v, beta, gk, S0 = _kda_case(24, T=1)
+    gk[0, 0, 0, :, 2] = -np.inf
+    _, st = oracle.kda_verify(q, k, v, beta, gk, S0, [1], want_states=True)
+    kh = _unit(k[0, 0, 0, 0])
+    for h in range(2):
+        Sd = S0[0, 0, h].T * np.exp(gk[0, 0, 0, h])[None, :]   # dv x dk
+        assert np.all(Sd[:, 2] == 0)
+        u = beta[0, 0, 0, h] * (v[0, 0, 0, h] - Sd @ kh)
+        np.testing.assert_allclose(st[0, 0, 0, h].T[:, 2], u * kh[2],
+                                   rtol=0, atol=1e-14)
