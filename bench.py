@@ -83,7 +83,8 @@ def alg_flops_fused(t_lane, m_prev):
     return alg_flops_verify(t_lane) + NL * HV * DK * DV * 2 * int(np.sum(m_prev))
 
 
-def kernel_source_hash(files=("gdn_window.hip", "gdn_step.h")):
+def kernel_source_hash(files=("gdn_window.hip", "gdn_window_common.h",
+                              "gdn_step.h")):
     """sha256 of the kernel sources with // comments and blank lines removed
     (a comment edit leaves the recorded counters valid)."""
     import hashlib
@@ -108,7 +109,7 @@ def measured_traffic(kernel):
         return None
     k = rec.get(kernel)
     files = (("gdn_prefill.hip",) if kernel.startswith("prefill")
-             else ("gdn_window.hip", "gdn_step.h"))
+             else ("gdn_window.hip", "gdn_window_common.h", "gdn_step.h"))
     if not k or k.get("source_sha256") != kernel_source_hash(files):
         return None
     return float(k["bytes_per_launch"])
@@ -241,6 +242,52 @@ def bench_tree(reps=20, warmup=3):
             "node_updates_per_s": upd / ((ms_v + ms_c) * 1e-3)}
 
 
+def bench_kda(reps=20, warmup=3):
+    """KDA (per-channel decay) verify + commit on the same batch shape:
+    8 lanes x 48 layers x 32/16 heads, d = 128, T = 16, m ~ U{0..16};
+    event-timed."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
+    t_lane = np.full(N, T, dtype=np.int32)
+    w = gs.window_inputs(shape, (10, 0))
+
+    def d16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = d16(w.q), d16(w.k), d16(w.v)
+    beta = torch.from_numpy(w.beta).to(dev)
+    g = torch.from_numpy(gs.kda_gates(shape, (10, 0))).to(dev)
+    S = torch.from_numpy(gs.initial_state(shape, (10, 0))).to(dev)
+    o = torch.empty((NL, N, T, HV, DV), device=dev)
+    rec = torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8, device=dev)
+    ms_all = [gs.accepted_uniform(t_lane, (10, 1 + r)) for r in range(reps + warmup)]
+    stream = torch.cuda.current_stream()
+    for r in range(warmup):
+        gdn.kda_verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
+        gdn.kda_commit(dims, ms_all[r], t_lane, rec, S, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(reps)]
+    for r, e in enumerate(evs):
+        e[0].record(stream)
+        gdn.kda_verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
+        e[1].record(stream)
+        gdn.kda_commit(dims, ms_all[warmup + r], t_lane, rec, S, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    upd = N * T * NL * HV
+    return {"workload": "KDA verify+commit: 8 lanes x 48 layers x 32/16 heads, "
+                        "d=128, T=16, m ~ U{0..16}",
+            "verify_ms": ms_v, "commit_ms": ms_c,
+            "updates_per_s": upd / ((ms_v + ms_c) * 1e-3)}
+
+
 def bench_snapshot(reps=5):
     """Snapshot of the whole 8-lane, 48-layer state (768 MiB) to a device
     buffer and to pinned host memory, and the restore from pinned memory:
@@ -320,6 +367,7 @@ def main():
                          "one is the headline when timed)")
     ap.add_argument("--no-snapshot", action="store_true")
     ap.add_argument("--no-tree", action="store_true")
+    ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -505,6 +553,8 @@ def main():
         out["state_snapshot"] = bench_snapshot()
     if not args.no_tree:
         out["draft_tree"] = bench_tree()
+    if not args.no_kda:
+        out["kda"] = bench_kda()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

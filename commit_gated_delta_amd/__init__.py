@@ -25,6 +25,7 @@ GDN_MAX_T = 64
 
 EXPORTED = ("gdn_records_bytes", "gdn_verify", "gdn_commit",
             "gdn_commit_verify", "gdn_verify_tree", "gdn_commit_path",
+            "gdn_kda_records_bytes", "gdn_kda_verify", "gdn_kda_commit",
             "gdn_state_snapshot", "gdn_state_restore",
             "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_strerror", "gdn_last_error")
@@ -74,6 +75,12 @@ def _load_library():
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, f,
                                       ctypes.c_int, vp]
     lib.gdn_commit_verify.restype = ctypes.c_int
+    lib.gdn_kda_records_bytes.argtypes = [dp]
+    lib.gdn_kda_records_bytes.restype = sz
+    lib.gdn_kda_verify.argtypes = lib.gdn_verify.argtypes
+    lib.gdn_kda_verify.restype = ctypes.c_int
+    lib.gdn_kda_commit.argtypes = lib.gdn_commit.argtypes
+    lib.gdn_kda_commit.restype = ctypes.c_int
     lib.gdn_verify_tree.argtypes = [dp, ip, ip, vp, vp, vp, ctypes.c_int, vp,
                                     vp, vp, vp, vp, vp, f, ctypes.c_int, vp]
     lib.gdn_verify_tree.restype = ctypes.c_int
@@ -183,6 +190,35 @@ def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
     if raw_status:
         return st
     _check(st, "gdn_commit_verify")
+
+
+def kda_records_bytes(dims: Dims) -> int:
+    return int(lib.gdn_kda_records_bytes(ctypes.byref(dims)))
+
+
+def kda_verify(dims: Dims, t_lane, q, k, v, beta, g, S, o, records,
+               dbg_states=None, scale=1.0, l2norm=True, stream=None,
+               raw_status=False):
+    """gdn_kda_verify; g is [NL][N][T][Hv][d_k] (per-channel log-decay)."""
+    st = lib.gdn_kda_verify(ctypes.byref(dims), _int_array(t_lane, dims.n_lanes),
+                            _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                            _ptr(beta), _ptr(g), _ptr(S), _ptr(o),
+                            _ptr(records), _ptr(dbg_states), float(scale),
+                            GDN_FLAG_L2NORM_QK if l2norm else 0,
+                            _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_kda_verify")
+
+
+def kda_commit(dims: Dims, m_lane, t_lane, records, S, stream=None,
+               raw_status=False):
+    st = lib.gdn_kda_commit(ctypes.byref(dims), _int_array(m_lane, dims.n_lanes),
+                            _int_array(t_lane, dims.n_lanes), _ptr(records),
+                            _ptr(S), _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_kda_commit")
 
 
 def _table(rows, n, t_max, fill):

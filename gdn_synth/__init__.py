@@ -247,3 +247,16 @@ def accepted_tree_paths(parent, t_lane, key: tuple):
         node = int(r.integers(-1, int(T)))
         paths.append([] if node < 0 else tree_path(parent[n], node))
     return paths
+
+
+# ------------------------------------------------------------- KDA gates
+_STREAM_KDA = 11
+
+
+def kda_gates(shape: WindowShape, key: tuple, g_mean: float = 0.0):
+    """Per-channel log-decays of a KDA window: g = -softplus(N(g_mean, 1)),
+    f32 [n_layers, n_lanes, t_max, h_v, d_k]."""
+    s = shape
+    r = rng(_STREAM_KDA, *key)
+    x = r.standard_normal((s.n_layers, s.n_lanes, s.t_max, s.h_v, s.d_k)) + g_mean
+    return (-_softplus(x)).astype(np.float32)

@@ -15,6 +15,8 @@
  *   gdn_commit_verify    both in one launch: commit the previous window's
  *                        accepted prefix, then verify the next window from
  *                        the committed state without reading it again.
+ *   gdn_kda_verify,      verify and commit of the per-channel-decay sibling
+ *   gdn_kda_commit       (KDA), same window protocol.
  *   gdn_state_snapshot,  copy the recurrent state of chosen lanes out to a
  *   gdn_state_restore    compact snapshot (device or pinned host memory) and
  *                        back, for requests that are paused and resumed.
@@ -259,6 +261,33 @@ int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
                         const float* g, const float* S_init, float* S_final,
                         float* o, float* checkpoints, void* workspace,
                         size_t ws_bytes, float scale, int flags, void* stream);
+
+/*
+ * KDA: the sibling rule with one decay per key channel (Kimi Delta
+ * Attention, Kimi Linear, 2025; the review names its recurrent state beside
+ * GDN's and a kda_replay op contract).  Per value head, with
+ * alpha_t = exp(g_t) a d_k vector:
+ *   S'_t = S_{t-1} diag(alpha_t),  u_t = beta_t (v_t - S'_t khat_t),
+ *   S_t = S'_t + u_t khat_t^T,     o_t = scale * S_t qhat_t.
+ * gdn_kda_verify / gdn_kda_commit have the contract of gdn_verify /
+ * gdn_commit (S0 untouched by verify; commit(m) bitwise equal to verify's
+ * state after token m) with these differences:
+ *   g        device f32 [n_layers][n_lanes][t_max][h_v][d_k] (per channel)
+ *   records  gdn_kda_records_bytes(dims) bytes: per token the raw key rows
+ *            (f32 [h_k][d_k]), u_t / sqrt(|k_t|^2 + 1e-6) (f32 [h_v][d_v])
+ *            and alpha_t (f32 [h_v][d_k])
+ * Supported: d_k == 128 (GDN_EUNSUPPORTED otherwise; gdn_kda_records_bytes
+ * returns 0).
+ */
+size_t gdn_kda_records_bytes(const gdn_dims* dims);
+int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
+                   const void* q, const void* k, const void* v, int in_dtype,
+                   const float* beta, const float* g, const float* S, float* o,
+                   void* records, float* dbg_states, float scale, int flags,
+                   void* stream);
+int gdn_kda_commit(const gdn_dims* dims, const int32_t* m_lane,
+                   const int32_t* t_lane, const void* records, float* S,
+                   void* stream);
 
 /*
  * Recurrent-state snapshot and restore.  Under memory pressure the review's

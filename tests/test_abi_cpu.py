@@ -159,6 +159,36 @@ def test_commit_verify_rejects_bad_arguments_on_host():
     assert cv(d, [0, 0], [2, 1], [0, 0], rec_prev=None) == gdn.GDN_OK
 
 
+def test_kda_calls_reject_bad_arguments_on_host():
+    d = _dims()
+    n = gdn.kda_records_bytes(d)
+    ntok = 1 * 2 * 8
+    # raw keys f32 [h_k][d_k] + ut f32 [h_v][d_v] + alpha f32 [h_v][d_k]
+    assert n >= ntok * (2 * 128 * 4 + 4 * 128 * 4 + 4 * 128 * 4)
+    assert n % 256 == 0
+    assert gdn.kda_records_bytes(_dims(d_k=64)) == 0
+    f = dict(q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),
+             g=_Fake(gdn.GDN_F32), S=_Fake(gdn.GDN_F32), o=_Fake(gdn.GDN_F32),
+             rec=_Fake(gdn.GDN_F32))
+
+    def kv(dims, t, **over):
+        a = dict(f)
+        a.update(over)
+        return gdn.kda_verify(dims, t, a["q"], a["k"], a["v"], a["beta"],
+                              a["g"], a["S"], a["o"], a["rec"], stream=0,
+                              raw_status=True)
+
+    assert kv(_dims(d_k=64), [1, 1]) == gdn.GDN_EUNSUPPORTED
+    assert kv(d, [9, 1]) == gdn.GDN_EINVAL
+    assert kv(d, [1, 1], g=None) == gdn.GDN_EINVAL
+    assert kv(d, [0, 0]) == gdn.GDN_OK
+    kc = lambda m, t, dims=d: gdn.kda_commit(dims, m, t, f["rec"], f["S"],
+                                             stream=0, raw_status=True)
+    assert kc([3, 0], [2, 1]) == gdn.GDN_EINVAL
+    assert kc([0, 0], [2, 1], _dims(d_k=32)) == gdn.GDN_EUNSUPPORTED
+    assert kc([0, 0], [2, 1]) == gdn.GDN_OK
+
+
 def test_tree_calls_reject_bad_arguments_on_host():
     d = _dims(n_lanes=2, t_max=4)
     a = dict(q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),

@@ -1,0 +1,143 @@
+"""GPU parity of gdn_kda_verify / gdn_kda_commit (per-channel decay) against
+the fp64 oracle, and bit-exact replay: commit(m) equals verify's own state
+after token m.  Every call goes through the C ABI; tolerance 2e-4
+block-relative."""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+import oracle
+from tests.gpu_util import TOL, o_rel_err, s_rel_err, to_dev, window_to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import commit_gated_delta_amd as gdn  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _kda_run(dims, w, gk, S_dev, dbg=True):
+    q, k, v, beta, _ = window_to_dev(w, torch)
+    g = to_dev(gk, torch)
+    o = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
+                    dims.d_v), float("nan"), device="cuda")
+    rec = torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8,
+                      device="cuda")
+    d = None
+    if dbg:
+        d = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
+                        dims.d_k, dims.d_v), float("nan"), device="cuda")
+    gdn.kda_verify(dims, w.t_lane, q, k, v, beta, g, S_dev, o, rec, d)
+    return o, rec, d
+
+
+CASES = [
+    # (name, NL, N, Hv, Hk, dv, T, bf16, g_fill)
+    ("bf16_two_col_blocks", 2, 3, 4, 2, 128, 16, True, None),
+    ("f32_dv200", 1, 2, 3, 3, 200, 7, False, None),
+    ("bf16_channel_forgetting", 1, 2, 4, 2, 64, 12, True, "zero"),
+    ("bf16_strong_decay", 1, 2, 4, 2, 128, 16, True, "strong"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_kda_parity_and_bitexact_replay(case):
+    name, NL, N, Hv, Hk, dv, T, bf16, fill = case
+    say("case", name)
+    shape = gs.WindowShape(NL, N, Hv, Hk, 128, dv, T)
+    key = (600, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    gk = gs.kda_gates(shape, key)
+    if fill == "zero":
+        gk[:, :, 2, :, ::3] = -np.inf     # alpha = 0 on every third channel
+        gk[:, :, 7, :, :] = -200.0        # underflows to 0 in f32
+    elif fill == "strong":
+        gk[:] -= 4.0
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _kda_run(dims, w, gk, S_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(S_dev.cpu(), torch.from_numpy(S0)), "verify wrote S0"
+    o_np, dbg_np = o.cpu().numpy(), dbg.cpu().numpy()
+    q64, k64, v64, b64, _ = w.as_f64()
+    g64 = gk.astype(np.float64)
+    o_ref, st_ref = oracle.kda_verify(q64, k64, v64, b64, g64, S0, w.t_lane,
+                                      want_states=True)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    say("  o err %.2e" % e_o)
+    assert e_o <= TOL
+    for t in range(T):
+        lanes = [n for n in range(N) if w.t_lane[n] > t]
+        if lanes:
+            assert s_rel_err(dbg_np[:, lanes, t], st_ref[:, lanes, t]) <= TOL, t
+    for m in range(0, T + 1, 3):
+        m_lane = np.minimum(m, w.t_lane)
+        S_c = to_dev(S0, torch)
+        gdn.kda_commit(dims, m_lane, w.t_lane, rec, S_c)
+        S_c = S_c.cpu().numpy()
+        for n in range(N):
+            mm = int(m_lane[n])
+            want = S0[:, n] if mm == 0 else dbg_np[:, n, mm - 1]
+            assert np.array_equal(S_c[:, n], want), (m, n)
+        S_ref = oracle.kda_commit(q64, k64, v64, b64, g64, S0, m_lane)
+        assert s_rel_err(S_c, S_ref) <= TOL
+
+
+def test_kda_zero_gates_are_bitwise_identity():
+    """beta = 0 and alpha = 1 on every channel: S * 1 then fma(0, k, S)
+    leave the state bit for bit."""
+    shape = gs.WindowShape(1, 2, 4, 2, 128, 128, 8)
+    w = gs.window_inputs(shape, (601,))
+    w.beta[:] = 0.0
+    gk = np.zeros((1, 2, 8, 4, 128), np.float32)
+    S0 = gs.initial_state(shape, (601,))
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    _, rec, _ = _kda_run(dims, w, gk, S_dev, dbg=False)
+    gdn.kda_commit(dims, w.t_lane, w.t_lane, rec, S_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(S_dev.cpu().numpy(), S0)
+
+
+def test_kda_chained_rounds_48_layers():
+    """48 layers x 2 lanes x 32/16 heads, T = 16, m ~ U{0..16}, 20 chained
+    rounds; the oracle follows layers 0 and 47."""
+    shape = gs.WindowShape(48, 2, 32, 16, 128, 128, 16)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S0 = gs.initial_state(shape, (602,))
+    S_dev = to_dev(S0, torch)
+    sl = [0, 47]
+    S_or = S0[sl].astype(np.float64)
+    rec = torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8,
+                      device="cuda")
+    o = torch.empty((48, 2, 16, 32, 128), device="cuda")
+    t_lane = np.full(2, 16, np.int32)
+    for r in range(20):
+        w = gs.window_inputs(shape, (602, r))
+        gk = gs.kda_gates(shape, (602, r), g_mean=-1.0)
+        m = gs.accepted_uniform(t_lane, (602, r))
+        q, k, v, beta, _ = window_to_dev(w, torch)
+        gdn.kda_verify(dims, t_lane, q, k, v, beta, to_dev(gk, torch), S_dev,
+                       o, rec)
+        gdn.kda_commit(dims, m, t_lane, rec, S_dev)
+        torch.cuda.synchronize()
+        q64, k64, v64 = (gs.bf16_bits_to_f64(a[sl]) for a in (w.q, w.k, w.v))
+        b64, g64 = w.beta[sl].astype(np.float64), gk[sl].astype(np.float64)
+        o_ref, _ = oracle.kda_verify(q64, k64, v64, b64, g64, S_or, t_lane)
+        S_or = oracle.kda_commit(q64, k64, v64, b64, g64, S_or, m)
+        e_o = o_rel_err(o[sl].cpu().numpy(), o_ref, t_lane)
+        e_s = s_rel_err(S_dev[sl].cpu().numpy(), S_or)
+        if r % 5 == 0 or r == 19:
+            say("  round %d: o err %.2e S err %.2e" % (r, e_o, e_s))
+        assert e_o <= TOL and e_s <= TOL
