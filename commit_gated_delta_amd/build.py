@@ -22,6 +22,9 @@ FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
          "-ffp-contract=off", "-fno-fast-math",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
+# The prefill state chain scales and splits its MFMA accumulators every
+# chunk; keeping them in ordinary VGPRs avoids a copy through AGPRs.
+EXTRA = {"gdn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -29,7 +32,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(LIB_DIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

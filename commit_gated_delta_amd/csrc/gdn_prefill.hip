@@ -27,13 +27,15 @@
 //       the workspace as split bf16 pairs (hi = bf16(x), lo = bf16(x - hi)),
 //       with the per-row scale vectors.
 //   p2  one workgroup per (sequence, value head, 16-column tile of d_v),
-//       sequential over the chunks; the d_k x 16 state tile stays in f32 MFMA
-//       accumulators (wave w holds rows 32w..32w+31).  Products with an f32
-//       operand use split bf16: two passes against an exact bf16 operand
-//       (K H, Q H, K^T V'), three passes f32 x f32 (T X, P V_new); about
-//       2^-17 relative error per product.  The state is never rounded below
-//       f32, so a run resumed from a checkpoint is bitwise the straight run.
-//       The output O of each chunk is produced here too (no separate pass).
+//       sequential over the chunks, with one wave per role: the state chain
+//       (the d_k x 16 state tile in f32 MFMA accumulators of one wave), two
+//       output waves and one staging wave (details at p2 below).  Products
+//       with an f32 operand use split bf16: two passes against an exact bf16
+//       operand (K H, Q H, K^T V'), three passes f32 x f32 (T X, P V_new);
+//       about 2^-17 relative error per product.  The state is never rounded
+//       below f32, so a run resumed from a checkpoint is bitwise the straight
+//       run.  The output O of each chunk is produced here too (no separate
+//       pass).
 //   Checkpoints: the state after every token count that is a positive
 //   multiple of the interval (context_cache.checkpoint_interval, NInfer
 //   technical review, blog.123qwe.co.kr post 4624, section "Architecture 2").
@@ -47,6 +49,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -70,17 +73,31 @@ struct PDims {
 };
 
 // Workspace per (sequence, chunk, value head).  T and P are stored as MFMA
-// A-operand fragments in the order p2 reads them: for wave w, piece x (T hi,
-// T lo for k-step 0, the same for k-step 1, then P likewise) and lane l, 16
-// bytes holding row 16w + l%16, columns 32*ks + 8*(l/16) + 0..7, at
-// ((w*8 + x)*64 + l)*16 -- one load instruction of a wave reads 1 KiB of
-// consecutive bytes.
+// A-operand fragments, 1 KiB each (lane l: 16 bytes at l*16, so one load or
+// copy instruction of a wave moves 1 KiB of consecutive bytes).  Both are
+// lower triangular, so of the (row block mi, k-step kb) pairs of 16 rows x
+// 32 columns only six are nonzero: pair index pair_of(mi, kb) for
+// (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); each pair has a hi and a lo fragment
+// (slots 2*pair and 2*pair + 1).  Lane l of a fragment holds row
+// 16*mi + l%16 and, with g = l/16,
+//   P: columns 32*kb + 8g + 0..7                       (natural order)
+//   T: columns 32*kb + 4g + 0..3, 32*kb + 16 + 4g + 0..3 (order "pi")
+// The pi order matches the MFMA result layout: a lane's result rows
+// 4g + 0..3 of two adjacent 16-row blocks are exactly the contraction entries
+// that the lane supplies in pi order, so results feed the next product from
+// registers (the contraction is a sum; both operands use the same order).
 struct WsLayout {
-  static constexpr size_t kFrag = 4 * 64 * 8 * 16;               // 32 KiB
-  static constexpr size_t kVec = kFrag;      // float [64][4]: sb sk so sd
-  static constexpr size_t kGc = kVec + kC * 4 * sizeof(float);   // float
-  static constexpr size_t kBytes = (kGc + sizeof(float) + 255) & ~size_t(255);
+  static constexpr size_t kSlot = 64 * 16;
+  static constexpr size_t kT = 0;              // 12 slots
+  static constexpr size_t kP = 12 * kSlot;     // 12 slots
+  static constexpr size_t kVec = 24 * kSlot;   // float [4][64]: sb sk so sd
+  static constexpr size_t kGc = kVec + 4 * kC * sizeof(float);  // {gamma_63, 0, 0, 0}
+  static constexpr size_t kBytes = (kGc + 16 + 255) & ~size_t(255);
 };
+
+__host__ __device__ constexpr int pair_of(int mi, int kb) {
+  return mi < 2 ? mi : 2 * mi - 2 + kb;
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -294,92 +311,195 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     __syncthreads();
   }
 
-  // ---- write T, P (split bf16, fragment order) and the row vectors
+  // ---- write T (pi order), P (natural order) as split bf16 fragments, and
+  // the row vectors
   uint8_t* wsb = ws + ((size_t)bid) * WsLayout::kBytes;
   {
-    const int i = 16 * w + l % 16;
-    uint4* dst = reinterpret_cast<uint4*>(wsb) + (size_t)w * 8 * 64 + l;
+    const int i = 16 * w + l % 16, g4 = l / 16;
+    for (int kb = 0; kb < (w >= 2 ? 2 : 1); ++kb) {
+      const int pr = pair_of(w, kb);
+      uint4* tdst = reinterpret_cast<uint4*>(wsb + WsLayout::kT) + 2 * pr * 64 + l;
+      uint4* pdst = reinterpret_cast<uint4*>(wsb + WsLayout::kP) + 2 * pr * 64 + l;
+      uint32_t hi[4], lo[4];
+      const int ja = 32 * kb + 4 * g4, jb = ja + 16;
+      split2(Ts[i * FS + ja], Ts[i * FS + ja + 1], hi[0], lo[0]);
+      split2(Ts[i * FS + ja + 2], Ts[i * FS + ja + 3], hi[1], lo[1]);
+      split2(Ts[i * FS + jb], Ts[i * FS + jb + 1], hi[2], lo[2]);
+      split2(Ts[i * FS + jb + 2], Ts[i * FS + jb + 3], hi[3], lo[3]);
+      tdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      tdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      const int j0 = 32 * kb + 8 * g4;
 #pragma unroll
-    for (int mat = 0; mat < 2; ++mat) {
-      const float* M = mat ? Ps : Ts;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int j0 = 32 * ks + 8 * (l / 16);
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          split2(M[i * FS + j0 + 2 * e], M[i * FS + j0 + 2 * e + 1], hi[e], lo[e]);
-        dst[(mat * 4 + ks * 2 + 0) * 64] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        dst[(mat * 4 + ks * 2 + 1) * 64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      }
+      for (int e = 0; e < 4; ++e)
+        split2(Ps[i * FS + j0 + 2 * e], Ps[i * FS + j0 + 2 * e + 1], hi[e], lo[e]);
+      pdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      pdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
   }
   if (tid < kC) {
     const int i = tid;
     const float Gc = G_s[kC - 1];
     const float gam = __expf(G_s[i]);
-    float4 v;
-    v.x = b_s[i];                                // sb: beta
-    v.y = b_s[i] * gam * rk_s[i];                // sk: beta gamma rk
-    v.z = gam * rq_s[i] * d.scale;               // so: gamma rq scale
-    v.w = rk_s[i] * __expf(Gc - G_s[i]);         // sd: rk exp(G_63 - G_i)
-    reinterpret_cast<float4*>(wsb + WsLayout::kVec)[i] = v;
-    if (i == 0) *reinterpret_cast<float*>(wsb + WsLayout::kGc) = __expf(Gc);
+    float* vec = reinterpret_cast<float*>(wsb + WsLayout::kVec);
+    vec[i] = b_s[i];                                  // sb: beta
+    vec[kC + i] = b_s[i] * gam * rk_s[i];             // sk: beta gamma rk
+    vec[2 * kC + i] = gam * rq_s[i] * d.scale;        // so: gamma rq scale
+    vec[3 * kC + i] = rk_s[i] * __expf(Gc - G_s[i]);  // sd: rk exp(G_63 - G_i)
+    if (i == 0)
+      *reinterpret_cast<float4*>(wsb + WsLayout::kGc) = make_float4(__expf(Gc), 0.f, 0.f, 0.f);
   }
 }
 
 // ------------------------------------------------------------------ p2
-// Per-chunk operands that a lane prefetches one chunk ahead.
-struct Pre {
-  uint4 q[4];     // A fragments of the lane's Q row (4 k-steps)
-  uint4 tp[8];    // A fragments of T and P (WsLayout order)
-  uint32_t v[4];  // bf16 V[row 16w + 4*(l/16) + e][column], in the low half
-  float4 vec[4];  // sb sk so sd of those rows
-  float gc;
-};
+// One workgroup of four waves per (sequence, value head, 16-column tile of
+// d_v), sequential over the chunks.  The work is split by role so that the
+// chunk-to-chunk recurrence never waits on global memory or on other waves:
+//   wave 0  the state chain.  Holds the 128 x 16 f32 state tile H in MFMA
+//           result registers and per chunk computes K H, X, V_new = T X and
+//           H' = gamma_63 H + K^T diag(sd) V_new.  Every operand comes from
+//           LDS (read one stage ahead) or from its own registers (pi order,
+//           see WsLayout).  It publishes H and V_new to LDS for the output
+//           waves.
+//   wave 1, 2  O = diag(so) Q H + P V_new for row blocks {0, 3} / {1, 2},
+//           with Q and P loaded straight into registers one chunk ahead.
+//   wave 3  stages the chain's operands (K rows, T fragments, the V tile,
+//           the row vectors) into LDS two chunks ahead.
+// Several waves issue global loads because one wave alone draws only about
+// a quarter of what a CU can take from L2.  One barrier per chunk.  Interval
+// c (between barriers) holds the second half of chunk c on the chain
+// (V_new -> H') and the first half of chunk c + 1 (K H -> X -> V_new), while
+// the output waves produce O of chunk c.  Every LDS buffer rotates over
+// three chunks (c, c + 1 in use, c + 2 being written).
+constexpr int kP2Threads = 256;
 
-__device__ __forceinline__ uint2 pack4(const uint32_t (&x)[4], int e0) {
-  return make_uint2(x[e0], x[e0 + 1]);
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// Swizzle of the 4-element groups of a staged K row r: group G is stored at
+// G ^ ksw(r).  The chain reads K in two patterns -- 8-byte A-fragment pieces
+// (16 rows x 2 groups per half wave) and transposing reads (8 rows x 4
+// groups) -- and this swizzle spreads both over distinct LDS banks.
+__device__ __forceinline__ int ksw(int r) {
+  r &= 15;
+  return 4 * (r & 3) + (r >> 2) + 16 * ((r >> 2) & 1);
 }
 
-__global__ __launch_bounds__(kThreads) void p2_kernel(
-    const u16* __restrict__ q, const u16* __restrict__ k,
-    const u16* __restrict__ v, const uint8_t* __restrict__ ws,
-    const float* __restrict__ S_init, float* __restrict__ S_final,
-    float* __restrict__ o, float* __restrict__ ckpt, PDims d) {
-  constexpr int KS = kD + 8;   // Kr row stride (bf16)
-  constexpr int TS = kC + 8;   // Kt / column-major tile row stride (bf16)
-  constexpr int HS = kD + 8;   // Hb row stride (bf16)
-  // double buffers (chunk parity) for the K copies and the state operand
-  __shared__ __attribute__((aligned(16))) u16 Kr[2][kC * KS];      // K rows
-  __shared__ __attribute__((aligned(16))) u16 Kt[2][kD * TS];      // K^T
-  __shared__ __attribute__((aligned(16))) u16 Hb[2][2][kTile * HS];// H hi/lo [n][dk]
-  __shared__ __attribute__((aligned(16))) u16 Xb[2][kTile * TS];   // X hi/lo [n][j]
-  __shared__ __attribute__((aligned(16))) u16 Vb[2][kTile * TS];   // V_new hi/lo
-  __shared__ __attribute__((aligned(16))) u16 Db[2][kTile * TS];   // sd V_new hi/lo
-  // Kt holds K^T with the 8-entry groups of each row XOR-swizzled by
-  // (dk / 8) % 8, so that the transposing stores of one wave spread over the
-  // LDS banks while every 8-entry group stays 16-byte aligned for the reads.
-  auto kt_at = [&](int dk, int j) {
-    return dk * TS + 8 * ((j >> 3) ^ ((dk >> 3) & 7)) + (j & 7);
-  };
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group g, lane
+// i receives element i%4 of the 8 bytes addressed by lane 16g + 4e + i/4 as
+// its element e (e = 0..3).
+__device__ __forceinline__ uint2 tr_read(const u16* p) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
 
-  // block -> (sequence, head, tile); the tiles of a head share one XCD
-  const int nb = gridDim.x;
-  int b = blockIdx.x;
-  if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
-  const int tile = b % (kD / kTile);
-  const int h = (b / (kD / kTile)) % d.Hv;
-  const int s = b / ((kD / kTile) * d.Hv);
-  const int kh = h / d.group;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int l = tid % 64;
-  const int n = l % 16;       // column inside the tile (C/D/B layouts)
-  const int q4 = l / 16;      // 0..3
+__device__ __forceinline__ bf16x8 frag(uint2 a, uint2 b) {
+  return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Split-bf16 words of two result tiles in pi order: elements 0..3 from tile
+// t0, 4..7 from tile t1.
+__device__ __forceinline__ void split_pi(const f32x4& t0, const f32x4& t1,
+                                         uint32_t (&hi)[4], uint32_t (&lo)[4]) {
+  split2(t0[0], t0[1], hi[0], lo[0]);
+  split2(t0[2], t0[3], hi[1], lo[1]);
+  split2(t1[0], t1[1], hi[2], lo[2]);
+  split2(t1[2], t1[3], hi[3], lo[3]);
+}
+
+__device__ __forceinline__ bf16x8 words(const uint32_t (&x)[4]) {
+  return as_bf16x8(make_uint4(x[0], x[1], x[2], x[3]));
+}
+
+// Operands staged into LDS by the staging wave, in flight from one interval
+// to the next.
+struct KvTransit {
+  uint4 k[16];  // 64 K rows x 128 columns
+  uint4 t[12];  // the T fragments
+  uint4 v[2];   // 64 rows x 16 columns of V
+  uint4 vec;    // the row vectors
+  uint4 gc;     // gamma_63
+};
+
+// Per-chunk operands of an output wave (row blocks mA with one k-step, mB
+// with two).
+struct OutOps {
+  uint4 qa[4], qb[4];  // Q A fragments (natural order)
+  uint4 p[3][2];       // P fragments (hi, lo): (mA,0), (mB,0), (mB,1)
+};
+
+// LDS of a p2 workgroup, shared by the role functions below.
+struct P2Lds {
+  __attribute__((aligned(16))) u16 Kr[3][kC * kD];        // K rows, swizzled
+  __attribute__((aligned(16))) uint4 Tf[3][12][64];       // T fragments
+  __attribute__((aligned(16))) u16 Vt[3][kC * kTile];     // V tile [row][col]
+  __attribute__((aligned(16))) float Vec[3][4 * kC + 4];  // sb sk so sd, gamma
+  __attribute__((aligned(16))) uint4 Hf[3][8][64];        // H (natural B)
+  __attribute__((aligned(16))) float Vf[3][2][64][8];     // V_new f32 (natural B rows)
+};
+__shared__ P2Lds p2lds;
+
+// A pointer argument made wave-uniform, rebuilt as a global-memory pointer
+// (cast back to a generic pointer, which address-space inference turns into
+// global loads and stores rather than flat ones).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  typedef T __attribute__((address_space(1))) GlobalT;
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  GlobalT* gp = reinterpret_cast<GlobalT*>(((uint64_t)hi << 32) | lo);
+  return (T*)gp;
+}
+
+__device__ __forceinline__ PDims uniform_dims(const PDims& a) {
+  PDims r;
+  r.n_seqs = __builtin_amdgcn_readfirstlane(a.n_seqs);
+  r.L = __builtin_amdgcn_readfirstlane(a.L);
+  r.Hv = __builtin_amdgcn_readfirstlane(a.Hv);
+  r.Hk = __builtin_amdgcn_readfirstlane(a.Hk);
+  r.group = __builtin_amdgcn_readfirstlane(a.group);
+  r.n_chunks = __builtin_amdgcn_readfirstlane(a.n_chunks);
+  r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
+  r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
+  r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
+  return r;
+}
+
+// The two roles are separate functions so that the compiler allocates
+// registers for each on its own (inlined into one kernel, the barriers that
+// both roles execute get merged and the state of both roles is kept live
+// at once).
+static __device__ __attribute__((noinline)) void p2_chain(
+    const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
+    const float* S_init_, float* S_final_, float* o_, float* ckpt_,
+    const PDims d_, const int tile_, const int h_, const int s_, const int kh_) {
+  // arguments of a device function arrive in VGPRs: make their uniformity
+  // explicit so that addresses and branches stay scalar
+  const u16* __restrict__ q = uniform_ptr(q_);
+  const u16* __restrict__ k = uniform_ptr(k_);
+  const u16* __restrict__ v = uniform_ptr(v_);
+  const uint8_t* __restrict__ ws = uniform_ptr(ws_);
+  const float* __restrict__ S_init = uniform_ptr(S_init_);
+  float* __restrict__ S_final = uniform_ptr(S_final_);
+  float* __restrict__ o = uniform_ptr(o_);
+  float* __restrict__ ckpt = uniform_ptr(ckpt_);
+  const PDims d = uniform_dims(d_);
+  const int tile = __builtin_amdgcn_readfirstlane(tile_);
+  const int h = __builtin_amdgcn_readfirstlane(h_);
+  const int s = __builtin_amdgcn_readfirstlane(s_);
+  const int kh = __builtin_amdgcn_readfirstlane(kh_);
+  (void)q; (void)k; (void)v; (void)S_init; (void)S_final; (void)o; (void)ckpt; (void)kh;
+  auto& Kr = p2lds.Kr;
+  auto& Tf = p2lds.Tf;
+  auto& Vt = p2lds.Vt;
+  auto& Vec = p2lds.Vec;
+  auto& Hf = p2lds.Hf;
+  auto& Vf = p2lds.Vf;
+  const int l = threadIdx.x % 64;
+  const int n = l % 16;   // result column inside the tile
+  const int g = l / 16;   // lane group
   const int col = kTile * tile + n;
   const int nch = d.n_chunks;
-
   // per-sequence bases; element offsets below fit in 32 bits (host check)
   const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
@@ -388,244 +508,500 @@ __global__ __launch_bounds__(kThreads) void p2_kernel(
   const uint8_t* __restrict__ wss =
       ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
-
-  // state fragments: wave w holds dk rows 32w + 16*mt + 4*q4 + e, column n
-  f32x4 H[2];
+  (void)qs; (void)kseq; (void)vs; (void)os; (void)wss; (void)ws_chunk;
+  (void)Kr; (void)Tf; (void)Vt; (void)Vec; (void)Hf; (void)Vf; (void)col;
+  // ================================================================ chain
+  // H[mb]: state rows dk = 16*mb + 4g + e, column col
+  f32x4 H[8];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 32 * w + 16 * mt + 4 * q4 + e;
-      H[mt][e] = S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
-    }
-
-  auto write_H = [&](int buf) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      uint32_t hi[2], lo[2];
-      split2(H[mt][0], H[mt][1], hi[0], lo[0]);
-      split2(H[mt][2], H[mt][3], hi[1], lo[1]);
-      const int r = 32 * w + 16 * mt + 4 * q4;
-      *reinterpret_cast<uint2*>(&Hb[buf][0][n * HS + r]) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(&Hb[buf][1][n * HS + r]) = make_uint2(lo[0], lo[1]);
-    }
-  };
-
-  // Loads are unconditional: rows past the end of the sequence are read from
-  // the last valid row instead.  Their values never reach a result: P1 gives
-  // such rows beta = 0, so X, V_new and their state contributions are 0, and
-  // their output rows are not stored.  (A load under a branch would make the
-  // compiler wait for it at the end of the branch, which defeats the
-  // one-chunk-ahead prefetch.)
-  auto prefetch = [&](int c, Pre& p) {
-    const int t0 = c * kC;
-    const int last = min(kC, d.L - t0) - 1;
-    const uint4* wf = reinterpret_cast<const uint4*>(wss + (size_t)c * ws_chunk) +
-                      w * 8 * 64 + l;
-    const uint32_t qoff =
-        ((uint32_t)(t0 + min(16 * w + n, last)) * d.Hk + kh) * kD + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      p.q[ks] = *reinterpret_cast<const uint4*>(qs + qoff + 32 * ks);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) p.tp[x] = wf[x * 64];
-    const float4* vec = reinterpret_cast<const float4*>(
-        wss + (size_t)c * ws_chunk + WsLayout::kVec);
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * q4 + e;
-      p.v[e] = vs[((uint32_t)(t0 + min(r, last)) * d.Hv + h) * kD + col];
-      p.vec[e] = vec[r];
+      const int r = 16 * mb + 4 * g + e;
+      H[mb][e] = S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
     }
-    p.gc = *reinterpret_cast<const float*>(wss + (size_t)c * ws_chunk + WsLayout::kGc);
-  };
+  uint32_t hw[4][4], lw[4][4];  // split H, pi order per 32-row k-step
+  f32x4 VN[4];                  // V_new rows 16*mi + 4g + e
 
-  // raw K pieces of one chunk, for the row-major and transposed LDS copies
-  uint4 kr[4];
-  auto load_K = [&](int c) {
-    const int t0 = c * kC;
-    const int last = min(kC, d.L - t0) - 1;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * kThreads + tid;
-      const int row = idx / 16, cc = (idx % 16) * 8;
-      kr[it] = *reinterpret_cast<const uint4*>(
-          kseq + ((uint32_t)(t0 + min(row, last)) * d.Hk + kh) * kD + cc);
-    }
-  };
+  // Lane constants: element offsets of the K pieces inside one buffer.
+  // K H A pieces: row 16*mj + n, groups (8*kb + 4*s + g) ^ ksw(n), at
+  //   2048*mj + (ka ^ (32*kb + 16*s)).
+  // K^T pieces (transposing reads): row 32*kb + 16*s + 4g + n/4, group
+  //   (4*mb + n%4) ^ ksw(4g + n/4), at 4096*kb + 2048*s + (kt ^ 16*mb).
+  const int ka = n * kD + 4 * (g ^ ksw(n));
+  const int kt = (4 * g + (n >> 2)) * kD + 4 * ((n & 3) ^ ksw(4 * g + (n >> 2)));
 
-  auto stage_K = [&](int buf) {
+  // H as natural B fragments for the output waves: rows 16*mb + 4g + e of
+  // a 32-row k-step are B rows 8*gp + ep with gp = 2*(mb%2) + g/2 and
+  // ep = 4*(g%2) + e
+  auto publish_H = [&](auto pb) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * kThreads + tid;
-      const int row = idx / 16, cc = (idx % 16) * 8;
-      *reinterpret_cast<uint4*>(&Kr[buf][row * KS + cc]) = kr[it];
-      const u16* e8 = reinterpret_cast<const u16*>(&kr[it]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Kt[buf][kt_at(cc + e, row)] = e8[e];
+    for (int mb = 0; mb < 8; ++mb) {
+      const int kb = mb >> 1, t = mb & 1, gp = 2 * t + (g >> 1);
+      uint2* dh = reinterpret_cast<uint2*>(&Hf[pb][2 * kb][16 * gp + n]) + (g & 1);
+      uint2* dl = reinterpret_cast<uint2*>(&Hf[pb][2 * kb + 1][16 * gp + n]) + (g & 1);
+      *dh = make_uint2(hw[kb][2 * t], hw[kb][2 * t + 1]);
+      *dl = make_uint2(lw[kb][2 * t], lw[kb][2 * t + 1]);
     }
   };
-
-  // Every global load is issued about one chunk before its data is used: at
-  // the top of chunk c one explicit wait covers the operands of chunk c
-  // (issued during chunk c-1) and the K rows of chunk c+1 (issued at the top
-  // of chunk c-1); nothing later in the chunk reads a register that is still
-  // being loaded.
-  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
-
-  // one chunk: uses `cur`, prefetches chunk c+1 into `nxt`
-  auto chunk = [&](int c, const Pre& cur, Pre& nxt) {
-    const int buf = c & 1;
-    const int t0 = c * kC;
-    const int nv = min(kC, d.L - t0);
-    wait_loads();
-    // K of chunk c+1 into the other buffers (last read in chunk c-1, before
-    // the barrier that ended it); visible to chunk c+1 after this chunk's
-    // barriers
-    if (c + 1 < nch) stage_K(buf ^ 1);
-    if (c + 2 < nch) load_K(c + 2);
-
-    // ---- K H and Q H for rows 16w..16w+15 (2 passes: H hi, H lo)
-    f32x4 KH = {0.f, 0.f, 0.f, 0.f}, QH = {0.f, 0.f, 0.f, 0.f};
+  // Operand fragments are read from LDS one stage before the MFMAs that use
+  // them (an LDS read takes about as long as four to six MFMAs):
+  //   KA[kb]  A fragments of K H; k-steps 0, 1 read during H' of the
+  //           previous chunk, 2, 3 at the start of K H
+  //   TF[pr]  T fragments; the k-step 0 pairs at the start of K H, the
+  //           k-step 1 pairs after it
+  //   KT[kb]  A fragments of K^T for H'; k-step 0 after K H, 1 at the start
+  //           of H'
+  bf16x8 KA[4][4], KT[2][8], TF[6][2];
+  auto sched_fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto read_KA = [&](auto B, int kb0, int kb1) {
+    const u16* K = Kr[B];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kk = 32 * ks + 8 * q4;
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Kr[buf][(16 * w + n) * KS + kk]));
-      const bf16x8 aq = as_bf16x8(cur.q[ks]);
-      const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[buf][0][n * HS + kk]));
-      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(&Hb[buf][1][n * HS + kk]));
-      KH = mfma(ak, bh, KH);
-      QH = mfma(aq, bh, QH);
-      KH = mfma(ak, bl, KH);
-      QH = mfma(aq, bl, QH);
+    for (int kb = kb0; kb < kb1; ++kb)
+#pragma unroll
+      for (int mj = 0; mj < 4; ++mj)
+        KA[kb][mj] = frag(*reinterpret_cast<const uint2*>(&K[2048 * mj + (ka ^ (32 * kb))]),
+                          *reinterpret_cast<const uint2*>(&K[2048 * mj + (ka ^ (32 * kb + 16))]));
+  };
+  auto read_KT = [&](auto B, int kb) {
+    const u16* K = Kr[B];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      KT[kb][mb] = frag(tr_read(&K[4096 * kb + (kt ^ (16 * mb))]),
+                        tr_read(&K[4096 * kb + 2048 + (kt ^ (16 * mb))]));
+  };
+  auto read_TF = [&](auto B, int kb) {
+    // k-step 0: pairs (0,0) (1,0) (2,0) (3,0); k-step 1: (2,1) (3,1)
+#pragma unroll
+    for (int mi = (kb ? 2 : 0); mi < 4; ++mi) {
+      const int pr = pair_of(mi, kb);
+      TF[pr][0] = as_bf16x8(Tf[B][2 * pr][l]);
+      TF[pr][1] = as_bf16x8(Tf[B][2 * pr + 1][l]);
     }
-    // operands of chunk c+1 (issued while the MFMAs above run)
-    if (c + 1 < nch) prefetch(c + 1, nxt);
-
-    // ---- X = sb V - sk (K H), to LDS as split bf16 (column-major)
-    {
-      float x[4];
+  };
+  // chunk c from the split H up to V_new (operands in buffer c % 3; KA
+  // k-steps 0, 1 of chunk c already read), and V_new in f32 for the output
+  // waves (same row mapping as publish_H)
+  auto front = [&](auto B) {
+    constexpr int bb = decltype(B)::value;
+    const float* vc = Vec[bb];
+    read_KA(B, 2, 4);
+    read_TF(B, 0);
+    f32x4 sb[4];
+    uint2 vv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x[e] = cur.vec[e].x * __uint_as_float(cur.v[e] << 16) - cur.vec[e].y * KH[e];
-      uint32_t hi[2], lo[2];
-      split2(x[0], x[1], hi[0], lo[0]);
-      split2(x[2], x[3], hi[1], lo[1]);
-      const int r = 16 * w + 4 * q4;
-      *reinterpret_cast<uint2*>(&Xb[0][n * TS + r]) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(&Xb[1][n * TS + r]) = make_uint2(lo[0], lo[1]);
+    for (int mj = 0; mj < 4; ++mj) {
+      sb[mj] = *reinterpret_cast<const f32x4*>(&vc[16 * mj + 4 * g]);
+      vv[mj] = tr_read(&Vt[bb][(16 * mj + 4 * g + (n >> 2)) * kTile + 4 * (n & 3)]);
     }
-    __syncthreads();
-
-    // ---- V_new = T X (3 passes); T is lower triangular: k-step 1 (rows
-    // 32..63 of X) only matters for waves 2 and 3
-    f32x4 VN = {0.f, 0.f, 0.f, 0.f};
+    sched_fence();
+    f32x4 KH[4], SV[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 1 && w < 2) break;
-      const int kk = 32 * ks + 8 * q4;
-      const bf16x8 xh = as_bf16x8(*reinterpret_cast<const uint4*>(&Xb[0][n * TS + kk]));
-      const bf16x8 xl = as_bf16x8(*reinterpret_cast<const uint4*>(&Xb[1][n * TS + kk]));
-      const bf16x8 th = as_bf16x8(cur.tp[2 * ks]), tl = as_bf16x8(cur.tp[2 * ks + 1]);
-      VN = mfma(th, xh, VN);
-      VN = mfma(th, xl, VN);
-      VN = mfma(tl, xh, VN);
+    for (int mj = 0; mj < 4; ++mj) KH[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 bh = words(hw[kb]), bl = words(lw[kb]);
+#pragma unroll
+      for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bh, KH[mj]);
+#pragma unroll
+      for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bl, KH[mj]);
     }
-    {
-      uint32_t hi[2], lo[2], dh[2], dl[2];
-      split2(VN[0], VN[1], hi[0], lo[0]);
-      split2(VN[2], VN[3], hi[1], lo[1]);
-      split2(cur.vec[0].w * VN[0], cur.vec[1].w * VN[1], dh[0], dl[0]);
-      split2(cur.vec[2].w * VN[2], cur.vec[3].w * VN[3], dh[1], dl[1]);
-      const int r = 16 * w + 4 * q4;
-      *reinterpret_cast<uint2*>(&Vb[0][n * TS + r]) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(&Vb[1][n * TS + r]) = make_uint2(lo[0], lo[1]);
-      *reinterpret_cast<uint2*>(&Db[0][n * TS + r]) = make_uint2(dh[0], dh[1]);
-      *reinterpret_cast<uint2*>(&Db[1][n * TS + r]) = make_uint2(dl[0], dl[1]);
+    // sb V (independent of K H: overlaps the MFMAs)
+#pragma unroll
+    for (int mj = 0; mj < 4; ++mj) {
+      const float v4[4] = {__uint_as_float(vv[mj].x << 16), __uint_as_float(vv[mj].x & 0xffff0000u),
+                           __uint_as_float(vv[mj].y << 16), __uint_as_float(vv[mj].y & 0xffff0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) SV[mj][e] = sb[mj][e] * v4[e];
     }
-    __syncthreads();
-
-    // ---- O = so (Q H) + P V_new (3 passes), rows 16w..16w+15
-    {
-      f32x4 O;
+    sched_fence();
+    read_KT(B, 0);
+    read_TF(B, 1);
+    f32x4 sk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = cur.vec[e].z * QH[e];
+    for (int mj = 0; mj < 4; ++mj) sk[mj] = *reinterpret_cast<const f32x4*>(&vc[kC + 16 * mj + 4 * g]);
+    sched_fence();
+    // X = sb V - sk (K H), rows 16*mj + 4g + e, split per 32-row k-step;
+    // V_new = T X (3 passes, T lower triangular) one k-step at a time
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 1 && w < 2) break;
-        const int kk = 32 * ks + 8 * q4;
-        const bf16x8 vh = as_bf16x8(*reinterpret_cast<const uint4*>(&Vb[0][n * TS + kk]));
-        const bf16x8 vl = as_bf16x8(*reinterpret_cast<const uint4*>(&Vb[1][n * TS + kk]));
-        const bf16x8 ph = as_bf16x8(cur.tp[4 + 2 * ks]), pl = as_bf16x8(cur.tp[5 + 2 * ks]);
-        O = mfma(ph, vh, O);
-        O = mfma(ph, vl, O);
-        O = mfma(pl, vh, O);
+    for (int mi = 0; mi < 4; ++mi) VN[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 X[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int mj = 2 * kb + t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[t][e] = SV[mj][e] - sk[mj][e] * KH[mj][e];
       }
+      uint32_t xh[4], xl[4];
+      split_pi(X[0], X[1], xh, xl);
+      const bf16x8 bh = words(xh), bl = words(xl);
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          if (kb == 1 && mi < 2) continue;
+          const int pr = pair_of(mi, kb);
+          VN[mi] = mfma(TF[pr][pass == 2 ? 1 : 0], pass == 1 ? bl : bh, VN[mi]);
+        }
+    }
+    constexpr int pb = bb;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int kb = mi >> 1, t = mi & 1, gp = 2 * t + (g >> 1);
+      *reinterpret_cast<f32x4*>(&Vf[pb][kb][16 * gp + n][4 * (g & 1)]) = VN[mi];
+    }
+  };
+  // chunk c from V_new to H' = gamma_63 H + K^T diag(sd) V_new (KT of
+  // chunk c already read), two 16-row blocks of H at a time, each pair split
+  // for the next K H as soon as it is complete.  Reads KA k-steps 0, 1 of
+  // chunk c + 1 when there is one.
+  auto back = [&](auto B, auto NB, bool more) {
+    const float* vc = Vec[B];
+    const float gc = vc[4 * kC];
+    f32x4 s0[2], s1[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s0[kb] = *reinterpret_cast<const f32x4*>(&vc[3 * kC + 32 * kb + 4 * g]);
+      s1[kb] = *reinterpret_cast<const f32x4*>(&vc[3 * kC + 32 * kb + 16 + 4 * g]);
+    }
+    read_KT(B, 1);  // used after the k-step 0 MFMAs
+    sched_fence();
+    uint32_t dh[2][4], dl[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 D0, D1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * q4 + e;
-        if (r < nv) os[((uint32_t)(t0 + r) * d.Hv + h) * kD + col] = O[e];
+        D0[e] = s0[kb][e] * VN[2 * kb][e];
+        D1[e] = s1[kb][e] * VN[2 * kb + 1][e];
       }
+      split_pi(D0, D1, dh[kb], dl[kb]);
     }
-
-    // ---- H' = gamma_63 H + K^T (sd V_new)  (2 passes), rows 32w..32w+31
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc;
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = cur.gc * H[mt][e];
-      const int arow = 32 * w + 16 * mt + n;  // dk index
+      for (int e = 0; e < 4; ++e) H[mb][e] = gc * H[mb][e];
+    // k-step 0 (tokens 0..31) for all rows, then k-step 1 pair by pair, each
+    // pair split for the next K H as soon as it is complete
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kk = 32 * ks + 8 * q4;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[buf][kt_at(arow, kk)]));
-        const bf16x8 dh = as_bf16x8(*reinterpret_cast<const uint4*>(&Db[0][n * TS + kk]));
-        const bf16x8 dl = as_bf16x8(*reinterpret_cast<const uint4*>(&Db[1][n * TS + kk]));
-        acc = mfma(a, dh, acc);
-        acc = mfma(a, dl, acc);
-      }
-      H[mt] = acc;
+    for (int pq = 0; pq < 4; ++pq)
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int mb = 2 * pq + t;
+          H[mb] = mfma(KT[0][mb], words(pass ? dl[0] : dh[0]), H[mb]);
+        }
+    if (more) {
+      sched_fence();
+      read_KA(NB, 0, 2);
+      sched_fence();
     }
+#pragma unroll
+    for (int pq = 0; pq < 4; ++pq) {
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int mb = 2 * pq + t;
+          H[mb] = mfma(KT[1][mb], words(pass ? dl[1] : dh[1]), H[mb]);
+        }
+      split_pi(H[2 * pq], H[2 * pq + 1], hw[pq], lw[pq]);
+    }
+  };
 
-    // ---- checkpoint after token t0 + nv when it is a multiple of the interval
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<int, 2> B2;
+  __syncthreads();  // chunks 0 and 1 staged
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) split_pi(H[2 * kb], H[2 * kb + 1], hw[kb], lw[kb]);
+  publish_H(B0{});
+  read_KA(B0{}, 0, 2);
+  front(B0{});
+  __syncthreads();
+  // one interval: chunk c from V_new to H_{c+1}, then chunk c + 1 up to
+  // V_new; the buffers of chunk c and c + 1 are compile-time constants (the
+  // loop is unrolled by three) so that every LDS address is a lane constant
+  // plus an immediate offset
+  auto step = [&](int c, auto B, auto NB) {
+    const bool more = c + 1 < nch;
+    back(B, NB, more);
+    const int t0 = c * kC, nv = min(kC, d.L - t0);
+    // checkpoint after token t0 + nv when it is a multiple of the interval
     if (d.ckpt_interval > 0 && ckpt && (t0 + nv) % d.ckpt_interval == 0) {
       const int idx = (t0 + nv) / d.ckpt_interval - 1;
       const int n_ck = d.L / d.ckpt_interval;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 32 * w + 16 * mt + 4 * q4 + e;
-          ckpt[((((size_t)s * n_ck + idx) * d.Hv + h) * kD + r) * kD + col] = H[mt][e];
+          const int r = 16 * mb + 4 * g + e;
+          ckpt[((((size_t)s * n_ck + idx) * d.Hv + h) * kD + r) * kD + col] = H[mb][e];
         }
     }
-
-    // the state operand of chunk c+1 goes to the other buffer (last read in
-    // chunk c-1)
-    if (c + 1 < nch) write_H(buf ^ 1);
+    if (more) {
+      publish_H(NB);
+      front(NB);
+    }
     __syncthreads();
   };
-
-  Pre A, B;
-  load_K(0);
-  wait_loads();
-  stage_K(0);
-  prefetch(0, A);
-  if (nch > 1) load_K(1);
-  write_H(0);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    chunk(c, A, B);
-    if (c + 1 < nch) chunk(c + 1, B, A);
+  for (int c = 0; c < nch; c += 3) {
+    step(c, B0{}, B1{});
+    if (c + 1 < nch) step(c + 1, B1{}, B2{});
+    if (c + 2 < nch) step(c + 2, B2{}, B0{});
   }
-
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 32 * w + 16 * mt + 4 * q4 + e;
-      S_final[(((size_t)s * d.Hv + h) * kD + r) * kD + col] = H[mt][e];
+      const int r = 16 * mb + 4 * g + e;
+      S_final[(((size_t)s * d.Hv + h) * kD + r) * kD + col] = H[mb][e];
     }
+}
+
+// Loads are unconditional: rows past the end of the sequence are read from
+// the last valid row.  Their values never reach a result: P1 gives such rows
+// beta = 0 (so X, V_new and their state contributions are 0), and their
+// output rows are not stored.
+
+// Staging wave: the K rows, the T fragments, the V tile and the row vectors
+// of chunk c + 2 are written to LDS in interval c (loaded during interval
+// c - 1).
+static __device__ __attribute__((noinline)) void p2_stage(
+    const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
+    const float* S_init_, float* S_final_, float* o_, float* ckpt_,
+    const PDims d_, const int tile_, const int h_, const int s_, const int kh_) {
+  const u16* __restrict__ q = uniform_ptr(q_);
+  const u16* __restrict__ k = uniform_ptr(k_);
+  const u16* __restrict__ v = uniform_ptr(v_);
+  const uint8_t* __restrict__ ws = uniform_ptr(ws_);
+  float* __restrict__ o = uniform_ptr(o_);
+  const PDims d = uniform_dims(d_);
+  const int tile = __builtin_amdgcn_readfirstlane(tile_);
+  const int h = __builtin_amdgcn_readfirstlane(h_);
+  const int s = __builtin_amdgcn_readfirstlane(s_);
+  const int kh = __builtin_amdgcn_readfirstlane(kh_);
+  (void)S_init_; (void)S_final_; (void)ckpt_;
+  const int l = threadIdx.x % 64;
+  const int n = l % 16;
+  const int g = l / 16;
+  const int col = kTile * tile + n;
+  const int nch = d.n_chunks;
+  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
+  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const uint8_t* __restrict__ wss =
+      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+  const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
+  (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
+  auto& Kr = p2lds.Kr;
+  auto& Tf = p2lds.Tf;
+  auto& Vt = p2lds.Vt;
+  auto& Vec = p2lds.Vec;
+  auto load = [&](int c, KvTransit& tr) {
+    const int t0 = c * kC;
+    const int last = min(kC, d.L - t0) - 1;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + l;
+      const int row = idx >> 4, pc = idx & 15;
+      tr.k[it] = *reinterpret_cast<const uint4*>(
+          kseq + ((uint32_t)(t0 + min(row, last)) * d.Hk + kh) * kD + 8 * pc);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int row = 32 * it + (l >> 1);
+      tr.v[it] = *reinterpret_cast<const uint4*>(
+          vs + ((uint32_t)(t0 + min(row, last)) * d.Hv + h) * kD + kTile * tile + 8 * (l & 1));
+    }
+    const uint8_t* wc = wss + (size_t)c * ws_chunk;
+#pragma unroll
+    for (int x = 0; x < 12; ++x) tr.t[x] = reinterpret_cast<const uint4*>(wc + WsLayout::kT)[x * 64 + l];
+    tr.vec = reinterpret_cast<const uint4*>(wc + WsLayout::kVec)[l];
+    tr.gc = *reinterpret_cast<const uint4*>(wc + WsLayout::kGc);
+  };
+  auto store = [&](int buf, const KvTransit& tr) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + l;
+      const int row = idx >> 4, pc = idx & 15;
+      const int hs = ksw(row);
+      const uint4 x = tr.k[it];
+      const uint4 y = (hs & 1) ? make_uint4(x.z, x.w, x.x, x.y) : x;
+      *reinterpret_cast<uint4*>(&Kr[buf][row * kD + 4 * ((2 * pc) ^ (hs & ~1))]) = y;
+    }
+#pragma unroll
+    for (int x = 0; x < 12; ++x) Tf[buf][x][l] = tr.t[x];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      *reinterpret_cast<uint4*>(&Vt[buf][(32 * it + (l >> 1)) * kTile + 8 * (l & 1)]) = tr.v[it];
+    reinterpret_cast<uint4*>(Vec[buf])[l] = tr.vec;
+    if (l == 0) reinterpret_cast<uint4*>(Vec[buf])[kC] = tr.gc;
+  };
+  KvTransit tr;
+  load(0, tr);
+  store(0, tr);
+  if (nch > 1) {
+    load(1, tr);
+    store(1, tr);
+  }
+  if (nch > 2) load(2, tr);
+  __syncthreads();  // chunks 0 and 1 staged
+  __syncthreads();  // chain: chunk 0 up to V_new
+  for (int c = 0; c < nch; ++c) {
+    if (c + 2 < nch) store((c + 2) % 3, tr);
+    load(min(c + 3, nch - 1), tr);  // unconditional, see p2_out
+    __syncthreads();
+  }
+}
+
+// Output wave ow (0 or 1): O = diag(so) Q H + P V_new for row blocks
+// mA = ow (P has one k-step there) and mB = 3 - ow (two).
+static __device__ __attribute__((noinline)) void p2_out(
+    const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
+    const float* S_init_, float* S_final_, float* o_, float* ckpt_,
+    const PDims d_, const int tile_, const int h_, const int s_, const int kh_, const int ow) {
+  const u16* __restrict__ q = uniform_ptr(q_);
+  const u16* __restrict__ k = uniform_ptr(k_);
+  const u16* __restrict__ v = uniform_ptr(v_);
+  const uint8_t* __restrict__ ws = uniform_ptr(ws_);
+  float* __restrict__ o = uniform_ptr(o_);
+  const PDims d = uniform_dims(d_);
+  const int tile = __builtin_amdgcn_readfirstlane(tile_);
+  const int h = __builtin_amdgcn_readfirstlane(h_);
+  const int s = __builtin_amdgcn_readfirstlane(s_);
+  const int kh = __builtin_amdgcn_readfirstlane(kh_);
+  (void)S_init_; (void)S_final_; (void)ckpt_;
+  const int l = threadIdx.x % 64;
+  const int n = l % 16;
+  const int g = l / 16;
+  const int col = kTile * tile + n;
+  const int nch = d.n_chunks;
+  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
+  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
+  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const uint8_t* __restrict__ wss =
+      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+  const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
+  (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
+  auto& Vec = p2lds.Vec;
+  auto& Hf = p2lds.Hf;
+  auto& Vf = p2lds.Vf;
+  const int mA = ow, mB = 3 - ow;
+  const int prA = pair_of(mA, 0), prB = pair_of(mB, 0);
+  auto ops_load = [&](int c, OutOps& op) {
+    const int t0 = c * kC;
+    const int last = min(kC, d.L - t0) - 1;
+    const uint32_t ra = ((uint32_t)(t0 + min(16 * mA + n, last)) * d.Hk + kh) * kD + 8 * g;
+    const uint32_t rb = ((uint32_t)(t0 + min(16 * mB + n, last)) * d.Hk + kh) * kD + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      op.qa[kb] = *reinterpret_cast<const uint4*>(qs + ra + 32 * kb);
+      op.qb[kb] = *reinterpret_cast<const uint4*>(qs + rb + 32 * kb);
+    }
+    const uint4* psrc = reinterpret_cast<const uint4*>(wss + (size_t)c * ws_chunk + WsLayout::kP);
+    const int prs[3] = {prA, prB, prB + 1};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      op.p[x][0] = psrc[2 * prs[x] * 64 + l];
+      op.p[x][1] = psrc[(2 * prs[x] + 1) * 64 + l];
+    }
+  };
+  auto outputs = [&](int c, const OutOps& op) {
+    const int hb = c % 3, bb = c % 3;
+    const int t0 = c * kC, nv = min(kC, d.L - t0);
+    f32x4 QA = {0.f, 0.f, 0.f, 0.f}, QB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 bh = as_bf16x8(Hf[hb][2 * kb][l]);
+      const bf16x8 bl = as_bf16x8(Hf[hb][2 * kb + 1][l]);
+      const bf16x8 aa = as_bf16x8(op.qa[kb]), ab = as_bf16x8(op.qb[kb]);
+      QA = mfma(aa, bh, QA);
+      QB = mfma(ab, bh, QB);
+      QA = mfma(aa, bl, QA);
+      QB = mfma(ab, bl, QB);
+    }
+    const f32x4 soA = *reinterpret_cast<const f32x4*>(&Vec[bb][2 * kC + 16 * mA + 4 * g]);
+    const f32x4 soB = *reinterpret_cast<const f32x4*>(&Vec[bb][2 * kC + 16 * mB + 4 * g]);
+    f32x4 OA, OB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      OA[e] = soA[e] * QA[e];
+      OB[e] = soB[e] * QB[e];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&Vf[hb][kb][l][0]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&Vf[hb][kb][l][4]);
+      uint32_t hi[4], lo[4];
+      split2(v0[0], v0[1], hi[0], lo[0]);
+      split2(v0[2], v0[3], hi[1], lo[1]);
+      split2(v1[0], v1[1], hi[2], lo[2]);
+      split2(v1[2], v1[3], hi[3], lo[3]);
+      const bf16x8 vh = words(hi), vl = words(lo);
+      const bf16x8 ph = as_bf16x8(op.p[1 + kb][0]), pl = as_bf16x8(op.p[1 + kb][1]);
+      OB = mfma(ph, vh, OB);
+      OB = mfma(ph, vl, OB);
+      OB = mfma(pl, vh, OB);
+      if (kb == 0) {
+        const bf16x8 qh = as_bf16x8(op.p[0][0]), ql = as_bf16x8(op.p[0][1]);
+        OA = mfma(qh, vh, OA);
+        OA = mfma(qh, vl, OA);
+        OA = mfma(ql, vh, OA);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ra = 16 * mA + 4 * g + e, rb = 16 * mB + 4 * g + e;
+      if (ra < nv) os[((uint32_t)(t0 + ra) * d.Hv + h) * kD + col] = OA[e];
+      if (rb < nv) os[((uint32_t)(t0 + rb) * d.Hv + h) * kD + col] = OB[e];
+    }
+  };
+
+  OutOps A, B;
+  ops_load(0, A);
+  __syncthreads();  // chunks 0 and 1 staged
+  __syncthreads();  // chain: chunk 0 up to V_new
+  // interval c: loads of the operands of chunk c + 1, then O of chunk c
+  // (the loads are issued unconditionally, past the last chunk for the last
+  // chunk again: a load under a branch makes the compiler wait for every
+  // outstanding load where the branches join)
+  auto interval = [&](int c, const OutOps& cur, OutOps& nxt) {
+    ops_load(min(c + 1, nch - 1), nxt);
+    outputs(c, cur);
+    __syncthreads();
+  };
+  for (int c = 0; c < nch; c += 2) {
+    interval(c, A, B);
+    if (c + 1 < nch) interval(c + 1, B, A);
+  }
+}
+
+__global__ __launch_bounds__(kP2Threads) void p2_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k,
+    const u16* __restrict__ v, const uint8_t* __restrict__ ws,
+    const float* __restrict__ S_init, float* __restrict__ S_final,
+    float* __restrict__ o, float* __restrict__ ckpt, PDims d) {
+  // block -> (sequence, head, tile); the tiles of a head share one XCD
+  const int nb = gridDim.x;
+  int b = blockIdx.x;
+  if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+  const int tile = b % (kD / kTile);
+  const int h = (b / (kD / kTile)) % d.Hv;
+  const int s = b / ((kD / kTile) * d.Hv);
+  const int kh = h / d.group;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  if (w == 0)
+    p2_chain(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+  else if (w < 3)
+    p2_out(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, w - 1);
+  else
+    p2_stage(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
 }
 
 // ------------------------------------------------------------------ host
@@ -740,7 +1116,7 @@ extern "C" int gdn_prefill_chunked(
                     (void*)&checkpoints, (void*)&dd};
     hipError_t e = hipLaunchKernel((const void*)p2_kernel,
                                    dim3(n_seqs * h_v * (kD / kTile)),
-                                   dim3(kThreads), args, 0, st);
+                                   dim3(kP2Threads), args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill p2 launch", e);
   }
   return GDN_OK;

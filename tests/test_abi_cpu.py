@@ -241,8 +241,10 @@ def test_binding_checks_lane_count():
 
 def test_prefill_workspace_bytes():
     n = gdn.prefill_workspace_bytes(1, 32768, 32, 32, 128, 128)
-    # per (chunk, head): T and P as split bf16 (4 x 8 KiB) + row vectors
-    assert n >= 512 * 32 * (4 * 8192 + 64 * 16)
+    # per (chunk, head): the nonzero 16 x 32 blocks of the lower-triangular
+    # T and P (6 each) as split bf16 (hi, lo: 1 KiB per fragment), four row
+    # vectors of 64 floats and gamma_63
+    assert n >= 512 * 32 * (2 * 6 * 2 * 1024 + 4 * 64 * 4 + 4)
     assert gdn.prefill_workspace_bytes(1, 100, 4, 3, 128, 128) == 0   # h_v % h_k
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 64, 64) == 0     # d != 128
     assert gdn.prefill_workspace_bytes(0, 100, 4, 4, 128, 128) == 0
