@@ -374,14 +374,17 @@ constexpr int kP2Threads = 256;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-// Swizzle of the 4-element groups of a staged K row r: group G is stored at
-// G ^ ksw(r).  The chain reads K in two patterns -- 8-byte A-fragment pieces
-// (16 rows x 2 groups per half wave) and transposing reads (8 rows x 4
-// groups) -- and this swizzle spreads both over distinct LDS banks.
-__device__ __forceinline__ int ksw(int r) {
-  r &= 15;
-  return 4 * (r & 3) + (r >> 2) + 16 * ((r >> 2) & 1);
+// Staged K rows: row stride kKS (padded against bank conflicts) and, inside
+// each 32-column block, the 4-column groups stored in the order
+// 0 4 1 5 2 6 3 7, so that the pi-order A fragment of K H (columns
+// 32*kb + 4g + 0..3 and 32*kb + 16 + 4g + 0..3) is one 16-byte read at
+// 32*kb + 8g.  kpos(col) is the stored position of a column.
+constexpr int kKS = kD + 8;
+__host__ __device__ constexpr int kpos(int col) {
+  return (col & ~31) + 4 * (((col >> 2) & 3) * 2 + ((col >> 4) & 1)) + (col & 3);
 }
+constexpr int kSVS = kC + 4;  // row stride of the transposed sb V tile (f32)
+constexpr int kWarm = 5;      // chunks ahead that the output waves warm L2 for
 
 // LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group g, lane
 // i receives element i%4 of the 8 bytes addressed by lane 16g + 4e + i/4 as
@@ -416,9 +419,11 @@ struct KvTransit {
   uint4 k[16];  // 64 K rows x 128 columns
   uint4 t[12];  // the T fragments
   uint4 v[2];   // 64 rows x 16 columns of V
+  float sb[2];  // sb of the two V rows of the lane
   uint4 vec;    // the row vectors
   uint4 gc;     // gamma_63
 };
+
 
 // Per-chunk operands of an output wave (row blocks mA with one k-step, mB
 // with two).
@@ -429,9 +434,9 @@ struct OutOps {
 
 // LDS of a p2 workgroup, shared by the role functions below.
 struct P2Lds {
-  __attribute__((aligned(16))) u16 Kr[3][kC * kD];        // K rows, swizzled
+  __attribute__((aligned(16))) u16 Kr[3][kC * kKS];       // K rows (kpos order)
   __attribute__((aligned(16))) uint4 Tf[3][12][64];       // T fragments
-  __attribute__((aligned(16))) u16 Vt[3][kC * kTile];     // V tile [row][col]
+  __attribute__((aligned(16))) float SVt[3][kTile * kSVS]; // diag(sb) V, [col][row]
   __attribute__((aligned(16))) float Vec[3][4 * kC + 4];  // sb sk so sd, gamma
   __attribute__((aligned(16))) uint4 Hf[3][8][64];        // H (natural B)
   __attribute__((aligned(16))) float Vf[3][2][64][8];     // V_new f32 (natural B rows)
@@ -491,7 +496,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
   (void)q; (void)k; (void)v; (void)S_init; (void)S_final; (void)o; (void)ckpt; (void)kh;
   auto& Kr = p2lds.Kr;
   auto& Tf = p2lds.Tf;
-  auto& Vt = p2lds.Vt;
+  auto& SVt = p2lds.SVt;
   auto& Vec = p2lds.Vec;
   auto& Hf = p2lds.Hf;
   auto& Vf = p2lds.Vf;
@@ -509,7 +514,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
       ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)wss; (void)ws_chunk;
-  (void)Kr; (void)Tf; (void)Vt; (void)Vec; (void)Hf; (void)Vf; (void)col;
+  (void)Kr; (void)Tf; (void)SVt; (void)Vec; (void)Hf; (void)Vf; (void)col;
   // ================================================================ chain
   // H[mb]: state rows dk = 16*mb + 4g + e, column col
   f32x4 H[8];
@@ -524,12 +529,12 @@ static __device__ __attribute__((noinline)) void p2_chain(
   f32x4 VN[4];                  // V_new rows 16*mi + 4g + e
 
   // Lane constants: element offsets of the K pieces inside one buffer.
-  // K H A pieces: row 16*mj + n, groups (8*kb + 4*s + g) ^ ksw(n), at
-  //   2048*mj + (ka ^ (32*kb + 16*s)).
-  // K^T pieces (transposing reads): row 32*kb + 16*s + 4g + n/4, group
-  //   (4*mb + n%4) ^ ksw(4g + n/4), at 4096*kb + 2048*s + (kt ^ 16*mb).
-  const int ka = n * kD + 4 * (g ^ ksw(n));
-  const int kt = (4 * g + (n >> 2)) * kD + 4 * ((n & 3) ^ ksw(4 * g + (n >> 2)));
+  // K H A fragment (mj, kb): row 16*mj + n, stored columns 32*kb + 8g + 0..7,
+  //   at ka + 16*kKS*mj + 32*kb.
+  // K^T pieces (transposing reads, columns 16*mb + 4*(n%4) + 0..3 of row
+  //   32*kb + 16*s + 4g + n/4), at kt + (32*kb + 16*s)*kKS + kpos(16*mb).
+  const int ka = n * kKS + 8 * g;
+  const int kt = (4 * g + (n >> 2)) * kKS + 8 * (n & 3);
 
   // H as natural B fragments for the output waves: rows 16*mb + 4g + e of
   // a 32-row k-step are B rows 8*gp + ep with gp = 2*(mb%2) + g/2 and
@@ -560,15 +565,14 @@ static __device__ __attribute__((noinline)) void p2_chain(
     for (int kb = kb0; kb < kb1; ++kb)
 #pragma unroll
       for (int mj = 0; mj < 4; ++mj)
-        KA[kb][mj] = frag(*reinterpret_cast<const uint2*>(&K[2048 * mj + (ka ^ (32 * kb))]),
-                          *reinterpret_cast<const uint2*>(&K[2048 * mj + (ka ^ (32 * kb + 16))]));
+        KA[kb][mj] = as_bf16x8(*reinterpret_cast<const uint4*>(&K[ka + 16 * kKS * mj + 32 * kb]));
   };
   auto read_KT = [&](auto B, int kb) {
     const u16* K = Kr[B];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
-      KT[kb][mb] = frag(tr_read(&K[4096 * kb + (kt ^ (16 * mb))]),
-                        tr_read(&K[4096 * kb + 2048 + (kt ^ (16 * mb))]));
+      KT[kb][mb] = frag(tr_read(&K[kt + 32 * kb * kKS + kpos(16 * mb)]),
+                        tr_read(&K[kt + (32 * kb + 16) * kKS + kpos(16 * mb)]));
   };
   auto read_TF = [&](auto B, int kb) {
     // k-step 0: pairs (0,0) (1,0) (2,0) (3,0); k-step 1: (2,1) (3,1)
@@ -587,15 +591,12 @@ static __device__ __attribute__((noinline)) void p2_chain(
     const float* vc = Vec[bb];
     read_KA(B, 2, 4);
     read_TF(B, 0);
-    f32x4 sb[4];
-    uint2 vv[4];
+    f32x4 SV[4];  // sb V, rows 16*mj + 4g + e
 #pragma unroll
-    for (int mj = 0; mj < 4; ++mj) {
-      sb[mj] = *reinterpret_cast<const f32x4*>(&vc[16 * mj + 4 * g]);
-      vv[mj] = tr_read(&Vt[bb][(16 * mj + 4 * g + (n >> 2)) * kTile + 4 * (n & 3)]);
-    }
+    for (int mj = 0; mj < 4; ++mj)
+      SV[mj] = *reinterpret_cast<const f32x4*>(&SVt[bb][n * kSVS + 16 * mj + 4 * g]);
     sched_fence();
-    f32x4 KH[4], SV[4];
+    f32x4 KH[4];
 #pragma unroll
     for (int mj = 0; mj < 4; ++mj) KH[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -605,14 +606,6 @@ static __device__ __attribute__((noinline)) void p2_chain(
       for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bh, KH[mj]);
 #pragma unroll
       for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bl, KH[mj]);
-    }
-    // sb V (independent of K H: overlaps the MFMAs)
-#pragma unroll
-    for (int mj = 0; mj < 4; ++mj) {
-      const float v4[4] = {__uint_as_float(vv[mj].x << 16), __uint_as_float(vv[mj].x & 0xffff0000u),
-                           __uint_as_float(vv[mj].y << 16), __uint_as_float(vv[mj].y & 0xffff0000u)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) SV[mj][e] = sb[mj][e] * v4[e];
     }
     sched_fence();
     read_KT(B, 0);
@@ -767,8 +760,8 @@ static __device__ __attribute__((noinline)) void p2_chain(
 // beta = 0 (so X, V_new and their state contributions are 0), and their
 // output rows are not stored.
 
-// Staging wave: the K rows, the T fragments, the V tile and the row vectors
-// of chunk c + 2 are written to LDS in interval c (loaded during interval
+// Staging wave: the K rows, the T fragments, sb V and the row vectors of
+// chunk c + 2 are written to LDS in interval c (loaded during interval
 // c - 1).
 static __device__ __attribute__((noinline)) void p2_stage(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
@@ -800,7 +793,7 @@ static __device__ __attribute__((noinline)) void p2_stage(
   (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
   auto& Kr = p2lds.Kr;
   auto& Tf = p2lds.Tf;
-  auto& Vt = p2lds.Vt;
+  auto& SVt = p2lds.SVt;
   auto& Vec = p2lds.Vec;
   auto load = [&](int c, KvTransit& tr) {
     const int t0 = c * kC;
@@ -821,6 +814,9 @@ static __device__ __attribute__((noinline)) void p2_stage(
     const uint8_t* wc = wss + (size_t)c * ws_chunk;
 #pragma unroll
     for (int x = 0; x < 12; ++x) tr.t[x] = reinterpret_cast<const uint4*>(wc + WsLayout::kT)[x * 64 + l];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      tr.sb[it] = reinterpret_cast<const float*>(wc + WsLayout::kVec)[32 * it + (l >> 1)];
     tr.vec = reinterpret_cast<const uint4*>(wc + WsLayout::kVec)[l];
     tr.gc = *reinterpret_cast<const uint4*>(wc + WsLayout::kGc);
   };
@@ -829,16 +825,24 @@ static __device__ __attribute__((noinline)) void p2_stage(
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + l;
       const int row = idx >> 4, pc = idx & 15;
-      const int hs = ksw(row);
       const uint4 x = tr.k[it];
-      const uint4 y = (hs & 1) ? make_uint4(x.z, x.w, x.x, x.y) : x;
-      *reinterpret_cast<uint4*>(&Kr[buf][row * kD + 4 * ((2 * pc) ^ (hs & ~1))]) = y;
+      // columns 8*pc + 0..3 and 8*pc + 4..7 land in separate groups
+      *reinterpret_cast<uint2*>(&Kr[buf][row * kKS + kpos(8 * pc)]) = make_uint2(x.x, x.y);
+      *reinterpret_cast<uint2*>(&Kr[buf][row * kKS + kpos(8 * pc + 4)]) = make_uint2(x.z, x.w);
     }
 #pragma unroll
     for (int x = 0; x < 12; ++x) Tf[buf][x][l] = tr.t[x];
+    // sb V, transposed to [column][row]
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-      *reinterpret_cast<uint4*>(&Vt[buf][(32 * it + (l >> 1)) * kTile + 8 * (l & 1)]) = tr.v[it];
+    for (int it = 0; it < 2; ++it) {
+      const int row = 32 * it + (l >> 1);
+      const uint32_t w[4] = {tr.v[it].x, tr.v[it].y, tr.v[it].z, tr.v[it].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+        SVt[buf][(8 * (l & 1) + e) * kSVS + row] = tr.sb[it] * __uint_as_float(b);
+      }
+    }
     reinterpret_cast<uint4*>(Vec[buf])[l] = tr.vec;
     if (l == 0) reinterpret_cast<uint4*>(Vec[buf])[kC] = tr.gc;
   };
@@ -860,7 +864,11 @@ static __device__ __attribute__((noinline)) void p2_stage(
 }
 
 // Output wave ow (0 or 1): O = diag(so) Q H + P V_new for row blocks
-// mA = ow (P has one k-step there) and mB = 3 - ow (two).
+// mA = ow (P has one k-step there) and mB = 3 - ow (two).  The output waves
+// also warm L2 for chunk c + kWarm: the eight workgroups of a head (same
+// XCD, same L2) each touch one eighth of the cache lines that the head's
+// workgroups will load for that chunk, one dword per lane, so that the
+// loads issued one or two chunks ahead find their data in L2.
 static __device__ __attribute__((noinline)) void p2_out(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
     const float* S_init_, float* S_final_, float* o_, float* ckpt_,
@@ -894,6 +902,27 @@ static __device__ __attribute__((noinline)) void p2_out(
   auto& Vf = p2lds.Vf;
   const int mA = ow, mB = 3 - ow;
   const int prA = pair_of(mA, 0), prB = pair_of(mB, 0);
+  // L2 warm-up line of this lane: index u over the lines a head loads per
+  // chunk (K rows 128, Q rows 128, V rows 128, workspace block), taken by
+  // workgroup `tile` as u = 128*tile + 64*ow + l (lines past the end are
+  // clamped to the last one)
+  const int u = 128 * tile + 64 * ow + l;
+  auto warm = [&](int c) -> uint32_t {
+    const int t0 = c * kC;
+    const int last = min(kC, d.L - t0) - 1;
+    const int row = min((u & 127) >> 1, last), half = u & 1;
+    const uint32_t* p;
+    if (u < 128)
+      p = reinterpret_cast<const uint32_t*>(kseq + ((uint32_t)(t0 + row) * d.Hk + kh) * kD + 64 * half);
+    else if (u < 256)
+      p = reinterpret_cast<const uint32_t*>(qs + ((uint32_t)(t0 + row) * d.Hk + kh) * kD + 64 * half);
+    else if (u < 384)
+      p = reinterpret_cast<const uint32_t*>(vs + ((uint32_t)(t0 + row) * d.Hv + h) * kD + 64 * half);
+    else
+      p = reinterpret_cast<const uint32_t*>(
+          wss + (size_t)c * ws_chunk + min((size_t)(u - 384) * 128, WsLayout::kBytes - 4));
+    return *p;
+  };
   auto ops_load = [&](int c, OutOps& op) {
     const int t0 = c * kC;
     const int last = min(kC, d.L - t0) - 1;
@@ -967,19 +996,26 @@ static __device__ __attribute__((noinline)) void p2_out(
   ops_load(0, A);
   __syncthreads();  // chunks 0 and 1 staged
   __syncthreads();  // chain: chunk 0 up to V_new
-  // interval c: loads of the operands of chunk c + 1, then O of chunk c
-  // (the loads are issued unconditionally, past the last chunk for the last
-  // chunk again: a load under a branch makes the compiler wait for every
-  // outstanding load where the branches join)
+  // interval c: warm L2 for chunk c + kWarm, load the output operands of
+  // chunk c + 1, then O of chunk c.  Loads are issued unconditionally, past
+  // the last chunk for the last chunk again (a load under a branch makes the
+  // compiler wait for every outstanding load where the branches join); a
+  // warm-up value is consumed two intervals later, when it has long arrived.
+  uint32_t w0 = 0, w1 = 0;
   auto interval = [&](int c, const OutOps& cur, OutOps& nxt) {
+    const uint32_t w2 = warm(min(c + kWarm, nch - 1));
     ops_load(min(c + 1, nch - 1), nxt);
     outputs(c, cur);
+    asm volatile("" ::"v"(w0));
+    w0 = w1;
+    w1 = w2;
     __syncthreads();
   };
   for (int c = 0; c < nch; c += 2) {
     interval(c, A, B);
     if (c + 1 < nch) interval(c + 1, B, A);
   }
+  asm volatile("" ::"v"(w0), "v"(w1));
 }
 
 __global__ __launch_bounds__(kP2Threads) void p2_kernel(
