@@ -140,9 +140,10 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     uint8_t* __restrict__ ws, PDims d) {
   constexpr int KS = kD + 8;  // padded LDS row (bf16) against bank conflicts
   constexpr int FS = kC + 1;  // padded f32 row
+  constexpr int LS = kC + 4;  // padded f32 row, 16-byte aligned
   __shared__ __attribute__((aligned(16))) u16 Ks[kC * KS];
   __shared__ __attribute__((aligned(16))) u16 Qs[kC * KS];  // later: P (f32)
-  __shared__ float Ls[kC * FS];                             // L (f32)
+  __shared__ __attribute__((aligned(16))) float Lt[kC * LS];  // L transposed
   __shared__ float rk_s[kC], rq_s[kC], G_s[kC], b_s[kC];
   float* Ts = reinterpret_cast<float*>(Ks);  // T (f32) once K is consumed
   float* Ps = reinterpret_cast<float*>(Qs);
@@ -235,78 +236,83 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   }
   __syncthreads();  // every wave is done with Ks / Qs; norms and G are in LDS
 
-  // ---- L (strict lower) and P (lower with diagonal) in f32
+  // ---- L (strict lower, stored transposed: Lt[j][i] = L_ij) and P (lower
+  // with diagonal) in f32.  The decay is formed for every entry (its
+  // exponent is clamped to 0 above the diagonal, where the entry is 0), so
+  // that no branch surrounds the exponential.
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int j = 16 * nt + l % 16;
     const float rkj = rk_s[j], Gj = G_s[j];
+    f32x4 lv4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * (l / 16) + e;
-      const float dec = __expf(G_s[i] - Gj);
-      const float lv = (j < i) ? b_s[i] * rk_s[i] * rkj * accA[nt][e] * dec : 0.f;
-      const float pv =
-          (j <= i) ? d.scale * rq_s[i] * rkj * accB[nt][e] * dec : 0.f;
-      Ls[i * FS + j] = lv;
-      Ps[i * FS + j] = pv;
+      const float dx = G_s[i] - Gj;
+      const float dec = __expf(j <= i ? dx : 0.f);
+      const float lraw = b_s[i] * rk_s[i] * rkj * accA[nt][e] * dec;
+      const float praw = d.scale * rq_s[i] * rkj * accB[nt][e] * dec;
+      lv4[e] = (j < i) ? lraw : 0.f;
+      Ps[i * FS + j] = (j <= i) ? praw : 0.f;
     }
+    *reinterpret_cast<f32x4*>(&Lt[j * LS + 16 * w + 4 * (l / 16)]) = lv4;
   }
   __syncthreads();
 
-  // ---- T = (I + L)^-1, step 1: the four 16x16 diagonal blocks.
-  // Wave b, lane jj < 16: column jj of block b by forward substitution.
+  // ---- T = (I + L)^-1, step 1: the four 16x16 diagonal blocks.  Wave b,
+  // lane jj < 16 computes column jj of block b by right-looking
+  // substitution: once t_x is known, it updates the partial sums of every
+  // later row, so the dependent chain is one FMA per row instead of a dot
+  // product per row.  (The other lanes stay idle: every lane reads the same
+  // L entries, and fewer active lanes draw less LDS bandwidth.)
   if (l < 16) {
     const int b0 = 16 * w, jj = l;
-    float t[16];
+    float acc[16], t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = 0.f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int x = 0; x < r; ++x)
-        acc = __builtin_fmaf(Ls[(b0 + r) * FS + b0 + x], t[x], acc);
-      t[r] = (r == jj) ? 1.f : ((r < jj) ? 0.f : -acc);
+    for (int x = 0; x < 16; ++x) {
+      const float tx = (x == jj) ? 1.f : ((x < jj) ? 0.f : -acc[x]);
+      t[x] = tx;
+      const float* colx = &Lt[(b0 + x) * LS + b0];  // L[b0 + r][b0 + x]
+#pragma unroll
+      for (int r = x + 1; r < 16; ++r) acc[r] = __builtin_fmaf(colx[r], tx, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Ts[(b0 + r) * FS + b0 + jj] = t[r];
   }
-  // zero the strictly upper blocks
-  for (int idx = tid; idx < kC * kC; idx += kThreads) {
-    const int i = idx / kC, j = idx % kC;
-    if (j / 16 > i / 16) Ts[i * FS + j] = 0.f;
-  }
   __syncthreads();
 
-  // ---- step 2: block rows 1..3.  T_ib = -T_ii sum_{m=b}^{i-1} L_im T_mb;
-  // wave b computes block (i, b); lane: column cc = l%16, rows 4*(l/16)+e.
+  // ---- step 2: block rows 1..3, T_ib = -T_ii sum_{m=b}^{i-1} L_im T_mb, on
+  // f32 MFMA (v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and
+  // B[l/16][l%16] and holds D[4*(l/16) + e][l%16]); wave b computes block
+  // (i, b), the product Y = sum L_im T_mb goes through the wave's own LDS
+  // tile to become the B operand of T_ii Y.
   __shared__ float Ys[4][16 * 17];
   for (int bi = 1; bi < 4; ++bi) {
     if (w < bi) {
-      const int bb = w, cc = l % 16, r0 = 4 * (l / 16);
-      float y[4] = {0.f, 0.f, 0.f, 0.f};
+      const int bb = w, nn = l & 15, g4 = l >> 4;
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
       for (int m = bb; m < bi; ++m) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float tv = Ts[(16 * m + x) * FS + 16 * bb + cc];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            y[e] = __builtin_fmaf(Ls[(16 * bi + r0 + e) * FS + 16 * m + x], tv, y[e]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const int kr = 16 * m + 4 * ks + g4;
+          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(Lt[kr * LS + 16 * bi + nn],
+                                                   Ts[kr * FS + 16 * bb + nn], Y, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Ys[bb][(r0 + e) * 17 + cc] = y[e];
+      for (int e = 0; e < 4; ++e) Ys[bb][(4 * g4 + e) * 17 + nn] = Y[e];
       // the wave's own Ys block is read back by the same wave only
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-      float tvals[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 Tv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float yv = Ys[bb][x * 17 + cc];
+      for (int ks = 0; ks < 4; ++ks)
+        Tv = __builtin_amdgcn_mfma_f32_16x16x4f32(Ts[(16 * bi + nn) * FS + 16 * bi + 4 * ks + g4],
+                                                  Ys[bb][(4 * ks + g4) * 17 + nn], Tv, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          tvals[e] = __builtin_fmaf(Ts[(16 * bi + r0 + e) * FS + 16 * bi + x], yv, tvals[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ts[(16 * bi + r0 + e) * FS + 16 * bb + cc] = -tvals[e];
+      for (int e = 0; e < 4; ++e) Ts[(16 * bi + 4 * g4 + e) * FS + 16 * bb + nn] = -Tv[e];
     }
     __syncthreads();
   }
@@ -322,10 +328,13 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
       uint4* pdst = reinterpret_cast<uint4*>(wsb + WsLayout::kP) + 2 * pr * 64 + l;
       uint32_t hi[4], lo[4];
       const int ja = 32 * kb + 4 * g4, jb = ja + 16;
+      // columns jb lie in the strictly upper block (0,1) or (2,3) of T,
+      // which is zero and never written
+      const bool zb = (w == 0 && kb == 0) || (w == 2 && kb == 1);
       split2(Ts[i * FS + ja], Ts[i * FS + ja + 1], hi[0], lo[0]);
       split2(Ts[i * FS + ja + 2], Ts[i * FS + ja + 3], hi[1], lo[1]);
-      split2(Ts[i * FS + jb], Ts[i * FS + jb + 1], hi[2], lo[2]);
-      split2(Ts[i * FS + jb + 2], Ts[i * FS + jb + 3], hi[3], lo[3]);
+      split2(zb ? 0.f : Ts[i * FS + jb], zb ? 0.f : Ts[i * FS + jb + 1], hi[2], lo[2]);
+      split2(zb ? 0.f : Ts[i * FS + jb + 2], zb ? 0.f : Ts[i * FS + jb + 3], hi[3], lo[3]);
       tdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       tdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
       const int j0 = 32 * kb + 8 * g4;
@@ -536,29 +545,39 @@ static __device__ __attribute__((noinline)) void p2_chain(
   const int ka = n * kKS + 8 * g;
   const int kt = (4 * g + (n >> 2)) * kKS + 8 * (n & 3);
 
-  // H as natural B fragments for the output waves: rows 16*mb + 4g + e of
-  // a 32-row k-step are B rows 8*gp + ep with gp = 2*(mb%2) + g/2 and
-  // ep = 4*(g%2) + e
-  auto publish_H = [&](auto pb) {
+  // H as natural B fragments for the output waves, 32 rows (pair pq of
+  // 16-row blocks) at a time: rows 16*mb + 4g + e of a 32-row k-step are B
+  // rows 8*gp + ep with gp = 2*(mb%2) + g/2 and ep = 4*(g%2) + e
+  auto publish_pair = [&](auto pb, int pq) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int kb = mb >> 1, t = mb & 1, gp = 2 * t + (g >> 1);
-      uint2* dh = reinterpret_cast<uint2*>(&Hf[pb][2 * kb][16 * gp + n]) + (g & 1);
-      uint2* dl = reinterpret_cast<uint2*>(&Hf[pb][2 * kb + 1][16 * gp + n]) + (g & 1);
-      *dh = make_uint2(hw[kb][2 * t], hw[kb][2 * t + 1]);
-      *dl = make_uint2(lw[kb][2 * t], lw[kb][2 * t + 1]);
+    for (int t = 0; t < 2; ++t) {
+      const int gp = 2 * t + (g >> 1);
+      uint2* dh = reinterpret_cast<uint2*>(&Hf[pb][2 * pq][16 * gp + n]) + (g & 1);
+      uint2* dl = reinterpret_cast<uint2*>(&Hf[pb][2 * pq + 1][16 * gp + n]) + (g & 1);
+      *dh = make_uint2(hw[pq][2 * t], hw[pq][2 * t + 1]);
+      *dl = make_uint2(lw[pq][2 * t], lw[pq][2 * t + 1]);
     }
   };
-  // Operand fragments are read from LDS one stage before the MFMAs that use
-  // them (an LDS read takes about as long as four to six MFMAs):
-  //   KA[kb]  A fragments of K H; k-steps 0, 1 read during H' of the
-  //           previous chunk, 2, 3 at the start of K H
-  //   TF[pr]  T fragments; the k-step 0 pairs at the start of K H, the
-  //           k-step 1 pairs after it
-  //   KT[kb]  A fragments of K^T for H'; k-step 0 after K H, 1 at the start
-  //           of H'
+  // Operand fragments are read from LDS well before the MFMAs that use them
+  // (an LDS read takes about as long as four to six MFMAs):
+  //   KA[kb]  A fragments of K H (for the next chunk, during H')
+  //   KT[kb]  A fragments of K^T for H' (k-step 0 after K H of the chunk,
+  //           k-step 1 at the start of H')
+  //   TF[pr]  T fragments (during the last k-steps of K H)
   bf16x8 KA[4][4], KT[2][8], TF[6][2];
+  f32x4 KH[4], SV[4], SK[4];
   auto sched_fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // ask the scheduler to alternate one MFMA with up to three VALU
+  // instructions and one LDS access, n times, over the region before the
+  // next fence: VALU work then issues while the MFMAs run
+  auto interleave = [](auto n) {
+#pragma unroll
+    for (int i = 0; i < decltype(n)::value; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);
+    }
+  };
   auto read_KA = [&](auto B, int kb0, int kb1) {
     const u16* K = Kr[B];
 #pragma unroll
@@ -574,48 +593,32 @@ static __device__ __attribute__((noinline)) void p2_chain(
       KT[kb][mb] = frag(tr_read(&K[kt + 32 * kb * kKS + kpos(16 * mb)]),
                         tr_read(&K[kt + (32 * kb + 16) * kKS + kpos(16 * mb)]));
   };
-  auto read_TF = [&](auto B, int kb) {
-    // k-step 0: pairs (0,0) (1,0) (2,0) (3,0); k-step 1: (2,1) (3,1)
+  // T fragments and the row data of X (sb V and sk) of the chunk in buffer B
+  auto read_front_ops = [&](auto B) {
 #pragma unroll
-    for (int mi = (kb ? 2 : 0); mi < 4; ++mi) {
-      const int pr = pair_of(mi, kb);
+    for (int pr = 0; pr < 6; ++pr) {
       TF[pr][0] = as_bf16x8(Tf[B][2 * pr][l]);
       TF[pr][1] = as_bf16x8(Tf[B][2 * pr + 1][l]);
     }
-  };
-  // chunk c from the split H up to V_new (operands in buffer c % 3; KA
-  // k-steps 0, 1 of chunk c already read), and V_new in f32 for the output
-  // waves (same row mapping as publish_H)
-  auto front = [&](auto B) {
-    constexpr int bb = decltype(B)::value;
-    const float* vc = Vec[bb];
-    read_KA(B, 2, 4);
-    read_TF(B, 0);
-    f32x4 SV[4];  // sb V, rows 16*mj + 4g + e
 #pragma unroll
-    for (int mj = 0; mj < 4; ++mj)
-      SV[mj] = *reinterpret_cast<const f32x4*>(&SVt[bb][n * kSVS + 16 * mj + 4 * g]);
-    sched_fence();
-    f32x4 KH[4];
-#pragma unroll
-    for (int mj = 0; mj < 4; ++mj) KH[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bf16x8 bh = words(hw[kb]), bl = words(lw[kb]);
-#pragma unroll
-      for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bh, KH[mj]);
-#pragma unroll
-      for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bl, KH[mj]);
+    for (int mj = 0; mj < 4; ++mj) {
+      SV[mj] = *reinterpret_cast<const f32x4*>(&SVt[B][n * kSVS + 16 * mj + 4 * g]);
+      SK[mj] = *reinterpret_cast<const f32x4*>(&Vec[B][kC + 16 * mj + 4 * g]);
     }
-    sched_fence();
-    read_KT(B, 0);
-    read_TF(B, 1);
-    f32x4 sk[4];
+  };
+  // K H, k-step kb (H split hw/lw, both passes)
+  auto kh_step = [&](int kb) {
+    const bf16x8 bh = words(hw[kb]), bl = words(lw[kb]);
 #pragma unroll
-    for (int mj = 0; mj < 4; ++mj) sk[mj] = *reinterpret_cast<const f32x4*>(&vc[kC + 16 * mj + 4 * g]);
-    sched_fence();
-    // X = sb V - sk (K H), rows 16*mj + 4g + e, split per 32-row k-step;
-    // V_new = T X (3 passes, T lower triangular) one k-step at a time
+    for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bh, KH[mj]);
+#pragma unroll
+    for (int mj = 0; mj < 4; ++mj) KH[mj] = mfma(KA[kb][mj], bl, KH[mj]);
+  };
+  // the chunk in buffer B from K H (complete) to V_new, published in f32
+  // for the output waves (same row mapping as publish_pair); X is split and
+  // multiplied by T one k-step at a time
+  auto finish_front = [&](auto B) {
+    constexpr int bb = decltype(B)::value;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) VN[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -625,7 +628,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
       for (int t = 0; t < 2; ++t) {
         const int mj = 2 * kb + t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[t][e] = SV[mj][e] - sk[mj][e] * KH[mj][e];
+        for (int e = 0; e < 4; ++e) X[t][e] = __builtin_fmaf(-SK[mj][e], KH[mj][e], SV[mj][e]);
       }
       uint32_t xh[4], xl[4];
       split_pi(X[0], X[1], xh, xl);
@@ -639,18 +642,41 @@ static __device__ __attribute__((noinline)) void p2_chain(
           VN[mi] = mfma(TF[pr][pass == 2 ? 1 : 0], pass == 1 ? bl : bh, VN[mi]);
         }
     }
-    constexpr int pb = bb;
+    interleave(std::integral_constant<int, 18>{});
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int kb = mi >> 1, t = mi & 1, gp = 2 * t + (g >> 1);
-      *reinterpret_cast<f32x4*>(&Vf[pb][kb][16 * gp + n][4 * (g & 1)]) = VN[mi];
+      *reinterpret_cast<f32x4*>(&Vf[bb][kb][16 * gp + n][4 * (g & 1)]) = VN[mi];
     }
   };
-  // chunk c from V_new to H' = gamma_63 H + K^T diag(sd) V_new (KT of
-  // chunk c already read), two 16-row blocks of H at a time, each pair split
-  // for the next K H as soon as it is complete.  Reads KA k-steps 0, 1 of
-  // chunk c + 1 when there is one.
-  auto back = [&](auto B, auto NB, bool more) {
+
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  typedef std::integral_constant<int, 2> B2;
+  __syncthreads();  // chunks 0 and 1 staged
+  // chunk 0 up to V_new
+  read_KA(B0{}, 0, 4);
+  read_front_ops(B0{});
+#pragma unroll
+  for (int pq = 0; pq < 4; ++pq) {
+    split_pi(H[2 * pq], H[2 * pq + 1], hw[pq], lw[pq]);
+    publish_pair(B0{}, pq);
+  }
+#pragma unroll
+  for (int mj = 0; mj < 4; ++mj) KH[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kh_step(kb);
+  read_KT(B0{}, 0);
+  finish_front(B0{});
+  __syncthreads();
+  // One interval: chunk c from V_new to H_{c+1}, software-pipelined with
+  // chunk c + 1 up to V_new: each 32-row pair of H_{c+1} is split and
+  // published and its K H k-step issued while the next pair's MFMAs run.
+  // The buffers of chunk c and c + 1 are compile-time constants (the loop
+  // is unrolled by three), so every LDS address is a lane constant plus an
+  // immediate.  After the last chunk the second half runs on stale buffers
+  // and its results are never read (no branch in the MFMA stream).
+  auto step = [&](int c, auto B, auto NB) {
     const float* vc = Vec[B];
     const float gc = vc[4 * kC];
     f32x4 s0[2], s1[2];
@@ -659,8 +685,10 @@ static __device__ __attribute__((noinline)) void p2_chain(
       s0[kb] = *reinterpret_cast<const f32x4*>(&vc[3 * kC + 32 * kb + 4 * g]);
       s1[kb] = *reinterpret_cast<const f32x4*>(&vc[3 * kC + 32 * kb + 16 + 4 * g]);
     }
-    read_KT(B, 1);  // used after the k-step 0 MFMAs
+    read_KT(B, 1);
+    read_KA(NB, 0, 1);
     sched_fence();
+    // D = diag(sd) V_new, split per k-step
     uint32_t dh[2][4], dl[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -676,8 +704,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) H[mb][e] = gc * H[mb][e];
-    // k-step 0 (tokens 0..31) for all rows, then k-step 1 pair by pair, each
-    // pair split for the next K H as soon as it is complete
+    // H' k-step 0 (tokens 0..31) for every row block
 #pragma unroll
     for (int pq = 0; pq < 4; ++pq)
 #pragma unroll
@@ -687,11 +714,14 @@ static __device__ __attribute__((noinline)) void p2_chain(
           const int mb = 2 * pq + t;
           H[mb] = mfma(KT[0][mb], words(pass ? dl[0] : dh[0]), H[mb]);
         }
-    if (more) {
-      sched_fence();
-      read_KA(NB, 0, 2);
-      sched_fence();
-    }
+    interleave(std::integral_constant<int, 16>{});
+    sched_fence();
+    read_KA(NB, 1, 4);
+    sched_fence();
+#pragma unroll
+    for (int mj = 0; mj < 4; ++mj) KH[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // H' k-step 1 pair by pair; pair pq - 1 is split, published and its
+    // K H k-step issued behind pair pq's MFMAs
 #pragma unroll
     for (int pq = 0; pq < 4; ++pq) {
 #pragma unroll
@@ -701,27 +731,21 @@ static __device__ __attribute__((noinline)) void p2_chain(
           const int mb = 2 * pq + t;
           H[mb] = mfma(KT[1][mb], words(pass ? dl[1] : dh[1]), H[mb]);
         }
-      split_pi(H[2 * pq], H[2 * pq + 1], hw[pq], lw[pq]);
+      if (pq >= 1) {
+        split_pi(H[2 * pq - 2], H[2 * pq - 1], hw[pq - 1], lw[pq - 1]);
+        publish_pair(NB, pq - 1);
+        kh_step(pq - 1);
+      }
+      if (pq == 3) {
+        interleave(std::integral_constant<int, 28>{});
+        sched_fence();
+        read_front_ops(NB);
+        sched_fence();
+      }
     }
-  };
-
-  typedef std::integral_constant<int, 0> B0;
-  typedef std::integral_constant<int, 1> B1;
-  typedef std::integral_constant<int, 2> B2;
-  __syncthreads();  // chunks 0 and 1 staged
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) split_pi(H[2 * kb], H[2 * kb + 1], hw[kb], lw[kb]);
-  publish_H(B0{});
-  read_KA(B0{}, 0, 2);
-  front(B0{});
-  __syncthreads();
-  // one interval: chunk c from V_new to H_{c+1}, then chunk c + 1 up to
-  // V_new; the buffers of chunk c and c + 1 are compile-time constants (the
-  // loop is unrolled by three) so that every LDS address is a lane constant
-  // plus an immediate offset
-  auto step = [&](int c, auto B, auto NB) {
-    const bool more = c + 1 < nch;
-    back(B, NB, more);
+    split_pi(H[6], H[7], hw[3], lw[3]);
+    publish_pair(NB, 3);
+    kh_step(3);
     const int t0 = c * kC, nv = min(kC, d.L - t0);
     // checkpoint after token t0 + nv when it is a multiple of the interval
     if (d.ckpt_interval > 0 && ckpt && (t0 + nv) % d.ckpt_interval == 0) {
@@ -735,10 +759,10 @@ static __device__ __attribute__((noinline)) void p2_chain(
           ckpt[((((size_t)s * n_ck + idx) * d.Hv + h) * kD + r) * kD + col] = H[mb][e];
         }
     }
-    if (more) {
-      publish_H(NB);
-      front(NB);
-    }
+    sched_fence();
+    read_KT(NB, 0);
+    sched_fence();
+    finish_front(NB);
     __syncthreads();
   };
   for (int c = 0; c < nch; c += 3) {
