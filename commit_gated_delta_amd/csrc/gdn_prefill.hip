@@ -79,9 +79,8 @@ struct PDims {
 // 32 columns only six are nonzero: pair index pair_of(mi, kb) for
 // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); each pair has a hi and a lo fragment
 // (slots 2*pair and 2*pair + 1).  Lane l of a fragment holds row
-// 16*mi + l%16 and, with g = l/16,
-//   P: columns 32*kb + 8g + 0..7                       (natural order)
-//   T: columns 32*kb + 4g + 0..3, 32*kb + 16 + 4g + 0..3 (order "pi")
+// 16*mi + l%16 and, with g = l/16, columns 32*kb + 4g + 0..3 and
+// 32*kb + 16 + 4g + 0..3 (order "pi").
 // The pi order matches the MFMA result layout: a lane's result rows
 // 4g + 0..3 of two adjacent 16-row blocks are exactly the contraction entries
 // that the lane supplies in pi order, so results feed the next product from
@@ -114,6 +113,16 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi,
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
+// Split-bf16 words of two result tiles in pi order: elements 0..3 from tile
+// t0, 4..7 from tile t1.
+__device__ __forceinline__ void split_pi(const f32x4& t0, const f32x4& t1,
+                                         uint32_t (&hi)[4], uint32_t (&lo)[4]) {
+  split2(t0[0], t0[1], hi[0], lo[0]);
+  split2(t0[2], t0[3], hi[1], lo[1]);
+  split2(t1[0], t1[1], hi[2], lo[2]);
+  split2(t1[2], t1[3], hi[3], lo[3]);
+}
+
 __device__ __forceinline__ float bf16_f(u16 b) {
   return __uint_as_float((uint32_t)b << 16);
 }
@@ -134,20 +143,26 @@ __device__ __forceinline__ float dpp(float x) {
 }
 
 // ------------------------------------------------------------------ p1
+// Wave w owns the rows i = 16w..16w+15 of the chunk.  It computes the tiles
+// (j-block nt <= w, i-block w) of K K^T and K Q^T with K rows as the A
+// operand (K staged once in LDS, Q fragments loaded into registers); in the MFMA
+// result layout a lane then holds, for its row i, four consecutive columns
+// j of each tile -- exactly the lane's part of a pi-order A fragment of P,
+// which is split and written without passing through LDS.  L goes to LDS
+// transposed (Lt[j][i]) for the inversion.  The squared key norms are the
+// diagonal of K K^T; the query norms come from the wave's Q fragments.
 __global__ __launch_bounds__(kThreads) void p1_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k,
     const float* __restrict__ beta, const float* __restrict__ g,
     uint8_t* __restrict__ ws, PDims d) {
-  constexpr int KS = kD + 8;  // padded LDS row (bf16) against bank conflicts
-  constexpr int FS = kC + 1;  // padded f32 row
-  constexpr int LS = kC + 4;  // padded f32 row, 16-byte aligned
-  __shared__ __attribute__((aligned(16))) u16 Ks[kC * KS];
-  __shared__ __attribute__((aligned(16))) u16 Qs[kC * KS];  // later: P (f32)
+  constexpr int KS = kD + 8;  // padded bf16 row of K
+  constexpr int FS = kC + 1;  // padded f32 row of T
+  constexpr int LS = kC + 4;  // padded f32 row of Lt, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) u16 Ks[kC * KS];      // K rows; later T
   __shared__ __attribute__((aligned(16))) float Lt[kC * LS];  // L transposed
-  __shared__ float rk_s[kC], rq_s[kC], G_s[kC], b_s[kC];
-  float* Ts = reinterpret_cast<float*>(Ks);  // T (f32) once K is consumed
-  float* Ps = reinterpret_cast<float*>(Qs);
+  float* Ts = reinterpret_cast<float*>(Ks);  // written once K is consumed
   static_assert(sizeof(float) * kC * FS <= sizeof(u16) * kC * KS, "alias");
+  __shared__ float rk_s[kC], rq_s[kC], G_s[kC], b_s[kC];
 
   const int bid = blockIdx.x;
   const int h = bid % d.Hv;
@@ -159,20 +174,26 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int l = tid % 64;
+  const int n = l % 16, g4 = l / 16;
 
-  // ---- load K, Q rows (bf16) to LDS.  Rows past the end of the sequence
-  // are read from the last valid row (no branch around the loads): they only
-  // meet beta = 0, or feed output rows that are not stored.
+  // ---- K rows to LDS, Q fragments of block w to registers.  Rows past the
+  // end of the sequence are read from the last valid row (no branch around
+  // the loads): they only meet beta = 0, or feed output rows that are not
+  // stored.
   const int last = nv - 1;
+  const size_t rs = (size_t)d.Hk * kD;  // row stride
+  const u16* kbase = k + (((size_t)s * d.L + t0) * d.Hk + kh) * kD;
+  const u16* qbase = q + (((size_t)s * d.L + t0) * d.Hk + kh) * kD + 8 * g4;
+  uint4 QW[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    QW[ks] = *reinterpret_cast<const uint4*>(qbase + min(16 * w + n, last) * rs + 32 * ks);
+#pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int idx = it * kThreads + tid;  // 1024 pieces of 8 bf16
     const int row = idx / 16, col = (idx % 16) * 8;
-    const size_t off =
-        (((size_t)s * d.L + t0 + min(row, last)) * d.Hk + kh) * kD + col;
     *reinterpret_cast<uint4*>(&Ks[row * KS + col]) =
-        *reinterpret_cast<const uint4*>(k + off);
-    *reinterpret_cast<uint4*>(&Qs[row * KS + col]) =
-        *reinterpret_cast<const uint4*>(q + off);
+        *reinterpret_cast<const uint4*>(kbase + min(row, last) * rs + col);
   }
   if (tid < kC) {
     const size_t gi = ((size_t)s * d.L + t0 + min(tid, last)) * d.Hv + h;
@@ -188,76 +209,94 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     }
     G_s[tid] = x;
   }
-  __syncthreads();
+  __syncthreads();  // K rows, b, G in LDS
 
-  // ---- norms: four threads per row, 32 entries each
-  {
-    const int row = tid / 4, part = tid % 4;
-    float sk = 0.f, sq = 0.f;
+  // ---- AK[nt] = (K K^T)[16nt + 4g4 + e][16w + n], AQ[nt] = (K Q^T)[...]
+  f32x4 AK[4], AQ[4];
+  uint4 KW[4];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float kv = bf16_f(Ks[row * KS + part * 32 + e]);
-      const float qv = bf16_f(Qs[row * KS + part * 32 + e]);
-      sk = __builtin_fmaf(kv, kv, sk);
-      sq = __builtin_fmaf(qv, qv, sq);
-    }
-    sk += dpp<0xB1>(sk);  // quad_perm [1,0,3,2]
-    sk += dpp<0x4E>(sk);  // quad_perm [2,3,0,1]
-    sq += dpp<0xB1>(sq);
-    sq += dpp<0x4E>(sq);
-    if (part == 0) {
-      rk_s[row] = d.l2norm ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f;
-      rq_s[row] = d.l2norm ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
-    }
-  }
-
-  // ---- A = K K^T and B = Q K^T: wave w owns rows 16w..16w+15
-  f32x4 accA[4], accB[4];
+  for (int ks = 0; ks < 4; ++ks)
+    KW[ks] = *reinterpret_cast<const uint4*>(&Ks[(16 * w + n) * KS + 32 * ks + 8 * g4]);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    accA[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  {
-    const int arow = 16 * w + l % 16;
+    AK[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    AQ[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nt <= w) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kk = 32 * ks + 8 * (l / 16);
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[arow * KS + kk]));
-      const bf16x8 aq = as_bf16x8(*reinterpret_cast<const uint4*>(&Qs[arow * KS + kk]));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int brow = 16 * nt + l % 16;  // B[kk][j] = K[j][kk]
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[brow * KS + kk]));
-        accA[nt] = mfma(ak, b, accA[nt]);
-        accB[nt] = mfma(aq, b, accB[nt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[(16 * nt + n) * KS + 32 * ks + 8 * g4]));
+        AK[nt] = mfma(a, as_bf16x8(KW[ks]), AK[nt]);
+        AQ[nt] = mfma(a, as_bf16x8(QW[ks]), AQ[nt]);
       }
     }
   }
-  __syncthreads();  // every wave is done with Ks / Qs; norms and G are in LDS
-
-  // ---- L (strict lower, stored transposed: Lt[j][i] = L_ij) and P (lower
-  // with diagonal) in f32.  The decay is formed for every entry (its
-  // exponent is clamped to 0 above the diagonal, where the entry is 0), so
-  // that no branch surrounds the exponential.
+  // ---- inverse norms of the rows i = 16w + n: |k_i|^2 is the diagonal of
+  // the tile nt = w (lane with 4*g4 + e = n); |q_i|^2 from the Q fragments
+  {
+    float sq = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int j = 16 * nt + l % 16;
-    const float rkj = rk_s[j], Gj = G_s[j];
-    f32x4 lv4;
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t wd[4] = {QW[ks].x, QW[ks].y, QW[ks].z, QW[ks].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * (l / 16) + e;
-      const float dx = G_s[i] - Gj;
-      const float dec = __expf(j <= i ? dx : 0.f);
-      const float lraw = b_s[i] * rk_s[i] * rkj * accA[nt][e] * dec;
-      const float praw = d.scale * rq_s[i] * rkj * accB[nt][e] * dec;
-      lv4[e] = (j < i) ? lraw : 0.f;
-      Ps[i * FS + j] = (j <= i) ? praw : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(wd[e] << 16), hi = __uint_as_float(wd[e] & 0xffff0000u);
+        sq = __builtin_fmaf(lo, lo, sq);
+        sq = __builtin_fmaf(hi, hi, sq);
+      }
     }
-    *reinterpret_cast<f32x4*>(&Lt[j * LS + 16 * w + 4 * (l / 16)]) = lv4;
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    float kk = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt == w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * g4 + e == n) kk = AK[nt][e];
+      }
+    if (g4 == n / 4) rk_s[16 * w + n] = d.l2norm ? __builtin_amdgcn_rsqf(kk + 1e-6f) : 1.0f;
+    if (g4 == 0) rq_s[16 * w + n] = d.l2norm ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
   }
-  __syncthreads();
+  __syncthreads();  // norms, b, G in LDS
+
+  // ---- L (strict lower, to LDS transposed) and P (lower with diagonal,
+  // kept in registers) for row i = 16w + n, columns j = 16nt + 4g4 + e.  The
+  // decay is formed for every entry (its exponent clamped to 0 above the
+  // diagonal, where the entry is 0), so no branch surrounds the exponential.
+  uint8_t* wsb = ws + ((size_t)bid) * WsLayout::kBytes;
+  {
+    const int i = 16 * w + n;
+    const float Gi = G_s[i], bki = b_s[i] * rk_s[i], sqi = d.scale * rq_s[i];
+    f32x4 pv[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      pv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (nt <= w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * nt + 4 * g4 + e;
+          const float rkj = rk_s[j];
+          const float dec = __expf(j <= i ? Gi - G_s[j] : 0.f);
+          const float lraw = bki * rkj * AK[nt][e] * dec;
+          const float praw = sqi * rkj * AQ[nt][e] * dec;
+          Lt[j * LS + i] = (j < i) ? lraw : 0.f;
+          pv[nt][e] = (j <= i) ? praw : 0.f;
+        }
+      }
+    }
+    // P fragments, pi order: columns 32kb + 4g4 + 0..3 (tile 2kb) and
+    // 32kb + 16 + 4g4 + 0..3 (tile 2kb + 1)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && w < 2) break;
+      uint32_t hi[4], lo[4];
+      split_pi(pv[2 * kb], pv[2 * kb + 1], hi, lo);
+      uint4* pdst = reinterpret_cast<uint4*>(wsb + WsLayout::kP) + 2 * pair_of(w, kb) * 64 + l;
+      pdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      pdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+  __syncthreads();  // Lt complete
 
   // ---- T = (I + L)^-1, step 1: the four 16x16 diagonal blocks.  Wave b,
   // lane jj < 16 computes column jj of block b by right-looking
@@ -317,15 +356,12 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     __syncthreads();
   }
 
-  // ---- write T (pi order), P (natural order) as split bf16 fragments, and
-  // the row vectors
-  uint8_t* wsb = ws + ((size_t)bid) * WsLayout::kBytes;
+  // ---- write T (pi order) as split bf16 fragments, and the row vectors
   {
-    const int i = 16 * w + l % 16, g4 = l / 16;
+    const int i = 16 * w + l % 16;
     for (int kb = 0; kb < (w >= 2 ? 2 : 1); ++kb) {
       const int pr = pair_of(w, kb);
       uint4* tdst = reinterpret_cast<uint4*>(wsb + WsLayout::kT) + 2 * pr * 64 + l;
-      uint4* pdst = reinterpret_cast<uint4*>(wsb + WsLayout::kP) + 2 * pr * 64 + l;
       uint32_t hi[4], lo[4];
       const int ja = 32 * kb + 4 * g4, jb = ja + 16;
       // columns jb lie in the strictly upper block (0,1) or (2,3) of T,
@@ -337,12 +373,6 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
       split2(zb ? 0.f : Ts[i * FS + jb + 2], zb ? 0.f : Ts[i * FS + jb + 3], hi[3], lo[3]);
       tdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       tdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      const int j0 = 32 * kb + 8 * g4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        split2(Ps[i * FS + j0 + 2 * e], Ps[i * FS + j0 + 2 * e + 1], hi[e], lo[e]);
-      pdst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      pdst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
   }
   if (tid < kC) {
@@ -408,16 +438,6 @@ __device__ __forceinline__ bf16x8 frag(uint2 a, uint2 b) {
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
-// Split-bf16 words of two result tiles in pi order: elements 0..3 from tile
-// t0, 4..7 from tile t1.
-__device__ __forceinline__ void split_pi(const f32x4& t0, const f32x4& t1,
-                                         uint32_t (&hi)[4], uint32_t (&lo)[4]) {
-  split2(t0[0], t0[1], hi[0], lo[0]);
-  split2(t0[2], t0[3], hi[1], lo[1]);
-  split2(t1[0], t1[1], hi[2], lo[2]);
-  split2(t1[2], t1[3], hi[3], lo[3]);
-}
-
 __device__ __forceinline__ bf16x8 words(const uint32_t (&x)[4]) {
   return as_bf16x8(make_uint4(x[0], x[1], x[2], x[3]));
 }
@@ -438,7 +458,7 @@ struct KvTransit {
 // with two).
 struct OutOps {
   uint4 qa[4], qb[4];  // Q A fragments (natural order)
-  uint4 p[3][2];       // P fragments (hi, lo): (mA,0), (mB,0), (mB,1)
+  uint4 p[3][2];       // P fragments, pi order (hi, lo): (mA,0), (mB,0), (mB,1)
 };
 
 // LDS of a p2 workgroup, shared by the role functions below.
@@ -448,7 +468,7 @@ struct P2Lds {
   __attribute__((aligned(16))) float SVt[3][kTile * kSVS]; // diag(sb) V, [col][row]
   __attribute__((aligned(16))) float Vec[3][4 * kC + 4];  // sb sk so sd, gamma
   __attribute__((aligned(16))) uint4 Hf[3][8][64];        // H (natural B)
-  __attribute__((aligned(16))) float Vf[3][2][64][8];     // V_new f32 (natural B rows)
+  __attribute__((aligned(16))) float Vf[3][2][64][8];     // V_new f32 (pi-order B rows)
 };
 __shared__ P2Lds p2lds;
 
@@ -643,11 +663,11 @@ static __device__ __attribute__((noinline)) void p2_chain(
         }
     }
     interleave(std::integral_constant<int, 18>{});
+    // V_new for the output waves as pi-order B fragments: lane l holds rows
+    // 32*kb + 4g + 0..3 and 32*kb + 16 + 4g + 0..3 (f32)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int kb = mi >> 1, t = mi & 1, gp = 2 * t + (g >> 1);
-      *reinterpret_cast<f32x4*>(&Vf[bb][kb][16 * gp + n][4 * (g & 1)]) = VN[mi];
-    }
+    for (int mi = 0; mi < 4; ++mi)
+      *reinterpret_cast<f32x4*>(&Vf[bb][mi >> 1][l][4 * (mi & 1)]) = VN[mi];
   };
 
   typedef std::integral_constant<int, 0> B0;
