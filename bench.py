@@ -34,7 +34,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-F32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published f32 vector peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 METRIC = "GDN verify+commit head-token updates/s & % HBM roofline (8 lanes, T=16)"
 
@@ -59,13 +58,6 @@ def alg_bytes_commit(m_lane):
     return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
 
 
-def alg_flops_verify(t_lane):
-    """Algorithmic flops of one verify call: per state element and token the
-    prediction (1 FMA = 2), the decayed rank-1 write (1 mul + 1 FMA = 3) and
-    the output (1 FMA = 2): 7 flops x d_k x d_v x h_v x T per lane-layer."""
-    return NL * sum(7 * DK * DV * HV * int(t) for t in t_lane)
-
-
 def alg_bytes_fused(t_lane, m_prev):
     """Algorithmic bytes of one gdn_commit_verify: per lane-layer the state
     read, the committed state write when m_prev > 0, m_prev records read,
@@ -77,14 +69,11 @@ def alg_bytes_fused(t_lane, m_prev):
                           for m in m_prev)
 
 
-def alg_flops_fused(t_lane, m_prev):
-    """Verify flops plus the replay: one FMA (2 flops) per state element per
-    accepted token."""
-    return alg_flops_verify(t_lane) + NL * HV * DK * DV * 2 * int(np.sum(m_prev))
+WINDOW_SOURCES = ("gdn_window.hip", "gdn_window_mfma.hip",
+                  "gdn_window_common.h", "gdn_step.h")
 
 
-def kernel_source_hash(files=("gdn_window.hip", "gdn_window_common.h",
-                              "gdn_step.h")):
+def kernel_source_hash(files=WINDOW_SOURCES):
     """sha256 of the kernel sources with // comments and blank lines removed
     (a comment edit leaves the recorded counters valid)."""
     import hashlib
@@ -109,7 +98,7 @@ def measured_traffic(kernel):
         return None
     k = rec.get(kernel)
     files = (("gdn_prefill.hip",) if kernel.startswith("prefill")
-             else ("gdn_window.hip", "gdn_window_common.h", "gdn_step.h"))
+             else WINDOW_SOURCES)
     if not k or k.get("source_sha256") != kernel_source_hash(files):
         return None
     return float(k["bytes_per_launch"])
@@ -458,18 +447,17 @@ def main():
         bv = alg_bytes_verify(t_lane)
         bc = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
                             for s in range(args.steps)]))
-        fv = alg_flops_verify(t_lane)
         res["two-call"] = {
             "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
             "hbm_roofline_frac_path": (bv + bc) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "verify_ms": ms_v, "commit_ms": ms_c,
-            "verify_tflops": fv / (ms_v * 1e-3) / 1e12,
             "verify_alg_GBps": bv / (ms_v * 1e-3) / 1e9,
+            "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "commit_alg_GBps": bc / (ms_c * 1e-3) / 1e9,
             "commit_hbm_frac": bc / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "verify_traffic": measured_traffic("verify_kernel"),
             "commit_traffic": measured_traffic("commit_kernel"),
-            "alg_bytes_per_step": bv + bc, "alg_flops_verify": fv}
+            "alg_bytes_verify": bv, "alg_bytes_per_step": bv + bc}
         del S, rec
     if args.path in ("fused", "both"):
         S = torch.from_numpy(S0).to(dev)
@@ -494,36 +482,32 @@ def main():
         ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         mp = [m_prev_of(args.warmup + s) for s in range(args.steps)]
         bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in mp]))
-        ff = float(np.mean([alg_flops_fused(t_lane, m) for m in mp]))
         res["fused"] = {
             "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
             "hbm_roofline_frac_path": bf / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_ms": ms_f, "tflops": ff / (ms_f * 1e-3) / 1e12,
+            "kernel_ms": ms_f,
             "alg_GBps": bf / (ms_f * 1e-3) / 1e9,
             "traffic": measured_traffic("fused_kernel"),
-            "alg_bytes_per_step": bf, "alg_flops_per_launch": ff}
+            "alg_bytes_per_step": bf}
         del S, recs
 
     head = "fused" if "fused" in res else "two-call"
     h = res[head]
     ms_per_step = h["ms_per_step"]
     if head == "fused":
-        roof = {"bound": "alu",
-                "kernel": "gdn_commit_verify (verify_kernel, replay on)",
-                "achieved": h["tflops"], "peak": F32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": h["tflops"] / F32_VECTOR_PEAK_TFLOPS,
+        roof = {"bound": "hbm",
+                "kernel": "gdn_commit_verify (mverify_kernel, replay on)",
+                "achieved": h["alg_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": h["alg_GBps"] / HBM_PEAK_GBS,
                 "traffic": h["traffic"],
-                "alg_flops_per_launch": h["alg_flops_per_launch"],
                 "alg_bytes_per_launch": h["alg_bytes_per_step"],
                 "avg_launch_ms": h["kernel_ms"]}
     else:
-        roof = {"bound": "alu", "kernel": "gdn_verify (verify_kernel)",
-                "achieved": h["verify_tflops"], "peak": F32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": h["verify_tflops"] / F32_VECTOR_PEAK_TFLOPS,
+        roof = {"bound": "hbm", "kernel": "gdn_verify (mverify_kernel)",
+                "achieved": h["verify_alg_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": h["verify_hbm_frac"],
                 "traffic": h["verify_traffic"],
-                "alg_flops_per_launch": h["alg_flops_verify"],
-                "alg_bytes_per_launch": alg_bytes_verify(t_lane),
+                "alg_bytes_per_launch": h["alg_bytes_verify"],
                 "avg_launch_ms": h["verify_ms"]}
     out = {
         "metric": METRIC,

@@ -97,14 +97,6 @@ struct StepScalars {
   float f1, f2, f3, phi;
   float beta, c, kq, pad;  // kq = k_t . q_t (raw rows)
 };
-// Records of the previous window, replayed by the fused commit + verify
-// before the new window starts (unused by a plain verify).
-struct PrevRecords {
-  const float* k;
-  const float* u;
-  const float2* scale;
-  LaneTable m;  // accepted prefix per lane
-};
 
 // Replay of m recorded tokens on the held state (the commit of the
 // ReplaySSM section): the same fold, write and materialisation as
@@ -552,18 +544,6 @@ void set_error(const char* msg) {
   snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
 }
 
-struct VerifyArgs {
-  const void *q, *k, *v;
-  const float *beta, *g;
-  float* S;
-  float* o;
-  float *rk, *ru;
-  float2* ra;
-  float* dbg;
-  float scale;
-  int l2;
-};
-
 template <int DK, bool DBG, typename TIn, bool REPLAY, bool TREE, typename Tab>
 static hipError_t launch_verify_t(const WinDims& w, const LaneTable& tl,
                                   const VerifyArgs& a, const PrevRecords& pr,
@@ -683,8 +663,12 @@ extern "C" int gdn_verify(const gdn_dims* dims, const int32_t* t_lane,
   if (!any) return GDN_OK;
   PrevRecords none;
   memset(&none, 0, sizeof(none));
-  hipError_t e = launch_verify<false>(win_dims(*dims), tl, in_dtype, a, none,
-                                      (hipStream_t)stream);
+  hipError_t e =
+      mverify_eligible(*dims, in_dtype, a)
+          ? launch_mverify(win_dims(*dims), tl, a, none, false,
+                           (hipStream_t)stream)
+          : launch_verify<false>(win_dims(*dims), tl, in_dtype, a, none,
+                                 (hipStream_t)stream);
   return hip_status(e, "gdn_verify launch");
 }
 
@@ -872,8 +856,11 @@ extern "C" int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
     for (int n = 0; n < d.n_lanes; ++n) pr.m.v[n] = (uint8_t)m_prev[n];
   }
   if (!any && ct.n_act == 0) return GDN_OK;
-  hipError_t e = launch_verify<true>(win_dims(d), tl, in_dtype, a, pr,
-                                     (hipStream_t)stream);
+  hipError_t e = mverify_eligible(d, in_dtype, a)
+                      ? launch_mverify(win_dims(d), tl, a, pr, true,
+                                       (hipStream_t)stream)
+                      : launch_verify<true>(win_dims(d), tl, in_dtype, a, pr,
+                                            (hipStream_t)stream);
   return hip_status(e, "gdn_commit_verify launch");
 }
 

@@ -38,6 +38,28 @@ struct CommitTable {
   uint8_t m[GDN_MAX_LANES];
 };
 
+// Records of the previous window, replayed by the fused commit + verify
+// before the new window starts (unused by a plain verify).
+struct PrevRecords {
+  const float* k;
+  const float* u;
+  const float2* scale;
+  LaneTable m;  // accepted prefix per lane
+};
+
+// Host-side arguments of a verify launch.
+struct VerifyArgs {
+  const void *q, *k, *v;
+  const float *beta, *g;
+  float* S;
+  float* o;
+  float *rk, *ru;
+  float2* ra;
+  float* dbg;
+  float scale;
+  int l2;
+};
+
 // Draft trees (windows where a node steps from its parent's state): the
 // parents of every lane's nodes, or for a commit the accepted nodes of every
 // active lane, as bytes in the kernel arguments.
@@ -275,5 +297,13 @@ static int commit_lanes(const char* fn, const gdn_dims& d,
   ct.n_act = n_act;
   return GDN_OK;
 }
+
+// The matrix-core verify (gdn_window_mfma.hip): whether a call can take it,
+// and its launch (replay = the fused commit + verify).
+__attribute__((visibility("hidden"))) bool mverify_eligible(
+    const gdn_dims& d, int in_dtype, const VerifyArgs& a);
+__attribute__((visibility("hidden"))) hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
+                          const VerifyArgs& a, const PrevRecords& pr,
+                          bool replay, hipStream_t st);
 
 }  // namespace gdn

@@ -1,0 +1,581 @@
+// gdn_window_mfma.hip -- speculative-window verify and the fused commit +
+// verify on the gfx950 matrix cores, for bf16 inputs, d_k = 128, d_v a
+// multiple of 128 and windows of at most 16 tokens (the shapes of the
+// speculative-decoding section of the NInfer technical review,
+// blog.123qwe.co.kr post 4624).  Other shapes take gdn_window.hip.
+//
+// The window is one chunk of the block (WY/UT) form of the rule: Yang et
+// al., "Parallelizing Linear Transformers with the Delta Rule over Sequence
+// Length" (NeurIPS 2024), Sec. 3, with the per-token decay of Gated DeltaNet
+// (ICLR 2025, Sec. 3).  With the window's start state H (d_k x d_v, key-major
+// as stored), raw key / query rows k_t, q_t (t = 0..15), their inverse norms
+// rk_t, rq_t, and dec(t, s) = exp(g_{s+1} + ... + g_t) the decay from token s
+// to token t (A_t = dec(t, -1) the decay since the window start):
+//   L_ts = beta_t rk_t rk_s dec(t, s) (k_t . k_s)            s < t
+//   T    = (I + L)^-1                                     (unit lower)
+//   P_ts = scale rq_t rk_s dec(t, s) (q_t . k_s)             s <= t
+//   X_t  = beta_t v_t - beta_t A_t rk_t (K H)_t
+//   U    = T X                          (row t: the delta u_t of token t)
+//   O_t  = scale rq_t A_t (Q H)_t + (P U)_t      (o_t = scale S_t qhat_t)
+// Unrolling the token-by-token rule over the window gives exactly these
+// expressions.  The decays come from sums of the gates inside segments
+// that end at a gate whose exponential is 0 in f32 (g < -128, g = -inf): a
+// decay across such a token is 0, and no difference of two infinite sums
+// is ever formed.
+//
+// Records: the same records as gdn_window.hip -- raw key rows as f32, the
+// scale step (phi, c) of every token (the lazy-decay scale sequence of
+// gdn_step.h, with its folds) and ut_t = u_t rk_t / c_t -- so gdn_commit
+// replays them unchanged.  The state that verify holds after token t is, by
+// definition here, the replay of its own first t + 1 records: the debug
+// states are produced exactly so (the same fold, fma and materialisation,
+// in the same order, on the same values as commit), hence commit(m) is
+// bitwise the debug state m - 1.  The outputs come from the chunk form, so
+// they agree with the replayed states to rounding, not bit for bit.
+//
+// Work decomposition: one 256-thread workgroup per (layer, lane, value head,
+// block of 128 value columns); wave w owns 32 columns.  Lane l (g4 = l/16,
+// n = l%16) holds the state entries of rows 32 ks + 8 g4 + e (ks = 0..3,
+// e = 0..7) at its two columns 2n, 2n + 1: for every row the 16 lanes of a
+// group read 128 contiguous bytes.  Those eight rows are exactly the lane's
+// B operand of v_mfma_f32_16x16x32_bf16 for k-step ks, after a split of
+// every f32 entry into bf16 hi + lo (x = hi + lo + ~2^-17 |x|): K H and
+// Q H take 32 MFMAs per wave against the exact bf16 key / query rows.
+// Every wave also forms the window's 16 x 16 matrices itself (K K^T and
+// K Q^T on MFMA, the gates, L, P and T), so the four waves never wait for
+// each other; T comes from a right-looking substitution in the wave's own
+// LDS tile.  T X and P U run on v_mfma_f32_16x16x4_f32, whose B operand is
+// the D layout of the previous product (k-slot g4 of step e is token
+// 4 g4 + e).  The small loads (rows, gates) are issued before the 64 KB of
+// state, so that everything but the state products overlaps its latency.
+//
+// MFMA layouts (wave64):
+//   16x16x32 bf16: lane l holds A[l%16][8(l/16) + e], B[8(l/16) + e][l%16]
+//   16x16x4 f32:   lane l holds A[l%16][l/16], B[l/16][l%16]
+//   both:          D[4(l/16) + e][l%16], e = 0..3.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "gdn_step.h"
+#include "gdn_window_common.h"
+
+namespace gdn {
+namespace wm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDK = 128;        // key rows
+constexpr int kKS = kDK / 32;   // k-steps of the bf16 products
+constexpr int kTok = 16;        // window tokens: one 16-row MFMA tile
+constexpr int kCB = 128;        // value columns per workgroup
+constexpr int kLS = 20;         // padded row of a 16 x 16 LDS matrix
+constexpr int kUS = 33;         // padded row of a wave's ut tile
+constexpr float kReset = -128.f;  // exp(g) rounds to 0 in f32 below this
+
+// Records of the previous window, staged for the fused replay.
+struct Stage {
+  float k[kTok][kDK];  // raw key rows
+  float u[kTok][kCB];  // ut of this workgroup's columns
+  f32x2 sc[kTok];      // (phi, c)
+};
+// A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
+struct WaveLds {
+  __attribute__((aligned(16))) float Lt[kTok * kLS];
+  __attribute__((aligned(16))) float Ts[kTok * kLS];
+  float Us[kTok * kUS];
+};
+
+__device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two f32 values as packed bf16 pairs: hi = bf16(x), lo = bf16(x - hi), both
+// rounded to nearest even.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi,
+                                       uint32_t& lo) {
+  const f32x2 x = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const f32x2 r = {a - lo_f(hi), b - hi_f(hi)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+
+// LDS written by some lanes of a wave and read by others of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float bcast(float x, int src) {
+  return __shfl(x, src, kWave);
+}
+__device__ __forceinline__ float lane_value(float x, int t) {  // t uniform
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
+}
+
+template <bool REPLAY, bool DBG>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void mverify_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ g, float* S, float* __restrict__ o,
+    float* __restrict__ rec_k, float* __restrict__ rec_u,
+    float2* __restrict__ rec_scale, float* __restrict__ dbg, WinDims d,
+    LaneTable tl, float scale, int l2norm, PrevRecords prev) {
+  __shared__ WaveLds wl[kWaves];
+  __shared__ std::conditional_t<REPLAY, Stage, char> stage;
+
+  const int nc = d.dv / kCB;
+  int item = xcd_item(blockIdx.x, gridDim.x);
+  const int cb = item % nc;
+  item /= nc;
+  const int h = item % d.Hv;
+  item /= d.Hv;
+  const int lane = item % d.N;
+  const int layer = item / d.N;
+  const int T = tl.v[lane];
+  const int m_prev = REPLAY ? prev.m.v[lane] : 0;
+  if (T == 0 && m_prev == 0) return;
+
+  const int tid = (int)threadIdx.x;
+  const int w = uniform(tid / kWave);
+  const int l = tid % kWave;
+  const int g4 = l >> 4, n = l & 15;
+  const int kh = h / d.group;
+  const int dv = d.dv;
+  const int c0 = kCB * cb + 32 * w + 2 * n;  // this lane's columns c0, c0 + 1
+  const size_t ll = (size_t)layer * d.N + lane;
+  const size_t tok0 = ll * d.T;              // token 0 of this lane-layer
+  const size_t kq_step = (size_t)d.Hk * kDK;  // per token: q, k, key records
+  const size_t vo_step = (size_t)d.Hv * dv;   // per token: v, o, ut records
+  const uint16_t* __restrict__ k0 = k + (tok0 * d.Hk + kh) * kDK;
+  const uint16_t* __restrict__ q0 = q + (tok0 * d.Hk + kh) * kDK;
+  const uint16_t* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)dv;
+  const size_t gh0 = tok0 * d.Hv + h;  // gate index of token 0 (step Hv)
+  float* const Sh = S + (ll * d.Hv + h) * (size_t)kDK * dv;
+  WaveLds& W = wl[w];
+
+  // ---- small loads: token n's gates and key / query row pieces (the A
+  // operands); below, the values of the tokens 4 g4 + e at this lane's
+  // columns.  Tokens at or past T read token 0 and are replaced by zeros.  A plain
+  // verify issues them before the state, so that everything but the state
+  // products overlaps its latency; the fused call after its replay, which
+  // keeps them out of the registers the replay needs.
+  const bool tv = n < T;
+  const int tn = tv ? n : 0;
+  float gt, bt;
+  u32x4 Kf[kKS], Qf[kKS];
+  uint32_t vw[4];
+  auto load_small = [&]() {
+    gt = tv ? g[gh0 + (size_t)tn * d.Hv] : 0.f;
+    bt = tv ? beta[gh0 + (size_t)tn * d.Hv] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const uint32_t off = (uint32_t)(tn * kq_step) + 32 * ks + 8 * g4;
+      const u32x4 kr = *reinterpret_cast<const u32x4*>(k0 + off);
+      const u32x4 qr = *reinterpret_cast<const u32x4*>(q0 + off);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      Kf[ks] = tv ? kr : z;
+      Qf[ks] = tv ? qr : z;
+    }
+  };
+  // the value words are needed only after the state products: issued after
+  // the state, they hold no registers through the prologue
+  auto load_v = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g4 + e;
+      const int tc = t < T ? t : 0;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(
+          v0 + (uint32_t)(tc * vo_step) + c0);
+      vw[e] = t < T ? x : 0u;
+    }
+  };
+  if constexpr (!REPLAY) load_small();
+
+  // ---- the state: rows 32 ks + 8 g4 + e, columns c0 and c0 + 1
+  f32x2 s2[kKS][8];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      s2[ks][e] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(
+          Sh + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)));
+
+  // ---- fused commit: the accepted prefix of the previous window, replayed
+  // on the held state with exactly the operations of gdn_commit (fold,
+  // fma per entry, materialisation) and stored.  The records come in
+  // through LDS: two float4 of key rows and two of ut per thread, and the
+  // scale steps.
+  if constexpr (REPLAY) {
+    if (m_prev > 0) {
+      const float* __restrict__ pk = prev.k + (tok0 * d.Hk + kh) * kDK;
+      const float* __restrict__ pu =
+          prev.u + (tok0 * d.Hv + h) * (size_t)dv + kCB * cb;
+      f32x4 kst[2], ust[2];
+#pragma unroll
+      for (int rep = 0; rep < 2; ++rep) {
+        const int e = tid + kBlock * rep;  // float4 slot: token e/32
+        int tok = e >> 5;
+        tok = tok < m_prev ? tok : m_prev - 1;
+        kst[rep] = *reinterpret_cast<const f32x4*>(
+            pk + (uint32_t)(tok * kq_step) + 4 * (e & 31));
+        ust[rep] = *reinterpret_cast<const f32x4*>(
+            pu + (uint32_t)(tok * vo_step) + 4 * (e & 31));
+      }
+      const int ts = tid < m_prev ? tid : m_prev - 1;
+      const f32x2 scst = *reinterpret_cast<const f32x2*>(
+          prev.scale + gh0 + (size_t)ts * d.Hv);
+#pragma unroll
+      for (int rep = 0; rep < 2; ++rep) {
+        const int e = tid + kBlock * rep;
+        reinterpret_cast<f32x4*>(&stage.k[0][0])[e] = kst[rep];
+        reinterpret_cast<f32x4*>(&stage.u[0][0])[e] = ust[rep];
+      }
+      if (tid < kTok) stage.sc[tid] = scst;
+      __syncthreads();
+      float cf = 1.0f;
+#pragma unroll 1
+      for (int t = 0; t < m_prev; ++t) {
+        const f32x2 fc = stage.sc[t];
+        const f32x2 uc =
+            *reinterpret_cast<const f32x2*>(&stage.u[t][32 * w + 2 * n]);
+        f32x4 kc[2 * kKS];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          kc[2 * ks] =
+              *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4]);
+          kc[2 * ks + 1] =
+              *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4 + 4]);
+        }
+        const float ph = __int_as_float(
+            __builtin_amdgcn_readfirstlane(__float_as_int(fc[0])));
+        if (ph != 1.f) {
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              s2[ks][e][0] = ph * s2[ks][e][0];
+              s2[ks][e][1] = ph * s2[ks][e][1];
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kv = kc[2 * ks + e / 4][e % 4];
+            s2[ks][e][0] = state_update(s2[ks][e][0], uc[0], kv);
+            s2[ks][e][1] = state_update(s2[ks][e][1], uc[1], kv);
+          }
+        cf = fc[1];
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s2[ks][e][0] = materialise(cf, s2[ks][e][0]);
+          s2[ks][e][1] = materialise(cf, s2[ks][e][1]);
+          __builtin_nontemporal_store(
+              s2[ks][e], reinterpret_cast<f32x2*>(
+                             Sh + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)));
+        }
+    }
+    if (T == 0) return;
+    load_small();
+  }
+
+  // ---- inverse norms of token n (sums over the lane's row pieces, then
+  // over the four groups)
+  float skk = 0.f, sqq = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const u32x4 kw = Kf[ks], qw = Qf[ks];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      skk = __builtin_fmaf(lo_f(kw[p]), lo_f(kw[p]), skk);
+      skk = __builtin_fmaf(hi_f(kw[p]), hi_f(kw[p]), skk);
+      sqq = __builtin_fmaf(lo_f(qw[p]), lo_f(qw[p]), sqq);
+      sqq = __builtin_fmaf(hi_f(qw[p]), hi_f(qw[p]), sqq);
+    }
+  }
+  skk += __shfl_xor(skk, 16, kWave);
+  sqq += __shfl_xor(sqq, 16, kWave);
+  skk += __shfl_xor(skk, 32, kWave);
+  sqq += __shfl_xor(sqq, 32, kWave);
+  const float rk = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
+  const float rq = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
+
+  // the key record rows (raw rows as f32), written while the widened
+  // values are at hand
+  if (cb == 0 && h % d.group == 0 && tv) {
+    // raw key rows as f32: wave w writes the k-step w piece of row n
+    float* __restrict__ dst =
+        rec_k + (tok0 * d.Hk + kh) * kDK + (uint32_t)(n * kq_step) + 32 * w + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      if (ks == w) {
+        const u32x4 kw = Kf[ks];
+        reinterpret_cast<float4*>(dst)[0] =
+            make_float4(lo_f(kw[0]), hi_f(kw[0]), lo_f(kw[1]), hi_f(kw[1]));
+        reinterpret_cast<float4*>(dst)[1] =
+            make_float4(lo_f(kw[2]), hi_f(kw[2]), lo_f(kw[3]), hi_f(kw[3]));
+      }
+    }
+  }
+
+  // ---- K K^T and K Q^T: lane (g4, n), entry e = (k_{4g4+e} . k_n) and
+  // (k_{4g4+e} . q_n) -- row n, column s = 4 g4 + e of the A layout of the
+  // f32 products below
+  f32x4 KK = {0.f, 0.f, 0.f, 0.f}, KQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    KK = mma_bf16(Kf[ks], Kf[ks], KK);
+    KQ = mma_bf16(Kf[ks], Qf[ks], KQ);
+  }
+
+  // ---- gates of token n, within each 16-lane group: segmented sums Gs
+  // (restarting after the last token R <= n whose decay is 0) and the scale
+  // sequence c of gdn_step.h (prefix products of alpha, folded when out of
+  // [2^-32, 2^32]; that rare case walks the tokens in order)
+  const bool reset = gt < kReset;
+  float Gs = reset ? 0.f : gt;
+  int R = reset ? n : -1;
+  const float a_t = tv ? __expf(gt) : 1.0f;
+  float c = a_t;
+#pragma unroll
+  for (int off = 1; off < kTok; off <<= 1) {
+    const float ys = __shfl_up(Gs, off, kTok);
+    const int yR = __shfl_up(R, off, kTok);
+    const float yc = __shfl_up(c, off, kTok);
+    if (n >= off) {
+      Gs = R < 0 ? ys + Gs : Gs;
+      R = R > yR ? R : yR;
+      c *= yc;
+    }
+  }
+  float phi = 1.f;
+  {
+    const bool out = !(c >= kScaleLo && c <= kScaleHi);
+    if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
+      float cc = 1.0f;
+      for (int t = 0; t < T; ++t) {
+        float cn, fo = 1.f;
+        if (scale_step(cc, lane_value(a_t, t), cn)) {
+          fo = cn;
+          cn = 1.0f;
+        }
+        if (n == t) {
+          c = cn;
+          phi = fo;
+        }
+        cc = cn;
+      }
+    }
+  }
+  const float A = R >= 0 ? 0.f : __expf(Gs);
+  const float f2 = rk * __builtin_amdgcn_rcpf(c);  // ut = u * f2
+  const float so = scale * rq * A;                 // on (Q H)_n
+  const float xb = bt * A * rk;                    // on (K H)_n
+
+  // ---- L and P entries of row n, columns s = 4 g4 + e
+  float PA[4];
+  {
+    const float bk = bt * rk, sq = scale * rq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 4 * g4 + e;
+      const float rks = bcast(rk, s);
+      const float Gss = bcast(Gs, s);
+      const float dx = __expf(Gs - Gss);
+      const float dec = (s <= n && s >= R) ? dx : 0.f;
+      const float lv = bk * rks * KK[e] * dec;
+      W.Lt[s * kLS + n] = s < n ? lv : 0.f;  // L[n][s], transposed
+      PA[e] = s <= n ? sq * rks * KQ[e] * dec : 0.f;
+    }
+  }
+  wave_lds_sync();
+  // ---- T = (I + L)^-1: lane n < 16 of group 0 solves column n by
+  // right-looking substitution (once t_x is known it updates every later
+  // row), then the columns meet in LDS to be read back as row pieces
+  if (l < kTok) {
+    float acc[kTok];
+#pragma unroll
+    for (int r = 0; r < kTok; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int x = 0; x < kTok; ++x) {
+      const float tx = x == n ? 1.f : (x < n ? 0.f : -acc[x]);
+      W.Ts[x * kLS + n] = tx;
+#pragma unroll
+      for (int r = x + 1; r < kTok; ++r)
+        acc[r] = __builtin_fmaf(W.Lt[x * kLS + r], tx, acc[r]);
+    }
+  }
+  wave_lds_sync();
+  const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
+
+  load_v();
+
+  // ---- K H and Q H: per k-step, the eight rows of each column split into
+  // bf16 hi and lo, two MFMAs each against the exact key / query pieces
+  f32x4 KH[2], QH[2];
+#pragma unroll
+  for (int cs = 0; cs < 2; ++cs) {
+    KH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    QH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    uint32_t h0[4], lo0[4], h1[4], lo1[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      split2(s2[ks][2 * p][0], s2[ks][2 * p + 1][0], h0[p], lo0[p]);
+      split2(s2[ks][2 * p][1], s2[ks][2 * p + 1][1], h1[p], lo1[p]);
+    }
+    const u32x4 H0 = {h0[0], h0[1], h0[2], h0[3]};
+    const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
+    const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
+    const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
+    KH[0] = mma_bf16(Kf[ks], H0, KH[0]);
+    KH[1] = mma_bf16(Kf[ks], H1, KH[1]);
+    QH[0] = mma_bf16(Qf[ks], H0, QH[0]);
+    QH[1] = mma_bf16(Qf[ks], H1, QH[1]);
+    KH[0] = mma_bf16(Kf[ks], L0, KH[0]);
+    KH[1] = mma_bf16(Kf[ks], L1, KH[1]);
+    QH[0] = mma_bf16(Qf[ks], L0, QH[0]);
+    QH[1] = mma_bf16(Qf[ks], L1, QH[1]);
+  }
+
+  // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
+  float bte[4], xbe[4], soe[4], f2e[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int s = 4 * g4 + e;
+    bte[e] = bcast(bt, s);
+    xbe[e] = bcast(xb, s);
+    soe[e] = bcast(so, s);
+    f2e[e] = bcast(f2, s);
+  }
+  f32x4 X[2];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool te = 4 * g4 + e < T;
+    const float x0 = __builtin_fmaf(-xbe[e], KH[0][e], bte[e] * lo_f(vw[e]));
+    const float x1 = __builtin_fmaf(-xbe[e], KH[1][e], bte[e] * hi_f(vw[e]));
+    X[0][e] = te ? x0 : 0.f;
+    X[1][e] = te ? x1 : 0.f;
+  }
+  const float ta[4] = {TA.x, TA.y, TA.z, TA.w};
+  f32x4 U[2], O[2];
+#pragma unroll
+  for (int cs = 0; cs < 2; ++cs) {
+    U[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) U[cs] = mma_f32(ta[e], X[cs][e], U[cs]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[cs][e] = soe[e] * QH[cs][e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
+  }
+  float* __restrict__ o0 = o + (tok0 * d.Hv + h) * (size_t)dv;
+  float* __restrict__ u0 = rec_u + (tok0 * d.Hv + h) * (size_t)dv;
+  float ut[2][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 4 * g4 + e;
+    ut[0][e] = U[0][e] * f2e[e];
+    ut[1][e] = U[1][e] * f2e[e];
+    if (t < T) {
+      const uint32_t off = (uint32_t)(t * vo_step) + c0;
+      *reinterpret_cast<float2*>(o0 + off) = make_float2(O[0][e], O[1][e]);
+      *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
+    }
+  }
+  if (cb == 0 && w == 0 && l < T)
+    rec_scale[gh0 + (size_t)l * d.Hv] = make_float2(phi, c);
+  // ---- debug states: the replay of this window's own records on the
+  // start state (the committed state in the fused call), token by token
+  if constexpr (DBG) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
+      W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
+    }
+    wave_lds_sync();
+#pragma unroll 1
+    for (int t = 0; t < T; ++t) {
+      const float ph = lane_value(phi, t);
+      const float ct = lane_value(c, t);
+      if (ph != 1.f) {
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s2[ks][e][0] = ph * s2[ks][e][0];
+            s2[ks][e][1] = ph * s2[ks][e][1];
+          }
+      }
+      const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
+      float* __restrict__ dp =
+          dbg + (((tok0 + t) * d.Hv + h) * (size_t)kDK) * dv;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(
+            k0 + (uint32_t)(t * kq_step) + 32 * ks + 8 * g4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
+          s2[ks][e][0] = state_update(s2[ks][e][0], ua, kv);
+          s2[ks][e][1] = state_update(s2[ks][e][1], ub, kv);
+          *reinterpret_cast<float2*>(
+              dp + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)) =
+              make_float2(materialise(ct, s2[ks][e][0]),
+                          materialise(ct, s2[ks][e][1]));
+        }
+      }
+    }
+  }
+}
+
+template <bool REPLAY, bool DBG>
+static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
+                           const VerifyArgs& a, const PrevRecords& pr,
+                           hipStream_t st) {
+  const int blocks = w.NL * w.N * w.Hv * (w.dv / kCB);
+  return launch(mverify_kernel<REPLAY, DBG>, dim3(blocks), dim3(kBlock), st,
+                (const uint16_t*)a.q, (const uint16_t*)a.k,
+                (const uint16_t*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
+                a.dbg, w, tl, a.scale, a.l2, pr);
+}
+
+}  // namespace wm
+
+bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a) {
+  auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
+  return in_dtype == GDN_BF16 && d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
+         d.t_max <= wm::kTok && al(a.q, 16) && al(a.k, 16) && al(a.v, 4) &&
+         al(a.S, 8) && al(a.o, 8) && (a.dbg == nullptr || al(a.dbg, 8));
+}
+
+hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
+                          const VerifyArgs& a, const PrevRecords& pr,
+                          bool replay, hipStream_t st) {
+  if (replay)
+    return a.dbg ? wm::launch_t<true, true>(w, tl, a, pr, st)
+                 : wm::launch_t<true, false>(w, tl, a, pr, st);
+  return a.dbg ? wm::launch_t<false, true>(w, tl, a, pr, st)
+               : wm::launch_t<false, false>(w, tl, a, pr, st);
+}
+
+}  // namespace gdn
