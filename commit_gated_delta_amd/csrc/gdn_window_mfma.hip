@@ -69,6 +69,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDK = 128;        // key rows
 constexpr int kKS = kDK / 32;   // k-steps of the bf16 products
@@ -77,6 +78,8 @@ constexpr int kCB = 128;        // value columns per workgroup
 constexpr int kLS = 20;         // padded row of a 16 x 16 LDS matrix
 constexpr int kUS = 33;         // padded row of a wave's ut tile
 constexpr float kReset = -128.f;  // exp(g) rounds to 0 in f32 below this
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, 32-bit data
+constexpr int kNT = 2;                 // nontemporal cache policy
 
 // Records of the previous window, staged for the fused replay.
 struct Stage {
@@ -118,6 +121,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Entry i of a per-lane byte table in the kernel arguments, through a
+// scalar load of the dword that holds it (i is uniform).  A by-value kernel
+// argument lives in the kernel-argument segment (the constant address
+// space), so its address converts back to that space.
+__device__ __forceinline__ int table_byte(const LaneTable& t, int i) {
+  typedef const __attribute__((address_space(4))) uint32_t cword;
+  i = __builtin_amdgcn_readfirstlane(i);
+  const uint32_t w = ((cword*)(const void*)t.v)[i >> 2];
+  return (int)((w >> (8 * (i & 3))) & 0xffu);
+}
+
 __device__ __forceinline__ float bcast(float x, int src) {
   return __shfl(x, src, kWave);
 }
@@ -126,7 +140,7 @@ __device__ __forceinline__ float lane_value(float x, int t) {  // t uniform
 }
 
 template <bool REPLAY, bool DBG>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(REPLAY && !DBG ? 3 : 2)))
 void mverify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ beta,
@@ -145,8 +159,8 @@ void mverify_kernel(
   item /= d.Hv;
   const int lane = item % d.N;
   const int layer = item / d.N;
-  const int T = tl.v[lane];
-  const int m_prev = REPLAY ? prev.m.v[lane] : 0;
+  const int T = table_byte(tl, lane);
+  const int m_prev = REPLAY ? table_byte(prev.m, lane) : 0;
   if (T == 0 && m_prev == 0) return;
 
   const int tid = (int)threadIdx.x;
@@ -165,6 +179,25 @@ void mverify_kernel(
   const uint16_t* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)dv;
   const size_t gh0 = tok0 * d.Hv + h;  // gate index of token 0 (step Hv)
   float* const Sh = S + (ll * d.Hv + h) * (size_t)kDK * dv;
+  // The head's state through a buffer resource: row 32 ks + 8 g4 + e is the
+  // uniform byte offset of row 32 ks + e (an SGPR) plus this lane's offset
+  // (one VGPR for all 32 accesses); accesses past the head's rows would
+  // read 0 and write nothing.
+  const uint32_t soff = (uint32_t)(8 * g4 * dv + c0) * 4u;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      Sh, 0, kDK * dv * (int)sizeof(float), kBufWord3);
+  auto sload = [&](int r) -> f32x2 {
+    return __builtin_bit_cast(
+        f32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, soff, r * dv * 4, kNT));
+  };
+  auto sstore = [&](int r, f32x2 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), srs,
+                                          soff, r * dv * 4, kNT);
+  };
+  auto srow = [&](float* base, int r) -> f32x2* {
+    return reinterpret_cast<f32x2*>(
+        reinterpret_cast<char*>(base + (size_t)r * dv) + soff);
+  };
   WaveLds& W = wl[w];
 
   // ---- small loads: token n's gates and key / query row pieces (the A
@@ -178,9 +211,7 @@ void mverify_kernel(
   float gt, bt;
   u32x4 Kf[kKS], Qf[kKS];
   uint32_t vw[4];
-  auto load_small = [&]() {
-    gt = tv ? g[gh0 + (size_t)tn * d.Hv] : 0.f;
-    bt = tv ? beta[gh0 + (size_t)tn * d.Hv] : 0.f;
+  auto load_kq = [&]() {
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       const uint32_t off = (uint32_t)(tn * kq_step) + 32 * ks + 8 * g4;
@@ -190,6 +221,13 @@ void mverify_kernel(
       Kf[ks] = tv ? kr : z;
       Qf[ks] = tv ? qr : z;
     }
+  };
+  auto load_small = [&]() {
+    const float gl = g[gh0 + (size_t)tn * d.Hv];  // unconditional loads
+    const float bl = beta[gh0 + (size_t)tn * d.Hv];
+    gt = tv ? gl : 0.f;
+    bt = tv ? bl : 0.f;
+    load_kq();
   };
   // the value words are needed only after the state products: issued after
   // the state, they hold no registers through the prologue
@@ -211,8 +249,11 @@ void mverify_kernel(
   for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      s2[ks][e] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(
-          Sh + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)));
+      s2[ks][e] = sload(32 * ks + e);
+  // keep the state requests here, right behind the small loads: the
+  // scheduler would otherwise sink them below the first uses of the small
+  // loads and wait for those first
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- fused commit: the accepted prefix of the previous window, replayed
   // on the held state with exactly the operations of gdn_commit (fold,
@@ -246,9 +287,8 @@ void mverify_kernel(
       }
       if (tid < kTok) stage.sc[tid] = scst;
       __syncthreads();
-      float cf = 1.0f;
-#pragma unroll 1
-      for (int t = 0; t < m_prev; ++t) {
+      // one step: fold (when the record has one), then the rank-1 write
+      auto step = [&](int t, bool may_fold) {
         const f32x2 fc = stage.sc[t];
         const f32x2 uc =
             *reinterpret_cast<const f32x2*>(&stage.u[t][32 * w + 2 * n]);
@@ -260,16 +300,18 @@ void mverify_kernel(
           kc[2 * ks + 1] =
               *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4 + 4]);
         }
-        const float ph = __int_as_float(
-            __builtin_amdgcn_readfirstlane(__float_as_int(fc[0])));
-        if (ph != 1.f) {
+        if (may_fold) {
+          const float ph = __int_as_float(
+              __builtin_amdgcn_readfirstlane(__float_as_int(fc[0])));
+          if (ph != 1.f) {
 #pragma unroll
-          for (int ks = 0; ks < kKS; ++ks)
+            for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              s2[ks][e][0] = ph * s2[ks][e][0];
-              s2[ks][e][1] = ph * s2[ks][e][1];
-            }
+              for (int e = 0; e < 8; ++e) {
+                s2[ks][e][0] = ph * s2[ks][e][0];
+                s2[ks][e][1] = ph * s2[ks][e][1];
+              }
+          }
         }
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks)
@@ -279,17 +321,28 @@ void mverify_kernel(
             s2[ks][e][0] = state_update(s2[ks][e][0], uc[0], kv);
             s2[ks][e][1] = state_update(s2[ks][e][1], uc[1], kv);
           }
-        cf = fc[1];
+      };
+      // folds are rare: a prefix without one runs a branch-free loop
+      const bool any_fold =
+          __builtin_amdgcn_ballot_w64(l < m_prev && stage.sc[l < kTok ? l : 0][0] != 1.f) != 0;
+      if (any_fold) {
+#pragma unroll 1
+        for (int t = 0; t < m_prev; ++t) step(t, true);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+          if (t >= m_prev) break;
+          step(t, false);
+        }
       }
+      const float cf = stage.sc[m_prev - 1][1];
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           s2[ks][e][0] = materialise(cf, s2[ks][e][0]);
           s2[ks][e][1] = materialise(cf, s2[ks][e][1]);
-          __builtin_nontemporal_store(
-              s2[ks][e], reinterpret_cast<f32x2*>(
-                             Sh + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)));
+          sstore(32 * ks + e, s2[ks][e]);
         }
     }
     if (T == 0) return;
@@ -426,6 +479,10 @@ void mverify_kernel(
   const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
 
   load_v();
+  // the key / query pieces again (L1 / L2 hits): the first copies died after
+  // K K^T and the norms, so they held no registers through the solve
+  asm volatile("" ::: "memory");
+  load_kq();
 
   // ---- K H and Q H: per k-step, the eight rows of each column split into
   // bf16 hi and lo, two MFMAs each against the exact key / query pieces
@@ -538,10 +595,8 @@ void mverify_kernel(
           const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
           s2[ks][e][0] = state_update(s2[ks][e][0], ua, kv);
           s2[ks][e][1] = state_update(s2[ks][e][1], ub, kv);
-          *reinterpret_cast<float2*>(
-              dp + (uint32_t)((32 * ks + 8 * g4 + e) * dv + c0)) =
-              make_float2(materialise(ct, s2[ks][e][0]),
-                          materialise(ct, s2[ks][e][1]));
+          *srow(dp, 32 * ks + e) =
+              f32x2{materialise(ct, s2[ks][e][0]), materialise(ct, s2[ks][e][1])};
         }
       }
     }
