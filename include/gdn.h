@@ -130,6 +130,12 @@ size_t gdn_records_bytes(const gdn_dims* dims);
  *   dbg_states  device f32 [n_layers][n_lanes][t_max][h_v][d_k][d_v] or
  *               NULL: when given, every intermediate state S_1..S_T, as the
  *               kernel holds it (for tests; costs 64 KiB per head per token).
+ *               For bf16 inputs with d_k = d_v = 128 and t_max <= 16 the
+ *               window is evaluated as one block (the chunked WY/UT form of
+ *               the delta rule, Yang et al., NeurIPS 2024, Sec. 3) on the
+ *               matrix cores; its intermediate states are then defined as the
+ *               token-by-token replay of its own records, which is what
+ *               dbg_states receives.
  *   scale       multiplies o only (1.0f for o_t = S_t q_t).
  *   flags       GDN_FLAG_L2NORM_QK or 0.
  *   stream      hipStream_t (NULL = the null stream).
@@ -145,7 +151,8 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
  * that the matching gdn_verify read) and store S_m into S in place.  Lanes
  * with m = 0 are neither read nor written.  S_m is bit-for-bit the state that
  * gdn_verify held after its m-th token (and wrote to dbg_states), because
- * both run the same per-step instruction sequence; no steps are folded.
+ * both run the same per-step instruction sequence on the recorded values; no
+ * replayed steps are folded into a block product.
  *   m_lane   host int32[n_lanes], 0..t_lane[lane]
  *   t_lane   host int32[n_lanes], as passed to the matching gdn_verify
  *   records  device, as filled by that gdn_verify
