@@ -755,8 +755,12 @@ extern "C" int gdn_verify_tree(const gdn_dims* dims, const int32_t* t_lane,
   if (!any) return GDN_OK;
   PrevRecords none;
   memset(&none, 0, sizeof(none));
-  hipError_t e = launch_verify<false, true>(win_dims(*dims), tl, in_dtype, a,
-                                            none, (hipStream_t)stream, tab);
+  hipError_t e =
+      mverify_eligible(*dims, in_dtype, a)
+          ? launch_mverify_tree(win_dims(*dims), tl, a, tab,
+                                (hipStream_t)stream)
+          : launch_verify<false, true>(win_dims(*dims), tl, in_dtype, a, none,
+                                       (hipStream_t)stream, tab);
   return hip_status(e, "gdn_verify_tree launch");
 }
 

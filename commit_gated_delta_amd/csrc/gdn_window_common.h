@@ -302,8 +302,12 @@ static int commit_lanes(const char* fn, const gdn_dims& d,
 // and its launch (replay = the fused commit + verify).
 __attribute__((visibility("hidden"))) bool mverify_eligible(
     const gdn_dims& d, int in_dtype, const VerifyArgs& a);
-__attribute__((visibility("hidden"))) hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
-                          const VerifyArgs& a, const PrevRecords& pr,
-                          bool replay, hipStream_t st);
+__attribute__((visibility("hidden"))) hipError_t launch_mverify(
+    const WinDims& w, const LaneTable& tl, const VerifyArgs& a,
+    const PrevRecords& pr, bool replay, hipStream_t st);
+// The matrix-core verify of a draft-tree window (same eligibility).
+__attribute__((visibility("hidden"))) hipError_t launch_mverify_tree(
+    const WinDims& w, const LaneTable& tl, const VerifyArgs& a,
+    const TreeTable& tree, hipStream_t st);
 
 }  // namespace gdn

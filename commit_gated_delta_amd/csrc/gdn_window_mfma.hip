@@ -56,6 +56,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 #include <type_traits>
 
 #include "gdn_step.h"
@@ -138,8 +139,27 @@ __device__ __forceinline__ float bcast(float x, int src) {
 __device__ __forceinline__ float lane_value(float x, int t) {  // t uniform
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
 }
+__device__ __forceinline__ int lane_int(int x, int t) {  // t uniform
+  return __builtin_amdgcn_readlane(x, t);
+}
+// Parent of cell i of a draft-tree table (-1 for a root), read like
+// table_byte.
+__device__ __forceinline__ int tree_parent(const TreeTable& t, int i) {
+  typedef const __attribute__((address_space(4))) uint32_t cword;
+  i = __builtin_amdgcn_readfirstlane(i);
+  const uint32_t w = ((cword*)(const void*)t.v)[i >> 2];
+  const int p = (int)((w >> (8 * (i & 3))) & 0xffu);
+  return p == kNoParent ? -1 : p;
+}
+__device__ __forceinline__ int tree_parent(const NoTable&, int) { return -1; }
 
-template <bool REPLAY, bool DBG>
+// TREE: a draft-tree window (no fused replay).  Node t steps from the state
+// of its parent (S0 for a root); the block form holds with the causal mask
+// replaced by the ancestor relation: L_ts and P_ts are nonzero only for s an
+// ancestor (or, for P, t itself), dec(t, s) is the decay along the path from
+// s to t, and the scale sequence continues the parent's scale.  A parent
+// precedes its children, so L stays strictly lower triangular.
+template <bool REPLAY, bool DBG, bool TREE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(REPLAY && !DBG ? 3 : 2)))
 void mverify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -147,7 +167,9 @@ void mverify_kernel(
     const float* __restrict__ g, float* S, float* __restrict__ o,
     float* __restrict__ rec_k, float* __restrict__ rec_u,
     float2* __restrict__ rec_scale, float* __restrict__ dbg, WinDims d,
-    LaneTable tl, float scale, int l2norm, PrevRecords prev) {
+    LaneTable tl, float scale, int l2norm, PrevRecords prev,
+    std::conditional_t<TREE, TreeTable, NoTable> tree) {
+  static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
   __shared__ WaveLds wl[kWaves];
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
 
@@ -402,24 +424,57 @@ void mverify_kernel(
   // (restarting after the last token R <= n whose decay is 0) and the scale
   // sequence c of gdn_step.h (prefix products of alpha, folded when out of
   // [2^-32, 2^32]; that rare case walks the tokens in order)
-  const bool reset = gt < kReset;
-  float Gs = reset ? 0.f : gt;
-  int R = reset ? n : -1;
   const float a_t = tv ? __expf(gt) : 1.0f;
-  float c = a_t;
-#pragma unroll
-  for (int off = 1; off < kTok; off <<= 1) {
-    const float ys = __shfl_up(Gs, off, kTok);
-    const int yR = __shfl_up(R, off, kTok);
-    const float yc = __shfl_up(c, off, kTok);
-    if (n >= off) {
-      Gs = R < 0 ? ys + Gs : Gs;
-      R = R > yR ? R : yR;
-      c *= yc;
+  float Gs, c, phi = 1.f;
+  int R;
+  uint32_t anc;  // bit s: token s is a strict ancestor of token n
+  if constexpr (TREE) {
+    // node by node in index order (a parent precedes its children); after
+    // the walk lane n holds node n's segment sum, deepest zero-decay node
+    // on its path, scale step and ancestor set
+    Gs = 0.f;
+    c = 1.f;
+    R = -1;
+    anc = 0u;
+    for (int t = 0; t < T; ++t) {
+      const int par = tree_parent(tree, lane * d.T + t);
+      const float gtt = lane_value(gt, t);
+      const float Gp = par < 0 ? 0.f : lane_value(Gs, par);
+      const int Rp = par < 0 ? -1 : lane_int(R, par);
+      const float cp = par < 0 ? 1.0f : lane_value(c, par);
+      const uint32_t ap =
+          par < 0 ? 0u : ((uint32_t)lane_int((int)anc, par) | (1u << par));
+      const bool rs = gtt < kReset;
+      float cn, fo = 1.f;
+      if (scale_step(cp, lane_value(a_t, t), cn)) {
+        fo = cn;
+        cn = 1.0f;
+      }
+      if (n == t) {
+        Gs = rs ? 0.f : Gp + gtt;
+        R = rs ? t : Rp;
+        c = cn;
+        phi = fo;
+        anc = ap;
+      }
     }
-  }
-  float phi = 1.f;
-  {
+  } else {
+    const bool reset = gt < kReset;
+    Gs = reset ? 0.f : gt;
+    R = reset ? n : -1;
+    anc = (1u << n) - 1u;
+    c = a_t;
+#pragma unroll
+    for (int off = 1; off < kTok; off <<= 1) {
+      const float ys = __shfl_up(Gs, off, kTok);
+      const int yR = __shfl_up(R, off, kTok);
+      const float yc = __shfl_up(c, off, kTok);
+      if (n >= off) {
+        Gs = R < 0 ? ys + Gs : Gs;
+        R = R > yR ? R : yR;
+        c *= yc;
+      }
+    }
     const bool out = !(c >= kScaleLo && c <= kScaleHi);
     if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
       float cc = 1.0f;
@@ -451,11 +506,13 @@ void mverify_kernel(
       const int s = 4 * g4 + e;
       const float rks = bcast(rk, s);
       const float Gss = bcast(Gs, s);
+      const bool below = (anc >> s) & 1u;  // s a strict ancestor of n
+      const bool on_path = below || s == n;
       const float dx = __expf(Gs - Gss);
-      const float dec = (s <= n && s >= R) ? dx : 0.f;
+      const float dec = (on_path && s >= R) ? dx : 0.f;
       const float lv = bk * rks * KK[e] * dec;
-      W.Lt[s * kLS + n] = s < n ? lv : 0.f;  // L[n][s], transposed
-      PA[e] = s <= n ? sq * rks * KQ[e] * dec : 0.f;
+      W.Lt[s * kLS + n] = below ? lv : 0.f;  // L[n][s], transposed
+      PA[e] = on_path ? sq * rks * KQ[e] * dec : 0.f;
     }
   }
   wave_lds_sync();
@@ -562,7 +619,8 @@ void mverify_kernel(
   if (cb == 0 && w == 0 && l < T)
     rec_scale[gh0 + (size_t)l * d.Hv] = make_float2(phi, c);
   // ---- debug states: the replay of this window's own records on the
-  // start state (the committed state in the fused call), token by token
+  // start state (the committed state in the fused call), token by token; in
+  // a draft tree, node t's state is the replay of the records on its path
   if constexpr (DBG) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -570,48 +628,75 @@ void mverify_kernel(
       W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
     }
     wave_lds_sync();
-#pragma unroll 1
-    for (int t = 0; t < T; ++t) {
-      const float ph = lane_value(phi, t);
-      const float ct = lane_value(c, t);
+    // record r applied to st: the fold, then the rank-1 write
+    auto apply = [&](f32x2 (&st)[kKS][8], int r) {
+      const float ph = lane_value(phi, r);
       if (ph != 1.f) {
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            s2[ks][e][0] = ph * s2[ks][e][0];
-            s2[ks][e][1] = ph * s2[ks][e][1];
+            st[ks][e][0] = ph * st[ks][e][0];
+            st[ks][e][1] = ph * st[ks][e][1];
           }
       }
-      const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
-      float* __restrict__ dp =
-          dbg + (((tok0 + t) * d.Hv + h) * (size_t)kDK) * dv;
+      const float ua = W.Us[r * kUS + 2 * n], ub = W.Us[r * kUS + 2 * n + 1];
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const u32x4 kw = *reinterpret_cast<const u32x4*>(
-            k0 + (uint32_t)(t * kq_step) + 32 * ks + 8 * g4);
+            k0 + (uint32_t)(r * kq_step) + 32 * ks + 8 * g4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
-          s2[ks][e][0] = state_update(s2[ks][e][0], ua, kv);
-          s2[ks][e][1] = state_update(s2[ks][e][1], ub, kv);
-          *srow(dp, 32 * ks + e) =
-              f32x2{materialise(ct, s2[ks][e][0]), materialise(ct, s2[ks][e][1])};
+          st[ks][e][0] = state_update(st[ks][e][0], ua, kv);
+          st[ks][e][1] = state_update(st[ks][e][1], ub, kv);
         }
+      }
+    };
+    auto emit = [&](const f32x2 (&st)[kKS][8], int t) {
+      const float ct = lane_value(c, t);
+      float* __restrict__ dp =
+          dbg + (((tok0 + t) * d.Hv + h) * (size_t)kDK) * dv;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *srow(dp, 32 * ks + e) =
+              f32x2{materialise(ct, st[ks][e][0]), materialise(ct, st[ks][e][1])};
+    };
+    if constexpr (TREE) {
+#pragma unroll 1
+      for (int t = 0; t < T; ++t) {
+        const uint32_t path = (uint32_t)lane_int((int)anc, t) | (1u << t);
+        f32x2 sd[kKS][8];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sd[ks][e] = s2[ks][e];
+#pragma unroll 1
+        for (int r = 0; r <= t; ++r)
+          if ((path >> r) & 1u) apply(sd, r);
+        emit(sd, t);
+      }
+    } else {
+#pragma unroll 1
+      for (int t = 0; t < T; ++t) {
+        apply(s2, t);
+        emit(s2, t);
       }
     }
   }
 }
 
-template <bool REPLAY, bool DBG>
+template <bool REPLAY, bool DBG, bool TREE, typename Tab>
 static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
                            const VerifyArgs& a, const PrevRecords& pr,
-                           hipStream_t st) {
+                           const Tab& tree, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv * (w.dv / kCB);
-  return launch(mverify_kernel<REPLAY, DBG>, dim3(blocks), dim3(kBlock), st,
-                (const uint16_t*)a.q, (const uint16_t*)a.k,
+  return launch(mverify_kernel<REPLAY, DBG, TREE>, dim3(blocks), dim3(kBlock),
+                st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                 (const uint16_t*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
-                a.dbg, w, tl, a.scale, a.l2, pr);
+                a.dbg, w, tl, a.scale, a.l2, pr, tree);
 }
 
 }  // namespace wm
@@ -626,11 +711,21 @@ bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a) {
 hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
                           const VerifyArgs& a, const PrevRecords& pr,
                           bool replay, hipStream_t st) {
+  const NoTable none{};
   if (replay)
-    return a.dbg ? wm::launch_t<true, true>(w, tl, a, pr, st)
-                 : wm::launch_t<true, false>(w, tl, a, pr, st);
-  return a.dbg ? wm::launch_t<false, true>(w, tl, a, pr, st)
-               : wm::launch_t<false, false>(w, tl, a, pr, st);
+    return a.dbg ? wm::launch_t<true, true, false>(w, tl, a, pr, none, st)
+                 : wm::launch_t<true, false, false>(w, tl, a, pr, none, st);
+  return a.dbg ? wm::launch_t<false, true, false>(w, tl, a, pr, none, st)
+               : wm::launch_t<false, false, false>(w, tl, a, pr, none, st);
+}
+
+hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,
+                               const VerifyArgs& a, const TreeTable& tree,
+                               hipStream_t st) {
+  PrevRecords none;
+  memset(&none, 0, sizeof(none));
+  return a.dbg ? wm::launch_t<false, true, true>(w, tl, a, none, tree, st)
+               : wm::launch_t<false, false, true>(w, tl, a, none, tree, st);
 }
 
 }  // namespace gdn
