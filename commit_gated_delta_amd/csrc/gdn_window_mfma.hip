@@ -92,6 +92,7 @@ struct Stage {
 struct WaveLds {
   __attribute__((aligned(16))) float Lt[kTok * kLS];
   __attribute__((aligned(16))) float Ts[kTok * kLS];
+  __attribute__((aligned(16))) float vec[6][kTok];  // per-token factors
   float Us[kTok * kUS];
 };
 
@@ -133,11 +134,19 @@ __device__ __forceinline__ int table_byte(const LaneTable& t, int i) {
   return (int)((w >> (8 * (i & 3))) & 0xffu);
 }
 
-__device__ __forceinline__ float bcast(float x, int src) {
-  return __shfl(x, src, kWave);
-}
 __device__ __forceinline__ float lane_value(float x, int t) {  // t uniform
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
+}
+// x from the lane CTRL selects within the 16-lane row (a DPP row shift);
+// lanes whose source lies outside the row get `id`.
+template <int CTRL>
+__device__ __forceinline__ float row_shift(float x, float id) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(id), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int row_shift_int(int x, int id) {
+  return __builtin_amdgcn_update_dpp(id, x, CTRL, 0xf, 0xf, false);
 }
 __device__ __forceinline__ int lane_int(int x, int t) {  // t uniform
   return __builtin_amdgcn_readlane(x, t);
@@ -464,17 +473,21 @@ void mverify_kernel(
     R = reset ? n : -1;
     anc = (1u << n) - 1u;
     c = a_t;
-#pragma unroll
-    for (int off = 1; off < kTok; off <<= 1) {
-      const float ys = __shfl_up(Gs, off, kTok);
-      const int yR = __shfl_up(R, off, kTok);
-      const float yc = __shfl_up(c, off, kTok);
-      if (n >= off) {
-        Gs = R < 0 ? ys + Gs : Gs;
-        R = R > yR ? R : yR;
-        c *= yc;
-      }
-    }
+    // inclusive scans over the 16 lanes of each row by DPP row shifts; a
+    // lane without a source reads the identity (0, -1, 1)
+    auto scan_step = [&](auto ctrl) {
+      constexpr int kCtrl = decltype(ctrl)::value;
+      const float ys = row_shift<kCtrl>(Gs, 0.f);
+      const int yR = row_shift_int<kCtrl>(R, -1);
+      const float yc = row_shift<kCtrl>(c, 1.f);
+      Gs = R < 0 ? ys + Gs : Gs;
+      R = R > yR ? R : yR;
+      c *= yc;
+    };
+    scan_step(std::integral_constant<int, 0x111>{});  // row_shr:1
+    scan_step(std::integral_constant<int, 0x112>{});  // row_shr:2
+    scan_step(std::integral_constant<int, 0x114>{});  // row_shr:4
+    scan_step(std::integral_constant<int, 0x118>{});  // row_shr:8
     const bool out = !(c >= kScaleLo && c <= kScaleHi);
     if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
       float cc = 1.0f;
@@ -497,15 +510,30 @@ void mverify_kernel(
   const float so = scale * rq * A;                 // on (Q H)_n
   const float xb = bt * A * rk;                    // on (K H)_n
 
+  // ---- per-token factors through the wave's LDS: lane (g4, n) reads those
+  // of the tokens 4 g4 .. 4 g4 + 3 as one float4 each
+  if (l < kTok) {
+    W.vec[0][n] = rk;
+    W.vec[1][n] = Gs;
+    W.vec[2][n] = bt;
+    W.vec[3][n] = xb;
+    W.vec[4][n] = so;
+    W.vec[5][n] = f2;
+  }
+  wave_lds_sync();
+  auto vec4 = [&](int i) {
+    return *reinterpret_cast<const f32x4*>(&W.vec[i][4 * g4]);
+  };
   // ---- L and P entries of row n, columns s = 4 g4 + e
   float PA[4];
   {
     const float bk = bt * rk, sq = scale * rq;
+    const f32x4 rk4 = vec4(0), gs4 = vec4(1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = 4 * g4 + e;
-      const float rks = bcast(rk, s);
-      const float Gss = bcast(Gs, s);
+      const float rks = rk4[e];
+      const float Gss = gs4[e];
       const bool below = (anc >> s) & 1u;  // s a strict ancestor of n
       const bool on_path = below || s == n;
       const float dx = __expf(Gs - Gss);
@@ -572,15 +600,7 @@ void mverify_kernel(
   }
 
   // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
-  float bte[4], xbe[4], soe[4], f2e[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int s = 4 * g4 + e;
-    bte[e] = bcast(bt, s);
-    xbe[e] = bcast(xb, s);
-    soe[e] = bcast(so, s);
-    f2e[e] = bcast(f2, s);
-  }
+  const f32x4 bte = vec4(2), xbe = vec4(3), soe = vec4(4), f2e = vec4(5);
   f32x4 X[2];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
