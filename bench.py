@@ -176,6 +176,74 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
             "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
 
 
+def bench_t_sweep(ts=(1, 2, 4, 6, 8, 12, 16), reps=20, warmup=3):
+    """Window length sweep of the same batch (8 lanes x 48 layers x 32 value /
+    16 key heads, d = 128) at T in ts, every lane at T: verify alone, and
+    the fused commit + verify with the previous window's m ~ U{0..T}.  Shows
+    where the per-head state read stops dominating; event-timed."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def d16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    S0 = torch.from_numpy(gs.initial_state(
+        gs.WindowShape(NL, N, HV, HK, DK, DV, 1), (9, 0))).to(dev)
+    out = []
+    for tt in ts:
+        shape = gs.WindowShape(NL, N, HV, HK, DK, DV, tt)
+        dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, tt)
+        t_lane = np.full(N, tt, dtype=np.int32)
+        pool = []
+        for p in range(4):
+            w = gs.window_inputs(shape, (9, tt, p))
+            pool.append((d16(w.q), d16(w.k), d16(w.v),
+                         torch.from_numpy(w.beta).to(dev),
+                         torch.from_numpy(w.g).to(dev)))
+        S = S0.clone()
+        o = torch.empty((NL, N, tt, HV, DV), device=dev)
+        nrec = gdn.records_bytes(dims)
+        recs = [torch.empty(nrec, dtype=torch.uint8, device=dev)
+                for _ in range(2)]
+        ms_all = [gs.accepted_uniform(t_lane, (9, tt, 100 + r))
+                  for r in range(warmup + reps + 1)]
+
+        def timed(fn):
+            for r in range(warmup):
+                fn(r)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True),
+                   torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for r, (a, b) in enumerate(ev):
+                a.record(stream)
+                fn(warmup + r)
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+        ms_v = timed(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o,
+                                          recs[r % 2], stream=stream))
+        ms_f = timed(lambda r: gdn.commit_verify(
+            dims, ms_all[r], t_lane, recs[(r + 1) % 2], t_lane, *pool[r % 4],
+            S, o, recs[r % 2], stream=stream))
+        bv = alg_bytes_verify(t_lane)
+        bf = float(np.mean([alg_bytes_fused(t_lane, ms_all[warmup + r])
+                            for r in range(reps)]))
+        upd = int(t_lane.sum()) * NL * HV
+        out.append({"t": tt, "verify_ms": ms_v, "fused_ms": ms_f,
+                    "verify_updates_per_s": upd / (ms_v * 1e-3),
+                    "fused_updates_per_s": upd / (ms_f * 1e-3),
+                    "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "fused_hbm_frac": bf / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del S, o, recs, pool
+    return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, every lane "
+                        "at T; fused with the previous window's m ~ U{0..T}",
+            "points": out}
+
+
 def bench_tree(reps=20, warmup=3):
     """Draft-tree verify of the same batch (8 lanes x 48 layers x 32 value /
     16 key heads, d = 128), 16-node trees per lane in depth-first order
@@ -356,6 +424,8 @@ def main():
                          "one is the headline when timed)")
     ap.add_argument("--no-snapshot", action="store_true")
     ap.add_argument("--no-tree", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the window-length sweep")
     ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
@@ -535,6 +605,8 @@ def main():
         out["prefill"] = bench_prefill()
     if not args.no_snapshot:
         out["state_snapshot"] = bench_snapshot()
+    if not args.no_sweep:
+        out["t_sweep"] = bench_t_sweep()
     if not args.no_tree:
         out["draft_tree"] = bench_tree()
     if not args.no_kda:
