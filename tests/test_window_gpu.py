@@ -58,6 +58,11 @@ SMALL = [
     ("d32_dv200_f32", 1, 1, 3, 3, 32, 200, 7, False, False, True, 1.0),
     ("d16_noscale_nonorm", 2, 2, 2, 2, 16, 16, 4, False, False, False, 0.5),
     ("d128_group4", 1, 2, 8, 2, 128, 64, 3, True, False, True, 1.0),
+    # matrix-core verify (bf16, d_k = d_v = 128, t_max <= 16): unnormalised
+    # keys with an output scale, one key head per value head, T = 1 windows
+    ("d128_noscale_nonorm", 1, 2, 4, 2, 128, 128, 8, True, True, False, 0.5),
+    ("d128_group1", 1, 2, 2, 2, 128, 128, 5, True, True, True, 1.0),
+    ("d128_t1", 2, 3, 2, 1, 128, 128, 1, True, False, True, 1.0),
 ]
 
 
@@ -69,8 +74,12 @@ def test_window_parity_and_bitexact_replay(case):
     key = (100, zlib.crc32(name.encode()) % 1000)
     w = gs.window_inputs(shape, key, bf16=bf16, ragged=ragged)
     if not l2norm:   # unnormalised keys must keep the rule stable
-        w.k = (w.k.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
-        w.q = (w.q.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
+        if bf16:     # scale the values, stay bf16 (round to nearest even)
+            w.k = gs.f32_to_bf16_bits(gs.bf16_bits_to_f32(w.k) / np.sqrt(dk))
+            w.q = gs.f32_to_bf16_bits(gs.bf16_bits_to_f32(w.q) / np.sqrt(dk))
+        else:
+            w.k = (w.k.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
+            w.q = (w.q.astype(np.float32) / np.sqrt(dk)).astype(np.float32)
     S0 = gs.initial_state(shape, key)
     dims = gdn.Dims.of(NL, N, Hv, Hk, dk, dv, T)
     S_dev = to_dev(S0, torch)
