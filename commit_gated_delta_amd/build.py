@@ -11,7 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(LIB_DIR, "libgdn.so")
-SOURCES = ["gdn_window.hip", "gdn_window_mfma.hip", "gdn_kda.hip", "gdn_prefill.hip", "gdn_state.hip"]
+SOURCES = ["gdn_window.hip", "gdn_window_mfma.hip", "gdn_kda.hip",
+           "gdn_kda_mfma.hip", "gdn_prefill.hip", "gdn_state.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

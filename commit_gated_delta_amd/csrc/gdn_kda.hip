@@ -332,7 +332,10 @@ extern "C" int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
   hipStream_t st = (hipStream_t)stream;
   const int l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
   hipError_t e;
-  if (in_dtype == GDN_BF16)
+  if (mkda_eligible(d, in_dtype, q, k, v, g, S, o, dbg_states))
+    e = launch_mkda(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states,
+                    scale, l2, st);
+  else if (in_dtype == GDN_BF16)
     e = dbg_states
             ? launch_kda_verify<128, true, uint16_t>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states, scale, l2, st)
             : launch_kda_verify<128, false, uint16_t>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, nullptr, scale, l2, st);

@@ -47,6 +47,9 @@ CASES = [
     ("f32_dv200", 1, 2, 3, 3, 200, 7, False, None),
     ("bf16_channel_forgetting", 1, 2, 4, 2, 64, 12, True, "zero"),
     ("bf16_strong_decay", 1, 2, 4, 2, 128, 16, True, "strong"),
+    # the matrix-core KDA verify (bf16, d_v = 128, t_max <= 16) with zero
+    # decays on some channels
+    ("bf16_channel_forgetting_d128", 1, 2, 4, 2, 128, 12, True, "zero"),
 ]
 
 
