@@ -70,7 +70,7 @@ def alg_bytes_fused(t_lane, m_prev):
 
 
 WINDOW_SOURCES = ("gdn_window.hip", "gdn_window_mfma.hip",
-                  "gdn_window_common.h", "gdn_step.h")
+                  "gdn_window_common.h", "gdn_mfma_util.h", "gdn_step.h")
 
 
 def kernel_source_hash(files=WINDOW_SOURCES):
