@@ -172,9 +172,14 @@ int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
  * ReplaySSM requirement, per node).
  *   parent   host int32 [n_lanes][t_max]: parent[n][t] in -1..t-1 for
  *            t < t_lane[n] (-1: the node steps from S0); nodes are ordered so
- *            that a parent precedes its children.  Depth-first order is
- *            cheapest: verify rebuilds the parent's state (S0 plus the
- *            path's recorded steps) whenever parent[t] != t - 1.
+ *            that a parent precedes its children.  For bf16 inputs with
+ *            d_k = d_v = 128 and t_max <= 16 the tree is evaluated as one
+ *            block product (the causal mask of the chunked form replaced by
+ *            the ancestor relation) and any order costs the same; the debug
+ *            state of a node is then the replay of the records on its root
+ *            path.  Otherwise depth-first order is cheapest: verify rebuilds
+ *            the parent's state (S0 plus the path's recorded steps) whenever
+ *            parent[t] != t - 1.
  *   path     host int32 [n_lanes][t_max]: the first m_lane[n] entries are the
  *            accepted nodes, root first, each the parent of the next.
  *   other arguments as for gdn_verify / gdn_commit.
@@ -284,7 +289,9 @@ int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
  *            (f32 [h_k][d_k]), u_t / sqrt(|k_t|^2 + 1e-6) (f32 [h_v][d_v])
  *            and alpha_t (f32 [h_v][d_k])
  * Supported: d_k == 128 (GDN_EUNSUPPORTED otherwise; gdn_kda_records_bytes
- * returns 0).
+ * returns 0).  For bf16 inputs with d_v = 128 and t_max <= 16 the window is
+ * evaluated as one block product with channel-weighted decays; dbg_states
+ * then receives the replay of its records (as for gdn_verify).
  */
 size_t gdn_kda_records_bytes(const gdn_dims* dims);
 int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
