@@ -46,6 +46,7 @@ CASES = [
     ("d64_col_tail", 1, 3, 2, 1, 64, 96, 5, True, 5, False),
     ("d32_f32", 1, 2, 3, 3, 32, 200, 7, False, 4, True),
     ("d16_f32", 2, 2, 2, 2, 16, 16, 4, False, 5, False),
+    ("d128_dv256", 1, 3, 2, 1, 128, 256, 8, True, 4, True),
 ]
 
 

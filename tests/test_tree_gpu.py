@@ -91,6 +91,7 @@ CASES = [
     ("bf16_d64_tail", 1, 3, 2, 1, 64, 96, 12, True),
     ("f32_d32", 1, 2, 3, 3, 32, 64, 9, False),
     ("f32_d16", 2, 2, 2, 2, 16, 16, 7, False),
+    ("bf16_d128_dv256", 1, 2, 2, 1, 128, 256, 10, True),
 ]
 
 

@@ -63,6 +63,7 @@ SMALL = [
     ("d128_noscale_nonorm", 1, 2, 4, 2, 128, 128, 8, True, True, False, 0.5),
     ("d128_group1", 1, 2, 2, 2, 128, 128, 5, True, True, True, 1.0),
     ("d128_t1", 2, 3, 2, 1, 128, 128, 1, True, False, True, 1.0),
+    ("d128_dv256", 1, 2, 2, 1, 128, 256, 9, True, True, True, 1.0),
 ]
 
 
