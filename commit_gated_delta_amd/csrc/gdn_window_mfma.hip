@@ -1,7 +1,7 @@
-// gdn_window_mfma.hip -- speculative-window verify and the fused commit +
-// verify on the gfx950 matrix cores, for bf16 inputs, d_k = 128, d_v a
-// multiple of 128 and windows of at most 16 tokens (the shapes of the
-// speculative-decoding section of the NInfer technical review,
+// gdn_window_mfma.hip -- speculative-window verify, draft-tree verify and
+// the fused commit + verify on the gfx950 matrix cores, for bf16 inputs,
+// d_k = 128, d_v a multiple of 128 and windows of at most 16 tokens (the
+// shapes of the speculative-decoding section of the NInfer technical review,
 // blog.123qwe.co.kr post 4624).  Other shapes take gdn_window.hip.
 //
 // The window is one chunk of the block (WY/UT) form of the rule: Yang et
@@ -49,10 +49,10 @@
 // 4 g4 + e).  The small loads (rows, gates) are issued before the 64 KB of
 // state, so that everything but the state products overlaps its latency.
 //
-// MFMA layouts (wave64):
-//   16x16x32 bf16: lane l holds A[l%16][8(l/16) + e], B[8(l/16) + e][l%16]
-//   16x16x4 f32:   lane l holds A[l%16][l/16], B[l/16][l%16]
-//   both:          D[4(l/16) + e][l%16], e = 0..3.
+// The fused call first replays the previous window's accepted prefix on the
+// state it loads, with the commit's operations, and stores it; a draft tree
+// replaces the causal mask by the ancestor relation (see mverify_kernel).
+// MFMA layouts: gdn_mfma_util.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
