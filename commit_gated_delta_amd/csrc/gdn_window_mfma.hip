@@ -81,6 +81,11 @@ struct Stage {
   f32x2 sc[kTok];      // (phi, c)
 };
 // A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
+// The window's key / query A fragments (the same in the four waves): wave 0
+// writes them in its prologue, every wave reads them for the state products.
+struct KQLds {
+  u32x4 f[2][4][64];  // [key, query][k-step][lane]
+};
 struct WaveLds {
   __attribute__((aligned(16))) float Lt[kTok * kLS];
   __attribute__((aligned(16))) float Ts[kTok * kLS];
@@ -95,7 +100,7 @@ struct WaveLds {
 // s to t, and the scale sequence continues the parent's scale.  A parent
 // precedes its children, so L stays strictly lower triangular.
 template <bool REPLAY, bool DBG, bool TREE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(REPLAY && !DBG ? 3 : 2)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG ? 2 : 3)))
 void mverify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ beta,
@@ -106,6 +111,7 @@ void mverify_kernel(
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
   __shared__ WaveLds wl[kWaves];
+  __shared__ KQLds kqs;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
 
   const int nc = d.dv / kCB;
@@ -345,6 +351,13 @@ void mverify_kernel(
     }
   }
 
+  if (w == 0) {  // the A fragments of the state products, for every wave
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      kqs.f[0][ks][l] = Kf[ks];
+      kqs.f[1][ks][l] = Qf[ks];
+    }
+  }
   // ---- K K^T and K Q^T: lane (g4, n), entry e = (k_{4g4+e} . k_n) and
   // (k_{4g4+e} . q_n) -- row n, column s = 4 g4 + e of the A layout of the
   // f32 products below
@@ -490,10 +503,10 @@ void mverify_kernel(
   const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
 
   load_v();
-  // the key / query pieces again (L1 / L2 hits): the first copies died after
-  // K K^T and the norms, so they held no registers through the solve
-  asm volatile("" ::: "memory");
-  load_kq();
+  // the key / query fragments come back from LDS (wave 0 wrote them): the
+  // first copies died after K K^T and the norms, so they held no registers
+  // through the solve, and no global round trip follows the state's arrival
+  __syncthreads();
 
   // ---- K H and Q H: per k-step, the eight rows of each column split into
   // bf16 hi and lo, two MFMAs each against the exact key / query pieces
@@ -515,14 +528,15 @@ void mverify_kernel(
     const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
     const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
     const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
-    KH[0] = mma_bf16(Kf[ks], H0, KH[0]);
-    KH[1] = mma_bf16(Kf[ks], H1, KH[1]);
-    QH[0] = mma_bf16(Qf[ks], H0, QH[0]);
-    QH[1] = mma_bf16(Qf[ks], H1, QH[1]);
-    KH[0] = mma_bf16(Kf[ks], L0, KH[0]);
-    KH[1] = mma_bf16(Kf[ks], L1, KH[1]);
-    QH[0] = mma_bf16(Qf[ks], L0, QH[0]);
-    QH[1] = mma_bf16(Qf[ks], L1, QH[1]);
+    const u32x4 kf = kqs.f[0][ks][l], qf = kqs.f[1][ks][l];
+    KH[0] = mma_bf16(kf, H0, KH[0]);
+    KH[1] = mma_bf16(kf, H1, KH[1]);
+    QH[0] = mma_bf16(qf, H0, QH[0]);
+    QH[1] = mma_bf16(qf, H1, QH[1]);
+    KH[0] = mma_bf16(kf, L0, KH[0]);
+    KH[1] = mma_bf16(kf, L1, KH[1]);
+    QH[0] = mma_bf16(qf, L0, QH[0]);
+    QH[1] = mma_bf16(qf, L1, QH[1]);
   }
 
   // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
