@@ -120,9 +120,9 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   KdaWave& W = wv[w];
 
   // ---- window rows first (one 16-byte piece of k and q, two float4 of the
-  // gates per thread), then the state, so that everything before the state
-  // products overlaps its latency.  Tokens at or past T read token 0 and
-  // become k = q = 0, alpha = 1, beta = 0.
+  // gates per thread, the value words), then the state, so that everything
+  // before the state products overlaps its latency.  Tokens at or past T
+  // read token 0 and become k = q = 0, alpha = 1, beta = 0.
   const int rt = tid >> 4, rp = tid & 15;  // row token, 8-entry piece
   const bool rv = rt < T;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -141,6 +141,14 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         g0 + (uint32_t)((t < T ? t : 0) * g_step) + 4 * (e & 31));
   }
   const float bl = beta[(tok0 + (tid < T ? tid : 0)) * d.Hv + h];
+  uint32_t vw[4];  // values of the tokens 4 g4 + e at this lane's columns
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 4 * g4 + e;
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(
+        v0 + (uint32_t)((t < T ? t : 0) * vo_step) + c0);
+    vw[e] = t < T ? x : 0u;
+  }
 
   const uint32_t soff = (uint32_t)(8 * g4 * kD + c0) * 4u;
   const auto srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -277,14 +285,6 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   wave_lds_sync();
   const f32x4 TA = *reinterpret_cast<const f32x4*>(&W.Ts[n * kLS + 4 * g4]);
   const f32x4 PA = *reinterpret_cast<const f32x4*>(&sh.P[n * kLS + 4 * g4]);
-  uint32_t vw[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g4 + e;
-    const uint32_t x = *reinterpret_cast<const uint32_t*>(
-        v0 + (uint32_t)((t < T ? t : 0) * vo_step) + c0);
-    vw[e] = t < T ? x : 0u;
-  }
 
   // ---- (k . C) H and (q . C) H: per k-step, the decayed rows of token n
   // (entries 32 ks + 8 g4 .. + 7) and the state split into bf16 hi + lo

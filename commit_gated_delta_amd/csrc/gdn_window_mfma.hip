@@ -164,8 +164,8 @@ void mverify_kernel(
   WaveLds& W = wl[w];
 
   // ---- small loads: token n's gates and key / query row pieces (the A
-  // operands); below, the values of the tokens 4 g4 + e at this lane's
-  // columns.  Tokens at or past T read token 0 and are replaced by zeros.  A plain
+  // operands), and the values of the tokens 4 g4 + e at this lane's columns.
+  // Tokens at or past T read token 0 and are replaced by zeros.  A plain
   // verify issues them before the state, so that everything but the state
   // products overlaps its latency; the fused call after its replay, which
   // keeps them out of the registers the replay needs.
@@ -192,8 +192,9 @@ void mverify_kernel(
     bt = tv ? bl : 0.f;
     load_kq();
   };
-  // the value words are needed only after the state products: issued after
-  // the state, they hold no registers through the prologue
+  // the value words of the tokens 4 g4 + e at this lane's columns, issued
+  // with the small loads so that their latency is over when the state
+  // products end
   auto load_v = [&]() {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -204,7 +205,10 @@ void mverify_kernel(
       vw[e] = t < T ? x : 0u;
     }
   };
-  if constexpr (!REPLAY) load_small();
+  if constexpr (!REPLAY) {
+    load_small();
+    load_v();
+  }
 
   // ---- the state: rows 32 ks + 8 g4 + e, columns c0 and c0 + 1
   f32x2 s2[kKS][8];
@@ -310,6 +314,7 @@ void mverify_kernel(
     }
     if (T == 0) return;
     load_small();
+    load_v();
   }
 
   // ---- inverse norms of token n (sums over the lane's row pieces, then
@@ -502,7 +507,6 @@ void mverify_kernel(
   wave_lds_sync();
   const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
 
-  load_v();
   // the key / query fragments come back from LDS (wave 0 wrote them): the
   // first copies died after K K^T and the norms, so they held no registers
   // through the solve, and no global round trip follows the state's arrival
