@@ -80,12 +80,15 @@ struct Stage {
   float u[kTok][kCB];  // ut of this workgroup's columns
   f32x2 sc[kTok];      // (phi, c)
 };
-// A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
-// The window's key / query A fragments (the same in the four waves): wave 0
-// writes them in its prologue, every wave reads them for the state products.
-struct KQLds {
-  u32x4 f[2][4][64];  // [key, query][k-step][lane]
+// The window's raw key / query rows and gates, staged once per workgroup
+// (every wave reads its A fragments and per-token gates from here).
+struct RowLds {
+  __attribute__((aligned(16))) uint16_t k[kTok][kDK];
+  __attribute__((aligned(16))) uint16_t q[kTok][kDK];
+  __attribute__((aligned(16))) uint16_t v[kTok][kCB];  // this block's columns
+  float g[kTok], b[kTok];
 };
+// A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
 struct WaveLds {
   __attribute__((aligned(16))) float Lt[kTok * kLS];
   __attribute__((aligned(16))) float Ts[kTok * kLS];
@@ -111,7 +114,7 @@ void mverify_kernel(
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
   __shared__ WaveLds wl[kWaves];
-  __shared__ KQLds kqs;
+  __shared__ RowLds rows;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
 
   const int nc = d.dv / kCB;
@@ -163,52 +166,53 @@ void mverify_kernel(
   };
   WaveLds& W = wl[w];
 
-  // ---- small loads: token n's gates and key / query row pieces (the A
-  // operands), and the values of the tokens 4 g4 + e at this lane's columns.
-  // Tokens at or past T read token 0 and are replaced by zeros.  A plain
-  // verify issues them before the state, so that everything but the state
-  // products overlaps its latency; the fused call after its replay, which
-  // keeps them out of the registers the replay needs.
+  // ---- the window's rows, staged cooperatively: thread (rt, rp) loads one
+  // 16-byte piece of key row rt, of query row rt and of value row rt (this
+  // block's columns), threads 0..15 the gates of token tid.  All of it is
+  // requested before the state, so that everything but the state products
+  // overlaps the state's latency.  Tokens at or past T read token 0 and are
+  // replaced by zeros.
   const bool tv = n < T;
-  const int tn = tv ? n : 0;
-  float gt, bt;
-  u32x4 Kf[kKS], Qf[kKS];
-  uint32_t vw[4];
-  auto load_kq = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const uint32_t off = (uint32_t)(tn * kq_step) + 32 * ks + 8 * g4;
-      const u32x4 kr = *reinterpret_cast<const u32x4*>(k0 + off);
-      const u32x4 qr = *reinterpret_cast<const u32x4*>(q0 + off);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      Kf[ks] = tv ? kr : z;
-      Qf[ks] = tv ? qr : z;
+  const int rt = tid >> 4, rp = tid & 15;
+  const bool rv = rt < T;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  u32x4 kr = *reinterpret_cast<const u32x4*>(
+      k0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
+  u32x4 qr = *reinterpret_cast<const u32x4*>(
+      q0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
+  kr = rv ? kr : z4;
+  qr = rv ? qr : z4;
+  const int tg = tid < T ? tid : 0;
+  const float gl = g[gh0 + (size_t)tg * d.Hv];
+  const float bl = beta[gh0 + (size_t)tg * d.Hv];
+  u32x4 vr = *reinterpret_cast<const u32x4*>(
+      v0 + (uint32_t)((rv ? rt : 0) * vo_step) + kCB * cb + 8 * rp);
+  vr = rv ? vr : z4;
+  auto stage_rows = [&]() {
+    *reinterpret_cast<u32x4*>(&rows.k[rt][8 * rp]) = kr;
+    *reinterpret_cast<u32x4*>(&rows.q[rt][8 * rp]) = qr;
+    *reinterpret_cast<u32x4*>(&rows.v[rt][8 * rp]) = vr;
+    if (tid < kTok) {
+      rows.g[tid] = tid < T ? gl : 0.f;
+      rows.b[tid] = tid < T ? bl : 0.f;
+    }
+    // the key record rows (raw rows as f32): thread (rt, rp) writes its
+    // piece; done here so that the pieces are dead past the staging
+    if (cb == 0 && h % d.group == 0 && rv) {
+      float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kDK +
+                                (uint32_t)(rt * kq_step) + 8 * rp;
+      reinterpret_cast<float4*>(dst)[0] =
+          make_float4(lo_f(kr[0]), hi_f(kr[0]), lo_f(kr[1]), hi_f(kr[1]));
+      reinterpret_cast<float4*>(dst)[1] =
+          make_float4(lo_f(kr[2]), hi_f(kr[2]), lo_f(kr[3]), hi_f(kr[3]));
     }
   };
-  auto load_small = [&]() {
-    const float gl = g[gh0 + (size_t)tn * d.Hv];  // unconditional loads
-    const float bl = beta[gh0 + (size_t)tn * d.Hv];
-    gt = tv ? gl : 0.f;
-    bt = tv ? bl : 0.f;
-    load_kq();
+  auto frag_k = [&](int ks) {
+    return *reinterpret_cast<const u32x4*>(&rows.k[n][32 * ks + 8 * g4]);
   };
-  // the value words of the tokens 4 g4 + e at this lane's columns, issued
-  // with the small loads so that their latency is over when the state
-  // products end
-  auto load_v = [&]() {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 4 * g4 + e;
-      const int tc = t < T ? t : 0;
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(
-          v0 + (uint32_t)(tc * vo_step) + c0);
-      vw[e] = t < T ? x : 0u;
-    }
+  auto frag_q = [&](int ks) {
+    return *reinterpret_cast<const u32x4*>(&rows.q[n][32 * ks + 8 * g4]);
   };
-  if constexpr (!REPLAY) {
-    load_small();
-    load_v();
-  }
 
   // ---- the state: rows 32 ks + 8 g4 + e, columns c0 and c0 + 1
   f32x2 s2[kKS][8];
@@ -221,6 +225,8 @@ void mverify_kernel(
   // scheduler would otherwise sink them below the first uses of the small
   // loads and wait for those first
   __builtin_amdgcn_sched_barrier(0);
+  stage_rows();
+  __syncthreads();
 
   // ---- fused commit: the accepted prefix of the previous window, replayed
   // on the held state with exactly the operations of gdn_commit (fold,
@@ -313,8 +319,13 @@ void mverify_kernel(
         }
     }
     if (T == 0) return;
-    load_small();
-    load_v();
+  }
+  const float gt = rows.g[n], bt = rows.b[n];
+  u32x4 Kf[kKS], Qf[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    Kf[ks] = frag_k(ks);
+    Qf[ks] = frag_q(ks);
   }
 
   // ---- inverse norms of token n (sums over the lane's row pieces, then
@@ -338,31 +349,7 @@ void mverify_kernel(
   const float rk = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
   const float rq = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
 
-  // the key record rows (raw rows as f32), written while the widened
-  // values are at hand
-  if (cb == 0 && h % d.group == 0 && tv) {
-    // raw key rows as f32: wave w writes the k-step w piece of row n
-    float* __restrict__ dst =
-        rec_k + (tok0 * d.Hk + kh) * kDK + (uint32_t)(n * kq_step) + 32 * w + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      if (ks == w) {
-        const u32x4 kw = Kf[ks];
-        reinterpret_cast<float4*>(dst)[0] =
-            make_float4(lo_f(kw[0]), hi_f(kw[0]), lo_f(kw[1]), hi_f(kw[1]));
-        reinterpret_cast<float4*>(dst)[1] =
-            make_float4(lo_f(kw[2]), hi_f(kw[2]), lo_f(kw[3]), hi_f(kw[3]));
-      }
-    }
-  }
 
-  if (w == 0) {  // the A fragments of the state products, for every wave
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      kqs.f[0][ks][l] = Kf[ks];
-      kqs.f[1][ks][l] = Qf[ks];
-    }
-  }
   // ---- K K^T and K Q^T: lane (g4, n), entry e = (k_{4g4+e} . k_n) and
   // (k_{4g4+e} . q_n) -- row n, column s = 4 g4 + e of the A layout of the
   // f32 products below
@@ -507,10 +494,9 @@ void mverify_kernel(
   wave_lds_sync();
   const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
 
-  // the key / query fragments come back from LDS (wave 0 wrote them): the
+  // the key / query fragments are read again from the staged rows: the
   // first copies died after K K^T and the norms, so they held no registers
   // through the solve, and no global round trip follows the state's arrival
-  __syncthreads();
 
   // ---- K H and Q H: per k-step, the eight rows of each column split into
   // bf16 hi and lo, two MFMAs each against the exact key / query pieces
@@ -532,7 +518,7 @@ void mverify_kernel(
     const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
     const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
     const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
-    const u32x4 kf = kqs.f[0][ks][l], qf = kqs.f[1][ks][l];
+    const u32x4 kf = frag_k(ks), qf = frag_q(ks);
     KH[0] = mma_bf16(kf, H0, KH[0]);
     KH[1] = mma_bf16(kf, H1, KH[1]);
     QH[0] = mma_bf16(qf, H0, QH[0]);
@@ -545,6 +531,11 @@ void mverify_kernel(
 
   // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
   const f32x4 bte = vec4(2), xbe = vec4(3), soe = vec4(4), f2e = vec4(5);
+  uint32_t vw[4];  // values of the tokens 4 g4 + e at columns c0, c0 + 1
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    vw[e] = *reinterpret_cast<const uint32_t*>(
+        &rows.v[4 * g4 + e][32 * w + 2 * n]);
   f32x4 X[2];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
