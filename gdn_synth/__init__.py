@@ -100,7 +100,7 @@ def window_inputs(shape: WindowShape, key: tuple, bf16: bool = True,
                   t_lane=None, ragged: bool = False, g_mean: float = 0.0
                   ) -> WindowInputs:
     """Draw one verify window for every (layer, lane).  ``key`` is a tuple of
-    ints naming the case (config id, round, ...)."""
+    ints naming the case (case key, round, ...)."""
     s = shape
     r = rng(_STREAM_WINDOW, *key)
     qk_shape = (s.n_layers, s.n_lanes, s.t_max, s.h_k, s.d_k)
@@ -187,17 +187,13 @@ def prefill_state(h_v: int, d_k: int, d_v: int, key: tuple, sigma: float = 0.1):
 
 
 # ------------------------------------------------------------ named cases
-def config_shape(cfg: int) -> WindowShape:
-    """Window shapes of the synthetic cases (prefill case 4 excluded)."""
-    if cfg == 0:
-        return WindowShape(1, 1, 2, 2, 16, 16, 4)
-    if cfg == 1:
-        return WindowShape(48, 1, 32, 16, 128, 128, 16)
-    if cfg == 2:
-        return WindowShape(48, 8, 32, 16, 128, 128, 16)
-    if cfg == 3:
-        return WindowShape(48, 12, 32, 16, 128, 128, 6)
-    raise ValueError(cfg)
+# Window shapes of the synthetic workloads, with the first seed-key entry
+# each case uses (a stream identifier only).
+TINY = WindowShape(1, 1, 2, 2, 16, 16, 4)          # 1 lane, 1 layer, d = 16, T = 4
+ONE_LANE = WindowShape(48, 1, 32, 16, 128, 128, 16)       # 1 lane x 48 layers
+EIGHT_LANES = WindowShape(48, 8, 32, 16, 128, 128, 16)    # 8 lanes x 48 layers
+TWELVE_LANES_T6 = WindowShape(48, 12, 32, 16, 128, 128, 6)  # 12 lanes, T = 6
+KEY_TINY, KEY_ONE_LANE, KEY_EIGHT_LANES, KEY_TWELVE_LANES = 0, 1, 2, 3
 
 
 # ------------------------------------------------------------- draft trees

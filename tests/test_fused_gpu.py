@@ -116,13 +116,13 @@ def test_fused_equals_commit_then_verify(case):
     assert s_rel_err(S_b.cpu().numpy(), S_or) <= TOL
 
 
-def test_fused_config1_shape_chain():
+def test_fused_one_lane_48_layers_chain():
     """48 layers x 1 lane x 32/16 heads, d = 128, T = 16, m ~ U{0..16}:
     30 fused rounds; the oracle follows layers 0 and 47 and the two-call
     path runs beside it (bitwise)."""
-    shape = gs.config_shape(1)
+    shape = gs.ONE_LANE
     dims = gdn.Dims.of(*shape.__dict__.values())
-    S0 = gs.initial_state(shape, (1, 0))
+    S0 = gs.initial_state(shape, (gs.KEY_ONE_LANE, 0))
     S_a, S_b = to_dev(S0, torch), to_dev(S0, torch)
     sl = [0, 47]
     S_or = S0[sl].astype(np.float64)
@@ -135,8 +135,8 @@ def test_fused_config1_shape_chain():
     t = np.full(1, 16, np.int32)
     m_prev = np.zeros(1, np.int32)
     for r in range(30):
-        w = gs.window_inputs(shape, (1, 3000 + r))
-        m = gs.accepted_uniform(t, (1, r))
+        w = gs.window_inputs(shape, (gs.KEY_ONE_LANE, 3000 + r))
+        m = gs.accepted_uniform(t, (gs.KEY_ONE_LANE, r))
         q, k, v, beta, g = window_to_dev(w, torch)
         gdn.commit(dims, m_prev, t, rec_a, S_a)
         gdn.verify(dims, t, q, k, v, beta, g, S_a, o_a, rec_a)

@@ -96,7 +96,7 @@ def test_paused_request_resumes_bit_for_bit_in_another_lane():
 def test_full_batch_snapshot_round_trip():
     """8 lanes x 48 layers x 32 heads x 128 x 128 (768 MiB): snapshot of all
     lanes in reverse order to pinned host memory, restore, identical."""
-    shape = gs.config_shape(2)
+    shape = gs.EIGHT_LANES
     dims = gdn.Dims.of(*shape.__dict__.values())
     say("full batch: state")
     S = torch.randn((48, 8, 32, 128, 128), device="cuda")

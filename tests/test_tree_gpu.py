@@ -150,7 +150,7 @@ def test_tree_full_batch_sampled_layer():
     """48 layers x 8 lanes x 32/16 heads, d = 128, 16-node DFS trees: the
     oracle follows layer 0 (outputs and an accepted-path commit per lane),
     and the 48-layer commit of layer 0 matches a one-layer debug run bitwise."""
-    shape = gs.config_shape(2)
+    shape = gs.EIGHT_LANES
     dims = gdn.Dims.of(*shape.__dict__.values())
     w = gs.window_inputs(shape, (502,), ragged=True)
     parent = gs.tree_parents(w.t_lane, 16, (502,))

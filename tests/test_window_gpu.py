@@ -52,7 +52,7 @@ def _check_untouched_rows(o_np, t_lane):
 
 SMALL = [
     # (name, NL, N, Hv, Hk, dk, dv, T, bf16, ragged, l2norm, scale)
-    ("cfg0_like", 1, 1, 2, 2, 16, 16, 4, False, False, True, 1.0),
+    ("tiny_d16_t4", 1, 1, 2, 2, 16, 16, 4, False, False, True, 1.0),
     ("d128_two_col_blocks", 2, 3, 4, 2, 128, 128, 16, True, True, True, 1.0),
     ("d64_col_tail", 1, 2, 2, 1, 64, 96, 5, True, True, True, 1.0),
     ("d32_dv200_f32", 1, 1, 3, 3, 32, 200, 7, False, False, True, 1.0),
@@ -240,12 +240,12 @@ def test_strong_decay_folds(case):
     _fold_check("decay_" + name, dk, dv, bf16, fill)
 
 
-def test_config0_tiny_case():
+def test_tiny_case_f32():
     """1 lane, 1 layer, 2 heads, d = 16, T = 4, f32 inputs; m ~ U{0..4}."""
-    shape = gs.config_shape(0)
-    w = gs.window_inputs(shape, (0, 0), bf16=False)
-    S0 = gs.initial_state(shape, (0, 0))
-    m = gs.accepted_uniform(w.t_lane, (0, 0))
+    shape, key = gs.TINY, (gs.KEY_TINY, 0)
+    w = gs.window_inputs(shape, key, bf16=False)
+    S0 = gs.initial_state(shape, key)
+    m = gs.accepted_uniform(w.t_lane, key)
     dims = gdn.Dims.of(*shape.__dict__.values())
     S_dev = to_dev(S0, torch)
     o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
@@ -255,7 +255,7 @@ def test_config0_tiny_case():
     o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
     S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m)
     S_gpu = S_dev.cpu().numpy()
-    say("config 0: m =", m, "o err %.2e S err %.2e" % (
+    say("tiny case: m =", m, "o err %.2e S err %.2e" % (
         o_rel_err(o.cpu().numpy(), o_ref, w.t_lane), s_rel_err(S_gpu, S_ref)))
     assert o_rel_err(o.cpu().numpy(), o_ref, w.t_lane) <= TOL
     assert s_rel_err(S_gpu, S_ref) <= TOL
@@ -263,31 +263,31 @@ def test_config0_tiny_case():
     assert np.array_equal(S_gpu, want)
 
 
-def test_config2_full_size_ragged():
+def test_eight_lanes_48_layers_ragged():
     """8 lanes x 48 layers x 32/16 heads, d = 128, T_l ~ U{1..16},
     m_l ~ U{0..T_l}: full o and S parity against the oracle, and bit-exact
     replay on layer 0 (debug states)."""
-    shape = gs.config_shape(2)
-    say("config 2: generating inputs")
-    w = gs.window_inputs(shape, (2, 0), ragged=True)
-    S0 = gs.initial_state(shape, (2, 0))
-    m = gs.accepted_uniform(w.t_lane, (2, 0))
+    shape, key = gs.EIGHT_LANES, (gs.KEY_EIGHT_LANES, 0)
+    say("8 lanes x 48 layers: generating inputs")
+    w = gs.window_inputs(shape, key, ragged=True)
+    S0 = gs.initial_state(shape, key)
+    m = gs.accepted_uniform(w.t_lane, key)
     dims = gdn.Dims.of(*shape.__dict__.values())
     S_dev = to_dev(S0, torch)
-    say("config 2: verify, T =", w.t_lane, "m =", m)
+    say("8 lanes x 48 layers: verify, T =", w.t_lane, "m =", m)
     o, rec, _ = _run_verify(dims, w, S_dev)
     o_np = o.cpu().numpy()
     _check_untouched_rows(o_np, w.t_lane)
     gdn.commit(dims, m, w.t_lane, rec, S_dev)
     S_gpu = S_dev.cpu().numpy()
-    say("config 2: oracle")
+    say("8 lanes x 48 layers: oracle")
     q64, k64, v64, b64, g64 = w.as_f64()
     o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
     e_o = o_rel_err(o_np, o_ref, w.t_lane)
     del o_ref
     S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m)
     e_s = s_rel_err(S_gpu, S_ref)
-    say("config 2: o err %.3e  S err %.3e" % (e_o, e_s))
+    say("8 lanes x 48 layers: o err %.3e  S err %.3e" % (e_o, e_s))
     assert e_o <= TOL and e_s <= TOL
 
     # bit-exact replay on layer 0 through a one-layer call with debug states
@@ -307,16 +307,15 @@ def test_config2_full_size_ragged():
     assert np.array_equal(S1, S_gpu[:1])
 
 
-def _chained(cfg, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
+def _chained(shape, case, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
     """Chained verify -> commit(m) rounds; the oracle follows the sampled
     layers through every round.  Window inputs cycle through a pool of
     seeded sets, gates are redrawn every round.  Returns per-round errors."""
-    shape = gs.config_shape(cfg)
     dims = gdn.Dims.of(*shape.__dict__.values())
-    S0 = gs.initial_state(shape, (cfg, 0))
+    S0 = gs.initial_state(shape, (case, 0))
     S_dev = to_dev(S0, torch)
     S_or = S0[sample_layers].astype(np.float64)
-    pool_w = [gs.window_inputs(shape, (cfg, 1000 + p)) for p in range(pool)]
+    pool_w = [gs.window_inputs(shape, (case, 1000 + p)) for p in range(pool)]
     o_buf = torch.empty((shape.n_layers, shape.n_lanes, shape.t_max, shape.h_v,
                          shape.d_v), device="cuda")
     rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device="cuda")
@@ -328,9 +327,9 @@ def _chained(cfg, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
         base = pool_w[r % pool]
         gw = gs.window_inputs(gs.WindowShape(shape.n_layers, shape.n_lanes,
                                              shape.h_v, 1, 1, 1, shape.t_max),
-                              (cfg, 5000 + r))
+                              (case, 5000 + r))
         beta, g = gw.beta, gw.g
-        m = acc(t_lane, (cfg, r))
+        m = acc(t_lane, (case, r))
         q, k, v = dev_pool[r % pool]
         beta_d, g_d = to_dev(beta, torch), to_dev(g, torch)
         # bit-exact replay, every round, on one sampled layer: a one-layer
@@ -370,17 +369,17 @@ def _chained(cfg, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
     return errs
 
 
-def test_config1_chained_100_rounds():
+def test_one_lane_100_chained_rounds():
     """1 lane x 48 layers, T = 16, m ~ U{0..16}, 100 rounds carrying S."""
-    say("config 1")
-    errs = _chained(1, 100, gs.accepted_uniform, [0, 23, 47], 16)
+    say("1 lane x 48 layers, 100 rounds")
+    errs = _chained(gs.ONE_LANE, gs.KEY_ONE_LANE, 100, gs.accepted_uniform, [0, 23, 47], 16)
     assert max(max(e) for e in errs) <= TOL
 
 
-def test_config3_chained_256_rounds():
+def test_twelve_lanes_256_chained_rounds():
     """12 lanes x 48 layers, T = 6, m ~ Binomial(6, 0.7), 256 rounds."""
-    say("config 3")
-    errs = _chained(3, 256, lambda t, key: gs.accepted_binomial(t, 0.7, key),
+    say("12 lanes x 48 layers, 256 rounds")
+    errs = _chained(gs.TWELVE_LANES_T6, gs.KEY_TWELVE_LANES, 256, lambda t, key: gs.accepted_binomial(t, 0.7, key),
                     [5], 6, say_every=32)
     worst = max(max(e) for e in errs)
     assert worst <= TOL
