@@ -47,6 +47,7 @@ CASES = [
     ("d32_f32", 1, 2, 3, 3, 32, 200, 7, False, 4, True),
     ("d16_f32", 2, 2, 2, 2, 16, 16, 4, False, 5, False),
     ("d128_dv256", 1, 3, 2, 1, 128, 256, 8, True, 4, True),
+    ("d128_t40_long_window", 1, 3, 2, 1, 128, 128, 40, True, 3, False),
 ]
 
 

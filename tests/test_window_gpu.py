@@ -64,6 +64,10 @@ SMALL = [
     ("d128_group1", 1, 2, 2, 2, 128, 128, 5, True, True, True, 1.0),
     ("d128_t1", 2, 3, 2, 1, 128, 128, 1, True, False, True, 1.0),
     ("d128_dv256", 1, 2, 2, 1, 128, 256, 9, True, True, True, 1.0),
+    # the longest windows the ABI takes (64 tokens): the token-by-token
+    # kernel, bf16 at d = 128 and f32 at d_k = 64
+    ("d128_t64_max_window", 1, 2, 4, 2, 128, 128, 64, True, True, True, 1.0),
+    ("d64_t33_f32", 1, 2, 2, 1, 64, 64, 33, False, True, True, 1.0),
 ]
 
 
