@@ -16,7 +16,11 @@
 //   O      = diag(gamma rq) (Q H) + P V_new   (times the output scale)
 //   H'     = gamma_63 H + K^T diag(rk exp(G_63 - G)) V_new
 // Unrolling the token-by-token rule inside one chunk gives exactly these
-// expressions; only the evaluation order differs.
+// expressions; only the evaluation order differs.  G is summed in segments
+// that restart after a gate whose exponential is 0 in f32 (g < -128, g =
+// -inf): every decay across such a gate is exactly 0 (the state before it
+// is forgotten, alpha = 0), and no difference of two infinite or huge sums
+// is formed.
 //
 // Kernels:
 //   p1  one workgroup per (sequence, chunk, value head), all chunks in
@@ -60,6 +64,7 @@ constexpr int kC = 64;     // chunk length
 constexpr int kD = 128;    // d_k = d_v
 constexpr int kTile = 16;  // value columns per p2 workgroup
 constexpr int kThreads = 256;
+constexpr float kReset = -128.f;  // exp(g) rounds to 0 in f32 below this
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   float* Ts = reinterpret_cast<float*>(Ks);  // written once K is consumed
   static_assert(sizeof(float) * kC * FS <= sizeof(u16) * kC * KS, "alias");
   __shared__ float rk_s[kC], rq_s[kC], G_s[kC], b_s[kC];
+  __shared__ int R_s[kC];  // last reset at or before the token, -1 if none
 
   const int bid = blockIdx.x;
   const int h = bid % d.Hv;
@@ -200,14 +206,29 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
     const float bb = (tid < nv) ? beta[gi] : 0.f;
     const float gg = (tid < nv) ? g[gi] : 0.f;
     b_s[tid] = bb;
-    // inclusive prefix sum of g over the chunk (wave 0), fixed order
-    float x = gg;
+    // segmented inclusive prefix sum of g over the chunk (wave 0), fixed
+    // order.  A gate below kReset (its exponential is 0 in f32; g = -inf
+    // included) starts a new segment and adds 0, so every decay between two
+    // tokens of one segment is exp of a difference of finite sums, and a
+    // decay across a reset is exactly 0 (never inf - inf).  Without resets
+    // this is the plain prefix sum.
+    const bool reset = gg < kReset;
+    float x = reset ? 0.f : gg;
+    int head = reset ? 1 : 0;
+    int lr = reset ? tid : -1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
-      if (tid >= off) x += y;
+      const int hy = __shfl_up(head, off, 64);
+      const int ly = __shfl_up(lr, off, 64);
+      if (tid >= off) {
+        if (!head) x += y;
+        head |= hy;
+        lr = max(lr, ly);
+      }
     }
     G_s[tid] = x;
+    R_s[tid] = lr;
   }
   __syncthreads();  // K rows, b, G in LDS
 
@@ -267,6 +288,7 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   {
     const int i = 16 * w + n;
     const float Gi = G_s[i], bki = b_s[i] * rk_s[i], sqi = d.scale * rq_s[i];
+    const int Ri = R_s[i];
     f32x4 pv[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -276,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * nt + 4 * g4 + e;
           const float rkj = rk_s[j];
-          const float dec = __expf(j <= i ? Gi - G_s[j] : 0.f);
+          // 0 across a reset between j and i
+          const float dec = Ri <= j ? __expf(j <= i ? Gi - G_s[j] : 0.f) : 0.f;
           const float lraw = bki * rkj * AK[nt][e] * dec;
           const float praw = sqi * rkj * AQ[nt][e] * dec;
           Lt[j * LS + i] = (j < i) ? lraw : 0.f;
@@ -377,15 +400,19 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   }
   if (tid < kC) {
     const int i = tid;
+    // decays from the chunk start (gamma) and to the chunk end, 0 across a
+    // reset
     const float Gc = G_s[kC - 1];
-    const float gam = __expf(G_s[i]);
+    const int Rc = R_s[kC - 1];
+    const float gam = R_s[i] < 0 ? __expf(G_s[i]) : 0.f;
     float* vec = reinterpret_cast<float*>(wsb + WsLayout::kVec);
     vec[i] = b_s[i];                                  // sb: beta
     vec[kC + i] = b_s[i] * gam * rk_s[i];             // sk: beta gamma rk
     vec[2 * kC + i] = gam * rq_s[i] * d.scale;        // so: gamma rq scale
-    vec[3 * kC + i] = rk_s[i] * __expf(Gc - G_s[i]);  // sd: rk exp(G_63 - G_i)
+    vec[3 * kC + i] = Rc <= i ? rk_s[i] * __expf(Gc - G_s[i]) : 0.f;  // sd: rk exp(G_63 - G_i)
     if (i == 0)
-      *reinterpret_cast<float4*>(wsb + WsLayout::kGc) = make_float4(__expf(Gc), 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(wsb + WsLayout::kGc) =
+          make_float4(Rc < 0 ? __expf(Gc) : 0.f, 0.f, 0.f, 0.f);
   }
 }
 

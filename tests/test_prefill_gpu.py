@@ -131,6 +131,41 @@ def test_resume_from_checkpoint_is_bitwise():
         assert np.array_equal(o2[0], o[0, t:]), j
 
 
+# positions (token, value head) of the planted gates: the first, a middle
+# and the last token of chunks, two adjacent tokens, and the sequence's last
+FORGET_AT = [(0, 0), (64, 1), (100, 0), (101, 0), (127, 1), (191, 0),
+             (250, 1), (299, 0)]
+
+
+@pytest.mark.parametrize("gate", ["alpha_zero", "strong_decay"])
+def test_prefill_forgetting_gates(gate):
+    """Tokens whose decay is exactly 0 (g = -inf) or vanishes in f32
+    (g = -200) inside chunks: the state before them is forgotten.  Parity
+    with the oracle on outputs, checkpoints and S_final, and bitwise resume
+    from a checkpoint."""
+    L, Hv, Hk, interval = 300, 2, 1, 128
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (43, hash_case(gate)),
+                          g_mean=0.0)
+    val = -np.inf if gate == "alpha_zero" else -200.0
+    for t, hh in FORGET_AT:
+        p.g[t, hh] = val
+    S0 = gs.prefill_state(Hv, 128, 128, (43,))[None]
+    o, ck, Sf = run_prefill(p, [p], S0, interval)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, S0[0].astype(np.float64), interval)
+    e_o, e_s = o_err(o[0], o_ref), s_err(Sf[0], Sf_ref)
+    say("  %s: o err %.2e  S err %.2e" % (gate, e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL
+    for j in range(L // interval):
+        assert s_err(ck[0, j], ck_ref[j]) <= TOL
+    t = interval
+    tail = gs.PrefillInputs(L - t, Hv, Hk, 128, 128, True, p.q[t:], p.k[t:],
+                            p.v[t:], p.beta[t:], p.g[t:])
+    o2, _, Sf2 = run_prefill(tail, [tail], ck[:, 0], interval)
+    assert np.array_equal(Sf2, Sf)
+    assert np.array_equal(o2[0], o[0, t:])
+
+
 def test_short_prefill_agrees_with_verify():
     """A prefill of T <= 16 tokens and a verify window over the same tokens
     run different kernels; both match the oracle, and each other."""
