@@ -123,6 +123,61 @@ def test_window_parity_and_bitexact_replay(case):
         assert s_rel_err(S_c, S_ref) <= TOL
 
 
+MAX_LANES = [
+    # (name, Hv, Hk, dk, dv, T, bf16): the matrix-core and the
+    # token-by-token verify at the ABI's lane limit
+    ("bf16_d128", 2, 1, 128, 128, 16, True),
+    ("f32_d16", 2, 2, 16, 16, 8, False),
+]
+
+
+@pytest.mark.parametrize("case", MAX_LANES, ids=[c[0] for c in MAX_LANES])
+def test_max_lanes(case):
+    """GDN_MAX_LANES (256) lanes with ragged windows: outputs against the
+    oracle, commit(m) bitwise against the debug states for every lane, and
+    the fused call bitwise against commit + verify (the per-lane tables
+    travel in the kernel arguments)."""
+    name, Hv, Hk, dk, dv, T, bf16 = case
+    N = gdn.GDN_MAX_LANES
+    shape = gs.WindowShape(1, N, Hv, Hk, dk, dv, T)
+    key = (102, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    S0 = gs.initial_state(shape, key)
+    m = gs.accepted_uniform(w.t_lane, key)
+    dims = gdn.Dims.of(1, N, Hv, Hk, dk, dv, T)
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    gdn.commit(dims, m, w.t_lane, rec, S_dev)
+    torch.cuda.synchronize()
+    o_np, dbg_np, S_np = o.cpu().numpy(), dbg.cpu().numpy(), S_dev.cpu().numpy()
+    _check_untouched_rows(o_np, w.t_lane)
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    say("  %s: o err %.2e" % (name, e_o))
+    assert e_o <= TOL
+    for n in range(N):
+        want = S0[:, n] if m[n] == 0 else dbg_np[:, n, m[n] - 1]
+        assert np.array_equal(S_np[:, n], want), n
+    S_ref = oracle.commit(q64, k64, v64, b64, g64, S0, m)
+    assert s_rel_err(S_np, S_ref) <= TOL
+    # one fused round on top: commit of this window + verify of the next
+    w2 = gs.window_inputs(shape, key + (1,), bf16=bf16, ragged=True)
+    q, k, v, beta, g = window_to_dev(w2, torch)
+    S_a, S_b = to_dev(S0, torch), to_dev(S0, torch)
+    o_a = torch.zeros((1, N, T, Hv, dv), device="cuda")
+    o_b = torch.zeros_like(o_a)
+    rec_a = torch.empty_like(rec)
+    rec_b = torch.empty_like(rec)
+    gdn.commit(dims, m, w.t_lane, rec, S_a)
+    gdn.verify(dims, w2.t_lane, q, k, v, beta, g, S_a, o_a, rec_a)
+    gdn.commit_verify(dims, m, w.t_lane, rec, w2.t_lane, q, k, v, beta, g,
+                      S_b, o_b, rec_b)
+    torch.cuda.synchronize()
+    assert torch.equal(S_a, S_b)
+    assert torch.equal(o_a, o_b)
+
+
 def test_verify_is_deterministic_and_leaves_state():
     shape = gs.WindowShape(2, 4, 4, 2, 128, 128, 16)
     w = gs.window_inputs(shape, (101,), ragged=True)
