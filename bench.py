@@ -58,6 +58,24 @@ def alg_bytes_commit(m_lane):
     return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
 
 
+def alg_bytes_kda_verify(t_lane):
+    """KDA verify: the S0 read plus, per window token, q and k (bf16), v
+    (bf16), beta (f32 per value head), the per-channel gates g (f32
+    [h_v][d_k]), o (f32) and the records (raw k f32 [h_k][d_k], u f32
+    [h_v][d_v], the per-channel decays f32 [h_v][d_k])."""
+    s0 = HV * DK * DV * 4
+    per_tok = (2 * HK * DK * 2 + HV * DV * 2 + HV * 4 + HV * DK * 4 +
+               HV * DV * 4 + HK * DK * 4 + HV * DV * 4 + HV * DK * 4)
+    return NL * sum(s0 + per_tok * int(t) for t in t_lane)
+
+
+def alg_bytes_kda_commit(m_lane):
+    """S0 read + S_m write for lanes with m > 0, plus m KDA records each."""
+    s = HV * DK * DV * 4
+    rec = HK * DK * 4 + HV * DV * 4 + HV * DK * 4
+    return NL * sum((2 * s + rec * int(m)) if m > 0 else 0 for m in m_lane)
+
+
 def alg_bytes_fused(t_lane, m_prev):
     """Algorithmic bytes of one gdn_commit_verify: per lane-layer the state
     read, the committed state write when m_prev > 0, m_prev records read,
@@ -293,10 +311,16 @@ def bench_tree(reps=20, warmup=3):
     ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     upd = N * T * NL * HV
+    # a node has the window traffic of a token; the path commit moves the
+    # commit's bytes for the path's length
+    bv = alg_bytes_verify(t_lane)
+    bc = alg_bytes_commit([len(p) for p in paths])
     return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, 16-node "
                         "depth-first draft trees, accepted-path commit",
             "rebuilds": rebuilds, "verify_ms": ms_v, "commit_ms": ms_c,
-            "node_updates_per_s": upd / ((ms_v + ms_c) * 1e-3)}
+            "node_updates_per_s": upd / ((ms_v + ms_c) * 1e-3),
+            "verify_hbm_frac": bv / (ms_v * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "commit_hbm_frac": bc / (ms_c * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
 
 def bench_kda(reps=20, warmup=3):
@@ -339,10 +363,14 @@ def bench_kda(reps=20, warmup=3):
     ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     upd = N * T * NL * HV
+    bv = alg_bytes_kda_verify(t_lane)
+    bc = float(np.mean([alg_bytes_kda_commit(m) for m in ms_all[warmup:]]))
     return {"workload": "KDA verify+commit: 8 lanes x 48 layers x 32/16 heads, "
                         "d=128, T=16, m ~ U{0..16}",
             "verify_ms": ms_v, "commit_ms": ms_c,
-            "updates_per_s": upd / ((ms_v + ms_c) * 1e-3)}
+            "updates_per_s": upd / ((ms_v + ms_c) * 1e-3),
+            "verify_hbm_frac": bv / (ms_v * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "commit_hbm_frac": bc / (ms_c * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
 
 def bench_snapshot(reps=5):

@@ -36,6 +36,20 @@ def test_window_bytes_follow_the_record_layout_and_shapes():
     assert b.alg_bytes_verify([0]) == b.NL * state
 
 
+def test_kda_bytes_follow_the_kda_record_layout():
+    b = _bench()
+    dims = gdn.Dims.of(1, 1, b.HV, b.HK, b.DK, b.DV, 64)
+    rec_tok = gdn.kda_records_bytes(dims) / 64.0
+    inputs = (2 * b.HK * b.DK * 2 + b.HV * b.DV * 2 + b.HV * 4  # q k v, beta
+              + b.HV * b.DK * 4)                                # per-channel g
+    out = b.HV * b.DV * 4
+    per_tok = (b.alg_bytes_kda_verify([2]) - b.alg_bytes_kda_verify([1])) / b.NL
+    assert abs(per_tok - (inputs + out + rec_tok)) < 16
+    per_rec = (b.alg_bytes_kda_commit([2]) - b.alg_bytes_kda_commit([1])) / b.NL
+    assert abs(per_rec - rec_tok) < 16
+    assert b.alg_bytes_kda_commit([1]) / b.NL > 2 * b.HV * b.DK * b.DV * 4
+
+
 def test_verify_bytes_of_the_8_lane_t16_round():
     b = _bench()
     # 48 layers x 8 lanes: the 2 MiB state read plus 16 tokens of 57,856 B
