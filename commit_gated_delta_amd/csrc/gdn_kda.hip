@@ -210,7 +210,9 @@ void kda_verify_kernel(
 }
 
 template <int DK>
-__global__ __launch_bounds__(kBlock) void kda_commit_kernel(
+// Six waves per SIMD: the LDS stage lets the compiler hoist every row read
+// of a token, which at the default limit halves the occupancy.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void kda_commit_kernel(
     const float* __restrict__ rec_k, const float* __restrict__ rec_u,
     const float* __restrict__ rec_a, float* __restrict__ S, WinDims d,
     CommitTable ct) {
@@ -245,22 +247,59 @@ __global__ __launch_bounds__(kBlock) void kda_commit_kernel(
 #pragma unroll
   for (int r = 0; r < R; ++r)
     s[r] = __builtin_nontemporal_load(Sh + (uint32_t)(r * d.dv + ic));
-  // ut of token t+1 is requested before token t is applied; the key and
-  // decay rows (scalar loads, 2 x R registers) are loaded per token and
-  // their latency is covered by the other workgroups on the CU
+  // The key rows (this workgroup's key head) and decay rows (its value
+  // head) of up to kStageTok tokens are staged in LDS with one cooperative
+  // load and one wait; the replay then reads them as broadcasts.  ut of
+  // token t+1 is requested before token t is applied.  The operations and
+  // their order per entry are those of the verify's state update.
+  constexpr int kStageTok = 16;
+  constexpr int kRow4 = DK / 4;                        // float4 per row
+  constexpr int kRep = 2 * kStageTok * kRow4 / kBlock;  // loads per thread
+  static_assert(2 * kStageTok * kRow4 % kBlock == 0, "staging split");
+  __shared__ float4 st_k[kStageTok][kRow4];
+  __shared__ float4 st_a[kStageTok][kRow4];
+  const int tid = (int)threadIdx.x;
   float ut = u0[(uint32_t)ic];
-  for (int t = 0; t < m; ++t) {
-    const int nt = t + 1 < m ? t + 1 : t;
-    const float ut_n = u0[nt * vo_step + (uint32_t)ic];
-    RowWords<float, R> kw, aw;
-    kw.load(k0 + t * kq_step, j0);
-    aw.load(a0 + t * g_step, j0);
+  for (int t0 = 0; t0 < m; t0 += kStageTok) {
+    const int nb = m - t0 < kStageTok ? m - t0 : kStageTok;
+    float4 reg[kRep];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      s[r] = s[r] * aw.at(r);
-      s[r] = __builtin_fmaf(ut, kw.at(r), s[r]);
+    for (int rep = 0; rep < kRep; ++rep) {
+      const int e = tid + rep * kBlock;
+      const int which = e / (kStageTok * kRow4);  // 0: key row, 1: decay row
+      const int idx = e % (kStageTok * kRow4);
+      int tok = idx / kRow4;
+      tok = tok < nb ? tok : nb - 1;
+      const int c4 = idx % kRow4;
+      const float* src = which ? a0 + (size_t)(t0 + tok) * g_step
+                               : k0 + (size_t)(t0 + tok) * kq_step;
+      reg[rep] = reinterpret_cast<const float4*>(src)[c4];
     }
-    ut = ut_n;
+#pragma unroll
+    for (int rep = 0; rep < kRep; ++rep) {
+      const int e = tid + rep * kBlock;
+      const int which = e / (kStageTok * kRow4);
+      const int idx = e % (kStageTok * kRow4);
+      (which ? &st_a[0][0] : &st_k[0][0])[idx] = reg[rep];
+    }
+    __syncthreads();
+    for (int t = 0; t < nb; ++t) {
+      const int tg = t0 + t;
+      const int nt = tg + 1 < m ? tg + 1 : tg;
+      const float ut_n = u0[nt * vo_step + (uint32_t)ic];
+      const float4* kr = &st_k[t][j0 / 4];
+      const float4* ar = &st_a[t][j0 / 4];
+#pragma unroll
+      for (int r4 = 0; r4 < R / 4; ++r4) {
+        const float4 kk = kr[r4], aa = ar[r4];
+        s[4 * r4 + 0] = __builtin_fmaf(ut, kk.x, s[4 * r4 + 0] * aa.x);
+        s[4 * r4 + 1] = __builtin_fmaf(ut, kk.y, s[4 * r4 + 1] * aa.y);
+        s[4 * r4 + 2] = __builtin_fmaf(ut, kk.z, s[4 * r4 + 2] * aa.z);
+        s[4 * r4 + 3] = __builtin_fmaf(ut, kk.w, s[4 * r4 + 3] * aa.w);
+      }
+      ut = ut_n;
+    }
+    __syncthreads();  // the next batch overwrites the stage
   }
   if (act) {
 #pragma unroll
