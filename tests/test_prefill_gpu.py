@@ -131,6 +131,25 @@ def test_resume_from_checkpoint_is_bitwise():
         assert np.array_equal(o2[0], o[0, t:]), j
 
 
+def test_prefill_without_key_normalisation():
+    """Flag L2NORM_QK off, with an output scale: the kernel takes the raw
+    key and query rows.  Keys and queries are drawn pre-scaled by d_k^-1/2
+    (rounded to bf16) so that the rule stays stable without the norm."""
+    L, Hv, Hk, interval = 260, 4, 2, 128
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (44,), g_mean=0.0)
+    p.k = gs.f32_to_bf16_bits(gs.bf16_bits_to_f32(p.k) / np.sqrt(128.0))
+    p.q = gs.f32_to_bf16_bits(gs.bf16_bits_to_f32(p.q) / np.sqrt(128.0))
+    S0 = gs.prefill_state(Hv, 128, 128, (44,))[None]
+    o, ck, Sf = run_prefill(p, [p], S0, interval, scale=0.7, l2norm=False)
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, S0[0].astype(np.float64),
+                                           interval, scale=0.7, l2norm=False)
+    e_o, e_s = o_err(o[0], o_ref), s_err(Sf[0], Sf_ref)
+    say("  no norm: o err %.2e  S err %.2e" % (e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL
+    for j in range(L // interval):
+        assert s_err(ck[0, j], ck_ref[j]) <= TOL
+
+
 # positions (token, value head) of the planted gates: the first, a middle
 # and the last token of chunks, two adjacent tokens, and the sequence's last
 FORGET_AT = [(0, 0), (64, 1), (100, 0), (101, 0), (127, 1), (191, 0),
