@@ -36,6 +36,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "gdn_mfma_util.h"
 #include "gdn_window_common.h"
@@ -59,6 +60,12 @@ struct KdaLds {
   __attribute__((aligned(16))) float P[kTok * kLS];   // P[t][s]
   float beta[kTok], rk[kTok], rq[kTok];
 };
+// A fragments of (k . C) H and (q . C) H: [k-step][k hi, k lo, q hi, q lo]
+// [lane], 16 KiB.  Without debug states they overlay the decays a and C
+// (16 KiB, dead once L, P and the fragments are formed); the debug replay
+// still reads a, so there they have their own space.
+typedef u32x4 AFrags[kKS][4][kWave];
+static_assert(sizeof(AFrags) == 2 * sizeof(float) * kTok * kD, "overlay size");
 struct KdaWave {
   __attribute__((aligned(16))) float Ts[kTok * kLS];
   float Us[kTok * kUS];
@@ -93,6 +100,8 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  int l2norm) {
   __shared__ KdaLds sh;
   __shared__ KdaWave wv[kWaves];
+  __shared__ std::conditional_t<DBG, AFrags, char> af_own;
+  AFrags& Af = *reinterpret_cast<AFrags*>(DBG ? (void*)&af_own : (void*)&sh.a[0][0]);
 
   int item = xcd_item(blockIdx.x, gridDim.x);
   const int h = item % d.Hv;
@@ -230,9 +239,14 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
 
   // ---- L and P: thread (s, cq) runs E_ts over channels 8 cq .. 8 cq + 7 for
-  // t = s .. 15; the 16 channel slices of a row meet by a DPP row sum
+  // t = s .. 15; the 16 channel slices of a row meet by a DPP row sum.  Wave
+  // w holds the rows s = 4w .. 4w + 3, so its loop starts at t = 4w (every
+  // entry before that is above the diagonal: P's are zeroed here, L's are
+  // never read)
   {
     const int s = tid >> 4, cq = tid & 15;
+    if (cq == 0)
+      for (int t = 0; t < 4 * w; ++t) sh.P[t * kLS + s] = 0.f;
     float ksv[8];
     widen8(*reinterpret_cast<const u32x4*>(&sh.k[s][8 * cq]), ksv);
     float E[8];
@@ -240,7 +254,7 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int i = 0; i < 8; ++i) E[i] = 1.0f;
     const float rks = sh.rk[s];
 #pragma unroll 1
-    for (int t = 0; t < kTok; ++t) {
+    for (int t = 4 * w; t < kTok; ++t) {
       float kt[8], qt[8];
       widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][8 * cq]), kt);
       widen8(*reinterpret_cast<const u32x4*>(&sh.q[t][8 * cq]), qt);
@@ -265,6 +279,32 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
   }
+  // ---- the decayed key and query rows of token n (entries 32 ks + 8 g4 ..
+  // + 7) split into bf16 hi + lo: the A fragments of (k . C) H and (q . C) H
+  // are the same for every wave, so wave w forms k-step w once for all
+  u32x4 af[4];
+  {
+    const int j0 = 32 * w + 8 * g4;
+    float kx[8], qx[8];
+    widen8(*reinterpret_cast<const u32x4*>(&sh.k[n][j0]), kx);
+    widen8(*reinterpret_cast<const u32x4*>(&sh.q[n][j0]), qx);
+    const f32x4 ca = *reinterpret_cast<const f32x4*>(&sh.c[n][j0]);
+    const f32x4 cb = *reinterpret_cast<const f32x4*>(&sh.c[n][j0 + 4]);
+    const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
+    uint32_t kh4[4], kl4[4], qh4[4], ql4[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      split2(kx[2 * p] * cv[2 * p], kx[2 * p + 1] * cv[2 * p + 1], kh4[p], kl4[p]);
+      split2(qx[2 * p] * cv[2 * p], qx[2 * p + 1] * cv[2 * p + 1], qh4[p], ql4[p]);
+    }
+    af[0] = u32x4{kh4[0], kh4[1], kh4[2], kh4[3]};
+    af[1] = u32x4{kl4[0], kl4[1], kl4[2], kl4[3]};
+    af[2] = u32x4{qh4[0], qh4[1], qh4[2], qh4[3]};
+    af[3] = u32x4{ql4[0], ql4[1], ql4[2], ql4[3]};
+  }
+  __syncthreads();  // L, P complete; a and C read for the last time
+#pragma unroll
+  for (int x = 0; x < 4; ++x) Af[w][x][l] = af[x];
   __syncthreads();
 
   // ---- T = (I + L)^-1 in each wave's tile (lane n < 16 of group 0 solves
@@ -296,23 +336,8 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
-    const int j0 = 32 * ks + 8 * g4;
-    float kx[8], qx[8];
-    widen8(*reinterpret_cast<const u32x4*>(&sh.k[n][j0]), kx);
-    widen8(*reinterpret_cast<const u32x4*>(&sh.q[n][j0]), qx);
-    const f32x4 ca = *reinterpret_cast<const f32x4*>(&sh.c[n][j0]);
-    const f32x4 cb = *reinterpret_cast<const f32x4*>(&sh.c[n][j0 + 4]);
-    const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
-    uint32_t kh4[4], kl4[4], qh4[4], ql4[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      split2(kx[2 * p] * cv[2 * p], kx[2 * p + 1] * cv[2 * p + 1], kh4[p], kl4[p]);
-      split2(qx[2 * p] * cv[2 * p], qx[2 * p + 1] * cv[2 * p + 1], qh4[p], ql4[p]);
-    }
-    const u32x4 KAh = {kh4[0], kh4[1], kh4[2], kh4[3]};
-    const u32x4 KAl = {kl4[0], kl4[1], kl4[2], kl4[3]};
-    const u32x4 QAh = {qh4[0], qh4[1], qh4[2], qh4[3]};
-    const u32x4 QAl = {ql4[0], ql4[1], ql4[2], ql4[3]};
+    const u32x4 KAh = Af[ks][0][l], KAl = Af[ks][1][l];
+    const u32x4 QAh = Af[ks][2][l], QAl = Af[ks][3][l];
     uint32_t h0[4], lo0[4], h1[4], lo1[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
