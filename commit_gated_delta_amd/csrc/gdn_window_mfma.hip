@@ -369,33 +369,54 @@ void mverify_kernel(
   int R;
   uint32_t anc;  // bit s: token s is a strict ancestor of token n
   if constexpr (TREE) {
-    // node by node in index order (a parent precedes its children); after
-    // the walk lane n holds node n's segment sum, deepest zero-decay node
-    // on its path, scale step and ancestor set
-    Gs = 0.f;
-    c = 1.f;
-    R = -1;
-    anc = 0u;
+    // pointer jumping over the ancestor chain: lane n holds the aggregate
+    // of the path segment (J, n] (segment sum and deepest zero-decay node,
+    // ancestor set, product of the decays) and combines it with the one that
+    // lane J holds for (J', J], all lanes at once; parents precede their
+    // children, so a path has at most 16 nodes and four jumps reach the
+    // root.  On a chain this is the window's scan, step for step.
+    int J = -1;
     for (int t = 0; t < T; ++t) {
       const int par = tree_parent(tree, lane * d.T + t);
-      const float gtt = lane_value(gt, t);
-      const float Gp = par < 0 ? 0.f : lane_value(Gs, par);
-      const int Rp = par < 0 ? -1 : lane_int(R, par);
-      const float cp = par < 0 ? 1.0f : lane_value(c, par);
-      const uint32_t ap =
-          par < 0 ? 0u : ((uint32_t)lane_int((int)anc, par) | (1u << par));
-      const bool rs = gtt < kReset;
-      float cn, fo = 1.f;
-      if (scale_step(cp, lane_value(a_t, t), cn)) {
-        fo = cn;
-        cn = 1.0f;
+      J = n == t ? par : J;
+    }
+    const bool reset = gt < kReset;
+    Gs = reset ? 0.f : gt;
+    R = reset ? n : -1;
+    anc = 0u;
+    c = a_t;
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      const int src = J < 0 ? 0 : J;
+      const float Gy = __shfl(Gs, src, 16);
+      const int Ry = __shfl(R, src, 16);
+      const uint32_t ay = (uint32_t)__shfl((int)anc, src, 16);
+      const float cy = __shfl(c, src, 16);
+      const int Jy = __shfl(J, src, 16);
+      if (J >= 0) {
+        Gs = R < 0 ? Gy + Gs : Gs;
+        R = R > Ry ? R : Ry;
+        anc = anc | ay | (1u << J);
+        c *= cy;
+        J = Jy;
       }
-      if (n == t) {
-        Gs = rs ? 0.f : Gp + gtt;
-        R = rs ? t : Rp;
-        c = cn;
-        phi = fo;
-        anc = ap;
+    }
+    // the scale sequence of gdn_step.h needs a fold somewhere (rare): walk
+    // the nodes in index order, each continuing its parent's scale
+    const bool out = !(c >= kScaleLo && c <= kScaleHi);
+    if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
+      for (int t = 0; t < T; ++t) {
+        const int par = tree_parent(tree, lane * d.T + t);
+        const float cp = par < 0 ? 1.0f : lane_value(c, par);
+        float cn, fo = 1.f;
+        if (scale_step(cp, lane_value(a_t, t), cn)) {
+          fo = cn;
+          cn = 1.0f;
+        }
+        if (n == t) {
+          c = cn;
+          phi = fo;
+        }
       }
     }
   } else {
