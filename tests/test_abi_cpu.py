@@ -288,3 +288,20 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert _prefill(ws_bytes=1024) == gdn.GDN_EWORKSPACE
     assert _prefill(q=_Fake(addr=(1 << 20) + 8)) == gdn.GDN_EINVAL
     assert b"prefill" in gdn.lib.gdn_last_error()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the package refuses to import: there is no
+    fallback path that computes anything elsewhere."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "commit_gated_delta_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(gdn.__file__), "__init__.py"),
+                pkg / "__init__.py")
+    r = subprocess.run(
+        [sys.executable, "-c", "import commit_gated_delta_amd"],
+        cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "not built" in r.stderr
