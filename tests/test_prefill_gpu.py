@@ -150,6 +150,24 @@ def test_prefill_without_key_normalisation():
         assert s_err(ck[0, j], ck_ref[j]) <= TOL
 
 
+def test_prefill_zero_key_and_query_rows():
+    """All-zero key or query rows inside chunks (the L2 norm then scales an
+    exact 0): parity with the oracle on outputs, checkpoints and S_final."""
+    L, Hv, Hk, interval = 200, 2, 1, 64
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (45,), g_mean=0.0)
+    for t in (0, 31, 64, 127, 150):
+        p.k[t, 0] = 0
+    for t in (3, 64, 199):
+        p.q[t, 0] = 0
+    S0 = gs.prefill_state(Hv, 128, 128, (45,))[None]
+    o, ck, Sf = run_prefill(p, [p], S0, interval)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, S0[0].astype(np.float64), interval)
+    assert o_err(o[0], o_ref) <= TOL and s_err(Sf[0], Sf_ref) <= TOL
+    for j in range(L // interval):
+        assert s_err(ck[0, j], ck_ref[j]) <= TOL
+
+
 # positions (token, value head) of the planted gates: the first, a middle
 # and the last token of chunks, two adjacent tokens, and the sequence's last
 FORGET_AT = [(0, 0), (64, 1), (100, 0), (101, 0), (127, 1), (191, 0),

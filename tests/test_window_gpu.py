@@ -123,6 +123,44 @@ def test_window_parity_and_bitexact_replay(case):
         assert s_rel_err(S_c, S_ref) <= TOL
 
 
+@pytest.mark.parametrize("case", [("bf16_d128", 128, True), ("f32_d32", 32, False)],
+                         ids=["bf16_d128", "f32_d32"])
+def test_zero_key_and_query_rows(case):
+    """All-zero key or query rows (the L2 norm then scales an exact 0): the
+    token writes nothing into the state, or reads 0, exactly as the oracle
+    has it; parity and bit-exact commit for every m."""
+    name, dk, bf16 = case
+    shape = gs.WindowShape(1, 3, 4, 2, dk, dk, 16)
+    key = (103, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    for n, t in ((0, 0), (0, 5), (1, 3), (2, 15)):
+        w.k[:, n, t] = 0
+    for n, t in ((0, 2), (1, 3), (2, 7)):
+        w.q[:, n, t] = 0
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    torch.cuda.synchronize()
+    o_np, dbg_np = o.cpu().numpy(), dbg.cpu().numpy()
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, st_ref = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane,
+                                  want_states=True)
+    assert o_rel_err(o_np, o_ref, w.t_lane) <= TOL
+    for t in range(16):
+        lanes = [n for n in range(3) if w.t_lane[n] > t]
+        if lanes:
+            assert s_rel_err(dbg_np[:, lanes, t], st_ref[:, lanes, t]) <= TOL
+    for m in range(17):
+        m_lane = np.minimum(m, w.t_lane)
+        S_c = to_dev(S0, torch)
+        gdn.commit(dims, m_lane, w.t_lane, rec, S_c)
+        S_c = S_c.cpu().numpy()
+        for n in range(3):
+            want = S0[:, n] if m_lane[n] == 0 else dbg_np[:, n, m_lane[n] - 1]
+            assert np.array_equal(S_c[:, n], want), (m, n)
+
+
 MAX_LANES = [
     # (name, Hv, Hk, dk, dv, T, bf16): the matrix-core and the
     # token-by-token verify at the ABI's lane limit
