@@ -150,6 +150,23 @@ def test_prefill_without_key_normalisation():
         assert s_err(ck[0, j], ck_ref[j]) <= TOL
 
 
+def test_prefill_zero_gates_keep_the_state_bitwise():
+    """beta = 0 and g = 0: every chunk adds nothing and decays by exactly 1,
+    so every checkpoint and S_final equal S_init bit for bit; the outputs
+    are S_init q (parity)."""
+    L, Hv, Hk, interval = 300, 2, 1, 128
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (46,))
+    p.beta[:] = 0.0
+    p.g[:] = 0.0
+    S0 = gs.prefill_state(Hv, 128, 128, (46,))[None]
+    o, ck, Sf = run_prefill(p, [p], S0, interval)
+    assert np.array_equal(Sf, S0)
+    for j in range(L // interval):
+        assert np.array_equal(ck[:, j], S0)
+    o_ref, _, _ = oracle_prefill(p, S0[0].astype(np.float64), interval)
+    assert o_err(o[0], o_ref) <= TOL
+
+
 def test_prefill_zero_key_and_query_rows():
     """All-zero key or query rows inside chunks (the L2 norm then scales an
     exact 0): parity with the oracle on outputs, checkpoints and S_final."""
