@@ -167,6 +167,29 @@ def test_prefill_zero_gates_keep_the_state_bitwise():
     assert o_err(o[0], o_ref) <= TOL
 
 
+def test_prefill_orthonormal_keys_store_their_values():
+    """Closed form of the delta write (no oracle involved): with alpha = 1,
+    beta = 1 and orthonormal keys (a permuted standard basis, exact in
+    bf16; norm flag off), the final state maps every key to its value: row
+    j of the stored state (d_k x d_v) is the value written with key e_j."""
+    L, Hv, Hk = 100, 2, 1
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (47,), g_mean=0.0)
+    perm = np.random.default_rng(47).permutation(128)[:L]
+    k = np.zeros((L, Hk, 128), np.float32)
+    k[np.arange(L), 0, perm] = 1.0
+    p.k = gs.f32_to_bf16_bits(k)
+    p.beta[:] = 1.0
+    p.g[:] = 0.0
+    S0 = gs.prefill_state(Hv, 128, 128, (47,))[None]
+    _, _, Sf = run_prefill(p, [p], S0, 64, l2norm=False)
+    v = gs.bf16_bits_to_f32(p.v)                      # [L, Hv, dv]
+    for h in range(Hv):
+        got = Sf[0, h][perm]                          # rows e_j -> values
+        err = np.max(np.abs(got - v[:, h])) / np.max(np.abs(v[:, h]))
+        say("  head %d: max rel err %.2e" % (h, err))
+        assert err <= TOL
+
+
 def test_prefill_zero_key_and_query_rows():
     """All-zero key or query rows inside chunks (the L2 norm then scales an
     exact 0): parity with the oracle on outputs, checkpoints and S_final."""

@@ -161,6 +161,38 @@ def test_zero_key_and_query_rows(case):
             assert np.array_equal(S_c[:, n], want), (m, n)
 
 
+@pytest.mark.parametrize("case", [("bf16_d128", 128, True), ("f32_d32", 32, False)],
+                         ids=["bf16_d128", "f32_d32"])
+def test_orthonormal_keys_store_their_values(case):
+    """Closed form of the delta write (no oracle involved): alpha = 1,
+    beta = 1 and orthonormal keys (a permuted standard basis, exact in bf16;
+    norm flag off) make the committed state map every key to its value:
+    row j of the stored state (d_k x d_v) is the value written with e_j."""
+    name, dk, bf16 = case
+    T = 16
+    shape = gs.WindowShape(1, 2, 2, 1, dk, dk, T)
+    key = (104, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16)
+    perm = np.random.default_rng(104).permutation(dk)[:T]
+    kk = np.zeros((1, 2, T, 1, dk), np.float32)
+    kk[:, :, np.arange(T), 0, perm] = 1.0
+    w.k = gs.f32_to_bf16_bits(kk) if bf16 else kk
+    w.beta[:] = 1.0
+    w.g[:] = 0.0
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    _, rec, _ = _run_verify(dims, w, S_dev, l2norm=False)
+    gdn.commit(dims, [T, T], [T, T], rec, S_dev)
+    S = S_dev.cpu().numpy()
+    v = gs.bf16_bits_to_f32(w.v) if bf16 else w.v.astype(np.float32)
+    for n in range(2):
+        for h in range(2):
+            got = S[0, n, h][perm]
+            ref = v[0, n, :, h]
+            assert np.max(np.abs(got - ref)) / np.max(np.abs(ref)) <= TOL, (n, h)
+
+
 MAX_LANES = [
     # (name, Hv, Hk, dk, dv, T, bf16): the matrix-core and the
     # token-by-token verify at the ABI's lane limit
