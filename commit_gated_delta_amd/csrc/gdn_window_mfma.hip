@@ -86,7 +86,7 @@ struct RowLds {
   __attribute__((aligned(16))) uint16_t k[kTok][kDK];
   __attribute__((aligned(16))) uint16_t q[kTok][kDK];
   __attribute__((aligned(16))) uint16_t v[kTok][kCB];  // this block's columns
-  float g[kTok], b[kTok];
+  float g[kTok + 1], b[kTok + 1];  // slot kTok: discarded writes
 };
 // A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
 struct WaveLds {
@@ -192,10 +192,12 @@ void mverify_kernel(
     *reinterpret_cast<u32x4*>(&rows.k[rt][8 * rp]) = kr;
     *reinterpret_cast<u32x4*>(&rows.q[rt][8 * rp]) = qr;
     *reinterpret_cast<u32x4*>(&rows.v[rt][8 * rp]) = vr;
-    if (tid < kTok) {
-      rows.g[tid] = tid < T ? gl : 0.f;
-      rows.b[tid] = tid < T ? bl : 0.f;
-    }
+    // every thread stores (threads past kTok into the discarded slot): a
+    // store under a branch lets the compiler sink the gate loads into it,
+    // behind the state requests, and wait for the whole state there
+    const int gs = tid < kTok ? tid : kTok;
+    rows.g[gs] = tid < T ? gl : 0.f;
+    rows.b[gs] = tid < T ? bl : 0.f;
     // the key record rows (raw rows as f32): thread (rt, rp) writes its
     // piece; done here so that the pieces are dead past the staging
     if (cb == 0 && h % d.group == 0 && rv) {
