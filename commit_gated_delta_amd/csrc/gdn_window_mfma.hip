@@ -78,7 +78,7 @@ constexpr float kReset = -128.f;  // exp(g) rounds to 0 in f32 below this
 struct Stage {
   float k[kTok][kDK];  // raw key rows
   float u[kTok][kCB];  // ut of this workgroup's columns
-  f32x2 sc[kTok];      // (phi, c)
+  f32x2 sc[kTok + 1];  // (phi, c); slot kTok: discarded writes
 };
 // The window's raw key / query rows and gates, staged once per workgroup
 // (every wave reads its A fragments and per-token gates from here).
@@ -260,7 +260,9 @@ void mverify_kernel(
         reinterpret_cast<f32x4*>(&stage.k[0][0])[e] = kst[rep];
         reinterpret_cast<f32x4*>(&stage.u[0][0])[e] = ust[rep];
       }
-      if (tid < kTok) stage.sc[tid] = scst;
+      // every thread stores (past kTok into the discarded slot), so that
+      // the scale load is not sunk behind the record loads into a branch
+      stage.sc[tid < kTok ? tid : kTok] = scst;
       __syncthreads();
       // one step: fold (when the record has one), then the rank-1 write
       auto step = [&](int t, bool may_fold) {
