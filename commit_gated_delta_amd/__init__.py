@@ -28,7 +28,8 @@ EXPORTED = ("gdn_records_bytes", "gdn_verify", "gdn_commit",
             "gdn_kda_records_bytes", "gdn_kda_verify", "gdn_kda_commit",
             "gdn_state_snapshot", "gdn_state_restore",
             "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-            "gdn_strerror", "gdn_last_error")
+            "gdn_prefill_chunked_noalloc", "gdn_strerror", "gdn_last_error")
+PREFILL_SCRATCH_BYTES = 64 << 20
 
 
 class GdnError(RuntimeError):
@@ -94,6 +95,9 @@ def _load_library():
     lib.gdn_prefill_chunked.argtypes = [i32] * 7 + [vp] * 3 + [ctypes.c_int] + [
         vp] * 7 + [sz, f, ctypes.c_int, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_noalloc.argtypes = [i32] * 7 + [vp] * 3 + [
+        ctypes.c_int] + [vp] * 6 + [f, ctypes.c_int, vp]
+    lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -312,3 +316,20 @@ def prefill_chunked(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v, beta, g,
     if raw_status:
         return st
     _check(st, "gdn_prefill_chunked")
+
+
+def prefill_chunked_noalloc(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v,
+                            beta, g, S_init, S_final, o, checkpoints,
+                            ckpt_interval=8192, scale=1.0, l2norm=True,
+                            stream=None, raw_status=False):
+    """gdn_prefill_chunked_noalloc: the prefill with the library's fixed
+    scratch array as its workspace (no allocation; calls that overlap on
+    one GPU race)."""
+    st = lib.gdn_prefill_chunked_noalloc(
+        n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, _ptr(q), _ptr(k),
+        _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
+        _ptr(S_final), _ptr(o), _ptr(checkpoints), float(scale),
+        GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+    if raw_status:
+        return st
+    _check(st, "gdn_prefill_chunked_noalloc")

@@ -53,6 +53,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn.h"
@@ -1162,15 +1163,53 @@ extern "C" size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
   return ws_bytes(n_seqs, seq_len, h_v);
 }
 
-extern "C" int gdn_prefill_chunked(
-    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t d_k,
-    int32_t d_v, int32_t ckpt_interval, const void* q, const void* k,
-    const void* v, int in_dtype, const float* beta, const float* g,
-    const float* S_init, float* S_final, float* o, float* checkpoints,
-    void* workspace, size_t ws_size, float scale, int flags, void* stream) {
+// Workspace of the entry point that allocates nothing: a fixed device
+// array, one copy per GPU, held until the process ends.  Host code never
+// names it directly (on the host the name is only a stand-in); it takes the
+// per-device address that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = (size_t)GDN_PREFILL_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace gdnp {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current.
+static int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("prefill scratch: hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    return fail(GDN_EUNSUPPORTED, "prefill scratch: device index out of range");
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      return hip_fail("prefill scratch: hipGetSymbolAddress",
+                      e != hipSuccess ? e : hipErrorInvalidSymbol);
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+// Every argument check except those of the workspace pointer; no HIP call.
+static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
+                      int32_t h_k, int32_t d_k, int32_t d_v,
+                      int32_t ckpt_interval, const void* q, const void* k,
+                      const void* v, int in_dtype, const float* beta,
+                      const float* g, const float* S_init, float* S_final,
+                      float* o, float* checkpoints, size_t ws_size,
+                      int flags) {
   int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v);
   if (rc != GDN_OK) return rc;
-  if (!q || !k || !v || !beta || !g || !S_final || !o || !workspace) {
+  if (!q || !k || !v || !beta || !g || !S_final || !o) {
     return fail(GDN_EINVAL, "prefill: required pointer is NULL");
   }
   if (in_dtype != GDN_BF16) {
@@ -1184,14 +1223,23 @@ extern "C" int gdn_prefill_chunked(
   }
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 2) ||
       misaligned(beta, 4) || misaligned(g, 4) || misaligned(S_final, 4) ||
-      misaligned(o, 4) || misaligned(workspace, 256) ||
-      (S_init && misaligned(S_init, 4)) ||
+      misaligned(o, 4) || (S_init && misaligned(S_init, 4)) ||
       (checkpoints && misaligned(checkpoints, 4))) {
     return fail(GDN_EINVAL, "prefill: misaligned pointer");
   }
   if (ws_size < ws_bytes(n_seqs, seq_len, h_v)) {
     return fail(GDN_EWORKSPACE, "prefill: workspace too small");
   }
+  return GDN_OK;
+}
+
+// Launches P1 and P2 (arguments already checked).
+static int prefill_launch(
+    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k,
+    int32_t ckpt_interval, const void* q, const void* k, const void* v,
+    const float* beta, const float* g, const float* S_init, float* S_final,
+    float* o, float* checkpoints, void* workspace, float scale, int flags,
+    void* stream) {
   PDims dd;
   dd.n_seqs = n_seqs;
   dd.L = seq_len;
@@ -1227,4 +1275,50 @@ extern "C" int gdn_prefill_chunked(
     if (e != hipSuccess) return hip_fail("prefill p2 launch", e);
   }
   return GDN_OK;
+}
+
+}  // namespace gdnp
+
+extern "C" int gdn_prefill_chunked(
+    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t d_k,
+    int32_t d_v, int32_t ckpt_interval, const void* q, const void* k,
+    const void* v, int in_dtype, const float* beta, const float* g,
+    const float* S_init, float* S_final, float* o, float* checkpoints,
+    void* workspace, size_t ws_size, float scale, int flags, void* stream) {
+  int rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, q,
+                      k, v, in_dtype, beta, g, S_init, S_final, o, checkpoints,
+                      ws_size, flags);
+  if (rc != GDN_OK) return rc;
+  if (!workspace) return fail(GDN_EINVAL, "prefill: required pointer is NULL");
+  if (misaligned(workspace, 256)) {
+    return fail(GDN_EINVAL, "prefill: misaligned pointer");
+  }
+  return prefill_launch(n_seqs, seq_len, h_v, h_k, ckpt_interval, q, k, v,
+                        beta, g, S_init, S_final, o, checkpoints, workspace,
+                        scale, flags, stream);
+}
+
+extern "C" int gdn_prefill_chunked_noalloc(
+    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t d_k,
+    int32_t d_v, int32_t ckpt_interval, const void* q, const void* k,
+    const void* v, int in_dtype, const float* beta, const float* g,
+    const float* S_init, float* S_final, float* o, float* checkpoints,
+    float scale, int flags, void* stream) {
+  int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v);
+  if (rc != GDN_OK) return rc;
+  if (ws_bytes(n_seqs, seq_len, h_v) > kScratchBytes) {
+    return fail(GDN_EWORKSPACE,
+                "prefill (no-alloc): the workspace for these sizes exceeds the "
+                "library's fixed scratch array (GDN_PREFILL_SCRATCH_BYTES)");
+  }
+  rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, q, k, v,
+                  in_dtype, beta, g, S_init, S_final, o, checkpoints,
+                  kScratchBytes, flags);
+  if (rc != GDN_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != GDN_OK) return rc;
+  return prefill_launch(n_seqs, seq_len, h_v, h_k, ckpt_interval, q, k, v,
+                        beta, g, S_init, S_final, o, checkpoints, ws, scale,
+                        flags, stream);
 }

@@ -23,6 +23,9 @@
  *   gdn_prefill_chunked  run the same recurrence over a long sequence in
  *                        chunks and emit fp32 state checkpoints at every
  *                        multiple of the checkpoint interval.
+ *   gdn_prefill_chunked_noalloc  the same with the library's fixed scratch
+ *                        array as workspace, for callers that cannot
+ *                        allocate.
  *
  * The rule (Yang, Kautz & Hatamizadeh, "Gated Delta Networks: Improving
  * Mamba2 with Delta Rule", ICLR 2025, Sec. 3), per value head with state S
@@ -58,7 +61,8 @@
  *
  * Ownership: the caller allocates every buffer (device memory unless stated
  * "host"); the library allocates, frees and synchronises nothing and keeps no
- * state between calls.  All pointers to device memory must be 4-byte aligned
+ * state between calls, except the fixed scratch array that
+ * gdn_prefill_chunked_noalloc uses as its workspace.  All pointers to device memory must be 4-byte aligned
  * (16-byte aligned for best speed).
  *
  * Errors: every argument error is found on the host, before any HIP call, and
@@ -273,6 +277,30 @@ int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
                         const float* g, const float* S_init, float* S_final,
                         float* o, float* checkpoints, void* workspace,
                         size_t ws_bytes, float scale, int flags, void* stream);
+
+/*
+ * gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a fixed array inside
+ * the library, GDN_PREFILL_SCRATCH_BYTES per GPU (each GPU the library runs
+ * on holds its own copy until the process ends); this entry point calls no
+ * allocator.  Every call on one GPU uses that GPU's array, so calls that
+ * overlap in time on one GPU (different streams, or several host threads
+ * without ordering) race and give undefined results: order them on one
+ * stream or with events.  Nothing in the array needs to start at zero.
+ * Sizes whose workspace (gdn_prefill_workspace_bytes) exceeds the array
+ * return GDN_EWORKSPACE.  Arguments, results and the other errors are those
+ * of gdn_prefill_chunked; the results are bit for bit the same.
+ */
+#define GDN_PREFILL_SCRATCH_BYTES (64u << 20)
+int gdn_prefill_chunked_noalloc(int32_t n_seqs, int32_t seq_len, int32_t h_v,
+                                int32_t h_k, int32_t d_k, int32_t d_v,
+                                int32_t ckpt_interval, const void* q,
+                                const void* k, const void* v, int in_dtype,
+                                const float* beta, const float* g,
+                                const float* S_init, float* S_final, float* o,
+                                float* checkpoints, float scale, int flags,
+                                void* stream);
 
 /*
  * KDA: the sibling rule with one decay per key channel (Kimi Delta

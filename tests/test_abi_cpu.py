@@ -290,6 +290,35 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert b"prefill" in gdn.lib.gdn_last_error()
 
 
+def _prefill_noalloc(**over):
+    a = dict(n_seqs=1, L=256, hv=2, hk=1, dk=128, dv=128, interval=128,
+             q=_Fake(), k=_Fake(), v=_Fake(), beta=_Fake(gdn.GDN_F32),
+             g=_Fake(gdn.GDN_F32), Si=None, Sf=_Fake(gdn.GDN_F32),
+             o=_Fake(gdn.GDN_F32), ck=_Fake(gdn.GDN_F32))
+    a.update(over)
+    return gdn.prefill_chunked_noalloc(
+        a["n_seqs"], a["L"], a["hv"], a["hk"], a["dk"], a["dv"], a["q"],
+        a["k"], a["v"], a["beta"], a["g"], a["Si"], a["Sf"], a["o"], a["ck"],
+        ckpt_interval=a["interval"], stream=0, raw_status=True)
+
+
+def test_prefill_noalloc_rejects_bad_arguments_on_host():
+    """The entry point without a workspace checks every argument, and that
+    the fixed scratch array is large enough, before its first HIP call."""
+    ws = gdn.prefill_workspace_bytes(1, 32768, 32, 32, 128, 128)
+    assert ws > gdn.PREFILL_SCRATCH_BYTES
+    assert _prefill_noalloc(L=32768, hv=32, hk=32,
+                            interval=8192) == gdn.GDN_EWORKSPACE
+    assert b"scratch" in gdn.lib.gdn_last_error()
+    assert _prefill_noalloc(dk=64, dv=64) == gdn.GDN_EUNSUPPORTED
+    assert _prefill_noalloc(hv=3, hk=2) == gdn.GDN_EINVAL
+    assert _prefill_noalloc(interval=100) == gdn.GDN_EINVAL
+    assert _prefill_noalloc(o=None) == gdn.GDN_EINVAL
+    assert _prefill_noalloc(q=_Fake(gdn.GDN_F32), k=_Fake(gdn.GDN_F32),
+                            v=_Fake(gdn.GDN_F32)) == gdn.GDN_EUNSUPPORTED
+    assert _prefill_noalloc(q=_Fake(addr=(1 << 20) + 8)) == gdn.GDN_EINVAL
+
+
 def test_missing_library_fails_loudly(tmp_path):
     """Without the built library the package refuses to import: there is no
     fallback path that computes anything elsewhere."""
