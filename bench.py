@@ -87,6 +87,13 @@ def alg_bytes_fused(t_lane, m_prev):
                           for m in m_prev)
 
 
+def alg_bytes_commit_one(m):
+    """Bytes of a commit of one lane-layer with m > 0 records replayed."""
+    s = HV * DK * DV * 4
+    rec = HK * DK * 4 + HV * DV * 4 + HV * 8
+    return (2 * s + rec * int(m)) if m > 0 else 0
+
+
 WINDOW_SOURCES = ("gdn_window.hip", "gdn_window_mfma.hip",
                   "gdn_window_common.h", "gdn_mfma_util.h", "gdn_step.h")
 
@@ -413,6 +420,288 @@ def bench_snapshot(reps=5):
             "from_pinned_host_GBps": nbytes / (h2d * 1e-3) / 1e9}
 
 
+def _dev_bf16(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+
+
+def bench_token_verify(reps=20, warmup=3):
+    """The token-by-token verify at the headline batch (8 lanes x 48 layers x
+    32/16 heads, d = 128, T = 16): the same windows declared with a window
+    stride t_max = 17, which routes them to the kernel that evaluates the
+    rule one token at a time and holds every intermediate state (the design
+    that the block form replaces at these shapes).  Event-timed."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    tm = T + 1
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, tm)
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, tm)
+    t_lane = np.full(N, T, dtype=np.int32)
+    pool = []
+    for p in range(4):
+        w = gs.window_inputs(shape, (12, p), t_lane=t_lane)
+        pool.append((_dev_bf16(w.q, dev), _dev_bf16(w.k, dev),
+                     _dev_bf16(w.v, dev), torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(w.g).to(dev)))
+    S = torch.from_numpy(gs.initial_state(shape, (12, 0))).to(dev)
+    o = torch.empty((NL, N, tm, HV, DV), device=dev)
+    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for r in range(warmup):
+        gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r, (a, b) in enumerate(evs):
+        a.record(stream)
+        gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    bv = alg_bytes_verify(t_lane)
+    return {"workload": "verify of 8 lanes x 48 layers x 32/16 heads, d=128, "
+                        "T=16 on the token-by-token kernel (window stride 17)",
+            "verify_ms": ms,
+            "updates_per_s": int(t_lane.sum()) * NL * HV / (ms * 1e-3),
+            "verify_hbm_frac": bv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+# Synthetic workloads of the speculative-decoding round, timed as chains of
+# fused rounds (gdn_commit_verify: round r commits the accepted prefix of the
+# same state set's previous window and verifies window r).
+CHAIN_CONFIGS = {
+    "one_lane_100_rounds": dict(
+        n_lanes=1, t_max=16, rounds=400, n_sets=4, pool=8, t_kind="fixed",
+        m_kind="uniform",
+        workload="1 lane x 48 layers x 32 value / 16 key heads, d=128, T=16, "
+                 "m ~ U{0..16}; 4 state sets (96 MiB each) rotated so that "
+                 "the 256 MB Infinity Cache cannot hold a set between its "
+                 "rounds; 100 chained rounds per set"),
+    "eight_lanes_ragged": dict(
+        n_lanes=8, t_max=16, rounds=64, n_sets=1, pool=4, t_kind="ragged",
+        m_kind="uniform",
+        workload="8 lanes x 48 layers x 32/16 heads, d=128, per-lane window "
+                 "T ~ U{1..16} and m ~ U{0..T} drawn every round, 64 chained "
+                 "rounds"),
+    "twelve_lanes_t6_256_rounds": dict(
+        n_lanes=12, t_max=6, rounds=256, n_sets=1, pool=4, t_kind="fixed",
+        m_kind="binomial",
+        workload="12 lanes x 48 layers x 32/16 heads, d=128, T=6, "
+                 "m ~ Binomial(6, 0.7), 256 chained rounds"),
+}
+
+
+def bench_chain(name, cfg, warmup=4, sample_layer=17):
+    """One synthetic workload as a chain of fused rounds, event-timed over
+    the whole chain.  Returns the timing record and, for the parity check of
+    the CPU leg, the sampled chain (one layer of the state set that ran the
+    last round): its inputs, initial state, final state and last outputs.
+    Also checks on the GPU that the final commit of that layer is bit for
+    bit the state a verify with debug states held after the accepted
+    prefix."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    Nl, tm, R, ns, P = (cfg["n_lanes"], cfg["t_max"], cfg["rounds"],
+                        cfg["n_sets"], cfg["pool"])
+    key = 20 + list(CHAIN_CONFIGS).index(name)
+    shape = gs.WindowShape(NL, Nl, HV, HK, DK, DV, tm)
+    dims = gdn.Dims.of(NL, Nl, HV, HK, DK, DV, tm)
+    full = np.full(Nl, tm, dtype=np.int32)
+    pool_np, pool = [], []
+    for p in range(P):
+        w = gs.window_inputs(shape, (key, p), t_lane=full)
+        pool_np.append(w)
+        pool.append((_dev_bf16(w.q, dev), _dev_bf16(w.k, dev),
+                     _dev_bf16(w.v, dev), torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(w.g).to(dev)))
+    if cfg["t_kind"] == "ragged":
+        t_all = [gs.window_lengths(Nl, tm, (key, r)) for r in range(R)]
+    else:
+        t_all = [full.copy() for _ in range(R)]
+    if cfg["m_kind"] == "binomial":
+        m_all = [gs.accepted_binomial(t_all[r], 0.7, (key, r)) for r in range(R)]
+    else:
+        m_all = [gs.accepted_uniform(t_all[r], (key, r)) for r in range(R)]
+    S0 = [gs.initial_state(gs.WindowShape(NL, Nl, HV, HK, DK, DV, 1),
+                           (key, 1000 + j)) for j in range(ns)]
+    S = [torch.from_numpy(x).to(dev) for x in S0]
+    nrec = gdn.records_bytes(dims)
+    recs = [[torch.empty(nrec, dtype=torch.uint8, device=dev) for _ in range(2)]
+            for _ in range(ns)]
+    o = torch.empty((NL, Nl, tm, HV, DV), device=dev)
+    zero = np.zeros(Nl, dtype=np.int32)
+
+    def run(n_rounds, evs=None):
+        prev = [None] * ns
+        for r in range(n_rounds):
+            j = r % ns
+            cur = (r // ns) % 2
+            t_prev, m_prev = (zero, zero) if prev[j] is None else prev[j]
+            if evs is not None and r == 0:
+                evs[0].record(stream)
+            gdn.commit_verify(dims, m_prev, t_prev, recs[j][1 - cur],
+                              t_all[r], *pool[r % P], S[j], o, recs[j][cur],
+                              stream=stream)
+            prev[j] = (t_all[r], m_all[r])
+        if evs is not None:
+            evs[1].record(stream)
+        return prev
+
+    run(warmup)
+    torch.cuda.synchronize()
+    for j in range(ns):
+        S[j].copy_(torch.from_numpy(S0[j]))
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    prev = run(R, ev)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    # end of every chain: commit the last window's accepted prefix
+    js = (R - 1) % ns
+    ls = sample_layer
+    S_pre = S[js][ls:ls + 1].clone()
+    for j in range(ns):
+        last = R - 1 - ((R - 1 - j) % ns)
+        gdn.commit(dims, prev[j][1], prev[j][0], recs[j][(last // ns) % 2],
+                   S[j], stream=stream)
+    o_last = o[ls:ls + 1].cpu().numpy()
+    S_end = S[js][ls:ls + 1].cpu().numpy()
+    # bit-exact replay on the sampled layer: verify the last window of set
+    # js with debug states from the state before its final commit
+    d1 = gdn.Dims.of(1, Nl, HV, HK, DK, DV, tm)
+    inp = [x[ls:ls + 1] for x in pool[(R - 1) % P]]
+    dbg = torch.empty((1, Nl, tm, HV, DK, DV), device=dev)
+    o1 = torch.empty((1, Nl, tm, HV, DV), device=dev)
+    r1 = torch.empty(gdn.records_bytes(d1), dtype=torch.uint8, device=dev)
+    gdn.verify(d1, t_all[R - 1], *inp, S_pre, o1, r1, dbg, stream=stream)
+    torch.cuda.synchronize()
+    dbg_np, pre_np = dbg.cpu().numpy(), S_pre.cpu().numpy()
+    bitexact = True
+    for n in range(Nl):
+        mm = int(m_all[R - 1][n])
+        want = pre_np[0, n] if mm == 0 else dbg_np[0, n, mm - 1]
+        bitexact &= bool(np.array_equal(S_end[0, n], want))
+    upd = sum(int(t.sum()) for t in t_all) * NL * HV
+    m_prev_seq = [zero if r < ns else m_all[r - ns] for r in range(R)]
+    byts = sum(alg_bytes_fused(t_all[r], m_prev_seq[r]) for r in range(R))
+    rec = {"workload": cfg["workload"], "rounds": R, "ms_total": ms,
+           "ms_per_round": ms / R, "updates_per_s": upd / (ms * 1e-3),
+           "alg_bytes_per_round": byts / R,
+           "alg_GBps": byts / (ms * 1e-3) / 1e9,
+           "hbm_roofline_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "bitexact_replay_sampled_layer": bitexact,
+           "parity": None}
+    sample = {"name": name, "layer": ls, "set": js, "rounds": [
+        r for r in range(R) if r % ns == js], "pool_np": pool_np, "P": P,
+        "t_all": t_all, "m_all": m_all, "S0": S0[js][ls:ls + 1],
+        "S_end": S_end, "o_last": o_last}
+    del S, recs, pool, o, dbg
+    torch.cuda.empty_cache()
+    return rec, sample
+
+
+def _layer_f64(w, ls):
+    """fp64 inputs of one layer of a window input set, shapes [1, ...]."""
+    q, k, v, b, g = w.as_f64()
+    return tuple(a[ls:ls + 1] for a in (q, k, v, b, g))
+
+
+def oracle_chain_parity(sample):
+    """The fp64 oracle over a sampled chain (one layer of one state set,
+    every round of that set): the final state and the last round's outputs,
+    against the GPU's.  Max block-relative error per (lane, head) block, and
+    the oracle's own throughput on this sample."""
+    import oracle
+    S = sample["S0"].astype(np.float64)
+    rounds = sample["rounds"]
+    t0 = time.perf_counter()
+    upd = 0
+    o_ref = None
+    for r in rounds:
+        q, k, v, b, g = _layer_f64(sample["pool_np"][r % sample["P"]],
+                                   sample["layer"])
+        t_lane = sample["t_all"][r]
+        if r == rounds[-1]:
+            o_ref, _ = oracle.verify(q, k, v, b, g, S, t_lane)
+        S = oracle.commit(q, k, v, b, g, S, sample["m_all"][r])
+        upd += int(t_lane.sum()) * HV
+    dt = time.perf_counter() - t0
+
+    def blk(x, ref, axes):
+        x = np.moveaxis(np.asarray(x, np.float64), axes, range(len(axes)))
+        ref = np.moveaxis(np.asarray(ref, np.float64), axes, range(len(axes)))
+        nb = int(np.prod(x.shape[:len(axes)]))
+        x, ref = x.reshape(nb, -1), ref.reshape(nb, -1)
+        den = np.max(np.abs(ref), axis=1)
+        return float(np.max(np.max(np.abs(x - ref), axis=1) /
+                            np.where(den > 0, den, 1.0)))
+
+    o_gpu = np.array(sample["o_last"], dtype=np.float64)
+    t_last = sample["t_all"][rounds[-1]]
+    for n, t in enumerate(t_last):
+        o_gpu[:, n, t:] = 0.0
+        o_ref[:, n, t:] = 0.0
+    return {"sample": "layer %d, state set %d: %d chained rounds"
+                      % (sample["layer"], sample["set"], len(rounds)),
+            "max_rel_err_S": blk(sample["S_end"], S, (0, 1, 2)),
+            "max_rel_err_o": blk(o_gpu, o_ref, (0, 1, 3)),
+            "oracle_s": dt, "oracle_updates_per_s": upd / dt}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _parse_clocks(text):
+    try:
+        d = json.loads(text)
+    except ValueError:
+        return None
+    for card in d.values():
+        if isinstance(card, dict):
+            return {k.strip(" :"): v for k, v in card.items()
+                    if any(x in k.lower() for x in ("sclk", "mclk", "fclk"))}
+    return None
+
+
+def gpu_clocks_under_load(busy, seconds=1.5):
+    """Engine and memory clocks read by rocm-smi (a child process) while
+    `busy()` keeps the GPU running the headline kernel; None if rocm-smi is
+    unavailable."""
+    import subprocess
+    import torch
+    try:
+        pr = subprocess.Popen(["rocm-smi", "--showclocks", "--json"],
+                              stdout=subprocess.PIPE,
+                              stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while pr.poll() is None and time.perf_counter() - t0 < seconds + 30:
+        busy()
+        torch.cuda.synchronize()
+    try:
+        out, _ = pr.communicate(timeout=30)
+    except subprocess.SubprocessError:
+        pr.kill()
+        return None
+    return _parse_clocks(out)
+
+
 def cpu_baseline(rounds=16):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: `rounds` chained rounds (verify + commit) of the full
@@ -431,11 +720,28 @@ def cpu_baseline(rounds=16):
         S = oracle.commit(q, k, v, b, g, S, m)
         dt += time.perf_counter() - t0
     upd = rounds * NL * N * T * HV
+    cores = oracle.num_threads()
+    # the same round at one thread: a single chained round of the batch
+    w = gs.window_inputs(shape, (9, rounds))
+    m = gs.accepted_uniform(w.t_lane, (9, rounds))
+    q, k, v, b, g = w.as_f64()
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.verify(q, k, v, b, g, S, w.t_lane)
+        oracle.commit(q, k, v, b, g, S, m)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
     return {"value": upd / dt, "unit": "head-token updates/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d chained rounds (verify + commit) of the full "
                       "48-layer x 8-lane batch, T=16, fp64 C oracle with "
-                      "OpenMP over chains; %.1f s of oracle time" % (rounds, dt)}
+                      "OpenMP over chains; %.1f s of oracle time" % (rounds, dt),
+            "one_thread": {"value": NL * N * T * HV / dt1, "cores": 1,
+                           "sample": "1 round (verify + commit) of the same "
+                                     "batch, %.1f s" % dt1}}
 
 
 def main():
@@ -455,6 +761,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the window-length sweep")
     ap.add_argument("--no-kda", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 1-lane, ragged 8-lane and 12-lane chains")
+    ap.add_argument("--no-token-verify", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -578,6 +887,11 @@ def main():
 
         ms, evs = timed(stepf, 2)
         ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+        def busy():
+            for s_ in range(20):
+                stepf(args.warmup + s_ % args.steps)
+        clocks = gpu_clocks_under_load(busy)
         mp = [m_prev_of(args.warmup + s) for s in range(args.steps)]
         bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in mp]))
         res["fused"] = {
@@ -586,7 +900,7 @@ def main():
             "kernel_ms": ms_f,
             "alg_GBps": bf / (ms_f * 1e-3) / 1e9,
             "traffic": measured_traffic("fused_kernel"),
-            "alg_bytes_per_step": bf}
+            "alg_bytes_per_step": bf, "gpu_clocks_under_load": clocks}
         del S, recs
 
     head = "fused" if "fused" in res else "two-call"
@@ -618,7 +932,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state / bf16 q,k,v",
+        "dtype": "f32 state / bf16 q,k,v; state products on bf16 MFMA as "
+                 "split-bf16 pairs (hi + lo, ~2^-17 rel.), f32 accumulate",
         "data": "synthetic (seeded gdn_synth inputs; S0 ~ N(0, 0.01))",
         "config": {"workload": "verify+commit round: 8 lanes x 48 layers x "
                                "32 value / 16 key heads, d_k=d_v=128, T=16, "
@@ -629,6 +944,15 @@ def main():
         "roofline": roof,
         "paths": res,
     }
+    samples = []
+    if not args.no_configs:
+        out["configs"] = {}
+        for name, cfg in CHAIN_CONFIGS.items():
+            rec, smp = bench_chain(name, cfg)
+            out["configs"][name] = rec
+            samples.append(smp)
+    if not args.no_token_verify:
+        out["token_by_token_verify"] = bench_token_verify()
     if not args.no_prefill:
         out["prefill"] = bench_prefill()
     if not args.no_snapshot:
@@ -641,6 +965,9 @@ def main():
         out["kda"] = bench_kda()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
+        for smp in samples:
+            out["configs"][smp["name"]]["parity"] = oracle_chain_parity(smp)
+    out["gpu_clocks"] = res.get("fused", {}).get("gpu_clocks_under_load")
     print(json.dumps(out), flush=True)
 
 

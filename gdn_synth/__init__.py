@@ -132,6 +132,13 @@ def initial_state(shape: WindowShape, key: tuple, sigma: float = 0.1
             * sigma).astype(np.float32)
 
 
+def window_lengths(n_lanes: int, t_max: int, key: tuple) -> np.ndarray:
+    """Ragged per-lane window lengths T ~ Uniform{1..t_max} (MTP windows of
+    1..5 and DFlash windows of up to 15 drafts plus the anchor)."""
+    r = rng(_STREAM_T, 7, *key)
+    return r.integers(1, t_max + 1, size=n_lanes).astype(np.int32)
+
+
 def accepted_uniform(t_lane: np.ndarray, key: tuple) -> np.ndarray:
     """m_lane ~ Uniform{0..T_lane} per lane."""
     r = rng(_STREAM_M, *key)

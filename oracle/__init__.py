@@ -90,6 +90,8 @@ def _load():
         lib.oracle_prefill.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
+        lib.oracle_set_num_threads.argtypes = [i]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -123,6 +125,11 @@ def _d(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the OpenMP loops over independent chains."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def verify(q, k, v, beta, g, S0, t_lane, scale=1.0, l2norm=True,

@@ -475,3 +475,14 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops over independent chains (the CPU
+ * baseline is timed at one thread and at all cores).  Not arithmetic: every
+ * chain runs the same loop nest whatever the count. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
