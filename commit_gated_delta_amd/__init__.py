@@ -15,7 +15,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "libgdn.so")
+# GDN_LIBRARY names another build of the same library (the CPU tests load
+# a sanitizer build of the host code this way).
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "_build",
+                                                         "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_BF16, GDN_F32 = 0, 1
@@ -90,12 +93,12 @@ def _load_library():
     for fn in (lib.gdn_state_snapshot, lib.gdn_state_restore):
         fn.argtypes = [dp, i32, ip, vp, vp, vp]
         fn.restype = ctypes.c_int
-    lib.gdn_prefill_workspace_bytes.argtypes = [i32] * 6
+    lib.gdn_prefill_workspace_bytes.argtypes = [i32] * 7
     lib.gdn_prefill_workspace_bytes.restype = sz
-    lib.gdn_prefill_chunked.argtypes = [i32] * 7 + [vp] * 3 + [ctypes.c_int] + [
+    lib.gdn_prefill_chunked.argtypes = [i32] * 8 + [vp] * 3 + [ctypes.c_int] + [
         vp] * 7 + [sz, f, ctypes.c_int, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
-    lib.gdn_prefill_chunked_noalloc.argtypes = [i32] * 7 + [vp] * 3 + [
+    lib.gdn_prefill_chunked_noalloc.argtypes = [i32] * 8 + [vp] * 3 + [
         ctypes.c_int] + [vp] * 6 + [f, ctypes.c_int, vp]
     lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.gdn_strerror.argtypes = [ctypes.c_int]
@@ -297,20 +300,21 @@ def state_restore(dims: Dims, lanes, snapshot, S, stream=None,
     _check(st, "gdn_state_restore")
 
 
-def prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k, d_v) -> int:
+def prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k, d_v,
+                            chunk=64) -> int:
     return int(lib.gdn_prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k,
-                                               d_v))
+                                               d_v, chunk))
 
 
 def prefill_chunked(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v, beta, g,
                     S_init, S_final, o, checkpoints, workspace,
                     ckpt_interval=8192, scale=1.0, l2norm=True, stream=None,
-                    raw_status=False):
+                    raw_status=False, chunk=64):
     """gdn_prefill_chunked on torch tensors."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_prefill_chunked(
-        n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, _ptr(q), _ptr(k),
-        _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
+        n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk, ckpt_interval, _ptr(q),
+        _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
         _ptr(S_final), _ptr(o), _ptr(checkpoints), _ptr(workspace), ws_bytes,
         float(scale), GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
     if raw_status:
@@ -321,13 +325,13 @@ def prefill_chunked(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v, beta, g,
 def prefill_chunked_noalloc(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v,
                             beta, g, S_init, S_final, o, checkpoints,
                             ckpt_interval=8192, scale=1.0, l2norm=True,
-                            stream=None, raw_status=False):
+                            stream=None, raw_status=False, chunk=64):
     """gdn_prefill_chunked_noalloc: the prefill with the library's fixed
     scratch array as its workspace (no allocation; calls that overlap on
     one GPU race)."""
     st = lib.gdn_prefill_chunked_noalloc(
-        n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, _ptr(q), _ptr(k),
-        _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
+        n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk, ckpt_interval, _ptr(q),
+        _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
         _ptr(S_final), _ptr(o), _ptr(checkpoints), float(scale),
         GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
     if raw_status:

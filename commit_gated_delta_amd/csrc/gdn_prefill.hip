@@ -1,6 +1,8 @@
 // gdn_prefill.hip -- chunked prefill of the gated delta rule on gfx950 MFMA.
 //
-// Block (WY/UT) form of the rule over chunks of C = 64 tokens: Yang et al.,
+// Block (WY/UT) form of the rule over chunks of C = 16, 32 or 64 tokens, each
+// chunk in a 64-row tile (rows past a short chunk are inert, see ws_bytes):
+// Yang et al.,
 // "Parallelizing Linear Transformers with the Delta Rule over Sequence
 // Length" (NeurIPS 2024), Sec. 3 (the UT transform), with the per-token decay
 // of Gated DeltaNet (ICLR 2025).  In the stored orientation H = S^T (d_k x d_v)
@@ -73,6 +75,7 @@ typedef uint16_t u16;
 
 struct PDims {
   int n_seqs, L, Hv, Hk, group, n_chunks;
+  int chunk;          // tokens per chunk: 16, 32 or 64 (<= kC)
   int ckpt_interval;  // 0: no checkpoints
   float scale;
   int l2norm;
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void p1_kernel(
   const int c = (bid / d.Hv) % d.n_chunks;
   const int s = bid / (d.Hv * d.n_chunks);
   const int kh = h / d.group;
-  const int t0 = c * kC;
-  const int nv = min(kC, d.L - t0);  // valid rows of this chunk
+  const int t0 = c * d.chunk;
+  const int nv = min(d.chunk, d.L - t0);  // valid rows of this chunk
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int l = tid % 64;
@@ -521,6 +524,7 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
   r.Hk = __builtin_amdgcn_readfirstlane(a.Hk);
   r.group = __builtin_amdgcn_readfirstlane(a.group);
   r.n_chunks = __builtin_amdgcn_readfirstlane(a.n_chunks);
+  r.chunk = __builtin_amdgcn_readfirstlane(a.chunk);
   r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
   r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
   r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
@@ -794,7 +798,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
     split_pi(H[6], H[7], hw[3], lw[3]);
     publish_pair(NB, 3);
     kh_step(3);
-    const int t0 = c * kC, nv = min(kC, d.L - t0);
+    const int t0 = c * d.chunk, nv = min(d.chunk, d.L - t0);
     // checkpoint after token t0 + nv when it is a multiple of the interval
     if (d.ckpt_interval > 0 && ckpt && (t0 + nv) % d.ckpt_interval == 0) {
       const int idx = (t0 + nv) / d.ckpt_interval - 1;
@@ -868,8 +872,8 @@ static __device__ __attribute__((noinline)) void p2_stage(
   auto& SVt = p2lds.SVt;
   auto& Vec = p2lds.Vec;
   auto load = [&](int c, KvTransit& tr) {
-    const int t0 = c * kC;
-    const int last = min(kC, d.L - t0) - 1;
+    const int t0 = c * d.chunk;
+    const int last = min(d.chunk, d.L - t0) - 1;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + l;
@@ -980,8 +984,8 @@ static __device__ __attribute__((noinline)) void p2_out(
   // clamped to the last one)
   const int u = 128 * tile + 64 * ow + l;
   auto warm = [&](int c) -> uint32_t {
-    const int t0 = c * kC;
-    const int last = min(kC, d.L - t0) - 1;
+    const int t0 = c * d.chunk;
+    const int last = min(d.chunk, d.L - t0) - 1;
     const int row = min((u & 127) >> 1, last), half = u & 1;
     const uint32_t* p;
     if (u < 128)
@@ -996,8 +1000,8 @@ static __device__ __attribute__((noinline)) void p2_out(
     return *p;
   };
   auto ops_load = [&](int c, OutOps& op) {
-    const int t0 = c * kC;
-    const int last = min(kC, d.L - t0) - 1;
+    const int t0 = c * d.chunk;
+    const int last = min(d.chunk, d.L - t0) - 1;
     const uint32_t ra = ((uint32_t)(t0 + min(16 * mA + n, last)) * d.Hk + kh) * kD + 8 * g;
     const uint32_t rb = ((uint32_t)(t0 + min(16 * mB + n, last)) * d.Hk + kh) * kD + 8 * g;
 #pragma unroll
@@ -1015,7 +1019,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   };
   auto outputs = [&](int c, const OutOps& op) {
     const int hb = c % 3, bb = c % 3;
-    const int t0 = c * kC, nv = min(kC, d.L - t0);
+    const int t0 = c * d.chunk, nv = min(d.chunk, d.L - t0);
     f32x4 QA = {0.f, 0.f, 0.f, 0.f}, QB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -1129,22 +1133,31 @@ static bool misaligned(const void* p, size_t a) {
   return ((uintptr_t)p % a) != 0;
 }
 
-static size_t ws_bytes(int32_t n_seqs, int32_t L, int32_t Hv) {
-  const size_t n_chunks = ((size_t)L + kC - 1) / kC;
+// Chunks of 16 and 32 tokens run in the 64-row tiles of both kernels with
+// the rows past the chunk inert, exactly as the tail chunk of a sequence:
+// their loads repeat the last valid row, P1 gives them beta = 0 and gate 0,
+// so their X, V_new and D rows are exact zeros and T is the identity on
+// them (L has zero rows there); they add nothing to the state and their
+// output rows are never stored.
+static size_t ws_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
+  const size_t n_chunks = ((size_t)L + C - 1) / C;
   return (size_t)n_seqs * n_chunks * Hv * WsLayout::kBytes;
 }
 
 static int check_sizes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t Hk,
-                       int32_t dk, int32_t dv) {
-  if (n_seqs < 1 || L < 1 || Hv < 1 || Hk < 1 || Hv % Hk != 0) {
+                       int32_t dk, int32_t dv, int32_t C) {
+  if (n_seqs < 1 || L < 1 || Hv < 1 || Hk < 1 || Hv % Hk != 0 || C < 1) {
     return fail(GDN_EINVAL, "prefill: sizes out of range");
+  }
+  if (C != 16 && C != 32 && C != kC) {
+    return fail(GDN_EUNSUPPORTED, "prefill: chunk must be 16, 32 or 64");
   }
   if (dk != kD || dv != kD) {
     return fail(GDN_EUNSUPPORTED, "prefill: d_k = d_v = 128 only");
   }
   if ((double)L * Hv * kD >= 2147483648.0 || (double)L * Hk * kD >= 2147483648.0)
     return fail(GDN_EUNSUPPORTED, "prefill: seq_len x heads x 128 must stay below 2^31");
-  const double blocks = (double)n_seqs * ((L + kC - 1) / kC) * Hv;
+  const double blocks = (double)n_seqs * ((L + C - 1) / C) * Hv;
   const double elems = (double)n_seqs * L * Hv * kD;
   if (blocks > (double)INT_MAX || elems > 4.0e15) {
     return fail(GDN_EINVAL, "prefill: sizes overflow");
@@ -1158,9 +1171,10 @@ using namespace gdnp;
 
 extern "C" size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
                                               int32_t h_v, int32_t h_k,
-                                              int32_t d_k, int32_t d_v) {
-  if (check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v) != GDN_OK) return 0;
-  return ws_bytes(n_seqs, seq_len, h_v);
+                                              int32_t d_k, int32_t d_v,
+                                              int32_t chunk) {
+  if (check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk) != GDN_OK) return 0;
+  return ws_bytes(n_seqs, seq_len, h_v, chunk);
 }
 
 // Workspace of the entry point that allocates nothing: a fixed device
@@ -1201,13 +1215,13 @@ static int scratch_address(void** out) {
 
 // Every argument check except those of the workspace pointer; no HIP call.
 static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
-                      int32_t h_k, int32_t d_k, int32_t d_v,
+                      int32_t h_k, int32_t d_k, int32_t d_v, int32_t chunk,
                       int32_t ckpt_interval, const void* q, const void* k,
                       const void* v, int in_dtype, const float* beta,
                       const float* g, const float* S_init, float* S_final,
                       float* o, float* checkpoints, size_t ws_size,
                       int flags) {
-  int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v);
+  int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk);
   if (rc != GDN_OK) return rc;
   if (!q || !k || !v || !beta || !g || !S_final || !o) {
     return fail(GDN_EINVAL, "prefill: required pointer is NULL");
@@ -1218,8 +1232,8 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
   if (flags & ~GDN_FLAG_L2NORM_QK) {
     return fail(GDN_EINVAL, "prefill: unknown flag bits");
   }
-  if (checkpoints && (ckpt_interval < kC || ckpt_interval % kC != 0)) {
-    return fail(GDN_EINVAL, "prefill: ckpt_interval must be a positive multiple of 64");
+  if (checkpoints && (ckpt_interval < chunk || ckpt_interval % chunk != 0)) {
+    return fail(GDN_EINVAL, "prefill: ckpt_interval must be a positive multiple of the chunk");
   }
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 2) ||
       misaligned(beta, 4) || misaligned(g, 4) || misaligned(S_final, 4) ||
@@ -1227,7 +1241,7 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
       (checkpoints && misaligned(checkpoints, 4))) {
     return fail(GDN_EINVAL, "prefill: misaligned pointer");
   }
-  if (ws_size < ws_bytes(n_seqs, seq_len, h_v)) {
+  if (ws_size < ws_bytes(n_seqs, seq_len, h_v, chunk)) {
     return fail(GDN_EWORKSPACE, "prefill: workspace too small");
   }
   return GDN_OK;
@@ -1235,7 +1249,7 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
 
 // Launches P1 and P2 (arguments already checked).
 static int prefill_launch(
-    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k,
+    int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t chunk,
     int32_t ckpt_interval, const void* q, const void* k, const void* v,
     const float* beta, const float* g, const float* S_init, float* S_final,
     float* o, float* checkpoints, void* workspace, float scale, int flags,
@@ -1246,7 +1260,8 @@ static int prefill_launch(
   dd.Hv = h_v;
   dd.Hk = h_k;
   dd.group = h_v / h_k;
-  dd.n_chunks = (seq_len + kC - 1) / kC;
+  dd.chunk = chunk;
+  dd.n_chunks = (seq_len + chunk - 1) / chunk;
   dd.ckpt_interval = checkpoints ? ckpt_interval : 0;
   dd.scale = scale;
   dd.l2norm = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
@@ -1281,44 +1296,45 @@ static int prefill_launch(
 
 extern "C" int gdn_prefill_chunked(
     int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t d_k,
-    int32_t d_v, int32_t ckpt_interval, const void* q, const void* k,
-    const void* v, int in_dtype, const float* beta, const float* g,
-    const float* S_init, float* S_final, float* o, float* checkpoints,
-    void* workspace, size_t ws_size, float scale, int flags, void* stream) {
-  int rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, q,
-                      k, v, in_dtype, beta, g, S_init, S_final, o, checkpoints,
-                      ws_size, flags);
+    int32_t d_v, int32_t chunk, int32_t ckpt_interval, const void* q,
+    const void* k, const void* v, int in_dtype, const float* beta,
+    const float* g, const float* S_init, float* S_final, float* o,
+    float* checkpoints, void* workspace, size_t ws_size, float scale,
+    int flags, void* stream) {
+  int rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk,
+                      ckpt_interval, q, k, v, in_dtype, beta, g, S_init,
+                      S_final, o, checkpoints, ws_size, flags);
   if (rc != GDN_OK) return rc;
   if (!workspace) return fail(GDN_EINVAL, "prefill: required pointer is NULL");
   if (misaligned(workspace, 256)) {
     return fail(GDN_EINVAL, "prefill: misaligned pointer");
   }
-  return prefill_launch(n_seqs, seq_len, h_v, h_k, ckpt_interval, q, k, v,
-                        beta, g, S_init, S_final, o, checkpoints, workspace,
+  return prefill_launch(n_seqs, seq_len, h_v, h_k, chunk, ckpt_interval, q, k,
+                        v, beta, g, S_init, S_final, o, checkpoints, workspace,
                         scale, flags, stream);
 }
 
 extern "C" int gdn_prefill_chunked_noalloc(
     int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t d_k,
-    int32_t d_v, int32_t ckpt_interval, const void* q, const void* k,
-    const void* v, int in_dtype, const float* beta, const float* g,
-    const float* S_init, float* S_final, float* o, float* checkpoints,
-    float scale, int flags, void* stream) {
-  int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v);
+    int32_t d_v, int32_t chunk, int32_t ckpt_interval, const void* q,
+    const void* k, const void* v, int in_dtype, const float* beta,
+    const float* g, const float* S_init, float* S_final, float* o,
+    float* checkpoints, float scale, int flags, void* stream) {
+  int rc = check_sizes(n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk);
   if (rc != GDN_OK) return rc;
-  if (ws_bytes(n_seqs, seq_len, h_v) > kScratchBytes) {
+  if (ws_bytes(n_seqs, seq_len, h_v, chunk) > kScratchBytes) {
     return fail(GDN_EWORKSPACE,
                 "prefill (no-alloc): the workspace for these sizes exceeds the "
                 "library's fixed scratch array (GDN_PREFILL_SCRATCH_BYTES)");
   }
-  rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, ckpt_interval, q, k, v,
-                  in_dtype, beta, g, S_init, S_final, o, checkpoints,
+  rc = check_args(n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk, ckpt_interval, q,
+                  k, v, in_dtype, beta, g, S_init, S_final, o, checkpoints,
                   kScratchBytes, flags);
   if (rc != GDN_OK) return rc;
   void* ws = nullptr;
   rc = scratch_address(&ws);
   if (rc != GDN_OK) return rc;
-  return prefill_launch(n_seqs, seq_len, h_v, h_k, ckpt_interval, q, k, v,
-                        beta, g, S_init, S_final, o, checkpoints, ws, scale,
+  return prefill_launch(n_seqs, seq_len, h_v, h_k, chunk, ckpt_interval, q, k,
+                        v, beta, g, S_init, S_final, o, checkpoints, ws, scale,
                         flags, stream);
 }

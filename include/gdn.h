@@ -153,10 +153,17 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
  * ReplaySSM commit (ReplaySSM section of the review): for every lane with
  * m_lane[lane] > 0, replay records[0:m] from S (which must still hold the S0
  * that the matching gdn_verify read) and store S_m into S in place.  Lanes
- * with m = 0 are neither read nor written.  S_m is bit-for-bit the state that
- * gdn_verify held after its m-th token (and wrote to dbg_states), because
- * both run the same per-step instruction sequence on the recorded values; no
- * replayed steps are folded into a block product.
+ * with m = 0 are neither read nor written.  Commit never folds replayed
+ * steps into a block product: it applies the recorded steps one token at a
+ * time.  S_m is bit-for-bit the state written to dbg_states for token m:
+ *   - on the token-by-token verify (f32 inputs, d_k < 128, d_v != 128,
+ *     windows over 16 tokens) that is the state verify held after its m-th
+ *     token, formed by the same per-step instruction sequence;
+ *   - on the block-form verify (bf16, d_k = d_v = 128, t_max <= 16), which
+ *     never forms per-token states, it is the replay of verify's records
+ *     with commit's own operations.  There the emitted deltas and outputs
+ *     agree with the rule applied to those replayed states to within about
+ *     3e-7 (deltas) and 5e-6 (outputs) relative, not bit for bit.
  *   m_lane   host int32[n_lanes], 0..t_lane[lane]
  *   t_lane   host int32[n_lanes], as passed to the matching gdn_verify
  *   records  device, as filled by that gdn_verify
@@ -233,21 +240,26 @@ int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
                       float* dbg_states, float scale, int flags, void* stream);
 
 /*
- * Workspace bytes that gdn_prefill_chunked needs for these sizes (0 for
- * invalid sizes).
+ * Workspace bytes that gdn_prefill_chunked needs for these sizes and chunk
+ * length (0 for invalid or unsupported sizes).
  */
 size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
                                    int32_t h_v, int32_t h_k, int32_t d_k,
-                                   int32_t d_v);
+                                   int32_t d_v, int32_t chunk);
 
 /*
  * Chunked prefill of the gated delta rule with periodic state checkpoints
  * (interval default 8192 tokens: context_cache.checkpoint_interval in the
  * review's section "Architecture 2: context byte pool and prefix reuse").
- * Chunks of 64 tokens use the WY/UT block form of Yang et al., "Parallelizing
- * Linear Transformers with the Delta Rule over Sequence Length" (NeurIPS
- * 2024), extended with the per-token decay of Gated DeltaNet.
+ * Each chunk of `chunk` tokens is one step of the WY/UT block form of Yang
+ * et al., "Parallelizing Linear Transformers with the Delta Rule over
+ * Sequence Length" (NeurIPS 2024), extended with the per-token decay of
+ * Gated DeltaNet; the state is carried in f32 from chunk to chunk (the
+ * review's run configuration sets the prefill chunk as a parameter).
  *   n_seqs       >= 1 independent sequences of equal length seq_len >= 1
+ *   chunk        tokens per block step: 16, 32 or 64 (GDN_EUNSUPPORTED
+ *                otherwise; 64 is fastest: shorter chunks run in the same
+ *                64-row tiles with the rows past the chunk inert)
  *   q, k         device [n_seqs][seq_len][h_k][d_k] in_dtype
  *   v            device [n_seqs][seq_len][h_v][d_v] in_dtype
  *   beta, g      device f32 [n_seqs][seq_len][h_v]
@@ -258,7 +270,7 @@ size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
  *   checkpoints  device f32 [n_seqs][seq_len / ckpt_interval][h_v][d_k][d_v]
  *                or NULL: the state after every token count that is a
  *                positive multiple of ckpt_interval
- *   ckpt_interval  positive multiple of 64
+ *   ckpt_interval  positive multiple of chunk
  *   workspace    device, ws_bytes >= gdn_prefill_workspace_bytes(...);
  *                scratch owned by the caller, contents undefined on return
  *   scale, flags as for gdn_verify
@@ -271,7 +283,7 @@ size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
  * GDN_EWORKSPACE when ws_bytes is too small, GDN_EHIP when a launch fails.
  */
 int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
-                        int32_t h_k, int32_t d_k, int32_t d_v,
+                        int32_t h_k, int32_t d_k, int32_t d_v, int32_t chunk,
                         int32_t ckpt_interval, const void* q, const void* k,
                         const void* v, int in_dtype, const float* beta,
                         const float* g, const float* S_init, float* S_final,
@@ -295,7 +307,8 @@ int gdn_prefill_chunked(int32_t n_seqs, int32_t seq_len, int32_t h_v,
 #define GDN_PREFILL_SCRATCH_BYTES (64u << 20)
 int gdn_prefill_chunked_noalloc(int32_t n_seqs, int32_t seq_len, int32_t h_v,
                                 int32_t h_k, int32_t d_k, int32_t d_v,
-                                int32_t ckpt_interval, const void* q,
+                                int32_t chunk, int32_t ckpt_interval,
+                                const void* q,
                                 const void* k, const void* v, int in_dtype,
                                 const float* beta, const float* g,
                                 const float* S_init, float* S_final, float* o,

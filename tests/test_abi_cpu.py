@@ -248,6 +248,12 @@ def test_prefill_workspace_bytes():
     assert gdn.prefill_workspace_bytes(1, 100, 4, 3, 128, 128) == 0   # h_v % h_k
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 64, 64) == 0     # d != 128
     assert gdn.prefill_workspace_bytes(0, 100, 4, 4, 128, 128) == 0
+    # the same per-chunk block for every chunk length: 16-token chunks need
+    # four times the blocks of 64-token chunks
+    assert (gdn.prefill_workspace_bytes(1, 4096, 2, 2, 128, 128, 16) ==
+            4 * gdn.prefill_workspace_bytes(1, 4096, 2, 2, 128, 128, 64))
+    assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 48) == 0
+    assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 0) == 0
 
 
 def _prefill(**over):
@@ -273,7 +279,7 @@ def _prefill(**over):
                                a["g"], a["Si"], a["Sf"], a["o"], a["ck"],
                                _WS(a["ws_bytes"]),
                                ckpt_interval=a["interval"], stream=0,
-                               raw_status=True)
+                               raw_status=True, chunk=a.get("chunk", 64))
 
 
 def test_prefill_rejects_bad_arguments_on_host():
@@ -288,6 +294,12 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert _prefill(ws_bytes=1024) == gdn.GDN_EWORKSPACE
     assert _prefill(q=_Fake(addr=(1 << 20) + 8)) == gdn.GDN_EINVAL
     assert b"prefill" in gdn.lib.gdn_last_error()
+    # chunk length: 16, 32 or 64; the interval must be a multiple of it
+    assert _prefill(chunk=48) == gdn.GDN_EUNSUPPORTED
+    assert _prefill(chunk=128) == gdn.GDN_EUNSUPPORTED
+    assert _prefill(chunk=0) == gdn.GDN_EINVAL
+    assert _prefill(chunk=32, interval=48) == gdn.GDN_EINVAL
+    assert _prefill(chunk=16, interval=48, ws_bytes=1024) == gdn.GDN_EWORKSPACE
 
 
 def _prefill_noalloc(**over):
