@@ -196,7 +196,8 @@ void kda_verify_kernel(
     const int owner = t % kWaves;
     if (w == owner && act) {
       u0[t * vo_step + (uint32_t)i] = ut;
-      o0[t * vo_step + (uint32_t)i] = z.f3 * __builtin_fmaf(ut, z.kq, PQ);
+      __builtin_nontemporal_store(z.f3 * __builtin_fmaf(ut, z.kq, PQ),
+                                  o0 + t * vo_step + (uint32_t)i);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(ut, kv[r], s[r]);

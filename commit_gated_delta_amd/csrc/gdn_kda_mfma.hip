@@ -398,7 +398,9 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     ut[1][e] = U[1][e] * rke[e];
     if (t < T) {
       const uint32_t off = (uint32_t)(t * vo_step) + c0;
-      *reinterpret_cast<float2*>(o0 + off) = make_float2(O[0][e], O[1][e]);
+      // outputs are not read again by this path: nontemporal stores
+      __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
+                                  reinterpret_cast<f32x2*>(o0 + off));
       *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
     }
   }

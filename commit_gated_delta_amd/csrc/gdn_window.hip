@@ -467,7 +467,8 @@ void verify_kernel(
     const int owner = t % kWaves;  // wave that writes this token's outputs
     if (w == owner && act) {
       u0[t * vo_step + (uint32_t)i] = ut;
-      o0[t * vo_step + (uint32_t)i] = z.f3 * __builtin_fmaf(ut, z.kq, PQ);
+      __builtin_nontemporal_store(z.f3 * __builtin_fmaf(ut, z.kq, PQ),
+                                  o0 + t * vo_step + (uint32_t)i);
     }
     if constexpr (TREE) {
       if (w == owner) uth[t][x] = ut;  // read back after a later barrier
@@ -858,6 +859,24 @@ extern "C" int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
     pr.u = (const float*)(p0 + L.u);
     pr.scale = (const float2*)(p0 + L.scale);
     for (int n = 0; n < d.n_lanes; ++n) pr.m.v[n] = (uint8_t)m_prev[n];
+  }
+  // Workgroups of one launch differ in cost by lane: a lane with m_prev > 0
+  // also writes its committed state and replays m_prev records.  The
+  // matrix-core kernel takes the lanes in decreasing order of that cost
+  // within each XCD's share of the work, so that the cheap workgroups fill
+  // the end of the launch (longest processing time first).
+  {
+    int ord[GDN_MAX_LANES];
+    auto cost = [&](int n) {
+      const int m = ct.n_act > 0 ? (int)pr.m.v[n] : 0;
+      return (m > 0 ? 1024 : 0) + 32 * m + t_lane[n];
+    };
+    for (int i = 0; i < d.n_lanes; ++i) {  // stable insertion sort
+      int j = i;
+      for (; j > 0 && cost(ord[j - 1]) < cost(i); --j) ord[j] = ord[j - 1];
+      ord[j] = i;
+    }
+    for (int n = 0; n < d.n_lanes; ++n) pr.order.v[n] = (uint8_t)ord[n];
   }
   if (!any && ct.n_act == 0) return GDN_OK;
   hipError_t e = mverify_eligible(d, in_dtype, a)

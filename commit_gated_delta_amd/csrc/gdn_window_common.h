@@ -44,7 +44,8 @@ struct PrevRecords {
   const float* k;
   const float* u;
   const float2* scale;
-  LaneTable m;  // accepted prefix per lane
+  LaneTable m;      // accepted prefix per lane
+  LaneTable order;  // lanes by decreasing work (rank -> lane), see below
 };
 
 // Host-side arguments of a verify launch.

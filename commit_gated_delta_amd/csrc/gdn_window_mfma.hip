@@ -123,8 +123,19 @@ void mverify_kernel(
   item /= nc;
   const int h = item % d.Hv;
   item /= d.Hv;
-  const int lane = item % d.N;
-  const int layer = item / d.N;
+  // (layer, lane): an XCD's share is a range of layers (xcd_item); in the
+  // fused call its workgroups go lane by lane in prev.order (costliest
+  // lanes first), every layer of a lane together
+  int lane, layer;
+  if (REPLAY && gridDim.x % 8 == 0 && d.NL % 8 == 0) {
+    const int lx = d.NL / 8;
+    const int x = item / (lx * d.N), j = item % (lx * d.N);
+    lane = table_byte(prev.order, j / lx);
+    layer = x * lx + j % lx;
+  } else {
+    lane = item % d.N;
+    layer = item / d.N;
+  }
   const int T = table_byte(tl, lane);
   const int m_prev = REPLAY ? table_byte(prev.m, lane) : 0;
   if (T == 0 && m_prev == 0) return;
@@ -592,7 +603,11 @@ void mverify_kernel(
     ut[1][e] = U[1][e] * f2e[e];
     if (t < T) {
       const uint32_t off = (uint32_t)(t * vo_step) + c0;
-      *reinterpret_cast<float2*>(o0 + off) = make_float2(O[0][e], O[1][e]);
+      // outputs are not read again by this path: nontemporal stores keep
+      // them from displacing the records and rows in the caches (verify
+      // 0.206 -> 0.188 ms at 8 lanes x 48 layers, T = 16)
+      __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
+                                  reinterpret_cast<f32x2*>(o0 + off));
       *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
     }
   }
