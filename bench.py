@@ -469,6 +469,94 @@ def bench_token_verify(reps=20, warmup=3):
             "verify_hbm_frac": bv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_general_shapes(reps=10, warmup=2):
+    """Shapes that the token-by-token kernels serve, on the same 8-lane x
+    48-layer x 32/16-head batch (d = 128): f32 inputs at T = 16, bf16
+    windows of 32 and 64 tokens, and 32-node draft trees.  Verify, commit
+    and the fused round are event-timed; HBM fractions against the same
+    algorithmic byte counts as the headline (inputs at their own width)."""
+    import torch
+    import gdn_synth as gs
+    import commit_gated_delta_amd as gdn
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for r in range(warmup):
+            fn(r)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r, (a, b) in enumerate(ev):
+            a.record(stream)
+            fn(warmup + r)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    out = []
+    for name, tm, bf16, tree in (("f32_T16", 16, False, False),
+                                 ("bf16_T32", 32, True, False),
+                                 ("bf16_T64", 64, True, False),
+                                 ("bf16_tree32", 32, True, True)):
+        shape = gs.WindowShape(NL, N, HV, HK, DK, DV, tm)
+        dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, tm)
+        t_lane = np.full(N, tm, dtype=np.int32)
+        w = gs.window_inputs(shape, (13, tm, int(bf16)), bf16=bf16)
+        if bf16:
+            ins = (_dev_bf16(w.q, dev), _dev_bf16(w.k, dev), _dev_bf16(w.v, dev))
+        else:
+            ins = tuple(torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+        ins = ins + (torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(w.g).to(dev))
+        S = torch.from_numpy(gs.initial_state(shape, (13, tm))).to(dev)
+        o = torch.empty((NL, N, tm, HV, DV), device=dev)
+        nrec = gdn.records_bytes(dims)
+        recs = [torch.empty(nrec, dtype=torch.uint8, device=dev)
+                for _ in range(2)]
+        m_all = [gs.accepted_uniform(t_lane, (13, tm, r))
+                 for r in range(warmup + reps)]
+        isz = 2 if bf16 else 4
+        # inputs at their own width: q, k, v rows of isz bytes per element
+        win_extra = (0 if bf16 else
+                     (2 * HK * DK * 2 + HV * DV * 2) * NL * N * tm)
+        bv = alg_bytes_verify(t_lane) + win_extra
+        rec = {"shape": name, "t": tm, "inputs": "bf16" if bf16 else "f32"}
+        if tree:
+            parent = [list(p) for p in gs.tree_parents(t_lane, tm, (13, tm))]
+            paths = gs.accepted_tree_paths(np.array(parent), t_lane, (13, tm))
+            ms_v = timed(lambda r: gdn.verify_tree(dims, t_lane, parent, *ins,
+                                                   S, o, recs[0],
+                                                   stream=stream))
+            Sc = S.clone()
+            ms_c = timed(lambda r: gdn.commit_path(dims, paths, t_lane, parent,
+                                                   recs[0], Sc, stream=stream))
+            bc = alg_bytes_commit([len(p) for p in paths])
+            rec.update({"verify_ms": ms_v, "commit_ms": ms_c,
+                        "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "commit_hbm_frac": bc / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "node_updates_per_s": N * tm * NL * HV / (ms_v * 1e-3)})
+        else:
+            ms_v = timed(lambda r: gdn.verify(dims, t_lane, *ins, S, o,
+                                              recs[r % 2], stream=stream))
+            ms_f = timed(lambda r: gdn.commit_verify(
+                dims, m_all[r], t_lane, recs[(r + 1) % 2], t_lane, *ins, S, o,
+                recs[r % 2], stream=stream))
+            bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in m_all]))
+            bf += win_extra
+            upd = N * tm * NL * HV
+            rec.update({"verify_ms": ms_v, "fused_ms": ms_f,
+                        "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "fused_hbm_frac": bf / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "fused_updates_per_s": upd / (ms_f * 1e-3)})
+        out.append(rec)
+        del S, o, recs, ins
+        torch.cuda.empty_cache()
+    return {"workload": "token-by-token kernels on 8 lanes x 48 layers x "
+                        "32/16 heads, d=128, every lane at T (fused: previous "
+                        "window's m ~ U{0..T})", "points": out}
+
+
 # Synthetic workloads of the speculative-decoding round, timed as chains of
 # fused rounds (gdn_commit_verify: round r commits the accepted prefix of the
 # same state set's previous window and verifies window r).
@@ -764,6 +852,12 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the 1-lane, ragged 8-lane and 12-lane chains")
     ap.add_argument("--no-token-verify", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip reading the clocks under load (profiler runs)")
+    ap.add_argument("--no-general", action="store_true",
+                    help="skip f32 / long-window / 32-node-tree shapes")
+    ap.add_argument("--general-only", action="store_true",
+                    help="time only the token-by-token kernel shapes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -790,6 +884,10 @@ def main():
         torch.mul(cx, 1.0, out=cy)
         torch.cuda.synchronize()
         del cx, cy
+    if args.general_only:
+        print(json.dumps({"general_shapes": bench_general_shapes(
+            reps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill(reps=args.steps,
                                                    warmup=args.warmup)}),
@@ -815,12 +913,22 @@ def main():
     m_all = [gs.accepted_uniform(t_lane, (7, 100 + s)) for s in range(total)]
     stream = torch.cuda.current_stream()
 
+    # On ROCm an event record is a queue marker that lengthens the launch
+    # it brackets (a fused step took about 10 us longer with events around
+    # every launch).  The fused round is one launch per step, so its
+    # average launch duration is the timed region's event time / K (back to
+    # back, launch gaps included) and it records no per-launch events; the
+    # two-call round needs per-launch events to split verify from commit,
+    # and records them on every EV_EVERY-th step only.
+    EV_EVERY = 5
+
     def timed(step, n_ev):
         for s in range(args.warmup):
             step(s)
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-               for _ in range(args.steps)]
+               if n_ev and s % EV_EVERY == 0 else None
+               for s in range(args.steps)]
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -849,19 +957,22 @@ def main():
                 ev[2].record(stream)
 
         ms, evs = timed(step2, 3)
-        ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        smp = [s for s in range(args.steps) if evs[s] is not None]
+        ms_v = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in smp]))
+        ms_c = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in smp]))
         bv = alg_bytes_verify(t_lane)
         bc = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
                             for s in range(args.steps)]))
+        bc_smp = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
+                                for s in smp]))
         res["two-call"] = {
             "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
             "hbm_roofline_frac_path": (bv + bc) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "verify_ms": ms_v, "commit_ms": ms_c,
             "verify_alg_GBps": bv / (ms_v * 1e-3) / 1e9,
             "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "commit_alg_GBps": bc / (ms_c * 1e-3) / 1e9,
-            "commit_hbm_frac": bc / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "commit_alg_GBps": bc_smp / (ms_c * 1e-3) / 1e9,
+            "commit_hbm_frac": bc_smp / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "verify_traffic": measured_traffic("verify_kernel"),
             "commit_traffic": measured_traffic("commit_kernel"),
             "alg_bytes_verify": bv, "alg_bytes_per_step": bv + bc}
@@ -885,20 +996,22 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
-        ms, evs = timed(stepf, 2)
-        ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ms, _ = timed(stepf, 0)
+        ms_f = ms  # one launch per step, back to back
 
         def busy():
             for s_ in range(20):
                 stepf(args.warmup + s_ % args.steps)
-        clocks = gpu_clocks_under_load(busy)
+        clocks = None if args.no_clocks else gpu_clocks_under_load(busy)
         mp = [m_prev_of(args.warmup + s) for s in range(args.steps)]
         bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in mp]))
+
         res["fused"] = {
             "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
             "hbm_roofline_frac_path": bf / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_ms": ms_f,
+            "kernel_ms": ms_f, "kernel_launches_timed": args.steps,
             "alg_GBps": bf / (ms_f * 1e-3) / 1e9,
+            "alg_bytes_per_launch_timed": bf,
             "traffic": measured_traffic("fused_kernel"),
             "alg_bytes_per_step": bf, "gpu_clocks_under_load": clocks}
         del S, recs
@@ -909,11 +1022,14 @@ def main():
     if head == "fused":
         roof = {"bound": "hbm",
                 "kernel": "gdn_commit_verify (mverify_kernel, replay on)",
+                "duration": "timed region / K: one launch per step, back to "
+                            "back, launch gaps included",
                 "achieved": h["alg_GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": h["alg_GBps"] / HBM_PEAK_GBS,
                 "traffic": h["traffic"],
-                "alg_bytes_per_launch": h["alg_bytes_per_step"],
-                "avg_launch_ms": h["kernel_ms"]}
+                "alg_bytes_per_launch": h["alg_bytes_per_launch_timed"],
+                "avg_launch_ms": h["kernel_ms"],
+                "launches_timed": h["kernel_launches_timed"]}
     else:
         roof = {"bound": "hbm", "kernel": "gdn_verify (mverify_kernel)",
                 "achieved": h["verify_alg_GBps"], "peak": HBM_PEAK_GBS,
@@ -953,6 +1069,8 @@ def main():
             samples.append(smp)
     if not args.no_token_verify:
         out["token_by_token_verify"] = bench_token_verify()
+    if not args.no_general:
+        out["general_shapes"] = bench_general_shapes()
     if not args.no_prefill:
         out["prefill"] = bench_prefill()
     if not args.no_snapshot:
