@@ -129,6 +129,25 @@ def measured_traffic(kernel):
     return float(k["bytes_per_launch"])
 
 
+def region_ms(fn, reps, warmup, stream):
+    """Average time of fn(r) over `reps` calls run back to back on `stream`,
+    bracketed by one pair of HIP events (an event record between launches
+    is a queue marker on ROCm and would lengthen the launches it sits
+    between), after `warmup` untimed calls."""
+    import torch
+    for r in range(warmup):
+        fn(r)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(reps):
+        fn(warmup + r)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 PF_L, PF_H, PF_C = 32768, 32, 64
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
@@ -173,17 +192,7 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
         gdn.prefill_chunked(1, PF_L, PF_H, h_k, 128, 128, q, k, v, beta, g,
                             None, Sf, o, ck, ws, stream=stream)
 
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        run()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms = region_ms(lambda r: run(), reps, warmup, stream)
     useful, issued = prefill_flops()
     io_bytes = (PF_L * h_k * 128 * 2 * 2 + PF_L * PF_H * 128 * 2 +
                 PF_L * PF_H * 4 * 2 + PF_L * PF_H * 128 * 4 +
@@ -237,17 +246,7 @@ def bench_t_sweep(ts=(1, 2, 4, 6, 8, 12, 16), reps=20, warmup=3):
                   for r in range(warmup + reps + 1)]
 
         def timed(fn):
-            for r in range(warmup):
-                fn(r)
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True),
-                   torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for r, (a, b) in enumerate(ev):
-                a.record(stream)
-                fn(warmup + r)
-                b.record(stream)
-            torch.cuda.synchronize()
-            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            return region_ms(fn, reps, warmup, stream)
 
         ms_v = timed(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o,
                                           recs[r % 2], stream=stream))
@@ -298,25 +297,15 @@ def bench_tree(reps=20, warmup=3):
     stream = torch.cuda.current_stream()
     plist = [list(r) for r in parent]
 
-    def run_verify():
-        gdn.verify_tree(dims, t_lane, plist, q, k, v, beta, g, S, o, rec,
-                        stream=stream)
-
-    for _ in range(warmup):
-        run_verify()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(reps)]
+    ms_v = region_ms(lambda r: gdn.verify_tree(
+        dims, t_lane, plist, q, k, v, beta, g, S, o, rec, stream=stream),
+        reps, warmup, stream)
+    # path commits of the same accepted paths, back to back (each replays
+    # the path's records on the state the previous one left)
     S_c = S.clone()
-    for e in evs:
-        e[0].record(stream)
-        run_verify()
-        e[1].record(stream)
-        gdn.commit_path(dims, paths, t_lane, plist, rec, S_c, stream=stream)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_c = region_ms(lambda r: gdn.commit_path(dims, paths, t_lane, plist, rec,
+                                               S_c, stream=stream),
+                     reps, warmup, stream)
     upd = N * T * NL * HV
     # a node has the window traffic of a token; the path commit moves the
     # commit's bytes for the path's length
@@ -354,21 +343,14 @@ def bench_kda(reps=20, warmup=3):
     rec = torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8, device=dev)
     ms_all = [gs.accepted_uniform(t_lane, (10, 1 + r)) for r in range(reps + warmup)]
     stream = torch.cuda.current_stream()
-    for r in range(warmup):
-        gdn.kda_verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
-        gdn.kda_commit(dims, ms_all[r], t_lane, rec, S, stream=stream)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(reps)]
-    for r, e in enumerate(evs):
-        e[0].record(stream)
-        gdn.kda_verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
-        e[1].record(stream)
-        gdn.kda_commit(dims, ms_all[warmup + r], t_lane, rec, S, stream=stream)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    ms_v = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_c = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_v = region_ms(lambda r: gdn.kda_verify(dims, t_lane, q, k, v, beta, g,
+                                              S, o, rec, stream=stream),
+                     reps, warmup, stream)
+    # commits of the drawn prefixes, back to back, from the last verify's
+    # records (each on the state the previous one left)
+    ms_c = region_ms(lambda r: gdn.kda_commit(dims, ms_all[r], t_lane, rec, S,
+                                              stream=stream),
+                     reps, warmup, stream)
     upd = N * T * NL * HV
     bv = alg_bytes_kda_verify(t_lane)
     bc = float(np.mean([alg_bytes_kda_commit(m) for m in ms_all[warmup:]]))
@@ -450,17 +432,8 @@ def bench_token_verify(reps=20, warmup=3):
     o = torch.empty((NL, N, tm, HV, DV), device=dev)
     rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    for r in range(warmup):
-        gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec, stream=stream)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for r, (a, b) in enumerate(evs):
-        a.record(stream)
-        gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec,
+                                        stream=stream), reps, warmup, stream)
     bv = alg_bytes_verify(t_lane)
     return {"workload": "verify of 8 lanes x 48 layers x 32/16 heads, d=128, "
                         "T=16 on the token-by-token kernel (window stride 17)",
@@ -482,17 +455,7 @@ def bench_general_shapes(reps=10, warmup=2):
     stream = torch.cuda.current_stream()
 
     def timed(fn):
-        for r in range(warmup):
-            fn(r)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for r, (a, b) in enumerate(ev):
-            a.record(stream)
-            fn(warmup + r)
-            b.record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return region_ms(fn, reps, warmup, stream)
 
     out = []
     for name, tm, bf16, tree in (("f32_T16", 16, False, False),
@@ -913,31 +876,24 @@ def main():
     m_all = [gs.accepted_uniform(t_lane, (7, 100 + s)) for s in range(total)]
     stream = torch.cuda.current_stream()
 
-    # On ROCm an event record is a queue marker that lengthens the launch
-    # it brackets (a fused step took about 10 us longer with events around
-    # every launch).  The fused round is one launch per step, so its
-    # average launch duration is the timed region's event time / K (back to
-    # back, launch gaps included) and it records no per-launch events; the
-    # two-call round needs per-launch events to split verify from commit,
-    # and records them on every EV_EVERY-th step only.
-    EV_EVERY = 5
-
-    def timed(step, n_ev):
+    # The K timed steps run back to back between one pair of HIP events:
+    # on ROCm an event record is a queue marker that lengthens the launches
+    # it sits between (a fused step took about 10 us longer with events
+    # around every launch).  Per-kernel times come from regions of their
+    # own (region_ms).
+    def timed(step):
         for s in range(args.warmup):
             step(s)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-               if n_ev and s % EV_EVERY == 0 else None
-               for s in range(args.steps)]
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
         for s in range(args.steps):
-            step(args.warmup + s, evs[s])
+            step(args.warmup + s)
         end.record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / args.steps, evs
+        return start.elapsed_time(end) / args.steps
 
     upd_per_step = int(t_lane.sum()) * NL * HV
     res = {}
@@ -945,26 +901,26 @@ def main():
         S = torch.from_numpy(S0).to(dev)
         rec = torch.empty(nrec, dtype=torch.uint8, device=dev)
 
-        def step2(s, ev=None):
+        def step2(s):
             q, k, v, beta, g = pool[s % len(pool)]
-            if ev is not None:
-                ev[0].record(stream)
             gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
             gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
 
-        ms, evs = timed(step2, 3)
-        smp = [s for s in range(args.steps) if evs[s] is not None]
-        ms_v = float(np.mean([evs[s][0].elapsed_time(evs[s][1]) for s in smp]))
-        ms_c = float(np.mean([evs[s][1].elapsed_time(evs[s][2]) for s in smp]))
+        ms = timed(step2)
         bv = alg_bytes_verify(t_lane)
         bc = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
                             for s in range(args.steps)]))
-        bc_smp = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
-                                for s in smp]))
+        # each kernel back to back in a region of its own: verify leaves S
+        # as it is; the commits replay the drawn prefixes of the last
+        # window's records, each on the state the previous one left
+        ms_v = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % len(pool)],
+                                              S, o, rec, stream=stream),
+                         args.steps, 2, stream)
+        ms_c = region_ms(lambda r: gdn.commit(dims, m_all[r % total], t_lane,
+                                              rec, S, stream=stream),
+                         args.steps, 2, stream)
+        bc_smp = float(np.mean([alg_bytes_commit(m_all[(2 + r) % total])
+                                for r in range(args.steps)]))
         res["two-call"] = {
             "ms_per_step": ms, "updates_per_s": upd_per_step / (ms * 1e-3),
             "hbm_roofline_frac_path": (bv + bc) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -986,17 +942,13 @@ def main():
         def m_prev_of(s):
             return zero if s == 0 else m_all[s - 1]
 
-        def stepf(s, ev=None):
+        def stepf(s):
             q, k, v, beta, g = pool[s % len(pool)]
-            if ev is not None:
-                ev[0].record(stream)
             gdn.commit_verify(dims, m_prev_of(s), t_lane, recs[(s + 1) % 2],
                               t_lane, q, k, v, beta, g, S, o, recs[s % 2],
                               stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
 
-        ms, _ = timed(stepf, 0)
+        ms = timed(stepf)
         ms_f = ms  # one launch per step, back to back
 
         def busy():
@@ -1075,6 +1027,14 @@ def main():
         out["prefill"] = bench_prefill()
     if not args.no_snapshot:
         out["state_snapshot"] = bench_snapshot()
+        # context for the roofline: what a plain device copy (read + write,
+        # the fused round's own mix of state traffic) reaches on this machine
+        cp = out["state_snapshot"]["device_GBps"]
+        roof["copy_ceiling"] = {
+            "kernel": "gdn_state_snapshot device to device (768 MiB read + "
+                      "768 MiB write)",
+            "GBps": cp, "frac_of_peak": cp / HBM_PEAK_GBS,
+            "achieved_over_copy": roof["achieved"] / cp}
     if not args.no_sweep:
         out["t_sweep"] = bench_t_sweep()
     if not args.no_tree:
