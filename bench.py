@@ -193,6 +193,23 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
                             None, Sf, o, ck, ws, stream=stream)
 
     ms = region_ms(lambda r: run(), reps, warmup, stream)
+    # The same head-tokens as 4 independent sequences of 8,192 tokens: four
+    # times the workgroups, each a quarter of the chunk chain.  This is the
+    # pass that produces the outputs in a sequence-parallel prefill with
+    # four segments (each segment's chain run from its start state), before
+    # the segments' transition matrices and the scan are counted.
+    nseg = 4
+    Ls = PF_L // nseg
+    Sf4 = torch.empty((nseg, PF_H, 128, 128), device=dev)
+    ck4 = torch.empty((nseg, Ls // 8192, PF_H, 128, 128), device=dev)
+
+    def run4():
+        gdn.prefill_chunked(nseg, Ls, PF_H, h_k, 128, 128, q.view(nseg, Ls, h_k, 128),
+                            k.view(nseg, Ls, h_k, 128), v.view(nseg, Ls, PF_H, 128),
+                            beta.view(nseg, Ls, PF_H), g.view(nseg, Ls, PF_H), None,
+                            Sf4, o.view(nseg, Ls, PF_H, 128), ck4, ws, stream=stream)
+
+    ms4 = region_ms(lambda r: run4(), reps, warmup, stream)
     useful, issued = prefill_flops()
     io_bytes = (PF_L * h_k * 128 * 2 * 2 + PF_L * PF_H * 128 * 2 +
                 PF_L * PF_H * 4 * 2 + PF_L * PF_H * 128 * 4 +
@@ -205,6 +222,7 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
             "mfma_frac_issued": issued / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "mfma_frac_useful": useful / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "io_GBps": io_bytes / (ms * 1e-3) / 1e9,
+            "as_4_sequences_of_8192_ms": ms4,
             "traffic_p1": measured_traffic("prefill_p1"),
             "traffic_p2": measured_traffic("prefill_p2"),
             "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
