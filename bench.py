@@ -724,15 +724,32 @@ def oracle_chain_parity(sample):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping numbers (a virtualised host may report only the brand) and the
+    logical CPUs this process may run on."""
+    import os
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break       # first processor's block only
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
         pass
     import platform
-    return platform.processor() or "unknown"
+    name = info.get("model name") or platform.processor() or "unknown"
+    ids = ", ".join("%s %s" % (k.replace("cpu ", ""), info[k])
+                    for k in ("cpu family", "model", "stepping") if k in info)
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return "%s (%s; %s logical CPUs usable of %s)" % (
+        name, ids or "ids unknown", usable, os.cpu_count())
 
 
 def _parse_clocks(text):

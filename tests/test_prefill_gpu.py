@@ -98,6 +98,7 @@ CASES = [
     ("eq_heads_no_init", 512, 4, 4, 1, False, 128, 1.0, True),
     ("short_tail", 70, 2, 2, 1, True, 64, 1.0, True),
     ("tiny", 5, 2, 1, 1, True, 64, 1.0, True),
+    ("one_token", 1, 2, 1, 1, True, 64, 1.0, True),
 ]
 
 

@@ -305,6 +305,55 @@ def test_idle_lane_and_zero_accept():
     assert np.array_equal(S1[:, 2], dbg.cpu().numpy()[:, 2, 1])
 
 
+@pytest.mark.parametrize("case", [("bf16_d128", 128, True), ("f32_d32", 32, False)],
+                         ids=lambda c: c[0])
+def test_all_lanes_idle(case):
+    """Degenerate batches on both verify kernels: with every lane idle
+    (t_lane = 0, m = 0) verify, commit and the fused call read and write
+    nothing (outputs, records and debug states keep their fill, the state
+    its bits); a fused call whose next windows are all empty still commits
+    the previous prefixes, bit for bit as commit alone."""
+    name, d, bf16 = case
+    shape = gs.WindowShape(2, 3, 2, 1, d, d, 16)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S0 = gs.initial_state(shape, (109,))
+    idle = np.zeros(3, dtype=np.int32)
+    w0 = gs.window_inputs(shape, (109,), bf16=bf16, t_lane=[0, 0, 0])
+    q, k, v, beta, g = window_to_dev(w0, torch)
+    S_dev = to_dev(S0, torch)
+    o = torch.full((2, 3, 16, 2, d), float("nan"), device="cuda")
+    dbg = torch.full((2, 3, 16, 2, d, d), float("nan"), device="cuda")
+    rec = torch.full((gdn.records_bytes(dims),), 0xA5, dtype=torch.uint8,
+                     device="cuda")
+    gdn.verify(dims, idle, q, k, v, beta, g, S_dev, o, rec, dbg)
+    gdn.commit(dims, idle, idle, rec, S_dev)
+    rec2 = rec.clone()
+    gdn.commit_verify(dims, idle, idle, rec, idle, q, k, v, beta, g, S_dev,
+                      o, rec2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all() and torch.isnan(dbg).all()
+    assert (rec == 0xA5).all() and (rec2 == 0xA5).all()
+    assert np.array_equal(S_dev.cpu().numpy(), S0)
+    # previous windows of 4, 0 and 2 tokens, accepted 3, 0 and 1; the next
+    # windows empty: the fused call is the commit alone
+    w1 = gs.window_inputs(shape, (109, 1), bf16=bf16, t_lane=[4, 0, 2])
+    m = np.array([3, 0, 1], dtype=np.int32)
+    S_v = to_dev(S0, torch)
+    _, rec1, _ = _run_verify(dims, w1, S_v)
+    S_c, S_f = to_dev(S0, torch), to_dev(S0, torch)
+    gdn.commit(dims, m, w1.t_lane, rec1, S_c)
+    o_f = torch.full_like(o, float("nan"))
+    rec_f = torch.full_like(rec, 0xA5)
+    gdn.commit_verify(dims, m, w1.t_lane, rec1, idle, q, k, v, beta, g, S_f,
+                      o_f, rec_f)
+    torch.cuda.synchronize()
+    assert torch.equal(S_c, S_f)
+    assert not np.array_equal(S_c.cpu().numpy()[:, 0], S0[:, 0])
+    assert np.array_equal(S_c.cpu().numpy()[:, 1], S0[:, 1])
+    assert torch.isnan(o_f).all() and (rec_f == 0xA5).all()
+    say("  %s: idle batch untouched, empty next windows commit only" % name)
+
+
 FOLD_CASES = [
     # (name, dk, dv, bf16): the matrix-core readout (bf16, d_k >= 32) and
     # the general loop (f32 inputs, d_k = 16)
