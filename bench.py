@@ -129,14 +129,59 @@ def measured_traffic(kernel):
     return float(k["bytes_per_launch"])
 
 
-def region_ms(fn, reps, warmup, stream):
-    """Average time of fn(r) over `reps` calls run back to back on `stream`,
-    bracketed by one pair of HIP events (an event record between launches
-    is a queue marker on ROCm and would lengthen the launches it sits
-    between), after `warmup` untimed calls."""
+def region_ms(fn, reps, warmup, stream, settle_s=0.05):
+    """Average time of fn(r) over `reps` calls that run back to back, as a
+    serving loop runs them: after `warmup` untimed calls, the `reps` calls
+    fn(warmup), ..., fn(warmup + reps - 1) are captured once into a HIP graph
+    on `stream` (every entry point only launches kernels, so the calls
+    capture as they run; fn must launch on `stream`), the graph is replayed
+    untimed for at least `settle_s` seconds (a region that starts after the
+    GPU has idled through host-side setup otherwise runs its first
+    milliseconds slow), then once between one pair of HIP events.  The
+    replay runs
+    the same kernels with the same arguments as the calls; it removes the
+    host work and the dispatch gaps between them (an event record between
+    launches is a queue marker on ROCm and would lengthen the launches it
+    sits between, so there is one pair for the whole region)."""
     import torch
+    if stream == torch.cuda.default_stream():
+        raise RuntimeError("region_ms: the timed stream must be capturable "
+                           "(not the default stream)")
     for r in range(warmup):
         fn(r)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for r in range(reps):
+            fn(warmup + r)
+    t0 = time.perf_counter()
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= settle_s:
+            break
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return a.elapsed_time(b) / reps
+
+
+def stream_launch_ms(fn, reps, warmup, stream, settle_s=0.05):
+    """The same region with the calls launched one by one from the host
+    (host work and dispatch gaps between the launches included), after the
+    same settling time."""
+    import torch
+    t0 = time.perf_counter()
+    r = 0
+    while r < warmup or time.perf_counter() - t0 < settle_s:
+        fn(r % max(warmup, 1))
+        r += 1
+        if r % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -606,7 +651,8 @@ def bench_chain(name, cfg, warmup=4, sample_layer=17):
     o = torch.empty((NL, Nl, tm, HV, DV), device=dev)
     zero = np.zeros(Nl, dtype=np.int32)
 
-    def run(n_rounds, evs=None):
+    def run(n_rounds, evs=None, strm=None):
+        strm = stream if strm is None else strm
         prev = [None] * ns
         for r in range(n_rounds):
             j = r % ns
@@ -616,7 +662,7 @@ def bench_chain(name, cfg, warmup=4, sample_layer=17):
                 evs[0].record(stream)
             gdn.commit_verify(dims, m_prev, t_prev, recs[j][1 - cur],
                               t_all[r], *pool[r % P], S[j], o, recs[j][cur],
-                              stream=stream)
+                              stream=strm)
             prev[j] = (t_all[r], m_all[r])
         if evs is not None:
             evs[1].record(stream)
@@ -656,6 +702,30 @@ def bench_chain(name, cfg, warmup=4, sample_layer=17):
         mm = int(m_all[R - 1][n])
         want = pre_np[0, n] if mm == 0 else dbg_np[0, n, mm - 1]
         bitexact &= bool(np.array_equal(S_end[0, n], want))
+    # The same chain captured once into a HIP graph and replayed (every entry
+    # point only launches kernels, so the rounds capture as they run): the
+    # rounds then follow each other with no host work in between.  The
+    # replay continues from the states the chain above left.
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run(R, None, side)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:                  # settle, as in region_ms
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= 0.05:
+            break
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ge[0].record(stream)
+    graph.replay()
+    ge[1].record(stream)
+    torch.cuda.synchronize()
+    ms_g = ge[0].elapsed_time(ge[1])
+    del graph
     upd = sum(int(t.sum()) for t in t_all) * NL * HV
     m_prev_seq = [zero if r < ns else m_all[r - ns] for r in range(R)]
     byts = sum(alg_bytes_fused(t_all[r], m_prev_seq[r]) for r in range(R))
@@ -664,6 +734,10 @@ def bench_chain(name, cfg, warmup=4, sample_layer=17):
            "alg_bytes_per_round": byts / R,
            "alg_GBps": byts / (ms * 1e-3) / 1e9,
            "hbm_roofline_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "graph_replay": {
+               "ms_per_round": ms_g / R,
+               "updates_per_s": upd / (ms_g * 1e-3),
+               "hbm_roofline_frac": byts / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS},
            "bitexact_replay_sampled_layer": bitexact,
            "parity": None}
     sample = {"name": name, "layer": ls, "set": js, "rounds": [
@@ -876,6 +950,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # Everything runs on one stream of default priority other than the
+    # default stream, so that timed regions can be captured into HIP graphs.
+    torch.cuda.set_stream(torch.cuda.Stream(device=dev))
     if args.calibrate_copy:
         cx = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         cy = torch.empty_like(cx)
@@ -911,24 +988,12 @@ def main():
     m_all = [gs.accepted_uniform(t_lane, (7, 100 + s)) for s in range(total)]
     stream = torch.cuda.current_stream()
 
-    # The K timed steps run back to back between one pair of HIP events:
-    # on ROCm an event record is a queue marker that lengthens the launches
-    # it sits between (a fused step took about 10 us longer with events
-    # around every launch).  Per-kernel times come from regions of their
-    # own (region_ms).
+    # The K timed steps run back to back as one HIP graph replay between one
+    # pair of HIP events (region_ms); per-kernel times come from regions of
+    # their own.  The same K steps launched one by one from the host are
+    # reported beside it.
     def timed(step):
-        for s in range(args.warmup):
-            step(s)
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for s in range(args.steps):
-            step(args.warmup + s)
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / args.steps
+        return region_ms(step, args.steps, args.warmup, stream)
 
     upd_per_step = int(t_lane.sum()) * NL * HV
     res = {}
@@ -985,6 +1050,7 @@ def main():
 
         ms = timed(stepf)
         ms_f = ms  # one launch per step, back to back
+        ms_host = stream_launch_ms(stepf, args.steps, args.warmup, stream)
 
         def busy():
             for s_ in range(20):
@@ -1000,7 +1066,12 @@ def main():
             "alg_GBps": bf / (ms_f * 1e-3) / 1e9,
             "alg_bytes_per_launch_timed": bf,
             "traffic": measured_traffic("fused_kernel"),
-            "alg_bytes_per_step": bf, "gpu_clocks_under_load": clocks}
+            "alg_bytes_per_step": bf, "gpu_clocks_under_load": clocks,
+            "host_launched": {
+                "ms_per_step": ms_host,
+                "updates_per_s": upd_per_step / (ms_host * 1e-3),
+                "hbm_roofline_frac_path":
+                    bf / (ms_host * 1e-3) / 1e9 / HBM_PEAK_GBS}}
         del S, recs
 
     head = "fused" if "fused" in res else "two-call"
@@ -1009,8 +1080,9 @@ def main():
     if head == "fused":
         roof = {"bound": "hbm",
                 "kernel": "gdn_commit_verify (mverify_kernel, replay on)",
-                "duration": "timed region / K: one launch per step, back to "
-                            "back, launch gaps included",
+                "duration": "timed region / K: the K steps replayed back to "
+                            "back from one HIP graph, one launch per step, "
+                            "gaps between the launches included",
                 "achieved": h["alg_GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": h["alg_GBps"] / HBM_PEAK_GBS,
                 "traffic": h["traffic"],
