@@ -173,12 +173,15 @@ def region_ms(fn, reps, warmup, stream, settle_s=0.05):
 def stream_launch_ms(fn, reps, warmup, stream, settle_s=0.05):
     """The same region with the calls launched one by one from the host
     (host work and dispatch gaps between the launches included), after the
-    same settling time."""
+    warm-up calls and the same settling time, spent on the timed calls
+    themselves (the steady-state sequence, as the graph replays it)."""
     import torch
+    for r in range(warmup):
+        fn(r)
     t0 = time.perf_counter()
     r = 0
-    while r < warmup or time.perf_counter() - t0 < settle_s:
-        fn(r % max(warmup, 1))
+    while time.perf_counter() - t0 < settle_s:
+        fn(warmup + r % reps)
         r += 1
         if r % 8 == 0:
             torch.cuda.synchronize()
