@@ -54,8 +54,10 @@ struct KdaScalars {
   float rk, f3, beta, kq;  // f3 = scale * rq; kq = k_t . q_t (raw)
 };
 
+// Six waves per SIMD (at most 80 VGPRs); the variant that writes every
+// intermediate state gets two (60 spilled VGPRs at 80, 18 at 128).
 template <int DK, bool DBG, typename TIn>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG ? 2 : 6)))
 void kda_verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ beta,

@@ -226,10 +226,12 @@ __device__ __forceinline__ float replay_staged(
 // Six waves per SIMD (at most 80 VGPRs) for windows; draft trees at d_k of
 // 64 and 128 keep a second copy of the held state while they rebuild a
 // parent's state, and spill at 80 VGPRs (a 32-node tree verify took 3.36 ms
-// with 104 spilled VGPRs, 1.79 ms with none), so they get more registers.
+// with 104 spilled VGPRs, 1.79 ms with none), so they get more registers,
+// and so do the variants that write every intermediate state at d_k = 128
+// (36 spilled VGPRs at 80).
 template <int DK, bool DBG, typename TIn, bool REPLAY, bool TREE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(
-    TREE ? (DK == 128 ? 2 : DK == 64 ? 4 : 6) : 6)))
+    TREE ? (DK == 128 ? 2 : DK == 64 ? 4 : 6) : (DBG && DK == 128 ? 4 : 6))))
 void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ beta,
