@@ -213,10 +213,11 @@ def prefill_flops(L=PF_L, H=PF_H, C=PF_C, D=128):
     return useful, issued
 
 
-def bench_prefill(reps=10, warmup=2, h_k=PF_H):
+def bench_prefill(reps=10, warmup=2, h_k=PF_H, segments=True):
     """Chunked prefill of one 32,768-token sequence, 32 value heads (h_k key
     heads), d = 128, bf16 q/k/v, zero initial state, checkpoints every
-    8,192 tokens.  Event-timed on the stream the kernels run on."""
+    8,192 tokens, timed by region_ms; with `segments`, also the same
+    head-tokens as four 8,192-token sequences."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
@@ -241,6 +242,20 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
                             None, Sf, o, ck, ws, stream=stream)
 
     ms = region_ms(lambda r: run(), reps, warmup, stream)
+    useful, issued = prefill_flops()
+    io_bytes = (PF_L * h_k * 128 * 2 * 2 + PF_L * PF_H * 128 * 2 +
+                PF_L * PF_H * 4 * 2 + PF_L * PF_H * 128 * 4 +
+                (PF_L // 8192 + 1) * PF_H * 128 * 128 * 4)
+    rec = {"workload": "1 sequence x 32768 tokens, 32 value / %d key heads, "
+                       "d=128, chunk 64, checkpoints every 8192" % h_k,
+           "ms": ms, "head_tokens_per_s": PF_L * PF_H / (ms * 1e-3),
+           "useful_tflops": useful / (ms * 1e-3) / 1e12,
+           "issued_mfma_tflops": issued / (ms * 1e-3) / 1e12,
+           "mfma_frac_issued": issued / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+           "mfma_frac_useful": useful / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+           "io_GBps": io_bytes / (ms * 1e-3) / 1e9}
+    if not segments:
+        return rec
     # The same head-tokens as 4 independent sequences of 8,192 tokens: four
     # times the workgroups, each a quarter of the chunk chain.  This is the
     # pass that produces the outputs in a sequence-parallel prefill with
@@ -258,22 +273,11 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H):
                             Sf4, o.view(nseg, Ls, PF_H, 128), ck4, ws, stream=stream)
 
     ms4 = region_ms(lambda r: run4(), reps, warmup, stream)
-    useful, issued = prefill_flops()
-    io_bytes = (PF_L * h_k * 128 * 2 * 2 + PF_L * PF_H * 128 * 2 +
-                PF_L * PF_H * 4 * 2 + PF_L * PF_H * 128 * 4 +
-                (PF_L // 8192 + 1) * PF_H * 128 * 128 * 4)
-    return {"workload": "1 sequence x 32768 tokens, 32 value / %d key heads, "
-                        "d=128, chunk 64, checkpoints every 8192" % h_k,
-            "ms": ms, "head_tokens_per_s": PF_L * PF_H / (ms * 1e-3),
-            "useful_tflops": useful / (ms * 1e-3) / 1e12,
-            "issued_mfma_tflops": issued / (ms * 1e-3) / 1e12,
-            "mfma_frac_issued": issued / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "mfma_frac_useful": useful / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "io_GBps": io_bytes / (ms * 1e-3) / 1e9,
-            "as_4_sequences_of_8192_ms": ms4,
-            "traffic_p1": measured_traffic("prefill_p1"),
-            "traffic_p2": measured_traffic("prefill_p2"),
-            "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}
+    rec.update({"as_4_sequences_of_8192_ms": ms4,
+                "traffic_p1": measured_traffic("prefill_p1"),
+                "traffic_p2": measured_traffic("prefill_p2"),
+                "peak_mfma_tflops": BF16_MFMA_PEAK_TFLOPS})
+    return rec
 
 
 def bench_t_sweep(ts=(1, 2, 4, 6, 8, 12, 16), reps=20, warmup=3):
@@ -1135,6 +1139,8 @@ def main():
         out["general_shapes"] = bench_general_shapes()
     if not args.no_prefill:
         out["prefill"] = bench_prefill()
+        # the same prefill with 16 key heads (two value heads per key head)
+        out["prefill_h_k16"] = bench_prefill(h_k=16, segments=False)
     if not args.no_snapshot:
         out["state_snapshot"] = bench_snapshot()
         # context for the roofline: what a plain device copy (read + write,
