@@ -68,6 +68,12 @@ SMALL = [
     # kernel, bf16 at d = 128 and f32 at d_k = 64
     ("d128_t64_max_window", 1, 2, 4, 2, 128, 128, 64, True, True, True, 1.0),
     ("d64_t33_f32", 1, 2, 2, 1, 64, 64, 33, False, True, True, 1.0),
+    # the ABI's value-dimension limits: d_v = 1024 on both kernels (bf16:
+    # eight 128-column blocks on the matrix cores; f32: token by token) and
+    # d_v = 1
+    ("d128_dv1024_max", 1, 1, 2, 1, 128, 1024, 6, True, True, True, 1.0),
+    ("f32_d128_dv1024_max", 1, 1, 2, 1, 128, 1024, 5, False, True, True, 1.0),
+    ("d32_dv1_min", 1, 2, 2, 1, 32, 1, 5, True, True, True, 1.0),
 ]
 
 
