@@ -306,6 +306,29 @@ def test_prefill_32k_tokens_32_heads(hk):
     assert e_o <= TOL and e_s <= TOL and e_c <= TOL
 
 
+def test_prefill_longest_sequence_of_the_pages():
+    """The longest prefill the review reports (260,096 tokens: 4,064 chunks
+    of 64, 31 checkpoints at 8,192), on 4 value heads sharing 2 key heads.
+    The oracle runs value heads 0 and 3 (key heads 0 and 1): every
+    checkpoint, S_final and the outputs per 64-token block."""
+    L, Hv, Hk, interval = 260096, 4, 2, 8192
+    heads = [0, 3]
+    say("prefill %d tokens: generating" % L)
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (49,))
+    o, ck, Sf = run_prefill(p, [p], None, interval)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    n_ck = L // interval
+    assert ck.shape[1] == n_ck == 31
+    say("  oracle on value heads", heads)
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, None, interval, heads=heads)
+    e_o = o_err_blocks(o[0][:, heads], o_ref)
+    e_s = s_err(Sf[0][heads], Sf_ref)
+    e_c = max(s_err(ck[0, j][heads], ck_ref[j]) for j in range(n_ck))
+    say("  o err per 64-token block %.2e  S err %.2e  ckpt err %.2e"
+        % (e_o, e_s, e_c))
+    assert e_o <= TOL and e_s <= TOL and e_c <= TOL
+
+
 def test_chunk_sizes_agree():
     """The chunk length is an evaluation detail: chunks of 16, 32 and 64
     tokens give the same outputs, checkpoints and final state within the
