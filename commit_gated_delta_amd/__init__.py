@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "_build",
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_BF16, GDN_F32 = 0, 1
 GDN_FLAG_L2NORM_QK = 1
+GDN_FLAG_PREFILL_ONE_CHAIN = 2
 GDN_MAX_LANES = 256
 GDN_MAX_T = 64
 
@@ -306,17 +307,23 @@ def prefill_workspace_bytes(n_seqs, seq_len, h_v, h_k, d_k, d_v,
                                                d_v, chunk))
 
 
+def _prefill_flags(l2norm, segments):
+    return ((GDN_FLAG_L2NORM_QK if l2norm else 0) |
+            (0 if segments else GDN_FLAG_PREFILL_ONE_CHAIN))
+
+
 def prefill_chunked(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v, beta, g,
                     S_init, S_final, o, checkpoints, workspace,
                     ckpt_interval=8192, scale=1.0, l2norm=True, stream=None,
-                    raw_status=False, chunk=64):
-    """gdn_prefill_chunked on torch tensors."""
+                    raw_status=False, chunk=64, segments=True):
+    """gdn_prefill_chunked on torch tensors (segments=False sets
+    GDN_FLAG_PREFILL_ONE_CHAIN)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_prefill_chunked(
         n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk, ckpt_interval, _ptr(q),
         _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
         _ptr(S_final), _ptr(o), _ptr(checkpoints), _ptr(workspace), ws_bytes,
-        float(scale), GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+        float(scale), _prefill_flags(l2norm, segments), _stream(stream))
     if raw_status:
         return st
     _check(st, "gdn_prefill_chunked")
@@ -325,7 +332,8 @@ def prefill_chunked(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v, beta, g,
 def prefill_chunked_noalloc(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v,
                             beta, g, S_init, S_final, o, checkpoints,
                             ckpt_interval=8192, scale=1.0, l2norm=True,
-                            stream=None, raw_status=False, chunk=64):
+                            stream=None, raw_status=False, chunk=64,
+                            segments=True):
     """gdn_prefill_chunked_noalloc: the prefill with the library's fixed
     scratch array as its workspace (no allocation; calls that overlap on
     one GPU race)."""
@@ -333,7 +341,7 @@ def prefill_chunked_noalloc(n_seqs, seq_len, h_v, h_k, d_k, d_v, q, k, v,
         n_seqs, seq_len, h_v, h_k, d_k, d_v, chunk, ckpt_interval, _ptr(q),
         _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S_init),
         _ptr(S_final), _ptr(o), _ptr(checkpoints), float(scale),
-        GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+        _prefill_flags(l2norm, segments), _stream(stream))
     if raw_status:
         return st
     _check(st, "gdn_prefill_chunked_noalloc")

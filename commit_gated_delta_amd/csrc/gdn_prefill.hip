@@ -45,6 +45,10 @@
 //   Checkpoints: the state after every token count that is a positive
 //   multiple of the interval (context_cache.checkpoint_interval, NInfer
 //   technical review, blog.123qwe.co.kr post 4624, section "Architecture 2").
+//   segments  one sequence with few heads runs as segments of kSeg tokens:
+//       P2 passes give each segment's transition and offset,
+//       seg_scan_kernel chains them, a last P2 pass produces the outputs
+//       (details at seg_scan_kernel below).
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l of a wave holds
 //   A[l%16][8*(l/16) + e], B[8*(l/16) + e][l%16]   (e = 0..7, bf16)
@@ -79,7 +83,12 @@ struct PDims {
   int ckpt_interval;  // 0: no checkpoints
   float scale;
   int l2norm;
+  int mode;           // kMode* bits of a p2 pass of a segmented prefill
 };
+
+// p2 passes of a segmented prefill (see seg_scan_kernel): V taken as zero,
+// no outputs, the chain started from the identity instead of S_init.
+enum { kModeVZero = 1, kModeNoOut = 2, kModeIdentity = 4 };
 
 // Workspace per (sequence, chunk, value head).  T and P are stored as MFMA
 // A-operand fragments, 1 KiB each (lane l: 16 bytes at l*16, so one load or
@@ -528,6 +537,7 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
   r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
   r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
   r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
+  r.mode = __builtin_amdgcn_readfirstlane(a.mode);
   return r;
 }
 
@@ -584,7 +594,8 @@ static __device__ __attribute__((noinline)) void p2_chain(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * mb + 4 * g + e;
-      H[mb][e] = S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
+      H[mb][e] = (d.mode & kModeIdentity) ? (r == col ? 1.f : 0.f)
+                 : S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
     }
   uint32_t hw[4][4], lw[4][4];  // split H, pi order per 32-row k-step
   f32x4 VN[4];                  // V_new rows 16*mi + 4g + e
@@ -916,7 +927,8 @@ static __device__ __attribute__((noinline)) void p2_stage(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-        SVt[buf][(8 * (l & 1) + e) * kSVS + row] = tr.sb[it] * __uint_as_float(b);
+        SVt[buf][(8 * (l & 1) + e) * kSVS + row] =
+            (d.mode & kModeVZero) ? 0.f : tr.sb[it] * __uint_as_float(b);
       }
     }
     reinterpret_cast<uint4*>(Vec[buf])[l] = tr.vec;
@@ -1068,6 +1080,12 @@ static __device__ __attribute__((noinline)) void p2_out(
     }
   };
 
+  if (d.mode & kModeNoOut) {  // the same barriers, nothing else
+    __syncthreads();
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) __syncthreads();
+    return;
+  }
   OutOps A, B;
   ops_load(0, A);
   __syncthreads();  // chunks 0 and 1 staged
@@ -1116,6 +1134,99 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
     p2_stage(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
 }
 
+// ------------------------------------------------------------ segments
+// Sequence-parallel prefill of one long sequence with few heads.  The P2
+// chains are sequential over the chunks, and with h_v heads there are only
+// 8 h_v of them: with fewer chains than CUs the chip idles.  The state after
+// a segment of kSeg tokens is affine in the state before it,
+// H_end = A_s H_start + B_s (stored orientation, A_s d_k x d_k): A_s is the
+// chain run from the identity with V taken as zero, B_s the chain run from
+// zero.  So the prefill runs as
+//   P1 over the whole sequence;
+//   P2 on every segment but the last with kModeVZero | kModeIdentity
+//     (giving A_s) and from zero (giving B_s), both with kModeNoOut;
+//   seg_scan_kernel: H_0 = S_init, H_{s+1} = A_s H_s + B_s;
+//   P2 on every segment from H_s, producing the outputs;
+//   seg_place_kernel: checkpoints and S_final.
+// The segments start at multiples of kSeg, which divides the checkpoint
+// interval, so every checkpoint is a segment boundary and holds the scanned
+// state that the next segment started from.  A prefill resumed from a
+// checkpoint cuts its segments at the same tokens, starts its scan from that
+// state and repeats the same operations: it reproduces the rest bit for bit.
+constexpr int kSeg = 4096;       // tokens per segment (a multiple of every chunk)
+constexpr int kSegMaxHeads = 8;  // at most 64 chains: below a quarter of the CUs
+
+// H_{s+1} = A_s H_s + B_s for s = 0..S-2, per head, in f32 (each sum over
+// the 128 products in order, then + B).  One workgroup per (head, 16-column
+// tile), sequential over the segments; A_s is staged in LDS and the column
+// tile of H_s stays there.  Hs[0] is S_init (zero when absent).
+__global__ __launch_bounds__(256) void seg_scan_kernel(
+    const float* __restrict__ A, const float* __restrict__ B,
+    const float* __restrict__ S_init, float* __restrict__ Hs, int S, int Hv) {
+  __shared__ __attribute__((aligned(16))) float As[kD][kD + 4];
+  __shared__ float Ht[kD][kTile + 1];
+  const int h = blockIdx.x / (kD / kTile), tile = blockIdx.x % (kD / kTile);
+  const int tid = threadIdx.x;
+  const int c = tid % kTile, r0 = (tid / kTile) * 8;  // 8 rows, one column
+  const int col = kTile * tile + c;
+  const size_t head = (size_t)kD * kD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + i;
+    const float x = S_init ? S_init[h * head + r * kD + col] : 0.f;
+    Ht[r][c] = x;
+    Hs[h * head + r * kD + col] = x;
+  }
+  for (int sg = 0; sg + 1 < S; ++sg) {
+    const float* Ag = A + ((size_t)sg * Hv + h) * head;
+    const float* Bg = B + ((size_t)sg * Hv + h) * head;
+    __syncthreads();  // Ht complete, As free
+    for (int x = tid; x < kD * kD / 4; x += 256) {
+      const int r = x / (kD / 4), cc = 4 * (x % (kD / 4));
+      *reinterpret_cast<float4*>(&As[r][cc]) = reinterpret_cast<const float4*>(Ag)[x];
+    }
+    __syncthreads();
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < kD; ++j) {
+      const float hj = Ht[j][c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(As[r0 + i][j], hj, acc[i]);
+    }
+    __syncthreads();  // every read of Ht done
+    float* Hn = Hs + ((size_t)(sg + 1) * Hv + h) * head;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = r0 + i;
+      const float x = acc[i] + Bg[r * kD + col];
+      Ht[r][c] = x;
+      Hn[r * kD + col] = x;
+    }
+  }
+}
+
+// Checkpoints and S_final of a segmented prefill, one workgroup per (job,
+// head).  Job j < n_ck is checkpoint j, the state at token
+// (j + 1) * interval: the start state of segment b = (j + 1) * segs_per_ck
+// (the scanned state), or the last segment's end state when b = S (the end
+// of the sequence).  Job n_ck is S_final, the last segment's end state.
+__global__ __launch_bounds__(256) void seg_place_kernel(
+    const float* __restrict__ Hs, const float* __restrict__ Send,
+    float* __restrict__ ckpt, float* __restrict__ S_final, int n_ck,
+    int segs_per_ck, int S, int Hv) {
+  const int job = blockIdx.x / Hv, h = blockIdx.x % Hv;
+  const size_t head = (size_t)kD * kD;
+  const float* src = Send + ((size_t)(S - 1) * Hv + h) * head;
+  float* dst = S_final + (size_t)h * head;
+  if (job < n_ck) {
+    const int b = (job + 1) * segs_per_ck;
+    if (b < S) src = Hs + ((size_t)b * Hv + h) * head;
+    dst = ckpt + ((size_t)job * Hv + h) * head;
+  }
+  for (int x = threadIdx.x; x < kD * kD; x += 256) dst[x] = src[x];
+}
+
 // ------------------------------------------------------------------ host
 static int fail(int status, const char* msg) {
   gdn::set_error(msg);
@@ -1139,9 +1250,44 @@ static bool misaligned(const void* p, size_t a) {
 // so their X, V_new and D rows are exact zeros and T is the identity on
 // them (L has zero rows there); they add nothing to the state and their
 // output rows are never stored.
-static size_t ws_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
+static size_t p1_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
   const size_t n_chunks = ((size_t)L + C - 1) / C;
   return (size_t)n_seqs * n_chunks * Hv * WsLayout::kBytes;
+}
+
+// Sizes for which a prefill may run in segments (one sequence, few heads,
+// more than one segment); whether it does also depends on the checkpoint
+// interval and the flags (use_segments).
+static bool segment_sizes(int32_t n_seqs, int32_t L, int32_t Hv) {
+  return n_seqs == 1 && Hv <= kSegMaxHeads && L > kSeg;
+}
+
+static bool use_segments(int32_t n_seqs, int32_t L, int32_t Hv,
+                         const float* checkpoints, int32_t ckpt_interval,
+                         int flags) {
+  return segment_sizes(n_seqs, L, Hv) && !(flags & GDN_FLAG_PREFILL_ONE_CHAIN) &&
+         (!checkpoints || ckpt_interval % kSeg == 0);
+}
+
+// Segment buffers after the P1 workspace: A_s and B_s of every segment but
+// the last, the scanned start state and the end state of every segment.
+struct SegLayout {
+  int S;
+  size_t a, b, hs, send, end;
+  SegLayout(int32_t L, int32_t Hv, size_t p1) {
+    const size_t st = (size_t)Hv * kD * kD * sizeof(float);
+    S = (L + kSeg - 1) / kSeg;
+    a = (p1 + 255) & ~size_t(255);
+    b = a + (size_t)(S - 1) * st;
+    hs = b + (size_t)(S - 1) * st;
+    send = hs + (size_t)S * st;
+    end = send + (size_t)S * st;
+  }
+};
+
+static size_t ws_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
+  const size_t p1 = p1_bytes(n_seqs, L, Hv, C);
+  return segment_sizes(n_seqs, L, Hv) ? SegLayout(L, Hv, p1).end : p1;
 }
 
 static int check_sizes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t Hk,
@@ -1229,7 +1375,7 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
   if (in_dtype != GDN_BF16) {
     return fail(in_dtype == GDN_F32 ? GDN_EUNSUPPORTED : GDN_EINVAL, "prefill: bf16 inputs only");
   }
-  if (flags & ~GDN_FLAG_L2NORM_QK) {
+  if (flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_PREFILL_ONE_CHAIN)) {
     return fail(GDN_EINVAL, "prefill: unknown flag bits");
   }
   if (checkpoints && (ckpt_interval < chunk || ckpt_interval % chunk != 0)) {
@@ -1247,7 +1393,22 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
   return GDN_OK;
 }
 
-// Launches P1 and P2 (arguments already checked).
+static int launch_p2(const PDims& dd, int n_seqs, const u16* qq,
+                     const u16* kk, const u16* vv, const uint8_t* ws,
+                     const float* S_init, float* S_final, float* o,
+                     float* checkpoints, hipStream_t st) {
+  PDims d = dd;
+  d.n_seqs = n_seqs;
+  void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&ws,
+                  (void*)&S_init, (void*)&S_final, (void*)&o,
+                  (void*)&checkpoints, (void*)&d};
+  hipError_t e = hipLaunchKernel((const void*)p2_kernel,
+                                 dim3(n_seqs * d.Hv * (kD / kTile)),
+                                 dim3(kP2Threads), args, 0, st);
+  return e == hipSuccess ? GDN_OK : hip_fail("prefill p2 launch", e);
+}
+
+// Launches P1 and P2, or the segmented passes (arguments already checked).
 static int prefill_launch(
     int32_t n_seqs, int32_t seq_len, int32_t h_v, int32_t h_k, int32_t chunk,
     int32_t ckpt_interval, const void* q, const void* k, const void* v,
@@ -1265,6 +1426,7 @@ static int prefill_launch(
   dd.ckpt_interval = checkpoints ? ckpt_interval : 0;
   dd.scale = scale;
   dd.l2norm = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+  dd.mode = 0;
   hipStream_t st = (hipStream_t)stream;
 
   const u16* qq = (const u16*)q;
@@ -1279,15 +1441,65 @@ static int prefill_launch(
                                    dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill p1 launch", e);
   }
+  if (!use_segments(n_seqs, seq_len, h_v, checkpoints, ckpt_interval, flags)) {
+    return launch_p2(dd, n_seqs, qq, kk, vv, wsb, S_init, S_final, o,
+                     checkpoints, st);
+  }
+  // Segments: every segment is a sequence of kSeg tokens for P2 (the P1
+  // workspace is indexed by the chunk over the whole sequence, which is
+  // the segment-major chunk index); a shorter last segment runs on its own.
+  const SegLayout sl(seq_len, h_v, p1_bytes(1, seq_len, h_v, chunk));
+  const int S = sl.S, full = seq_len / kSeg, tail = seq_len - full * kSeg;
+  float* A = reinterpret_cast<float*>(wsb + sl.a);
+  float* B = reinterpret_cast<float*>(wsb + sl.b);
+  float* Hs = reinterpret_cast<float*>(wsb + sl.hs);
+  float* Send = reinterpret_cast<float*>(wsb + sl.send);
+  const size_t st_floats = (size_t)h_v * kD * kD;
+  PDims ds = dd;
+  ds.L = kSeg;
+  ds.n_chunks = kSeg / chunk;
+  ds.ckpt_interval = 0;
+  int rc;
+  ds.mode = kModeVZero | kModeNoOut | kModeIdentity;
+  rc = launch_p2(ds, S - 1, qq, kk, vv, wsb, nullptr, A, o, nullptr, st);
+  if (rc != GDN_OK) return rc;
+  ds.mode = kModeNoOut;
+  rc = launch_p2(ds, S - 1, qq, kk, vv, wsb, nullptr, B, o, nullptr, st);
+  if (rc != GDN_OK) return rc;
   {
-    const uint8_t* wsc = wsb;
-    void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&wsc,
-                    (void*)&S_init, (void*)&S_final, (void*)&o,
-                    (void*)&checkpoints, (void*)&dd};
-    hipError_t e = hipLaunchKernel((const void*)p2_kernel,
-                                   dim3(n_seqs * h_v * (kD / kTile)),
-                                   dim3(kP2Threads), args, 0, st);
-    if (e != hipSuccess) return hip_fail("prefill p2 launch", e);
+    void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
+                    (void*)&S, (void*)&h_v};
+    hipError_t e = hipLaunchKernel((const void*)seg_scan_kernel,
+                                   dim3(h_v * (kD / kTile)), dim3(256), args,
+                                   0, st);
+    if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
+  }
+  ds.mode = 0;
+  rc = launch_p2(ds, full, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
+  if (rc != GDN_OK) return rc;
+  if (tail > 0) {
+    const size_t t0 = (size_t)full * kSeg;
+    PDims dt = dd;
+    dt.L = tail;
+    dt.n_chunks = (tail + chunk - 1) / chunk;
+    dt.ckpt_interval = 0;
+    rc = launch_p2(dt, 1, qq + t0 * h_k * kD, kk + t0 * h_k * kD,
+                   vv + t0 * h_v * kD,
+                   wsb + (size_t)(full * (kSeg / chunk)) * h_v * WsLayout::kBytes,
+                   Hs + (size_t)full * st_floats, Send + (size_t)full * st_floats,
+                   o + t0 * h_v * kD, nullptr, st);
+    if (rc != GDN_OK) return rc;
+  }
+  {
+    int n_ck = checkpoints ? seq_len / ckpt_interval : 0;
+    int per = checkpoints ? ckpt_interval / kSeg : 1;
+    float* ck = checkpoints;
+    void* args[] = {(void*)&Hs, (void*)&Send, (void*)&ck, (void*)&S_final,
+                    (void*)&n_ck, (void*)&per, (void*)&S, (void*)&h_v};
+    hipError_t e = hipLaunchKernel((const void*)seg_place_kernel,
+                                   dim3((n_ck + 1) * h_v), dim3(256), args, 0,
+                                   st);
+    if (e != hipSuccess) return hip_fail("prefill segment placement launch", e);
   }
   return GDN_OK;
 }

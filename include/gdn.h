@@ -92,7 +92,10 @@ typedef enum {
 
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 
-enum { GDN_FLAG_L2NORM_QK = 1 }; /* normalise q and k inside the kernels */
+enum {
+  GDN_FLAG_L2NORM_QK = 1,        /* normalise q and k inside the kernels */
+  GDN_FLAG_PREFILL_ONE_CHAIN = 2 /* gdn_prefill_chunked*: never in segments */
+};
 
 typedef struct {
   int32_t n_layers; /* >= 1: independent layers batched in one call       */
@@ -273,7 +276,22 @@ size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
  *   ckpt_interval  positive multiple of chunk
  *   workspace    device, ws_bytes >= gdn_prefill_workspace_bytes(...);
  *                scratch owned by the caller, contents undefined on return
- *   scale, flags as for gdn_verify
+ *   scale        as for gdn_verify
+ *   flags        GDN_FLAG_L2NORM_QK, GDN_FLAG_PREFILL_ONE_CHAIN, or 0
+ * Segments: the chunk steps form one sequential chain per (head, 16 value
+ * columns), so a sequence with few heads leaves most of the GPU idle.  One
+ * sequence (n_seqs = 1) of more than 4,096 tokens with at most 8 value heads
+ * therefore runs in segments of 4,096 tokens, when checkpoints are off or
+ * their interval is a multiple of 4,096.  The state at a segment's end is
+ * affine in its start state (the rule is linear in the state, so the maps
+ * of consecutive tokens compose): each segment's
+ * transition and offset are formed in parallel, scanned in f32, and the
+ * segments then produce their outputs from the scanned start states.  The
+ * results agree with the one-chain evaluation to rounding, not bit for bit;
+ * checkpoints sit on segment boundaries, so a resumed prefill still
+ * reproduces the rest bit for bit.  GDN_FLAG_PREFILL_ONE_CHAIN keeps the
+ * one chain.  The workspace query includes room for the segments whenever
+ * the sizes allow them.
  * Supported: d_k == d_v == 128, in_dtype == GDN_BF16 (q, k, v enter the
  * matrix cores as bf16; GDN_F32 returns GDN_EUNSUPPORTED).  The state,
  * decays and every accumulation are f32.  S_final and every checkpoint are

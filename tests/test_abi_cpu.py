@@ -254,6 +254,20 @@ def test_prefill_workspace_bytes():
             4 * gdn.prefill_workspace_bytes(1, 4096, 2, 2, 128, 128, 64))
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 48) == 0
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 0) == 0
+    # one sequence of more than 4,096 tokens with at most 8 heads may run in
+    # segments: room for each segment's transition and offset (all but the
+    # last), and the start and end state of every segment (64 KiB per head)
+    L, H = 3 * 4096 + 1000, 4
+    per_chunk = gdn.prefill_workspace_bytes(1, 4096, 32, 32, 128, 128) // (64 * 32)
+    p1 = (L + 63) // 64 * H * per_chunk
+    seg = ((p1 + 255) // 256 * 256) + (2 * 3 + 2 * 4) * H * 65536
+    assert gdn.prefill_workspace_bytes(1, L, H, H, 128, 128) == seg
+    # not for two sequences, more than 8 heads, or one segment
+    assert gdn.prefill_workspace_bytes(2, L, H, H, 128, 128) == 2 * p1
+    assert (gdn.prefill_workspace_bytes(1, L, 16, 16, 128, 128) ==
+            (L + 63) // 64 * 16 * per_chunk)
+    assert (gdn.prefill_workspace_bytes(1, 4096, H, H, 128, 128) ==
+            64 * H * per_chunk)
 
 
 def _prefill(**over):
@@ -279,7 +293,8 @@ def _prefill(**over):
                                a["g"], a["Si"], a["Sf"], a["o"], a["ck"],
                                _WS(a["ws_bytes"]),
                                ckpt_interval=a["interval"], stream=0,
-                               raw_status=True, chunk=a.get("chunk", 64))
+                               raw_status=True, chunk=a.get("chunk", 64),
+                               segments=a.get("segments", True))
 
 
 def test_prefill_rejects_bad_arguments_on_host():
@@ -294,6 +309,16 @@ def test_prefill_rejects_bad_arguments_on_host():
     assert _prefill(ws_bytes=1024) == gdn.GDN_EWORKSPACE
     assert _prefill(q=_Fake(addr=(1 << 20) + 8)) == gdn.GDN_EINVAL
     assert b"prefill" in gdn.lib.gdn_last_error()
+    # flag bits: the norm and the one-chain flag only (the accepted flag
+    # lets the call go on to the workspace check)
+    assert _prefill(segments=False, ws_bytes=1024) == gdn.GDN_EWORKSPACE
+    P = gdn._ptr
+    st = gdn.lib.gdn_prefill_chunked(
+        1, 256, 2, 1, 128, 128, 64, 128, P(_Fake()), P(_Fake()), P(_Fake()),
+        gdn.GDN_BF16, P(_Fake(gdn.GDN_F32)), P(_Fake(gdn.GDN_F32)), None,
+        P(_Fake(gdn.GDN_F32)), P(_Fake(gdn.GDN_F32)), None,
+        P(_Fake(gdn.GDN_F32)), 1 << 30, 1.0, 4, None)
+    assert st == gdn.GDN_EINVAL and b"flag" in gdn.lib.gdn_last_error()
     # chunk length: 16, 32 or 64; the interval must be a multiple of it
     assert _prefill(chunk=48) == gdn.GDN_EUNSUPPORTED
     assert _prefill(chunk=128) == gdn.GDN_EUNSUPPORTED

@@ -29,7 +29,7 @@ def say(*a):
 
 
 def run_prefill(p, n_seqs_inputs, S_init=None, ckpt_interval=8192, scale=1.0,
-                l2norm=True, chunk=64):
+                l2norm=True, chunk=64, segments=True):
     """p: list of PrefillInputs (one per sequence, equal shapes)."""
     n_seqs = len(n_seqs_inputs)
     L, Hv, Hk = p.seq_len, p.h_v, p.h_k
@@ -47,7 +47,7 @@ def run_prefill(p, n_seqs_inputs, S_init=None, ckpt_interval=8192, scale=1.0,
                      dtype=torch.uint8, device="cuda")
     gdn.prefill_chunked(n_seqs, L, Hv, Hk, 128, 128, q, k, v, beta, g, Si, Sf,
                         o, ck, ws, ckpt_interval=ckpt_interval, scale=scale,
-                        l2norm=l2norm, chunk=chunk)
+                        l2norm=l2norm, chunk=chunk, segments=segments)
     torch.cuda.synchronize()
     return (o.cpu().numpy(), None if ck is None else ck.cpu().numpy(),
             Sf.cpu().numpy())
@@ -326,6 +326,101 @@ def test_prefill_longest_sequence_of_the_pages():
     e_c = max(s_err(ck[0, j][heads], ck_ref[j]) for j in range(n_ck))
     say("  o err per 64-token block %.2e  S err %.2e  ckpt err %.2e"
         % (e_o, e_s, e_c))
+    assert e_o <= TOL and e_s <= TOL and e_c <= TOL
+
+
+SEG = 4096  # tokens per segment of a segmented prefill
+
+
+def _long_memory_inputs(L, Hv, Hk, key):
+    """Prefill inputs whose state is remembered across a segment: slow
+    gates (g = -softplus(N(-8, 1)), alpha^4096 ~ 0.25) and small write
+    strengths (beta scaled by 0.02).  With the default synthetic gates and
+    beta a chain forgets its start state within a few hundred tokens, and
+    chains started from different states meet bit for bit long before a
+    segment ends."""
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, key, g_mean=-8.0)
+    p.beta[...] *= 0.02
+    return p
+
+
+def _tail_inputs(p, t):
+    return gs.PrefillInputs(p.seq_len - t, p.h_v, p.h_k, 128, 128, True,
+                            p.q[t:], p.k[t:], p.v[t:], p.beta[t:], p.g[t:])
+
+
+def test_segmented_prefill_parity():
+    """One sequence with few heads runs in segments of 4,096 tokens (each
+    segment's transition and offset, a scan over the segments, then the
+    outputs per segment).  Three full segments and a ragged tail, with an
+    initial state and checkpoints at every segment boundary: the outputs
+    per 64-token block, every checkpoint and S_final against the oracle.
+    The same call with GDN_FLAG_PREFILL_ONE_CHAIN (one chain over the whole
+    sequence) meets the same bar and agrees with it, but not bit for bit:
+    the segments really ran."""
+    L, Hv, Hk, interval = 3 * SEG + 1000, 2, 1, SEG
+    p = _long_memory_inputs(L, Hv, Hk, (50,))
+    S0 = gs.prefill_state(Hv, 128, 128, (50,))[None]
+    seg = run_prefill(p, [p], S0, interval)
+    one = run_prefill(p, [p], S0, interval, segments=False)
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, S0[0].astype(np.float64),
+                                           interval)
+    for name, (o, ck, Sf) in (("segments", seg), ("one chain", one)):
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+        e_o, e_s = o_err_blocks(o[0], o_ref), s_err(Sf[0], Sf_ref)
+        e_c = max(s_err(ck[0, j], ck_ref[j]) for j in range(L // interval))
+        say("  %s: o err %.2e  S err %.2e  ckpt err %.2e"
+            % (name, e_o, e_s, e_c))
+        assert e_o <= TOL and e_s <= TOL and e_c <= TOL
+    assert o_err_blocks(seg[0][0], one[0][0]) <= TOL
+    assert s_err(seg[2][0], one[2][0]) <= TOL
+    assert not np.array_equal(seg[2], one[2])
+
+
+def test_segmented_prefill_resumes_bitwise():
+    """Checkpoints every 8,192 tokens (two segments per interval): a prefill
+    resumed from any checkpoint, itself in segments or a single segment,
+    reproduces the rest bit for bit; a sequence that ends on a checkpoint
+    has that checkpoint equal to S_final."""
+    L, Hv, Hk, interval = 2 * 8192 + 3000, 2, 2, 8192
+    p = _long_memory_inputs(L, Hv, Hk, (51,))
+    o, ck, Sf = run_prefill(p, [p], None, interval)
+    for j in range(L // interval):
+        t = interval * (j + 1)
+        tail = _tail_inputs(p, t)
+        o2, _, Sf2 = run_prefill(tail, [tail], ck[:, j], interval)
+        assert np.array_equal(Sf2, Sf), j
+        assert np.array_equal(o2[0], o[0, t:]), j
+    p2 = _long_memory_inputs(2 * 8192, Hv, Hk, (52,))
+    _, ck2, Sf2 = run_prefill(p2, [p2], None, interval)
+    assert np.array_equal(ck2[0, 1], Sf2[0])
+    _, ck3, Sf3 = run_prefill(_tail_inputs(p2, 8192), [_tail_inputs(p2, 8192)],
+                              ck2[:, 0], interval)
+    assert np.array_equal(Sf3, Sf2)
+
+
+def test_prefill_interval_off_the_segment_grid_runs_one_chain():
+    """A checkpoint interval that is not a multiple of the segment length
+    would put checkpoints inside segments: such a prefill runs as one chain,
+    bit for bit the call with GDN_FLAG_PREFILL_ONE_CHAIN."""
+    L, Hv, Hk, interval = 2 * SEG + 100, 2, 1, 2048
+    p = gs.prefill_inputs(L, Hv, Hk, 128, 128, (53,))
+    a = run_prefill(p, [p], None, interval)
+    b = run_prefill(p, [p], None, interval, segments=False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_segmented_prefill_chunk16():
+    """Segments with 16-token chunks (256 chunks per segment) and a short
+    tail, against the oracle."""
+    L, Hv, Hk, interval = SEG + 500, 2, 2, SEG
+    p = _long_memory_inputs(L, Hv, Hk, (54,))
+    o, ck, Sf = run_prefill(p, [p], None, interval, chunk=16)
+    o_ref, ck_ref, Sf_ref = oracle_prefill(p, None, interval)
+    e_o, e_s = o_err_blocks(o[0], o_ref), s_err(Sf[0], Sf_ref)
+    e_c = s_err(ck[0, 0], ck_ref[0])
+    say("  o err %.2e  S err %.2e  ckpt err %.2e" % (e_o, e_s, e_c))
     assert e_o <= TOL and e_s <= TOL and e_c <= TOL
 
 
