@@ -83,11 +83,11 @@ struct PDims {
   int ckpt_interval;  // 0: no checkpoints
   float scale;
   int l2norm;
-  int mode;           // kMode* bits of a p2 pass of a segmented prefill
 };
 
-// p2 passes of a segmented prefill (see seg_scan_kernel): V taken as zero,
-// no outputs, the chain started from the identity instead of S_init.
+// p2 passes of a segmented prefill (see seg_scan_kernel), a template
+// argument of p2_kernel: V taken as zero, no outputs, the chain started from
+// the identity instead of S_init.  Mode 0 is the plain pass.
 enum { kModeVZero = 1, kModeNoOut = 2, kModeIdentity = 4 };
 
 // Workspace per (sequence, chunk, value head).  T and P are stored as MFMA
@@ -537,7 +537,6 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
   r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
   r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
   r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
-  r.mode = __builtin_amdgcn_readfirstlane(a.mode);
   return r;
 }
 
@@ -545,6 +544,7 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
 // registers for each on its own (inlined into one kernel, the barriers that
 // both roles execute get merged and the state of both roles is kept live
 // at once).
+template <int MODE>
 static __device__ __attribute__((noinline)) void p2_chain(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
     const float* S_init_, float* S_final_, float* o_, float* ckpt_,
@@ -594,8 +594,10 @@ static __device__ __attribute__((noinline)) void p2_chain(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * mb + 4 * g + e;
-      H[mb][e] = (d.mode & kModeIdentity) ? (r == col ? 1.f : 0.f)
-                 : S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
+      if constexpr ((MODE & kModeIdentity) != 0)
+        H[mb][e] = r == col ? 1.f : 0.f;
+      else
+        H[mb][e] = S_init ? S_init[(((size_t)s * d.Hv + h) * kD + r) * kD + col] : 0.f;
     }
   uint32_t hw[4][4], lw[4][4];  // split H, pi order per 32-row k-step
   f32x4 VN[4];                  // V_new rows 16*mi + 4g + e
@@ -850,6 +852,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
 // Staging wave: the K rows, the T fragments, sb V and the row vectors of
 // chunk c + 2 are written to LDS in interval c (loaded during interval
 // c - 1).
+template <int MODE>
 static __device__ __attribute__((noinline)) void p2_stage(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
     const float* S_init_, float* S_final_, float* o_, float* ckpt_,
@@ -928,7 +931,7 @@ static __device__ __attribute__((noinline)) void p2_stage(
       for (int e = 0; e < 8; ++e) {
         const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
         SVt[buf][(8 * (l & 1) + e) * kSVS + row] =
-            (d.mode & kModeVZero) ? 0.f : tr.sb[it] * __uint_as_float(b);
+            (MODE & kModeVZero) ? 0.f : tr.sb[it] * __uint_as_float(b);
       }
     }
     reinterpret_cast<uint4*>(Vec[buf])[l] = tr.vec;
@@ -957,6 +960,7 @@ static __device__ __attribute__((noinline)) void p2_stage(
 // XCD, same L2) each touch one eighth of the cache lines that the head's
 // workgroups will load for that chunk, one dword per lane, so that the
 // loads issued one or two chunks ahead find their data in L2.
+template <int MODE>
 static __device__ __attribute__((noinline)) void p2_out(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
     const float* S_init_, float* S_final_, float* o_, float* ckpt_,
@@ -1080,7 +1084,7 @@ static __device__ __attribute__((noinline)) void p2_out(
     }
   };
 
-  if (d.mode & kModeNoOut) {  // the same barriers, nothing else
+  if constexpr ((MODE & kModeNoOut) != 0) {  // the same barriers, nothing else
     __syncthreads();
     __syncthreads();
     for (int c = 0; c < nch; ++c) __syncthreads();
@@ -1112,6 +1116,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   asm volatile("" ::"v"(w0), "v"(w1));
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kP2Threads) void p2_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k,
     const u16* __restrict__ v, const uint8_t* __restrict__ ws,
@@ -1127,11 +1132,11 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
   const int kh = h / d.group;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   if (w == 0)
-    p2_chain(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+    p2_chain<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
   else if (w < 3)
-    p2_out(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, w - 1);
+    p2_out<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, w - 1);
   else
-    p2_stage(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+    p2_stage<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
 }
 
 // ------------------------------------------------------------ segments
@@ -1393,7 +1398,7 @@ static int check_args(int32_t n_seqs, int32_t seq_len, int32_t h_v,
   return GDN_OK;
 }
 
-static int launch_p2(const PDims& dd, int n_seqs, const u16* qq,
+static int launch_p2(int mode, const PDims& dd, int n_seqs, const u16* qq,
                      const u16* kk, const u16* vv, const uint8_t* ws,
                      const float* S_init, float* S_final, float* o,
                      float* checkpoints, hipStream_t st) {
@@ -1402,7 +1407,11 @@ static int launch_p2(const PDims& dd, int n_seqs, const u16* qq,
   void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&ws,
                   (void*)&S_init, (void*)&S_final, (void*)&o,
                   (void*)&checkpoints, (void*)&d};
-  hipError_t e = hipLaunchKernel((const void*)p2_kernel,
+  const void* fn =
+      mode == 0 ? (const void*)p2_kernel<0>
+      : mode == kModeNoOut ? (const void*)p2_kernel<kModeNoOut>
+      : (const void*)p2_kernel<kModeVZero | kModeNoOut | kModeIdentity>;
+  hipError_t e = hipLaunchKernel(fn,
                                  dim3(n_seqs * d.Hv * (kD / kTile)),
                                  dim3(kP2Threads), args, 0, st);
   return e == hipSuccess ? GDN_OK : hip_fail("prefill p2 launch", e);
@@ -1426,7 +1435,6 @@ static int prefill_launch(
   dd.ckpt_interval = checkpoints ? ckpt_interval : 0;
   dd.scale = scale;
   dd.l2norm = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
-  dd.mode = 0;
   hipStream_t st = (hipStream_t)stream;
 
   const u16* qq = (const u16*)q;
@@ -1442,7 +1450,7 @@ static int prefill_launch(
     if (e != hipSuccess) return hip_fail("prefill p1 launch", e);
   }
   if (!use_segments(n_seqs, seq_len, h_v, checkpoints, ckpt_interval, flags)) {
-    return launch_p2(dd, n_seqs, qq, kk, vv, wsb, S_init, S_final, o,
+    return launch_p2(0, dd, n_seqs, qq, kk, vv, wsb, S_init, S_final, o,
                      checkpoints, st);
   }
   // Segments: every segment is a sequence of kSeg tokens for P2 (the P1
@@ -1459,12 +1467,11 @@ static int prefill_launch(
   ds.L = kSeg;
   ds.n_chunks = kSeg / chunk;
   ds.ckpt_interval = 0;
-  int rc;
-  ds.mode = kModeVZero | kModeNoOut | kModeIdentity;
-  rc = launch_p2(ds, S - 1, qq, kk, vv, wsb, nullptr, A, o, nullptr, st);
+  int rc = launch_p2(kModeVZero | kModeNoOut | kModeIdentity, ds, S - 1, qq, kk,
+                     vv, wsb, nullptr, A, o, nullptr, st);
   if (rc != GDN_OK) return rc;
-  ds.mode = kModeNoOut;
-  rc = launch_p2(ds, S - 1, qq, kk, vv, wsb, nullptr, B, o, nullptr, st);
+  rc = launch_p2(kModeNoOut, ds, S - 1, qq, kk, vv, wsb, nullptr, B, o, nullptr,
+                 st);
   if (rc != GDN_OK) return rc;
   {
     void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
@@ -1474,8 +1481,7 @@ static int prefill_launch(
                                    0, st);
     if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
   }
-  ds.mode = 0;
-  rc = launch_p2(ds, full, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
+  rc = launch_p2(0, ds, full, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
   if (rc != GDN_OK) return rc;
   if (tail > 0) {
     const size_t t0 = (size_t)full * kSeg;
@@ -1483,7 +1489,7 @@ static int prefill_launch(
     dt.L = tail;
     dt.n_chunks = (tail + chunk - 1) / chunk;
     dt.ckpt_interval = 0;
-    rc = launch_p2(dt, 1, qq + t0 * h_k * kD, kk + t0 * h_k * kD,
+    rc = launch_p2(0, dt, 1, qq + t0 * h_k * kD, kk + t0 * h_k * kD,
                    vv + t0 * h_v * kD,
                    wsb + (size_t)(full * (kSeg / chunk)) * h_v * WsLayout::kBytes,
                    Hs + (size_t)full * st_floats, Send + (size_t)full * st_floats,
