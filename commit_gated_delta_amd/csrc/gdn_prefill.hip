@@ -85,10 +85,12 @@ struct PDims {
   int l2norm;
 };
 
-// p2 passes of a segmented prefill (see seg_scan_kernel), a template
-// argument of p2_kernel: V taken as zero, no outputs, the chain started from
-// the identity instead of S_init.  Mode 0 is the plain pass.
-enum { kModeVZero = 1, kModeNoOut = 2, kModeIdentity = 4 };
+// Template arguments of the p2 roles for a segmented prefill (see
+// seg_scan_kernel): a chain with V taken as zero, or started from the
+// identity instead of S_init; output waves that only warm L2.  p2_kernel's
+// own argument is 0 (the plain pass) or kModePair (two chains of one
+// segment tile side by side, see p2_kernel).
+enum { kModeVZero = 1, kModeNoOut = 2, kModeIdentity = 4, kModePair = 8 };
 
 // Workspace per (sequence, chunk, value head).  T and P are stored as MFMA
 // A-operand fragments, 1 KiB each (lane l: 16 bytes at l*16, so one load or
@@ -667,7 +669,10 @@ static __device__ __attribute__((noinline)) void p2_chain(
     }
 #pragma unroll
     for (int mj = 0; mj < 4; ++mj) {
-      SV[mj] = *reinterpret_cast<const f32x4*>(&SVt[B][n * kSVS + 16 * mj + 4 * g]);
+      if constexpr ((MODE & kModeVZero) != 0)
+        SV[mj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      else
+        SV[mj] = *reinterpret_cast<const f32x4*>(&SVt[B][n * kSVS + 16 * mj + 4 * g]);
       SK[mj] = *reinterpret_cast<const f32x4*>(&Vec[B][kC + 16 * mj + 4 * g]);
     }
   };
@@ -852,7 +857,6 @@ static __device__ __attribute__((noinline)) void p2_chain(
 // Staging wave: the K rows, the T fragments, sb V and the row vectors of
 // chunk c + 2 are written to LDS in interval c (loaded during interval
 // c - 1).
-template <int MODE>
 static __device__ __attribute__((noinline)) void p2_stage(
     const u16* q_, const u16* k_, const u16* v_, const uint8_t* ws_,
     const float* S_init_, float* S_final_, float* o_, float* ckpt_,
@@ -930,8 +934,7 @@ static __device__ __attribute__((noinline)) void p2_stage(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-        SVt[buf][(8 * (l & 1) + e) * kSVS + row] =
-            (MODE & kModeVZero) ? 0.f : tr.sb[it] * __uint_as_float(b);
+        SVt[buf][(8 * (l & 1) + e) * kSVS + row] = tr.sb[it] * __uint_as_float(b);
       }
     }
     reinterpret_cast<uint4*>(Vec[buf])[l] = tr.vec;
@@ -999,7 +1002,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   // workgroup `tile` as u = 128*tile + 64*ow + l (lines past the end are
   // clamped to the last one)
   const int u = 128 * tile + 64 * ow + l;
-  auto warm = [&](int c) -> uint32_t {
+  auto warm_at = [&](int c, int u) -> uint32_t {
     const int t0 = c * d.chunk;
     const int last = min(d.chunk, d.L - t0) - 1;
     const int row = min((u & 127) >> 1, last), half = u & 1;
@@ -1015,6 +1018,7 @@ static __device__ __attribute__((noinline)) void p2_out(
           wss + (size_t)c * ws_chunk + min((size_t)(u - 384) * 128, WsLayout::kBytes - 4));
     return *p;
   };
+  auto warm = [&](int c) { return warm_at(c, u); };
   auto ops_load = [&](int c, OutOps& op) {
     const int t0 = c * d.chunk;
     const int last = min(d.chunk, d.L - t0) - 1;
@@ -1084,10 +1088,20 @@ static __device__ __attribute__((noinline)) void p2_out(
     }
   };
 
-  if constexpr ((MODE & kModeNoOut) != 0) {  // the same barriers, nothing else
+  if constexpr ((MODE & kModeNoOut) != 0) {
+    // the barriers and the L2 warm-up of both output waves' lines
     __syncthreads();
     __syncthreads();
-    for (int c = 0; c < nch; ++c) __syncthreads();
+    uint32_t w0 = 0, w1 = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int cw = min(c + kWarm, nch - 1);
+      const uint32_t w2 = warm_at(cw, u) ^ warm_at(cw, u + 64);
+      asm volatile("" ::"v"(w0));
+      w0 = w1;
+      w1 = w2;
+      __syncthreads();
+    }
+    asm volatile("" ::"v"(w0), "v"(w1));
     return;
   }
   OutOps A, B;
@@ -1131,12 +1145,30 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
   const int s = b / ((kD / kTile) * d.Hv);
   const int kh = h / d.group;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  if (w == 0)
-    p2_chain<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
-  else if (w < 3)
-    p2_out<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, w - 1);
-  else
-    p2_stage<MODE>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+  if constexpr (MODE == kModePair) {
+    // One segment and column tile, two chains on one staging: wave 0 runs
+    // the chain from the identity with V taken as zero (its end state, the
+    // segment's transition A_s, goes to S_final), wave 1 the chain from zero
+    // (the offset B_s, to the array passed as o: a pair pass writes no
+    // outputs).  Wave 2 only warms L2.  Both chains publish H and V_new to
+    // the same LDS buffers, which nothing reads in this pass.
+    if (w == 0)
+      p2_chain<kModeIdentity | kModeVZero>(q, k, v, ws, nullptr, S_final, o,
+                                           nullptr, d, tile, h, s, kh);
+    else if (w == 1)
+      p2_chain<0>(q, k, v, ws, nullptr, o, o, nullptr, d, tile, h, s, kh);
+    else if (w == 2)
+      p2_out<kModeNoOut>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, 0);
+    else
+      p2_stage(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+  } else {
+    if (w == 0)
+      p2_chain<0>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+    else if (w < 3)
+      p2_out<0>(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh, w - 1);
+    else
+      p2_stage(q, k, v, ws, S_init, S_final, o, ckpt, d, tile, h, s, kh);
+  }
 }
 
 // ------------------------------------------------------------ segments
@@ -1148,8 +1180,10 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
 // chain run from the identity with V taken as zero, B_s the chain run from
 // zero.  So the prefill runs as
 //   P1 over the whole sequence;
-//   P2 on every segment but the last with kModeVZero | kModeIdentity
-//     (giving A_s) and from zero (giving B_s), both with kModeNoOut;
+//   P2 on every segment but the last as kModePair: in one workgroup per
+//     segment and column tile, the chain from the identity with V taken as
+//     zero (giving A_s) and the chain from zero (giving B_s) share one
+//     staging of the segment's operands;
 //   seg_scan_kernel: H_0 = S_init, H_{s+1} = A_s H_s + B_s;
 //   P2 on every segment from H_s, producing the outputs;
 //   seg_place_kernel: checkpoints and S_final.
@@ -1407,10 +1441,8 @@ static int launch_p2(int mode, const PDims& dd, int n_seqs, const u16* qq,
   void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&ws,
                   (void*)&S_init, (void*)&S_final, (void*)&o,
                   (void*)&checkpoints, (void*)&d};
-  const void* fn =
-      mode == 0 ? (const void*)p2_kernel<0>
-      : mode == kModeNoOut ? (const void*)p2_kernel<kModeNoOut>
-      : (const void*)p2_kernel<kModeVZero | kModeNoOut | kModeIdentity>;
+  const void* fn = mode == kModePair ? (const void*)p2_kernel<kModePair>
+                                     : (const void*)p2_kernel<0>;
   hipError_t e = hipLaunchKernel(fn,
                                  dim3(n_seqs * d.Hv * (kD / kTile)),
                                  dim3(kP2Threads), args, 0, st);
@@ -1467,11 +1499,9 @@ static int prefill_launch(
   ds.L = kSeg;
   ds.n_chunks = kSeg / chunk;
   ds.ckpt_interval = 0;
-  int rc = launch_p2(kModeVZero | kModeNoOut | kModeIdentity, ds, S - 1, qq, kk,
-                     vv, wsb, nullptr, A, o, nullptr, st);
-  if (rc != GDN_OK) return rc;
-  rc = launch_p2(kModeNoOut, ds, S - 1, qq, kk, vv, wsb, nullptr, B, o, nullptr,
-                 st);
+  // A_s to S_final's place, B_s to o's (see p2_kernel)
+  int rc = launch_p2(kModePair, ds, S - 1, qq, kk, vv, wsb, nullptr, A, B,
+                     nullptr, st);
   if (rc != GDN_OK) return rc;
   {
     void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
