@@ -1196,52 +1196,52 @@ constexpr int kSeg = 4096;       // tokens per segment (a multiple of every chun
 constexpr int kSegMaxHeads = 8;  // at most 64 chains: below a quarter of the CUs
 
 // H_{s+1} = A_s H_s + B_s for s = 0..S-2, per head, in f32 (each sum over
-// the 128 products in order, then + B).  One workgroup per (head, 16-column
-// tile), sequential over the segments; A_s is staged in LDS and the column
-// tile of H_s stays there.  Hs[0] is S_init (zero when absent).
-__global__ __launch_bounds__(256) void seg_scan_kernel(
+// the 128 products in order of j, then + B).  One workgroup of 128 threads
+// per (head, 4-column tile of d_v), sequential over the segments: thread r
+// owns row r of the tile and reads row r of A_s straight from memory (no
+// other thread of the workgroup uses it), issued before the wait for the
+// previous step; the tile of H_s (128 x 4) stays in LDS.  Hs[0] is S_init
+// (zero when absent).
+constexpr int kScanCols = 4;
+__global__ __launch_bounds__(kD) void seg_scan_kernel(
     const float* __restrict__ A, const float* __restrict__ B,
     const float* __restrict__ S_init, float* __restrict__ Hs, int S, int Hv) {
-  __shared__ __attribute__((aligned(16))) float As[kD][kD + 4];
-  __shared__ float Ht[kD][kTile + 1];
-  const int h = blockIdx.x / (kD / kTile), tile = blockIdx.x % (kD / kTile);
-  const int tid = threadIdx.x;
-  const int c = tid % kTile, r0 = (tid / kTile) * 8;  // 8 rows, one column
-  const int col = kTile * tile + c;
+  __shared__ float4 Ht[kD];  // row j of the tile of H_s
+  const int tiles = kD / kScanCols;
+  const int h = blockIdx.x / tiles, c0 = kScanCols * (blockIdx.x % tiles);
+  const int r = threadIdx.x;
   const size_t head = (size_t)kD * kD;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + i;
-    const float x = S_init ? S_init[h * head + r * kD + col] : 0.f;
-    Ht[r][c] = x;
-    Hs[h * head + r * kD + col] = x;
-  }
+  const size_t off = (size_t)h * head + (size_t)r * kD + c0;  // 16-byte aligned
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (S_init)  // a caller's array, 4-byte aligned only
+    x = make_float4(S_init[off], S_init[off + 1], S_init[off + 2], S_init[off + 3]);
+  Ht[r] = x;
+  *reinterpret_cast<float4*>(Hs + off) = x;
   for (int sg = 0; sg + 1 < S; ++sg) {
-    const float* Ag = A + ((size_t)sg * Hv + h) * head;
-    const float* Bg = B + ((size_t)sg * Hv + h) * head;
-    __syncthreads();  // Ht complete, As free
-    for (int x = tid; x < kD * kD / 4; x += 256) {
-      const int r = x / (kD / 4), cc = 4 * (x % (kD / 4));
-      *reinterpret_cast<float4*>(&As[r][cc]) = reinterpret_cast<const float4*>(Ag)[x];
-    }
-    __syncthreads();
-    float acc[8];
+    const size_t base = (size_t)sg * Hv * head;
+    float4 a[kD / 4];
+    const float4* Ar = reinterpret_cast<const float4*>(A + base + (size_t)h * head + (size_t)r * kD);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < kD; ++j) {
-      const float hj = Ht[j][c];
+    for (int q = 0; q < kD / 4; ++q) a[q] = Ar[q];
+    const float4 b = *reinterpret_cast<const float4*>(B + base + off);
+    __syncthreads();  // the tile of H_s is complete
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(As[r0 + i][j], hj, acc[i]);
-    }
-    __syncthreads();  // every read of Ht done
-    float* Hn = Hs + ((size_t)(sg + 1) * Hv + h) * head;
+    for (int q = 0; q < kD / 4; ++q) {
+      const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = r0 + i;
-      const float x = acc[i] + Bg[r * kD + col];
-      Ht[r][c] = x;
-      Hn[r * kD + col] = x;
+      for (int e = 0; e < 4; ++e) {
+        const float4 hj = Ht[4 * q + e];
+        acc.x = __builtin_fmaf(av[e], hj.x, acc.x);
+        acc.y = __builtin_fmaf(av[e], hj.y, acc.y);
+        acc.z = __builtin_fmaf(av[e], hj.z, acc.z);
+        acc.w = __builtin_fmaf(av[e], hj.w, acc.w);
+      }
     }
+    __syncthreads();  // every read of the tile done
+    x = make_float4(acc.x + b.x, acc.y + b.y, acc.z + b.z, acc.w + b.w);
+    Ht[r] = x;
+    *reinterpret_cast<float4*>(Hs + base + (size_t)Hv * head + off) = x;
   }
 }
 
@@ -1507,8 +1507,8 @@ static int prefill_launch(
     void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
                     (void*)&S, (void*)&h_v};
     hipError_t e = hipLaunchKernel((const void*)seg_scan_kernel,
-                                   dim3(h_v * (kD / kTile)), dim3(256), args,
-                                   0, st);
+                                   dim3(h_v * (kD / kScanCols)), dim3(kD),
+                                   args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
   }
   rc = launch_p2(0, ds, full, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
