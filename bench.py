@@ -977,6 +977,9 @@ def main():
                     help="time only the token-by-token kernel shapes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
+    ap.add_argument("--prefill-long-only", action="store_true",
+                    help="time only the 260,096-token prefill of 4 heads, in "
+                         "segments and as one chain (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB f32 copy kernel (y = x * 1) "
                          "before the timed region, as the reference point "
@@ -1012,6 +1015,10 @@ def main():
         print(json.dumps({"prefill": bench_prefill(reps=args.steps,
                                                    warmup=args.warmup)}),
               flush=True)
+        return
+    if args.prefill_long_only:
+        print(json.dumps({"prefill_long_few_heads": bench_prefill_long(
+            reps=args.steps, warmup=args.warmup)}), flush=True)
         return
     shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
     dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)

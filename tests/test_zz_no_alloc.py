@@ -57,6 +57,9 @@ def _run(noalloc, n_seqs, L, Hv, Hk, interval, ins):
     # first, and its chunk-head blocks sit where the first call left data
     ((2, 1000, 8, 4, 256), (1, 333, 4, 4, 128)),
     ((1, 4096, 16, 16, 1024), (1, 100, 2, 1, 64)),
+    # both calls in segments (one sequence, few heads, more than 4,096
+    # tokens): the segment buffers live in the scratch array too
+    ((1, 3 * 4096 + 500, 2, 1, 4096), (1, 4096 + 64, 2, 2, 4096)),
 ])
 def test_noalloc_matches_workspace_entry_point(sizes):
     for i, (n, L, Hv, Hk, iv) in enumerate(sizes):
