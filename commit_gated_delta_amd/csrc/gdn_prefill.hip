@@ -78,7 +78,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 struct PDims {
-  int n_seqs, L, Hv, Hk, group, n_chunks;
+  int n_seqs, L, Hv, Hk, group, n_chunks;  // L, n_chunks: per sequence
+  int L_last;         // tokens of sequence n_seqs - 1 (<= L; sequences are
+                      // still L tokens and n_chunks chunks apart)
   int chunk;          // tokens per chunk: 16, 32 or 64 (<= kC)
   int ckpt_interval;  // 0: no checkpoints
   float scale;
@@ -536,6 +538,7 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
   r.group = __builtin_amdgcn_readfirstlane(a.group);
   r.n_chunks = __builtin_amdgcn_readfirstlane(a.n_chunks);
   r.chunk = __builtin_amdgcn_readfirstlane(a.chunk);
+  r.L_last = __builtin_amdgcn_readfirstlane(a.L_last);
   r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
   r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
   r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
@@ -577,14 +580,16 @@ static __device__ __attribute__((noinline)) void p2_chain(
   const int n = l % 16;   // result column inside the tile
   const int g = l / 16;   // lane group
   const int col = kTile * tile + n;
-  const int nch = d.n_chunks;
+  // the last sequence may be shorter (the tail of a segmented prefill)
+  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  const int nch = (Ls + d.chunk - 1) / d.chunk;
   // per-sequence bases; element offsets below fit in 32 bits (host check)
   const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
   float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)wss; (void)ws_chunk;
   (void)Kr; (void)Tf; (void)SVt; (void)Vec; (void)Hf; (void)Vf; (void)col;
@@ -816,7 +821,7 @@ static __device__ __attribute__((noinline)) void p2_chain(
     split_pi(H[6], H[7], hw[3], lw[3]);
     publish_pair(NB, 3);
     kh_step(3);
-    const int t0 = c * d.chunk, nv = min(d.chunk, d.L - t0);
+    const int t0 = c * d.chunk, nv = min(d.chunk, Ls - t0);
     // checkpoint after token t0 + nv when it is a multiple of the interval
     if (d.ckpt_interval > 0 && ckpt && (t0 + nv) % d.ckpt_interval == 0) {
       const int idx = (t0 + nv) / d.ckpt_interval - 1;
@@ -876,13 +881,15 @@ static __device__ __attribute__((noinline)) void p2_stage(
   const int n = l % 16;
   const int g = l / 16;
   const int col = kTile * tile + n;
-  const int nch = d.n_chunks;
+  // the last sequence may be shorter (the tail of a segmented prefill)
+  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  const int nch = (Ls + d.chunk - 1) / d.chunk;
   const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
   float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
   auto& Kr = p2lds.Kr;
@@ -891,7 +898,7 @@ static __device__ __attribute__((noinline)) void p2_stage(
   auto& Vec = p2lds.Vec;
   auto load = [&](int c, KvTransit& tr) {
     const int t0 = c * d.chunk;
-    const int last = min(d.chunk, d.L - t0) - 1;
+    const int last = min(d.chunk, Ls - t0) - 1;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + l;
@@ -983,13 +990,15 @@ static __device__ __attribute__((noinline)) void p2_out(
   const int n = l % 16;
   const int g = l / 16;
   const int col = kTile * tile + n;
-  const int nch = d.n_chunks;
+  // the last sequence may be shorter (the tail of a segmented prefill)
+  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  const int nch = (Ls + d.chunk - 1) / d.chunk;
   const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
   const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
   float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * nch * d.Hv + h) * WsLayout::kBytes;
+      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
   auto& Vec = p2lds.Vec;
@@ -1004,7 +1013,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   const int u = 128 * tile + 64 * ow + l;
   auto warm_at = [&](int c, int u) -> uint32_t {
     const int t0 = c * d.chunk;
-    const int last = min(d.chunk, d.L - t0) - 1;
+    const int last = min(d.chunk, Ls - t0) - 1;
     const int row = min((u & 127) >> 1, last), half = u & 1;
     const uint32_t* p;
     if (u < 128)
@@ -1021,7 +1030,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   auto warm = [&](int c) { return warm_at(c, u); };
   auto ops_load = [&](int c, OutOps& op) {
     const int t0 = c * d.chunk;
-    const int last = min(d.chunk, d.L - t0) - 1;
+    const int last = min(d.chunk, Ls - t0) - 1;
     const uint32_t ra = ((uint32_t)(t0 + min(16 * mA + n, last)) * d.Hk + kh) * kD + 8 * g;
     const uint32_t rb = ((uint32_t)(t0 + min(16 * mB + n, last)) * d.Hk + kh) * kD + 8 * g;
 #pragma unroll
@@ -1039,7 +1048,7 @@ static __device__ __attribute__((noinline)) void p2_out(
   };
   auto outputs = [&](int c, const OutOps& op) {
     const int hb = c % 3, bb = c % 3;
-    const int t0 = c * d.chunk, nv = min(d.chunk, d.L - t0);
+    const int t0 = c * d.chunk, nv = min(d.chunk, Ls - t0);
     f32x4 QA = {0.f, 0.f, 0.f, 0.f}, QB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -1464,6 +1473,7 @@ static int prefill_launch(
   dd.group = h_v / h_k;
   dd.chunk = chunk;
   dd.n_chunks = (seq_len + chunk - 1) / chunk;
+  dd.L_last = seq_len;
   dd.ckpt_interval = checkpoints ? ckpt_interval : 0;
   dd.scale = scale;
   dd.l2norm = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
@@ -1487,16 +1497,16 @@ static int prefill_launch(
   }
   // Segments: every segment is a sequence of kSeg tokens for P2 (the P1
   // workspace is indexed by the chunk over the whole sequence, which is
-  // the segment-major chunk index); a shorter last segment runs on its own.
+  // the segment-major chunk index); the last one may be shorter.
   const SegLayout sl(seq_len, h_v, p1_bytes(1, seq_len, h_v, chunk));
-  const int S = sl.S, full = seq_len / kSeg, tail = seq_len - full * kSeg;
+  const int S = sl.S, tail = seq_len - (S - 1) * kSeg;
   float* A = reinterpret_cast<float*>(wsb + sl.a);
   float* B = reinterpret_cast<float*>(wsb + sl.b);
   float* Hs = reinterpret_cast<float*>(wsb + sl.hs);
   float* Send = reinterpret_cast<float*>(wsb + sl.send);
-  const size_t st_floats = (size_t)h_v * kD * kD;
   PDims ds = dd;
   ds.L = kSeg;
+  ds.L_last = kSeg;
   ds.n_chunks = kSeg / chunk;
   ds.ckpt_interval = 0;
   // A_s to S_final's place, B_s to o's (see p2_kernel)
@@ -1511,21 +1521,10 @@ static int prefill_launch(
                                    args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
   }
-  rc = launch_p2(0, ds, full, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
+  // the outputs of every segment, the last one with its own length
+  ds.L_last = tail;
+  rc = launch_p2(0, ds, S, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
   if (rc != GDN_OK) return rc;
-  if (tail > 0) {
-    const size_t t0 = (size_t)full * kSeg;
-    PDims dt = dd;
-    dt.L = tail;
-    dt.n_chunks = (tail + chunk - 1) / chunk;
-    dt.ckpt_interval = 0;
-    rc = launch_p2(0, dt, 1, qq + t0 * h_k * kD, kk + t0 * h_k * kD,
-                   vv + t0 * h_v * kD,
-                   wsb + (size_t)(full * (kSeg / chunk)) * h_v * WsLayout::kBytes,
-                   Hs + (size_t)full * st_floats, Send + (size_t)full * st_floats,
-                   o + t0 * h_v * kD, nullptr, st);
-    if (rc != GDN_OK) return rc;
-  }
   {
     int n_ck = checkpoints ? seq_len / ckpt_interval : 0;
     int per = checkpoints ? ckpt_interval / kSeg : 1;
