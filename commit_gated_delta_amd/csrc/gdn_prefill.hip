@@ -1204,53 +1204,147 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
 constexpr int kSeg = 4096;       // tokens per segment (a multiple of every chunk)
 constexpr int kSegMaxHeads = 8;  // at most 64 chains: below a quarter of the CUs
 
-// H_{s+1} = A_s H_s + B_s for s = 0..S-2, per head, in f32 (each sum over
-// the 128 products in order of j, then + B).  One workgroup of 128 threads
-// per (head, 4-column tile of d_v), sequential over the segments: thread r
-// owns row r of the tile and reads row r of A_s straight from memory (no
-// other thread of the workgroup uses it), issued before the wait for the
-// previous step; the tile of H_s (128 x 4) stays in LDS.  Hs[0] is S_init
-// (zero when absent).
-constexpr int kScanCols = 4;
-__global__ __launch_bounds__(kD) void seg_scan_kernel(
+// The scan H_{s+1} = A_s H_s + B_s (s = 0..S-2, per head) is a chain of
+// dense 128 x 128 x 128 products, run on the matrix cores with f32-grade
+// accuracy: each f32 operand is split into three bf16 parts, x = x1 + x2 +
+// x3 + O(2^-27 |x|), and the product takes the six part products of order
+// at most 2^-16 (a1 h1, a1 h2, a2 h1, a1 h3, a2 h2, a3 h1) with f32
+// accumulation; the dropped ones are below 2^-24 of |a||h|.
+//
+// One workgroup of eight waves per (head, 16-column tile of d_v); wave w
+// produces row block w (rows 16w..16w+15).  The 128 contraction indices run
+// as four k-steps p of 32, k-step p pairing H rows 32p + 4q + e (k-slot
+// 8q + e) and 32p + 16 + 4q + e (k-slot 8q + 4 + e) for q = 0..3, e = 0..3:
+// the rows that lane 16q + n holds in the result tiles of waves 2p and
+// 2p + 1 (row 16 w + 4q + e, column n).  So each wave publishes its new rows
+// as one half of k-step p's B fragments, and the A fragment of lane 16q + n
+// is A_s[16w + n][32p + 4q + 0..3] and A_s[16w + n][32p + 16 + 4q + 0..3]:
+// two float4 loads.  Step s loads A_{s+1} and B_{s+1} while its MFMAs run
+// and splits A_{s+1} after them; one barrier per step.  Measured on this
+// chain, the loads' latency from L2 and beyond, not the MFMAs, sets the
+// step time.
+constexpr int kScanLevels = 3;
+constexpr int kScanWaves = kD / 16;
+constexpr int kScanFrags = 4 * kScanLevels;  // per lane: (k-step, level)
+
+// Three-level bf16 split of two f32 values, packed as bf16 pairs.
+__device__ __forceinline__ void split3(float a, float b, uint32_t& w1,
+                                       uint32_t& w2, uint32_t& w3) {
+  uint32_t r;
+  split2(a, b, w1, r);
+  const float ra = a - __uint_as_float(w1 << 16) - __uint_as_float(r << 16);
+  const float rb = b - __uint_as_float(w1 & 0xffff0000u) - __uint_as_float(r & 0xffff0000u);
+  w2 = r;
+  const f32x2 x = {ra, rb};
+  w3 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// Hs[0] is S_init (zero when absent); Hs[s + 1] = A_s Hs[s] + B_s.
+__global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
     const float* __restrict__ A, const float* __restrict__ B,
     const float* __restrict__ S_init, float* __restrict__ Hs, int S, int Hv) {
-  __shared__ float4 Ht[kD];  // row j of the tile of H_s
-  const int tiles = kD / kScanCols;
-  const int h = blockIdx.x / tiles, c0 = kScanCols * (blockIdx.x % tiles);
-  const int r = threadIdx.x;
+  __shared__ uint4 Hb[2][4][kScanLevels][64];  // [buffer][k-step][level][lane]
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;  // a head's tiles on one XCD
+  const int h = bid / (kD / kTile), c0 = kTile * (bid % (kD / kTile));
+  const int w = threadIdx.x / 64, l = threadIdx.x % 64, q = l / 16, n = l % 16;
   const size_t head = (size_t)kD * kD;
-  const size_t off = (size_t)h * head + (size_t)r * kD + c0;  // 16-byte aligned
-  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (S_init)  // a caller's array, 4-byte aligned only
-    x = make_float4(S_init[off], S_init[off + 1], S_init[off + 2], S_init[off + 3]);
-  Ht[r] = x;
-  *reinterpret_cast<float4*>(Hs + off) = x;
-  for (int sg = 0; sg + 1 < S; ++sg) {
-    const size_t base = (size_t)sg * Hv * head;
-    float4 a[kD / 4];
-    const float4* Ar = reinterpret_cast<const float4*>(A + base + (size_t)h * head + (size_t)r * kD);
+  // element e of this lane's result tile: row 16w + 4q + e, column c0 + n
+  auto at = [&](int e) -> size_t {
+    return (size_t)(16 * w + 4 * q + e) * kD + c0 + n;
+  };
+  // this wave's rows as half (w % 2) of the B fragments of k-step w / 2
+  auto publish = [&](int buf, const f32x4& t) {
+    uint32_t w1[2], w2[2], w3[2];
+    split3(t[0], t[1], w1[0], w2[0], w3[0]);
+    split3(t[2], t[3], w1[1], w2[1], w3[1]);
+    reinterpret_cast<uint2*>(&Hb[buf][w / 2][0][l])[w % 2] = make_uint2(w1[0], w1[1]);
+    reinterpret_cast<uint2*>(&Hb[buf][w / 2][1][l])[w % 2] = make_uint2(w2[0], w2[1]);
+    reinterpret_cast<uint2*>(&Hb[buf][w / 2][2][l])[w % 2] = make_uint2(w3[0], w3[1]);
+  };
+  {
+    const float* Si = S_init ? S_init + (size_t)h * head : nullptr;
+    float* H0 = Hs + (size_t)h * head;
+    f32x4 x;
 #pragma unroll
-    for (int q = 0; q < kD / 4; ++q) a[q] = Ar[q];
-    const float4 b = *reinterpret_cast<const float4*>(B + base + off);
-    __syncthreads();  // the tile of H_s is complete
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int q = 0; q < kD / 4; ++q) {
-      const float av[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 hj = Ht[4 * q + e];
-        acc.x = __builtin_fmaf(av[e], hj.x, acc.x);
-        acc.y = __builtin_fmaf(av[e], hj.y, acc.y);
-        acc.z = __builtin_fmaf(av[e], hj.z, acc.z);
-        acc.w = __builtin_fmaf(av[e], hj.w, acc.w);
-      }
+    for (int e = 0; e < 4; ++e) {
+      x[e] = Si ? Si[at(e)] : 0.f;
+      H0[at(e)] = x[e];
     }
-    __syncthreads();  // every read of the tile done
-    x = make_float4(acc.x + b.x, acc.y + b.y, acc.z + b.z, acc.w + b.w);
-    Ht[r] = x;
-    *reinterpret_cast<float4*>(Hs + base + (size_t)Hv * head + off) = x;
+    publish(0, x);
+  }
+  auto load = [&](int sg, float4 (&ra)[8], float (&rb)[4]) {
+    const float* row = A + (size_t)(sg * Hv + h) * head + (size_t)(16 * w + n) * kD;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      ra[2 * p] = *reinterpret_cast<const float4*>(row + 32 * p + 4 * q);
+      ra[2 * p + 1] = *reinterpret_cast<const float4*>(row + 32 * p + 16 + 4 * q);
+    }
+    const float* Bs = B + (size_t)(sg * Hv + h) * head;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rb[e] = Bs[at(e)];
+  };
+  auto split = [&](const float4 (&ra)[8], uint4 (&fa)[kScanFrags]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float4 x0 = ra[2 * p], x1 = ra[2 * p + 1];
+      uint32_t w1[4], w2[4], w3[4];
+      split3(x0.x, x0.y, w1[0], w2[0], w3[0]);
+      split3(x0.z, x0.w, w1[1], w2[1], w3[1]);
+      split3(x1.x, x1.y, w1[2], w2[2], w3[2]);
+      split3(x1.z, x1.w, w1[3], w2[3], w3[3]);
+      fa[kScanLevels * p + 0] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      fa[kScanLevels * p + 1] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+      fa[kScanLevels * p + 2] = make_uint4(w3[0], w3[1], w3[2], w3[3]);
+    }
+  };
+  // step sg: A_s split in a, B_s in b; leaves A_{s+1} split in na, B_{s+1}
+  // in nbv (the last step reloads its own: no branch around the loads)
+  auto step = [&](int sg, const uint4 (&a)[kScanFrags], const float (&b)[4],
+                  uint4 (&na)[kScanFrags], float (&nbv)[4]) {
+    const int cur = sg & 1;
+    float4 ra[8];
+    load(min(sg + 1, S - 2), ra, nbv);
+    __builtin_amdgcn_sched_barrier(0);  // loads issued before the MFMAs
+    // two accumulators (even and odd k-steps), smallest parts first
+    f32x4 t = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bf16x8 h1 = as_bf16x8(Hb[cur][p][0][l]);
+      const bf16x8 h2 = as_bf16x8(Hb[cur][p][1][l]);
+      const bf16x8 h3 = as_bf16x8(Hb[cur][p][2][l]);
+      const uint4* f = a + kScanLevels * p;
+      const bf16x8 a1 = as_bf16x8(f[0]), a2 = as_bf16x8(f[1]), a3 = as_bf16x8(f[2]);
+      f32x4& acc = (p & 1) ? u : t;
+      acc = mfma(a3, h1, acc);
+      acc = mfma(a2, h2, acc);
+      acc = mfma(a1, h3, acc);
+      acc = mfma(a2, h1, acc);
+      acc = mfma(a1, h2, acc);
+      acc = mfma(a1, h1, acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    split(ra, na);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (t[e] + u[e]) + b[e];
+    float* Hn = Hs + (size_t)((sg + 1) * Hv + h) * head;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Hn[at(e)] = t[e];
+    publish(cur ^ 1, t);
+    __syncthreads();  // H_{s+1} complete in the other buffer
+  };
+  uint4 a0[kScanFrags], a1[kScanFrags];
+  float b0[4], b1[4];
+  if (S > 1) {
+    float4 ra[8];
+    load(0, ra, b0);
+    split(ra, a0);
+  }
+  __syncthreads();  // H_0 published
+  for (int sg = 0; sg + 1 < S; sg += 2) {
+    step(sg, a0, b0, a1, b1);
+    if (sg + 2 < S) step(sg + 1, a1, b1, a0, b0);
   }
 }
 
@@ -1517,8 +1611,8 @@ static int prefill_launch(
     void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
                     (void*)&S, (void*)&h_v};
     hipError_t e = hipLaunchKernel((const void*)seg_scan_kernel,
-                                   dim3(h_v * (kD / kScanCols)), dim3(kD),
-                                   args, 0, st);
+                                   dim3(h_v * (kD / kTile)),
+                                   dim3(64 * kScanWaves), args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
   }
   // the outputs of every segment, the last one with its own length
