@@ -284,7 +284,7 @@ def bench_prefill_long(reps=3, warmup=1, L=260096, h_v=4, h_k=2):
     """The longest prefill the review reports (260,096 tokens, checkpoints
     every 8,192) on 4 value / 2 key heads -- one GPU's share of 32 heads
     spread over eight -- in segments of 4,096 tokens (the library's choice
-    for one sequence with at most 8 heads) and as one chain
+    for batches of at most 8 sequence-heads) and as one chain
     (GDN_FLAG_PREFILL_ONE_CHAIN), timed by region_ms."""
     import torch
     import gdn_synth as gs

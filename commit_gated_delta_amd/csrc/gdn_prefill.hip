@@ -45,10 +45,10 @@
 //   Checkpoints: the state after every token count that is a positive
 //   multiple of the interval (context_cache.checkpoint_interval, NInfer
 //   technical review, blog.123qwe.co.kr post 4624, section "Architecture 2").
-//   segments  one sequence with few heads runs as segments of kSeg tokens:
-//       P2 passes give each segment's transition and offset,
-//       seg_scan_kernel chains them, a last P2 pass produces the outputs
-//       (details at seg_scan_kernel below).
+//   segments  a batch of at most kSegMaxHeads sequence-heads runs as
+//       segments of kSeg tokens: P2 passes give each segment's transition
+//       and offset, seg_scan_kernel chains them, a last P2 pass produces the
+//       outputs (details in the segments section below).
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l of a wave holds
 //   A[l%16][8*(l/16) + e], B[8*(l/16) + e][l%16]   (e = 0..7, bf16)
@@ -78,9 +78,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 struct PDims {
-  int n_seqs, L, Hv, Hk, group, n_chunks;  // L, n_chunks: per sequence
-  int L_last;         // tokens of sequence n_seqs - 1 (<= L; sequences are
-                      // still L tokens and n_chunks chunks apart)
+  int n_seqs, L, Hv, Hk, group, n_chunks;  // n_seqs parts of L tokens
+  // A P2 launch runs n_seqs parts; part s is piece s % segs of sequence
+  // s / segs (segs = 1: every part a whole sequence).  Piece j starts at
+  // token j * L of its sequence of seq_L tokens (seq_chunks chunks); the
+  // last piece of each sequence has L_last <= L tokens.  P1 takes whole
+  // sequences (segs = 1, seq_L = L_last = L).
+  int segs, seq_L, seq_chunks, L_last;
   int chunk;          // tokens per chunk: 16, 32 or 64 (<= kC)
   int ckpt_interval;  // 0: no checkpoints
   float scale;
@@ -538,11 +542,29 @@ __device__ __forceinline__ PDims uniform_dims(const PDims& a) {
   r.group = __builtin_amdgcn_readfirstlane(a.group);
   r.n_chunks = __builtin_amdgcn_readfirstlane(a.n_chunks);
   r.chunk = __builtin_amdgcn_readfirstlane(a.chunk);
+  r.segs = __builtin_amdgcn_readfirstlane(a.segs);
+  r.seq_L = __builtin_amdgcn_readfirstlane(a.seq_L);
+  r.seq_chunks = __builtin_amdgcn_readfirstlane(a.seq_chunks);
   r.L_last = __builtin_amdgcn_readfirstlane(a.L_last);
   r.ckpt_interval = __builtin_amdgcn_readfirstlane(a.ckpt_interval);
   r.scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale)));
   r.l2norm = __builtin_amdgcn_readfirstlane(a.l2norm);
   return r;
+}
+
+// Where part s of a P2 launch lies: its first token and first chunk
+// within the whole batch, and its length.
+struct PartPos {
+  size_t t0, c0;
+  int len;
+};
+__device__ __forceinline__ PartPos part_pos(const PDims& d, int s) {
+  const int seq = s / d.segs, j = s - seq * d.segs;
+  PartPos p;
+  p.t0 = (size_t)seq * d.seq_L + (size_t)j * d.L;
+  p.c0 = (size_t)seq * d.seq_chunks + (size_t)j * d.n_chunks;
+  p.len = j == d.segs - 1 ? d.L_last : d.L;
+  return p;
 }
 
 // The two roles are separate functions so that the compiler allocates
@@ -580,16 +602,17 @@ static __device__ __attribute__((noinline)) void p2_chain(
   const int n = l % 16;   // result column inside the tile
   const int g = l / 16;   // lane group
   const int col = kTile * tile + n;
-  // the last sequence may be shorter (the tail of a segmented prefill)
-  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  // the last piece of a sequence may be shorter (segmented prefill)
+  const PartPos pp = part_pos(d, s);
+  const int Ls = pp.len;
   const int nch = (Ls + d.chunk - 1) / d.chunk;
   // per-sequence bases; element offsets below fit in 32 bits (host check)
-  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
-  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const u16* __restrict__ qs = q + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ kseq = k + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ vs = v + pp.t0 * d.Hv * kD;
+  float* __restrict__ os = o + pp.t0 * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
+      ws + (pp.c0 * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)wss; (void)ws_chunk;
   (void)Kr; (void)Tf; (void)SVt; (void)Vec; (void)Hf; (void)Vf; (void)col;
@@ -881,15 +904,16 @@ static __device__ __attribute__((noinline)) void p2_stage(
   const int n = l % 16;
   const int g = l / 16;
   const int col = kTile * tile + n;
-  // the last sequence may be shorter (the tail of a segmented prefill)
-  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  // the last piece of a sequence may be shorter (segmented prefill)
+  const PartPos pp = part_pos(d, s);
+  const int Ls = pp.len;
   const int nch = (Ls + d.chunk - 1) / d.chunk;
-  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
-  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const u16* __restrict__ qs = q + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ kseq = k + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ vs = v + pp.t0 * d.Hv * kD;
+  float* __restrict__ os = o + pp.t0 * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
+      ws + (pp.c0 * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
   auto& Kr = p2lds.Kr;
@@ -990,15 +1014,16 @@ static __device__ __attribute__((noinline)) void p2_out(
   const int n = l % 16;
   const int g = l / 16;
   const int col = kTile * tile + n;
-  // the last sequence may be shorter (the tail of a segmented prefill)
-  const int Ls = s == d.n_seqs - 1 ? d.L_last : d.L;
+  // the last piece of a sequence may be shorter (segmented prefill)
+  const PartPos pp = part_pos(d, s);
+  const int Ls = pp.len;
   const int nch = (Ls + d.chunk - 1) / d.chunk;
-  const u16* __restrict__ qs = q + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ kseq = k + (size_t)s * d.L * d.Hk * kD;
-  const u16* __restrict__ vs = v + (size_t)s * d.L * d.Hv * kD;
-  float* __restrict__ os = o + (size_t)s * d.L * d.Hv * kD;
+  const u16* __restrict__ qs = q + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ kseq = k + pp.t0 * d.Hk * kD;
+  const u16* __restrict__ vs = v + pp.t0 * d.Hv * kD;
+  float* __restrict__ os = o + pp.t0 * d.Hv * kD;
   const uint8_t* __restrict__ wss =
-      ws + ((size_t)s * d.n_chunks * d.Hv + h) * WsLayout::kBytes;
+      ws + (pp.c0 * d.Hv + h) * WsLayout::kBytes;
   const size_t ws_chunk = (size_t)d.Hv * WsLayout::kBytes;
   (void)qs; (void)kseq; (void)vs; (void)os; (void)col; (void)g; (void)kh;
   auto& Vec = p2lds.Vec;
@@ -1181,18 +1206,18 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
 }
 
 // ------------------------------------------------------------ segments
-// Sequence-parallel prefill of one long sequence with few heads.  The P2
-// chains are sequential over the chunks, and with h_v heads there are only
-// 8 h_v of them: with fewer chains than CUs the chip idles.  The state after
+// Sequence-parallel prefill of a batch with few sequence-heads.  The P2
+// chains are sequential over the chunks, and n_seqs sequences of h_v heads
+// make only 8 n_seqs h_v of them: with fewer chains than CUs the chip idles.  The state after
 // a segment of kSeg tokens is affine in the state before it,
 // H_end = A_s H_start + B_s (stored orientation, A_s d_k x d_k): A_s is the
 // chain run from the identity with V taken as zero, B_s the chain run from
 // zero.  So the prefill runs as
-//   P1 over the whole sequence;
-//   P2 on every segment but the last as kModePair: in one workgroup per
-//     segment and column tile, the chain from the identity with V taken as
-//     zero (giving A_s) and the chain from zero (giving B_s) share one
-//     staging of the segment's operands;
+//   P1 over the whole sequences;
+//   P2 on every segment but the last of each sequence as kModePair: in
+//     one workgroup per segment and column tile, the chain from the
+//     identity with V taken as zero (giving A_s) and the chain from zero
+//     (giving B_s) share one staging of the segment's operands;
 //   seg_scan_kernel: H_0 = S_init, H_{s+1} = A_s H_s + B_s;
 //   P2 on every segment from H_s, producing the outputs;
 //   seg_place_kernel: checkpoints and S_final.
@@ -1202,7 +1227,7 @@ __global__ __launch_bounds__(kP2Threads) void p2_kernel(
 // checkpoint cuts its segments at the same tokens, starts its scan from that
 // state and repeats the same operations: it reproduces the rest bit for bit.
 constexpr int kSeg = 4096;       // tokens per segment (a multiple of every chunk)
-constexpr int kSegMaxHeads = 8;  // at most 64 chains: below a quarter of the CUs
+constexpr int kSegMaxHeads = 8;  // sequences x heads: at most 64 chains, a quarter of the CUs
 
 // The scan H_{s+1} = A_s H_s + B_s (s = 0..S-2, per head) is a chain of
 // dense 128 x 128 x 128 products, run on the matrix cores with f32-grade
@@ -1239,7 +1264,9 @@ __device__ __forceinline__ void split3(float a, float b, uint32_t& w1,
   w3 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// Hs[0] is S_init (zero when absent); Hs[s + 1] = A_s Hs[s] + B_s.
+// Per sequence: Hs[0] is S_init (zero when absent), Hs[s + 1] = A_s Hs[s]
+// + B_s.  A and B hold S - 1 entries per sequence, Hs S, each entry Hv
+// states (sequence-major).  One workgroup per (sequence, head, tile).
 __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
     const float* __restrict__ A, const float* __restrict__ B,
     const float* __restrict__ S_init, float* __restrict__ Hs, int S, int Hv) {
@@ -1247,9 +1274,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
   const int nb = gridDim.x;
   int bid = blockIdx.x;
   if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;  // a head's tiles on one XCD
-  const int h = bid / (kD / kTile), c0 = kTile * (bid % (kD / kTile));
+  const int sh = bid / (kD / kTile), c0 = kTile * (bid % (kD / kTile));
+  const int seq = sh / Hv, h = sh % Hv;
   const int w = threadIdx.x / 64, l = threadIdx.x % 64, q = l / 16, n = l % 16;
   const size_t head = (size_t)kD * kD;
+  // entry x of this sequence's transitions / offsets and of its states
+  auto ab = [&](int x) { return (size_t)((seq * (S - 1) + x) * Hv + h) * head; };
+  auto hs = [&](int x) { return (size_t)((seq * S + x) * Hv + h) * head; };
   // element e of this lane's result tile: row 16w + 4q + e, column c0 + n
   auto at = [&](int e) -> size_t {
     return (size_t)(16 * w + 4 * q + e) * kD + c0 + n;
@@ -1264,8 +1295,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
     reinterpret_cast<uint2*>(&Hb[buf][w / 2][2][l])[w % 2] = make_uint2(w3[0], w3[1]);
   };
   {
-    const float* Si = S_init ? S_init + (size_t)h * head : nullptr;
-    float* H0 = Hs + (size_t)h * head;
+    const float* Si = S_init ? S_init + (size_t)sh * head : nullptr;
+    float* H0 = Hs + hs(0);
     f32x4 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1275,13 +1306,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
     publish(0, x);
   }
   auto load = [&](int sg, float4 (&ra)[8], float (&rb)[4]) {
-    const float* row = A + (size_t)(sg * Hv + h) * head + (size_t)(16 * w + n) * kD;
+    const float* row = A + ab(sg) + (size_t)(16 * w + n) * kD;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       ra[2 * p] = *reinterpret_cast<const float4*>(row + 32 * p + 4 * q);
       ra[2 * p + 1] = *reinterpret_cast<const float4*>(row + 32 * p + 16 + 4 * q);
     }
-    const float* Bs = B + (size_t)(sg * Hv + h) * head;
+    const float* Bs = B + ab(sg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) rb[e] = Bs[at(e)];
   };
@@ -1328,7 +1359,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
     split(ra, na);
 #pragma unroll
     for (int e = 0; e < 4; ++e) t[e] = (t[e] + u[e]) + b[e];
-    float* Hn = Hs + (size_t)((sg + 1) * Hv + h) * head;
+    float* Hn = Hs + hs(sg + 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) Hn[at(e)] = t[e];
     publish(cur ^ 1, t);
@@ -1348,8 +1379,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void seg_scan_kernel(
   }
 }
 
-// Checkpoints and S_final of a segmented prefill, one workgroup per (job,
-// head).  Job j < n_ck is checkpoint j, the state at token
+// Checkpoints and S_final of a segmented prefill, one workgroup per
+// (sequence, job, head).  Job j < n_ck is checkpoint j, the state at token
 // (j + 1) * interval: the start state of segment b = (j + 1) * segs_per_ck
 // (the scanned state), or the last segment's end state when b = S (the end
 // of the sequence).  Job n_ck is S_final, the last segment's end state.
@@ -1357,14 +1388,15 @@ __global__ __launch_bounds__(256) void seg_place_kernel(
     const float* __restrict__ Hs, const float* __restrict__ Send,
     float* __restrict__ ckpt, float* __restrict__ S_final, int n_ck,
     int segs_per_ck, int S, int Hv) {
-  const int job = blockIdx.x / Hv, h = blockIdx.x % Hv;
+  const int h = blockIdx.x % Hv, job = (blockIdx.x / Hv) % (n_ck + 1);
+  const int seq = blockIdx.x / (Hv * (n_ck + 1));
   const size_t head = (size_t)kD * kD;
-  const float* src = Send + ((size_t)(S - 1) * Hv + h) * head;
-  float* dst = S_final + (size_t)h * head;
+  const float* src = Send + ((size_t)(seq * S + S - 1) * Hv + h) * head;
+  float* dst = S_final + ((size_t)seq * Hv + h) * head;
   if (job < n_ck) {
     const int b = (job + 1) * segs_per_ck;
-    if (b < S) src = Hs + ((size_t)b * Hv + h) * head;
-    dst = ckpt + ((size_t)job * Hv + h) * head;
+    if (b < S) src = Hs + ((size_t)(seq * S + b) * Hv + h) * head;
+    dst = ckpt + ((size_t)(seq * n_ck + job) * Hv + h) * head;
   }
   for (int x = threadIdx.x; x < kD * kD; x += 256) dst[x] = src[x];
 }
@@ -1397,11 +1429,11 @@ static size_t p1_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
   return (size_t)n_seqs * n_chunks * Hv * WsLayout::kBytes;
 }
 
-// Sizes for which a prefill may run in segments (one sequence, few heads,
-// more than one segment); whether it does also depends on the checkpoint
+// Sizes for which a prefill may run in segments (few sequence-heads, more
+// than one segment); whether it does also depends on the checkpoint
 // interval and the flags (use_segments).
 static bool segment_sizes(int32_t n_seqs, int32_t L, int32_t Hv) {
-  return n_seqs == 1 && Hv <= kSegMaxHeads && L > kSeg;
+  return (int64_t)n_seqs * Hv <= kSegMaxHeads && L > kSeg;
 }
 
 static bool use_segments(int32_t n_seqs, int32_t L, int32_t Hv,
@@ -1411,13 +1443,14 @@ static bool use_segments(int32_t n_seqs, int32_t L, int32_t Hv,
          (!checkpoints || ckpt_interval % kSeg == 0);
 }
 
-// Segment buffers after the P1 workspace: A_s and B_s of every segment but
-// the last, the scanned start state and the end state of every segment.
+// Segment buffers after the P1 workspace, each sequence-major with Hv
+// states per entry: A_s and B_s of every segment but the last of each
+// sequence, the scanned start state and the end state of every segment.
 struct SegLayout {
-  int S;
+  int S;  // segments per sequence
   size_t a, b, hs, send, end;
-  SegLayout(int32_t L, int32_t Hv, size_t p1) {
-    const size_t st = (size_t)Hv * kD * kD * sizeof(float);
+  SegLayout(int32_t n_seqs, int32_t L, int32_t Hv, size_t p1) {
+    const size_t st = (size_t)n_seqs * Hv * kD * kD * sizeof(float);
     S = (L + kSeg - 1) / kSeg;
     a = (p1 + 255) & ~size_t(255);
     b = a + (size_t)(S - 1) * st;
@@ -1429,7 +1462,7 @@ struct SegLayout {
 
 static size_t ws_bytes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t C) {
   const size_t p1 = p1_bytes(n_seqs, L, Hv, C);
-  return segment_sizes(n_seqs, L, Hv) ? SegLayout(L, Hv, p1).end : p1;
+  return segment_sizes(n_seqs, L, Hv) ? SegLayout(n_seqs, L, Hv, p1).end : p1;
 }
 
 static int check_sizes(int32_t n_seqs, int32_t L, int32_t Hv, int32_t Hk,
@@ -1567,6 +1600,9 @@ static int prefill_launch(
   dd.group = h_v / h_k;
   dd.chunk = chunk;
   dd.n_chunks = (seq_len + chunk - 1) / chunk;
+  dd.segs = 1;
+  dd.seq_L = seq_len;
+  dd.seq_chunks = dd.n_chunks;
   dd.L_last = seq_len;
   dd.ckpt_interval = checkpoints ? ckpt_interval : 0;
   dd.scale = scale;
@@ -1589,10 +1625,10 @@ static int prefill_launch(
     return launch_p2(0, dd, n_seqs, qq, kk, vv, wsb, S_init, S_final, o,
                      checkpoints, st);
   }
-  // Segments: every segment is a sequence of kSeg tokens for P2 (the P1
-  // workspace is indexed by the chunk over the whole sequence, which is
-  // the segment-major chunk index); the last one may be shorter.
-  const SegLayout sl(seq_len, h_v, p1_bytes(1, seq_len, h_v, chunk));
+  // Segments: P2 runs the segments of every sequence as parts of kSeg
+  // tokens (the last one of each sequence may be shorter); the P1
+  // workspace is indexed by (sequence, chunk), which part_pos follows.
+  const SegLayout sl(n_seqs, seq_len, h_v, p1_bytes(n_seqs, seq_len, h_v, chunk));
   const int S = sl.S, tail = seq_len - (S - 1) * kSeg;
   float* A = reinterpret_cast<float*>(wsb + sl.a);
   float* B = reinterpret_cast<float*>(wsb + sl.b);
@@ -1600,24 +1636,27 @@ static int prefill_launch(
   float* Send = reinterpret_cast<float*>(wsb + sl.send);
   PDims ds = dd;
   ds.L = kSeg;
-  ds.L_last = kSeg;
   ds.n_chunks = kSeg / chunk;
+  ds.segs = S - 1;
+  ds.L_last = kSeg;
   ds.ckpt_interval = 0;
   // A_s to S_final's place, B_s to o's (see p2_kernel)
-  int rc = launch_p2(kModePair, ds, S - 1, qq, kk, vv, wsb, nullptr, A, B,
-                     nullptr, st);
+  int rc = launch_p2(kModePair, ds, n_seqs * (S - 1), qq, kk, vv, wsb, nullptr,
+                     A, B, nullptr, st);
   if (rc != GDN_OK) return rc;
   {
     void* args[] = {(void*)&A, (void*)&B, (void*)&S_init, (void*)&Hs,
                     (void*)&S, (void*)&h_v};
     hipError_t e = hipLaunchKernel((const void*)seg_scan_kernel,
-                                   dim3(h_v * (kD / kTile)),
+                                   dim3(n_seqs * h_v * (kD / kTile)),
                                    dim3(64 * kScanWaves), args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill segment scan launch", e);
   }
-  // the outputs of every segment, the last one with its own length
+  // the outputs of every segment, the last one of each sequence with its
+  // own length
+  ds.segs = S;
   ds.L_last = tail;
-  rc = launch_p2(0, ds, S, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
+  rc = launch_p2(0, ds, n_seqs * S, qq, kk, vv, wsb, Hs, Send, o, nullptr, st);
   if (rc != GDN_OK) return rc;
   {
     int n_ck = checkpoints ? seq_len / ckpt_interval : 0;
@@ -1626,8 +1665,8 @@ static int prefill_launch(
     void* args[] = {(void*)&Hs, (void*)&Send, (void*)&ck, (void*)&S_final,
                     (void*)&n_ck, (void*)&per, (void*)&S, (void*)&h_v};
     hipError_t e = hipLaunchKernel((const void*)seg_place_kernel,
-                                   dim3((n_ck + 1) * h_v), dim3(256), args, 0,
-                                   st);
+                                   dim3(n_seqs * (n_ck + 1) * h_v), dim3(256),
+                                   args, 0, st);
     if (e != hipSuccess) return hip_fail("prefill segment placement launch", e);
   }
   return GDN_OK;

@@ -279,13 +279,15 @@ size_t gdn_prefill_workspace_bytes(int32_t n_seqs, int32_t seq_len,
  *   scale        as for gdn_verify
  *   flags        GDN_FLAG_L2NORM_QK, GDN_FLAG_PREFILL_ONE_CHAIN, or 0
  * Segments: the chunk steps form one sequential chain per (head, 16 value
- * columns), so a sequence with few heads leaves most of the GPU idle.  One
- * sequence (n_seqs = 1) of more than 4,096 tokens with at most 8 value heads
- * therefore runs in segments of 4,096 tokens, when checkpoints are off or
- * their interval is a multiple of 4,096.  The state at a segment's end is
+ * columns), so a batch with few sequence-heads leaves most of the GPU idle.
+ * Sequences of more than 4,096 tokens with n_seqs * h_v <= 8 therefore run
+ * in segments of 4,096 tokens, when checkpoints are off or their interval
+ * is a multiple of 4,096.  Each sequence's results are bit for bit those of
+ * the same sequence prefilled alone.  The state at a segment's end is
  * affine in its start state (the rule is linear in the state, so the maps
  * of consecutive tokens compose): each segment's
- * transition and offset are formed in parallel, scanned in f32, and the
+ * transition and offset are formed in parallel, scanned (f32-grade
+ * products on the matrix cores), and the
  * segments then produce their outputs from the scanned start states.  The
  * results agree with the one-chain evaluation to rounding, not bit for bit;
  * checkpoints sit on segment boundaries, so a resumed prefill still

@@ -254,16 +254,21 @@ def test_prefill_workspace_bytes():
             4 * gdn.prefill_workspace_bytes(1, 4096, 2, 2, 128, 128, 64))
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 48) == 0
     assert gdn.prefill_workspace_bytes(1, 100, 4, 4, 128, 128, 0) == 0
-    # one sequence of more than 4,096 tokens with at most 8 heads may run in
-    # segments: room for each segment's transition and offset (all but the
+    # sequences of more than 4,096 tokens, at most 8 sequence-heads, may run
+    # in segments: room for each segment's transition and offset (all but the
     # last), and the start and end state of every segment (64 KiB per head)
     L, H = 3 * 4096 + 1000, 4
     per_chunk = gdn.prefill_workspace_bytes(1, 4096, 32, 32, 128, 128) // (64 * 32)
     p1 = (L + 63) // 64 * H * per_chunk
     seg = ((p1 + 255) // 256 * 256) + (2 * 3 + 2 * 4) * H * 65536
     assert gdn.prefill_workspace_bytes(1, L, H, H, 128, 128) == seg
-    # not for two sequences, more than 8 heads, or one segment
-    assert gdn.prefill_workspace_bytes(2, L, H, H, 128, 128) == 2 * p1
+    # several sequences: the same per sequence (sequences x heads <= 8)
+    p1_2 = 2 * p1
+    assert (gdn.prefill_workspace_bytes(2, L, H, H, 128, 128) ==
+            ((p1_2 + 255) // 256 * 256) + 2 * (2 * 3 + 2 * 4) * H * 65536)
+    # not for more than 8 sequence-heads, or one segment
+    assert (gdn.prefill_workspace_bytes(3, L, H, H, 128, 128) ==
+            3 * ((L + 63) // 64) * H * per_chunk)
     assert (gdn.prefill_workspace_bytes(1, L, 16, 16, 128, 128) ==
             (L + 63) // 64 * 16 * per_chunk)
     assert (gdn.prefill_workspace_bytes(1, 4096, H, H, 128, 128) ==

@@ -350,7 +350,7 @@ def _tail_inputs(p, t):
 
 
 def test_segmented_prefill_parity():
-    """One sequence with few heads runs in segments of 4,096 tokens (each
+    """A sequence with few heads runs in segments of 4,096 tokens (each
     segment's transition and offset, a scan over the segments, then the
     outputs per segment).  Three full segments and a ragged tail, with an
     initial state and checkpoints at every segment boundary: the outputs
@@ -397,6 +397,49 @@ def test_segmented_prefill_resumes_bitwise():
     _, ck3, Sf3 = run_prefill(_tail_inputs(p2, 8192), [_tail_inputs(p2, 8192)],
                               ck2[:, 0], interval)
     assert np.array_equal(Sf3, Sf2)
+
+
+def test_segmented_prefill_several_sequences():
+    """Two sequences of 4 heads (8 sequence-heads, the most that run in
+    segments), each with its own initial state and a ragged tail: every
+    sequence's outputs per 64-token block, checkpoints and S_final against
+    the oracle, and bit for bit the same sequence run alone (the segments of
+    the sequences are independent parts of the same passes)."""
+    L, Hv, Hk, interval = 2 * SEG + 700, 4, 2, SEG
+    ps = [_long_memory_inputs(L, Hv, Hk, (54, i)) for i in range(2)]
+    S0 = np.stack([gs.prefill_state(Hv, 128, 128, (54, i)) for i in range(2)])
+    o, ck, Sf = run_prefill(ps[0], ps, S0, interval)
+    for i, p in enumerate(ps):
+        o_ref, ck_ref, Sf_ref = oracle_prefill(p, S0[i].astype(np.float64),
+                                               interval)
+        e_o, e_s = o_err_blocks(o[i], o_ref), s_err(Sf[i], Sf_ref)
+        e_c = max(s_err(ck[i, j], ck_ref[j]) for j in range(L // interval))
+        say("  sequence %d: o err %.2e  S err %.2e  ckpt err %.2e"
+            % (i, e_o, e_s, e_c))
+        assert e_o <= TOL and e_s <= TOL and e_c <= TOL
+        o1, ck1, Sf1 = run_prefill(p, [p], S0[i:i + 1], interval)
+        assert np.array_equal(o1[0], o[i]) and np.array_equal(Sf1[0], Sf[i])
+        assert np.array_equal(ck1[0], ck[i])
+
+
+@pytest.mark.parametrize("n_seqs,Hv,Hk,chunk", [(3, 2, 1, 32), (8, 1, 1, 64)])
+def test_segmented_prefill_batch_matches_single_runs(n_seqs, Hv, Hk, chunk):
+    """Batches at the segment limit in other shapes (3 x 2 heads with chunks
+    of 32, 8 x 1 head): each sequence bit for bit its run alone, and within
+    the tolerance of the one-chain call."""
+    L = SEG + 300
+    ps = [_long_memory_inputs(L, Hv, Hk, (55, n_seqs, i)) for i in range(n_seqs)]
+    # an initial state, so that the scan multiplies by a transition (from
+    # zero, two segments give exactly the one chain)
+    S0 = np.stack([gs.prefill_state(Hv, 128, 128, (55, n_seqs, i))
+                   for i in range(n_seqs)])
+    o, _, Sf = run_prefill(ps[0], ps, S0, 8192, chunk=chunk)
+    o2, _, Sf2 = run_prefill(ps[0], ps, S0, 8192, chunk=chunk, segments=False)
+    for i, p in enumerate(ps):
+        o1, _, Sf1 = run_prefill(p, [p], S0[i:i + 1], 8192, chunk=chunk)
+        assert np.array_equal(o1[0], o[i]) and np.array_equal(Sf1[0], Sf[i]), i
+        assert o_err_blocks(o[i], o2[i]) <= TOL and s_err(Sf[i], Sf2[i]) <= TOL
+    assert not np.array_equal(Sf, Sf2)
 
 
 def test_prefill_interval_off_the_segment_grid_runs_one_chain():

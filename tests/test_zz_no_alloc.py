@@ -60,6 +60,7 @@ def _run(noalloc, n_seqs, L, Hv, Hk, interval, ins):
     # both calls in segments (one sequence, few heads, more than 4,096
     # tokens): the segment buffers live in the scratch array too
     ((1, 3 * 4096 + 500, 2, 1, 4096), (1, 4096 + 64, 2, 2, 4096)),
+    ((2, 2 * 4096 + 300, 4, 2, 8192), (3, 4096 + 1, 2, 1, 4096)),
 ])
 def test_noalloc_matches_workspace_entry_point(sizes):
     for i, (n, L, Hv, Hk, iv) in enumerate(sizes):
