@@ -280,42 +280,48 @@ def bench_prefill(reps=10, warmup=2, h_k=PF_H, segments=True):
     return rec
 
 
-def bench_prefill_long(reps=3, warmup=1, L=260096, h_v=4, h_k=2):
-    """The longest prefill the review reports (260,096 tokens, checkpoints
-    every 8,192) on 4 value / 2 key heads -- one GPU's share of 32 heads
-    spread over eight -- in segments of 4,096 tokens (the library's choice
-    for batches of at most 8 sequence-heads) and as one chain
-    (GDN_FLAG_PREFILL_ONE_CHAIN), timed by region_ms."""
+def bench_prefill_long(reps=3, warmup=1, L=260096, h_v=4, h_k=2, n_seqs=1):
+    """Long prefills with few sequence-heads, in segments of 4,096 tokens
+    (the library's choice for batches of at most 8 sequence-heads) and as one
+    chain (GDN_FLAG_PREFILL_ONE_CHAIN), checkpoints every 8,192, timed by
+    region_ms.  The default is the longest prefill the review reports
+    (260,096 tokens) on 4 value / 2 key heads -- one GPU's share of 32 heads
+    spread over eight."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
     dev = torch.device("cuda:0")
-    p = gs.prefill_inputs(L, h_v, h_k, 128, 128, (5, L))
+    ps = [gs.prefill_inputs(L, h_v, h_k, 128, 128, (5, L) if n_seqs == 1
+                            else (5, L, i)) for i in range(n_seqs)]
 
     def d16(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    q, k, v = d16(p.q[None]), d16(p.k[None]), d16(p.v[None])
-    beta = torch.from_numpy(p.beta[None]).to(dev)
-    g = torch.from_numpy(p.g[None]).to(dev)
-    Sf = torch.empty((1, h_v, 128, 128), device=dev)
-    o = torch.empty((1, L, h_v, 128), device=dev)
-    ck = torch.empty((1, L // 8192, h_v, 128, 128), device=dev)
-    ws = torch.empty(gdn.prefill_workspace_bytes(1, L, h_v, h_k, 128, 128),
+    def stack(nm):
+        return np.stack([getattr(x, nm) for x in ps])
+
+    q, k, v = d16(stack("q")), d16(stack("k")), d16(stack("v"))
+    beta = torch.from_numpy(stack("beta")).to(dev)
+    g = torch.from_numpy(stack("g")).to(dev)
+    Sf = torch.empty((n_seqs, h_v, 128, 128), device=dev)
+    o = torch.empty((n_seqs, L, h_v, 128), device=dev)
+    ck = torch.empty((n_seqs, L // 8192, h_v, 128, 128), device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(n_seqs, L, h_v, h_k, 128, 128),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ms = {}
     for seg in (True, False):
         ms[seg] = region_ms(
-            lambda r: gdn.prefill_chunked(1, L, h_v, h_k, 128, 128, q, k, v,
-                                          beta, g, None, Sf, o, ck, ws,
+            lambda r: gdn.prefill_chunked(n_seqs, L, h_v, h_k, 128, 128, q, k,
+                                          v, beta, g, None, Sf, o, ck, ws,
                                           stream=stream, segments=seg),
             reps, warmup, stream)
-    return {"workload": "1 sequence x %d tokens, %d value / %d key heads, "
-                        "d=128, chunk 64, checkpoints every 8192" % (L, h_v, h_k),
+    return {"workload": "%d sequence%s x %d tokens, %d value / %d key heads, "
+                        "d=128, chunk 64, checkpoints every 8192"
+                        % (n_seqs, "" if n_seqs == 1 else "s", L, h_v, h_k),
             "segments_ms": ms[True], "one_chain_ms": ms[False],
             "speedup": ms[False] / ms[True],
-            "head_tokens_per_s": L * h_v / (ms[True] * 1e-3)}
+            "head_tokens_per_s": n_seqs * L * h_v / (ms[True] * 1e-3)}
 
 
 def bench_t_sweep(ts=(1, 2, 4, 6, 8, 12, 16), reps=20, warmup=3):
@@ -1187,6 +1193,8 @@ def main():
         # the same prefill with 16 key heads (two value heads per key head)
         out["prefill_h_k16"] = bench_prefill(h_k=16, segments=False)
         out["prefill_long_few_heads"] = bench_prefill_long()
+        out["prefill_batch_few_heads"] = bench_prefill_long(
+            L=131072, n_seqs=2)
     if not args.no_snapshot:
         out["state_snapshot"] = bench_snapshot()
         # context for the roofline: what a plain device copy (read + write,
