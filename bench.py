@@ -524,17 +524,16 @@ def _dev_bf16(a, dev):
 
 def bench_token_verify(reps=20, warmup=3):
     """The token-by-token verify at the headline batch (8 lanes x 48 layers x
-    32/16 heads, d = 128, T = 16): the same windows declared with a window
-    stride t_max = 17, which routes them to the kernel that evaluates the
-    rule one token at a time and holds every intermediate state (the design
-    that the block form replaces at these shapes).  Event-timed."""
+    32/16 heads, d = 128, T = 16) with GDN_FLAG_TOKENWISE: the kernel that
+    evaluates the rule one token at a time and holds every intermediate
+    state (the design that the block form replaces at these shapes).
+    Timed by region_ms."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
     dev = torch.device("cuda:0")
-    tm = T + 1
-    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, tm)
-    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, tm)
+    shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
+    dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
     t_lane = np.full(N, T, dtype=np.int32)
     pool = []
     for p in range(4):
@@ -543,25 +542,27 @@ def bench_token_verify(reps=20, warmup=3):
                      _dev_bf16(w.v, dev), torch.from_numpy(w.beta).to(dev),
                      torch.from_numpy(w.g).to(dev)))
     S = torch.from_numpy(gs.initial_state(shape, (12, 0))).to(dev)
-    o = torch.empty((NL, N, tm, HV, DV), device=dev)
+    o = torch.empty((NL, N, T, HV, DV), device=dev)
     rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ms = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec,
-                                        stream=stream), reps, warmup, stream)
+                                        stream=stream, tokenwise=True),
+                   reps, warmup, stream)
     bv = alg_bytes_verify(t_lane)
     return {"workload": "verify of 8 lanes x 48 layers x 32/16 heads, d=128, "
-                        "T=16 on the token-by-token kernel (window stride 17)",
+                        "T=16 on the token-by-token kernel (GDN_FLAG_TOKENWISE)",
             "verify_ms": ms,
             "updates_per_s": int(t_lane.sum()) * NL * HV / (ms * 1e-3),
             "verify_hbm_frac": bv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_general_shapes(reps=10, warmup=2):
-    """Shapes that the token-by-token kernels serve, on the same 8-lane x
-    48-layer x 32/16-head batch (d = 128): f32 inputs at T = 16, bf16
-    windows of 32 and 64 tokens, and 32-node draft trees.  Verify, commit
-    and the fused round are event-timed; HBM fractions against the same
-    algorithmic byte counts as the headline (inputs at their own width)."""
+    """Shapes beyond the pages' windows, on the same 8-lane x 48-layer x
+    32/16-head batch (d = 128): f32 inputs at T = 16 and 32-node draft
+    trees (token by token), bf16 windows of 32 and 64 tokens (block form in
+    blocks of 16).  Verify, commit and the fused round are timed by
+    region_ms; HBM fractions against the same algorithmic byte counts as the
+    headline (inputs at their own width)."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
@@ -629,9 +630,10 @@ def bench_general_shapes(reps=10, warmup=2):
         out.append(rec)
         del S, o, recs, ins
         torch.cuda.empty_cache()
-    return {"workload": "token-by-token kernels on 8 lanes x 48 layers x "
-                        "32/16 heads, d=128, every lane at T (fused: previous "
-                        "window's m ~ U{0..T})", "points": out}
+    return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, every "
+                        "lane at T (fused: previous window's m ~ U{0..T}); "
+                        "f32 and trees token by token, bf16 windows in "
+                        "blocks of 16", "points": out}
 
 
 # Synthetic workloads of the speculative-decoding round, timed as chains of
@@ -980,7 +982,7 @@ def main():
     ap.add_argument("--no-general", action="store_true",
                     help="skip f32 / long-window / 32-node-tree shapes")
     ap.add_argument("--general-only", action="store_true",
-                    help="time only the token-by-token kernel shapes")
+                    help="time only the shapes beyond the pages' windows")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (for profiling)")
     ap.add_argument("--prefill-long-only", action="store_true",

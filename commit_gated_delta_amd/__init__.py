@@ -24,6 +24,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, 
 GDN_BF16, GDN_F32 = 0, 1
 GDN_FLAG_L2NORM_QK = 1
 GDN_FLAG_PREFILL_ONE_CHAIN = 2
+GDN_FLAG_TOKENWISE = 4
 GDN_MAX_LANES = 256
 GDN_MAX_T = 64
 
@@ -158,15 +159,21 @@ def records_bytes(dims: Dims) -> int:
     return int(lib.gdn_records_bytes(ctypes.byref(dims)))
 
 
+def _verify_flags(l2norm, tokenwise):
+    return ((GDN_FLAG_L2NORM_QK if l2norm else 0) |
+            (GDN_FLAG_TOKENWISE if tokenwise else 0))
+
+
 def verify(dims: Dims, t_lane, q, k, v, beta, g, S, o, records,
            dbg_states=None, scale=1.0, l2norm=True, stream=None,
-           raw_status=False):
-    """gdn_verify on torch tensors (layouts in include/gdn.h)."""
+           raw_status=False, tokenwise=False):
+    """gdn_verify on torch tensors (layouts in include/gdn.h;
+    tokenwise=True sets GDN_FLAG_TOKENWISE)."""
     st = lib.gdn_verify(ctypes.byref(dims), _int_array(t_lane, dims.n_lanes),
                         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta),
                         _ptr(g), _ptr(S), _ptr(o), _ptr(records),
                         _ptr(dbg_states), float(scale),
-                        GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+                        _verify_flags(l2norm, tokenwise), _stream(stream))
     if raw_status:
         return st
     _check(st, "gdn_verify")
@@ -185,7 +192,7 @@ def commit(dims: Dims, m_lane, t_lane, records, S, stream=None,
 
 def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
                   beta, g, S, o, records, dbg_states=None, scale=1.0,
-                  l2norm=True, stream=None, raw_status=False):
+                  l2norm=True, stream=None, raw_status=False, tokenwise=False):
     """gdn_commit_verify on torch tensors: commit(m_prev) of the previous
     window's records, then verify of the new window, in one launch."""
     st = lib.gdn_commit_verify(
@@ -193,7 +200,7 @@ def commit_verify(dims: Dims, m_prev, t_prev, records_prev, t_lane, q, k, v,
         _int_array(t_prev, dims.n_lanes), _ptr(records_prev),
         _int_array(t_lane, dims.n_lanes), _ptr(q), _ptr(k), _ptr(v),
         _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S), _ptr(o), _ptr(records),
-        _ptr(dbg_states), float(scale), GDN_FLAG_L2NORM_QK if l2norm else 0,
+        _ptr(dbg_states), float(scale), _verify_flags(l2norm, tokenwise),
         _stream(stream))
     if raw_status:
         return st
@@ -206,13 +213,13 @@ def kda_records_bytes(dims: Dims) -> int:
 
 def kda_verify(dims: Dims, t_lane, q, k, v, beta, g, S, o, records,
                dbg_states=None, scale=1.0, l2norm=True, stream=None,
-               raw_status=False):
+               raw_status=False, tokenwise=False):
     """gdn_kda_verify; g is [NL][N][T][Hv][d_k] (per-channel log-decay)."""
     st = lib.gdn_kda_verify(ctypes.byref(dims), _int_array(t_lane, dims.n_lanes),
                             _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
                             _ptr(beta), _ptr(g), _ptr(S), _ptr(o),
                             _ptr(records), _ptr(dbg_states), float(scale),
-                            GDN_FLAG_L2NORM_QK if l2norm else 0,
+                            _verify_flags(l2norm, tokenwise),
                             _stream(stream))
     if raw_status:
         return st
@@ -243,14 +250,14 @@ def _table(rows, n, t_max, fill):
 
 def verify_tree(dims: Dims, t_lane, parent, q, k, v, beta, g, S, o, records,
                 dbg_states=None, scale=1.0, l2norm=True, stream=None,
-                raw_status=False):
+                raw_status=False, tokenwise=False):
     """gdn_verify_tree; parent is [n_lanes][<= t_max] (-1: from S0)."""
     keep, pp = _table(parent, dims.n_lanes, dims.t_max, -1)
     st = lib.gdn_verify_tree(
         ctypes.byref(dims), _int_array(t_lane, dims.n_lanes), pp, _ptr(q),
         _ptr(k), _ptr(v), _dtype_code(q), _ptr(beta), _ptr(g), _ptr(S),
         _ptr(o), _ptr(records), _ptr(dbg_states), float(scale),
-        GDN_FLAG_L2NORM_QK if l2norm else 0, _stream(stream))
+        _verify_flags(l2norm, tokenwise), _stream(stream))
     del keep
     if raw_status:
         return st

@@ -347,7 +347,7 @@ extern "C" int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
     return fail(GDN_EINVAL, "gdn_kda_verify: required pointer is NULL");
   if (in_dtype != GDN_BF16 && in_dtype != GDN_F32)
     return fail(GDN_EINVAL, "gdn_kda_verify: unknown in_dtype");
-  if (flags & ~GDN_FLAG_L2NORM_QK)
+  if (flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_TOKENWISE))
     return fail(GDN_EINVAL, "gdn_kda_verify: unknown flag bits");
   if (misaligned(q, 4) || misaligned(k, 4) ||
       misaligned(v, in_dtype == GDN_BF16 ? 2 : 4) || misaligned(beta, 4) ||
@@ -374,7 +374,8 @@ extern "C" int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
   hipStream_t st = (hipStream_t)stream;
   const int l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
   hipError_t e;
-  if (mkda_eligible(d, in_dtype, q, k, v, g, S, o, dbg_states))
+  if (!(flags & GDN_FLAG_TOKENWISE) &&
+      mkda_eligible(d, in_dtype, q, k, v, g, S, o, dbg_states))
     e = launch_mkda(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states,
                     scale, l2, st);
   else if (in_dtype == GDN_BF16)

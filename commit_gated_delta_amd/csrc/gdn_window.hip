@@ -606,7 +606,7 @@ static int verify_setup(const char* fn, const gdn_dims* dims,
     snprintf(msg, sizeof(msg), "%s: unknown in_dtype", fn);
     return fail(GDN_EINVAL, msg);
   }
-  if (flags & ~GDN_FLAG_L2NORM_QK) {
+  if (flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_TOKENWISE)) {
     snprintf(msg, sizeof(msg), "%s: unknown flag bits", fn);
     return fail(GDN_EINVAL, msg);
   }
@@ -672,7 +672,7 @@ extern "C" int gdn_verify(const gdn_dims* dims, const int32_t* t_lane,
   PrevRecords none;
   memset(&none, 0, sizeof(none));
   hipError_t e =
-      mverify_eligible(*dims, in_dtype, a)
+      !(flags & GDN_FLAG_TOKENWISE) && mverify_eligible(*dims, in_dtype, a, false)
           ? launch_mverify(win_dims(*dims), tl, a, none, false,
                            (hipStream_t)stream)
           : launch_verify<false>(win_dims(*dims), tl, in_dtype, a, none,
@@ -764,7 +764,7 @@ extern "C" int gdn_verify_tree(const gdn_dims* dims, const int32_t* t_lane,
   PrevRecords none;
   memset(&none, 0, sizeof(none));
   hipError_t e =
-      mverify_eligible(*dims, in_dtype, a)
+      !(flags & GDN_FLAG_TOKENWISE) && mverify_eligible(*dims, in_dtype, a, true)
           ? launch_mverify_tree(win_dims(*dims), tl, a, tab,
                                 (hipStream_t)stream)
           : launch_verify<false, true>(win_dims(*dims), tl, in_dtype, a, none,
@@ -886,7 +886,8 @@ extern "C" int gdn_commit_verify(const gdn_dims* dims, const int32_t* m_prev,
     for (int n = 0; n < d.n_lanes; ++n) pr.order.v[n] = (uint8_t)ord[n];
   }
   if (!any && ct.n_act == 0) return GDN_OK;
-  hipError_t e = mverify_eligible(d, in_dtype, a)
+  hipError_t e = !(flags & GDN_FLAG_TOKENWISE) &&
+                          mverify_eligible(d, in_dtype, a, false)
                       ? launch_mverify(win_dims(d), tl, a, pr, true,
                                        (hipStream_t)stream)
                       : launch_verify<true>(win_dims(d), tl, in_dtype, a, pr,

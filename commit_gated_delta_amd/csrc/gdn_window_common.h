@@ -299,14 +299,15 @@ static int commit_lanes(const char* fn, const gdn_dims& d,
   return GDN_OK;
 }
 
-// The matrix-core verify (gdn_window_mfma.hip): whether a call can take it,
-// and its launch (replay = the fused commit + verify).
+// The matrix-core verify (gdn_window_mfma.hip): whether a call can take it
+// (windows of up to GDN_MAX_T tokens, draft trees of up to 16 nodes), and
+// its launch (replay = the fused commit + verify).
 __attribute__((visibility("hidden"))) bool mverify_eligible(
-    const gdn_dims& d, int in_dtype, const VerifyArgs& a);
+    const gdn_dims& d, int in_dtype, const VerifyArgs& a, bool tree);
 __attribute__((visibility("hidden"))) hipError_t launch_mverify(
     const WinDims& w, const LaneTable& tl, const VerifyArgs& a,
     const PrevRecords& pr, bool replay, hipStream_t st);
-// The matrix-core verify of a draft-tree window (same eligibility).
+// The matrix-core verify of a draft-tree window.
 __attribute__((visibility("hidden"))) hipError_t launch_mverify_tree(
     const WinDims& w, const LaneTable& tl, const VerifyArgs& a,
     const TreeTable& tree, hipStream_t st);

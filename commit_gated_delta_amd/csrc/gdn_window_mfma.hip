@@ -102,8 +102,8 @@ struct WaveLds {
 // ancestor (or, for P, t itself), dec(t, s) is the decay along the path from
 // s to t, and the scale sequence continues the parent's scale.  A parent
 // precedes its children, so L stays strictly lower triangular.
-template <bool REPLAY, bool DBG, bool TREE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG ? 2 : 3)))
+template <bool REPLAY, bool DBG, bool TREE, bool MB>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG || (MB && REPLAY) ? 2 : 3)))
 void mverify_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ beta,
@@ -113,6 +113,7 @@ void mverify_kernel(
     LaneTable tl, float scale, int l2norm, PrevRecords prev,
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
+  static_assert(!(TREE && MB), "draft trees have at most one block");
   __shared__ WaveLds wl[kWaves];
   __shared__ RowLds rows;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
@@ -183,23 +184,30 @@ void mverify_kernel(
   // requested before the state, so that everything but the state products
   // overlaps the state's latency.  Tokens at or past T read token 0 and are
   // replaced by zeros.
-  const bool tv = n < T;
   const int rt = tid >> 4, rp = tid & 15;
-  const bool rv = rt < T;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  u32x4 kr = *reinterpret_cast<const u32x4*>(
-      k0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
-  u32x4 qr = *reinterpret_cast<const u32x4*>(
-      q0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
-  kr = rv ? kr : z4;
-  qr = rv ? qr : z4;
-  const int tg = tid < T ? tid : 0;
-  const float gl = g[gh0 + (size_t)tg * d.Hv];
-  const float bl = beta[gh0 + (size_t)tg * d.Hv];
-  u32x4 vr = *reinterpret_cast<const u32x4*>(
-      v0 + (uint32_t)((rv ? rt : 0) * vo_step) + kCB * cb + 8 * rp);
-  vr = rv ? vr : z4;
-  auto stage_rows = [&]() {
+  u32x4 kr, qr, vr;
+  float gl, bl;
+  // the rows of the block of tokens tb .. tb + Tb - 1: thread (rt, rp) one
+  // 16-byte piece of key row rt, of query row rt and of value row rt (this
+  // workgroup's columns), threads 0..15 the gates of token tid; tokens at or
+  // past Tb read the block's first token and are replaced by zeros
+  auto load_rows = [&](int tb, int Tb) {
+    const bool rv = rt < Tb;
+    const int tr = tb + (rv ? rt : 0);
+    kr = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + 8 * rp);
+    qr = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + 8 * rp);
+    kr = rv ? kr : z4;
+    qr = rv ? qr : z4;
+    const int tg = tb + (tid < Tb ? tid : 0);
+    gl = g[gh0 + (size_t)tg * d.Hv];
+    bl = beta[gh0 + (size_t)tg * d.Hv];
+    vr = *reinterpret_cast<const u32x4*>(
+        v0 + (uint32_t)(tr * vo_step) + kCB * cb + 8 * rp);
+    vr = rv ? vr : z4;
+  };
+  auto stage_rows = [&](int tb, int Tb) {
+    const bool rv = rt < Tb;
     *reinterpret_cast<u32x4*>(&rows.k[rt][8 * rp]) = kr;
     *reinterpret_cast<u32x4*>(&rows.q[rt][8 * rp]) = qr;
     *reinterpret_cast<u32x4*>(&rows.v[rt][8 * rp]) = vr;
@@ -207,19 +215,23 @@ void mverify_kernel(
     // store under a branch lets the compiler sink the gate loads into it,
     // behind the state requests, and wait for the whole state there
     const int gs = tid < kTok ? tid : kTok;
-    rows.g[gs] = tid < T ? gl : 0.f;
-    rows.b[gs] = tid < T ? bl : 0.f;
+    rows.g[gs] = tid < Tb ? gl : 0.f;
+    rows.b[gs] = tid < Tb ? bl : 0.f;
     // the key record rows (raw rows as f32): thread (rt, rp) writes its
     // piece; done here so that the pieces are dead past the staging
     if (cb == 0 && h % d.group == 0 && rv) {
       float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kDK +
-                                (uint32_t)(rt * kq_step) + 8 * rp;
+                                (uint32_t)((tb + rt) * kq_step) + 8 * rp;
       reinterpret_cast<float4*>(dst)[0] =
           make_float4(lo_f(kr[0]), hi_f(kr[0]), lo_f(kr[1]), hi_f(kr[1]));
       reinterpret_cast<float4*>(dst)[1] =
           make_float4(lo_f(kr[2]), hi_f(kr[2]), lo_f(kr[3]), hi_f(kr[3]));
     }
   };
+  // the first block's rows are requested before the state, so that
+  // everything but the state products overlaps the state's latency
+  const int T0 = MB ? (T < kTok ? T : kTok) : T;
+  load_rows(0, T0);
   auto frag_k = [&](int ks) {
     return *reinterpret_cast<const u32x4*>(&rows.k[n][32 * ks + 8 * g4]);
   };
@@ -238,7 +250,7 @@ void mverify_kernel(
   // scheduler would otherwise sink them below the first uses of the small
   // loads and wait for those first
   __builtin_amdgcn_sched_barrier(0);
-  stage_rows();
+  stage_rows(0, T0);
   __syncthreads();
 
   // ---- fused commit: the accepted prefix of the previous window, replayed
@@ -251,79 +263,88 @@ void mverify_kernel(
       const float* __restrict__ pk = prev.k + (tok0 * d.Hk + kh) * kDK;
       const float* __restrict__ pu =
           prev.u + (tok0 * d.Hv + h) * (size_t)dv + kCB * cb;
-      f32x4 kst[2], ust[2];
+      // the records arrive in chunks of kTok tokens (one chunk for windows
+      // of at most kTok tokens)
+      const int nrc = MB ? (m_prev + kTok - 1) / kTok : 1;
+      int mc = m_prev;
+      for (int rc = 0; rc < nrc; ++rc) {
+        const int r0 = rc * kTok;
+        mc = MB ? (m_prev - r0 < kTok ? m_prev - r0 : kTok) : m_prev;
+        if (MB && rc > 0) __syncthreads();  // the previous chunk is applied
+        f32x4 kst[2], ust[2];
 #pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int e = tid + kBlock * rep;  // float4 slot: token e/32
-        int tok = e >> 5;
-        tok = tok < m_prev ? tok : m_prev - 1;
-        kst[rep] = *reinterpret_cast<const f32x4*>(
-            pk + (uint32_t)(tok * kq_step) + 4 * (e & 31));
-        ust[rep] = *reinterpret_cast<const f32x4*>(
-            pu + (uint32_t)(tok * vo_step) + 4 * (e & 31));
-      }
-      const int ts = tid < m_prev ? tid : m_prev - 1;
-      const f32x2 scst = *reinterpret_cast<const f32x2*>(
-          prev.scale + gh0 + (size_t)ts * d.Hv);
-#pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int e = tid + kBlock * rep;
-        reinterpret_cast<f32x4*>(&stage.k[0][0])[e] = kst[rep];
-        reinterpret_cast<f32x4*>(&stage.u[0][0])[e] = ust[rep];
-      }
-      // every thread stores (past kTok into the discarded slot), so that
-      // the scale load is not sunk behind the record loads into a branch
-      stage.sc[tid < kTok ? tid : kTok] = scst;
-      __syncthreads();
-      // one step: fold (when the record has one), then the rank-1 write
-      auto step = [&](int t, bool may_fold) {
-        const f32x2 fc = stage.sc[t];
-        const f32x2 uc =
-            *reinterpret_cast<const f32x2*>(&stage.u[t][32 * w + 2 * n]);
-        f32x4 kc[2 * kKS];
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          kc[2 * ks] =
-              *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4]);
-          kc[2 * ks + 1] =
-              *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4 + 4]);
+        for (int rep = 0; rep < 2; ++rep) {
+          const int e = tid + kBlock * rep;  // float4 slot: token e/32
+          int tok = e >> 5;
+          tok = r0 + (tok < mc ? tok : mc - 1);
+          kst[rep] = *reinterpret_cast<const f32x4*>(
+              pk + (uint32_t)(tok * kq_step) + 4 * (e & 31));
+          ust[rep] = *reinterpret_cast<const f32x4*>(
+              pu + (uint32_t)(tok * vo_step) + 4 * (e & 31));
         }
-        if (may_fold) {
-          const float ph = __int_as_float(
-              __builtin_amdgcn_readfirstlane(__float_as_int(fc[0])));
-          if (ph != 1.f) {
+        const int ts = r0 + (tid < mc ? tid : mc - 1);
+        const f32x2 scst = *reinterpret_cast<const f32x2*>(
+            prev.scale + gh0 + (size_t)ts * d.Hv);
 #pragma unroll
-            for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                s2[ks][e][0] = ph * s2[ks][e][0];
-                s2[ks][e][1] = ph * s2[ks][e][1];
-              }
-          }
+        for (int rep = 0; rep < 2; ++rep) {
+          const int e = tid + kBlock * rep;
+          reinterpret_cast<f32x4*>(&stage.k[0][0])[e] = kst[rep];
+          reinterpret_cast<f32x4*>(&stage.u[0][0])[e] = ust[rep];
         }
+        // every thread stores (past kTok into the discarded slot), so that
+        // the scale load is not sunk behind the record loads into a branch
+        stage.sc[tid < kTok ? tid : kTok] = scst;
+        __syncthreads();
+        // one step: fold (when the record has one), then the rank-1 write
+        auto step = [&](int t, bool may_fold) {
+          const f32x2 fc = stage.sc[t];
+          const f32x2 uc =
+              *reinterpret_cast<const f32x2*>(&stage.u[t][32 * w + 2 * n]);
+          f32x4 kc[2 * kKS];
 #pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float kv = kc[2 * ks + e / 4][e % 4];
-            s2[ks][e][0] = state_update(s2[ks][e][0], uc[0], kv);
-            s2[ks][e][1] = state_update(s2[ks][e][1], uc[1], kv);
+          for (int ks = 0; ks < kKS; ++ks) {
+            kc[2 * ks] =
+                *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4]);
+            kc[2 * ks + 1] =
+                *reinterpret_cast<const f32x4*>(&stage.k[t][32 * ks + 8 * g4 + 4]);
           }
-      };
-      // folds are rare: a prefix without one runs a branch-free loop
-      const bool any_fold =
-          __builtin_amdgcn_ballot_w64(l < m_prev && stage.sc[l < kTok ? l : 0][0] != 1.f) != 0;
-      if (any_fold) {
+          if (may_fold) {
+            const float ph = __int_as_float(
+                __builtin_amdgcn_readfirstlane(__float_as_int(fc[0])));
+            if (ph != 1.f) {
+#pragma unroll
+              for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  s2[ks][e][0] = ph * s2[ks][e][0];
+                  s2[ks][e][1] = ph * s2[ks][e][1];
+                }
+            }
+          }
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float kv = kc[2 * ks + e / 4][e % 4];
+              s2[ks][e][0] = state_update(s2[ks][e][0], uc[0], kv);
+              s2[ks][e][1] = state_update(s2[ks][e][1], uc[1], kv);
+            }
+        };
+        // folds are rare: a prefix without one runs a branch-free loop
+        const bool any_fold =
+            __builtin_amdgcn_ballot_w64(l < mc && stage.sc[l < kTok ? l : 0][0] != 1.f) != 0;
+        if (any_fold) {
 #pragma unroll 1
-        for (int t = 0; t < m_prev; ++t) step(t, true);
-      } else {
+          for (int t = 0; t < mc; ++t) step(t, true);
+        } else {
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-          if (t >= m_prev) break;
-          step(t, false);
+          for (int t = 0; t < kTok; ++t) {
+            if (t >= mc) break;
+            step(t, false);
+          }
         }
       }
-      const float cf = stage.sc[m_prev - 1][1];
+      const float cf = stage.sc[mc - 1][1];
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
@@ -335,360 +356,393 @@ void mverify_kernel(
     }
     if (T == 0) return;
   }
-  const float gt = rows.g[n], bt = rows.b[n];
-  u32x4 Kf[kKS], Qf[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    Kf[ks] = frag_k(ks);
-    Qf[ks] = frag_q(ks);
-  }
-
-  // ---- inverse norms of token n (sums over the lane's row pieces, then
-  // over the four groups)
-  float skk = 0.f, sqq = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    const u32x4 kw = Kf[ks], qw = Qf[ks];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      skk = __builtin_fmaf(lo_f(kw[p]), lo_f(kw[p]), skk);
-      skk = __builtin_fmaf(hi_f(kw[p]), hi_f(kw[p]), skk);
-      sqq = __builtin_fmaf(lo_f(qw[p]), lo_f(qw[p]), sqq);
-      sqq = __builtin_fmaf(hi_f(qw[p]), hi_f(qw[p]), sqq);
+  // the window in blocks of kTok tokens (one block unless MB): block tb
+  // starts from the held state, the scaled replay state of the tokens
+  // before it with scale c_in
+  float c_in = 1.0f;
+  for (int tb = 0;; tb += kTok) {
+    const int Tb = MB ? (T - tb < kTok ? T - tb : kTok) : T;
+    if (MB && tb > 0) {
+      load_rows(tb, Tb);
+      __syncthreads();  // every wave is done with the previous block's rows
+      stage_rows(tb, Tb);
+      __syncthreads();
     }
-  }
-  skk += __shfl_xor(skk, 16, kWave);
-  sqq += __shfl_xor(sqq, 16, kWave);
-  skk += __shfl_xor(skk, 32, kWave);
-  sqq += __shfl_xor(sqq, 32, kWave);
-  const float rk = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
-  const float rq = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
-
-
-  // ---- K K^T and K Q^T: lane (g4, n), entry e = (k_{4g4+e} . k_n) and
-  // (k_{4g4+e} . q_n) -- row n, column s = 4 g4 + e of the A layout of the
-  // f32 products below
-  f32x4 KK = {0.f, 0.f, 0.f, 0.f}, KQ = {0.f, 0.f, 0.f, 0.f};
+    const float gt = rows.g[n], bt = rows.b[n];
+    u32x4 Kf[kKS], Qf[kKS];
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    KK = mma_bf16(Kf[ks], Kf[ks], KK);
-    KQ = mma_bf16(Kf[ks], Qf[ks], KQ);
-  }
-
-  // ---- gates of token n, within each 16-lane group: segmented sums Gs
-  // (restarting after the last token R <= n whose decay is 0) and the scale
-  // sequence c of gdn_step.h (prefix products of alpha, folded when out of
-  // [2^-32, 2^32]; that rare case walks the tokens in order)
-  const float a_t = tv ? __expf(gt) : 1.0f;
-  float Gs, c, phi = 1.f;
-  int R;
-  uint32_t anc;  // bit s: token s is a strict ancestor of token n
-  if constexpr (TREE) {
-    // pointer jumping over the ancestor chain: lane n holds the aggregate
-    // of the path segment (J, n] (segment sum and deepest zero-decay node,
-    // ancestor set, product of the decays) and combines it with the one that
-    // lane J holds for (J', J], all lanes at once; parents precede their
-    // children, so a path has at most 16 nodes and four jumps reach the
-    // root.  On a chain this is the window's scan, step for step.
-    int J = -1;
-    for (int t = 0; t < T; ++t) {
-      const int par = tree_parent(tree, lane * d.T + t);
-      J = n == t ? par : J;
+    for (int ks = 0; ks < kKS; ++ks) {
+      Kf[ks] = frag_k(ks);
+      Qf[ks] = frag_q(ks);
     }
-    const bool reset = gt < kReset;
-    Gs = reset ? 0.f : gt;
-    R = reset ? n : -1;
-    anc = 0u;
-    c = a_t;
+
+    // ---- inverse norms of token n (sums over the lane's row pieces, then
+    // over the four groups)
+    float skk = 0.f, sqq = 0.f;
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      const int src = J < 0 ? 0 : J;
-      const float Gy = __shfl(Gs, src, 16);
-      const int Ry = __shfl(R, src, 16);
-      const uint32_t ay = (uint32_t)__shfl((int)anc, src, 16);
-      const float cy = __shfl(c, src, 16);
-      const int Jy = __shfl(J, src, 16);
-      if (J >= 0) {
-        Gs = R < 0 ? Gy + Gs : Gs;
-        R = R > Ry ? R : Ry;
-        anc = anc | ay | (1u << J);
-        c *= cy;
-        J = Jy;
+    for (int ks = 0; ks < kKS; ++ks) {
+      const u32x4 kw = Kf[ks], qw = Qf[ks];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        skk = __builtin_fmaf(lo_f(kw[p]), lo_f(kw[p]), skk);
+        skk = __builtin_fmaf(hi_f(kw[p]), hi_f(kw[p]), skk);
+        sqq = __builtin_fmaf(lo_f(qw[p]), lo_f(qw[p]), sqq);
+        sqq = __builtin_fmaf(hi_f(qw[p]), hi_f(qw[p]), sqq);
       }
     }
-    // the scale sequence of gdn_step.h needs a fold somewhere (rare): walk
-    // the nodes in index order, each continuing its parent's scale
-    const bool out = !(c >= kScaleLo && c <= kScaleHi);
-    if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
+    skk += __shfl_xor(skk, 16, kWave);
+    sqq += __shfl_xor(sqq, 16, kWave);
+    skk += __shfl_xor(skk, 32, kWave);
+    sqq += __shfl_xor(sqq, 32, kWave);
+    const float rk = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
+    const float rq = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
+
+
+    // ---- K K^T and K Q^T: lane (g4, n), entry e = (k_{4g4+e} . k_n) and
+    // (k_{4g4+e} . q_n) -- row n, column s = 4 g4 + e of the A layout of the
+    // f32 products below
+    f32x4 KK = {0.f, 0.f, 0.f, 0.f}, KQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      KK = mma_bf16(Kf[ks], Kf[ks], KK);
+      KQ = mma_bf16(Kf[ks], Qf[ks], KQ);
+    }
+
+    // ---- gates of token n, within each 16-lane group: segmented sums Gs
+    // (restarting after the last token R <= n whose decay is 0) and the scale
+    // sequence c of gdn_step.h (prefix products of alpha, folded when out of
+    // [2^-32, 2^32]; that rare case walks the tokens in order)
+    const bool tv = n < Tb;
+    const float a_t = tv ? __expf(gt) : 1.0f;
+    float Gs, c, phi = 1.f;
+    int R;
+    uint32_t anc;  // bit s: token s is a strict ancestor of token n
+    if constexpr (TREE) {
+      // pointer jumping over the ancestor chain: lane n holds the aggregate
+      // of the path segment (J, n] (segment sum and deepest zero-decay node,
+      // ancestor set, product of the decays) and combines it with the one that
+      // lane J holds for (J', J], all lanes at once; parents precede their
+      // children, so a path has at most 16 nodes and four jumps reach the
+      // root.  On a chain this is the window's scan, step for step.
+      int J = -1;
       for (int t = 0; t < T; ++t) {
         const int par = tree_parent(tree, lane * d.T + t);
-        const float cp = par < 0 ? 1.0f : lane_value(c, par);
-        float cn, fo = 1.f;
-        if (scale_step(cp, lane_value(a_t, t), cn)) {
-          fo = cn;
-          cn = 1.0f;
-        }
-        if (n == t) {
-          c = cn;
-          phi = fo;
+        J = n == t ? par : J;
+      }
+      const bool reset = gt < kReset;
+      Gs = reset ? 0.f : gt;
+      R = reset ? n : -1;
+      anc = 0u;
+      c = a_t;
+#pragma unroll
+      for (int step = 0; step < 4; ++step) {
+        const int src = J < 0 ? 0 : J;
+        const float Gy = __shfl(Gs, src, 16);
+        const int Ry = __shfl(R, src, 16);
+        const uint32_t ay = (uint32_t)__shfl((int)anc, src, 16);
+        const float cy = __shfl(c, src, 16);
+        const int Jy = __shfl(J, src, 16);
+        if (J >= 0) {
+          Gs = R < 0 ? Gy + Gs : Gs;
+          R = R > Ry ? R : Ry;
+          anc = anc | ay | (1u << J);
+          c *= cy;
+          J = Jy;
         }
       }
-    }
-  } else {
-    const bool reset = gt < kReset;
-    Gs = reset ? 0.f : gt;
-    R = reset ? n : -1;
-    anc = (1u << n) - 1u;
-    c = a_t;
-    // inclusive scans over the 16 lanes of each row by DPP row shifts; a
-    // lane without a source reads the identity (0, -1, 1)
-    auto scan_step = [&](auto ctrl) {
-      constexpr int kCtrl = decltype(ctrl)::value;
-      const float ys = row_shift<kCtrl>(Gs, 0.f);
-      const int yR = row_shift_int<kCtrl>(R, -1);
-      const float yc = row_shift<kCtrl>(c, 1.f);
-      Gs = R < 0 ? ys + Gs : Gs;
-      R = R > yR ? R : yR;
-      c *= yc;
-    };
-    scan_step(std::integral_constant<int, 0x111>{});  // row_shr:1
-    scan_step(std::integral_constant<int, 0x112>{});  // row_shr:2
-    scan_step(std::integral_constant<int, 0x114>{});  // row_shr:4
-    scan_step(std::integral_constant<int, 0x118>{});  // row_shr:8
-    const bool out = !(c >= kScaleLo && c <= kScaleHi);
-    if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
-      float cc = 1.0f;
-      for (int t = 0; t < T; ++t) {
-        float cn, fo = 1.f;
-        if (scale_step(cc, lane_value(a_t, t), cn)) {
-          fo = cn;
-          cn = 1.0f;
-        }
-        if (n == t) {
-          c = cn;
-          phi = fo;
-        }
-        cc = cn;
-      }
-    }
-  }
-  const float A = R >= 0 ? 0.f : __expf(Gs);
-  const float f2 = rk * __builtin_amdgcn_rcpf(c);  // ut = u * f2
-  const float so = scale * rq * A;                 // on (Q H)_n
-  const float xb = bt * A * rk;                    // on (K H)_n
-
-  // ---- per-token factors through the wave's LDS: lane (g4, n) reads those
-  // of the tokens 4 g4 .. 4 g4 + 3 as one float4 each
-  if (l < kTok) {
-    W.vec[0][n] = rk;
-    W.vec[1][n] = Gs;
-    W.vec[2][n] = bt;
-    W.vec[3][n] = xb;
-    W.vec[4][n] = so;
-    W.vec[5][n] = f2;
-  }
-  wave_lds_sync();
-  auto vec4 = [&](int i) {
-    return *reinterpret_cast<const f32x4*>(&W.vec[i][4 * g4]);
-  };
-  // ---- L and P entries of row n, columns s = 4 g4 + e
-  float PA[4];
-  {
-    const float bk = bt * rk, sq = scale * rq;
-    const f32x4 rk4 = vec4(0), gs4 = vec4(1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int s = 4 * g4 + e;
-      const float rks = rk4[e];
-      const float Gss = gs4[e];
-      const bool below = (anc >> s) & 1u;  // s a strict ancestor of n
-      const bool on_path = below || s == n;
-      const float dx = __expf(Gs - Gss);
-      const float dec = (on_path && s >= R) ? dx : 0.f;
-      const float lv = bk * rks * KK[e] * dec;
-      W.Lt[s * kLS + n] = below ? lv : 0.f;  // L[n][s], transposed
-      PA[e] = on_path ? sq * rks * KQ[e] * dec : 0.f;
-    }
-  }
-  wave_lds_sync();
-  // ---- T = (I + L)^-1: lane n < 16 of group 0 solves column n by
-  // right-looking substitution (once t_x is known it updates every later
-  // row), then the columns meet in LDS to be read back as row pieces
-  if (l < kTok) {
-    float acc[kTok];
-#pragma unroll
-    for (int r = 0; r < kTok; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int x = 0; x < kTok; ++x) {
-      const float tx = x == n ? 1.f : (x < n ? 0.f : -acc[x]);
-      W.Ts[x * kLS + n] = tx;
-#pragma unroll
-      for (int r = x + 1; r < kTok; ++r)
-        acc[r] = __builtin_fmaf(W.Lt[x * kLS + r], tx, acc[r]);
-    }
-  }
-  wave_lds_sync();
-  const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
-
-  // the key / query fragments are read again from the staged rows: the
-  // first copies died after K K^T and the norms, so they held no registers
-  // through the solve, and no global round trip follows the state's arrival
-
-  // ---- K H and Q H: per k-step, the eight rows of each column split into
-  // bf16 hi and lo, two MFMAs each against the exact key / query pieces
-  f32x4 KH[2], QH[2];
-#pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    KH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-    QH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    uint32_t h0[4], lo0[4], h1[4], lo1[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      split2(s2[ks][2 * p][0], s2[ks][2 * p + 1][0], h0[p], lo0[p]);
-      split2(s2[ks][2 * p][1], s2[ks][2 * p + 1][1], h1[p], lo1[p]);
-    }
-    const u32x4 H0 = {h0[0], h0[1], h0[2], h0[3]};
-    const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
-    const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
-    const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
-    const u32x4 kf = frag_k(ks), qf = frag_q(ks);
-    KH[0] = mma_bf16(kf, H0, KH[0]);
-    KH[1] = mma_bf16(kf, H1, KH[1]);
-    QH[0] = mma_bf16(qf, H0, QH[0]);
-    QH[1] = mma_bf16(qf, H1, QH[1]);
-    KH[0] = mma_bf16(kf, L0, KH[0]);
-    KH[1] = mma_bf16(kf, L1, KH[1]);
-    QH[0] = mma_bf16(qf, L0, QH[0]);
-    QH[1] = mma_bf16(qf, L1, QH[1]);
-  }
-
-  // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
-  const f32x4 bte = vec4(2), xbe = vec4(3), soe = vec4(4), f2e = vec4(5);
-  uint32_t vw[4];  // values of the tokens 4 g4 + e at columns c0, c0 + 1
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    vw[e] = *reinterpret_cast<const uint32_t*>(
-        &rows.v[4 * g4 + e][32 * w + 2 * n]);
-  f32x4 X[2];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool te = 4 * g4 + e < T;
-    const float x0 = __builtin_fmaf(-xbe[e], KH[0][e], bte[e] * lo_f(vw[e]));
-    const float x1 = __builtin_fmaf(-xbe[e], KH[1][e], bte[e] * hi_f(vw[e]));
-    X[0][e] = te ? x0 : 0.f;
-    X[1][e] = te ? x1 : 0.f;
-  }
-  const float ta[4] = {TA.x, TA.y, TA.z, TA.w};
-  f32x4 U[2], O[2];
-#pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    U[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) U[cs] = mma_f32(ta[e], X[cs][e], U[cs]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[cs][e] = soe[e] * QH[cs][e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
-  }
-  float* __restrict__ o0 = o + (tok0 * d.Hv + h) * (size_t)dv;
-  float* __restrict__ u0 = rec_u + (tok0 * d.Hv + h) * (size_t)dv;
-  float ut[2][4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g4 + e;
-    ut[0][e] = U[0][e] * f2e[e];
-    ut[1][e] = U[1][e] * f2e[e];
-    if (t < T) {
-      const uint32_t off = (uint32_t)(t * vo_step) + c0;
-      // outputs are not read again by this path: nontemporal stores keep
-      // them from displacing the records and rows in the caches (verify
-      // 0.206 -> 0.188 ms at 8 lanes x 48 layers, T = 16)
-      __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
-                                  reinterpret_cast<f32x2*>(o0 + off));
-      *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
-    }
-  }
-  if (cb == 0 && w == 0 && l < T)
-    rec_scale[gh0 + (size_t)l * d.Hv] = make_float2(phi, c);
-  // ---- debug states: the replay of this window's own records on the
-  // start state (the committed state in the fused call), token by token; in
-  // a draft tree, node t's state is the replay of the records on its path
-  if constexpr (DBG) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
-      W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
-    }
-    wave_lds_sync();
-    // record r applied to st: the fold, then the rank-1 write
-    auto apply = [&](f32x2 (&st)[kKS][8], int r) {
-      const float ph = lane_value(phi, r);
-      if (ph != 1.f) {
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            st[ks][e][0] = ph * st[ks][e][0];
-            st[ks][e][1] = ph * st[ks][e][1];
+      // the scale sequence of gdn_step.h needs a fold somewhere (rare): walk
+      // the nodes in index order, each continuing its parent's scale
+      const bool out = !(c >= kScaleLo && c <= kScaleHi);
+      if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
+        for (int t = 0; t < T; ++t) {
+          const int par = tree_parent(tree, lane * d.T + t);
+          const float cp = par < 0 ? 1.0f : lane_value(c, par);
+          float cn, fo = 1.f;
+          if (scale_step(cp, lane_value(a_t, t), cn)) {
+            fo = cn;
+            cn = 1.0f;
           }
-      }
-      const float ua = W.Us[r * kUS + 2 * n], ub = W.Us[r * kUS + 2 * n + 1];
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(
-            k0 + (uint32_t)(r * kq_step) + 32 * ks + 8 * g4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
-          st[ks][e][0] = state_update(st[ks][e][0], ua, kv);
-          st[ks][e][1] = state_update(st[ks][e][1], ub, kv);
+          if (n == t) {
+            c = cn;
+            phi = fo;
+          }
         }
-      }
-    };
-    auto emit = [&](const f32x2 (&st)[kKS][8], int t) {
-      const float ct = lane_value(c, t);
-      float* __restrict__ dp =
-          dbg + (((tok0 + t) * d.Hv + h) * (size_t)kDK) * dv;
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *srow(dp, 32 * ks + e) =
-              f32x2{materialise(ct, st[ks][e][0]), materialise(ct, st[ks][e][1])};
-    };
-    if constexpr (TREE) {
-#pragma unroll 1
-      for (int t = 0; t < T; ++t) {
-        const uint32_t path = (uint32_t)lane_int((int)anc, t) | (1u << t);
-        f32x2 sd[kKS][8];
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sd[ks][e] = s2[ks][e];
-#pragma unroll 1
-        for (int r = 0; r <= t; ++r)
-          if ((path >> r) & 1u) apply(sd, r);
-        emit(sd, t);
       }
     } else {
-#pragma unroll 1
-      for (int t = 0; t < T; ++t) {
-        apply(s2, t);
-        emit(s2, t);
+      const bool reset = gt < kReset;
+      Gs = reset ? 0.f : gt;
+      R = reset ? n : -1;
+      anc = (1u << n) - 1u;
+      c = a_t;
+      // inclusive scans over the 16 lanes of each row by DPP row shifts; a
+      // lane without a source reads the identity (0, -1, 1)
+      auto scan_step = [&](auto ctrl) {
+        constexpr int kCtrl = decltype(ctrl)::value;
+        const float ys = row_shift<kCtrl>(Gs, 0.f);
+        const int yR = row_shift_int<kCtrl>(R, -1);
+        const float yc = row_shift<kCtrl>(c, 1.f);
+        Gs = R < 0 ? ys + Gs : Gs;
+        R = R > yR ? R : yR;
+        c *= yc;
+      };
+      scan_step(std::integral_constant<int, 0x111>{});  // row_shr:1
+      scan_step(std::integral_constant<int, 0x112>{});  // row_shr:2
+      scan_step(std::integral_constant<int, 0x114>{});  // row_shr:4
+      scan_step(std::integral_constant<int, 0x118>{});  // row_shr:8
+      // the scale continues from the previous block's last token
+      if constexpr (MB) c = c_in * c;
+      const bool out = !(c >= kScaleLo && c <= kScaleHi);
+      if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
+        float cc = c_in;
+        for (int t = 0; t < Tb; ++t) {
+          float cn, fo = 1.f;
+          if (scale_step(cc, lane_value(a_t, t), cn)) {
+            fo = cn;
+            cn = 1.0f;
+          }
+          if (n == t) {
+            c = cn;
+            phi = fo;
+          }
+          cc = cn;
+        }
       }
     }
+    const float A = R >= 0 ? 0.f : __expf(Gs);
+    const float f2 = rk * __builtin_amdgcn_rcpf(c);  // ut = u * f2
+    const float so = scale * rq * A;                 // on (Q H)_n
+    const float xb = bt * A * rk;                    // on (K H)_n
+
+    // ---- per-token factors through the wave's LDS: lane (g4, n) reads those
+    // of the tokens 4 g4 .. 4 g4 + 3 as one float4 each
+    if (l < kTok) {
+      W.vec[0][n] = rk;
+      W.vec[1][n] = Gs;
+      W.vec[2][n] = bt;
+      W.vec[3][n] = xb;
+      W.vec[4][n] = so;
+      W.vec[5][n] = f2;
+    }
+    wave_lds_sync();
+    auto vec4 = [&](int i) {
+      return *reinterpret_cast<const f32x4*>(&W.vec[i][4 * g4]);
+    };
+    // ---- L and P entries of row n, columns s = 4 g4 + e
+    float PA[4];
+    {
+      const float bk = bt * rk, sq = scale * rq;
+      const f32x4 rk4 = vec4(0), gs4 = vec4(1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 4 * g4 + e;
+        const float rks = rk4[e];
+        const float Gss = gs4[e];
+        const bool below = (anc >> s) & 1u;  // s a strict ancestor of n
+        const bool on_path = below || s == n;
+        const float dx = __expf(Gs - Gss);
+        const float dec = (on_path && s >= R) ? dx : 0.f;
+        const float lv = bk * rks * KK[e] * dec;
+        W.Lt[s * kLS + n] = below ? lv : 0.f;  // L[n][s], transposed
+        PA[e] = on_path ? sq * rks * KQ[e] * dec : 0.f;
+      }
+    }
+    wave_lds_sync();
+    // ---- T = (I + L)^-1: lane n < 16 of group 0 solves column n by
+    // right-looking substitution (once t_x is known it updates every later
+    // row), then the columns meet in LDS to be read back as row pieces
+    if (l < kTok) {
+      float acc[kTok];
+#pragma unroll
+      for (int r = 0; r < kTok; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int x = 0; x < kTok; ++x) {
+        const float tx = x == n ? 1.f : (x < n ? 0.f : -acc[x]);
+        W.Ts[x * kLS + n] = tx;
+#pragma unroll
+        for (int r = x + 1; r < kTok; ++r)
+          acc[r] = __builtin_fmaf(W.Lt[x * kLS + r], tx, acc[r]);
+      }
+    }
+    wave_lds_sync();
+    const float4 TA = *reinterpret_cast<const float4*>(&W.Ts[n * kLS + 4 * g4]);
+
+    // the key / query fragments are read again from the staged rows: the
+    // first copies died after K K^T and the norms, so they held no registers
+    // through the solve, and no global round trip follows the state's arrival
+
+    // ---- K H and Q H: per k-step, the eight rows of each column split into
+    // bf16 hi and lo, two MFMAs each against the exact key / query pieces
+    f32x4 KH[2], QH[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      KH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      QH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      uint32_t h0[4], lo0[4], h1[4], lo1[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        split2(s2[ks][2 * p][0], s2[ks][2 * p + 1][0], h0[p], lo0[p]);
+        split2(s2[ks][2 * p][1], s2[ks][2 * p + 1][1], h1[p], lo1[p]);
+      }
+      const u32x4 H0 = {h0[0], h0[1], h0[2], h0[3]};
+      const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
+      const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
+      const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
+      const u32x4 kf = frag_k(ks), qf = frag_q(ks);
+      KH[0] = mma_bf16(kf, H0, KH[0]);
+      KH[1] = mma_bf16(kf, H1, KH[1]);
+      QH[0] = mma_bf16(qf, H0, QH[0]);
+      QH[1] = mma_bf16(qf, H1, QH[1]);
+      KH[0] = mma_bf16(kf, L0, KH[0]);
+      KH[1] = mma_bf16(kf, L1, KH[1]);
+      QH[0] = mma_bf16(qf, L0, QH[0]);
+      QH[1] = mma_bf16(qf, L1, QH[1]);
+    }
+    if constexpr (MB) {
+      // past the first block the held state is the scaled replay state:
+      // S = c_in * St
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          KH[cs][e] *= c_in;
+          QH[cs][e] *= c_in;
+        }
+    }
+
+    // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
+    const f32x4 bte = vec4(2), xbe = vec4(3), soe = vec4(4), f2e = vec4(5);
+    uint32_t vw[4];  // values of the tokens 4 g4 + e at columns c0, c0 + 1
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vw[e] = *reinterpret_cast<const uint32_t*>(
+          &rows.v[4 * g4 + e][32 * w + 2 * n]);
+    f32x4 X[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool te = 4 * g4 + e < Tb;
+      const float x0 = __builtin_fmaf(-xbe[e], KH[0][e], bte[e] * lo_f(vw[e]));
+      const float x1 = __builtin_fmaf(-xbe[e], KH[1][e], bte[e] * hi_f(vw[e]));
+      X[0][e] = te ? x0 : 0.f;
+      X[1][e] = te ? x1 : 0.f;
+    }
+    const float ta[4] = {TA.x, TA.y, TA.z, TA.w};
+    f32x4 U[2], O[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      U[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[cs] = mma_f32(ta[e], X[cs][e], U[cs]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[cs][e] = soe[e] * QH[cs][e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
+    }
+    float* __restrict__ o0 = o + ((tok0 + tb) * d.Hv + h) * (size_t)dv;
+    float* __restrict__ u0 = rec_u + ((tok0 + tb) * d.Hv + h) * (size_t)dv;
+    float ut[2][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g4 + e;
+      ut[0][e] = U[0][e] * f2e[e];
+      ut[1][e] = U[1][e] * f2e[e];
+      if (t < Tb) {
+        const uint32_t off = (uint32_t)(t * vo_step) + c0;
+        // outputs are not read again by this path: nontemporal stores keep
+        // them from displacing the records and rows in the caches (verify
+        // 0.206 -> 0.188 ms at 8 lanes x 48 layers, T = 16)
+        __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
+                                    reinterpret_cast<f32x2*>(o0 + off));
+        *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
+      }
+    }
+    if (cb == 0 && w == 0 && l < Tb)
+      rec_scale[gh0 + (size_t)(tb + l) * d.Hv] = make_float2(phi, c);
+    // ---- debug states: the replay of this window's own records on the
+    // start state (the committed state in the fused call), token by token; in
+    // a draft tree, node t's state is the replay of the records on its path.
+    // A window of several blocks replays each block but the last on the held
+    // state, which the next block starts from.
+    const bool more = MB && tb + kTok < T;
+    if (DBG || more) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
+        W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
+      }
+      wave_lds_sync();
+      // record r applied to st: the fold, then the rank-1 write
+      auto apply = [&](f32x2 (&st)[kKS][8], int r) {
+        const float ph = lane_value(phi, r);
+        if (ph != 1.f) {
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              st[ks][e][0] = ph * st[ks][e][0];
+              st[ks][e][1] = ph * st[ks][e][1];
+            }
+        }
+        const float ua = W.Us[r * kUS + 2 * n], ub = W.Us[r * kUS + 2 * n + 1];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          // the block's raw key rows, still staged in LDS
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(
+              &rows.k[r][32 * ks + 8 * g4]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
+            st[ks][e][0] = state_update(st[ks][e][0], ua, kv);
+            st[ks][e][1] = state_update(st[ks][e][1], ub, kv);
+          }
+        }
+      };
+      [[maybe_unused]] auto emit = [&](const f32x2 (&st)[kKS][8], int t) {
+        const float ct = lane_value(c, t);
+        float* __restrict__ dp =
+            dbg + (((tok0 + tb + t) * d.Hv + h) * (size_t)kDK) * dv;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *srow(dp, 32 * ks + e) =
+                f32x2{materialise(ct, st[ks][e][0]), materialise(ct, st[ks][e][1])};
+      };
+      if constexpr (TREE) {
+#pragma unroll 1
+        for (int t = 0; t < T; ++t) {
+          const uint32_t path = (uint32_t)lane_int((int)anc, t) | (1u << t);
+          f32x2 sd[kKS][8];
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sd[ks][e] = s2[ks][e];
+#pragma unroll 1
+          for (int r = 0; r <= t; ++r)
+            if ((path >> r) & 1u) apply(sd, r);
+          emit(sd, t);
+        }
+      } else {
+#pragma unroll 1
+        for (int t = 0; t < Tb; ++t) {
+          apply(s2, t);
+          if constexpr (DBG) emit(s2, t);
+        }
+      }
+    }
+    if (!more) break;
+    c_in = lane_value(c, Tb - 1);
   }
 }
 
-template <bool REPLAY, bool DBG, bool TREE, typename Tab>
+template <bool REPLAY, bool DBG, bool TREE, bool MB, typename Tab>
 static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
                            const VerifyArgs& a, const PrevRecords& pr,
                            const Tab& tree, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv * (w.dv / kCB);
-  return launch(mverify_kernel<REPLAY, DBG, TREE>, dim3(blocks), dim3(kBlock),
+  return launch(mverify_kernel<REPLAY, DBG, TREE, MB>, dim3(blocks), dim3(kBlock),
                 st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                 (const uint16_t*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
                 a.dbg, w, tl, a.scale, a.l2, pr, tree);
@@ -696,22 +750,31 @@ static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
 
 }  // namespace wm
 
-bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a) {
+bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a,
+                      bool tree) {
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
   return in_dtype == GDN_BF16 && d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
-         d.t_max <= wm::kTok && al(a.q, 16) && al(a.k, 16) && al(a.v, 4) &&
-         al(a.S, 8) && al(a.o, 8) && (a.dbg == nullptr || al(a.dbg, 8));
+         d.t_max <= (tree ? wm::kTok : GDN_MAX_T) && al(a.q, 16) &&
+         al(a.k, 16) && al(a.v, 4) && al(a.S, 8) && al(a.o, 8) &&
+         (a.dbg == nullptr || al(a.dbg, 8));
 }
 
 hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
                           const VerifyArgs& a, const PrevRecords& pr,
                           bool replay, hipStream_t st) {
   const NoTable none{};
+  if (w.T > wm::kTok) {  // windows of several blocks
+    if (replay)
+      return a.dbg ? wm::launch_t<true, true, false, true>(w, tl, a, pr, none, st)
+                   : wm::launch_t<true, false, false, true>(w, tl, a, pr, none, st);
+    return a.dbg ? wm::launch_t<false, true, false, true>(w, tl, a, pr, none, st)
+                 : wm::launch_t<false, false, false, true>(w, tl, a, pr, none, st);
+  }
   if (replay)
-    return a.dbg ? wm::launch_t<true, true, false>(w, tl, a, pr, none, st)
-                 : wm::launch_t<true, false, false>(w, tl, a, pr, none, st);
-  return a.dbg ? wm::launch_t<false, true, false>(w, tl, a, pr, none, st)
-               : wm::launch_t<false, false, false>(w, tl, a, pr, none, st);
+    return a.dbg ? wm::launch_t<true, true, false, false>(w, tl, a, pr, none, st)
+                 : wm::launch_t<true, false, false, false>(w, tl, a, pr, none, st);
+  return a.dbg ? wm::launch_t<false, true, false, false>(w, tl, a, pr, none, st)
+               : wm::launch_t<false, false, false, false>(w, tl, a, pr, none, st);
 }
 
 hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,
@@ -719,8 +782,8 @@ hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,
                                hipStream_t st) {
   PrevRecords none;
   memset(&none, 0, sizeof(none));
-  return a.dbg ? wm::launch_t<false, true, true>(w, tl, a, none, tree, st)
-               : wm::launch_t<false, false, true>(w, tl, a, none, tree, st);
+  return a.dbg ? wm::launch_t<false, true, true, false>(w, tl, a, none, tree, st)
+               : wm::launch_t<false, false, true, false>(w, tl, a, none, tree, st);
 }
 
 }  // namespace gdn

@@ -94,7 +94,8 @@ typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 
 enum {
   GDN_FLAG_L2NORM_QK = 1,        /* normalise q and k inside the kernels */
-  GDN_FLAG_PREFILL_ONE_CHAIN = 2 /* gdn_prefill_chunked*: never in segments */
+  GDN_FLAG_PREFILL_ONE_CHAIN = 2, /* gdn_prefill_chunked*: never in segments */
+  GDN_FLAG_TOKENWISE = 4         /* the verify calls: always token by token */
 };
 
 typedef struct {
@@ -137,14 +138,17 @@ size_t gdn_records_bytes(const gdn_dims* dims);
  *   dbg_states  device f32 [n_layers][n_lanes][t_max][h_v][d_k][d_v] or
  *               NULL: when given, every intermediate state S_1..S_T, as the
  *               kernel holds it (for tests; costs 64 KiB per head per token).
- *               For bf16 inputs with d_k = d_v = 128 and t_max <= 16 the
- *               window is evaluated as one block (the chunked WY/UT form of
- *               the delta rule, Yang et al., NeurIPS 2024, Sec. 3) on the
- *               matrix cores; its intermediate states are then defined as the
- *               token-by-token replay of its own records, which is what
- *               dbg_states receives.
+ *               For bf16 inputs with d_k = 128 and d_v a multiple of 128
+ *               the window is evaluated in blocks of 16 tokens (the chunked
+ *               WY/UT form of the delta rule, Yang et al., NeurIPS 2024,
+ *               Sec. 3) on the matrix cores, each block from the replay of
+ *               the records of the blocks before it; its intermediate states
+ *               are then defined as the token-by-token replay of its own
+ *               records, which is what dbg_states receives.
  *   scale       multiplies o only (1.0f for o_t = S_t q_t).
- *   flags       GDN_FLAG_L2NORM_QK or 0.
+ *   flags       GDN_FLAG_L2NORM_QK, GDN_FLAG_TOKENWISE (evaluate token by
+ *               token at every shape: verify then holds each intermediate
+ *               state itself), or 0.
  *   stream      hipStream_t (NULL = the null stream).
  */
 int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
@@ -159,12 +163,13 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
  * with m = 0 are neither read nor written.  Commit never folds replayed
  * steps into a block product: it applies the recorded steps one token at a
  * time.  S_m is bit-for-bit the state written to dbg_states for token m:
- *   - on the token-by-token verify (f32 inputs, d_k < 128, d_v != 128,
- *     windows over 16 tokens) that is the state verify held after its m-th
- *     token, formed by the same per-step instruction sequence;
- *   - on the block-form verify (bf16, d_k = d_v = 128, t_max <= 16), which
- *     never forms per-token states, it is the replay of verify's records
- *     with commit's own operations.  There the emitted deltas and outputs
+ *   - on the token-by-token verify (f32 inputs, d_k < 128, d_v not a
+ *     multiple of 128, or GDN_FLAG_TOKENWISE) that is the state verify held
+ *     after its m-th token, formed by the same per-step instruction
+ *     sequence;
+ *   - on the block-form verify (bf16, d_k = 128, d_v a multiple of 128),
+ *     which never forms per-token states, it is the replay of verify's
+ *     records with commit's own operations.  There the emitted deltas and outputs
  *     agree with the rule applied to those replayed states to within about
  *     3e-7 (deltas) and 5e-6 (outputs) relative, not bit for bit.
  *   m_lane   host int32[n_lanes], 0..t_lane[lane]
@@ -187,9 +192,10 @@ int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
  *   parent   host int32 [n_lanes][t_max]: parent[n][t] in -1..t-1 for
  *            t < t_lane[n] (-1: the node steps from S0); nodes are ordered so
  *            that a parent precedes its children.  For bf16 inputs with
- *            d_k = d_v = 128 and t_max <= 16 the tree is evaluated as one
- *            block product (the causal mask of the chunked form replaced by
- *            the ancestor relation) and any order costs the same; the debug
+ *            d_k = d_v = 128 and t_max <= 16 (and without
+ *            GDN_FLAG_TOKENWISE) the tree is evaluated as one block product
+ *            (the causal mask of the chunked form replaced by the ancestor
+ *            relation) and any order costs the same; the debug
  *            state of a node is then the replay of the records on its root
  *            path.  Otherwise depth-first order is cheapest: verify rebuilds
  *            the parent's state (S0 plus the path's recorded steps) whenever
@@ -350,9 +356,10 @@ int gdn_prefill_chunked_noalloc(int32_t n_seqs, int32_t seq_len, int32_t h_v,
  *            (f32 [h_k][d_k]), u_t / sqrt(|k_t|^2 + 1e-6) (f32 [h_v][d_v])
  *            and alpha_t (f32 [h_v][d_k])
  * Supported: d_k == 128 (GDN_EUNSUPPORTED otherwise; gdn_kda_records_bytes
- * returns 0).  For bf16 inputs with d_v = 128 and t_max <= 16 the window is
- * evaluated as one block product with channel-weighted decays; dbg_states
- * then receives the replay of its records (as for gdn_verify).
+ * returns 0).  For bf16 inputs with d_v = 128 and t_max <= 16 (and without
+ * GDN_FLAG_TOKENWISE) the window is evaluated as one block product with
+ * channel-weighted decays; dbg_states then receives the replay of its
+ * records (as for gdn_verify).
  */
 size_t gdn_kda_records_bytes(const gdn_dims* dims);
 int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,

@@ -98,6 +98,18 @@ def test_verify_rejects_bad_arguments_on_host():
                             *[ctypes.c_void_p(1 << 20)] * 5, None,
                             ctypes.c_float(1.0), 6, None)
     assert st == gdn.GDN_EINVAL
+    st = gdn.lib.gdn_verify(ctypes.byref(d), (ctypes.c_int32 * 2)(1, 1),
+                            *[ctypes.c_void_p(1 << 20)] * 3, gdn.GDN_BF16,
+                            *[ctypes.c_void_p(1 << 20)] * 5, None,
+                            ctypes.c_float(1.0), 8, None)
+    assert st == gdn.GDN_EINVAL
+    # the norm and token-by-token flags are accepted (idle lanes: no launch)
+    st = gdn.lib.gdn_verify(ctypes.byref(d), (ctypes.c_int32 * 2)(0, 0),
+                            *[ctypes.c_void_p(1 << 20)] * 3, gdn.GDN_BF16,
+                            *[ctypes.c_void_p(1 << 20)] * 5, None,
+                            ctypes.c_float(1.0),
+                            gdn.GDN_FLAG_L2NORM_QK | gdn.GDN_FLAG_TOKENWISE, None)
+    assert st == gdn.GDN_OK
     # unknown dtype
     st = gdn.lib.gdn_verify(ctypes.byref(d), (ctypes.c_int32 * 2)(1, 1),
                             *[ctypes.c_void_p(1 << 20)] * 3, 7,

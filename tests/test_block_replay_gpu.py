@@ -162,12 +162,15 @@ FILLS = [("plain", _no_fill), ("alpha0", _zero_decay),
          ("folds", _strong_decay)]
 
 
+@pytest.mark.parametrize("T", [16, 64])
 @pytest.mark.parametrize("fill", FILLS, ids=[f[0] for f in FILLS])
-def test_verify_emits_the_rule_on_the_replayed_states(fill):
+def test_verify_emits_the_rule_on_the_replayed_states(fill, T):
+    """T = 64: four blocks of 16, each from the replay of the blocks
+    before it."""
     name, g_fill = fill
-    shape = gs.WindowShape(2, 4, 4, 2, 128, 128, 16)
-    key, w, S0 = _window("verify_" + name, shape, g_fill)
-    w.t_lane[0] = 16
+    shape = gs.WindowShape(2, 4, 4, 2, 128, 128, T)
+    key, w, S0 = _window("verify_%s_%d" % (name, T), shape, g_fill)
+    w.t_lane[0] = T
     dims = gdn.Dims.of(*shape.__dict__.values())
     q, k, v, beta, g = window_to_dev(w, torch)
     o, dbg = _empty(dims)
@@ -179,10 +182,12 @@ def test_verify_emits_the_rule_on_the_replayed_states(fill):
     assert e_u <= BOUND_U and e_o <= BOUND_O
 
 
-def test_fused_window_emits_the_rule_on_the_replayed_states():
+@pytest.mark.parametrize("T", [16, 40])
+def test_fused_window_emits_the_rule_on_the_replayed_states(T):
     """gdn_commit_verify: the new window starts from the committed S_m of
-    the previous one (replayed in the same launch)."""
-    shape = gs.WindowShape(2, 4, 4, 2, 128, 128, 16)
+    the previous one (replayed in the same launch; at T = 40 the previous
+    records arrive in chunks of 16 and the window runs as three blocks)."""
+    shape = gs.WindowShape(2, 4, 4, 2, 128, 128, T)
     dims = gdn.Dims.of(*shape.__dict__.values())
     _, w0, S0 = _window("fused_prev", shape)
     _, w1, _ = _window("fused_next", shape, _strong_decay)

@@ -29,7 +29,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _run_verify(dims, w, S_dev, dbg=False, scale=1.0, l2norm=True):
+def _run_verify(dims, w, S_dev, dbg=False, scale=1.0, l2norm=True,
+                tokenwise=False):
     q, k, v, beta, g = window_to_dev(w, torch)
     o = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
                     dims.d_v), float("nan"), device="cuda")
@@ -39,7 +40,7 @@ def _run_verify(dims, w, S_dev, dbg=False, scale=1.0, l2norm=True):
         dbg_t = torch.full((dims.n_layers, dims.n_lanes, dims.t_max, dims.h_v,
                             dims.d_k, dims.d_v), float("nan"), device="cuda")
     gdn.verify(dims, w.t_lane, q, k, v, beta, g, S_dev, o, rec, dbg_t,
-               scale=scale, l2norm=l2norm)
+               scale=scale, l2norm=l2norm, tokenwise=tokenwise)
     return o, rec, dbg_t
 
 
@@ -58,14 +59,14 @@ SMALL = [
     ("d32_dv200_f32", 1, 1, 3, 3, 32, 200, 7, False, False, True, 1.0),
     ("d16_noscale_nonorm", 2, 2, 2, 2, 16, 16, 4, False, False, False, 0.5),
     ("d128_group4", 1, 2, 8, 2, 128, 64, 3, True, False, True, 1.0),
-    # matrix-core verify (bf16, d_k = d_v = 128, t_max <= 16): unnormalised
+    # matrix-core verify (bf16, d_k = d_v = 128, one block): unnormalised
     # keys with an output scale, one key head per value head, T = 1 windows
     ("d128_noscale_nonorm", 1, 2, 4, 2, 128, 128, 8, True, True, False, 0.5),
     ("d128_group1", 1, 2, 2, 2, 128, 128, 5, True, True, True, 1.0),
     ("d128_t1", 2, 3, 2, 1, 128, 128, 1, True, False, True, 1.0),
     ("d128_dv256", 1, 2, 2, 1, 128, 256, 9, True, True, True, 1.0),
-    # the longest windows the ABI takes (64 tokens): the token-by-token
-    # kernel, bf16 at d = 128 and f32 at d_k = 64
+    # the longest windows the ABI takes (64 tokens): bf16 at d = 128 in four
+    # blocks of 16 on the matrix cores, f32 at d_k = 64 token by token
     ("d128_t64_max_window", 1, 2, 4, 2, 128, 128, 64, True, True, True, 1.0),
     ("d64_t33_f32", 1, 2, 2, 1, 64, 64, 33, False, True, True, 1.0),
     # the ABI's value-dimension limits: d_v = 1024 on both kernels (bf16:
@@ -75,6 +76,47 @@ SMALL = [
     ("f32_d128_dv1024_max", 1, 1, 2, 1, 128, 1024, 5, False, True, True, 1.0),
     ("d32_dv1_min", 1, 2, 2, 1, 32, 1, 5, True, True, True, 1.0),
 ]
+
+
+@pytest.mark.parametrize("T", [16, 40])
+def test_tokenwise_flag_at_block_shapes(T):
+    """GDN_FLAG_TOKENWISE at shapes the block form would take (bf16,
+    d = 128): verify runs token by token and holds every intermediate state
+    itself.  Its outputs and states meet the oracle, commit(m) is bit for bit
+    the state it held after token m, and it agrees with the block form to
+    the tolerance, not bit for bit (another kernel ran)."""
+    shape = gs.WindowShape(1, 3, 4, 2, 128, 128, T)
+    key = (104, T)
+    w = gs.window_inputs(shape, key, ragged=True)
+    w.t_lane[0] = T
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(1, 3, 4, 2, 128, 128, T)
+    o, rec, dbg = _run_verify(dims, w, to_dev(S0, torch), dbg=True,
+                              tokenwise=True)
+    ob, _, dbgb = _run_verify(dims, w, to_dev(S0, torch), dbg=True)
+    torch.cuda.synchronize()
+    o_np, dbg_np = o.cpu().numpy(), dbg.cpu().numpy()
+    q64, k64, v64, b64, g64 = w.as_f64()
+    o_ref, st_ref = oracle.verify(q64, k64, v64, b64, g64, S0, w.t_lane,
+                                  want_states=True)
+    e_o = o_rel_err(o_np, o_ref, w.t_lane)
+    say("  T=%d tokenwise: o err %.3e" % (T, e_o))
+    assert e_o <= TOL
+    assert o_rel_err(o_np, ob.cpu().numpy(), w.t_lane) <= TOL
+    assert not np.array_equal(o_np[:, 0, :T], ob.cpu().numpy()[:, 0, :T])
+    for t in range(T):
+        lanes = [n for n in range(3) if w.t_lane[n] > t]
+        assert s_rel_err(dbg_np[:, lanes, t], st_ref[:, lanes, t]) <= TOL, t
+        assert s_rel_err(dbg_np[:, lanes, t], dbgb.cpu().numpy()[:, lanes, t]) <= TOL, t
+    for m in (1, T // 2, T):
+        m_lane = np.minimum(m, w.t_lane)
+        S_c = to_dev(S0, torch)
+        gdn.commit(dims, m_lane, w.t_lane, rec, S_c)
+        S_c = S_c.cpu().numpy()
+        for n in range(3):
+            mm = int(m_lane[n])
+            want = S0[:, n] if mm == 0 else dbg_np[:, n, mm - 1]
+            assert np.array_equal(S_c[:, n], want), (m, n)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
