@@ -1,8 +1,10 @@
 // gdn_window_mfma.hip -- speculative-window verify, draft-tree verify and
 // the fused commit + verify on the gfx950 matrix cores, for bf16 inputs,
-// d_k = 128, d_v a multiple of 128 and windows of at most 16 tokens (the
+// d_k = 128 and d_v a multiple of 128: windows of at most 16 tokens (the
 // shapes of the speculative-decoding section of the NInfer technical review,
-// blog.123qwe.co.kr post 4624).  Other shapes take gdn_window.hip.
+// blog.123qwe.co.kr post 4624) as one block, longer windows (up to 64
+// tokens) in blocks of 16, trees of at most 16 nodes.  Other shapes, and
+// calls with GDN_FLAG_TOKENWISE, take gdn_window.hip.
 //
 // The window is one chunk of the block (WY/UT) form of the rule: Yang et
 // al., "Parallelizing Linear Transformers with the Delta Rule over Sequence
@@ -52,6 +54,10 @@
 // The fused call first replays the previous window's accepted prefix on the
 // state it loads, with the commit's operations, and stores it; a draft tree
 // replaces the causal mask by the ancestor relation (see mverify_kernel).
+// MB (windows of more than 16 tokens): block b runs from the held state,
+// then the block's own records are replayed on it (the commit's
+// operations), and block b + 1 starts from that scaled replay state, its
+// K H and Q H scaled by the scale of block b's last token.
 // MFMA layouts: gdn_mfma_util.h.
 #include <hip/hip_runtime.h>
 

@@ -1,9 +1,10 @@
 """The block-form windows against the states that commit stores.
 
-For bf16 inputs with d_k = d_v = 128 and windows of at most 16 tokens, the
-verify kernels (plain, fused with the previous commit, draft tree, KDA)
-evaluate a window as one block product on the matrix cores (the chunked
-WY/UT form) and never hold the per-token states.  What they record (the
+For bf16 inputs with d_k = d_v = 128, the verify kernels (plain, fused
+with the previous commit, draft tree, KDA) evaluate a window as block
+products on the matrix cores (the chunked WY/UT form; windows of more than
+16 tokens in blocks of 16, each from the replay of the blocks before it) and
+never hold the per-token states.  What they record (the
 deltas u_t, the decay steps, the raw keys) is replayed token by token by
 commit, and commit(m) is bit for bit the debug state after token m (tested
 elsewhere).  These tests close the remaining gap: the deltas and outputs
@@ -20,8 +21,9 @@ c_t * ut_t / rk_t.  Bounds: 2e-6 on u and 1e-5 on o, 100 and 20 times
 below the oracle tolerance.  The split-bf16 products of the block form
 (hi = bf16(x), lo = bf16(x - hi)) carry at most 2^-16 relative error per
 element and about 2^-18 typically, and those errors enter a dot product of
-128 terms with random signs; the replay's own f32 rounding over at most 16
-tokens is of order 1e-7.  Measured on MI355X: u within 1.9e-7 .. 2.8e-7 and
+128 terms with random signs; the replay's own f32 rounding is of order
+1e-7 (over at most 16 tokens within a block: every block starts from the
+replayed state).  Measured on MI355X: u within 1.9e-7 .. 2.8e-7 and
 o within 3.2e-7 .. 4.5e-6 over these cases.  The ReplaySSM passage of the
 NInfer review asks that the committed transitions equal what verify computed
 in finite precision; these checks measure how far the block form's emitted
