@@ -49,6 +49,7 @@ CASES = [
     ("d128_dv256", 1, 3, 2, 1, 128, 256, 8, True, 4, True),
     ("d128_t40_long_window", 1, 3, 2, 1, 128, 128, 40, True, 3, False),
     ("d128_t64_blocks_dbg", 1, 2, 2, 1, 128, 128, 64, True, 3, True),
+    ("d128_t17_blocks", 1, 4, 2, 1, 128, 128, 17, True, 4, True),
 ]
 
 

@@ -68,6 +68,8 @@ SMALL = [
     # the longest windows the ABI takes (64 tokens): bf16 at d = 128 in four
     # blocks of 16 on the matrix cores, f32 at d_k = 64 token by token
     ("d128_t64_max_window", 1, 2, 4, 2, 128, 128, 64, True, True, True, 1.0),
+    # a second block of one token
+    ("d128_t17_one_token_block", 1, 2, 2, 1, 128, 128, 17, True, False, True, 1.0),
     # three blocks with two 128-column blocks per head, no key norm, a scale
     ("d128_dv256_t40_blocks", 2, 2, 2, 1, 128, 256, 40, True, True, False, 0.5),
     ("d64_t33_f32", 1, 2, 2, 1, 64, 64, 33, False, True, True, 1.0),
