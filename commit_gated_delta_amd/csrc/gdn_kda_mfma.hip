@@ -1,6 +1,9 @@
 // gdn_kda_mfma.hip -- KDA verify (the per-channel-decay sibling of the rule)
-// on the gfx950 matrix cores, for bf16 inputs, d_k = d_v = 128 and windows
-// of at most 16 tokens.  Other shapes take gdn_kda.hip.
+// on the gfx950 matrix cores, for bf16 inputs and d_k = d_v = 128: a window
+// of at most 16 tokens as one block, longer windows (up to 64 tokens) in
+// blocks of 16, each block from the replay of the records before it (the
+// commit's decay multiply and fma on the held state).  Other shapes, and
+// calls with GDN_FLAG_TOKENWISE, take gdn_kda.hip.
 //
 // The rule (Kimi Delta Attention of Kimi Linear, 2025; the NInfer technical
 // review, blog.123qwe.co.kr post 4624, names its state and a kda_replay op
@@ -89,7 +92,7 @@ __device__ __forceinline__ void widen8(u32x4 w, float (&x)[8]) {
   }
 }
 
-template <bool DBG>
+template <bool DBG, bool MB>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
 void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const float* __restrict__ beta,
@@ -100,8 +103,10 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  int l2norm) {
   __shared__ KdaLds sh;
   __shared__ KdaWave wv[kWaves];
-  __shared__ std::conditional_t<DBG, AFrags, char> af_own;
-  AFrags& Af = *reinterpret_cast<AFrags*>(DBG ? (void*)&af_own : (void*)&sh.a[0][0]);
+  // the replay of the debug states and between the blocks of a long
+  // window reads the decays a: the fragments then have their own space
+  __shared__ std::conditional_t<DBG || MB, AFrags, char> af_own;
+  AFrags& Af = *reinterpret_cast<AFrags*>(DBG || MB ? (void*)&af_own : (void*)&sh.a[0][0]);
 
   int item = xcd_item(blockIdx.x, gridDim.x);
   const int h = item % d.Hv;
@@ -133,31 +138,37 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // before the state products overlaps its latency.  Tokens at or past T
   // read token 0 and become k = q = 0, alpha = 1, beta = 0.
   const int rt = tid >> 4, rp = tid & 15;  // row token, 8-entry piece
-  const bool rv = rt < T;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  u32x4 kr = *reinterpret_cast<const u32x4*>(
-      k0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
-  u32x4 qr = *reinterpret_cast<const u32x4*>(
-      q0 + (uint32_t)((rv ? rt : 0) * kq_step) + 8 * rp);
-  kr = rv ? kr : z4;
-  qr = rv ? qr : z4;
+  u32x4 kr, qr;
   f32x4 gr[2];
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int e = tid + kBlock * rep;  // float4 slot: token e / 32
-    const int t = e >> 5;
-    gr[rep] = *reinterpret_cast<const f32x4*>(
-        g0 + (uint32_t)((t < T ? t : 0) * g_step) + 4 * (e & 31));
-  }
-  const float bl = beta[(tok0 + (tid < T ? tid : 0)) * d.Hv + h];
+  float bl;
   uint32_t vw[4];  // values of the tokens 4 g4 + e at this lane's columns
+  // the rows of the block of tokens tb .. tb + Tb - 1
+  auto load_rows = [&](int tb, int Tb) {
+    const bool rv = rt < Tb;
+    const int tr = tb + (rv ? rt : 0);
+    kr = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + 8 * rp);
+    qr = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + 8 * rp);
+    kr = rv ? kr : z4;
+    qr = rv ? qr : z4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g4 + e;
-    const uint32_t x = *reinterpret_cast<const uint32_t*>(
-        v0 + (uint32_t)((t < T ? t : 0) * vo_step) + c0);
-    vw[e] = t < T ? x : 0u;
-  }
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = tid + kBlock * rep;  // float4 slot: token e / 32
+      const int t = e >> 5;
+      gr[rep] = *reinterpret_cast<const f32x4*>(
+          g0 + (uint32_t)((tb + (t < Tb ? t : 0)) * g_step) + 4 * (e & 31));
+    }
+    bl = beta[(tok0 + tb + (tid < Tb ? tid : 0)) * d.Hv + h];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g4 + e;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(
+          v0 + (uint32_t)((tb + (t < Tb ? t : 0)) * vo_step) + c0);
+      vw[e] = t < Tb ? x : 0u;
+    }
+  };
+  const int T0 = MB ? (T < kTok ? T : kTok) : T;
+  load_rows(0, T0);
 
   const uint32_t soff = (uint32_t)(8 * g4 * kD + c0) * 4u;
   const auto srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -174,277 +185,299 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- stage the rows, the decays and beta; write the key and decay records
-  *reinterpret_cast<u32x4*>(&sh.k[rt][8 * rp]) = kr;
-  *reinterpret_cast<u32x4*>(&sh.q[rt][8 * rp]) = qr;
-  if (rv && h % d.group == 0) {
-    float kx[8];
-    widen8(kr, kx);
-    float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kD +
-                              (uint32_t)(rt * kq_step) + 8 * rp;
-    reinterpret_cast<float4*>(dst)[0] = make_float4(kx[0], kx[1], kx[2], kx[3]);
-    reinterpret_cast<float4*>(dst)[1] = make_float4(kx[4], kx[5], kx[6], kx[7]);
-  }
+  auto stage_rows = [&](int tb, int Tb) {
+    const bool rv = rt < Tb;
+    *reinterpret_cast<u32x4*>(&sh.k[rt][8 * rp]) = kr;
+    *reinterpret_cast<u32x4*>(&sh.q[rt][8 * rp]) = qr;
+    if (rv && h % d.group == 0) {
+      float kx[8];
+      widen8(kr, kx);
+      float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kD +
+                                (uint32_t)((tb + rt) * kq_step) + 8 * rp;
+      reinterpret_cast<float4*>(dst)[0] = make_float4(kx[0], kx[1], kx[2], kx[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(kx[4], kx[5], kx[6], kx[7]);
+    }
 #pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int e = tid + kBlock * rep;
-    const int t = e >> 5;
-    f32x4 a;
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = tid + kBlock * rep;
+      const int t = e >> 5;
+      f32x4 a;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = t < T ? __expf(gr[rep][i]) : 1.0f;
-    *reinterpret_cast<f32x4*>(&sh.a[t][4 * (e & 31)]) = a;
-    if (t < T)
-      *reinterpret_cast<f32x4*>(rec_a + (tok0 * d.Hv + h) * (size_t)kD +
-                                (uint32_t)(t * g_step) + 4 * (e & 31)) = a;
-  }
-  if (tid < kTok) sh.beta[tid] = tid < T ? bl : 0.f;
+      for (int i = 0; i < 4; ++i) a[i] = t < Tb ? __expf(gr[rep][i]) : 1.0f;
+      *reinterpret_cast<f32x4*>(&sh.a[t][4 * (e & 31)]) = a;
+      if (t < Tb)
+        *reinterpret_cast<f32x4*>(rec_a + (tok0 * d.Hv + h) * (size_t)kD +
+                                  (uint32_t)((tb + t) * g_step) + 4 * (e & 31)) = a;
+    }
+    if (tid < kTok) sh.beta[tid] = tid < Tb ? bl : 0.f;
+  };
+  stage_rows(0, T0);
   __syncthreads();
 
-  // ---- C_t per channel (threads 0..127) and the inverse norms (threads
-  // 128..255: eight per token, 16 entries each)
-  if (tid < kD) {
-    float cc = 1.0f;
-#pragma unroll
-    for (int t = 0; t < kTok; ++t) {
-      cc = cc * sh.a[t][tid];
-      sh.c[t][tid] = cc;
+  // the window in blocks of kTok tokens (one block unless MB), each from
+  // the held state: the replay of the blocks before it
+  for (int tb = 0;; tb += kTok) {
+    const int Tb = MB ? (T - tb < kTok ? T - tb : kTok) : T;
+    if (MB && tb > 0) {
+      load_rows(tb, Tb);
+      __syncthreads();  // every wave is done with the previous block
+      stage_rows(tb, Tb);
+      __syncthreads();
     }
-  } else {
-    const int u = tid - kD, t = u >> 3, pc = u & 7;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(&sh.k[t][16 * pc]);
-    const u32x4* qp = reinterpret_cast<const u32x4*>(&sh.q[t][16 * pc]);
-    float skk = 0.f, sqq = 0.f;
+    // ---- C_t per channel (threads 0..127) and the inverse norms (threads
+    // 128..255: eight per token, 16 entries each)
+    if (tid < kD) {
+      float cc = 1.0f;
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      float kx[8], qx[8];
-      widen8(kp[hlf], kx);
-      widen8(qp[hlf], qx);
+      for (int t = 0; t < kTok; ++t) {
+        cc = cc * sh.a[t][tid];
+        sh.c[t][tid] = cc;
+      }
+    } else {
+      const int u = tid - kD, t = u >> 3, pc = u & 7;
+      const u32x4* kp = reinterpret_cast<const u32x4*>(&sh.k[t][16 * pc]);
+      const u32x4* qp = reinterpret_cast<const u32x4*>(&sh.q[t][16 * pc]);
+      float skk = 0.f, sqq = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        skk = __builtin_fmaf(kx[i], kx[i], skk);
-        sqq = __builtin_fmaf(qx[i], qx[i], sqq);
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        float kx[8], qx[8];
+        widen8(kp[hlf], kx);
+        widen8(qp[hlf], qx);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          skk = __builtin_fmaf(kx[i], kx[i], skk);
+          sqq = __builtin_fmaf(qx[i], qx[i], sqq);
+        }
+      }
+      // eight consecutive lanes: two quad swaps and the half-row mirror
+      skk += dpp<0xB1>(skk);
+      sqq += dpp<0xB1>(sqq);
+      skk += dpp<0x4E>(skk);
+      sqq += dpp<0x4E>(sqq);
+      skk += dpp<0x141>(skk);
+      sqq += dpp<0x141>(sqq);
+      if (pc == 0) {
+        sh.rk[t] = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
+        sh.rq[t] = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
       }
     }
-    // eight consecutive lanes: two quad swaps and the half-row mirror
-    skk += dpp<0xB1>(skk);
-    sqq += dpp<0xB1>(sqq);
-    skk += dpp<0x4E>(skk);
-    sqq += dpp<0x4E>(sqq);
-    skk += dpp<0x141>(skk);
-    sqq += dpp<0x141>(sqq);
-    if (pc == 0) {
-      sh.rk[t] = l2norm ? __builtin_amdgcn_rsqf(skk + 1e-6f) : 1.0f;
-      sh.rq[t] = l2norm ? __builtin_amdgcn_rsqf(sqq + 1e-6f) : 1.0f;
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- L and P: thread (s, cq) runs E_ts over channels 8 cq .. 8 cq + 7 for
-  // t = s .. 15; the 16 channel slices of a row meet by a DPP row sum.  Wave
-  // w holds the rows s = 4w .. 4w + 3, so its loop starts at t = 4w (every
-  // entry before that is above the diagonal: P's are zeroed here, L's are
-  // never read)
-  {
-    const int s = tid >> 4, cq = tid & 15;
-    if (cq == 0)
-      for (int t = 0; t < 4 * w; ++t) sh.P[t * kLS + s] = 0.f;
-    float ksv[8];
-    widen8(*reinterpret_cast<const u32x4*>(&sh.k[s][8 * cq]), ksv);
-    float E[8];
+    // ---- L and P: thread (s, cq) runs E_ts over channels 8 cq .. 8 cq + 7 for
+    // t = s .. 15; the 16 channel slices of a row meet by a DPP row sum.  Wave
+    // w holds the rows s = 4w .. 4w + 3, so its loop starts at t = 4w (every
+    // entry before that is above the diagonal: P's are zeroed here, L's are
+    // never read)
+    {
+      const int s = tid >> 4, cq = tid & 15;
+      if (cq == 0)
+        for (int t = 0; t < 4 * w; ++t) sh.P[t * kLS + s] = 0.f;
+      float ksv[8];
+      widen8(*reinterpret_cast<const u32x4*>(&sh.k[s][8 * cq]), ksv);
+      float E[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) E[i] = 1.0f;
-    const float rks = sh.rk[s];
+      for (int i = 0; i < 8; ++i) E[i] = 1.0f;
+      const float rks = sh.rk[s];
 #pragma unroll 1
-    for (int t = 4 * w; t < kTok; ++t) {
-      float kt[8], qt[8];
-      widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][8 * cq]), kt);
-      widen8(*reinterpret_cast<const u32x4*>(&sh.q[t][8 * cq]), qt);
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq + 4]);
-      const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      float aL = 0.f, aP = 0.f;
+      for (int t = 4 * w; t < kTok; ++t) {
+        float kt[8], qt[8];
+        widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][8 * cq]), kt);
+        widen8(*reinterpret_cast<const u32x4*>(&sh.q[t][8 * cq]), qt);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq + 4]);
+        const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        float aL = 0.f, aP = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        E[i] = t > s ? E[i] * av[i] : E[i];
-        const float ke = ksv[i] * E[i];
-        aL = __builtin_fmaf(kt[i], ke, aL);
-        aP = __builtin_fmaf(qt[i], ke, aP);
-      }
-      aL = row_sum16(aL);
-      aP = row_sum16(aP);
-      if (cq == 0) {
-        const float lv = sh.beta[t] * sh.rk[t] * rks * aL;
-        sh.Lt[s * kLS + t] = t > s ? lv : 0.f;  // L[t][s]
-        const float pv = scale * sh.rq[t] * rks * aP;
-        sh.P[t * kLS + s] = t >= s ? pv : 0.f;
-      }
-    }
-  }
-  // ---- the decayed key and query rows of token n (entries 32 ks + 8 g4 ..
-  // + 7) split into bf16 hi + lo: the A fragments of (k . C) H and (q . C) H
-  // are the same for every wave, so wave w forms k-step w once for all
-  u32x4 af[4];
-  {
-    const int j0 = 32 * w + 8 * g4;
-    float kx[8], qx[8];
-    widen8(*reinterpret_cast<const u32x4*>(&sh.k[n][j0]), kx);
-    widen8(*reinterpret_cast<const u32x4*>(&sh.q[n][j0]), qx);
-    const f32x4 ca = *reinterpret_cast<const f32x4*>(&sh.c[n][j0]);
-    const f32x4 cb = *reinterpret_cast<const f32x4*>(&sh.c[n][j0 + 4]);
-    const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
-    uint32_t kh4[4], kl4[4], qh4[4], ql4[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      split2(kx[2 * p] * cv[2 * p], kx[2 * p + 1] * cv[2 * p + 1], kh4[p], kl4[p]);
-      split2(qx[2 * p] * cv[2 * p], qx[2 * p + 1] * cv[2 * p + 1], qh4[p], ql4[p]);
-    }
-    af[0] = u32x4{kh4[0], kh4[1], kh4[2], kh4[3]};
-    af[1] = u32x4{kl4[0], kl4[1], kl4[2], kl4[3]};
-    af[2] = u32x4{qh4[0], qh4[1], qh4[2], qh4[3]};
-    af[3] = u32x4{ql4[0], ql4[1], ql4[2], ql4[3]};
-  }
-  __syncthreads();  // L, P complete; a and C read for the last time
-#pragma unroll
-  for (int x = 0; x < 4; ++x) Af[w][x][l] = af[x];
-  __syncthreads();
-
-  // ---- T = (I + L)^-1 in each wave's tile (lane n < 16 of group 0 solves
-  // column n by right-looking substitution)
-  if (l < kTok) {
-    float acc[kTok];
-#pragma unroll
-    for (int r = 0; r < kTok; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int x = 0; x < kTok; ++x) {
-      const float tx = x == n ? 1.f : (x < n ? 0.f : -acc[x]);
-      W.Ts[x * kLS + n] = tx;
-#pragma unroll
-      for (int r = x + 1; r < kTok; ++r)
-        acc[r] = __builtin_fmaf(sh.Lt[x * kLS + r], tx, acc[r]);
-    }
-  }
-  wave_lds_sync();
-  const f32x4 TA = *reinterpret_cast<const f32x4*>(&W.Ts[n * kLS + 4 * g4]);
-  const f32x4 PA = *reinterpret_cast<const f32x4*>(&sh.P[n * kLS + 4 * g4]);
-
-  // ---- (k . C) H and (q . C) H: per k-step, the decayed rows of token n
-  // (entries 32 ks + 8 g4 .. + 7) and the state split into bf16 hi + lo
-  f32x4 KH[2], QH[2];
-#pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    KH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-    QH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    const u32x4 KAh = Af[ks][0][l], KAl = Af[ks][1][l];
-    const u32x4 QAh = Af[ks][2][l], QAl = Af[ks][3][l];
-    uint32_t h0[4], lo0[4], h1[4], lo1[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      split2(s2[ks][2 * p][0], s2[ks][2 * p + 1][0], h0[p], lo0[p]);
-      split2(s2[ks][2 * p][1], s2[ks][2 * p + 1][1], h1[p], lo1[p]);
-    }
-    const u32x4 H0 = {h0[0], h0[1], h0[2], h0[3]};
-    const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
-    const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
-    const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
-    KH[0] = mma_bf16(KAh, H0, KH[0]);
-    KH[1] = mma_bf16(KAh, H1, KH[1]);
-    QH[0] = mma_bf16(QAh, H0, QH[0]);
-    QH[1] = mma_bf16(QAh, H1, QH[1]);
-    KH[0] = mma_bf16(KAh, L0, KH[0]);
-    KH[1] = mma_bf16(KAh, L1, KH[1]);
-    QH[0] = mma_bf16(QAh, L0, QH[0]);
-    QH[1] = mma_bf16(QAh, L1, QH[1]);
-    KH[0] = mma_bf16(KAl, H0, KH[0]);
-    KH[1] = mma_bf16(KAl, H1, KH[1]);
-    QH[0] = mma_bf16(QAl, H0, QH[0]);
-    QH[1] = mma_bf16(QAl, H1, QH[1]);
-  }
-
-  // ---- X, U = T X, O = diag(scale rq) (q . C) H + P U, ut = U rk
-  f32x4 X[2];
-  float rke[4], sqe[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g4 + e;
-    const float bt = sh.beta[t];
-    rke[e] = sh.rk[t];
-    sqe[e] = scale * sh.rq[t];
-    const float xb = bt * rke[e];
-    const float x0 = __builtin_fmaf(-xb, KH[0][e], bt * lo_f(vw[e]));
-    const float x1 = __builtin_fmaf(-xb, KH[1][e], bt * hi_f(vw[e]));
-    X[0][e] = t < T ? x0 : 0.f;
-    X[1][e] = t < T ? x1 : 0.f;
-  }
-  f32x4 U[2], O[2];
-#pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    U[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) U[cs] = mma_f32(TA[e], X[cs][e], U[cs]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[cs][e] = sqe[e] * QH[cs][e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
-  }
-  float* __restrict__ o0 = o + (tok0 * d.Hv + h) * (size_t)kD;
-  float* __restrict__ u0 = rec_u + (tok0 * d.Hv + h) * (size_t)kD;
-  float ut[2][4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g4 + e;
-    ut[0][e] = U[0][e] * rke[e];
-    ut[1][e] = U[1][e] * rke[e];
-    if (t < T) {
-      const uint32_t off = (uint32_t)(t * vo_step) + c0;
-      // outputs are not read again by this path: nontemporal stores
-      __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
-                                  reinterpret_cast<f32x2*>(o0 + off));
-      *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
-    }
-  }
-
-  // ---- debug states: the records replayed token by token on the start
-  // state with commit's operations (decay multiply, then the fma)
-  if constexpr (DBG) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
-      W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
-    }
-    wave_lds_sync();
-#pragma unroll 1
-    for (int t = 0; t < T; ++t) {
-      const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
-      float* __restrict__ dp = dbg + ((tok0 + t) * d.Hv + h) * (size_t)kD * kD;
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const int j0 = 32 * ks + 8 * g4;
-        float kx[8];
-        widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][j0]), kx);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = sh.a[t][j0 + e];
-          s2[ks][e][0] = s2[ks][e][0] * a;
-          s2[ks][e][1] = s2[ks][e][1] * a;
-          s2[ks][e][0] = __builtin_fmaf(ua, kx[e], s2[ks][e][0]);
-          s2[ks][e][1] = __builtin_fmaf(ub, kx[e], s2[ks][e][1]);
-          *reinterpret_cast<f32x2*>(dp + (size_t)(j0 + e) * kD + c0) = s2[ks][e];
+        for (int i = 0; i < 8; ++i) {
+          E[i] = t > s ? E[i] * av[i] : E[i];
+          const float ke = ksv[i] * E[i];
+          aL = __builtin_fmaf(kt[i], ke, aL);
+          aP = __builtin_fmaf(qt[i], ke, aP);
+        }
+        aL = row_sum16(aL);
+        aP = row_sum16(aP);
+        if (cq == 0) {
+          const float lv = sh.beta[t] * sh.rk[t] * rks * aL;
+          sh.Lt[s * kLS + t] = t > s ? lv : 0.f;  // L[t][s]
+          const float pv = scale * sh.rq[t] * rks * aP;
+          sh.P[t * kLS + s] = t >= s ? pv : 0.f;
         }
       }
     }
+    // ---- the decayed key and query rows of token n (entries 32 ks + 8 g4 ..
+    // + 7) split into bf16 hi + lo: the A fragments of (k . C) H and (q . C) H
+    // are the same for every wave, so wave w forms k-step w once for all
+    u32x4 af[4];
+    {
+      const int j0 = 32 * w + 8 * g4;
+      float kx[8], qx[8];
+      widen8(*reinterpret_cast<const u32x4*>(&sh.k[n][j0]), kx);
+      widen8(*reinterpret_cast<const u32x4*>(&sh.q[n][j0]), qx);
+      const f32x4 ca = *reinterpret_cast<const f32x4*>(&sh.c[n][j0]);
+      const f32x4 cb = *reinterpret_cast<const f32x4*>(&sh.c[n][j0 + 4]);
+      const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
+      uint32_t kh4[4], kl4[4], qh4[4], ql4[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        split2(kx[2 * p] * cv[2 * p], kx[2 * p + 1] * cv[2 * p + 1], kh4[p], kl4[p]);
+        split2(qx[2 * p] * cv[2 * p], qx[2 * p + 1] * cv[2 * p + 1], qh4[p], ql4[p]);
+      }
+      af[0] = u32x4{kh4[0], kh4[1], kh4[2], kh4[3]};
+      af[1] = u32x4{kl4[0], kl4[1], kl4[2], kl4[3]};
+      af[2] = u32x4{qh4[0], qh4[1], qh4[2], qh4[3]};
+      af[3] = u32x4{ql4[0], ql4[1], ql4[2], ql4[3]};
+    }
+    __syncthreads();  // L, P complete; a and C read for the last time
+#pragma unroll
+    for (int x = 0; x < 4; ++x) Af[w][x][l] = af[x];
+    __syncthreads();
+
+    // ---- T = (I + L)^-1 in each wave's tile (lane n < 16 of group 0 solves
+    // column n by right-looking substitution)
+    if (l < kTok) {
+      float acc[kTok];
+#pragma unroll
+      for (int r = 0; r < kTok; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int x = 0; x < kTok; ++x) {
+        const float tx = x == n ? 1.f : (x < n ? 0.f : -acc[x]);
+        W.Ts[x * kLS + n] = tx;
+#pragma unroll
+        for (int r = x + 1; r < kTok; ++r)
+          acc[r] = __builtin_fmaf(sh.Lt[x * kLS + r], tx, acc[r]);
+      }
+    }
+    wave_lds_sync();
+    const f32x4 TA = *reinterpret_cast<const f32x4*>(&W.Ts[n * kLS + 4 * g4]);
+    const f32x4 PA = *reinterpret_cast<const f32x4*>(&sh.P[n * kLS + 4 * g4]);
+
+    // ---- (k . C) H and (q . C) H: per k-step, the decayed rows of token n
+    // (entries 32 ks + 8 g4 .. + 7) and the state split into bf16 hi + lo
+    f32x4 KH[2], QH[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      KH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      QH[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const u32x4 KAh = Af[ks][0][l], KAl = Af[ks][1][l];
+      const u32x4 QAh = Af[ks][2][l], QAl = Af[ks][3][l];
+      uint32_t h0[4], lo0[4], h1[4], lo1[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        split2(s2[ks][2 * p][0], s2[ks][2 * p + 1][0], h0[p], lo0[p]);
+        split2(s2[ks][2 * p][1], s2[ks][2 * p + 1][1], h1[p], lo1[p]);
+      }
+      const u32x4 H0 = {h0[0], h0[1], h0[2], h0[3]};
+      const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
+      const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
+      const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
+      KH[0] = mma_bf16(KAh, H0, KH[0]);
+      KH[1] = mma_bf16(KAh, H1, KH[1]);
+      QH[0] = mma_bf16(QAh, H0, QH[0]);
+      QH[1] = mma_bf16(QAh, H1, QH[1]);
+      KH[0] = mma_bf16(KAh, L0, KH[0]);
+      KH[1] = mma_bf16(KAh, L1, KH[1]);
+      QH[0] = mma_bf16(QAh, L0, QH[0]);
+      QH[1] = mma_bf16(QAh, L1, QH[1]);
+      KH[0] = mma_bf16(KAl, H0, KH[0]);
+      KH[1] = mma_bf16(KAl, H1, KH[1]);
+      QH[0] = mma_bf16(QAl, H0, QH[0]);
+      QH[1] = mma_bf16(QAl, H1, QH[1]);
+    }
+
+    // ---- X, U = T X, O = diag(scale rq) (q . C) H + P U, ut = U rk
+    f32x4 X[2];
+    float rke[4], sqe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g4 + e;
+      const float bt = sh.beta[t];
+      rke[e] = sh.rk[t];
+      sqe[e] = scale * sh.rq[t];
+      const float xb = bt * rke[e];
+      const float x0 = __builtin_fmaf(-xb, KH[0][e], bt * lo_f(vw[e]));
+      const float x1 = __builtin_fmaf(-xb, KH[1][e], bt * hi_f(vw[e]));
+      X[0][e] = t < Tb ? x0 : 0.f;
+      X[1][e] = t < Tb ? x1 : 0.f;
+    }
+    f32x4 U[2], O[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      U[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[cs] = mma_f32(TA[e], X[cs][e], U[cs]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[cs][e] = sqe[e] * QH[cs][e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
+    }
+    float* __restrict__ o0 = o + ((tok0 + tb) * d.Hv + h) * (size_t)kD;
+    float* __restrict__ u0 = rec_u + ((tok0 + tb) * d.Hv + h) * (size_t)kD;
+    float ut[2][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g4 + e;
+      ut[0][e] = U[0][e] * rke[e];
+      ut[1][e] = U[1][e] * rke[e];
+      if (t < Tb) {
+        const uint32_t off = (uint32_t)(t * vo_step) + c0;
+        // outputs are not read again by this path: nontemporal stores
+        __builtin_nontemporal_store(f32x2{O[0][e], O[1][e]},
+                                    reinterpret_cast<f32x2*>(o0 + off));
+        *reinterpret_cast<float2*>(u0 + off) = make_float2(ut[0][e], ut[1][e]);
+      }
+    }
+
+    // ---- debug states: the records replayed token by token on the start
+    // state with commit's operations (decay multiply, then the fma); a window
+    // of several blocks replays each block but the last on the held state,
+    // which the next block starts from
+    const bool more = MB && tb + kTok < T;
+    if (DBG || more) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
+        W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
+      }
+      wave_lds_sync();
+#pragma unroll 1
+      for (int t = 0; t < Tb; ++t) {
+        const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
+        [[maybe_unused]] float* __restrict__ dp =
+            dbg + ((tok0 + tb + t) * d.Hv + h) * (size_t)kD * kD;
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          const int j0 = 32 * ks + 8 * g4;
+          float kx[8];
+          widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][j0]), kx);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float a = sh.a[t][j0 + e];
+            s2[ks][e][0] = s2[ks][e][0] * a;
+            s2[ks][e][1] = s2[ks][e][1] * a;
+            s2[ks][e][0] = __builtin_fmaf(ua, kx[e], s2[ks][e][0]);
+            s2[ks][e][1] = __builtin_fmaf(ub, kx[e], s2[ks][e][1]);
+            if constexpr (DBG)
+              *reinterpret_cast<f32x2*>(dp + (size_t)(j0 + e) * kD + c0) = s2[ks][e];
+          }
+        }
+      }
+    }
+    if (!more) break;
+
   }
 }
 
-template <bool DBG>
+template <bool DBG, bool MB>
 static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
                            const void* q, const void* k, const void* v,
                            const float* beta, const float* g, const float* S,
                            float* o, float* rk, float* ru, float* ra,
                            float* dbg, float scale, int l2, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv;
-  return launch(mkda_kernel<DBG>, dim3(blocks), dim3(kBlock), st,
+  return launch(mkda_kernel<DBG, MB>, dim3(blocks), dim3(kBlock), st,
                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                 beta, g, S, o, rk, ru, ra, dbg, w, tl, scale, l2);
 }
@@ -456,7 +489,7 @@ bool mkda_eligible(const gdn_dims& d, int in_dtype, const void* q,
                    const float* S, const float* o, const float* dbg) {
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
   return in_dtype == GDN_BF16 && d.d_k == wk::kD && d.d_v == wk::kD &&
-         d.t_max <= wk::kTok && al(q, 16) && al(k, 16) && al(v, 4) &&
+         d.t_max <= GDN_MAX_T && al(q, 16) && al(k, 16) && al(v, 4) &&
          al(g, 16) && al(S, 8) && al(o, 8) && (dbg == nullptr || al(dbg, 8));
 }
 
@@ -465,10 +498,15 @@ hipError_t launch_mkda(const WinDims& w, const LaneTable& tl, const void* q,
                        const float* g, const float* S, float* o, float* rk,
                        float* ru, float* ra, float* dbg, float scale, int l2,
                        hipStream_t st) {
-  return dbg ? wk::launch_t<true>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra,
-                                  dbg, scale, l2, st)
-             : wk::launch_t<false>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra,
-                                   dbg, scale, l2, st);
+  if (w.T > wk::kTok)  // windows of several blocks
+    return dbg ? wk::launch_t<true, true>(w, tl, q, k, v, beta, g, S, o, rk,
+                                          ru, ra, dbg, scale, l2, st)
+               : wk::launch_t<false, true>(w, tl, q, k, v, beta, g, S, o, rk,
+                                           ru, ra, dbg, scale, l2, st);
+  return dbg ? wk::launch_t<true, false>(w, tl, q, k, v, beta, g, S, o, rk, ru,
+                                         ra, dbg, scale, l2, st)
+             : wk::launch_t<false, false>(w, tl, q, k, v, beta, g, S, o, rk, ru,
+                                          ra, dbg, scale, l2, st);
 }
 
 }  // namespace gdn

@@ -229,10 +229,12 @@ def test_tree_emits_the_rule_on_the_replayed_states():
     assert e_u <= BOUND_U and e_o <= BOUND_O
 
 
-def test_kda_window_emits_the_rule_on_the_replayed_states():
-    """KDA: S'_t = S~_{t-1} diag(alpha_t), u_t = beta_t (v_t - S'_t khat_t)."""
-    shape = gs.WindowShape(1, 4, 4, 2, 128, 128, 16)
-    key, w, S0 = _window("kda", shape)
+@pytest.mark.parametrize("T", [16, 48])
+def test_kda_window_emits_the_rule_on_the_replayed_states(T):
+    """KDA: S'_t = S~_{t-1} diag(alpha_t), u_t = beta_t (v_t - S'_t khat_t);
+    at T = 48 in three blocks."""
+    shape = gs.WindowShape(1, 4, 4, 2, 128, 128, T)
+    key, w, S0 = _window("kda" if T == 16 else "kda_%d" % T, shape)
     gk = gs.kda_gates(shape, key)
     gk[:, :, 5, :, ::7] = -np.inf      # forgotten channels
     dims = gdn.Dims.of(*shape.__dict__.values())

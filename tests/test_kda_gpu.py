@@ -47,9 +47,13 @@ CASES = [
     ("f32_dv200", 1, 2, 3, 3, 200, 7, False, None),
     ("bf16_channel_forgetting", 1, 2, 4, 2, 64, 12, True, "zero"),
     ("bf16_strong_decay", 1, 2, 4, 2, 128, 16, True, "strong"),
-    # the matrix-core KDA verify (bf16, d_v = 128, t_max <= 16) with zero
+    # the matrix-core KDA verify (bf16, d_v = 128, one block) with zero
     # decays on some channels
     ("bf16_channel_forgetting_d128", 1, 2, 4, 2, 128, 12, True, "zero"),
+    # windows of 40 and 64 tokens: blocks of 16, each from the replay of
+    # the blocks before it
+    ("bf16_t40_blocks_forgetting", 1, 3, 2, 1, 128, 40, True, "zero"),
+    ("bf16_t64_blocks_strong", 1, 2, 2, 2, 128, 64, True, "strong"),
 ]
 
 
