@@ -50,12 +50,15 @@ CASES = [
     ("d128_t40_long_window", 1, 3, 2, 1, 128, 128, 40, True, 3, False),
     ("d128_t64_blocks_dbg", 1, 2, 2, 1, 128, 128, 64, True, 3, True),
     ("d128_t17_blocks", 1, 4, 2, 1, 128, 128, 17, True, 4, True),
+    # GDN_FLAG_TOKENWISE on both paths at a block-form shape
+    ("d128_tokenwise", 1, 4, 2, 1, 128, 128, 16, True, 4, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_fused_equals_commit_then_verify(case):
     name, NL, N, Hv, Hk, dk, dv, T, bf16, rounds, dbg = case
+    tw = name.endswith("tokenwise")
     say("case", name)
     shape = gs.WindowShape(NL, N, Hv, Hk, dk, dv, T)
     key = (200, zlib.crc32(name.encode()) % 1000)
@@ -87,10 +90,12 @@ def test_fused_equals_commit_then_verify(case):
         rn.zero_()
         # two calls
         gdn.commit(dims, m_prev, t_prev, ap, S_a)
-        gdn.verify(dims, w.t_lane, q, k, v, beta, g, S_a, o_a, an, d_a)
+        gdn.verify(dims, w.t_lane, q, k, v, beta, g, S_a, o_a, an, d_a,
+                   tokenwise=tw)
         # one fused call
         gdn.commit_verify(dims, m_prev, t_prev, None if r == 0 else rp,
-                          w.t_lane, q, k, v, beta, g, S_b, o_b, rn, d_b)
+                          w.t_lane, q, k, v, beta, g, S_b, o_b, rn, d_b,
+                          tokenwise=tw)
         torch.cuda.synchronize()
         assert torch.equal(S_a, S_b), ("state", r)
         assert torch.equal(torch.nan_to_num(o_a, 7.0),
