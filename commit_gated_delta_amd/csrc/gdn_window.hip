@@ -644,6 +644,7 @@ static int verify_setup(const char* fn, const gdn_dims* dims,
   a.dbg = dbg_states;
   a.scale = scale;
   a.l2 = (flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+  a.f32 = in_dtype == GDN_F32 ? 1 : 0;
   return GDN_OK;
 }
 

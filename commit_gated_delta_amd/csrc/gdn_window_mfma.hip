@@ -1,9 +1,10 @@
 // gdn_window_mfma.hip -- speculative-window verify, draft-tree verify and
-// the fused commit + verify on the gfx950 matrix cores, for bf16 inputs,
-// d_k = 128 and d_v a multiple of 128: windows of at most 16 tokens (the
+// the fused commit + verify on the gfx950 matrix cores, for d_k = 128 and
+// d_v a multiple of 128, bf16 or f32 inputs (f32 key / query rows enter the
+// products as three bf16 parts, see Frag): windows of at most 16 tokens (the
 // shapes of the speculative-decoding section of the NInfer technical review,
 // blog.123qwe.co.kr post 4624) as one block, longer windows (up to 64
-// tokens) in blocks of 16, trees of at most 16 nodes.  Other shapes, and
+// tokens) in blocks of 16, bf16 trees of at most 16 nodes.  Other shapes, and
 // calls with GDN_FLAG_TOKENWISE, take gdn_window.hip.
 //
 // The window is one chunk of the block (WY/UT) form of the rule: Yang et
@@ -86,14 +87,63 @@ struct Stage {
   float u[kTok][kCB];  // ut of this workgroup's columns
   f32x2 sc[kTok + 1];  // (phi, c); slot kTok: discarded writes
 };
-// The window's raw key / query rows and gates, staged once per workgroup
-// (every wave reads its A fragments and per-token gates from here).
+// The window's raw key / query / value rows (bf16 or f32, as given) and
+// gates, staged once per workgroup (every wave reads its A fragments and
+// per-token gates from here).
+template <typename In>
 struct RowLds {
-  __attribute__((aligned(16))) uint16_t k[kTok][kDK];
-  __attribute__((aligned(16))) uint16_t q[kTok][kDK];
-  __attribute__((aligned(16))) uint16_t v[kTok][kCB];  // this block's columns
+  __attribute__((aligned(16))) In k[kTok][kDK];
+  __attribute__((aligned(16))) In q[kTok][kDK];
+  __attribute__((aligned(16))) In v[kTok][kCB];  // this block's columns
   float g[kTok + 1], b[kTok + 1];  // slot kTok: discarded writes
 };
+// Eight consecutive entries of a staged row, widened to f32 (exact).
+__device__ __forceinline__ void row8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = lo_f(w[i]);
+    x[2 * i + 1] = hi_f(w[i]);
+  }
+}
+__device__ __forceinline__ void row8(const float* p, float (&x)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+// The bf16 A fragment of eight staged entries: the raw words for bf16 rows;
+// for f32 rows three parts, x = h + m + l + O(2^-25 |x|) (each bf16,
+// rounded to nearest even): a product of two f32 rows keeps f32 accuracy
+// only with all three (with two, a dot product of 128 terms that cancel
+// loses about four bits of its 16).
+struct Frag {
+  u32x4 h, m, l;
+};
+__device__ __forceinline__ Frag frag8(const uint16_t* p) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return Frag{*reinterpret_cast<const u32x4*>(p), z, z};
+}
+__device__ __forceinline__ Frag frag8(const float* p) {
+  float x[8];
+  row8(p, x);
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t r;
+    split2(x[2 * i], x[2 * i + 1], h[i], r);
+    m[i] = r;
+    const float ra = x[2 * i] - lo_f(h[i]) - lo_f(r);
+    const float rb = x[2 * i + 1] - hi_f(h[i]) - hi_f(r);
+    const f32x2 y = {ra, rb};
+    l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+  }
+  return Frag{u32x4{h[0], h[1], h[2], h[3]}, u32x4{m[0], m[1], m[2], m[3]},
+              u32x4{l[0], l[1], l[2], l[3]}};
+}
 // A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
 struct WaveLds {
   __attribute__((aligned(16))) float Lt[kTok * kLS];
@@ -108,11 +158,13 @@ struct WaveLds {
 // ancestor (or, for P, t itself), dec(t, s) is the decay along the path from
 // s to t, and the scale sequence continues the parent's scale.  A parent
 // precedes its children, so L stays strictly lower triangular.
-template <bool REPLAY, bool DBG, bool TREE, bool MB>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG || (MB && REPLAY) ? 2 : 3)))
+template <bool REPLAY, bool DBG, bool TREE, bool MB, bool F32>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG || F32 || (MB && REPLAY) ? 2 : 3)))
 void mverify_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
+    const std::conditional_t<F32, float, uint16_t>* __restrict__ k,
+    const std::conditional_t<F32, float, uint16_t>* __restrict__ v,
+    const float* __restrict__ beta,
     const float* __restrict__ g, float* S, float* __restrict__ o,
     float* __restrict__ rec_k, float* __restrict__ rec_u,
     float2* __restrict__ rec_scale, float* __restrict__ dbg, WinDims d,
@@ -120,8 +172,12 @@ void mverify_kernel(
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
   static_assert(!(TREE && MB), "draft trees have at most one block");
+  static_assert(!(TREE && F32), "draft trees take bf16 rows");
+  using In = std::conditional_t<F32, float, uint16_t>;
+  constexpr int kEl = 16 / (int)sizeof(In);  // entries per 16-byte piece
+  constexpr int kPc = F32 ? 2 : 1;           // pieces per thread and row
   __shared__ WaveLds wl[kWaves];
-  __shared__ RowLds rows;
+  __shared__ RowLds<In> rows;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
 
   const int nc = d.dv / kCB;
@@ -158,9 +214,9 @@ void mverify_kernel(
   const size_t tok0 = ll * d.T;              // token 0 of this lane-layer
   const size_t kq_step = (size_t)d.Hk * kDK;  // per token: q, k, key records
   const size_t vo_step = (size_t)d.Hv * dv;   // per token: v, o, ut records
-  const uint16_t* __restrict__ k0 = k + (tok0 * d.Hk + kh) * kDK;
-  const uint16_t* __restrict__ q0 = q + (tok0 * d.Hk + kh) * kDK;
-  const uint16_t* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)dv;
+  const In* __restrict__ k0 = k + (tok0 * d.Hk + kh) * kDK;
+  const In* __restrict__ q0 = q + (tok0 * d.Hk + kh) * kDK;
+  const In* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)dv;
   const size_t gh0 = tok0 * d.Hv + h;  // gate index of token 0 (step Hv)
   float* const Sh = S + (ll * d.Hv + h) * (size_t)kDK * dv;
   // The head's state through a buffer resource: row 32 ks + 8 g4 + e is the
@@ -192,31 +248,43 @@ void mverify_kernel(
   // replaced by zeros.
   const int rt = tid >> 4, rp = tid & 15;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  u32x4 kr, qr, vr;
+  u32x4 kr[kPc], qr[kPc], vr[kPc];
   float gl, bl;
-  // the rows of the block of tokens tb .. tb + Tb - 1: thread (rt, rp) one
-  // 16-byte piece of key row rt, of query row rt and of value row rt (this
-  // workgroup's columns), threads 0..15 the gates of token tid; tokens at or
-  // past Tb read the block's first token and are replaced by zeros
+  // the rows of the block of tokens tb .. tb + Tb - 1: thread (rt, rp) the
+  // 16-byte pieces rp (and rp + 16 for f32 rows) of key row rt, of query row
+  // rt and of value row rt (this workgroup's columns), threads 0..15 the
+  // gates of token tid; tokens at or past Tb read the block's first token
+  // and are replaced by zeros
   auto load_rows = [&](int tb, int Tb) {
     const bool rv = rt < Tb;
     const int tr = tb + (rv ? rt : 0);
-    kr = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + 8 * rp);
-    qr = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + 8 * rp);
-    kr = rv ? kr : z4;
-    qr = rv ? qr : z4;
+#pragma unroll
+    for (int p = 0; p < kPc; ++p) {
+      const int pe = kEl * (rp + 16 * p);
+      kr[p] = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + pe);
+      qr[p] = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + pe);
+      kr[p] = rv ? kr[p] : z4;
+      qr[p] = rv ? qr[p] : z4;
+    }
     const int tg = tb + (tid < Tb ? tid : 0);
     gl = g[gh0 + (size_t)tg * d.Hv];
     bl = beta[gh0 + (size_t)tg * d.Hv];
-    vr = *reinterpret_cast<const u32x4*>(
-        v0 + (uint32_t)(tr * vo_step) + kCB * cb + 8 * rp);
-    vr = rv ? vr : z4;
+#pragma unroll
+    for (int p = 0; p < kPc; ++p) {
+      vr[p] = *reinterpret_cast<const u32x4*>(
+          v0 + (uint32_t)(tr * vo_step) + kCB * cb + kEl * (rp + 16 * p));
+      vr[p] = rv ? vr[p] : z4;
+    }
   };
   auto stage_rows = [&](int tb, int Tb) {
     const bool rv = rt < Tb;
-    *reinterpret_cast<u32x4*>(&rows.k[rt][8 * rp]) = kr;
-    *reinterpret_cast<u32x4*>(&rows.q[rt][8 * rp]) = qr;
-    *reinterpret_cast<u32x4*>(&rows.v[rt][8 * rp]) = vr;
+#pragma unroll
+    for (int p = 0; p < kPc; ++p) {
+      const int pe = kEl * (rp + 16 * p);
+      *reinterpret_cast<u32x4*>(&rows.k[rt][pe]) = kr[p];
+      *reinterpret_cast<u32x4*>(&rows.q[rt][pe]) = qr[p];
+      *reinterpret_cast<u32x4*>(&rows.v[rt][pe]) = vr[p];
+    }
     // every thread stores (threads past kTok into the discarded slot): a
     // store under a branch lets the compiler sink the gate loads into it,
     // behind the state requests, and wait for the whole state there
@@ -224,26 +292,29 @@ void mverify_kernel(
     rows.g[gs] = tid < Tb ? gl : 0.f;
     rows.b[gs] = tid < Tb ? bl : 0.f;
     // the key record rows (raw rows as f32): thread (rt, rp) writes its
-    // piece; done here so that the pieces are dead past the staging
+    // pieces; done here so that the pieces are dead past the staging
     if (cb == 0 && h % d.group == 0 && rv) {
       float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kDK +
-                                (uint32_t)((tb + rt) * kq_step) + 8 * rp;
-      reinterpret_cast<float4*>(dst)[0] =
-          make_float4(lo_f(kr[0]), hi_f(kr[0]), lo_f(kr[1]), hi_f(kr[1]));
-      reinterpret_cast<float4*>(dst)[1] =
-          make_float4(lo_f(kr[2]), hi_f(kr[2]), lo_f(kr[3]), hi_f(kr[3]));
+                                (uint32_t)((tb + rt) * kq_step);
+      if constexpr (F32) {
+#pragma unroll
+        for (int p = 0; p < kPc; ++p)
+          *reinterpret_cast<u32x4*>(dst + kEl * (rp + 16 * p)) = kr[p];
+      } else {
+        const u32x4 kw = kr[0];
+        reinterpret_cast<float4*>(dst + 8 * rp)[0] =
+            make_float4(lo_f(kw[0]), hi_f(kw[0]), lo_f(kw[1]), hi_f(kw[1]));
+        reinterpret_cast<float4*>(dst + 8 * rp)[1] =
+            make_float4(lo_f(kw[2]), hi_f(kw[2]), lo_f(kw[3]), hi_f(kw[3]));
+      }
     }
   };
   // the first block's rows are requested before the state, so that
   // everything but the state products overlaps the state's latency
   const int T0 = MB ? (T < kTok ? T : kTok) : T;
   load_rows(0, T0);
-  auto frag_k = [&](int ks) {
-    return *reinterpret_cast<const u32x4*>(&rows.k[n][32 * ks + 8 * g4]);
-  };
-  auto frag_q = [&](int ks) {
-    return *reinterpret_cast<const u32x4*>(&rows.q[n][32 * ks + 8 * g4]);
-  };
+  auto frag_k = [&](int ks) { return frag8(&rows.k[n][32 * ks + 8 * g4]); };
+  auto frag_q = [&](int ks) { return frag8(&rows.q[n][32 * ks + 8 * g4]); };
 
   // ---- the state: rows 32 ks + 8 g4 + e, columns c0 and c0 + 1
   f32x2 s2[kKS][8];
@@ -375,7 +446,7 @@ void mverify_kernel(
       __syncthreads();
     }
     const float gt = rows.g[n], bt = rows.b[n];
-    u32x4 Kf[kKS], Qf[kKS];
+    Frag Kf[kKS], Qf[kKS];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       Kf[ks] = frag_k(ks);
@@ -385,15 +456,29 @@ void mverify_kernel(
     // ---- inverse norms of token n (sums over the lane's row pieces, then
     // over the four groups)
     float skk = 0.f, sqq = 0.f;
+    if constexpr (F32) {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const u32x4 kw = Kf[ks], qw = Qf[ks];
+      for (int ks = 0; ks < kKS; ++ks) {
+        float kx[8], qx[8];
+        row8(&rows.k[n][32 * ks + 8 * g4], kx);
+        row8(&rows.q[n][32 * ks + 8 * g4], qx);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        skk = __builtin_fmaf(lo_f(kw[p]), lo_f(kw[p]), skk);
-        skk = __builtin_fmaf(hi_f(kw[p]), hi_f(kw[p]), skk);
-        sqq = __builtin_fmaf(lo_f(qw[p]), lo_f(qw[p]), sqq);
-        sqq = __builtin_fmaf(hi_f(qw[p]), hi_f(qw[p]), sqq);
+        for (int i = 0; i < 8; ++i) {
+          skk = __builtin_fmaf(kx[i], kx[i], skk);
+          sqq = __builtin_fmaf(qx[i], qx[i], sqq);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const u32x4 kw = Kf[ks].h, qw = Qf[ks].h;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          skk = __builtin_fmaf(lo_f(kw[p]), lo_f(kw[p]), skk);
+          skk = __builtin_fmaf(hi_f(kw[p]), hi_f(kw[p]), skk);
+          sqq = __builtin_fmaf(lo_f(qw[p]), lo_f(qw[p]), sqq);
+          sqq = __builtin_fmaf(hi_f(qw[p]), hi_f(qw[p]), sqq);
+        }
       }
     }
     skk += __shfl_xor(skk, 16, kWave);
@@ -410,8 +495,20 @@ void mverify_kernel(
     f32x4 KK = {0.f, 0.f, 0.f, 0.f}, KQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      KK = mma_bf16(Kf[ks], Kf[ks], KK);
-      KQ = mma_bf16(Kf[ks], Qf[ks], KQ);
+      KK = mma_bf16(Kf[ks].h, Kf[ks].h, KK);
+      KQ = mma_bf16(Kf[ks].h, Qf[ks].h, KQ);
+      if constexpr (F32) {  // the part products of order at most 2^-16
+        KK = mma_bf16(Kf[ks].h, Kf[ks].m, KK);
+        KK = mma_bf16(Kf[ks].m, Kf[ks].h, KK);
+        KK = mma_bf16(Kf[ks].h, Kf[ks].l, KK);
+        KK = mma_bf16(Kf[ks].m, Kf[ks].m, KK);
+        KK = mma_bf16(Kf[ks].l, Kf[ks].h, KK);
+        KQ = mma_bf16(Kf[ks].h, Qf[ks].m, KQ);
+        KQ = mma_bf16(Kf[ks].m, Qf[ks].h, KQ);
+        KQ = mma_bf16(Kf[ks].h, Qf[ks].l, KQ);
+        KQ = mma_bf16(Kf[ks].m, Qf[ks].m, KQ);
+        KQ = mma_bf16(Kf[ks].l, Qf[ks].h, KQ);
+      }
     }
 
     // ---- gates of token n, within each 16-lane group: segmented sums Gs
@@ -596,15 +693,29 @@ void mverify_kernel(
       const u32x4 L0 = {lo0[0], lo0[1], lo0[2], lo0[3]};
       const u32x4 H1 = {h1[0], h1[1], h1[2], h1[3]};
       const u32x4 L1 = {lo1[0], lo1[1], lo1[2], lo1[3]};
-      const u32x4 kf = frag_k(ks), qf = frag_q(ks);
-      KH[0] = mma_bf16(kf, H0, KH[0]);
-      KH[1] = mma_bf16(kf, H1, KH[1]);
-      QH[0] = mma_bf16(qf, H0, QH[0]);
-      QH[1] = mma_bf16(qf, H1, QH[1]);
-      KH[0] = mma_bf16(kf, L0, KH[0]);
-      KH[1] = mma_bf16(kf, L1, KH[1]);
-      QH[0] = mma_bf16(qf, L0, QH[0]);
-      QH[1] = mma_bf16(qf, L1, QH[1]);
+      const Frag kf = frag_k(ks), qf = frag_q(ks);
+      KH[0] = mma_bf16(kf.h, H0, KH[0]);
+      KH[1] = mma_bf16(kf.h, H1, KH[1]);
+      QH[0] = mma_bf16(qf.h, H0, QH[0]);
+      QH[1] = mma_bf16(qf.h, H1, QH[1]);
+      KH[0] = mma_bf16(kf.h, L0, KH[0]);
+      KH[1] = mma_bf16(kf.h, L1, KH[1]);
+      QH[0] = mma_bf16(qf.h, L0, QH[0]);
+      QH[1] = mma_bf16(qf.h, L1, QH[1]);
+      if constexpr (F32) {  // the rows' m and l parts (state hi, lo)
+        KH[0] = mma_bf16(kf.m, H0, KH[0]);
+        KH[1] = mma_bf16(kf.m, H1, KH[1]);
+        QH[0] = mma_bf16(qf.m, H0, QH[0]);
+        QH[1] = mma_bf16(qf.m, H1, QH[1]);
+        KH[0] = mma_bf16(kf.m, L0, KH[0]);
+        KH[1] = mma_bf16(kf.m, L1, KH[1]);
+        QH[0] = mma_bf16(qf.m, L0, QH[0]);
+        QH[1] = mma_bf16(qf.m, L1, QH[1]);
+        KH[0] = mma_bf16(kf.l, H0, KH[0]);
+        KH[1] = mma_bf16(kf.l, H1, KH[1]);
+        QH[0] = mma_bf16(qf.l, H0, QH[0]);
+        QH[1] = mma_bf16(qf.l, H1, QH[1]);
+      }
     }
     if constexpr (MB) {
       // past the first block the held state is the scaled replay state:
@@ -620,17 +731,28 @@ void mverify_kernel(
 
     // ---- X, U = T X, O = diag(so) Q H + P U, ut = U f2 (rows t = 4 g4 + e)
     const f32x4 bte = vec4(2), xbe = vec4(3), soe = vec4(4), f2e = vec4(5);
-    uint32_t vw[4];  // values of the tokens 4 g4 + e at columns c0, c0 + 1
+    // values of the tokens 4 g4 + e at columns c0, c0 + 1
+    float va[4], vb[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vw[e] = *reinterpret_cast<const uint32_t*>(
-          &rows.v[4 * g4 + e][32 * w + 2 * n]);
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (F32) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(
+            &rows.v[4 * g4 + e][32 * w + 2 * n]);
+        va[e] = x[0];
+        vb[e] = x[1];
+      } else {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(
+            &rows.v[4 * g4 + e][32 * w + 2 * n]);
+        va[e] = lo_f(x);
+        vb[e] = hi_f(x);
+      }
+    }
     f32x4 X[2];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool te = 4 * g4 + e < Tb;
-      const float x0 = __builtin_fmaf(-xbe[e], KH[0][e], bte[e] * lo_f(vw[e]));
-      const float x1 = __builtin_fmaf(-xbe[e], KH[1][e], bte[e] * hi_f(vw[e]));
+      const float x0 = __builtin_fmaf(-xbe[e], KH[0][e], bte[e] * va[e]);
+      const float x1 = __builtin_fmaf(-xbe[e], KH[1][e], bte[e] * vb[e]);
       X[0][e] = te ? x0 : 0.f;
       X[1][e] = te ? x1 : 0.f;
     }
@@ -695,11 +817,11 @@ void mverify_kernel(
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
           // the block's raw key rows, still staged in LDS
-          const u32x4 kw = *reinterpret_cast<const u32x4*>(
-              &rows.k[r][32 * ks + 8 * g4]);
+          float kx[8];
+          row8(&rows.k[r][32 * ks + 8 * g4], kx);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float kv = (e & 1) ? hi_f(kw[e / 2]) : lo_f(kw[e / 2]);
+            const float kv = kx[e];
             st[ks][e][0] = state_update(st[ks][e][0], ua, kv);
             st[ks][e][1] = state_update(st[ks][e][1], ub, kv);
           }
@@ -743,14 +865,16 @@ void mverify_kernel(
   }
 }
 
-template <bool REPLAY, bool DBG, bool TREE, bool MB, typename Tab>
+template <bool REPLAY, bool DBG, bool TREE, bool MB, bool F32 = false,
+          typename Tab>
 static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
                            const VerifyArgs& a, const PrevRecords& pr,
                            const Tab& tree, hipStream_t st) {
+  using In = std::conditional_t<F32, float, uint16_t>;
   const int blocks = w.NL * w.N * w.Hv * (w.dv / kCB);
-  return launch(mverify_kernel<REPLAY, DBG, TREE, MB>, dim3(blocks), dim3(kBlock),
-                st, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                (const uint16_t*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
+  return launch(mverify_kernel<REPLAY, DBG, TREE, MB, F32>, dim3(blocks),
+                dim3(kBlock), st, (const In*)a.q, (const In*)a.k,
+                (const In*)a.v, a.beta, a.g, a.S, a.o, a.rk, a.ru, a.ra,
                 a.dbg, w, tl, a.scale, a.l2, pr, tree);
 }
 
@@ -759,28 +883,34 @@ static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
 bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a,
                       bool tree) {
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
-  return in_dtype == GDN_BF16 && d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
+  return (in_dtype == GDN_BF16 || (in_dtype == GDN_F32 && !tree)) &&
+         d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
          d.t_max <= (tree ? wm::kTok : GDN_MAX_T) && al(a.q, 16) &&
          al(a.k, 16) && al(a.v, 4) && al(a.S, 8) && al(a.o, 8) &&
          (a.dbg == nullptr || al(a.dbg, 8));
 }
 
+template <bool MB, bool F32>
+static hipError_t launch_window(const WinDims& w, const LaneTable& tl,
+                                const VerifyArgs& a, const PrevRecords& pr,
+                                bool replay, hipStream_t st) {
+  const NoTable none{};
+  if (replay)
+    return a.dbg ? wm::launch_t<true, true, false, MB, F32>(w, tl, a, pr, none, st)
+                 : wm::launch_t<true, false, false, MB, F32>(w, tl, a, pr, none, st);
+  return a.dbg ? wm::launch_t<false, true, false, MB, F32>(w, tl, a, pr, none, st)
+               : wm::launch_t<false, false, false, MB, F32>(w, tl, a, pr, none, st);
+}
+
 hipError_t launch_mverify(const WinDims& w, const LaneTable& tl,
                           const VerifyArgs& a, const PrevRecords& pr,
                           bool replay, hipStream_t st) {
-  const NoTable none{};
-  if (w.T > wm::kTok) {  // windows of several blocks
-    if (replay)
-      return a.dbg ? wm::launch_t<true, true, false, true>(w, tl, a, pr, none, st)
-                   : wm::launch_t<true, false, false, true>(w, tl, a, pr, none, st);
-    return a.dbg ? wm::launch_t<false, true, false, true>(w, tl, a, pr, none, st)
-                 : wm::launch_t<false, false, false, true>(w, tl, a, pr, none, st);
-  }
-  if (replay)
-    return a.dbg ? wm::launch_t<true, true, false, false>(w, tl, a, pr, none, st)
-                 : wm::launch_t<true, false, false, false>(w, tl, a, pr, none, st);
-  return a.dbg ? wm::launch_t<false, true, false, false>(w, tl, a, pr, none, st)
-               : wm::launch_t<false, false, false, false>(w, tl, a, pr, none, st);
+  const bool mb = w.T > wm::kTok;  // windows of several blocks
+  if (a.f32)
+    return mb ? launch_window<true, true>(w, tl, a, pr, replay, st)
+              : launch_window<false, true>(w, tl, a, pr, replay, st);
+  return mb ? launch_window<true, false>(w, tl, a, pr, replay, st)
+            : launch_window<false, false>(w, tl, a, pr, replay, st);
 }
 
 hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,

@@ -138,8 +138,8 @@ size_t gdn_records_bytes(const gdn_dims* dims);
  *   dbg_states  device f32 [n_layers][n_lanes][t_max][h_v][d_k][d_v] or
  *               NULL: when given, every intermediate state S_1..S_T, as the
  *               kernel holds it (for tests; costs 64 KiB per head per token).
- *               For bf16 inputs with d_k = 128 and d_v a multiple of 128
- *               the window is evaluated in blocks of 16 tokens (the chunked
+ *               With d_k = 128 and d_v a multiple of 128 the window is
+ *               evaluated in blocks of 16 tokens (the chunked
  *               WY/UT form of the delta rule, Yang et al., NeurIPS 2024,
  *               Sec. 3) on the matrix cores, each block from the replay of
  *               the records of the blocks before it; its intermediate states
@@ -163,11 +163,11 @@ int gdn_verify(const gdn_dims* dims, const int32_t* t_lane, const void* q,
  * with m = 0 are neither read nor written.  Commit never folds replayed
  * steps into a block product: it applies the recorded steps one token at a
  * time.  S_m is bit-for-bit the state written to dbg_states for token m:
- *   - on the token-by-token verify (f32 inputs, d_k < 128, d_v not a
- *     multiple of 128, or GDN_FLAG_TOKENWISE) that is the state verify held
+ *   - on the token-by-token verify (d_k < 128, d_v not a multiple of
+ *     128, or GDN_FLAG_TOKENWISE) that is the state verify held
  *     after its m-th token, formed by the same per-step instruction
  *     sequence;
- *   - on the block-form verify (bf16, d_k = 128, d_v a multiple of 128),
+ *   - on the block-form verify (d_k = 128, d_v a multiple of 128),
  *     which never forms per-token states, it is the replay of verify's
  *     records with commit's own operations.  There the emitted deltas and outputs
  *     agree with the rule applied to those replayed states to within about

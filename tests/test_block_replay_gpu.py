@@ -131,9 +131,9 @@ def _rule_gaps(w, dims, S0, o, rec, dbg, parent=None, kda_g=None, scale=1.0):
             float(np.max(o_num[act] / np.maximum(o_den[act], 1e-30))))
 
 
-def _window(name, shape, g_fill=None, ragged=True):
+def _window(name, shape, g_fill=None, ragged=True, bf16=True):
     key = (700, zlib.crc32(name.encode()) % 1000)
-    w = gs.window_inputs(shape, key, ragged=ragged)
+    w = gs.window_inputs(shape, key, ragged=ragged, bf16=bf16)
     if g_fill is not None:
         g_fill(w.g)
     return key, w, gs.initial_state(shape, key)
@@ -164,14 +164,18 @@ FILLS = [("plain", _no_fill), ("alpha0", _zero_decay),
          ("folds", _strong_decay)]
 
 
-@pytest.mark.parametrize("T", [16, 64])
+@pytest.mark.parametrize("T,bf16", [(16, True), (64, True), (16, False),
+                                    (40, False)],
+                         ids=["T16", "T64", "f32_T16", "f32_T40"])
 @pytest.mark.parametrize("fill", FILLS, ids=[f[0] for f in FILLS])
-def test_verify_emits_the_rule_on_the_replayed_states(fill, T):
+def test_verify_emits_the_rule_on_the_replayed_states(fill, T, bf16):
     """T = 64: four blocks of 16, each from the replay of the blocks
-    before it."""
+    before it; f32 inputs: key and query rows split into three bf16 parts
+    for the products."""
     name, g_fill = fill
     shape = gs.WindowShape(2, 4, 4, 2, 128, 128, T)
-    key, w, S0 = _window("verify_%s_%d" % (name, T), shape, g_fill)
+    key, w, S0 = _window("verify_%s_%d%s" % (name, T, "" if bf16 else "_f32"),
+                         shape, g_fill, bf16=bf16)
     w.t_lane[0] = T
     dims = gdn.Dims.of(*shape.__dict__.values())
     q, k, v, beta, g = window_to_dev(w, torch)

@@ -50,6 +50,7 @@ CASES = [
     ("d128_t40_long_window", 1, 3, 2, 1, 128, 128, 40, True, 3, False),
     ("d128_t64_blocks_dbg", 1, 2, 2, 1, 128, 128, 64, True, 3, True),
     ("d128_t17_blocks", 1, 4, 2, 1, 128, 128, 17, True, 4, True),
+    ("f32_d128_blocks", 1, 3, 2, 1, 128, 128, 24, False, 4, True),
     # GDN_FLAG_TOKENWISE on both paths at a block-form shape
     ("d128_tokenwise", 1, 4, 2, 1, 128, 128, 16, True, 4, True),
 ]

@@ -68,6 +68,10 @@ SMALL = [
     # the longest windows the ABI takes (64 tokens): bf16 at d = 128 in four
     # blocks of 16 on the matrix cores, f32 at d_k = 64 token by token
     ("d128_t64_max_window", 1, 2, 4, 2, 128, 128, 64, True, True, True, 1.0),
+    # f32 inputs on the matrix cores (key and query rows split into bf16
+    # hi + lo): one block, and three blocks without the key norm
+    ("f32_d128_t16", 1, 3, 4, 2, 128, 128, 16, False, True, True, 1.0),
+    ("f32_d128_t40_blocks", 1, 2, 2, 1, 128, 256, 40, False, True, False, 0.5),
     # a second block of one token
     ("d128_t17_one_token_block", 1, 2, 2, 1, 128, 128, 17, True, False, True, 1.0),
     # three blocks with two 128-column blocks per head, no key norm, a scale
