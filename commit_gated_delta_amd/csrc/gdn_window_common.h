@@ -301,8 +301,8 @@ static int commit_lanes(const char* fn, const gdn_dims& d,
 }
 
 // The matrix-core verify (gdn_window_mfma.hip): whether a call can take it
-// (bf16 or f32 windows of up to GDN_MAX_T tokens, bf16 draft trees of up to
-// 16 nodes), and its launch (replay = the fused commit + verify).
+// (bf16 or f32 windows of up to GDN_MAX_T tokens, draft trees of up to 16
+// nodes), and its launch (replay = the fused commit + verify).
 __attribute__((visibility("hidden"))) bool mverify_eligible(
     const gdn_dims& d, int in_dtype, const VerifyArgs& a, bool tree);
 __attribute__((visibility("hidden"))) hipError_t launch_mverify(

@@ -4,7 +4,7 @@
 // products as three bf16 parts, see Frag): windows of at most 16 tokens (the
 // shapes of the speculative-decoding section of the NInfer technical review,
 // blog.123qwe.co.kr post 4624) as one block, longer windows (up to 64
-// tokens) in blocks of 16, bf16 trees of at most 16 nodes.  Other shapes, and
+// tokens) in blocks of 16, trees of at most 16 nodes.  Other shapes, and
 // calls with GDN_FLAG_TOKENWISE, take gdn_window.hip.
 //
 // The window is one chunk of the block (WY/UT) form of the rule: Yang et
@@ -172,7 +172,6 @@ void mverify_kernel(
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
   static_assert(!(TREE && MB), "draft trees have at most one block");
-  static_assert(!(TREE && F32), "draft trees take bf16 rows");
   using In = std::conditional_t<F32, float, uint16_t>;
   constexpr int kEl = 16 / (int)sizeof(In);  // entries per 16-byte piece
   constexpr int kPc = F32 ? 2 : 1;           // pieces per thread and row
@@ -883,7 +882,7 @@ static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
 bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a,
                       bool tree) {
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
-  return (in_dtype == GDN_BF16 || (in_dtype == GDN_F32 && !tree)) &&
+  return (in_dtype == GDN_BF16 || in_dtype == GDN_F32) &&
          d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
          d.t_max <= (tree ? wm::kTok : GDN_MAX_T) && al(a.q, 16) &&
          al(a.k, 16) && al(a.v, 4) && al(a.S, 8) && al(a.o, 8) &&
@@ -918,6 +917,9 @@ hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,
                                hipStream_t st) {
   PrevRecords none;
   memset(&none, 0, sizeof(none));
+  if (a.f32)
+    return a.dbg ? wm::launch_t<false, true, true, false, true>(w, tl, a, none, tree, st)
+                 : wm::launch_t<false, false, true, false, true>(w, tl, a, none, tree, st);
   return a.dbg ? wm::launch_t<false, true, true, false>(w, tl, a, none, tree, st)
                : wm::launch_t<false, false, true, false>(w, tl, a, none, tree, st);
 }

@@ -191,8 +191,8 @@ int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
  * ReplaySSM requirement, per node).
  *   parent   host int32 [n_lanes][t_max]: parent[n][t] in -1..t-1 for
  *            t < t_lane[n] (-1: the node steps from S0); nodes are ordered so
- *            that a parent precedes its children.  For bf16 inputs with
- *            d_k = d_v = 128 and t_max <= 16 (and without
+ *            that a parent precedes its children.  With d_k = d_v = 128
+ *            and t_max <= 16 (and without
  *            GDN_FLAG_TOKENWISE) the tree is evaluated as one block product
  *            (the causal mask of the chunked form replaced by the ancestor
  *            relation) and any order costs the same; the debug

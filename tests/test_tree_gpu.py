@@ -92,6 +92,8 @@ CASES = [
     ("f32_d32", 1, 2, 3, 3, 32, 64, 9, False),
     ("f32_d16", 2, 2, 2, 2, 16, 16, 7, False),
     ("bf16_d128_dv256", 1, 2, 2, 1, 128, 256, 10, True),
+    # f32 inputs on the matrix cores (rows as three bf16 parts)
+    ("f32_d128", 1, 3, 4, 2, 128, 128, 16, False),
     # the largest trees the ABI takes (32 nodes): the token-by-token kernel
     ("bf16_d128_32_nodes", 1, 2, 2, 1, 128, 128, 32, True),
 ]
