@@ -376,8 +376,8 @@ extern "C" int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,
   hipError_t e;
   if (!(flags & GDN_FLAG_TOKENWISE) &&
       mkda_eligible(d, in_dtype, q, k, v, g, S, o, dbg_states))
-    e = launch_mkda(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states,
-                    scale, l2, st);
+    e = launch_mkda(w, tl, in_dtype == GDN_F32, q, k, v, beta, g, S, o, rk, ru,
+                    ra, dbg_states, scale, l2, st);
   else if (in_dtype == GDN_BF16)
     e = dbg_states
             ? launch_kda_verify<128, true, uint16_t>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg_states, scale, l2, st)

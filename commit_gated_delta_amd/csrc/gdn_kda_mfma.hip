@@ -1,7 +1,7 @@
 // gdn_kda_mfma.hip -- KDA verify (the per-channel-decay sibling of the rule)
-// on the gfx950 matrix cores, for bf16 inputs and d_k = d_v = 128: a window
-// of at most 16 tokens as one block, longer windows (up to 64 tokens) in
-// blocks of 16, each block from the replay of the records before it (the
+// on the gfx950 matrix cores, for bf16 or f32 inputs and d_k = d_v = 128: a
+// window of at most 16 tokens as one block, longer windows (up to 64 tokens)
+// in blocks of 16, each block from the replay of the records before it (the
 // commit's decay multiply and fma on the held state).  Other shapes, and
 // calls with GDN_FLAG_TOKENWISE, take gdn_kda.hip.
 //
@@ -54,9 +54,10 @@ constexpr int kTok = 16;       // window tokens
 constexpr int kLS = 20;        // padded row of a 16 x 16 LDS matrix
 constexpr int kUS = 33;        // padded row of a wave's ut tile
 
+template <typename In>
 struct KdaLds {
-  __attribute__((aligned(16))) uint16_t k[kTok][kD];  // raw key rows (bf16)
-  __attribute__((aligned(16))) uint16_t q[kTok][kD];  // raw query rows
+  __attribute__((aligned(16))) In k[kTok][kD];  // raw key rows (bf16 or f32)
+  __attribute__((aligned(16))) In q[kTok][kD];  // raw query rows
   __attribute__((aligned(16))) float a[kTok][kD];     // alpha_t
   __attribute__((aligned(16))) float c[kTok][kD];     // C_t
   __attribute__((aligned(16))) float Lt[kTok * kLS];  // L transposed
@@ -92,16 +93,21 @@ __device__ __forceinline__ void widen8(u32x4 w, float (&x)[8]) {
   }
 }
 
-template <bool DBG, bool MB>
+template <bool DBG, bool MB, bool F32>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
-void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                 const uint16_t* __restrict__ v, const float* __restrict__ beta,
+void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
+                 const std::conditional_t<F32, float, uint16_t>* __restrict__ k,
+                 const std::conditional_t<F32, float, uint16_t>* __restrict__ v,
+                 const float* __restrict__ beta,
                  const float* __restrict__ g, const float* S,
                  float* __restrict__ o, float* __restrict__ rec_k,
                  float* __restrict__ rec_u, float* __restrict__ rec_a,
                  float* __restrict__ dbg, WinDims d, LaneTable tl, float scale,
                  int l2norm) {
-  __shared__ KdaLds sh;
+  using In = std::conditional_t<F32, float, uint16_t>;
+  constexpr int kEl = 16 / (int)sizeof(In);  // entries per 16-byte piece
+  constexpr int kPc = F32 ? 2 : 1;           // pieces per thread and row
+  __shared__ KdaLds<In> sh;
   __shared__ KdaWave wv[kWaves];
   // the replay of the debug states and between the blocks of a long
   // window reads the decays a: the fragments then have their own space
@@ -127,9 +133,9 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const size_t kq_step = (size_t)d.Hk * kD;  // per token: q, k, key records
   const size_t vo_step = (size_t)d.Hv * kD;  // per token: v, o, ut records
   const size_t g_step = (size_t)d.Hv * kD;   // per token: g, alpha records
-  const uint16_t* __restrict__ k0 = k + (tok0 * d.Hk + kh) * kD;
-  const uint16_t* __restrict__ q0 = q + (tok0 * d.Hk + kh) * kD;
-  const uint16_t* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)kD;
+  const In* __restrict__ k0 = k + (tok0 * d.Hk + kh) * kD;
+  const In* __restrict__ q0 = q + (tok0 * d.Hk + kh) * kD;
+  const In* __restrict__ v0 = v + (tok0 * d.Hv + h) * (size_t)kD;
   const float* __restrict__ g0 = g + (tok0 * d.Hv + h) * (size_t)kD;
   KdaWave& W = wv[w];
 
@@ -137,20 +143,24 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // gates per thread, the value words), then the state, so that everything
   // before the state products overlaps its latency.  Tokens at or past T
   // read token 0 and become k = q = 0, alpha = 1, beta = 0.
-  const int rt = tid >> 4, rp = tid & 15;  // row token, 8-entry piece
+  const int rt = tid >> 4, rp = tid & 15;  // row token, 16-byte piece
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  u32x4 kr, qr;
+  u32x4 kr[kPc], qr[kPc];  // pieces rp (and rp + 16 for f32 rows)
   f32x4 gr[2];
   float bl;
-  uint32_t vw[4];  // values of the tokens 4 g4 + e at this lane's columns
+  float va[4], vb[4];  // values of the tokens 4 g4 + e at columns c0, c0 + 1
   // the rows of the block of tokens tb .. tb + Tb - 1
   auto load_rows = [&](int tb, int Tb) {
     const bool rv = rt < Tb;
     const int tr = tb + (rv ? rt : 0);
-    kr = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + 8 * rp);
-    qr = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + 8 * rp);
-    kr = rv ? kr : z4;
-    qr = rv ? qr : z4;
+#pragma unroll
+    for (int p = 0; p < kPc; ++p) {
+      const int pe = kEl * (rp + 16 * p);
+      kr[p] = *reinterpret_cast<const u32x4*>(k0 + (uint32_t)(tr * kq_step) + pe);
+      qr[p] = *reinterpret_cast<const u32x4*>(q0 + (uint32_t)(tr * kq_step) + pe);
+      kr[p] = rv ? kr[p] : z4;
+      qr[p] = rv ? qr[p] : z4;
+    }
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int e = tid + kBlock * rep;  // float4 slot: token e / 32
@@ -162,9 +172,19 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * g4 + e;
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(
-          v0 + (uint32_t)((tb + (t < Tb ? t : 0)) * vo_step) + c0);
-      vw[e] = t < Tb ? x : 0u;
+      const In* vp = v0 + (uint32_t)((tb + (t < Tb ? t : 0)) * vo_step) + c0;
+      float x0, x1;
+      if constexpr (F32) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(vp);
+        x0 = x[0];
+        x1 = x[1];
+      } else {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(vp);
+        x0 = lo_f(x);
+        x1 = hi_f(x);
+      }
+      va[e] = t < Tb ? x0 : 0.f;
+      vb[e] = t < Tb ? x1 : 0.f;
     }
   };
   const int T0 = MB ? (T < kTok ? T : kTok) : T;
@@ -187,15 +207,24 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // ---- stage the rows, the decays and beta; write the key and decay records
   auto stage_rows = [&](int tb, int Tb) {
     const bool rv = rt < Tb;
-    *reinterpret_cast<u32x4*>(&sh.k[rt][8 * rp]) = kr;
-    *reinterpret_cast<u32x4*>(&sh.q[rt][8 * rp]) = qr;
+#pragma unroll
+    for (int p = 0; p < kPc; ++p) {
+      *reinterpret_cast<u32x4*>(&sh.k[rt][kEl * (rp + 16 * p)]) = kr[p];
+      *reinterpret_cast<u32x4*>(&sh.q[rt][kEl * (rp + 16 * p)]) = qr[p];
+    }
     if (rv && h % d.group == 0) {
-      float kx[8];
-      widen8(kr, kx);
       float* __restrict__ dst = rec_k + (tok0 * d.Hk + kh) * kD +
-                                (uint32_t)((tb + rt) * kq_step) + 8 * rp;
-      reinterpret_cast<float4*>(dst)[0] = make_float4(kx[0], kx[1], kx[2], kx[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(kx[4], kx[5], kx[6], kx[7]);
+                                (uint32_t)((tb + rt) * kq_step);
+      if constexpr (F32) {
+#pragma unroll
+        for (int p = 0; p < kPc; ++p)
+          *reinterpret_cast<u32x4*>(dst + kEl * (rp + 16 * p)) = kr[p];
+      } else {
+        float kx[8];
+        widen8(kr[0], kx);
+        reinterpret_cast<float4*>(dst + 8 * rp)[0] = make_float4(kx[0], kx[1], kx[2], kx[3]);
+        reinterpret_cast<float4*>(dst + 8 * rp)[1] = make_float4(kx[4], kx[5], kx[6], kx[7]);
+      }
     }
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
@@ -235,14 +264,13 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     } else {
       const int u = tid - kD, t = u >> 3, pc = u & 7;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(&sh.k[t][16 * pc]);
-      const u32x4* qp = reinterpret_cast<const u32x4*>(&sh.q[t][16 * pc]);
+
       float skk = 0.f, sqq = 0.f;
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         float kx[8], qx[8];
-        widen8(kp[hlf], kx);
-        widen8(qp[hlf], qx);
+        row8(&sh.k[t][16 * pc + 8 * hlf], kx);
+        row8(&sh.q[t][16 * pc + 8 * hlf], qx);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           skk = __builtin_fmaf(kx[i], kx[i], skk);
@@ -273,7 +301,7 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       if (cq == 0)
         for (int t = 0; t < 4 * w; ++t) sh.P[t * kLS + s] = 0.f;
       float ksv[8];
-      widen8(*reinterpret_cast<const u32x4*>(&sh.k[s][8 * cq]), ksv);
+      row8(&sh.k[s][8 * cq], ksv);
       float E[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) E[i] = 1.0f;
@@ -281,8 +309,8 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll 1
       for (int t = 4 * w; t < kTok; ++t) {
         float kt[8], qt[8];
-        widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][8 * cq]), kt);
-        widen8(*reinterpret_cast<const u32x4*>(&sh.q[t][8 * cq]), qt);
+        row8(&sh.k[t][8 * cq], kt);
+        row8(&sh.q[t][8 * cq], qt);
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq]);
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sh.a[t][8 * cq + 4]);
         const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
@@ -311,8 +339,8 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     {
       const int j0 = 32 * w + 8 * g4;
       float kx[8], qx[8];
-      widen8(*reinterpret_cast<const u32x4*>(&sh.k[n][j0]), kx);
-      widen8(*reinterpret_cast<const u32x4*>(&sh.q[n][j0]), qx);
+      row8(&sh.k[n][j0], kx);
+      row8(&sh.q[n][j0], qx);
       const f32x4 ca = *reinterpret_cast<const f32x4*>(&sh.c[n][j0]);
       const f32x4 cb = *reinterpret_cast<const f32x4*>(&sh.c[n][j0 + 4]);
       const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
@@ -397,8 +425,8 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       rke[e] = sh.rk[t];
       sqe[e] = scale * sh.rq[t];
       const float xb = bt * rke[e];
-      const float x0 = __builtin_fmaf(-xb, KH[0][e], bt * lo_f(vw[e]));
-      const float x1 = __builtin_fmaf(-xb, KH[1][e], bt * hi_f(vw[e]));
+      const float x0 = __builtin_fmaf(-xb, KH[0][e], bt * va[e]);
+      const float x1 = __builtin_fmaf(-xb, KH[1][e], bt * vb[e]);
       X[0][e] = t < Tb ? x0 : 0.f;
       X[1][e] = t < Tb ? x1 : 0.f;
     }
@@ -451,7 +479,7 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int ks = 0; ks < kKS; ++ks) {
           const int j0 = 32 * ks + 8 * g4;
           float kx[8];
-          widen8(*reinterpret_cast<const u32x4*>(&sh.k[t][j0]), kx);
+          row8(&sh.k[t][j0], kx);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float a = sh.a[t][j0 + e];
@@ -470,15 +498,16 @@ void mkda_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-template <bool DBG, bool MB>
+template <bool DBG, bool MB, bool F32>
 static hipError_t launch_t(const WinDims& w, const LaneTable& tl,
                            const void* q, const void* k, const void* v,
                            const float* beta, const float* g, const float* S,
                            float* o, float* rk, float* ru, float* ra,
                            float* dbg, float scale, int l2, hipStream_t st) {
   const int blocks = w.NL * w.N * w.Hv;
-  return launch(mkda_kernel<DBG, MB>, dim3(blocks), dim3(kBlock), st,
-                (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+  using In = std::conditional_t<F32, float, uint16_t>;
+  return launch(mkda_kernel<DBG, MB, F32>, dim3(blocks), dim3(kBlock), st,
+                (const In*)q, (const In*)k, (const In*)v,
                 beta, g, S, o, rk, ru, ra, dbg, w, tl, scale, l2);
 }
 
@@ -488,25 +517,38 @@ bool mkda_eligible(const gdn_dims& d, int in_dtype, const void* q,
                    const void* k, const void* v, const float* g,
                    const float* S, const float* o, const float* dbg) {
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
-  return in_dtype == GDN_BF16 && d.d_k == wk::kD && d.d_v == wk::kD &&
-         d.t_max <= GDN_MAX_T && al(q, 16) && al(k, 16) && al(v, 4) &&
+  return (in_dtype == GDN_BF16 || in_dtype == GDN_F32) && d.d_k == wk::kD &&
+         d.d_v == wk::kD && d.t_max <= GDN_MAX_T && al(q, 16) && al(k, 16) &&
+         al(v, in_dtype == GDN_F32 ? 8 : 4) &&
          al(g, 16) && al(S, 8) && al(o, 8) && (dbg == nullptr || al(dbg, 8));
 }
 
-hipError_t launch_mkda(const WinDims& w, const LaneTable& tl, const void* q,
-                       const void* k, const void* v, const float* beta,
-                       const float* g, const float* S, float* o, float* rk,
-                       float* ru, float* ra, float* dbg, float scale, int l2,
-                       hipStream_t st) {
+template <bool F32>
+static hipError_t launch_kda(const WinDims& w, const LaneTable& tl,
+                             const void* q, const void* k, const void* v,
+                             const float* beta, const float* g, const float* S,
+                             float* o, float* rk, float* ru, float* ra,
+                             float* dbg, float scale, int l2, hipStream_t st) {
   if (w.T > wk::kTok)  // windows of several blocks
-    return dbg ? wk::launch_t<true, true>(w, tl, q, k, v, beta, g, S, o, rk,
-                                          ru, ra, dbg, scale, l2, st)
-               : wk::launch_t<false, true>(w, tl, q, k, v, beta, g, S, o, rk,
-                                           ru, ra, dbg, scale, l2, st);
-  return dbg ? wk::launch_t<true, false>(w, tl, q, k, v, beta, g, S, o, rk, ru,
-                                         ra, dbg, scale, l2, st)
-             : wk::launch_t<false, false>(w, tl, q, k, v, beta, g, S, o, rk, ru,
-                                          ra, dbg, scale, l2, st);
+    return dbg ? wk::launch_t<true, true, F32>(w, tl, q, k, v, beta, g, S, o,
+                                               rk, ru, ra, dbg, scale, l2, st)
+               : wk::launch_t<false, true, F32>(w, tl, q, k, v, beta, g, S, o,
+                                                rk, ru, ra, dbg, scale, l2, st);
+  return dbg ? wk::launch_t<true, false, F32>(w, tl, q, k, v, beta, g, S, o, rk,
+                                              ru, ra, dbg, scale, l2, st)
+             : wk::launch_t<false, false, F32>(w, tl, q, k, v, beta, g, S, o,
+                                               rk, ru, ra, dbg, scale, l2, st);
+}
+
+hipError_t launch_mkda(const WinDims& w, const LaneTable& tl, bool f32,
+                       const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* S,
+                       float* o, float* rk, float* ru, float* ra, float* dbg,
+                       float scale, int l2, hipStream_t st) {
+  return f32 ? launch_kda<true>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg,
+                                scale, l2, st)
+             : launch_kda<false>(w, tl, q, k, v, beta, g, S, o, rk, ru, ra, dbg,
+                                 scale, l2, st);
 }
 
 }  // namespace gdn

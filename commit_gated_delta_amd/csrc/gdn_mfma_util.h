@@ -38,6 +38,24 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Eight consecutive entries of a staged row, widened to f32 (exact).
+__device__ __forceinline__ void row8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = lo_f(w[i]);
+    x[2 * i + 1] = hi_f(w[i]);
+  }
+}
+__device__ __forceinline__ void row8(const float* p, float (&x)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
 // Two f32 values as packed bf16 pairs: hi = bf16(x), lo = bf16(x - hi), both
 // rounded to nearest even.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi,

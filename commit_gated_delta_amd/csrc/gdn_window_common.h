@@ -313,15 +313,16 @@ __attribute__((visibility("hidden"))) hipError_t launch_mverify_tree(
     const WinDims& w, const LaneTable& tl, const VerifyArgs& a,
     const TreeTable& tree, hipStream_t st);
 
-// The matrix-core KDA verify (gdn_kda_mfma.hip).
+// The matrix-core KDA verify (gdn_kda_mfma.hip; f32: the inputs are f32,
+// else bf16).
 __attribute__((visibility("hidden"))) bool mkda_eligible(
     const gdn_dims& d, int in_dtype, const void* q, const void* k,
     const void* v, const float* g, const float* S, const float* o,
     const float* dbg);
 __attribute__((visibility("hidden"))) hipError_t launch_mkda(
-    const WinDims& w, const LaneTable& tl, const void* q, const void* k,
-    const void* v, const float* beta, const float* g, const float* S,
-    float* o, float* rk, float* ru, float* ra, float* dbg, float scale,
-    int l2, hipStream_t st);
+    const WinDims& w, const LaneTable& tl, bool f32, const void* q,
+    const void* k, const void* v, const float* beta, const float* g,
+    const float* S, float* o, float* rk, float* ru, float* ra, float* dbg,
+    float scale, int l2, hipStream_t st);
 
 }  // namespace gdn

@@ -97,24 +97,6 @@ struct RowLds {
   __attribute__((aligned(16))) In v[kTok][kCB];  // this block's columns
   float g[kTok + 1], b[kTok + 1];  // slot kTok: discarded writes
 };
-// Eight consecutive entries of a staged row, widened to f32 (exact).
-__device__ __forceinline__ void row8(const uint16_t* p, float (&x)[8]) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = lo_f(w[i]);
-    x[2 * i + 1] = hi_f(w[i]);
-  }
-}
-__device__ __forceinline__ void row8(const float* p, float (&x)[8]) {
-  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
 // The bf16 A fragment of eight staged entries: the raw words for bf16 rows;
 // for f32 rows three parts, x = h + m + l + O(2^-25 |x|) (each bf16,
 // rounded to nearest even): a product of two f32 rows keeps f32 accuracy

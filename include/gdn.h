@@ -356,7 +356,7 @@ int gdn_prefill_chunked_noalloc(int32_t n_seqs, int32_t seq_len, int32_t h_v,
  *            (f32 [h_k][d_k]), u_t / sqrt(|k_t|^2 + 1e-6) (f32 [h_v][d_v])
  *            and alpha_t (f32 [h_v][d_k])
  * Supported: d_k == 128 (GDN_EUNSUPPORTED otherwise; gdn_kda_records_bytes
- * returns 0).  For bf16 inputs with d_v = 128 (and without
+ * returns 0).  For bf16 or f32 inputs with d_v = 128 (and without
  * GDN_FLAG_TOKENWISE) the window is evaluated in blocks of 16 tokens with
  * channel-weighted decays, each block from the replay of the records before
  * it; dbg_states then receives the replay of its records (as for

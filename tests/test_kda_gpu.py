@@ -54,6 +54,9 @@ CASES = [
     # the blocks before it
     ("bf16_t40_blocks_forgetting", 1, 3, 2, 1, 128, 40, True, "zero"),
     ("bf16_t64_blocks_strong", 1, 2, 2, 2, 128, 64, True, "strong"),
+    # f32 inputs on the matrix cores, one block and two blocks
+    ("f32_d128_forgetting", 1, 3, 4, 2, 128, 16, False, "zero"),
+    ("f32_t24_blocks_strong", 1, 2, 2, 1, 128, 24, False, "strong"),
 ]
 
 
