@@ -386,7 +386,8 @@ def bench_tree(reps=20, warmup=3):
     """Draft-tree verify of the same batch (8 lanes x 48 layers x 32 value /
     16 key heads, d = 128), 16-node trees per lane in depth-first order
     (each node extends the previous one with probability 0.6), plus the
-    commit of a drawn accepted path; event-timed."""
+    commit of a drawn accepted path; timed by region_ms, with the inputs
+    rotating over four sets and the records over two buffers."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
@@ -394,31 +395,32 @@ def bench_tree(reps=20, warmup=3):
     shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
     dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
     t_lane = np.full(N, T, dtype=np.int32)
-    w = gs.window_inputs(shape, (8, 0))
-
-    def d16(a):
-        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    q, k, v = d16(w.q), d16(w.k), d16(w.v)
-    beta, g = torch.from_numpy(w.beta).to(dev), torch.from_numpy(w.g).to(dev)
+    pool = []
+    for p in range(4):
+        w = gs.window_inputs(shape, (8, p))
+        pool.append((_dev_bf16(w.q, dev), _dev_bf16(w.k, dev),
+                     _dev_bf16(w.v, dev), torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(w.g).to(dev)))
     parent = gs.tree_parents(t_lane, T, (8, 0))
     paths = gs.accepted_tree_paths(parent, t_lane, (8, 0))
     rebuilds = int(sum((parent[n, t] != t - 1) for n in range(N)
                        for t in range(1, T)))
     S = torch.from_numpy(gs.initial_state(shape, (8, 0))).to(dev)
     o = torch.empty((NL, N, T, HV, DV), device=dev)
-    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    recs = [torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
     stream = torch.cuda.current_stream()
     plist = [list(r) for r in parent]
 
     ms_v = region_ms(lambda r: gdn.verify_tree(
-        dims, t_lane, plist, q, k, v, beta, g, S, o, rec, stream=stream),
+        dims, t_lane, plist, *pool[r % 4], S, o, recs[r % 2], stream=stream),
         reps, warmup, stream)
     # path commits of the same accepted paths, back to back (each replays
-    # the path's records on the state the previous one left)
+    # the path's records of one of the last two trees on the state the
+    # previous one left)
     S_c = S.clone()
-    ms_c = region_ms(lambda r: gdn.commit_path(dims, paths, t_lane, plist, rec,
-                                               S_c, stream=stream),
+    ms_c = region_ms(lambda r: gdn.commit_path(dims, paths, t_lane, plist,
+                                               recs[r % 2], S_c, stream=stream),
                      reps, warmup, stream)
     upd = N * T * NL * HV
     # a node has the window traffic of a token; the path commit moves the
@@ -436,7 +438,8 @@ def bench_tree(reps=20, warmup=3):
 def bench_kda(reps=20, warmup=3):
     """KDA (per-channel decay) verify + commit on the same batch shape:
     8 lanes x 48 layers x 32/16 heads, d = 128, T = 16, m ~ U{0..16};
-    event-timed."""
+    timed by region_ms, with the inputs (per-channel gates included)
+    rotating over four sets and the records over two buffers."""
     import torch
     import gdn_synth as gs
     import commit_gated_delta_amd as gdn
@@ -444,26 +447,25 @@ def bench_kda(reps=20, warmup=3):
     shape = gs.WindowShape(NL, N, HV, HK, DK, DV, T)
     dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, T)
     t_lane = np.full(N, T, dtype=np.int32)
-    w = gs.window_inputs(shape, (10, 0))
-
-    def d16(a):
-        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    q, k, v = d16(w.q), d16(w.k), d16(w.v)
-    beta = torch.from_numpy(w.beta).to(dev)
-    g = torch.from_numpy(gs.kda_gates(shape, (10, 0))).to(dev)
+    pool = []
+    for p in range(4):
+        w = gs.window_inputs(shape, (10, p))
+        pool.append((_dev_bf16(w.q, dev), _dev_bf16(w.k, dev),
+                     _dev_bf16(w.v, dev), torch.from_numpy(w.beta).to(dev),
+                     torch.from_numpy(gs.kda_gates(shape, (10, p))).to(dev)))
     S = torch.from_numpy(gs.initial_state(shape, (10, 0))).to(dev)
     o = torch.empty((NL, N, T, HV, DV), device=dev)
-    rec = torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8, device=dev)
+    recs = [torch.empty(gdn.kda_records_bytes(dims), dtype=torch.uint8,
+                        device=dev) for _ in range(2)]
     ms_all = [gs.accepted_uniform(t_lane, (10, 1 + r)) for r in range(reps + warmup)]
     stream = torch.cuda.current_stream()
-    ms_v = region_ms(lambda r: gdn.kda_verify(dims, t_lane, q, k, v, beta, g,
-                                              S, o, rec, stream=stream),
+    ms_v = region_ms(lambda r: gdn.kda_verify(dims, t_lane, *pool[r % 4],
+                                              S, o, recs[r % 2], stream=stream),
                      reps, warmup, stream)
-    # commits of the drawn prefixes, back to back, from the last verify's
-    # records (each on the state the previous one left)
-    ms_c = region_ms(lambda r: gdn.kda_commit(dims, ms_all[r], t_lane, rec, S,
-                                              stream=stream),
+    # commits of the drawn prefixes, back to back, from the last two
+    # verifies' records (each on the state the previous one left)
+    ms_c = region_ms(lambda r: gdn.kda_commit(dims, ms_all[r], t_lane,
+                                              recs[r % 2], S, stream=stream),
                      reps, warmup, stream)
     upd = N * T * NL * HV
     bv = alg_bytes_kda_verify(t_lane)
@@ -543,10 +545,12 @@ def bench_token_verify(reps=20, warmup=3):
                      torch.from_numpy(w.g).to(dev)))
     S = torch.from_numpy(gs.initial_state(shape, (12, 0))).to(dev)
     o = torch.empty((NL, N, T, HV, DV), device=dev)
-    rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+    recs = [torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
     stream = torch.cuda.current_stream()
-    ms = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o, rec,
-                                        stream=stream, tokenwise=True),
+    ms = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % 4], S, o,
+                                        recs[r % 2], stream=stream,
+                                        tokenwise=True),
                    reps, warmup, stream)
     bv = alg_bytes_verify(t_lane)
     return {"workload": "verify of 8 lanes x 48 layers x 32/16 heads, d=128, "
@@ -580,13 +584,19 @@ def bench_general_shapes(reps=10, warmup=2):
         shape = gs.WindowShape(NL, N, HV, HK, DK, DV, tm)
         dims = gdn.Dims.of(NL, N, HV, HK, DK, DV, tm)
         t_lane = np.full(N, tm, dtype=np.int32)
-        w = gs.window_inputs(shape, (13, tm, int(bf16)), bf16=bf16)
-        if bf16:
-            ins = (_dev_bf16(w.q, dev), _dev_bf16(w.k, dev), _dev_bf16(w.v, dev))
-        else:
-            ins = tuple(torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
-        ins = ins + (torch.from_numpy(w.beta).to(dev),
-                     torch.from_numpy(w.g).to(dev))
+        # two input sets (each at least 200 MB) in rotation, and two record
+        # buffers: no call finds the previous call's inputs or records in
+        # the 256 MB Infinity Cache
+        sets = []
+        for p in range(2):
+            w = gs.window_inputs(shape, (13, tm, int(bf16), p), bf16=bf16)
+            if bf16:
+                ins = (_dev_bf16(w.q, dev), _dev_bf16(w.k, dev),
+                       _dev_bf16(w.v, dev))
+            else:
+                ins = tuple(torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+            sets.append(ins + (torch.from_numpy(w.beta).to(dev),
+                               torch.from_numpy(w.g).to(dev)))
         S = torch.from_numpy(gs.initial_state(shape, (13, tm))).to(dev)
         o = torch.empty((NL, N, tm, HV, DV), device=dev)
         nrec = gdn.records_bytes(dims)
@@ -603,23 +613,24 @@ def bench_general_shapes(reps=10, warmup=2):
         if tree:
             parent = [list(p) for p in gs.tree_parents(t_lane, tm, (13, tm))]
             paths = gs.accepted_tree_paths(np.array(parent), t_lane, (13, tm))
-            ms_v = timed(lambda r: gdn.verify_tree(dims, t_lane, parent, *ins,
-                                                   S, o, recs[0],
-                                                   stream=stream))
+            ms_v = timed(lambda r: gdn.verify_tree(dims, t_lane, parent,
+                                                   *sets[r % 2], S, o,
+                                                   recs[r % 2], stream=stream))
             Sc = S.clone()
             ms_c = timed(lambda r: gdn.commit_path(dims, paths, t_lane, parent,
-                                                   recs[0], Sc, stream=stream))
+                                                   recs[r % 2], Sc,
+                                                   stream=stream))
             bc = alg_bytes_commit([len(p) for p in paths])
             rec.update({"verify_ms": ms_v, "commit_ms": ms_c,
                         "verify_hbm_frac": bv / (ms_v * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "commit_hbm_frac": bc / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "node_updates_per_s": N * tm * NL * HV / (ms_v * 1e-3)})
         else:
-            ms_v = timed(lambda r: gdn.verify(dims, t_lane, *ins, S, o,
-                                              recs[r % 2], stream=stream))
+            ms_v = timed(lambda r: gdn.verify(dims, t_lane, *sets[r % 2], S,
+                                              o, recs[r % 2], stream=stream))
             ms_f = timed(lambda r: gdn.commit_verify(
-                dims, m_all[r], t_lane, recs[(r + 1) % 2], t_lane, *ins, S, o,
-                recs[r % 2], stream=stream))
+                dims, m_all[r], t_lane, recs[(r + 1) % 2], t_lane,
+                *sets[r % 2], S, o, recs[r % 2], stream=stream))
             bf = float(np.mean([alg_bytes_fused(t_lane, m) for m in m_all]))
             bf += win_extra
             upd = N * tm * NL * HV
@@ -628,7 +639,7 @@ def bench_general_shapes(reps=10, warmup=2):
                         "fused_hbm_frac": bf / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "fused_updates_per_s": upd / (ms_f * 1e-3)})
         out.append(rec)
-        del S, o, recs, ins
+        del S, o, recs, ins, sets
         torch.cuda.empty_cache()
     return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, every "
                         "lane at T (fused: previous window's m ~ U{0..T}); "
@@ -1058,25 +1069,30 @@ def main():
     res = {}
     if args.path in ("two-call", "both"):
         S = torch.from_numpy(S0).to(dev)
-        rec = torch.empty(nrec, dtype=torch.uint8, device=dev)
+        recs = [torch.empty(nrec, dtype=torch.uint8, device=dev)
+                for _ in range(2)]
 
         def step2(s):
             q, k, v, beta, g = pool[s % len(pool)]
-            gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, rec, stream=stream)
-            gdn.commit(dims, m_all[s], t_lane, rec, S, stream=stream)
+            gdn.verify(dims, t_lane, q, k, v, beta, g, S, o, recs[s % 2],
+                       stream=stream)
+            gdn.commit(dims, m_all[s], t_lane, recs[s % 2], S, stream=stream)
 
         ms = timed(step2)
         bv = alg_bytes_verify(t_lane)
         bc = float(np.mean([alg_bytes_commit(m_all[args.warmup + s])
                             for s in range(args.steps)]))
         # each kernel back to back in a region of its own: verify leaves S
-        # as it is; the commits replay the drawn prefixes of the last
-        # window's records, each on the state the previous one left
+        # as it is; the commits replay the drawn prefixes of the last two
+        # windows' records, each on the state the previous one left.  The
+        # records alternate between two buffers (as the inputs rotate over
+        # the pool), so that no call rewrites or rereads what the call
+        # before it left in the 256 MB Infinity Cache.
         ms_v = region_ms(lambda r: gdn.verify(dims, t_lane, *pool[r % len(pool)],
-                                              S, o, rec, stream=stream),
+                                              S, o, recs[r % 2], stream=stream),
                          args.steps, 2, stream)
         ms_c = region_ms(lambda r: gdn.commit(dims, m_all[r % total], t_lane,
-                                              rec, S, stream=stream),
+                                              recs[r % 2], S, stream=stream),
                          args.steps, 2, stream)
         bc_smp = float(np.mean([alg_bytes_commit(m_all[(2 + r) % total])
                                 for r in range(args.steps)]))
@@ -1091,7 +1107,7 @@ def main():
             "verify_traffic": measured_traffic("verify_kernel"),
             "commit_traffic": measured_traffic("commit_kernel"),
             "alg_bytes_verify": bv, "alg_bytes_per_step": bv + bc}
-        del S, rec
+        del S, recs
     if args.path in ("fused", "both"):
         S = torch.from_numpy(S0).to(dev)
         recs = [torch.empty(nrec, dtype=torch.uint8, device=dev)
