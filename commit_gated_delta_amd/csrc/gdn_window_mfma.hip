@@ -56,9 +56,13 @@
 // state it loads, with the commit's operations, and stores it; a draft tree
 // replaces the causal mask by the ancestor relation (see mverify_kernel).
 // MB (windows of more than 16 tokens): block b runs from the held state,
-// then the block's own records are replayed on it (the commit's
-// operations), and block b + 1 starts from that scaled replay state, its
-// K H and Q H scaled by the scale of block b's last token.
+// which then moves on by the block's rank-1 writes summed in one product on
+// the matrix cores (St += K^T Ut over the block's records, f32 accurate);
+// block b + 1 starts from it, its K H and Q H scaled by the scale of block
+// b's last token.  The held state so agrees with the token-by-token replay
+// of the records (which commit stores, and which the debug states are)
+// to rounding; the sequential replay between blocks cost 0.1 ms per block
+// boundary at 8 lanes x 48 layers, the product about a tenth of that.
 // MFMA layouts: gdn_mfma_util.h.
 #include <hip/hip_runtime.h>
 
@@ -126,6 +130,11 @@ __device__ __forceinline__ Frag frag8(const float* p) {
   return Frag{u32x4{h[0], h[1], h[2], h[3]}, u32x4{m[0], m[1], m[2], m[3]},
               u32x4{l[0], l[1], l[2], l[3]}};
 }
+// Debug states of a window of several blocks: the token-by-token replay
+// state, carried from block to block (entry 2 (8 ks + e) + cs of thread tid).
+struct SeqLds {
+  float s[2 * 8 * kKS][kBlock];
+};
 // A wave's private LDS: L transposed, T, and (debug states only) its ut tile.
 struct WaveLds {
   __attribute__((aligned(16))) float Lt[kTok * kLS];
@@ -160,6 +169,7 @@ void mverify_kernel(
   __shared__ WaveLds wl[kWaves];
   __shared__ RowLds<In> rows;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
+  __shared__ std::conditional_t<DBG && MB, SeqLds, char> seq;
 
   const int nc = d.dv / kCB;
   int item = xcd_item(blockIdx.x, gridDim.x);
@@ -772,10 +782,12 @@ void mverify_kernel(
     // ---- debug states: the replay of this window's own records on the
     // start state (the committed state in the fused call), token by token; in
     // a draft tree, node t's state is the replay of the records on its path.
-    // A window of several blocks replays each block but the last on the held
-    // state, which the next block starts from.
+    // In a window of several blocks the replay runs on its own copy of the
+    // state, carried from block to block through LDS (the held state moves
+    // on by the block products below), so that it stays the token-by-token
+    // replay of every record before it.
     const bool more = MB && tb + kTok < T;
-    if (DBG || more) {
+    if constexpr (DBG) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
@@ -808,7 +820,7 @@ void mverify_kernel(
           }
         }
       };
-      [[maybe_unused]] auto emit = [&](const f32x2 (&st)[kKS][8], int t) {
+      auto emit = [&](const f32x2 (&st)[kKS][8], int t) {
         const float ct = lane_value(c, t);
         float* __restrict__ dp =
             dbg + (((tok0 + tb + t) * d.Hv + h) * (size_t)kDK) * dv;
@@ -833,13 +845,142 @@ void mverify_kernel(
             if ((path >> r) & 1u) apply(sd, r);
           emit(sd, t);
         }
+      } else if constexpr (MB) {
+        f32x2 sd[kKS][8];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sd[ks][e] = tb == 0 ? s2[ks][e]
+                                : f32x2{seq.s[2 * (8 * ks + e)][tid],
+                                        seq.s[2 * (8 * ks + e) + 1][tid]};
+#pragma unroll 1
+        for (int t = 0; t < Tb; ++t) {
+          apply(sd, t);
+          emit(sd, t);
+        }
+        if (more) {
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              seq.s[2 * (8 * ks + e)][tid] = sd[ks][e][0];
+              seq.s[2 * (8 * ks + e) + 1][tid] = sd[ks][e][1];
+            }
+        }
       } else {
 #pragma unroll 1
         for (int t = 0; t < Tb; ++t) {
           apply(s2, t);
-          if constexpr (DBG) emit(s2, t);
+          emit(s2, t);
         }
       }
+    }
+    // ---- the held state after the block, for the next one: the block's
+    // rank-1 writes summed in one product, St += K^T Ut (key rows as the A
+    // operand, the records ut as B), on v_mfma_f32_16x16x32_bf16.  The 32
+    // k-slots of lane group g carry tokens 4 g .. 4 g + 3 twice, once for
+    // each of two operand parts: ut enters as three bf16 parts, f32 key rows
+    // as three as well (the six part products of order at most 2^-16),
+    // bf16 key rows exactly.  Result row 4 g + i of tile (ks, half) is state
+    // row 32 ks + 8 g + 4 half + i, so each lane receives exactly the
+    // entries it holds.  Folds inside the block (rare) scale the start state
+    // by the product of the block's phi and each ut_t by the phi after
+    // token t: the closed form of the fold-then-write steps.
+    if (more) {
+      float ub[2][4];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ub[cs][e] = ut[cs][e];
+      if (__builtin_amdgcn_ballot_w64(phi != 1.f) != 0) {
+        float pall = 1.f, pf[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+        for (int t = 0; t < Tb; ++t) {
+          const float pt = lane_value(phi, t);
+          pall *= pt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pf[e] = t > 4 * g4 + e ? pf[e] * pt : pf[e];
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s2[ks][e][0] = pall * s2[ks][e][0];
+            s2[ks][e][1] = pall * s2[ks][e][1];
+          }
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ub[cs][e] *= pf[e];
+      }
+      // ut of tokens 4 g4 .. 4 g4 + 3 in three parts (h, m, l), packed pairs
+      u32x4 B1[2], B2[2];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float a = ub[cs][2 * i], b = ub[cs][2 * i + 1];
+          split2(a, b, ph[i], pm[i]);
+          const f32x2 y = {a - lo_f(ph[i]) - lo_f(pm[i]),
+                           b - hi_f(ph[i]) - hi_f(pm[i])};
+          pl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+        }
+        if constexpr (F32) {
+          B1[cs] = u32x4{ph[0], ph[1], pm[0], pm[1]};  // [h, m]
+          B2[cs] = u32x4{pl[0], pl[1], ph[0], ph[1]};  // [l, h]
+        } else {
+          B1[cs] = u32x4{ph[0], ph[1], pm[0], pm[1]};  // [h, m]
+          B2[cs] = u32x4{pl[0], pl[1], 0u, 0u};        // [l, 0]
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // key entry kx of tokens 4 g4 + j: the lane's A row
+          const int kx = 32 * ks + 8 * (n >> 2) + 4 * half + (n & 3);
+          f32x4 D[2];
+          if constexpr (F32) {
+            uint32_t ah[2], am[2], al[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const float a = rows.k[4 * g4 + 2 * i][kx];
+              const float b = rows.k[4 * g4 + 2 * i + 1][kx];
+              split2(a, b, ah[i], am[i]);
+              const f32x2 y = {a - lo_f(ah[i]) - lo_f(am[i]),
+                               b - hi_f(ah[i]) - hi_f(am[i])};
+              al[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+            }
+            const u32x4 Ahh = {ah[0], ah[1], ah[0], ah[1]};
+            const u32x4 Amm = {am[0], am[1], am[0], am[1]};
+            const u32x4 Ahl = {ah[0], ah[1], al[0], al[1]};
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+              D[cs] = mma_bf16(Ahh, B1[cs], f32x4{0.f, 0.f, 0.f, 0.f});
+              D[cs] = mma_bf16(Amm, B1[cs], D[cs]);
+              D[cs] = mma_bf16(Ahl, B2[cs], D[cs]);
+            }
+          } else {
+            uint32_t a[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              a[i] = (uint32_t)rows.k[4 * g4 + 2 * i][kx] |
+                     ((uint32_t)rows.k[4 * g4 + 2 * i + 1][kx] << 16);
+            const u32x4 A = {a[0], a[1], a[0], a[1]};
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+              D[cs] = mma_bf16(A, B1[cs], f32x4{0.f, 0.f, 0.f, 0.f});
+              D[cs] = mma_bf16(A, B2[cs], D[cs]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s2[ks][4 * half + i][0] += D[0][i];
+            s2[ks][4 * half + i][1] += D[1][i];
+          }
+        }
     }
     if (!more) break;
     c_in = lane_value(c, Tb - 1);

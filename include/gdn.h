@@ -141,10 +141,13 @@ size_t gdn_records_bytes(const gdn_dims* dims);
  *               With d_k = 128 and d_v a multiple of 128 the window is
  *               evaluated in blocks of 16 tokens (the chunked
  *               WY/UT form of the delta rule, Yang et al., NeurIPS 2024,
- *               Sec. 3) on the matrix cores, each block from the replay of
- *               the records of the blocks before it; its intermediate states
- *               are then defined as the token-by-token replay of its own
- *               records, which is what dbg_states receives.
+ *               Sec. 3) on the matrix cores, each block from the state the
+ *               blocks before it leave (their rank-1 writes summed in one
+ *               matrix-core product, equal to the token-by-token replay of
+ *               their records to rounding); its intermediate states are
+ *               then defined as the token-by-token replay of its own
+ *               records, which is what dbg_states receives (asking for them
+ *               changes neither o nor the records).
  *   scale       multiplies o only (1.0f for o_t = S_t q_t).
  *   flags       GDN_FLAG_L2NORM_QK, GDN_FLAG_TOKENWISE (evaluate token by
  *               token at every shape: verify then holds each intermediate

@@ -3,7 +3,7 @@
 For bf16 inputs with d_k = d_v = 128, the verify kernels (plain, fused
 with the previous commit, draft tree, KDA) evaluate a window as block
 products on the matrix cores (the chunked WY/UT form; windows of more than
-16 tokens in blocks of 16, each from the replay of the blocks before it) and
+16 tokens in blocks of 16, each from the state the blocks before it leave) and
 never hold the per-token states.  What they record (the
 deltas u_t, the decay steps, the raw keys) is replayed token by token by
 commit, and commit(m) is bit for bit the debug state after token m (tested
@@ -22,8 +22,9 @@ below the oracle tolerance.  The split-bf16 products of the block form
 (hi = bf16(x), lo = bf16(x - hi)) carry at most 2^-16 relative error per
 element and about 2^-18 typically, and those errors enter a dot product of
 128 terms with random signs; the replay's own f32 rounding is of order
-1e-7 (over at most 16 tokens within a block: every block starts from the
-replayed state).  Measured on MI355X: u within 1.9e-7 .. 2.8e-7 and
+1e-7, and so is the distance between the state a block starts from (the
+earlier blocks' writes summed on the matrix cores, f32 accurate) and the
+replayed state there.  Measured on MI355X: u within 1.9e-7 .. 2.8e-7 and
 o within 3.2e-7 .. 4.5e-6 over these cases.  The ReplaySSM passage of the
 NInfer review asks that the committed transitions equal what verify computed
 in finite precision; these checks measure how far the block form's emitted
@@ -169,8 +170,8 @@ FILLS = [("plain", _no_fill), ("alpha0", _zero_decay),
                          ids=["T16", "T64", "f32_T16", "f32_T40"])
 @pytest.mark.parametrize("fill", FILLS, ids=[f[0] for f in FILLS])
 def test_verify_emits_the_rule_on_the_replayed_states(fill, T, bf16):
-    """T = 64: four blocks of 16, each from the replay of the blocks
-    before it; f32 inputs: key and query rows split into three bf16 parts
+    """T = 64: four blocks of 16, each from the state the blocks before it
+    leave (their writes summed on the matrix cores); f32 inputs: key and query rows split into three bf16 parts
     for the products."""
     name, g_fill = fill
     shape = gs.WindowShape(2, 4, 4, 2, 128, 128, T)

@@ -324,6 +324,45 @@ def test_verify_is_deterministic_and_leaves_state():
     assert np.array_equal(S_dev.cpu().numpy(), S0)
 
 
+@pytest.mark.parametrize("case", [("bf16_T40_folds", 40, True),
+                                  ("f32_T40_folds", 40, False),
+                                  ("bf16_T64_alpha0", 64, True)],
+                         ids=lambda c: c[0])
+def test_debug_states_leave_outputs_unchanged(case):
+    """Windows of several blocks: asking for the debug states (which run the
+    token-by-token replay on a copy of the state) changes neither the
+    outputs nor the records, bit for bit, also with folds and alpha = 0
+    inside the blocks."""
+    name, T, bf16 = case
+    shape = gs.WindowShape(1, 3, 4, 2, 128, 128, T)
+    key = (112, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    w.t_lane[0] = T
+    if "folds" in name:
+        w.g[:] = -3.0 - 0.5 * np.arange(w.g.shape[-1])[None, None, None, :]
+    else:
+        w.g[:, :, 3] = -np.inf
+        w.g[:, :, 20, ::2] = -200.0
+        w.g[:, :, 37] = -np.inf
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o1, r1, dbg = _run_verify(dims, w, S_dev, dbg=True)
+    o2, r2, _ = _run_verify(dims, w, S_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(o1, 7.0), torch.nan_to_num(o2, 7.0))
+    m = w.t_lane.copy()
+    Sa, Sb = to_dev(S0, torch), to_dev(S0, torch)
+    gdn.commit(dims, m, w.t_lane, r1, Sa)
+    gdn.commit(dims, m, w.t_lane, r2, Sb)
+    assert torch.equal(Sa, Sb)
+    dbg_np = dbg.cpu().numpy()
+    Sa = Sa.cpu().numpy()
+    for n in range(3):
+        assert np.array_equal(Sa[:, n], dbg_np[:, n, int(w.t_lane[n]) - 1]), n
+    say("  %s: outputs and records unchanged by debug states" % name)
+
+
 def test_zero_gates_are_bitwise_identity():
     """beta = 0, g = 0: u = 0 and alpha = 1, so every step is
     fma(0, k, 1*S) = S exactly; commit(T) returns S0 bit for bit."""
