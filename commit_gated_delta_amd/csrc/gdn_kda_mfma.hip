@@ -1,8 +1,10 @@
 // gdn_kda_mfma.hip -- KDA verify (the per-channel-decay sibling of the rule)
 // on the gfx950 matrix cores, for bf16 or f32 inputs and d_k = d_v = 128: a
 // window of at most 16 tokens as one block, longer windows (up to 64 tokens)
-// in blocks of 16, each block from the replay of the records before it (the
-// commit's decay multiply and fma on the held state).  Other shapes, and
+// in blocks of 16, each block from the state the blocks before it leave
+// (their decay-then-write steps in closed form, the writes summed in one
+// matrix-core product; equal to the commit's token-by-token replay to f32
+// rounding).  Other shapes, and
 // calls with GDN_FLAG_TOKENWISE, take gdn_kda.hip.
 //
 // The rule (Kimi Delta Attention of Kimi Linear, 2025; the NInfer technical
@@ -74,6 +76,16 @@ struct KdaWave {
   __attribute__((aligned(16))) float Ts[kTok * kLS];
   float Us[kTok * kUS];
 };
+// Windows of several blocks: E_t = alpha_{t+1} ... alpha_15 per channel (the
+// decay from token t to the end of the block), and for debug states the
+// token-by-token replay state carried from block to block (entry
+// 2 (8 ks + e) + cs of thread tid).
+struct KdaSuffix {
+  __attribute__((aligned(16))) float e[kTok][kD];
+};
+struct KdaSeq {
+  float s[2 * 8 * kKS][kBlock];
+};
 
 // Sum over the 16 lanes of a DPP row (every lane of the row gets it).
 __device__ __forceinline__ float row_sum16(float x) {
@@ -112,6 +124,8 @@ void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
   // the replay of the debug states and between the blocks of a long
   // window reads the decays a: the fragments then have their own space
   __shared__ std::conditional_t<DBG || MB, AFrags, char> af_own;
+  __shared__ std::conditional_t<MB, KdaSuffix, char> suf;
+  __shared__ std::conditional_t<DBG && MB, KdaSeq, char> seq;
   AFrags& Af = *reinterpret_cast<AFrags*>(DBG || MB ? (void*)&af_own : (void*)&sh.a[0][0]);
 
   int item = xcd_item(blockIdx.x, gridDim.x);
@@ -244,7 +258,7 @@ void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
   __syncthreads();
 
   // the window in blocks of kTok tokens (one block unless MB), each from
-  // the held state: the replay of the blocks before it
+  // the held state the blocks before it leave
   for (int tb = 0;; tb += kTok) {
     const int Tb = MB ? (T - tb < kTok ? T - tb : kTok) : T;
     if (MB && tb > 0) {
@@ -261,6 +275,14 @@ void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
       for (int t = 0; t < kTok; ++t) {
         cc = cc * sh.a[t][tid];
         sh.c[t][tid] = cc;
+      }
+      if constexpr (MB) {
+        float ee = 1.0f;
+#pragma unroll
+        for (int t = kTok - 1; t >= 0; --t) {
+          suf.e[t][tid] = ee;
+          ee = ee * sh.a[t][tid];
+        }
       }
     } else {
       const int u = tid - kD, t = u >> 3, pc = u & 7;
@@ -459,36 +481,138 @@ void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
     }
 
     // ---- debug states: the records replayed token by token on the start
-    // state with commit's operations (decay multiply, then the fma); a window
-    // of several blocks replays each block but the last on the held state,
-    // which the next block starts from
+    // state with commit's operations (decay multiply, then the fma).  In a
+    // window of several blocks the replay runs on its own copy of the state,
+    // carried from block to block through LDS (the held state moves on by
+    // the block product below).
     const bool more = MB && tb + kTok < T;
-    if (DBG || more) {
+    if constexpr (DBG) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         W.Us[(4 * g4 + e) * kUS + 2 * n] = ut[0][e];
         W.Us[(4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
       }
       wave_lds_sync();
+      auto replay = [&](f32x2 (&st)[kKS][8]) {
 #pragma unroll 1
-      for (int t = 0; t < Tb; ++t) {
-        const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
-        [[maybe_unused]] float* __restrict__ dp =
-            dbg + ((tok0 + tb + t) * d.Hv + h) * (size_t)kD * kD;
+        for (int t = 0; t < Tb; ++t) {
+          const float ua = W.Us[t * kUS + 2 * n], ub = W.Us[t * kUS + 2 * n + 1];
+          float* __restrict__ dp =
+              dbg + ((tok0 + tb + t) * d.Hv + h) * (size_t)kD * kD;
 #pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          const int j0 = 32 * ks + 8 * g4;
-          float kx[8];
-          row8(&sh.k[t][j0], kx);
+          for (int ks = 0; ks < kKS; ++ks) {
+            const int j0 = 32 * ks + 8 * g4;
+            float kx[8];
+            row8(&sh.k[t][j0], kx);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float a = sh.a[t][j0 + e];
-            s2[ks][e][0] = s2[ks][e][0] * a;
-            s2[ks][e][1] = s2[ks][e][1] * a;
-            s2[ks][e][0] = __builtin_fmaf(ua, kx[e], s2[ks][e][0]);
-            s2[ks][e][1] = __builtin_fmaf(ub, kx[e], s2[ks][e][1]);
-            if constexpr (DBG)
-              *reinterpret_cast<f32x2*>(dp + (size_t)(j0 + e) * kD + c0) = s2[ks][e];
+            for (int e = 0; e < 8; ++e) {
+              const float a = sh.a[t][j0 + e];
+              st[ks][e][0] = st[ks][e][0] * a;
+              st[ks][e][1] = st[ks][e][1] * a;
+              st[ks][e][0] = __builtin_fmaf(ua, kx[e], st[ks][e][0]);
+              st[ks][e][1] = __builtin_fmaf(ub, kx[e], st[ks][e][1]);
+              *reinterpret_cast<f32x2*>(dp + (size_t)(j0 + e) * kD + c0) = st[ks][e];
+            }
+          }
+        }
+      };
+      if constexpr (MB) {
+        f32x2 sd[kKS][8];
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sd[ks][e] = tb == 0 ? s2[ks][e]
+                                : f32x2{seq.s[2 * (8 * ks + e)][tid],
+                                        seq.s[2 * (8 * ks + e) + 1][tid]};
+        replay(sd);
+        if (more) {
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              seq.s[2 * (8 * ks + e)][tid] = sd[ks][e][0];
+              seq.s[2 * (8 * ks + e) + 1][tid] = sd[ks][e][1];
+            }
+        }
+      } else {
+        replay(s2);
+      }
+    }
+    // ---- the held state after the block, for the next one: the closed form
+    // of the block's decay-then-write steps, St = diag(C_15) St + sum_t
+    // diag(E_t) k_t ut_t^T, the sum as one product on
+    // v_mfma_f32_16x16x32_bf16 with the decayed key rows k_t . E_t as the
+    // A operand and the records ut as B, each in three bf16 parts (the six
+    // part products of order at most 2^-16).  The 32 k-slots of lane group g
+    // carry tokens 4 g .. 4 g + 3 twice, once per operand part; result row
+    // 4 g + i of tile (ks, half) is state row 32 ks + 8 g + 4 half + i, the
+    // entries the lane holds.  Decays enter only as running products, so
+    // alpha = 0 channels stay exact.
+    if constexpr (MB) if (more) {
+      u32x4 B1[2], B2[2];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float a = ut[cs][2 * i], b = ut[cs][2 * i + 1];
+          split2(a, b, ph[i], pm[i]);
+          const f32x2 y = {a - lo_f(ph[i]) - lo_f(pm[i]),
+                           b - hi_f(ph[i]) - hi_f(pm[i])};
+          pl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+        }
+        B1[cs] = u32x4{ph[0], ph[1], pm[0], pm[1]};  // [h, m]
+        B2[cs] = u32x4{pl[0], pl[1], ph[0], ph[1]};  // [l, h]
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        // the block's decay of the lane's state rows 32 ks + 8 g4 + e
+        const f32x4 c0v = *reinterpret_cast<const f32x4*>(&sh.c[kTok - 1][32 * ks + 8 * g4]);
+        const f32x4 c1v = *reinterpret_cast<const f32x4*>(&sh.c[kTok - 1][32 * ks + 8 * g4 + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s2[ks][e][0] *= c0v[e];
+          s2[ks][e][1] *= c0v[e];
+          s2[ks][e + 4][0] *= c1v[e];
+          s2[ks][e + 4][1] *= c1v[e];
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // key entry kx of tokens 4 g4 + j, decayed to the block's end
+          const int kx = 32 * ks + 8 * (n >> 2) + 4 * half + (n & 3);
+          uint32_t ah[2], am[2], al[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int t0 = 4 * g4 + 2 * i;
+            float ka, kb;
+            if constexpr (F32) {
+              ka = sh.k[t0][kx];
+              kb = sh.k[t0 + 1][kx];
+            } else {
+              ka = lo_f((uint32_t)sh.k[t0][kx]);
+              kb = lo_f((uint32_t)sh.k[t0 + 1][kx]);
+            }
+            const float a = ka * suf.e[t0][kx], b = kb * suf.e[t0 + 1][kx];
+            split2(a, b, ah[i], am[i]);
+            const f32x2 y = {a - lo_f(ah[i]) - lo_f(am[i]),
+                             b - hi_f(ah[i]) - hi_f(am[i])};
+            al[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+          }
+          const u32x4 Ahh = {ah[0], ah[1], ah[0], ah[1]};
+          const u32x4 Amm = {am[0], am[1], am[0], am[1]};
+          const u32x4 Ahl = {ah[0], ah[1], al[0], al[1]};
+          f32x4 D[2];
+#pragma unroll
+          for (int cs = 0; cs < 2; ++cs) {
+            D[cs] = mma_bf16(Ahh, B1[cs], f32x4{0.f, 0.f, 0.f, 0.f});
+            D[cs] = mma_bf16(Amm, B1[cs], D[cs]);
+            D[cs] = mma_bf16(Ahl, B2[cs], D[cs]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s2[ks][4 * half + i][0] += D[0][i];
+            s2[ks][4 * half + i][1] += D[1][i];
           }
         }
       }

@@ -361,9 +361,11 @@ int gdn_prefill_chunked_noalloc(int32_t n_seqs, int32_t seq_len, int32_t h_v,
  * Supported: d_k == 128 (GDN_EUNSUPPORTED otherwise; gdn_kda_records_bytes
  * returns 0).  For bf16 or f32 inputs with d_v = 128 (and without
  * GDN_FLAG_TOKENWISE) the window is evaluated in blocks of 16 tokens with
- * channel-weighted decays, each block from the replay of the records before
- * it; dbg_states then receives the replay of its records (as for
- * gdn_verify).
+ * channel-weighted decays, each block from the state the blocks before it
+ * leave (their writes summed in one matrix-core product, equal to the
+ * token-by-token replay of their records to rounding); dbg_states then
+ * receives the replay of its records, and asking for it changes neither o
+ * nor the records (as for gdn_verify).
  */
 size_t gdn_kda_records_bytes(const gdn_dims* dims);
 int gdn_kda_verify(const gdn_dims* dims, const int32_t* t_lane,

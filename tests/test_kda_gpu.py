@@ -50,7 +50,7 @@ CASES = [
     # the matrix-core KDA verify (bf16, d_v = 128, one block) with zero
     # decays on some channels
     ("bf16_channel_forgetting_d128", 1, 2, 4, 2, 128, 12, True, "zero"),
-    # windows of 40 and 64 tokens: blocks of 16, each from the replay of
+    # windows of 40 and 64 tokens: blocks of 16, each from the state left by
     # the blocks before it
     ("bf16_t40_blocks_forgetting", 1, 3, 2, 1, 128, 40, True, "zero"),
     ("bf16_t64_blocks_strong", 1, 2, 2, 2, 128, 64, True, "strong"),
