@@ -104,6 +104,42 @@ def test_kda_parity_and_bitexact_replay(case):
         assert s_rel_err(S_c, S_ref) <= TOL
 
 
+@pytest.mark.parametrize("case", [("bf16_t40_forgetting", 40, True),
+                                  ("f32_t33_strong", 33, False)],
+                         ids=lambda c: c[0])
+def test_kda_debug_states_leave_outputs_unchanged(case):
+    """Windows of several blocks: asking for the debug states (the
+    token-by-token replay on a copy of the state) changes neither the
+    outputs nor the records, bit for bit."""
+    name, T, bf16 = case
+    shape = gs.WindowShape(1, 3, 4, 2, 128, 128, T)
+    key = (603, zlib.crc32(name.encode()) % 1000)
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    w.t_lane[0] = T
+    gk = gs.kda_gates(shape, key)
+    if "forgetting" in name:
+        gk[:, :, 2, :, ::3] = -np.inf
+        gk[:, :, 21, :, 1::4] = -200.0
+    else:
+        gk[:] -= 4.0
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o1, r1, dbg = _kda_run(dims, w, gk, S_dev)
+    o2, r2, _ = _kda_run(dims, w, gk, S_dev, dbg=False)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(o1, 7.0), torch.nan_to_num(o2, 7.0))
+    m = w.t_lane.copy()
+    Sa, Sb = to_dev(S0, torch), to_dev(S0, torch)
+    gdn.kda_commit(dims, m, w.t_lane, r1, Sa)
+    gdn.kda_commit(dims, m, w.t_lane, r2, Sb)
+    assert torch.equal(Sa, Sb)
+    Sa, dbg_np = Sa.cpu().numpy(), dbg.cpu().numpy()
+    for n in range(3):
+        assert np.array_equal(Sa[:, n], dbg_np[:, n, int(w.t_lane[n]) - 1]), n
+    say("  %s: outputs and records unchanged by debug states" % name)
+
+
 def test_kda_zero_gates_are_bitwise_identity():
     """beta = 0 and alpha = 1 on every channel: S * 1 then fma(0, k, S)
     leave the state bit for bit."""
