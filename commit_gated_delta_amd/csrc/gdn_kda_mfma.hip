@@ -328,8 +328,15 @@ void mkda_kernel(const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
 #pragma unroll
       for (int i = 0; i < 8; ++i) E[i] = 1.0f;
       const float rks = sh.rk[s];
+      // rows past the block's tokens: L and P stay exactly 0 (T is then the
+      // identity there and U, X vanish), without their running products
+      if (cq == 0)
+        for (int t = Tb > 4 * w ? Tb : 4 * w; t < kTok; ++t) {
+          sh.Lt[s * kLS + t] = 0.f;
+          sh.P[t * kLS + s] = 0.f;
+        }
 #pragma unroll 1
-      for (int t = 4 * w; t < kTok; ++t) {
+      for (int t = 4 * w; t < Tb; ++t) {
         float kt[8], qt[8];
         row8(&sh.k[t][8 * cq], kt);
         row8(&sh.q[t][8 * cq], qt);
