@@ -564,7 +564,8 @@ def bench_general_shapes(reps=10, warmup=2):
     """Shapes beyond the pages' windows, on the same 8-lane x 48-layer x
     32/16-head batch (d = 128): f32 inputs at T = 16 (block form, f32 rows
     in three bf16 parts), bf16 windows of 32 and 64 tokens (block form in
-    blocks of 16) and 32-node draft trees (token by token).  Verify, commit and the fused round are timed by
+    blocks of 16) and 32-node draft trees (block form, two blocks of 16).
+    Verify, commit and the fused round are timed by
     region_ms; HBM fractions against the same algorithmic byte counts as the
     headline (inputs at their own width)."""
     import torch
@@ -643,7 +644,7 @@ def bench_general_shapes(reps=10, warmup=2):
         torch.cuda.empty_cache()
     return {"workload": "8 lanes x 48 layers x 32/16 heads, d=128, every "
                         "lane at T (fused: previous window's m ~ U{0..T}); "
-                        "trees token by token, windows in blocks of 16", "points": out}
+                        "windows and 32-node trees in blocks of 16", "points": out}
 
 
 # Synthetic workloads of the speculative-decoding round, timed as chains of

@@ -4,7 +4,8 @@
 // products as three bf16 parts, see Frag): windows of at most 16 tokens (the
 // shapes of the speculative-decoding section of the NInfer technical review,
 // blog.123qwe.co.kr post 4624) as one block, longer windows (up to 64
-// tokens) in blocks of 16, trees of at most 16 nodes.  Other shapes, and
+// tokens) in blocks of 16, draft trees of up to 32 nodes in blocks of 16.
+// Other shapes, and
 // calls with GDN_FLAG_TOKENWISE, take gdn_window.hip.
 //
 // The window is one chunk of the block (WY/UT) form of the rule: Yang et
@@ -130,6 +131,22 @@ __device__ __forceinline__ Frag frag8(const float* p) {
   return Frag{u32x4{h[0], h[1], h[2], h[3]}, u32x4{m[0], m[1], m[2], m[3]},
               u32x4{l[0], l[1], l[2], l[3]}};
 }
+// Draft trees of more than 16 nodes: what later blocks need of a node (its
+// path aggregate -- segment sum G, deepest zero-decay node R, scale c, fold
+// phi, ancestor set -- its inverse key norm and raw key row), and per wave
+// the deltas U of every block but the last, in the D layout of T X.
+template <typename In>
+struct TreeLds {
+  __attribute__((aligned(16))) In k[GDN_MAX_T][kDK];
+  __attribute__((aligned(16))) f32x4 U[kWaves][GDN_MAX_T / kTok - 1][2][kWave];
+  float G[GDN_MAX_T], c[GDN_MAX_T], phi[GDN_MAX_T], rk[GDN_MAX_T];
+  int R[GDN_MAX_T];
+  uint32_t alo[GDN_MAX_T], ahi[GDN_MAX_T];
+};
+// Debug states of such trees: every node's ut tile, per wave.
+struct TreeDbgLds {
+  float Us[kWaves][GDN_MAX_T * kUS];
+};
 // Debug states of a window of several blocks: the token-by-token replay
 // state, carried from block to block (entry 2 (8 ks + e) + cs of thread tid).
 struct SeqLds {
@@ -148,9 +165,14 @@ struct WaveLds {
 // replaced by the ancestor relation: L_ts and P_ts are nonzero only for s an
 // ancestor (or, for P, t itself), dec(t, s) is the decay along the path from
 // s to t, and the scale sequence continues the parent's scale.  A parent
-// precedes its children, so L stays strictly lower triangular.
+// precedes its children, so L stays strictly lower triangular.  A tree of
+// several blocks (MB) is solved from the root state throughout, by block
+// forward substitution of the whole system: block b's nodes take
+// X_b -= L_bb' U_b' and O_b += P_bb' U_b' from every earlier block b'
+// (their keys, path aggregates and, per wave, U kept in LDS); the held
+// state never moves.
 template <bool REPLAY, bool DBG, bool TREE, bool MB, bool F32>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG || F32 || (MB && REPLAY) ? 2 : 3)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(DBG || F32 || (MB && (REPLAY || TREE)) ? 2 : 3)))
 void mverify_kernel(
     const std::conditional_t<F32, float, uint16_t>* __restrict__ q,
     const std::conditional_t<F32, float, uint16_t>* __restrict__ k,
@@ -162,14 +184,15 @@ void mverify_kernel(
     LaneTable tl, float scale, int l2norm, PrevRecords prev,
     std::conditional_t<TREE, TreeTable, NoTable> tree) {
   static_assert(!(TREE && REPLAY), "draft trees have no fused replay");
-  static_assert(!(TREE && MB), "draft trees have at most one block");
   using In = std::conditional_t<F32, float, uint16_t>;
   constexpr int kEl = 16 / (int)sizeof(In);  // entries per 16-byte piece
   constexpr int kPc = F32 ? 2 : 1;           // pieces per thread and row
   __shared__ WaveLds wl[kWaves];
   __shared__ RowLds<In> rows;
   __shared__ std::conditional_t<REPLAY, Stage, char> stage;
-  __shared__ std::conditional_t<DBG && MB, SeqLds, char> seq;
+  __shared__ std::conditional_t<DBG && MB && !TREE, SeqLds, char> seq;
+  __shared__ std::conditional_t<TREE && MB, TreeLds<In>, char> tn;
+  __shared__ std::conditional_t<TREE && MB && DBG, TreeDbgLds, char> tdbg;
 
   const int nc = d.dv / kCB;
   int item = xcd_item(blockIdx.x, gridDim.x);
@@ -275,6 +298,8 @@ void mverify_kernel(
       *reinterpret_cast<u32x4*>(&rows.k[rt][pe]) = kr[p];
       *reinterpret_cast<u32x4*>(&rows.q[rt][pe]) = qr[p];
       *reinterpret_cast<u32x4*>(&rows.v[rt][pe]) = vr[p];
+      if constexpr (TREE && MB)
+        *reinterpret_cast<u32x4*>(&tn.k[tb + rt][pe]) = kr[p];
     }
     // every thread stores (threads past kTok into the discarded slot): a
     // store under a branch lets the compiler sink the gate loads into it,
@@ -511,23 +536,28 @@ void mverify_kernel(
     const bool tv = n < Tb;
     const float a_t = tv ? __expf(gt) : 1.0f;
     float Gs, c, phi = 1.f;
-    int R;
-    uint32_t anc;  // bit s: token s is a strict ancestor of token n
+    int R;         // deepest zero-decay token or node on the path (window index)
+    uint32_t anc;  // bit s: token tb + s is a strict ancestor of token tb + n
+    [[maybe_unused]] uint64_t ancx = 0;  // trees: strict ancestors in earlier blocks
     if constexpr (TREE) {
       // pointer jumping over the ancestor chain: lane n holds the aggregate
       // of the path segment (J, n] (segment sum and deepest zero-decay node,
       // ancestor set, product of the decays) and combines it with the one that
       // lane J holds for (J', J], all lanes at once; parents precede their
-      // children, so a path has at most 16 nodes and four jumps reach the
-      // root.  On a chain this is the window's scan, step for step.
-      int J = -1;
-      for (int t = 0; t < T; ++t) {
-        const int par = tree_parent(tree, lane * d.T + t);
-        J = n == t ? par : J;
+      // children, so a segment inside the block has at most 16 nodes and four
+      // jumps reach its first node.  On a chain this is the window's scan,
+      // step for step.  In a tree of several blocks the segment then meets
+      // the aggregate of its first node's parent, a node of an earlier block
+      // (ext), kept in LDS.
+      int J = -1, ext = -1;
+      for (int t = 0; t < Tb; ++t) {
+        const int par = tree_parent(tree, lane * d.T + tb + t);
+        J = n == t ? (par >= tb ? par - tb : -1) : J;
+        ext = n == t ? (par >= tb ? -1 : par) : ext;
       }
       const bool reset = gt < kReset;
       Gs = reset ? 0.f : gt;
-      R = reset ? n : -1;
+      R = reset ? tb + n : -1;
       anc = 0u;
       c = a_t;
 #pragma unroll
@@ -538,21 +568,35 @@ void mverify_kernel(
         const uint32_t ay = (uint32_t)__shfl((int)anc, src, 16);
         const float cy = __shfl(c, src, 16);
         const int Jy = __shfl(J, src, 16);
+        const int ey = __shfl(ext, src, 16);
         if (J >= 0) {
           Gs = R < 0 ? Gy + Gs : Gs;
           R = R > Ry ? R : Ry;
           anc = anc | ay | (1u << J);
           c *= cy;
           J = Jy;
+          ext = ey;
+        }
+      }
+      if constexpr (MB) {
+        if (ext >= 0) {
+          Gs = R < 0 ? tn.G[ext] + Gs : Gs;
+          R = R > tn.R[ext] ? R : tn.R[ext];
+          ancx = ((uint64_t)tn.ahi[ext] << 32 | tn.alo[ext]) | (1ull << ext);
+          c *= tn.c[ext];
         }
       }
       // the scale sequence of gdn_step.h needs a fold somewhere (rare): walk
       // the nodes in index order, each continuing its parent's scale
       const bool out = !(c >= kScaleLo && c <= kScaleHi);
       if (__builtin_amdgcn_ballot_w64(out && tv) != 0) {
-        for (int t = 0; t < T; ++t) {
-          const int par = tree_parent(tree, lane * d.T + t);
-          const float cp = par < 0 ? 1.0f : lane_value(c, par);
+        for (int t = 0; t < Tb; ++t) {
+          const int par = tree_parent(tree, lane * d.T + tb + t);
+          float cp = 1.0f;
+          if (par >= tb) cp = lane_value(c, par - tb);
+          if constexpr (MB) {
+            if (par >= 0 && par < tb) cp = tn.c[par];
+          }
           float cn, fo = 1.f;
           if (scale_step(cp, lane_value(a_t, t), cn)) {
             fo = cn;
@@ -567,7 +611,7 @@ void mverify_kernel(
     } else {
       const bool reset = gt < kReset;
       Gs = reset ? 0.f : gt;
-      R = reset ? n : -1;
+      R = reset ? tb + n : -1;
       anc = (1u << n) - 1u;
       c = a_t;
       // inclusive scans over the 16 lanes of each row by DPP row shifts; a
@@ -605,6 +649,19 @@ void mverify_kernel(
       }
     }
     const float A = R >= 0 ? 0.f : __expf(Gs);
+    if constexpr (TREE && MB) {
+      // this block's nodes, for the blocks after it (and its debug replay)
+      if (w == 0 && l < Tb) {
+        const uint64_t a64 = ancx | ((uint64_t)anc << tb);
+        tn.G[tb + n] = Gs;
+        tn.R[tb + n] = R;
+        tn.c[tb + n] = c;
+        tn.phi[tb + n] = phi;
+        tn.rk[tb + n] = rk;
+        tn.alo[tb + n] = (uint32_t)a64;
+        tn.ahi[tb + n] = (uint32_t)(a64 >> 32);
+      }
+    }
     const float f2 = rk * __builtin_amdgcn_rcpf(c);  // ut = u * f2
     const float so = scale * rq * A;                 // on (Q H)_n
     const float xb = bt * A * rk;                    // on (K H)_n
@@ -636,7 +693,7 @@ void mverify_kernel(
         const bool below = (anc >> s) & 1u;  // s a strict ancestor of n
         const bool on_path = below || s == n;
         const float dx = __expf(Gs - Gss);
-        const float dec = (on_path && s >= R) ? dx : 0.f;
+        const float dec = (on_path && tb + s >= R) ? dx : 0.f;
         const float lv = bk * rks * KK[e] * dec;
         W.Lt[s * kLS + n] = below ? lv : 0.f;  // L[n][s], transposed
         PA[e] = on_path ? sq * rks * KQ[e] * dec : 0.f;
@@ -750,6 +807,64 @@ void mverify_kernel(
       X[0][e] = te ? x0 : 0.f;
       X[1][e] = te ? x1 : 0.f;
     }
+    // ---- draft trees of several blocks: the ancestors in earlier blocks,
+    // by block forward substitution of the whole window's system (every node
+    // is solved from the root state H): X_b -= L_bb' U_b' and O_b +=
+    // P_bb' U_b' for each earlier block b', with L_bb' and P_bb' the
+    // ancestor-masked, path-decayed entries between the blocks' nodes
+    [[maybe_unused]] f32x4 Oc[2] = {f32x4{0.f, 0.f, 0.f, 0.f},
+                                    f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (TREE && MB) {
+      const float bk = bt * rk, sq = scale * rq;
+      const uint32_t alo = (uint32_t)ancx, ahi = (uint32_t)(ancx >> 32);
+#pragma unroll 1
+      for (int bp = 0; bp < tb / kTok; ++bp) {
+        // lane (g4, n), entry e: (k_s . k_t) and (k_s . q_t) for node
+        // s = 16 bp + 4 g4 + e and node t = tb + n
+        f32x4 KKx = {0.f, 0.f, 0.f, 0.f}, KQx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          const Frag fb = frag8(&tn.k[kTok * bp + n][32 * ks + 8 * g4]);
+          const Frag kf = frag_k(ks), qf = frag_q(ks);
+          KKx = mma_bf16(fb.h, kf.h, KKx);
+          KQx = mma_bf16(fb.h, qf.h, KQx);
+          if constexpr (F32) {  // the part products of order at most 2^-16
+            KKx = mma_bf16(fb.h, kf.m, KKx);
+            KKx = mma_bf16(fb.m, kf.h, KKx);
+            KKx = mma_bf16(fb.h, kf.l, KKx);
+            KKx = mma_bf16(fb.m, kf.m, KKx);
+            KKx = mma_bf16(fb.l, kf.h, KKx);
+            KQx = mma_bf16(fb.h, qf.m, KQx);
+            KQx = mma_bf16(fb.m, qf.h, KQx);
+            KQx = mma_bf16(fb.h, qf.l, KQx);
+            KQx = mma_bf16(fb.m, qf.m, KQx);
+            KQx = mma_bf16(fb.l, qf.h, KQx);
+          }
+        }
+        float La[4], Pa[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sg = kTok * bp + 4 * g4 + e;
+          const bool an = (((sg < 32 ? alo >> sg : ahi >> (sg - 32))) & 1u) != 0;
+          const float dec = (an && sg >= R) ? __expf(Gs - tn.G[sg]) : 0.f;
+          const float rks = tn.rk[sg];
+          La[e] = bk * rks * KKx[e] * dec;
+          Pa[e] = sq * rks * KQx[e] * dec;
+        }
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          const f32x4 Ub = tn.U[w][bp][cs][l];
+          f32x4 Xc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Xc = mma_f32(La[e], Ub[e], Xc);
+            Oc[cs] = mma_f32(Pa[e], Ub[e], Oc[cs]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) X[cs][e] -= Xc[e];
+        }
+      }
+    }
     const float ta[4] = {TA.x, TA.y, TA.z, TA.w};
     f32x4 U[2], O[2];
 #pragma unroll
@@ -761,6 +876,13 @@ void mverify_kernel(
       for (int e = 0; e < 4; ++e) O[cs][e] = soe[e] * QH[cs][e];
 #pragma unroll
       for (int e = 0; e < 4; ++e) O[cs] = mma_f32(PA[e], U[cs][e], O[cs]);
+      if constexpr (TREE && MB) O[cs] += Oc[cs];
+    }
+    if constexpr (TREE && MB) {
+      if (tb + kTok < T) {
+        tn.U[w][tb / kTok][0][l] = U[0];
+        tn.U[w][tb / kTok][1][l] = U[1];
+      }
     }
     float* __restrict__ o0 = o + ((tok0 + tb) * d.Hv + h) * (size_t)dv;
     float* __restrict__ u0 = rec_u + ((tok0 + tb) * d.Hv + h) * (size_t)dv;
@@ -838,7 +960,54 @@ void mverify_kernel(
             *srow(dp, 32 * ks + e) =
                 f32x2{materialise(ct, st[ks][e][0]), materialise(ct, st[ks][e][1])};
       };
-      if constexpr (TREE) {
+      if constexpr (TREE && MB) {
+        // the path's records over every block: ut tiles, keys, folds and
+        // ancestor sets of all nodes so far from LDS
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tdbg.Us[w][(tb + 4 * g4 + e) * kUS + 2 * n] = ut[0][e];
+          tdbg.Us[w][(tb + 4 * g4 + e) * kUS + 2 * n + 1] = ut[1][e];
+        }
+        __syncthreads();  // this block's node records (wave 0) are in place
+        auto apply_node = [&](f32x2 (&st)[kKS][8], int r) {
+          const float ph = tn.phi[r];
+          if (ph != 1.f) {
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                st[ks][e][0] = ph * st[ks][e][0];
+                st[ks][e][1] = ph * st[ks][e][1];
+              }
+          }
+          const float ua = tdbg.Us[w][r * kUS + 2 * n];
+          const float ub = tdbg.Us[w][r * kUS + 2 * n + 1];
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks) {
+            float kx[8];
+            row8(&tn.k[r][32 * ks + 8 * g4], kx);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              st[ks][e][0] = state_update(st[ks][e][0], ua, kx[e]);
+              st[ks][e][1] = state_update(st[ks][e][1], ub, kx[e]);
+            }
+          }
+        };
+#pragma unroll 1
+        for (int t = 0; t < Tb; ++t) {
+          const uint64_t path = ((uint64_t)tn.ahi[tb + t] << 32 | tn.alo[tb + t]) |
+                                (1ull << (tb + t));
+          f32x2 sd[kKS][8];
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sd[ks][e] = s2[ks][e];
+#pragma unroll 1
+          for (int r = 0; r <= tb + t; ++r)
+            if ((path >> r) & 1ull) apply_node(sd, r);
+          emit(sd, t);
+        }
+      } else if constexpr (TREE) {
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
           const uint32_t path = (uint32_t)lane_int((int)anc, t) | (1u << t);
@@ -894,7 +1063,7 @@ void mverify_kernel(
     // entries it holds.  Folds inside the block (rare) scale the start state
     // by the product of the block's phi and each ut_t by the phi after
     // token t: the closed form of the fold-then-write steps.
-    if (more) {
+    if (!TREE && more) {
       float ub[2][4];
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs)
@@ -990,7 +1159,9 @@ void mverify_kernel(
         }
     }
     if (!more) break;
-    c_in = lane_value(c, Tb - 1);
+    // a chain's next block continues the scale; a tree's nodes continue
+    // their parents' scales (its blocks all start from the root state)
+    if constexpr (!TREE) c_in = lane_value(c, Tb - 1);
   }
 }
 
@@ -1014,7 +1185,7 @@ bool mverify_eligible(const gdn_dims& d, int in_dtype, const VerifyArgs& a,
   auto al = [](const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; };
   return (in_dtype == GDN_BF16 || in_dtype == GDN_F32) &&
          d.d_k == wm::kDK && d.d_v % wm::kCB == 0 &&
-         d.t_max <= (tree ? wm::kTok : GDN_MAX_T) && al(a.q, 16) &&
+         d.t_max <= GDN_MAX_T && al(a.q, 16) &&
          al(a.k, 16) && al(a.v, 4) && al(a.S, 8) && al(a.o, 8) &&
          (a.dbg == nullptr || al(a.dbg, 8));
 }
@@ -1047,6 +1218,13 @@ hipError_t launch_mverify_tree(const WinDims& w, const LaneTable& tl,
                                hipStream_t st) {
   PrevRecords none;
   memset(&none, 0, sizeof(none));
+  if (w.T > wm::kTok) {  // trees of more than 16 nodes: several blocks
+    if (a.f32)
+      return a.dbg ? wm::launch_t<false, true, true, true, true>(w, tl, a, none, tree, st)
+                   : wm::launch_t<false, false, true, true, true>(w, tl, a, none, tree, st);
+    return a.dbg ? wm::launch_t<false, true, true, true>(w, tl, a, none, tree, st)
+                 : wm::launch_t<false, false, true, true>(w, tl, a, none, tree, st);
+  }
   if (a.f32)
     return a.dbg ? wm::launch_t<false, true, true, false, true>(w, tl, a, none, tree, st)
                  : wm::launch_t<false, false, true, false, true>(w, tl, a, none, tree, st);

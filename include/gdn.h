@@ -194,13 +194,15 @@ int gdn_commit(const gdn_dims* dims, const int32_t* m_lane,
  * ReplaySSM requirement, per node).
  *   parent   host int32 [n_lanes][t_max]: parent[n][t] in -1..t-1 for
  *            t < t_lane[n] (-1: the node steps from S0); nodes are ordered so
- *            that a parent precedes its children.  With d_k = d_v = 128
- *            and t_max <= 16 (and without
- *            GDN_FLAG_TOKENWISE) the tree is evaluated as one block product
- *            (the causal mask of the chunked form replaced by the ancestor
- *            relation) and any order costs the same; the debug
- *            state of a node is then the replay of the records on its root
- *            path.  Otherwise depth-first order is cheapest: verify rebuilds
+ *            that a parent precedes its children.  With d_k = 128 and d_v a
+ *            multiple of 128 (and without GDN_FLAG_TOKENWISE) the tree is
+ *            evaluated as block products on the matrix cores (the causal
+ *            mask of the chunked form replaced by the ancestor relation;
+ *            trees of more than 16 nodes in two blocks of 16, the second
+ *            solved against its ancestors in the first) and any order costs
+ *            the same; the debug state of a node is then the replay of the
+ *            records on its root path, and asking for it changes neither o
+ *            nor the records.  Otherwise depth-first order is cheapest: verify rebuilds
  *            the parent's state (S0 plus the path's recorded steps) whenever
  *            parent[t] != t - 1.
  *   path     host int32 [n_lanes][t_max]: the first m_lane[n] entries are the

@@ -216,12 +216,15 @@ def test_fused_window_emits_the_rule_on_the_replayed_states(T):
     assert e_u <= BOUND_U and e_o <= BOUND_O
 
 
-def test_tree_emits_the_rule_on_the_replayed_states():
-    """Draft tree: node t steps from its parent's replayed state."""
-    shape = gs.WindowShape(1, 4, 4, 2, 128, 128, 16)
-    key, w, S0 = _window("tree", shape, _zero_decay)
+@pytest.mark.parametrize("T", [16, 32])
+def test_tree_emits_the_rule_on_the_replayed_states(T):
+    """Draft tree: node t steps from its parent's replayed state (32 nodes:
+    two blocks, ancestors across blocks)."""
+    shape = gs.WindowShape(1, 4, 4, 2, 128, 128, T)
+    key, w, S0 = _window("tree" if T == 16 else "tree%d" % T, shape, _zero_decay)
+    w.t_lane[0] = T
     dims = gdn.Dims.of(*shape.__dict__.values())
-    parent = gs.tree_parents(w.t_lane, 16, key)
+    parent = gs.tree_parents(w.t_lane, T, key)
     q, k, v, beta, g = window_to_dev(w, torch)
     o, dbg = _empty(dims)
     rec = torch.empty(gdn.records_bytes(dims), dtype=torch.uint8, device="cuda")

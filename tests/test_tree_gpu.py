@@ -94,8 +94,12 @@ CASES = [
     ("bf16_d128_dv256", 1, 2, 2, 1, 128, 256, 10, True),
     # f32 inputs on the matrix cores (rows as three bf16 parts)
     ("f32_d128", 1, 3, 4, 2, 128, 128, 16, False),
-    # the largest trees the ABI takes (32 nodes): the token-by-token kernel
+    # trees of more than 16 nodes (the ABI takes 32): two blocks of 16 on
+    # the matrix cores
     ("bf16_d128_32_nodes", 1, 2, 2, 1, 128, 128, 32, True),
+    ("bf16_d128_29_nodes", 2, 3, 4, 2, 128, 128, 29, True),
+    ("f32_d128_32_nodes", 1, 2, 2, 1, 128, 128, 32, False),
+    ("bf16_d128_dv256_24_nodes", 1, 2, 2, 1, 128, 256, 24, True),
 ]
 
 
@@ -106,20 +110,53 @@ def test_tree_parity_and_bitexact_path_commit(case):
                 gs.tree_parents)
 
 
-def test_star_tree_rebuilds_at_every_node():
+@pytest.mark.parametrize("T", [16, 32])
+def test_star_tree_rebuilds_at_every_node(T):
     """Every node hangs off the root: verify rebuilds the root's state before
-    every node after the first child."""
-    _check_tree("star", gs.WindowShape(1, 3, 4, 2, 128, 128, 16), True, _star)
+    every node after the first child (with 32 nodes, every node of the
+    second block has its parent in the first)."""
+    _check_tree("star%d" % T, gs.WindowShape(1, 3, 4, 2, 128, 128, T), True,
+                _star)
 
 
-def test_tree_with_scale_folds():
-    """Strong decay along deep branches: folds happen on some paths only."""
+@pytest.mark.parametrize("T", [16, 32])
+def test_tree_with_scale_folds(T):
+    """Strong decay along deep branches: folds happen on some paths only
+    (with 32 nodes also on paths that cross blocks), and alpha = 0 nodes."""
     def fill(g):
         g[:] = -3.0 - 0.5 * np.arange(g.shape[-1])[None, None, None, :]
         g[:, :, 5] = -np.inf
-    _check_tree("folds", gs.WindowShape(1, 3, 4, 2, 128, 128, 16), True,
-                lambda t, T, key: gs.tree_parents(t, T, key, p_deeper=0.85),
+        if g.shape[2] > 20:
+            g[:, :, 20, ::2] = -200.0
+    _check_tree("folds%d" % T, gs.WindowShape(1, 3, 4, 2, 128, 128, T), True,
+                lambda t, T_, key: gs.tree_parents(t, T_, key, p_deeper=0.85),
                 g_fill=fill)
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_tree_debug_states_leave_outputs_unchanged(bf16):
+    """32-node trees (two blocks): asking for the debug states changes
+    neither the outputs nor the records, bit for bit."""
+    shape = gs.WindowShape(1, 3, 4, 2, 128, 128, 32)
+    key = (503, int(bf16))
+    w = gs.window_inputs(shape, key, bf16=bf16, ragged=True)
+    w.t_lane[0] = 32
+    parent = gs.tree_parents(w.t_lane, 32, key)
+    S0 = gs.initial_state(shape, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o1, r1, dbg = _run_tree(dims, w, parent, S_dev)
+    o2, r2, _ = _run_tree(dims, w, parent, S_dev, dbg=False)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(o1, 7.0), torch.nan_to_num(o2, 7.0))
+    paths = gs.accepted_tree_paths(parent, w.t_lane, key)
+    Sa, Sb = to_dev(S0, torch), to_dev(S0, torch)
+    plist = [list(p) for p in parent]
+    gdn.commit_path(dims, paths, w.t_lane, plist, r1, Sa)
+    gdn.commit_path(dims, paths, w.t_lane, plist, r2, Sb)
+    assert torch.equal(Sa, Sb)
+    say("  %s: outputs and records unchanged by debug states"
+        % ("bf16" if bf16 else "f32"))
 
 
 def test_chain_tree_matches_the_linear_window():
