@@ -187,18 +187,23 @@ def test_chain_tree_matches_the_linear_window():
     assert s_rel_err(S_a.cpu().numpy(), S_b.cpu().numpy()) <= TOL
 
 
-def test_tree_full_batch_sampled_layer():
-    """48 layers x 8 lanes x 32/16 heads, d = 128, 16-node DFS trees: the
-    oracle follows layer 0 (outputs and an accepted-path commit per lane),
-    and the 48-layer commit of layer 0 matches a one-layer debug run bitwise."""
-    shape = gs.EIGHT_LANES
+@pytest.mark.parametrize("T", [16, 32])
+def test_tree_full_batch_sampled_layer(T):
+    """48 layers x 8 lanes x 32/16 heads, d = 128, DFS trees of up to 16 and
+    32 nodes (the bench's tree workloads): the oracle follows layer 0
+    (outputs and an accepted-path commit per lane), and the 48-layer commit
+    of layer 0 matches a one-layer debug run bitwise."""
+    shape = gs.WindowShape(gs.EIGHT_LANES.n_layers, gs.EIGHT_LANES.n_lanes,
+                           gs.EIGHT_LANES.h_v, gs.EIGHT_LANES.h_k, 128, 128, T)
     dims = gdn.Dims.of(*shape.__dict__.values())
-    w = gs.window_inputs(shape, (502,), ragged=True)
-    parent = gs.tree_parents(w.t_lane, 16, (502,))
-    paths = gs.accepted_tree_paths(parent, w.t_lane, (502,))
-    S0 = gs.initial_state(shape, (502,))
+    key = (502,) if T == 16 else (502, T)
+    w = gs.window_inputs(shape, key, ragged=True)
+    w.t_lane[0] = T
+    parent = gs.tree_parents(w.t_lane, T, key)
+    paths = gs.accepted_tree_paths(parent, w.t_lane, key)
+    S0 = gs.initial_state(shape, key)
     S_dev = to_dev(S0, torch)
-    say("tree full batch: verify")
+    say("tree full batch, %d nodes: verify" % T)
     o, rec, _ = _run_tree(dims, w, parent, S_dev, dbg=False)
     gdn.commit_path(dims, paths, w.t_lane, [list(p) for p in parent], rec,
                     S_dev)
@@ -212,7 +217,7 @@ def test_tree_full_batch_sampled_layer():
     e_s = s_rel_err(S_dev[:1].cpu().numpy(), S_ref)
     say("  layer 0: o err %.2e S err %.2e" % (e_o, e_s))
     assert e_o <= TOL and e_s <= TOL
-    d1 = gdn.Dims.of(1, 8, 32, 16, 128, 128, 16)
+    d1 = gdn.Dims.of(1, 8, 32, 16, 128, 128, T)
     w1 = gs.WindowInputs(d1, True, w.q[:1], w.k[:1], w.v[:1], w.beta[:1],
                          w.g[:1], w.t_lane)
     S1 = to_dev(S0[:1], torch)

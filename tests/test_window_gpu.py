@@ -580,6 +580,52 @@ def test_eight_lanes_48_layers_ragged():
     assert np.array_equal(S1, S_gpu[:1])
 
 
+@pytest.mark.parametrize("T", [32, 64])
+def test_eight_lanes_48_layers_long_windows(T):
+    """8 lanes x 48 layers x 32/16 heads, d = 128, windows of up to 32 and
+    64 tokens (blocks of 16, the bench's long-window shapes), m_l ~
+    U{0..T_l}: the oracle follows layers 0 and 47 (o of every token and the
+    committed state), and layer 0's commit is bit for bit a one-layer debug
+    run's state."""
+    base = gs.EIGHT_LANES
+    shape = gs.WindowShape(base.n_layers, base.n_lanes, base.h_v, base.h_k,
+                           128, 128, T)
+    key = (gs.KEY_EIGHT_LANES, T)
+    say("8 lanes x 48 layers, T = %d: generating inputs" % T)
+    w = gs.window_inputs(shape, key, ragged=True)
+    w.t_lane[0] = T
+    S0 = gs.initial_state(shape, key)
+    m = gs.accepted_uniform(w.t_lane, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    say("  verify, T =", w.t_lane, "m =", m)
+    o, rec, _ = _run_verify(dims, w, S_dev)
+    o_np = o.cpu().numpy()
+    _check_untouched_rows(o_np, w.t_lane)
+    gdn.commit(dims, m, w.t_lane, rec, S_dev)
+    S_gpu = S_dev.cpu().numpy()
+    sl = [0, base.n_layers - 1]
+    q64, k64, v64, b64, g64 = (a[sl] for a in w.as_f64())
+    o_ref, _ = oracle.verify(q64, k64, v64, b64, g64, S0[sl], w.t_lane)
+    e_o = o_rel_err(o_np[sl], o_ref, w.t_lane)
+    S_ref = oracle.commit(q64, k64, v64, b64, g64, S0[sl], m)
+    e_s = s_rel_err(S_gpu[sl], S_ref)
+    say("  layers %s: o err %.3e  S err %.3e" % (sl, e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL
+    d1 = gdn.Dims.of(1, shape.n_lanes, shape.h_v, shape.h_k, 128, 128, T)
+    w1 = gs.WindowInputs(d1, True, w.q[:1], w.k[:1], w.v[:1], w.beta[:1],
+                         w.g[:1], w.t_lane)
+    S1 = to_dev(S0[:1], torch)
+    _, rec1, dbg1 = _run_verify(d1, w1, S1, dbg=True)
+    gdn.commit(d1, m, w.t_lane, rec1, S1)
+    dbg1 = dbg1.cpu().numpy()
+    S1 = S1.cpu().numpy()
+    for n in range(shape.n_lanes):
+        want = S0[:1, n] if m[n] == 0 else dbg1[:, n, m[n] - 1]
+        assert np.array_equal(S1[:, n], want), n
+    assert np.array_equal(S1, S_gpu[:1])
+
+
 def _chained(shape, case, rounds, acc, sample_layers, t_fixed, pool=8, say_every=16):
     """Chained verify -> commit(m) rounds; the oracle follows the sampled
     layers through every round.  Window inputs cycle through a pool of
