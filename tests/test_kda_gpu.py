@@ -140,6 +140,48 @@ def test_kda_debug_states_leave_outputs_unchanged(case):
     say("  %s: outputs and records unchanged by debug states" % name)
 
 
+def test_kda_full_batch_long_windows():
+    """8 lanes x 48 layers x 32/16 heads, d = 128, windows of up to 40
+    tokens (blocks of 16), ragged, m ~ U{0..T}: the oracle follows layers 0
+    and 47 (o of every token and the committed state), and layer 0's commit
+    is bit for bit a one-layer debug run's state."""
+    T = 40
+    shape = gs.WindowShape(48, 8, 32, 16, 128, 128, T)
+    key = (604, T)
+    w = gs.window_inputs(shape, key, ragged=True)
+    w.t_lane[0] = T
+    gk = gs.kda_gates(shape, key)
+    S0 = gs.initial_state(shape, key)
+    m = gs.accepted_uniform(w.t_lane, key)
+    dims = gdn.Dims.of(*shape.__dict__.values())
+    S_dev = to_dev(S0, torch)
+    o, rec, _ = _kda_run(dims, w, gk, S_dev, dbg=False)
+    gdn.kda_commit(dims, m, w.t_lane, rec, S_dev)
+    torch.cuda.synchronize()
+    sl = [0, 47]
+    q64, k64, v64, b64, _ = (a[sl] for a in w.as_f64())
+    g64 = gk[sl].astype(np.float64)
+    o_ref, _ = oracle.kda_verify(q64, k64, v64, b64, g64, S0[sl], w.t_lane)
+    e_o = o_rel_err(o.cpu().numpy()[sl], o_ref, w.t_lane)
+    S_ref = oracle.kda_commit(q64, k64, v64, b64, g64, S0[sl], m)
+    S_all = S_dev.cpu().numpy()
+    e_s = s_rel_err(S_all[sl], S_ref)
+    say("  kda full batch T=%d, layers %s: o err %.2e S err %.2e" % (T, sl, e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL
+    d1 = gdn.Dims.of(1, 8, 32, 16, 128, 128, T)
+    w1 = gs.WindowInputs(d1, True, w.q[:1], w.k[:1], w.v[:1], w.beta[:1],
+                         w.g[:1], w.t_lane)
+    S1 = to_dev(S0[:1], torch)
+    _, rec1, dbg1 = _kda_run(d1, w1, gk[:1], S1)
+    gdn.kda_commit(d1, m, w.t_lane, rec1, S1)
+    torch.cuda.synchronize()
+    dbg1, S1 = dbg1.cpu().numpy(), S1.cpu().numpy()
+    for n in range(8):
+        want = S0[:1, n] if m[n] == 0 else dbg1[:, n, m[n] - 1]
+        assert np.array_equal(S1[:, n], want), n
+    assert np.array_equal(S1, S_all[:1])
+
+
 def test_kda_zero_gates_are_bitwise_identity():
     """beta = 0 and alpha = 1 on every channel: S * 1 then fma(0, k, S)
     leave the state bit for bit."""
